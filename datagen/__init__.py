@@ -1,0 +1,177 @@
+"""Seeded synthetic inputs for the absorbed Gated-MLA layer.
+
+This module is shared by the CPU oracle side and the HIP side of the tests and
+the benchmark.  It only draws random numbers and rounds them to the storage
+dtype; it contains none of the layer's arithmetic.
+
+Recipe (shapes follow the MLA variable table of the "符号表" page and the
+toy/full-size table of the "K3 混合架构" page):
+
+* every tensor is drawn from its own counter-based Philox4x64 stream, keyed by
+  ``(seed, tensor_id << 32 | chunk)``, so a tensor never depends on the size or
+  order of the others and large tensors are drawn in independent row chunks;
+* ``q ~ N(0,1)`` with shape ``[B,T,H,d_q]`` (prefill) or ``[B,H,d_q]`` (decode);
+* ``c`` is a row-wise RMS-normalised ``N(0,1)`` draw over the last axis
+  (gain 1, ``eps = 1e-6`` inside the square root), computed in float64;
+* ``W_UK [H,d_q,r]`` and ``W_UV [H,d_v,r]`` are ``N(0, 1/r)``;
+* ``gate`` (pre-sigmoid logits) ``~ N(0,1)`` with shape ``[B,T,H*d_v]`` or
+  ``[B,H*d_v]``;
+* decode cache lengths are i.i.d. uniform integers on ``[len_lo, len_hi]``;
+  ``cu_seqlens`` is their int32 exclusive prefix sum;
+* float64 draws are rounded to float32 (round-to-nearest-even) and, for bf16
+  storage, float32 is rounded to bf16 (round-to-nearest-even).
+
+Storage: bf16 tensors are returned as ``numpy.uint16`` bit patterns, float32
+tensors as ``numpy.float32``.  ``as_f32`` returns the exact float32 value of
+either, which is what the oracle consumes.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+
+_TID = {"q": 1, "c": 2, "w_uk": 3, "w_uv": 4, "gate": 5, "lens": 6}
+_CHUNK_ROWS = 1 << 15
+_RMS_EPS = 1e-6
+
+
+def _gen(seed: int, tid: int, chunk: int) -> np.random.Generator:
+    key = np.array([seed & 0xFFFFFFFFFFFFFFFF, (tid << 32) | chunk], dtype=np.uint64)
+    return np.random.Generator(np.random.Philox(key=key))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (round-to-nearest-even); returns uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rnd = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    return ((u + rnd) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact float32 value of bf16 bit patterns."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def as_f32(x: np.ndarray) -> np.ndarray:
+    """Exact float32 view of a stored tensor (bf16 bits or float32)."""
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f32(x)
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _store(x64: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = x64.astype(np.float32)
+    if dtype == BF16:
+        return f32_to_bf16_bits(x32)
+    if dtype == F32:
+        return x32
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _draw_rows(seed: int, name: str, rows: int, cols: int, std: float, dtype: str,
+               rms_norm: bool = False) -> np.ndarray:
+    """rows x cols standard-normal draw (times std), chunked by rows."""
+    out = np.empty((rows, cols), dtype=np.uint16 if dtype == BF16 else np.float32)
+    nchunks = max(1, -(-rows // _CHUNK_ROWS))
+
+    def work(ci: int) -> None:
+        r0 = ci * _CHUNK_ROWS
+        r1 = min(rows, r0 + _CHUNK_ROWS)
+        if r1 <= r0:
+            return
+        x = _gen(seed, _TID[name], ci).standard_normal((r1 - r0, cols))
+        if rms_norm:
+            x = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + _RMS_EPS)
+        elif std != 1.0:
+            x = x * std
+        out[r0:r1] = _store(x, dtype)
+
+    workers = min(nchunks, int(os.environ.get("DATAGEN_THREADS", "8")))
+    if workers <= 1:
+        for ci in range(nchunks):
+            work(ci)
+    else:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(work, range(nchunks)))
+    return out
+
+
+def prefill_inputs(B: int, T: int, H: int, d_q: int, d_v: int, r: int,
+                   dtype: str = BF16, seed: int = 0) -> dict:
+    """Inputs of one prefill call; all arrays row-major contiguous."""
+    if min(B, T, H, d_q, d_v, r) <= 0:
+        raise ValueError("all sizes must be positive")
+    q = _draw_rows(seed, "q", B * T * H, d_q, 1.0, dtype).reshape(B, T, H, d_q)
+    c = _draw_rows(seed, "c", B * T, r, 1.0, dtype, rms_norm=True).reshape(B, T, r)
+    w_uk = _draw_rows(seed, "w_uk", H * d_q, r, r ** -0.5, dtype).reshape(H, d_q, r)
+    w_uv = _draw_rows(seed, "w_uv", H * d_v, r, r ** -0.5, dtype).reshape(H, d_v, r)
+    gate = _draw_rows(seed, "gate", B * T, H * d_v, 1.0, dtype).reshape(B, T, H * d_v)
+    return dict(q=q, c=c, w_uk=w_uk, w_uv=w_uv, gate=gate,
+                B=B, T=T, H=H, d_q=d_q, d_v=d_v, r=r, dtype=dtype, seed=seed)
+
+
+def decode_lengths(B: int, len_lo: int, len_hi: int, seed: int = 0) -> np.ndarray:
+    """i.i.d. uniform integer cache lengths on [len_lo, len_hi] (inclusive)."""
+    if not (1 <= len_lo <= len_hi):
+        raise ValueError("need 1 <= len_lo <= len_hi")
+    return _gen(seed, _TID["lens"], 0).integers(len_lo, len_hi + 1, size=B).astype(np.int64)
+
+
+def decode_inputs(B: int, H: int, d_q: int, d_v: int, r: int, dtype: str = BF16,
+                  seed: int = 0, len_lo: int = 1024, len_hi: int = 32768,
+                  lengths=None) -> dict:
+    """Inputs of one decode call against a packed latent cache."""
+    lens = (np.asarray(lengths, dtype=np.int64) if lengths is not None
+            else decode_lengths(B, len_lo, len_hi, seed))
+    if lens.shape != (B,) or (lens < 1).any():
+        raise ValueError("lengths must be B positive integers")
+    cu = np.zeros(B + 1, dtype=np.int64)
+    np.cumsum(lens, out=cu[1:])
+    if cu[-1] >= 2 ** 31:
+        raise ValueError("total cache length exceeds int32")
+    total = int(cu[-1])
+    q = _draw_rows(seed, "q", B * H, d_q, 1.0, dtype).reshape(B, H, d_q)
+    c_cache = _draw_rows(seed, "c", total, r, 1.0, dtype, rms_norm=True)
+    w_uk = _draw_rows(seed, "w_uk", H * d_q, r, r ** -0.5, dtype).reshape(H, d_q, r)
+    w_uv = _draw_rows(seed, "w_uv", H * d_v, r, r ** -0.5, dtype).reshape(H, d_v, r)
+    gate = _draw_rows(seed, "gate", B, H * d_v, 1.0, dtype).reshape(B, H * d_v)
+    return dict(q=q, c_cache=c_cache, cu_seqlens=cu.astype(np.int32), lengths=lens,
+                w_uk=w_uk, w_uv=w_uv, gate=gate,
+                B=B, H=H, d_q=d_q, d_v=d_v, r=r, dtype=dtype, seed=seed,
+                max_len=int(lens.max()))
+
+
+# Named workloads: the pages' toy and full-scale shapes.  Seeds are
+# 0x4D4C41 + index so each workload draws independent data.
+SEED_BASE = 0x4D4C41
+
+WORKLOADS = {
+    "toy_f32": dict(kind="prefill", B=2, T=128, H=8, d_q=16, d_v=16, r=32, dtype=F32,
+                    scale=1.0, seed=SEED_BASE + 0),
+    "toy_max": dict(kind="prefill", B=4, T=2048, H=8, d_q=16, d_v=16, r=32, dtype=BF16,
+                    scale=16 ** -0.5, seed=SEED_BASE + 1),
+    "mid": dict(kind="prefill", B=4, T=4096, H=32, d_q=64, d_v=64, r=256, dtype=BF16,
+                scale=64 ** -0.5, seed=SEED_BASE + 2),
+    "full_prefill": dict(kind="prefill", B=1, T=8192, H=96, d_q=128, d_v=128, r=512,
+                         dtype=BF16, scale=128 ** -0.5, seed=SEED_BASE + 3),
+    "full_decode": dict(kind="decode", B=64, H=96, d_q=128, d_v=128, r=512, dtype=BF16,
+                        len_lo=1024, len_hi=32768, scale=128 ** -0.5, seed=SEED_BASE + 4),
+}
+
+
+def workload_inputs(name: str) -> dict:
+    w = dict(WORKLOADS[name])
+    kind = w.pop("kind")
+    scale = w.pop("scale")
+    if kind == "prefill":
+        d = prefill_inputs(**w)
+    else:
+        d = decode_inputs(**w)
+    d["scale"] = scale
+    d["kind"] = kind
+    return d

@@ -1,0 +1,176 @@
+"""Plain CPU oracle for the absorbed Gated MLA layer (ctypes wrapper).
+
+TEST INFRASTRUCTURE: only the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import this package.  The product library never loads
+it, and it shares no code with the HIP sources.
+
+The arithmetic lives in ``mla_oracle.c`` (fp64 accumulation, plain loops, one
+OpenMP loop over query rows); this module only compiles it with the host C
+compiler and marshals numpy arrays.  See the C file's header for the
+definition it computes and the passages of the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "mla_oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+
+_CFLAGS = ["-O3", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-mavx2", "-mfma",
+           "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build(out_path: str = LIB, mutant: int = 0, quiet: bool = True) -> str:
+    """Compile the oracle with gcc; mutant != 0 plants one known mistake."""
+    cmd = ["gcc", *_CFLAGS, f"-DORACLE_MUTANT={int(mutant)}", SRC, "-o", out_path + ".tmp", "-lm"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("oracle build failed:\n" + res.stdout + res.stderr)
+    if not quiet and res.stderr:
+        print(res.stderr)
+    os.replace(out_path + ".tmp", out_path)
+    return out_path
+
+
+def _f32(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ct.POINTER(ctype))
+
+
+class Oracle:
+    """One loaded build of the oracle (the default one, or a planted mutant)."""
+
+    def __init__(self, path: str = LIB):
+        if not os.path.exists(path):
+            raise FileNotFoundError(f"{path} not built; call oracle.build()")
+        self.path = path
+        self.lib = ct.CDLL(path)
+        L = self.lib
+        fp, dp, i64p = ct.POINTER(ct.c_float), ct.POINTER(ct.c_double), ct.POINTER(ct.c_int64)
+        I, I64, D = ct.c_int, ct.c_int64, ct.c_double
+        L.oracle_mutant.restype = I
+        L.oracle_qabs.argtypes = [fp, fp, I64, I, I, I, dp, I]
+        L.oracle_prefill.argtypes = [fp, fp, fp, fp, fp, I, I, I, I, I, I, D, i64p, I64, dp, I]
+        L.oracle_decode.argtypes = [fp, fp, i64p, fp, fp, fp, I, I, I, I, I, D, i64p, I64, dp, I]
+        L.oracle_prefill_decompressed.argtypes = [fp, fp, fp, fp, fp, I, I, I, I, I, I, D, dp, I]
+        L.oracle_prefill_attn.argtypes = [fp, fp, fp, I, I, I, I, I, D, dp]
+        for f in ("oracle_qabs", "oracle_prefill", "oracle_decode", "oracle_prefill_decompressed",
+                  "oracle_prefill_attn"):
+            getattr(L, f).restype = I
+
+    @property
+    def mutant(self) -> int:
+        return self.lib.oracle_mutant()
+
+    @staticmethod
+    def _check(rc: int, what: str) -> None:
+        if rc != 0:
+            raise ValueError(f"{what} failed with code {rc}")
+
+    def qabs(self, q, w_uk, threads: int = 0) -> np.ndarray:
+        """Step 1 alone.  q [..., H, dq] -> q_abs [..., H, r] (float64)."""
+        q, w_uk = _f32(q), _f32(w_uk)
+        H, dq, r = w_uk.shape
+        assert q.shape[-2:] == (H, dq)
+        N = int(np.prod(q.shape[:-2], dtype=np.int64))
+        out = np.empty(q.shape[:-1] + (r,), dtype=np.float64)
+        self._check(self.lib.oracle_qabs(_ptr(q, ct.c_float), _ptr(w_uk, ct.c_float), N, H, dq, r,
+                                         _ptr(out, ct.c_double), threads), "oracle_qabs")
+        return out
+
+    def prefill(self, q, c, w_uk, w_uv, gate, scale: float, rows=None, threads: int = 0) -> np.ndarray:
+        """Prefill.  rows: flattened b*T+t indices (None: all).  Returns
+        [B,T,H*dv] for all rows, else [len(rows), H*dv] (float64)."""
+        q, c, w_uk, w_uv, gate = map(_f32, (q, c, w_uk, w_uv, gate))
+        B, T, H, dq = q.shape
+        r = c.shape[-1]
+        dv = w_uv.shape[1]
+        assert c.shape == (B, T, r) and w_uk.shape == (H, dq, r) and w_uv.shape == (H, dv, r)
+        assert gate.shape == (B, T, H * dv)
+        if rows is None:
+            out = np.empty((B, T, H * dv), dtype=np.float64)
+            rp, n = None, B * T
+        else:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            out = np.empty((rows.shape[0], H * dv), dtype=np.float64)
+            rp, n = _ptr(rows, ct.c_int64), rows.shape[0]
+        self._check(self.lib.oracle_prefill(
+            _ptr(q, ct.c_float), _ptr(c, ct.c_float), _ptr(w_uk, ct.c_float), _ptr(w_uv, ct.c_float),
+            _ptr(gate, ct.c_float), B, T, H, dq, dv, r, float(scale), rp, n,
+            _ptr(out, ct.c_double), threads), "oracle_prefill")
+        return out
+
+    def decode(self, q, c_cache, cu_seqlens, w_uk, w_uv, gate, scale: float, seqs=None,
+               threads: int = 0) -> np.ndarray:
+        """Decode.  Returns [B, H*dv] (or [len(seqs), H*dv]) float64."""
+        q, c_cache, w_uk, w_uv, gate = map(_f32, (q, c_cache, w_uk, w_uv, gate))
+        cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+        B, H, dq = q.shape
+        r = c_cache.shape[-1]
+        dv = w_uv.shape[1]
+        assert cu.shape == (B + 1,) and c_cache.shape == (int(cu[-1]), r)
+        assert gate.shape == (B, H * dv)
+        if seqs is None:
+            sp, n = None, B
+        else:
+            seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+            sp, n = _ptr(seqs, ct.c_int64), seqs.shape[0]
+        out = np.empty((n, H * dv), dtype=np.float64)
+        self._check(self.lib.oracle_decode(
+            _ptr(q, ct.c_float), _ptr(c_cache, ct.c_float), _ptr(cu, ct.c_int64),
+            _ptr(w_uk, ct.c_float), _ptr(w_uv, ct.c_float), _ptr(gate, ct.c_float),
+            B, H, dq, dv, r, float(scale), sp, n, _ptr(out, ct.c_double), threads), "oracle_decode")
+        return out
+
+    def prefill_decompressed(self, q, c, w_uk, w_uv, gate, scale: float, threads: int = 0) -> np.ndarray:
+        q, c, w_uk, w_uv, gate = map(_f32, (q, c, w_uk, w_uv, gate))
+        B, T, H, dq = q.shape
+        r = c.shape[-1]
+        dv = w_uv.shape[1]
+        out = np.empty((B, T, H * dv), dtype=np.float64)
+        self._check(self.lib.oracle_prefill_decompressed(
+            _ptr(q, ct.c_float), _ptr(c, ct.c_float), _ptr(w_uk, ct.c_float), _ptr(w_uv, ct.c_float),
+            _ptr(gate, ct.c_float), B, T, H, dq, dv, r, float(scale), _ptr(out, ct.c_double), threads),
+            "oracle_prefill_decompressed")
+        return out
+
+    def attn(self, q, c, w_uk, scale: float) -> np.ndarray:
+        """Attention weights [B,H,T,T] (tiny shapes only)."""
+        q, c, w_uk = map(_f32, (q, c, w_uk))
+        B, T, H, dq = q.shape
+        r = c.shape[-1]
+        out = np.empty((B, H, T, T), dtype=np.float64)
+        self._check(self.lib.oracle_prefill_attn(
+            _ptr(q, ct.c_float), _ptr(c, ct.c_float), _ptr(w_uk, ct.c_float), B, T, H, dq, r,
+            float(scale), _ptr(out, ct.c_double)), "oracle_prefill_attn")
+        return out
+
+
+_default = None
+
+
+def get() -> Oracle:
+    """The default (non-mutant) oracle, built on first use if missing."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        _default = Oracle(LIB)
+    return _default
+
+
+def build_mutant(mutant: int, directory: str | None = None) -> Oracle:
+    """Build and load a planted-mistake variant into a scratch directory."""
+    directory = directory or tempfile.mkdtemp(prefix="oracle_mut_")
+    path = os.path.join(directory, f"liboracle_mut{mutant}.so")
+    build(path, mutant=mutant)
+    return Oracle(path)

@@ -1,0 +1,389 @@
+/*
+ * Plain CPU oracle for the matrix-absorbed, NoPE Gated MLA attention layer.
+ *
+ * TEST INFRASTRUCTURE.  Only the test-suite, the smoke check and the CPU
+ * baseline leg of the benchmark load this library.  It shares no code, header,
+ * table or helper with the HIP library; neither side includes the other.
+ *
+ * Every floating-point quantity is accumulated in float64.  Inputs are the
+ * stored values (float32, or bf16 widened exactly to float32 by the caller).
+ * No intermediate result is rounded to a narrower type.
+ *
+ * Sources (the K3 teaching notes):
+ *   [MLA]  page "Gated MLA（矩阵吸收版）" (matrix-absorbed Gated MLA):
+ *          section 低秩压缩 (low-rank compression: the latent c, W_UK, W_UV),
+ *          section 矩阵吸收的核心思路 (absorbing W_UK into q),
+ *          section 完整计算流（四步） (the four-step computation, steps 2-4),
+ *          section 代码对照 (the GatedMLA.forward listing),
+ *          the warning box on reordering (attn·c)·W_UV^T by associativity.
+ *   [SYM]  page "符号表" (symbol table): section MLA 变量 (MLA variables and
+ *          their shapes) and section Einsum 速查 (einsum cheat-sheet).
+ *
+ * Definition computed (prefill), for every batch b, head h, query t:
+ *   1. qa[j]  = sum_d q[b,t,h,d] * W_UK[h,d,j]                 ([MLA] step 2, absorb)
+ *   2. s_u    = scale * sum_j qa[j] * c[b,u,j]   for u <= t     ([MLA] step 2, score;
+ *               keys u > t are excluded, the causal mask keeps the diagonal)
+ *   3. w_u    = exp(s_u - m) / sum_{u'<=t} exp(s_u' - m),  m = max_u s_u
+ *                                                              ([MLA] step 2, softmax)
+ *   4. ol[j]  = sum_{u<=t} w_u * c[b,u,j]                       ([MLA] step 3, latent sum)
+ *   5. o[v]   = sum_j ol[j] * W_UV[h,v,j]                       ([MLA] step 3, W_UV^T)
+ *   6. out[b,t,h*d_v+v] = o[v] / (1 + exp(-gate[b,t,h*d_v+v])) ([MLA] step 4, gate;
+ *               heads flattened head-major, the output projection is not applied)
+ * The softmax scale is an explicit argument: the pages print none.
+ *
+ * Decode: sequence i with cache rows c_cache[cu[i] .. cu[i+1]) is the same
+ * computation for the query at position len_i - 1, which attends to all
+ * len_i cached rows (its own latent included).
+ *
+ * ORACLE_MUTANT (default 0) plants one known mistake; it exists only so that
+ * the pin tests can show that each such mistake is caught.  Product builds
+ * and every parity comparison use ORACLE_MUTANT == 0.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <omp.h>
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL 1
+#define ORACLE_ENOMEM 2
+
+int oracle_mutant(void) { return ORACLE_MUTANT; }
+
+/* Step 1 alone: q_abs[n,h,j] = sum_d q[n,h,d] W_UK[h,d,j] for n < N rows. */
+static void absorb_row(const float* qh, const float* wuk_h, int dq, int r, double* qa) {
+  for (int j = 0; j < r; ++j) qa[j] = 0.0;
+  for (int d = 0; d < dq; ++d) {
+    const double qd = (double)qh[d];
+    for (int j = 0; j < r; ++j) {
+#if ORACLE_MUTANT == 3
+      /* planted mistake: W_UK read as [H, r, d_q] */
+      qa[j] += qd * (double)wuk_h[(int64_t)j * dq + d];
+#else
+      qa[j] += qd * (double)wuk_h[(int64_t)d * r + j];
+#endif
+    }
+  }
+}
+
+int oracle_qabs(const float* q, const float* w_uk, int64_t N, int H, int dq, int r,
+                double* q_abs, int nthreads) {
+  if (!q || !w_uk || !q_abs || N < 0 || H <= 0 || dq <= 0 || r <= 0) return ORACLE_EINVAL;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+  for (int64_t n = 0; n < N; ++n)
+    for (int h = 0; h < H; ++h)
+      absorb_row(q + (n * H + h) * dq, w_uk + (int64_t)h * dq * r, dq, r,
+                 q_abs + (n * H + h) * r);
+  return ORACLE_OK;
+}
+
+/*
+ * One query row, all heads.  keys: nkeys latent rows of length r (row-major),
+ * qrow: [H, dq], grow: [H*dv] gate logits, out: [H*dv].
+ * scratch: r (qa) + r (ol) + nkeys (scores) doubles.
+ */
+static void attend_row(const float* qrow, const float* keys, int64_t nkeys, const float* grow,
+                       const float* w_uk, const float* w_uv, int H, int dq, int dv, int r,
+                       double scale, double* scratch, double* out) {
+  double* qa = scratch;
+  double* ol = scratch + r;
+  double* s = scratch + 2 * (int64_t)r;
+  for (int h = 0; h < H; ++h) {
+    /* step 1: absorb W_UK into the query */
+    absorb_row(qrow + (int64_t)h * dq, w_uk + (int64_t)h * dq * r, dq, r, qa);
+
+    /* step 2: latent scores against every visible key */
+    for (int64_t u = 0; u < nkeys; ++u) {
+      const float* cu = keys + u * r;
+      double acc = 0.0;
+#pragma omp simd reduction(+ : acc)
+      for (int j = 0; j < r; ++j) acc += qa[j] * (double)cu[j];
+#if ORACLE_MUTANT == 7
+      s[u] = acc; /* planted mistake: scale ignored */
+#else
+      s[u] = scale * acc;
+#endif
+    }
+
+    /* step 3: softmax over the visible keys (max-subtracted) */
+    double m = -INFINITY;
+    for (int64_t u = 0; u < nkeys; ++u) m = s[u] > m ? s[u] : m;
+    double sum = 0.0;
+    for (int64_t u = 0; u < nkeys; ++u) {
+#if ORACLE_MUTANT == 2
+      s[u] = exp(m - s[u]); /* planted mistake: sign of the exponent */
+#else
+      s[u] = exp(s[u] - m);
+#endif
+      sum += s[u];
+    }
+#if ORACLE_MUTANT != 8
+    for (int64_t u = 0; u < nkeys; ++u) s[u] /= sum;
+#endif
+    /* (mutant 8 plants a missing normalisation) */
+
+    /* step 4: weighted sum in the latent space */
+    for (int j = 0; j < r; ++j) ol[j] = 0.0;
+    for (int64_t u = 0; u < nkeys; ++u) {
+#if ORACLE_MUTANT == 9
+      const float* cu = keys + (nkeys - 1) * r; /* planted mistake: the query's own row */
+#else
+      const float* cu = keys + u * r;
+#endif
+      const double w = s[u];
+      for (int j = 0; j < r; ++j) ol[j] += w * (double)cu[j];
+    }
+
+    /* step 5: up-project with W_UV[h]^T, step 6: sigmoid gate, head-major flatten */
+    const float* wuv_h = w_uv + (int64_t)h * dv * r;
+    for (int v = 0; v < dv; ++v) {
+      double o = 0.0;
+#pragma omp simd reduction(+ : o)
+      for (int j = 0; j < r; ++j) {
+#if ORACLE_MUTANT == 4
+        o += ol[j] * (double)wuv_h[(int64_t)j * dv + v]; /* planted: W_UV read as [H, r, d_v] */
+#else
+        o += ol[j] * (double)wuv_h[(int64_t)v * r + j];
+#endif
+      }
+#if ORACLE_MUTANT == 5
+      const int64_t col = (int64_t)v * H + h; /* planted mistake: value-major flatten */
+#else
+      const int64_t col = (int64_t)h * dv + v;
+#endif
+#if ORACLE_MUTANT == 6
+      out[col] = o / (1.0 + exp((double)grow[col])); /* planted: sigmoid(-g) */
+#else
+      out[col] = o / (1.0 + exp(-(double)grow[col]));
+#endif
+    }
+  }
+}
+
+/*
+ * Prefill.  q [B,T,H,dq], c [B,T,r], w_uk [H,dq,r], w_uv [H,dv,r],
+ * gate [B,T,H*dv].  rows: nrows flattened indices b*T+t (NULL: every row in
+ * order, nrows must be B*T).  out: [nrows, H*dv].
+ */
+int oracle_prefill(const float* q, const float* c, const float* w_uk, const float* w_uv,
+                   const float* gate, int B, int T, int H, int dq, int dv, int r, double scale,
+                   const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+  if (!q || !c || !w_uk || !w_uv || !gate || !out) return ORACLE_EINVAL;
+  if (B <= 0 || T <= 0 || H <= 0 || dq <= 0 || dv <= 0 || r <= 0 || nrows < 0) return ORACLE_EINVAL;
+  if (!rows && nrows != (int64_t)B * T) return ORACLE_EINVAL;
+  if (rows)
+    for (int64_t i = 0; i < nrows; ++i)
+      if (rows[i] < 0 || rows[i] >= (int64_t)B * T) return ORACLE_EINVAL;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  const int64_t scratch_len = 2 * (int64_t)r + T;
+  int err = ORACLE_OK;
+#pragma omp parallel num_threads(nthreads)
+  {
+    double* scratch = (double*)malloc(sizeof(double) * scratch_len);
+    if (!scratch) {
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+    }
+#pragma omp barrier
+    if (err == ORACLE_OK) {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t i = 0; i < nrows; ++i) {
+        const int64_t row = rows ? rows[i] : i;
+        const int64_t b = row / T, t = row % T;
+#if ORACLE_MUTANT == 1
+        const int64_t nkeys = t; /* planted mistake: diagonal excluded */
+#else
+        const int64_t nkeys = t + 1;
+#endif
+        attend_row(q + row * H * dq, c + b * (int64_t)T * r, nkeys, gate + row * H * dv, w_uk,
+                   w_uv, H, dq, dv, r, scale, scratch, out + i * (int64_t)H * dv);
+      }
+    }
+    free(scratch);
+  }
+  return err;
+}
+
+/*
+ * Decode.  q [B,H,dq] (one query per sequence), c_cache [sum_len, r],
+ * cu_seqlens [B+1] exclusive prefix sums with len_i >= 1, gate [B,H*dv].
+ * seqs: nseqs sequence indices (NULL: all B in order).  out: [nseqs, H*dv].
+ */
+int oracle_decode(const float* q, const float* c_cache, const int64_t* cu_seqlens,
+                  const float* w_uk, const float* w_uv, const float* gate, int B, int H, int dq,
+                  int dv, int r, double scale, const int64_t* seqs, int64_t nseqs, double* out,
+                  int nthreads) {
+  if (!q || !c_cache || !cu_seqlens || !w_uk || !w_uv || !gate || !out) return ORACLE_EINVAL;
+  if (B <= 0 || H <= 0 || dq <= 0 || dv <= 0 || r <= 0 || nseqs < 0) return ORACLE_EINVAL;
+  if (!seqs && nseqs != B) return ORACLE_EINVAL;
+  if (cu_seqlens[0] != 0) return ORACLE_EINVAL;
+  int64_t max_len = 0;
+  for (int i = 0; i < B; ++i) {
+    const int64_t len = cu_seqlens[i + 1] - cu_seqlens[i];
+    if (len < 1) return ORACLE_EINVAL;
+    if (len > max_len) max_len = len;
+  }
+  if (seqs)
+    for (int64_t k = 0; k < nseqs; ++k)
+      if (seqs[k] < 0 || seqs[k] >= B) return ORACLE_EINVAL;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  const int64_t scratch_len = 2 * (int64_t)r + max_len;
+  int err = ORACLE_OK;
+#pragma omp parallel num_threads(nthreads)
+  {
+    double* scratch = (double*)malloc(sizeof(double) * scratch_len);
+    if (!scratch) {
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+    }
+#pragma omp barrier
+    if (err == ORACLE_OK) {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t k = 0; k < nseqs; ++k) {
+        const int64_t i = seqs ? seqs[k] : k;
+        const int64_t start = cu_seqlens[i];
+#if ORACLE_MUTANT == 10
+        const int64_t len = cu_seqlens[i + 1] - start - 1; /* planted: newest row dropped */
+#else
+        const int64_t len = cu_seqlens[i + 1] - start;
+#endif
+        attend_row(q + i * (int64_t)H * dq, c_cache + start * r, len, gate + i * (int64_t)H * dv,
+                   w_uk, w_uv, H, dq, dv, r, scale, scratch, out + k * (int64_t)H * dv);
+      }
+    }
+    free(scratch);
+  }
+  return err;
+}
+
+/*
+ * The decompressed ("standard") route, written separately: per head,
+ * K_h = c W_UK[h]^T  [T, dq] and V_h = c W_UV[h]^T  [T, dv], then causal
+ * softmax(scale * q_h K_h^T) V_h and the same gate.  By associativity this
+ * equals the absorbed route ([MLA] section 矩阵吸收的核心思路 and the warning
+ * box on reordering the W_UV product).  All rows, out [B,T,H*dv].
+ */
+int oracle_prefill_decompressed(const float* q, const float* c, const float* w_uk,
+                                const float* w_uv, const float* gate, int B, int T, int H, int dq,
+                                int dv, int r, double scale, double* out, int nthreads) {
+  if (!q || !c || !w_uk || !w_uv || !gate || !out) return ORACLE_EINVAL;
+  if (B <= 0 || T <= 0 || H <= 0 || dq <= 0 || dv <= 0 || r <= 0) return ORACLE_EINVAL;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  int err = ORACLE_OK;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(nthreads)
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < H; ++h) {
+      double* K = (double*)malloc(sizeof(double) * (size_t)T * dq);
+      double* V = (double*)malloc(sizeof(double) * (size_t)T * dv);
+      double* p = (double*)malloc(sizeof(double) * (size_t)T);
+      if (!K || !V || !p) {
+#pragma omp atomic write
+        err = ORACLE_ENOMEM;
+      } else {
+        const float* cb = c + (int64_t)b * T * r;
+        const float* wk = w_uk + (int64_t)h * dq * r;
+        const float* wv = w_uv + (int64_t)h * dv * r;
+        for (int u = 0; u < T; ++u) {
+          for (int d = 0; d < dq; ++d) {
+            double a = 0.0;
+            for (int j = 0; j < r; ++j) a += (double)cb[(int64_t)u * r + j] * (double)wk[(int64_t)d * r + j];
+            K[(int64_t)u * dq + d] = a;
+          }
+          for (int v = 0; v < dv; ++v) {
+            double a = 0.0;
+            for (int j = 0; j < r; ++j) a += (double)cb[(int64_t)u * r + j] * (double)wv[(int64_t)v * r + j];
+            V[(int64_t)u * dv + v] = a;
+          }
+        }
+        for (int t = 0; t < T; ++t) {
+          const float* qv = q + (((int64_t)b * T + t) * H + h) * dq;
+          double mx = -INFINITY;
+          for (int u = 0; u <= t; ++u) {
+            double a = 0.0;
+            for (int d = 0; d < dq; ++d) a += (double)qv[d] * K[(int64_t)u * dq + d];
+            p[u] = scale * a;
+            if (p[u] > mx) mx = p[u];
+          }
+          double sum = 0.0;
+          for (int u = 0; u <= t; ++u) {
+            p[u] = exp(p[u] - mx);
+            sum += p[u];
+          }
+          for (int v = 0; v < dv; ++v) {
+            double a = 0.0;
+            for (int u = 0; u <= t; ++u) a += p[u] * V[(int64_t)u * dv + v];
+            const int64_t col = (((int64_t)b * T + t) * H + h) * dv + v;
+            out[col] = (a / sum) / (1.0 + exp(-(double)gate[col]));
+          }
+        }
+      }
+      free(K);
+      free(V);
+      free(p);
+    }
+  }
+  return err;
+}
+
+/*
+ * Step 3 exposed for the structural pins: the attention weights
+ * attn[b,h,t,u] (zero for u > t), shape [B,H,T,T].  Same code path as
+ * oracle_prefill's steps 1-3.
+ */
+int oracle_prefill_attn(const float* q, const float* c, const float* w_uk, int B, int T, int H,
+                        int dq, int r, double scale, double* attn) {
+  if (!q || !c || !w_uk || !attn) return ORACLE_EINVAL;
+  if (B <= 0 || T <= 0 || H <= 0 || dq <= 0 || r <= 0) return ORACLE_EINVAL;
+  double* qa = (double*)malloc(sizeof(double) * (size_t)r);
+  double* s = (double*)malloc(sizeof(double) * (size_t)T);
+  if (!qa || !s) {
+    free(qa);
+    free(s);
+    return ORACLE_ENOMEM;
+  }
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h)
+      for (int t = 0; t < T; ++t) {
+        absorb_row(q + (((int64_t)b * T + t) * H + h) * dq, w_uk + (int64_t)h * dq * r, dq, r, qa);
+#if ORACLE_MUTANT == 1
+        const int nkeys = t;
+#else
+        const int nkeys = t + 1;
+#endif
+        double m = -INFINITY;
+        for (int u = 0; u < nkeys; ++u) {
+          const float* cu = c + ((int64_t)b * T + u) * r;
+          double acc = 0.0;
+          for (int j = 0; j < r; ++j) acc += qa[j] * (double)cu[j];
+          s[u] = scale * acc;
+          if (s[u] > m) m = s[u];
+        }
+        double sum = 0.0;
+        for (int u = 0; u < nkeys; ++u) {
+#if ORACLE_MUTANT == 2
+          s[u] = exp(m - s[u]);
+#else
+          s[u] = exp(s[u] - m);
+#endif
+          sum += s[u];
+        }
+        double* row = attn + (((int64_t)b * H + h) * T + t) * T;
+        for (int u = 0; u < T; ++u) row[u] = 0.0;
+        for (int u = 0; u < nkeys; ++u) {
+#if ORACLE_MUTANT == 8
+          row[u] = s[u];
+#else
+          row[u] = s[u] / sum;
+#endif
+        }
+      }
+  free(qa);
+  free(s);
+  return ORACLE_OK;
+}

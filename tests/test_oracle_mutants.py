@@ -1,0 +1,34 @@
+"""Each plausible mistake planted in the oracle (a dropped diagonal, a sign,
+a transposed weight, the flatten order, the gate sign, a missing scale or
+normalisation, the wrong key row, an off-by-one decode cache) must be caught
+by at least one pin.  Mutants are compiled on the CPU into a scratch dir."""
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {
+    1: "causal mask drops the diagonal",
+    2: "softmax exponent sign flipped",
+    3: "W_UK read transposed",
+    4: "W_UV read transposed",
+    5: "value-major flatten of heads",
+    6: "sigmoid of the negated gate",
+    7: "softmax scale ignored",
+    8: "softmax not normalised",
+    9: "weighted sum uses the query's own latent row",
+    10: "decode drops the newest cached row",
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=lambda m: f"m{m}")
+def test_mutant_is_caught(mutant, tmp_path):
+    o = oracle.build_mutant(mutant, str(tmp_path))
+    assert o.mutant == mutant
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, ValueError) as e:
+            caught.append(f"{pin.__name__}: {str(e)[:80]}")
+    assert caught, f"mutant {mutant} ({MUTANTS[mutant]}) passed every pin"
