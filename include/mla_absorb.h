@@ -1,0 +1,127 @@
+/*
+ * mla_absorb.h - C ABI of the MI355X (gfx950) library for the matrix-absorbed,
+ * NoPE Gated MLA attention layer.
+ *
+ * The layer (page "Gated MLA（矩阵吸收版）" of the K3 notes: sections 低秩压缩,
+ * 矩阵吸收的核心思路, 完整计算流（四步） steps 2-4 and the 代码对照 listing;
+ * shapes from page "符号表", section MLA 变量) computes for every batch b,
+ * head h and query position t:
+ *
+ *   q_abs[b,t,h,:] = q[b,t,h,:] . W_UK[h]                 (absorb W_UK, [r])
+ *   score[b,h,t,s] = scale * q_abs[b,t,h,:] . c[b,s,:]     (latent score)
+ *   attn           = softmax over s of score, keys s > t masked (causal)
+ *   o_lat[b,h,t,:] = sum_s attn[b,h,t,s] * c[b,s,:]        (latent weighted sum, [r])
+ *   o[b,h,t,v]     = o_lat[b,h,t,:] . W_UV[h,v,:]           (W_UV^T up-projection)
+ *   out[b,t,h*d_v+v] = sigmoid(gate[b,t,h*d_v+v]) * o[b,h,t,v]
+ *
+ * The pages print no softmax scale, so it is an explicit argument.  The
+ * output is the gated, head-major flattened tensor before the output
+ * projection.  Decode evaluates the same definition for one new query per
+ * sequence against a packed latent cache (the pages cache only c; the decode
+ * path itself is not written on the pages).
+ *
+ * Conventions for every entry point:
+ *  - All tensors are device pointers to row-major contiguous storage, all of
+ *    the same element type (dtype), 16-byte aligned.  cu_seqlens is int32.
+ *  - The caller owns every buffer.  The library never allocates, frees or
+ *    synchronises; scratch memory comes from the caller's workspace, whose
+ *    size the *_workspace_size functions return.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL means the null
+ *    stream) and the call returns without waiting.  MLA_OK means enqueued.
+ *  - Arguments are checked on the host before anything is launched:
+ *    MLA_ERR_INVALID_ARG (null or misaligned pointer, non-positive size,
+ *    non-finite scale), MLA_ERR_UNSUPPORTED ((d_q, d_v, r) outside the
+ *    compiled set for bf16, or sizes beyond the int32 index range),
+ *    MLA_ERR_WORKSPACE (workspace smaller than required).  A launch failure
+ *    reported by the HIP runtime returns MLA_ERR_HIP.
+ *  - Inputs are read only.  `out` must not alias any input or the workspace.
+ *  - Calls may run concurrently on different streams with distinct
+ *    workspaces; the library holds no mutable global state.
+ *
+ * Supported element types: MLA_DTYPE_BF16 (bf16 storage, fp32 accumulation,
+ * MFMA kernels; (d_q, d_v, r) in {(16,16,32), (64,64,256), (128,128,512)}) and
+ * MLA_DTYPE_F32 (fp32 throughout; any d_q, d_v <= 256 and r <= 1024).
+ */
+#ifndef MLA_ABSORB_H
+#define MLA_ABSORB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,
+  MLA_ERR_UNSUPPORTED = 2,
+  MLA_ERR_WORKSPACE = 3,
+  MLA_ERR_HIP = 4
+} mla_status;
+
+typedef enum { MLA_DTYPE_F32 = 0, MLA_DTYPE_BF16 = 1 } mla_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mla_status_string(mla_status s);
+
+/*
+ * Bytes of workspace mla_absorb_prefill needs for these sizes (0 is a valid
+ * answer).  Returns (size_t)-1 for invalid sizes.
+ */
+size_t mla_absorb_prefill_workspace_size(int B, int T, int H, int d_q, int r, mla_dtype dtype);
+
+/*
+ * Prefill: causal attention of every position of B sequences of length T.
+ *   q     [B, T, H, d_q]   queries (output of the query low-rank path)
+ *   c     [B, T, r]        KV latent, shared by all heads
+ *   w_uk  [H, d_q, r]      key decompression W_UK (the first H*d_q rows of
+ *                          kv_up.weight viewed as [H, d_q, r])
+ *   w_uv  [H, d_v, r]      value decompression W_UV (the following H*d_v rows)
+ *   gate  [B, T, H*d_v]    gate pre-activations (before the sigmoid)
+ *   out   [B, T, H*d_v]    gated output, column h*d_v + v
+ *   scale                  softmax scale applied to q_abs . c
+ */
+mla_status mla_absorb_prefill(const void* q, const void* c, const void* w_uk, const void* w_uv,
+                              const void* gate, void* out, int B, int T, int H, int d_q, int d_v,
+                              int r, float scale, mla_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace mla_absorb_decode needs.  num_splits <= 0 selects the
+ * library default (the device's compute-unit count, which queries the
+ * current device).  Returns (size_t)-1 for invalid sizes.
+ */
+size_t mla_absorb_decode_workspace_size(int B, int H, int d_q, int r, int num_splits,
+                                        mla_dtype dtype);
+
+/*
+ * Decode: one new query per sequence against a packed latent cache.
+ *   q          [B, H, d_q]      the query of each sequence, at position len_i - 1
+ *   c_cache    [total_len, r]   latents of all sequences back to back; sequence
+ *                               i owns rows cu_seqlens[i] .. cu_seqlens[i+1]-1,
+ *                               the last of which is the new token's own latent
+ *   cu_seqlens [B + 1] int32    device array, exclusive prefix sums of the
+ *                               lengths: cu_seqlens[0] = 0,
+ *                               cu_seqlens[B] = total_len, every length >= 1
+ *                               (a precondition; it is not read on the host)
+ *   w_uk, w_uv                  as for prefill
+ *   gate       [B, H*d_v]       gate pre-activations
+ *   out        [B, H*d_v]       gated output
+ *   total_len                   rows of c_cache (host value); every cache
+ *                               access is clamped below it
+ *   num_splits                  workgroups sharing the cache rows evenly
+ *                               (<= 0: library default); any value gives the
+ *                               same result up to rounding order
+ */
+mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* cu_seqlens,
+                             const void* w_uk, const void* w_uv, const void* gate, void* out,
+                             int B, int H, int d_q, int d_v, int r, int64_t total_len, float scale,
+                             int num_splits, mla_dtype dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_ABSORB_H */

@@ -1,0 +1,171 @@
+"""Python binding of the MI355X absorbed Gated MLA library (libmla_absorb.so).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI declared in include/mla_absorb.h.  Tensors are PyTorch
+tensors on the GPU (PyTorch provides device memory and streams); the binding
+checks shapes, dtypes and contiguity, allocates the output and workspace when
+the caller does not pass them, and calls the C entry point on the current
+stream.  There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes as ct
+import os
+
+__all__ = [
+    "LIB_PATH", "MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED", "MLA_ERR_WORKSPACE",
+    "MLA_ERR_HIP", "DTYPE_F32", "DTYPE_BF16", "MLAError", "lib", "status_string",
+    "prefill_workspace_size", "decode_workspace_size", "mla_absorb_prefill", "mla_absorb_decode",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_absorb.so")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+EXPORTS = (
+    "mla_status_string",
+    "mla_absorb_prefill_workspace_size",
+    "mla_absorb_prefill",
+    "mla_absorb_decode_workspace_size",
+    "mla_absorb_decode",
+)
+
+_lib = None
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def lib() -> ct.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with rank_latent_causal_amd.build.build()")
+        L = ct.CDLL(LIB_PATH)
+        vp, sz, I, I64, F = ct.c_void_p, ct.c_size_t, ct.c_int, ct.c_int64, ct.c_float
+        L.mla_status_string.argtypes = [I]
+        L.mla_status_string.restype = ct.c_char_p
+        L.mla_absorb_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
+        L.mla_absorb_prefill_workspace_size.restype = sz
+        L.mla_absorb_prefill.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, vp, sz, vp]
+        L.mla_absorb_prefill.restype = I
+        L.mla_absorb_decode_workspace_size.argtypes = [I, I, I, I, I, I]
+        L.mla_absorb_decode_workspace_size.restype = sz
+        L.mla_absorb_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, I64, F, I, I, vp, sz, vp]
+        L.mla_absorb_decode.restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mla_status_string(int(status)).decode()
+
+
+_BAD = ct.c_size_t(-1).value
+
+
+def prefill_workspace_size(B: int, T: int, H: int, d_q: int, r: int, dtype: int) -> int:
+    n = lib().mla_absorb_prefill_workspace_size(B, T, H, d_q, r, dtype)
+    if n == _BAD:
+        raise MLAError(MLA_ERR_INVALID_ARG, "mla_absorb_prefill_workspace_size")
+    return n
+
+
+def decode_workspace_size(B: int, H: int, d_q: int, r: int, num_splits: int, dtype: int) -> int:
+    n = lib().mla_absorb_decode_workspace_size(B, H, d_q, r, num_splits, dtype)
+    if n == _BAD:
+        raise MLAError(MLA_ERR_INVALID_ARG, "mla_absorb_decode_workspace_size")
+    return n
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(t, shape, dtype, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: must be a contiguous GPU tensor")
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ct.c_void_p(stream.cuda_stream)
+
+
+def mla_absorb_prefill(q, c, w_uk, w_uv, gate, scale: float, out=None, workspace=None, stream=None):
+    """Prefill of the absorbed Gated MLA layer.  q [B,T,H,d_q], c [B,T,r],
+    w_uk [H,d_q,r], w_uv [H,d_v,r], gate [B,T,H*d_v] -> out [B,T,H*d_v]."""
+    torch = _torch()
+    B, T, H, dq = q.shape
+    r = c.shape[-1]
+    dv = w_uv.shape[1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    for t, shp, n in ((q, (B, T, H, dq), "q"), (c, (B, T, r), "c"), (w_uk, (H, dq, r), "w_uk"),
+                      (w_uv, (H, dv, r), "w_uv"), (gate, (B, T, H * dv), "gate")):
+        _check(t, shp, dt, n)
+    if out is None:
+        out = torch.empty((B, T, H * dv), dtype=dt, device=q.device)
+    _check(out, (B, T, H * dv), dt, "out")
+    need = prefill_workspace_size(B, T, H, dq, r, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().mla_absorb_prefill(q.data_ptr(), c.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+                                  gate.data_ptr(), out.data_ptr(), B, T, H, dq, dv, r, float(scale),
+                                  code, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_absorb_prefill")
+    return out
+
+
+def mla_absorb_decode(q, c_cache, cu_seqlens, w_uk, w_uv, gate, scale: float, num_splits: int = 0,
+                      out=None, workspace=None, stream=None):
+    """Decode against a packed latent cache.  q [B,H,d_q], c_cache [N,r],
+    cu_seqlens [B+1] int32 (device), w_uk [H,d_q,r], w_uv [H,d_v,r],
+    gate [B,H*d_v] -> out [B,H*d_v]."""
+    torch = _torch()
+    B, H, dq = q.shape
+    N, r = c_cache.shape
+    dv = w_uv.shape[1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    for t, shp, n in ((q, (B, H, dq), "q"), (c_cache, (N, r), "c_cache"), (w_uk, (H, dq, r), "w_uk"),
+                      (w_uv, (H, dv, r), "w_uv"), (gate, (B, H * dv), "gate")):
+        _check(t, shp, dt, n)
+    _check(cu_seqlens, (B + 1,), torch.int32, "cu_seqlens")
+    if out is None:
+        out = torch.empty((B, H * dv), dtype=dt, device=q.device)
+    _check(out, (B, H * dv), dt, "out")
+    need = decode_workspace_size(B, H, dq, r, num_splits, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().mla_absorb_decode(q.data_ptr(), c_cache.data_ptr(), cu_seqlens.data_ptr(), w_uk.data_ptr(),
+                                 w_uv.data_ptr(), gate.data_ptr(), out.data_ptr(), B, H, dq, dv, r, N,
+                                 float(scale), int(num_splits), code, workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_absorb_decode")
+    return out

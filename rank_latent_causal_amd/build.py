@@ -1,0 +1,40 @@
+"""Compile the gfx950 HIP library (libmla_absorb.so) in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "csrc", "mla_absorb.hip")
+HEADERS = [os.path.join(HERE, "csrc", f) for f in os.listdir(os.path.join(HERE, "csrc")) if f.endswith(".h")]
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libmla_absorb.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(out_path: str = LIB, verbose: bool = False) -> str:
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           # packed fp32 VALU forms are kept out of every kernel
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           f"-I{INCLUDE}", SRC, "-o", out_path + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "not a recognized feature" not in l)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + msgs)
+    if verbose and msgs.strip():
+        print(msgs)
+    os.replace(out_path + ".tmp", out_path)
+    return out_path
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,227 @@
+// Per-wave latent-attention core shared by the prefill and decode kernels.
+//
+// A wave owns 16 query rows (the N index of every MFMA, lane l serves row
+// l % 16) and the full r-wide latent accumulator O^T [r x 16] in VGPRs.  One
+// 32-key latent tile held in LDS (row-major, chunk-swizzled) is consumed as
+//   S^T = c_tile . q_abs^T              (A = c rows via ds_read_b128)
+//   P   = exp2(S - m), online softmax   (per-lane statistics)
+//   O^T += c_tile^T . P^T               (A = c columns via ds_read_b64_tr_b16)
+// Because the score uses the same latent rows as the values (K = V = c),
+// a single LDS copy feeds both products.
+//
+// k-slot bookkeeping: lane (l16 = l % 16, kq = l / 16) of a C fragment holds
+// rows 4 kq + e.  Two 16-row C fragments (rows 0-15 and 16-31) therefore give
+// the lane the 8 values a B operand needs in k slots {4kq+e} and {16+4kq+e};
+// the A operands are read with that same key order, so C fragments are fed
+// back as B operands without any lane shuffle.
+#pragma once
+
+#include "common.h"
+
+namespace mla {
+
+template <int R>
+struct LatentTile {
+  static constexpr int KT = 32;             // keys per tile
+  static constexpr int BYTES = KT * R * 2;  // bf16 row-major tile
+  static constexpr int NKK = R / 32;        // score k-steps (32 latent dims)
+  static constexpr int NJT = R / 16;        // value tiles (16 latent dims)
+  static constexpr int COPIES = KT * (R / 8) / 64;  // 1 KiB wave copies per tile
+};
+
+template <int R>
+constexpr int copies_per_wave(int nwaves) {
+  return (LatentTile<R>::COPIES + nwaves - 1) / nwaves;
+}
+
+// Copies latent rows [row0, row0 + 32) into a swizzled LDS tile with raw
+// buffer loads.  The per-lane source offsets do not depend on the tile and
+// are computed once; rows at or past row_end read as zeros (their scores are
+// masked).  Copy qi (1 KiB of LDS) is issued by wave qi % NW, so each wave
+// issues either copies_per_wave(NW) copies or none.
+template <int R, int NW>
+struct TileCopier {
+  static constexpr int COPIES = LatentTile<R>::COPIES;
+  static constexpr int CPW = copies_per_wave<R>(NW);
+  unsigned voff[CPW];
+  int w;
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+    constexpr int CPR = R / 8;
+    w = wave;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int P = (wave + NW * c) * 64 + lane;
+      const int s = P / CPR;
+      const int L = (P % CPR) ^ chunk_swizzle<R>(s);
+      voff[c] = (unsigned)((s * R + L * 8) * 2);
+    }
+  }
+
+  __device__ __forceinline__ void issue(const bf16* __restrict__ base, long long row0, long long row_end,
+                                        MLA_LDS char* stage) const {
+    const long long rows = row_end - row0 < LatentTile<R>::KT ? row_end - row0 : LatentTile<R>::KT;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (size_t)row0 * R, (unsigned)(rows * R * 2));
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int qi = w + NW * c;
+      if (qi < COPIES) buf2lds16(rs, voff[c], stage + qi * 1024);
+    }
+  }
+};
+
+// q_abs^T for 16 rows: qT[kk] is the score B operand for latent dims
+// [32kk, 32kk+32) (slot p <-> dim 32kk + 8kq + p), already multiplied by
+// qscale.  qrow points at this lane's query row (DQ values, 16-byte aligned);
+// wkT at W_UK^T[h] ([R, DQ]).
+template <int DQ, int R>
+__device__ __forceinline__ void absorb_rows(const bf16* __restrict__ qrow, const bf16* __restrict__ wkT,
+                                            float qscale, int l16, int kq, bf16x8 (&qT)[R / 32]) {
+  constexpr int NKQ = (DQ + 31) / 32;
+  bf16x8 qb[NKQ];
+#pragma unroll
+  for (int k = 0; k < NKQ; ++k)
+    qb[k] = (32 * k + 8 * kq < DQ) ? *(const bf16x8*)(qrow + 32 * k + 8 * kq) : bf16x8{};
+#pragma unroll
+  for (int kk = 0; kk < R / 32; ++kk) {
+    f32x4 acc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // A row rho loads latent dim 32kk + 8(rho/4) + 4u + rho%4, so C row
+      // 4kq + e of this fragment is dim 32kk + 8kq + 4u + e
+      const int j = 32 * kk + 8 * (l16 >> 2) + 4 * u + (l16 & 3);
+      const bf16* wrow = wkT + (size_t)j * DQ;
+      acc[u] = f32x4{};
+#pragma unroll
+      for (int k = 0; k < NKQ; ++k) {
+        const bf16x8 av = (32 * k + 8 * kq < DQ) ? *(const bf16x8*)(wrow + 32 * k + 8 * kq) : bf16x8{};
+        acc[u] = mfma16(av, qb[k], acc[u]);
+      }
+    }
+    qT[kk] = pack44(acc[0], acc[1], qscale);
+  }
+}
+
+template <int R>
+struct WaveAttn {
+  static constexpr int NKK = R / 32;
+  static constexpr int NJT = R / 16;
+  // The swizzle only permutes the low 4 bits of a chunk index, so operand
+  // addresses are a per-lane base (one per value of those bits) plus an
+  // immediate multiple of 256 bytes.
+  static constexpr int NQB = NKK < 4 ? NKK : 4;
+  static constexpr int NTB = NJT < 8 ? NJT : 8;
+  static constexpr int ROWB = R * 2;
+  bf16x8 qT[NKK];
+  f32x4 oT[NJT];
+  float m_run, l_run;
+  int qk_base[NQB];  // score A operand: row l16, chunk 4u + kq
+  int tr_base[NTB];  // value A operand: row 4kq + l16/4, chunk 2u + (l16%4)/2, half l16%2
+
+  __device__ __forceinline__ void init_addressing(int l16, int kq) {
+#pragma unroll
+    for (int u = 0; u < NQB; ++u) qk_base[u] = tile_off<R>(l16, 4 * u + kq);
+    const int r = 4 * kq + (l16 >> 2), q = l16 & 3;
+#pragma unroll
+    for (int u = 0; u < NTB; ++u) tr_base[u] = tile_off<R>(r, 2 * u + (q >> 1)) + (q & 1) * 8;
+  }
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int t = 0; t < NJT; ++t) oT[t] = f32x4{};
+    m_run = -INFINITY;
+    l_run = 0.0f;
+  }
+
+  // S^T fragments for keys [0,16) (s0) and [16,32) (s1) of the tile.
+  __device__ __forceinline__ void scores(const MLA_LDS char* tile, f32x4& s0, f32x4& s1) const {
+    s0 = f32x4{};
+    s1 = f32x4{};
+    constexpr int CH = NKK < 4 ? NKK : 4;  // bounds the operand reads in flight
+#pragma unroll
+    for (int k0 = 0; k0 < NKK; k0 += CH) {
+#pragma unroll
+      for (int kk = k0; kk < k0 + CH; ++kk) {
+        const MLA_LDS char* p = tile + qk_base[kk % NQB] + (kk / NQB) * 256;
+        s0 = mfma16(lds_read_b128(p), qT[kk], s0);
+        s1 = mfma16(lds_read_b128(p + 16 * ROWB), qT[kk], s1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Online softmax over one tile's (already masked) log2-domain scores and
+  // the value accumulation.  The reference max only moves when a score
+  // exceeds it by more than 8, so the O^T rescale is rare and P <= 2^8.
+  __device__ __forceinline__ void update(const MLA_LDS char* tile, const f32x4& s0, const f32x4& s1) {
+    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    mx = col_max(mx);
+    const bool need = mx > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < NJT; ++t) oT[t] *= alpha;
+      m_run = m_new;
+    }
+    f32x4 p0, p1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p0[e] = fast_exp2(s0[e] - m_run);
+      p1[e] = fast_exp2(s1[e] - m_run);
+    }
+    l_run += (p0[0] + p0[1]) + (p0[2] + p0[3]) + (p1[0] + p1[1]) + (p1[2] + p1[3]);
+    const bf16x8 pB = pack44(p0, p1, 1.0f);
+
+    // value operand: lane i of 16-lane group kq takes latent dim 16t + i and
+    // keys {4kq+e} (lo) / {16+4kq+e} (hi); its tr16 source chunk is key row
+    // 4kq + i/4 (+16), dims 16t + 4(i%4) .. +3.
+    constexpr int CH = NJT < 8 ? NJT : 8;
+#pragma unroll
+    for (int t0 = 0; t0 < NJT; t0 += CH) {
+#pragma unroll
+      for (int t = t0; t < t0 + CH; ++t) {
+        const MLA_LDS char* p = tile + tr_base[t % NTB] + (t / NTB) * 256;
+        const bf16x4 lo = lds_read_tr16(p);
+        const bf16x4 hi = lds_read_tr16(p + 16 * ROWB);
+        oT[t] = mfma16(cat4(lo, hi), pB, oT[t]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+// Epilogue: o^T = W_UV[h] (O^T / l) for 16 rows, gated and stored.  orow
+// points at this lane's output row segment for head h (DV values) and grow at
+// the matching gate logits; valid = row and head exist.
+template <int DV, int R>
+__device__ __forceinline__ void project_gate_store(const f32x4 (&oT)[R / 16], float inv_l,
+                                                   const bf16* __restrict__ wv, const bf16* __restrict__ grow,
+                                                   bf16* __restrict__ orow, bool valid, int l16, int kq) {
+  bf16x8 ob[R / 32];
+#pragma unroll
+  for (int kk = 0; kk < R / 32; ++kk) ob[kk] = pack44(oT[2 * kk], oT[2 * kk + 1], inv_l);
+#pragma unroll
+  for (int vt = 0; vt < DV / 16; ++vt) {
+    const bf16* wrow = wv + (size_t)(16 * vt + l16) * R + 4 * kq;
+    f32x4 acc = f32x4{};
+#pragma unroll
+    for (int kk = 0; kk < R / 32; ++kk) {
+      const bf16x4 lo = *(const bf16x4*)(wrow + 32 * kk);
+      const bf16x4 hi = *(const bf16x4*)(wrow + 32 * kk + 16);
+      acc = mfma16(cat4(lo, hi), ob[kk], acc);
+    }
+    if (valid) {
+      const int v = 16 * vt + 4 * kq;
+      const bf16x4 gv = *(const bf16x4*)(grow + v);
+      bf16x4 ov;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[e] * sigmoidf_((float)gv[e]));
+      *(bf16x4*)(orow + v) = ov;
+    }
+  }
+}
+
+}  // namespace mla

@@ -1,0 +1,137 @@
+// Device-side building blocks shared by the gfx950 kernels of the absorbed
+// Gated MLA library: vector types, MFMA wrappers, LDS transpose reads, direct
+// global->LDS copies, the latent-tile swizzle and wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// D = A * B + C on a 16x16x32 bf16 MFMA.  Lane l holds A row (l % 16),
+// k = 8 * (l / 16) + 0..7; B column (l % 16) with the same k; C/D column
+// (l % 16), register i at row 4 * (l / 16) + i.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// XOR swizzle of the 16-byte chunks of a latent row held in LDS.  It keeps
+// both access patterns of a 32-row tile free of bank conflicts:
+//  * ds_read_b128 of one chunk from 16 consecutive rows (score operand), and
+//  * ds_read_b64_tr_b16 of 8 consecutive rows x 2 chunks per 32 lanes
+//    (value operand, both 8-byte halves of each chunk).
+template <int R>
+__device__ __host__ __forceinline__ constexpr int chunk_swizzle(int s) {
+  if constexpr (R / 8 >= 16) {
+    return ((s & 7) << 1) | ((s >> 3) & 1);
+  } else if constexpr (R / 8 == 4) {
+    return (((s >> 2) & 1) << 1) | ((s >> 3) & 1);
+  } else {
+    return 0;
+  }
+}
+
+// Byte offset of (row s, logical 16-byte chunk L) in a swizzled tile.
+template <int R>
+__device__ __forceinline__ int tile_off(int s, int L) {
+  return s * (R * 2) + ((L ^ chunk_swizzle<R>(s)) << 4);
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const MLA_LDS char* p) {
+  return *(const MLA_LDS bf16x8*)p;
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group the 16 lanes' 8-byte chunks
+// form a 4 x 16 matrix (lane 4e + q supplies row e, columns 4q..4q+3) and
+// lane i receives column i (four rows).
+__device__ __forceinline__ bf16x4 lds_read_tr16(const MLA_LDS char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_LDS bf16x4*)p);
+}
+
+__device__ __forceinline__ bf16x8 cat4(const bf16x4& lo, const bf16x4& hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Direct 16-byte global -> LDS copy: lane l's 16 bytes land at lds_base + 16*l
+// (lds_base must be wave-uniform).  Completion is tracked by vmcnt.
+__device__ __forceinline__ void g2lds16(const void* gptr, MLA_LDS char* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (MLA_LDS void*)lds_base, 16, 0, 0);
+}
+
+// Buffer descriptor over `bytes` bytes at `base` (gfx9 raw buffer: stride 0,
+// reads at or past `bytes` return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Direct 16-byte buffer -> LDS copy at byte offset voff: lane l's 16 bytes
+// land at lds_base + 16*l (lds_base wave-uniform); out-of-range lanes write
+// zeros.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, unsigned voff, MLA_LDS char* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MLA_LDS void*)lds_base, 16, (int)voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Value of x from the lane in the other half of the wave (l ^ 32) combined
+// with x itself, via v_permlane32_swap.
+__device__ __forceinline__ float xhalf_max(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+}
+
+// Combine x over the four lanes l, l^16, l^32, l^48 (one MFMA column).
+__device__ __forceinline__ float col_max(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
+  return xhalf_max(x);
+}
+__device__ __forceinline__ float col_sum(float x) {
+  unsigned u = __builtin_bit_cast(unsigned, x);
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+  return xhalf_sum(x);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + fast_exp2(-g * kLog2e)); }
+
+// Two 4-value C fragments (scaled) -> one bf16 MFMA operand (k slots 0-3
+// from lo, 4-7 from hi), round-to-nearest-even.
+__device__ __forceinline__ bf16x8 pack44(const f32x4& lo, const f32x4& hi, float s) {
+  bf16x8 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    r[p] = (bf16)(lo[p] * s);
+    r[p + 4] = (bf16)(hi[p] * s);
+  }
+  return r;
+}
+
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+
+}  // namespace mla

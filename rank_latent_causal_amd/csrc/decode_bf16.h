@@ -1,0 +1,315 @@
+// bf16 decode kernels for the absorbed Gated MLA layer on gfx950: one new
+// query per sequence attends to its whole cached latent (the cache holds only
+// c, page "Gated MLA（矩阵吸收版）", section 低秩压缩 and the KV-cache table of
+// section 形状与参数对比).  The pages stop short of a decode path; this one
+// evaluates the same definition as prefill for the last position.
+//
+//  mla_wuk_transpose    W_UK [H, DQ, R] -> W_UK^T [H, R, DQ] (workspace)
+//  mla_decode_absorb    q_abs[i, h, :] = scale*log2e * q[i, h, :] W_UK[h]
+//  mla_decode_split     the packed cache rows are cut into G equal ranges, one
+//                       per workgroup; each range is streamed from HBM into
+//                       LDS once and scored against all H heads (heads are the
+//                       MFMA columns, 16 per wave, up to 8 waves).  Every
+//                       sequence piece in a range leaves an unnormalised
+//                       partial (m, l, O[r]).
+//  mla_decode_merge     per (head, 16 sequences): log-sum-exp merge of the
+//                       partials, then o = o_lat W_UV[h]^T on MFMA, the
+//                       sigmoid gate and the store.
+//
+// Range k covers cache rows [floor(k*N/G), floor((k+1)*N/G)); the partial of
+// sequence i from range k is stored in slot k + i, which is unique because
+// the sequences met by consecutive ranges are consecutive.
+#pragma once
+
+#include "attn_core.h"
+
+namespace mla {
+
+// ----------------------------------------------------------------- W_UK^T
+template <typename T>
+__global__ void __launch_bounds__(256) mla_wuk_transpose(const T* __restrict__ w, T* __restrict__ wt,
+                                                         int H, int DQ, int R) {
+  // one 32 (d) x 32 (j) tile per workgroup: read rows of W_UK[h], write rows of W_UK^T[h]
+  __shared__ T tile[32][33];
+  const int h = blockIdx.z;
+  const int j0 = blockIdx.x * 32, d0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  const T* src = w + (size_t)h * DQ * R;
+  T* dst = wt + (size_t)h * R * DQ;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int d = d0 + ty + 8 * k, j = j0 + tx;
+    if (d < DQ && j < R) tile[ty + 8 * k][tx] = src[(size_t)d * R + j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int j = j0 + ty + 8 * k, d = d0 + tx;
+    if (d < DQ && j < R) dst[(size_t)j * DQ + d] = tile[tx][ty + 8 * k];
+  }
+}
+
+// ----------------------------------------------------------------- absorb
+struct DecodeAbsorbArgs {
+  const bf16* q;     // [B, H, DQ]
+  const bf16* wukT;  // [H, R, DQ]
+  bf16* qabs;        // [B, H, R]
+  int B, H;
+  float qscale;
+};
+
+// Wave (head h, 16 sequences): q_abs^T = W_UK[h]^T q^T, stored row-major
+// [B, H, R] so that the split kernel loads its score B operands with 16-byte
+// reads.
+template <int DQ, int R>
+__global__ void __launch_bounds__(256) mla_decode_absorb(DecodeAbsorbArgs a) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int h = blockIdx.y * 4 + w;
+  if (h >= a.H) return;
+  const int i = blockIdx.x * 16 + l16;
+  const bool ivalid = i < a.B;
+  const int ic = ivalid ? i : a.B - 1;
+  bf16x8 qT[R / 32];
+  absorb_rows<DQ, R>(a.q + ((size_t)ic * a.H + h) * DQ, a.wukT + (size_t)h * R * DQ, a.qscale, l16, kq, qT);
+  if (ivalid) {
+    bf16* dst = a.qabs + ((size_t)ic * a.H + h) * R + 8 * kq;
+#pragma unroll
+    for (int kk = 0; kk < R / 32; ++kk) *(bf16x8*)(dst + 32 * kk) = qT[kk];
+  }
+}
+
+// ----------------------------------------------------------------- split
+struct DecodeSplitArgs {
+  const bf16* qabs;     // [B, H, R]
+  const bf16* cache;    // [N, R]
+  const int* cu;        // [B + 1]
+  float* part_o;        // [(G + B), H, R]
+  float* part_ml;       // [(G + B), H, 2]
+  int B, H, G;
+  long long N;          // cache rows (total_len)
+};
+
+__device__ __forceinline__ long long range_start(long long k, long long N, long long G) {
+  return k * N / G;
+}
+
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeStages = 4;  // 3 tiles in flight cover HBM latency
+
+template <int R>
+__global__ void __launch_bounds__(64 * kDecodeWaves)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+mla_decode_split(DecodeSplitArgs a) {
+  using LT = LatentTile<R>;
+  constexpr int NS = kDecodeStages;
+  constexpr int LPW = copies_per_wave<R>(kDecodeWaves);
+  static_assert(LT::COPIES % kDecodeWaves == 0 || LT::COPIES < kDecodeWaves, "copy split");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * LT::BYTES];
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+
+  const int k = blockIdx.x;
+  const long long lo = range_start(k, a.N, a.G), hi = range_start(k + 1, a.N, a.G);
+  if (lo >= hi) return;  // whole workgroup (the host keeps G <= N)
+  const int ntiles = (int)((hi - lo + LT::KT - 1) / LT::KT);
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int h = 16 * w + l16;
+  const bool compute = 16 * w < a.H;  // wave-uniform
+  const bool hvalid = h < a.H;
+  const int hc = hvalid ? h : a.H - 1;
+
+  // first sequence with rows in [lo, hi): the largest i with cu[i] <= lo
+  int i;
+  {
+    int l = 0, r = a.B - 1;
+    while (l < r) {
+      const int mid = (l + r + 1) >> 1;
+      if ((long long)a.cu[mid] <= lo) l = mid; else r = mid - 1;
+    }
+    i = l;
+  }
+  long long seq_lo = a.cu[i], seq_end = a.cu[i + 1];
+
+  TileCopier<R, kDecodeWaves> copier;
+  copier.init(w, lane);
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < ntiles) copier.issue(a.cache, lo + (long long)p * LT::KT, hi, smem + p * LT::BYTES);
+
+  WaveAttn<R> st;
+  auto load_q = [&](int seq) {
+    const bf16* src = a.qabs + ((size_t)seq * a.H + hc) * R + 8 * kq;
+#pragma unroll
+    for (int kk = 0; kk < R / 32; ++kk) st.qT[kk] = *(const bf16x8*)(src + 32 * kk);
+  };
+  if (compute) load_q(i);
+  st.reset();
+  st.init_addressing(l16, kq);
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int nx = it + NS - 1;
+    if (nx < ntiles) {
+      copier.issue(a.cache, lo + (long long)nx * LT::KT, hi, smem + (nx % NS) * LT::BYTES);
+      wait_vmcnt<(NS - 1) * LPW>();
+    } else if (nx == ntiles) {
+      wait_vmcnt<(NS - 2) * LPW>();
+    } else if (nx == ntiles + 1) {
+      wait_vmcnt<(NS - 3) * LPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    const MLA_LDS char* tile = smem + (it % NS) * LT::BYTES;
+    const long long r0 = lo + (long long)it * LT::KT;
+    const long long r1 = min(r0 + LT::KT, hi);
+
+    // a tile may hold the end of one sequence and the start of the next
+    while (true) {
+      const long long a0 = max(r0, seq_lo);
+      const long long a1 = min(r1, seq_end);
+      if (compute && a0 < a1) {
+        f32x4 sa, sb;
+        st.scores(tile, sa, sb);
+        if (a0 > r0 || a1 < r0 + LT::KT) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const long long ka = r0 + 4 * kq + e, kb = ka + 16;
+            if (ka < a0 || ka >= a1) sa[e] = -INFINITY;
+            if (kb < a0 || kb >= a1) sb[e] = -INFINITY;
+          }
+        }
+        st.update(tile, sa, sb);
+      }
+      // the piece of sequence i inside this range ends in this tile: emit it
+      if (seq_end > r1 && r1 < hi) break;
+      if (compute) {
+        const int slot = k + i;
+        const float l_tot = col_sum(st.l_run);
+        if (hvalid) {
+          // O^T fragment t holds latent dims 16t + 4kq + e
+          float* dst = a.part_o + ((size_t)slot * a.H + h) * R + 4 * kq;
+#pragma unroll
+          for (int t = 0; t < R / 16; ++t) *(f32x4*)(dst + 16 * t) = st.oT[t];
+          if (kq == 0) {
+            a.part_ml[((size_t)slot * a.H + h) * 2 + 0] = st.m_run;
+            a.part_ml[((size_t)slot * a.H + h) * 2 + 1] = l_tot;
+          }
+        }
+      }
+      if (seq_end >= hi || i + 1 >= a.B) break;  // range finished
+      ++i;
+      seq_lo = seq_end;
+      seq_end = a.cu[i + 1];
+      if (compute) load_q(i);
+      st.reset();
+      if (seq_lo >= r1) break;  // the next sequence starts in a later tile
+    }
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------------------------- merge
+struct DecodeMergeArgs {
+  const float* part_o;   // [(G + B), H, R]
+  const float* part_ml;  // [(G + B), H, 2]
+  const int* cu;         // [B + 1]
+  const bf16* wuv;       // [H, DV, R]
+  const bf16* gate;      // [B, H*DV]
+  bf16* out;             // [B, H*DV]
+  int B, H, G;
+  long long N;
+};
+
+// index of the range that holds cache row x (every range is non-empty)
+__device__ __forceinline__ int range_of(long long x, long long N, long long G) {
+  return (int)(((x + 1) * G - 1) / N);
+}
+
+// Workgroup (16 sequences, head h), 4 waves.  Phase 1: wave w merges latent
+// columns [w R/4, (w+1) R/4) of every sequence into LDS (bf16, normalised).
+// Phase 2: wave w computes v-tiles w, w+4, ... of o^T = W_UV[h] o_lat^T.
+template <int DV, int R>
+__global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
+  constexpr int JW = R / 4;   // latent columns merged per wave
+  constexpr int JL = JW / 4;  // per lane (four lanes per sequence)
+  static_assert(JL % 4 == 0 || JL == 2, "merge split");
+  constexpr int JV = JL >= 4 ? JL / 4 : 1;
+  __shared__ __attribute__((aligned(16))) bf16 olat[16][R + 8];
+
+  const int h = blockIdx.y;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int i = blockIdx.x * 16 + l16;
+  const bool ivalid = i < a.B;
+  const int ic = ivalid ? i : a.B - 1;
+
+  {
+    const long long s0 = a.cu[ic], s1 = a.cu[ic + 1];
+    const int k0 = range_of(s0, a.N, a.G), k1 = range_of(s1 - 1, a.N, a.G);
+    float mstar = -INFINITY;
+    for (int k = k0; k <= k1; ++k) mstar = fmaxf(mstar, a.part_ml[((size_t)(k + ic) * a.H + h) * 2]);
+    float L = 0.0f;
+    for (int k = k0; k <= k1; ++k) {
+      const float* ml = a.part_ml + ((size_t)(k + ic) * a.H + h) * 2;
+      L += fast_exp2(ml[0] - mstar) * ml[1];
+    }
+    const float invL = 1.0f / L;
+    const int j0 = w * JW + kq * JL;
+    if constexpr (JL >= 4) {
+      f32x4 acc[JV];
+#pragma unroll
+      for (int u = 0; u < JV; ++u) acc[u] = f32x4{};
+      for (int k = k0; k <= k1; ++k) {
+        const size_t base = (size_t)(k + ic) * a.H + h;
+        const float wk = fast_exp2(a.part_ml[base * 2] - mstar) * invL;
+        const float* src = a.part_o + base * R + j0;
+#pragma unroll
+        for (int u = 0; u < JV; ++u) acc[u] += wk * *(const f32x4*)(src + 4 * u);
+      }
+#pragma unroll
+      for (int u = 0; u < JV; ++u) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[u][e];
+        *(bf16x4*)&olat[l16][j0 + 4 * u] = v;
+      }
+    } else {
+      float acc0 = 0.0f, acc1 = 0.0f;
+      for (int k = k0; k <= k1; ++k) {
+        const size_t base = (size_t)(k + ic) * a.H + h;
+        const float wk = fast_exp2(a.part_ml[base * 2] - mstar) * invL;
+        acc0 += wk * a.part_o[base * R + j0];
+        acc1 += wk * a.part_o[base * R + j0 + 1];
+      }
+      olat[l16][j0] = (bf16)acc0;
+      olat[l16][j0 + 1] = (bf16)acc1;
+    }
+  }
+  __syncthreads();
+
+  // o_lat^T B operand for k-step kk: slot p <-> latent dim 32kk + 8kq + p
+  const bf16* wv = a.wuv + (size_t)h * DV * R;
+  for (int vt = w; vt < DV / 16; vt += 4) {
+    const bf16* wrow = wv + (size_t)(16 * vt + l16) * R + 8 * kq;
+    f32x4 acc = f32x4{};
+#pragma unroll 4
+    for (int kk = 0; kk < R / 32; ++kk) {
+      const bf16x8 av = *(const bf16x8*)(wrow + 32 * kk);
+      const bf16x8 bv = *(const bf16x8*)&olat[l16][32 * kk + 8 * kq];
+      acc = mfma16(av, bv, acc);
+    }
+    if (ivalid) {
+      const size_t orow = (size_t)i * a.H * DV + (size_t)h * DV;
+      const int v = 16 * vt + 4 * kq;
+      const bf16x4 gv = *(const bf16x4*)(a.gate + orow + v);
+      bf16x4 ov;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[e] * sigmoidf_((float)gv[e]));
+      *(bf16x4*)(a.out + orow + v) = ov;
+    }
+  }
+}
+
+}  // namespace mla

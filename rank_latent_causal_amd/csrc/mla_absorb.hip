@@ -1,0 +1,228 @@
+// Host side of the MI355X absorbed Gated MLA library: argument checks,
+// workspace carving and kernel launches behind the C ABI of mla_absorb.h.
+#include "mla_absorb.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "common.h"
+#include "decode_bf16.h"
+#include "f32_kernels.h"
+#include "prefill_bf16.h"
+
+namespace {
+
+using mla::bf16;
+
+constexpr size_t kAlign = 256;
+constexpr size_t kBadSize = (size_t)-1;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool bf16_shape_supported(int dq, int dv, int r) {
+  return (dq == 16 && dv == 16 && r == 32) || (dq == 64 && dv == 64 && r == 256) ||
+         (dq == 128 && dv == 128 && r == 512);
+}
+
+bool f32_shape_supported(int dq, int dv, int r) { return dq <= 256 && dv <= 256 && r <= 1024; }
+
+// element counts must stay well inside int64 and the grids inside int32
+bool fits(long long a, long long b, long long c = 1, long long d = 1) {
+  const long double v = (long double)a * b * c * d;
+  return v < 4.0e18L;
+}
+
+mla_status launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+struct DecodeLayout {
+  size_t wukT = 0, qabs = 0, part_o = 0, part_ml = 0, total = 0;
+};
+
+DecodeLayout decode_layout(int B, int H, int dq, int r, int G) {
+  DecodeLayout L;
+  size_t off = 0;
+  L.wukT = off;
+  off = align_up(off + (size_t)H * r * dq * sizeof(bf16));
+  L.qabs = off;
+  off = align_up(off + (size_t)B * H * r * sizeof(bf16));
+  L.part_o = off;
+  off = align_up(off + (size_t)(G + B) * H * r * sizeof(float));
+  L.part_ml = off;
+  off = align_up(off + (size_t)(G + B) * H * 2 * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+template <int DQ, int DV, int R>
+void launch_prefill_bf16(const mla::PrefillArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((mla::mla_prefill_bf16_kernel<DQ, DV, R>), dim3(a.B * a.ntb * a.nhg), dim3(64 * mla::kPrefillWaves), 0, s, a);
+}
+
+template <int DQ, int DV, int R>
+void launch_decode_bf16(const mla::DecodeAbsorbArgs& aa, const mla::DecodeSplitArgs& sa,
+                        const mla::DecodeMergeArgs& ma, hipStream_t s) {
+  hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3((aa.B + 15) / 16, (aa.H + 3) / 4), dim3(256), 0, s, aa);
+  hipLaunchKernelGGL((mla::mla_decode_split<R>), dim3(sa.G), dim3(64 * mla::kDecodeWaves), 0, s, sa);
+  hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3((ma.B + 15) / 16, ma.H), dim3(256), 0, s, ma);
+}
+
+void launch_wuk_transpose(const bf16* w, bf16* wt, int H, int dq, int r, hipStream_t s) {
+  hipLaunchKernelGGL((mla::mla_wuk_transpose<bf16>), dim3((r + 31) / 32, (dq + 31) / 32, H), dim3(256), 0, s,
+                     w, wt, H, dq, r);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: null or misaligned pointer, non-positive size or non-finite scale";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape or dtype outside the compiled set";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace smaller than required";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: the HIP runtime reported a launch error";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+size_t mla_absorb_prefill_workspace_size(int B, int T, int H, int d_q, int r, mla_dtype dtype) {
+  if (B <= 0 || T <= 0 || H <= 0 || d_q <= 0 || r <= 0) return kBadSize;
+  if (dtype == MLA_DTYPE_F32) return 0;
+  if (dtype != MLA_DTYPE_BF16) return kBadSize;
+  return align_up((size_t)H * r * d_q * sizeof(bf16));
+}
+
+mla_status mla_absorb_prefill(const void* q, const void* c, const void* w_uk, const void* w_uv,
+                              const void* gate, void* out, int B, int T, int H, int d_q, int d_v,
+                              int r, float scale, mla_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!q || !c || !w_uk || !w_uv || !gate || !out) return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || T <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(c) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(gate) ||
+      !aligned16(out))
+    return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return MLA_ERR_INVALID_ARG;
+  if (!fits(B, T, H, d_q > d_v ? (d_q > r ? d_q : r) : (d_v > r ? d_v : r))) return MLA_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+
+  if (dtype == MLA_DTYPE_F32) {
+    if (!f32_shape_supported(d_q, d_v, r)) return MLA_ERR_UNSUPPORTED;
+    if ((long long)B * T >= (1LL << 31) || H > 65535) return MLA_ERR_UNSUPPORTED;
+    mla::F32Args a{};
+    a.q = (const float*)q; a.c = (const float*)c; a.cu = nullptr;
+    a.wuk = (const float*)w_uk; a.wuv = (const float*)w_uv; a.gate = (const float*)gate;
+    a.out = (float*)out;
+    a.B = B; a.T = T; a.H = H; a.DQ = d_q; a.DV = d_v; a.R = r; a.N = 0; a.scale = scale; a.decode = 0;
+    hipLaunchKernelGGL(mla::mla_f32_kernel, dim3(B * T, H), dim3(64), 0, s, a);
+    return launch_status();
+  }
+
+  if (!bf16_shape_supported(d_q, d_v, r)) return MLA_ERR_UNSUPPORTED;
+  const size_t need = mla_absorb_prefill_workspace_size(B, T, H, d_q, r, dtype);
+  if (!workspace || !aligned16(workspace)) return need ? MLA_ERR_WORKSPACE : MLA_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  const long long ntb = (T + 31) / 32, nhg = (H + 3) / 4;
+  if ((long long)B * ntb * nhg >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
+
+  bf16* wukT = (bf16*)workspace;
+  launch_wuk_transpose((const bf16*)w_uk, wukT, H, d_q, r, s);
+
+  mla::PrefillArgs a{};
+  a.q = (const bf16*)q; a.c = (const bf16*)c; a.wukT = wukT; a.wuv = (const bf16*)w_uv;
+  a.gate = (const bf16*)gate; a.out = (bf16*)out;
+  a.B = B; a.T = T; a.H = H;
+  a.qscale = scale * mla::kLog2e;
+  a.ntb = (int)ntb; a.nhg = (int)nhg;
+  a.xcd_remap = (nhg % 8) == 0 ? 1 : 0;
+  if (d_q == 16) launch_prefill_bf16<16, 16, 32>(a, s);
+  else if (d_q == 64) launch_prefill_bf16<64, 64, 256>(a, s);
+  else launch_prefill_bf16<128, 128, 512>(a, s);
+  return launch_status();
+}
+
+size_t mla_absorb_decode_workspace_size(int B, int H, int d_q, int r, int num_splits, mla_dtype dtype) {
+  if (B <= 0 || H <= 0 || d_q <= 0 || r <= 0) return kBadSize;
+  if (dtype == MLA_DTYPE_F32) return 0;
+  if (dtype != MLA_DTYPE_BF16) return kBadSize;
+  int G = num_splits > 0 ? num_splits : device_cu_count();
+  if (G <= 0) return kBadSize;
+  return decode_layout(B, H, d_q, r, G).total;
+}
+
+mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* cu_seqlens,
+                             const void* w_uk, const void* w_uv, const void* gate, void* out,
+                             int B, int H, int d_q, int d_v, int r, int64_t total_len, float scale,
+                             int num_splits, mla_dtype dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!q || !c_cache || !cu_seqlens || !w_uk || !w_uv || !gate || !out) return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0 || total_len < B) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(c_cache) || !aligned16(cu_seqlens) || !aligned16(w_uk) ||
+      !aligned16(w_uv) || !aligned16(gate) || !aligned16(out))
+    return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return MLA_ERR_INVALID_ARG;
+  if (total_len >= (1LL << 31) || !fits(total_len, r) || !fits(B, H, d_q > d_v ? d_q : d_v))
+    return MLA_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+
+  if (dtype == MLA_DTYPE_F32) {
+    if (!f32_shape_supported(d_q, d_v, r) || H > 65535) return MLA_ERR_UNSUPPORTED;
+    mla::F32Args a{};
+    a.q = (const float*)q; a.c = (const float*)c_cache; a.cu = cu_seqlens;
+    a.wuk = (const float*)w_uk; a.wuv = (const float*)w_uv; a.gate = (const float*)gate;
+    a.out = (float*)out;
+    a.B = B; a.T = 1; a.H = H; a.DQ = d_q; a.DV = d_v; a.R = r; a.N = total_len;
+    a.scale = scale; a.decode = 1;
+    hipLaunchKernelGGL(mla::mla_f32_kernel, dim3(B, H), dim3(64), 0, s, a);
+    return launch_status();
+  }
+
+  if (!bf16_shape_supported(d_q, d_v, r)) return MLA_ERR_UNSUPPORTED;
+  if (H > 16 * mla::kDecodeWaves) return MLA_ERR_UNSUPPORTED;  // 16 heads per wave
+  int G = num_splits > 0 ? num_splits : device_cu_count();
+  if (G <= 0) return MLA_ERR_HIP;
+  const size_t need = decode_layout(B, H, d_q, r, G).total;
+  if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  // every range must own at least one cache row (the merge relies on it)
+  if ((long long)G > total_len) G = (int)total_len;
+  const DecodeLayout L = decode_layout(B, H, d_q, r, G);
+  char* ws = (char*)workspace;
+
+  bf16* wukT = (bf16*)(ws + L.wukT);
+  launch_wuk_transpose((const bf16*)w_uk, wukT, H, d_q, r, s);
+
+  mla::DecodeAbsorbArgs aa{};
+  aa.q = (const bf16*)q; aa.wukT = wukT; aa.qabs = (bf16*)(ws + L.qabs);
+  aa.B = B; aa.H = H; aa.qscale = scale * mla::kLog2e;
+  mla::DecodeSplitArgs sa{};
+  sa.qabs = aa.qabs; sa.cache = (const bf16*)c_cache; sa.cu = cu_seqlens;
+  sa.part_o = (float*)(ws + L.part_o); sa.part_ml = (float*)(ws + L.part_ml);
+  sa.B = B; sa.H = H; sa.G = G; sa.N = total_len;
+  mla::DecodeMergeArgs ma{};
+  ma.part_o = sa.part_o; ma.part_ml = sa.part_ml; ma.cu = cu_seqlens;
+  ma.wuv = (const bf16*)w_uv; ma.gate = (const bf16*)gate; ma.out = (bf16*)out;
+  ma.B = B; ma.H = H; ma.G = G; ma.N = total_len;
+  if (d_q == 16) launch_decode_bf16<16, 16, 32>(aa, sa, ma, s);
+  else if (d_q == 64) launch_decode_bf16<64, 64, 256>(aa, sa, ma, s);
+  else launch_decode_bf16<128, 128, 512>(aa, sa, ma, s);
+  return launch_status();
+}
+
+}  // extern "C"

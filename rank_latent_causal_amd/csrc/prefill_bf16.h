@@ -1,0 +1,121 @@
+// Fused bf16 prefill kernel for the absorbed Gated MLA layer on gfx950.
+//
+// One workgroup = 8 waves = a block of 32 query positions x 4 heads (two
+// 16-row halves per head).  Each wave runs the whole chain of page
+// "Gated MLA（矩阵吸收版）", section 完整计算流（四步） steps 2-4 (the same
+// contractions are listed in page "符号表", section Einsum 速查) for its rows:
+//   prologue  q_abs^T = W_UK[h]^T q^T on MFMA, kept in VGPRs (absorb)
+//   main loop causal latent flash attention over 32-key tiles of c
+//   epilogue  o^T = W_UV[h] (O^T / l) on MFMA, sigmoid gate, store
+// Every latent tile is copied once from global memory straight into LDS
+// (global_load_lds, no register staging) and shared by the eight waves,
+// i.e. by 4 heads x 32 positions: heads are folded into the rows that reuse
+// one c tile.  Two LDS stages let the copy of tile n+1 overlap tile n.
+#pragma once
+
+#include "attn_core.h"
+
+namespace mla {
+
+struct PrefillArgs {
+  const bf16* q;     // [B, T, H, DQ]
+  const bf16* c;     // [B, T, R]
+  const bf16* wukT;  // [H, R, DQ]  (W_UK transposed per head, in the workspace)
+  const bf16* wuv;   // [H, DV, R]
+  const bf16* gate;  // [B, T, H*DV]
+  bf16* out;         // [B, T, H*DV]
+  int B, T, H;
+  float qscale;      // softmax scale * log2(e), folded into q_abs
+  int ntb;           // ceil(T / 32) query blocks
+  int nhg;           // ceil(H / 4) head groups
+  int xcd_remap;     // 1: head group hg runs on XCD hg % 8 (weights stay in its L2)
+};
+
+constexpr int kPrefillWaves = 8;
+
+template <int DQ, int DV, int R>
+__global__ void __launch_bounds__(64 * kPrefillWaves)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+mla_prefill_bf16_kernel(PrefillArgs a) {
+  using LT = LatentTile<R>;
+  constexpr int NS = 2;
+  constexpr int LPW = copies_per_wave<R>(kPrefillWaves);
+  static_assert(LT::COPIES % kPrefillWaves == 0 || LT::COPIES < kPrefillWaves, "copy split");
+  static_assert(DQ % 16 == 0 && DV % 16 == 0 && R % 32 == 0, "shape");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * LT::BYTES];
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+
+  // ---- work item: heaviest query blocks first
+  const int x = blockIdx.x;
+  int tb, b, hg;
+  if (a.xcd_remap) {
+    // gridDim.x = 8 * per; XCD x % 8 owns head groups hg = x % 8 (mod 8)
+    const int xcd = x & 7, pos = x >> 3, nh8 = a.nhg >> 3;
+    hg = (pos % nh8) * 8 + xcd;
+    const int rest = pos / nh8;
+    b = rest % a.B;
+    tb = a.ntb - 1 - rest / a.B;
+  } else {
+    hg = x % a.nhg;
+    const int rest = x / a.nhg;
+    b = rest % a.B;
+    tb = a.ntb - 1 - rest / a.B;
+  }
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int hw = w & 3, th = w >> 2;
+  const int h = hg * 4 + hw;
+  const bool hvalid = h < a.H;
+  const int hc = hvalid ? h : a.H - 1;
+  const int T = a.T, H = a.H;
+  const int t0 = tb * 32;
+  const int tw = t0 + 16 * th;  // first row of this wave
+  const int t = tw + l16;       // this lane's query row
+  const bool tvalid = t < T;
+  const int tc = tvalid ? t : T - 1;
+  const bf16* __restrict__ cb = a.c + (size_t)b * T * R;
+
+  const int ntiles = (min(t0 + 32, T) + LT::KT - 1) / LT::KT;
+
+  // stream the first latent tile while the absorb prologue runs
+  TileCopier<R, kPrefillWaves> copier;
+  copier.init(w, lane);
+  copier.issue(cb, 0, T, smem);
+
+  WaveAttn<R> st;
+  absorb_rows<DQ, R>(a.q + (((size_t)b * T + tc) * H + hc) * DQ, a.wukT + (size_t)hc * R * DQ, a.qscale,
+                     l16, kq, st.qT);
+  st.reset();
+  st.init_addressing(l16, kq);
+
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + 1 < ntiles) {
+      copier.issue(cb, (long long)(it + 1) * LT::KT, T, smem + ((it + 1) & 1) * LT::BYTES);
+      wait_vmcnt<LPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    const MLA_LDS char* tile = smem + (it & 1) * LT::BYTES;
+    const int s0 = it * LT::KT;
+    f32x4 sa, sb;
+    st.scores(tile, sa, sb);
+    if (s0 + LT::KT - 1 > tw) {  // causal mask (also hides keys past T)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (s0 + 4 * kq + e > t) sa[e] = -INFINITY;
+        if (s0 + 16 + 4 * kq + e > t) sb[e] = -INFINITY;
+      }
+    }
+    st.update(tile, sa, sb);
+    __syncthreads();  // this stage is refilled by the next iteration
+  }
+
+  const float inv_l = 1.0f / col_sum(st.l_run);
+  const size_t orow = ((size_t)b * T + tc) * (size_t)H * DV + (size_t)hc * DV;
+  project_gate_store<DV, R>(st.oT, inv_l, a.wuv + (size_t)hc * DV * R, a.gate + orow, a.out + orow,
+                            tvalid && hvalid, l16, kq);
+}
+
+}  // namespace mla

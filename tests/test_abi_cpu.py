@@ -1,0 +1,115 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, and rejects bad arguments before launching anything (no GPU is
+touched: every call here fails validation on the host)."""
+import ctypes as ct
+import os
+import re
+import subprocess
+
+import pytest
+
+import rank_latent_causal_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_absorb.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mla.LIB_PATH), reason="libmla_absorb.so not built")
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_exactly_the_bound_functions():
+    assert declared_functions() == sorted(mla.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ct.CDLL(mla.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (mla_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings():
+    for s in range(5):
+        assert mla.status_string(s).startswith(("MLA_OK", "MLA_ERR"))
+    assert "UNKNOWN" in mla.status_string(99)
+
+
+def test_prefill_workspace_sizes():
+    assert mla.prefill_workspace_size(2, 128, 8, 16, 32, mla.DTYPE_F32) == 0
+    n = mla.prefill_workspace_size(1, 8192, 96, 128, 512, mla.DTYPE_BF16)
+    assert n >= 96 * 512 * 128 * 2 and n % 256 == 0
+    with pytest.raises(mla.MLAError):
+        mla.prefill_workspace_size(0, 1, 1, 16, 32, mla.DTYPE_BF16)
+
+
+def test_decode_workspace_sizes_explicit_splits():
+    assert mla.decode_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_F32) == 0
+    n = mla.decode_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_BF16)
+    # W_UK^T + q_abs + (G+B) partial rows of r floats + (m, l)
+    assert n >= 96 * 512 * 128 * 2 + 64 * 96 * 512 * 2 + (256 + 64) * 96 * (512 + 2) * 4
+    assert mla.decode_workspace_size(64, 96, 128, 512, 512, mla.DTYPE_BF16) > n
+    with pytest.raises(mla.MLAError):
+        mla.decode_workspace_size(64, 96, 128, 512, 256, 7)
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, c=FAKE, w_uk=FAKE, w_uv=FAKE, gate=FAKE, out=FAKE, B=1, T=8, H=4, dq=128, dv=128,
+             r=512, scale=0.1, dtype=mla.DTYPE_BF16, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return mla.lib().mla_absorb_prefill(a["q"], a["c"], a["w_uk"], a["w_uv"], a["gate"], a["out"], a["B"],
+                                        a["T"], a["H"], a["dq"], a["dv"], a["r"], a["scale"], a["dtype"],
+                                        a["ws"], a["wsb"], a["stream"])
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, c=FAKE, cu=FAKE, w_uk=FAKE, w_uv=FAKE, gate=FAKE, out=FAKE, B=2, H=4, dq=128, dv=128,
+             r=512, N=100, scale=0.1, splits=8, dtype=mla.DTYPE_BF16, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return mla.lib().mla_absorb_decode(a["q"], a["c"], a["cu"], a["w_uk"], a["w_uv"], a["gate"], a["out"],
+                                       a["B"], a["H"], a["dq"], a["dv"], a["r"], a["N"], a["scale"],
+                                       a["splits"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(out=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(c=FAKE + 8), mla.MLA_ERR_INVALID_ARG),
+    (dict(B=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(T=-3), mla.MLA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mla.MLA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), mla.MLA_ERR_INVALID_ARG),
+    (dict(dtype=5), mla.MLA_ERR_INVALID_ARG),
+    (dict(dq=96, dv=96, r=384), mla.MLA_ERR_UNSUPPORTED),
+    (dict(dv=64), mla.MLA_ERR_UNSUPPORTED),
+    (dict(dtype=mla.DTYPE_F32, r=2048), mla.MLA_ERR_UNSUPPORTED),
+    (dict(ws=None), mla.MLA_ERR_WORKSPACE),
+    (dict(wsb=1024), mla.MLA_ERR_WORKSPACE),
+    (dict(ws=FAKE + 4), mla.MLA_ERR_WORKSPACE),
+])
+def test_prefill_rejects(kw, status):
+    assert _prefill(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(gate=FAKE + 2), mla.MLA_ERR_INVALID_ARG),
+    (dict(H=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(N=1), mla.MLA_ERR_INVALID_ARG),          # fewer cache rows than sequences
+    (dict(scale=float("-inf")), mla.MLA_ERR_INVALID_ARG),
+    (dict(N=1 << 31), mla.MLA_ERR_UNSUPPORTED),
+    (dict(H=256), mla.MLA_ERR_UNSUPPORTED),
+    (dict(dq=64), mla.MLA_ERR_UNSUPPORTED),
+    (dict(ws=None), mla.MLA_ERR_WORKSPACE),
+    (dict(wsb=4096), mla.MLA_ERR_WORKSPACE),
+])
+def test_decode_rejects(kw, status):
+    assert _decode(**kw) == status

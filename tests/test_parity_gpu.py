@@ -1,0 +1,164 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, element by element, plus structural invariants that
+hold at any size."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import datagen as dg
+import oracle
+from gpu_util import (assert_parity, oracle_decode, oracle_prefill, run_decode, run_prefill, sample_rows,
+                      to_host_f64)
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {"toy": (16, 16, 32), "mid": (64, 64, 256), "full": (128, 128, 512)}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.get()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rank_latent_causal_amd as mla
+    mla.lib()  # loud failure if the HIP library is missing
+    return torch
+
+
+# ------------------------------------------------------------------ prefill
+def test_prefill_toy_f32_workload(o):
+    d = dg.workload_inputs("toy_f32")
+    log(f"prefill toy_f32 B={d['B']} T={d['T']} H={d['H']}")
+    got = to_host_f64(run_prefill(d))
+    assert_parity(got, oracle_prefill(o, d), dg.F32, "toy_f32")
+
+
+@pytest.mark.parametrize("B,T,H,shape", [
+    (1, 1, 1, "toy"), (2, 37, 3, "toy"), (3, 100, 5, "toy"),
+    (1, 45, 2, "mid"), (2, 97, 9, "mid"),
+    (1, 33, 1, "full"), (2, 70, 5, "full"), (1, 130, 8, "full"),
+])
+def test_prefill_bf16_ragged(o, B, T, H, shape):
+    dq, dv, r = SHAPES[shape]
+    d = dg.prefill_inputs(B, T, H, dq, dv, r, dtype=dg.BF16, seed=1000 + B * 7 + T + H)
+    d["scale"] = dq ** -0.5
+    log(f"prefill bf16 B={B} T={T} H={H} dq={dq} r={r}")
+    got = to_host_f64(run_prefill(d))
+    assert_parity(got, oracle_prefill(o, d), dg.BF16, f"prefill {shape} B{B} T{T} H{H}")
+
+
+@pytest.mark.parametrize("B,T,H,shape", [(1, 40, 4, "full"), (2, 50, 3, "toy")])
+def test_prefill_f32_other_shapes(o, B, T, H, shape):
+    dq, dv, r = SHAPES[shape]
+    d = dg.prefill_inputs(B, T, H, dq, dv, r, dtype=dg.F32, seed=2000 + T)
+    log(f"prefill f32 B={B} T={T} H={H} r={r}")
+    got = to_host_f64(run_prefill(d, scale=0.3))
+    assert_parity(got, oracle_prefill(o, d, scale=0.3), dg.F32, f"prefill f32 {shape}")
+
+
+def test_prefill_toy_max_workload(o):
+    d = dg.workload_inputs("toy_max")
+    log("prefill toy_max B=4 T=2048 H=8")
+    got = to_host_f64(run_prefill(d))
+    assert_parity(got, oracle_prefill(o, d), dg.BF16, "toy_max")
+
+
+def test_prefill_mid_workload_sampled(o):
+    d = dg.workload_inputs("mid")
+    log("prefill mid B=4 T=4096 H=32 (sampled rows)")
+    got = to_host_f64(run_prefill(d)).reshape(d["B"] * d["T"], -1)
+    rows = sample_rows(d["B"], d["T"], 6, seed=5)
+    assert_parity(got[rows], oracle_prefill(o, d, rows=rows), dg.BF16, "mid sampled")
+
+
+def test_prefill_full_workload_sampled(o):
+    d = dg.workload_inputs("full_prefill")
+    log("prefill full B=1 T=8192 H=96 (sampled rows)")
+    got = to_host_f64(run_prefill(d)).reshape(d["B"] * d["T"], -1)
+    rows = sample_rows(d["B"], d["T"], 6, seed=6)
+    assert_parity(got[rows], oracle_prefill(o, d, rows=rows), dg.BF16, "full sampled")
+
+
+def test_prefill_first_position_closed_form():
+    """t = 0 sees only its own latent: out = sigmoid(g) * (c_0 W_UV^T) for any
+    q and scale (checked on the GPU output alone, at the full width)."""
+    d = dg.prefill_inputs(2, 64, 8, 128, 128, 512, dtype=dg.BF16, seed=3)
+    got = to_host_f64(run_prefill(d, scale=5.0))
+    c0 = dg.as_f32(d["c"])[:, 0].astype(np.float64)
+    wuv = dg.as_f32(d["w_uv"]).astype(np.float64)
+    g = dg.as_f32(d["gate"])[:, 0].astype(np.float64)
+    ref = np.einsum("bj,hvj->bhv", c0, wuv).reshape(2, -1) / (1 + np.exp(-g))
+    assert_parity(got[:, 0], ref, dg.BF16, "t=0 closed form")
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("lens,H,shape,splits", [
+    ([1], 4, "toy", 1),
+    ([5, 1, 40, 33, 64], 8, "toy", 3),
+    ([100, 7, 250], 32, "mid", 0),
+    ([31, 32, 33, 1, 200], 96, "full", 4),
+    ([300, 1, 129], 96, "full", 0),
+    ([1000, 17, 513, 64], 40, "full", 7),
+])
+def test_decode_bf16_ragged(o, lens, H, shape, splits):
+    dq, dv, r = SHAPES[shape]
+    d = dg.decode_inputs(len(lens), H, dq, dv, r, dtype=dg.BF16, seed=3000 + sum(lens), lengths=lens)
+    d["scale"] = dq ** -0.5
+    log(f"decode bf16 lens={lens} H={H} r={r} splits={splits}")
+    got = to_host_f64(run_decode(d, num_splits=splits))
+    assert_parity(got, oracle_decode(o, d), dg.BF16, f"decode {shape} {lens}")
+
+
+def test_decode_f32(o):
+    d = dg.decode_inputs(3, 8, 16, 16, 32, dtype=dg.F32, seed=4000, lengths=[9, 1, 130])
+    log("decode f32 toy")
+    got = to_host_f64(run_decode(d, scale=1.0))
+    assert_parity(got, oracle_decode(o, d, scale=1.0), dg.F32, "decode f32")
+
+
+def test_decode_split_count_invariance():
+    d = dg.decode_inputs(4, 96, 128, 128, 512, dtype=dg.BF16, seed=4100, lengths=[700, 3, 1500, 64])
+    d["scale"] = 128 ** -0.5
+    log("decode split invariance")
+    outs = [to_host_f64(run_decode(d, num_splits=s)) for s in (1, 2, 5, 64, 256)]
+    for s, x in zip((2, 5, 64, 256), outs[1:]):
+        assert np.abs(x - outs[0]).max() <= 2e-2, f"splits={s}"
+
+
+def test_decode_matches_prefill_last_row():
+    """Decode over a cache of len rows equals prefill row len - 1, both on the
+    GPU (same inputs laid out both ways)."""
+    B, T, H = 3, 96, 16
+    d = dg.prefill_inputs(B, T, H, 128, 128, 512, dtype=dg.BF16, seed=4200)
+    d["scale"] = 128 ** -0.5
+    lens = np.array([96, 1, 50])
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    dd = dict(q=np.stack([d["q"][i, lens[i] - 1] for i in range(B)]),
+              c_cache=np.concatenate([d["c"][i, :lens[i]] for i in range(B)]),
+              cu_seqlens=cu, w_uk=d["w_uk"], w_uv=d["w_uv"],
+              gate=np.stack([d["gate"][i, lens[i] - 1] for i in range(B)]), scale=d["scale"])
+    log("decode vs prefill last row")
+    pre = to_host_f64(run_prefill(d))
+    dec = to_host_f64(run_decode(dd))
+    ref = np.stack([pre[i, lens[i] - 1] for i in range(B)])
+    assert np.abs(dec - ref).max() <= 2e-2
+
+
+def test_decode_full_workload_sampled(o):
+    d = dg.workload_inputs("full_decode")
+    log(f"decode full B=64 total={int(d['cu_seqlens'][-1])} (sampled sequences)")
+    got = to_host_f64(run_decode(d))
+    seqs = np.array([0, 1, int(np.argmin(d["lengths"])), int(np.argmax(d["lengths"])), 31, 63], dtype=np.int64)
+    assert_parity(got[seqs], oracle_decode(o, d, seqs=seqs), dg.BF16, "full decode sampled")
