@@ -1,0 +1,199 @@
+"""Benchmark of the absorbed Gated MLA hot path on one MI355X.
+
+One step = one full-width prefill call (B=1, T=8192, H=96, d_q=d_v=128,
+r=512, bf16, causal, scale 1/sqrt(d_q)) plus one full-width decode call
+(64 sequences with cache lengths ~ U[1024, 32768], same widths) on seeded
+synthetic inputs already resident in HBM.  Each call is bracketed by HIP
+events on the stream it runs on.
+
+Printed (one JSON line): prefill TFLOP/s as `value` (causal-triangle
+algorithmic FLOPs), decode latent-cache GB/s (algorithmic bytes), the
+roofline object of each against MI355X's published peaks, and the CPU oracle
+timed on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import datagen as dg  # noqa: E402
+
+METRIC = "absorbed-MLA prefill TFLOP/s + decode latent-cache GB/s (% of roofline), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def prefill_flops(B, T, H, dq, dv, r):
+    """Algorithmic FLOPs of one prefill call: absorb + W_UV products on every
+    (b, t, h), and the score and latent-sum products on the causal triangle
+    (diagonal included)."""
+    pairs = B * H * T * (T + 1) // 2
+    return 2 * B * T * H * r * (dq + dv) + 4 * r * pairs
+
+
+def decode_flops(lengths, H, dq, dv, r):
+    return int(4 * r * H * int(np.sum(lengths)) + len(lengths) * H * 2 * r * (dq + dv))
+
+
+def decode_bytes(lengths, H, dq, dv, r, elt=2):
+    """Bytes the decode call must move: the latent cache once, both weight
+    tensors once, q, gate, out and cu_seqlens."""
+    B = len(lengths)
+    return int(elt * r * int(np.sum(lengths)) + elt * H * r * (dq + dv) + elt * B * H * (dq + 2 * dv) + 4 * (B + 1))
+
+
+def dev(x):
+    import torch
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def cpu_baseline(pre, target_s: float):
+    """The oracle on a sample of query rows of the prefill workload, sized to
+    take about target_s seconds; reported in TFLOP/s of the same count."""
+    import oracle
+    o = oracle.get()
+    f = dg.as_f32
+    q, c, wk, wv, g = [f(pre[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")]
+    B, T, H, dq, dv, r = pre["B"], pre["T"], pre["H"], pre["d_q"], pre["d_v"], pre["r"]
+
+    def row_flops(rows):
+        t = rows % T
+        return int(np.sum(H * (4 * r * (t + 1) + 2 * r * (dq + dv))))
+
+    def run(n):
+        rows = np.array([int((k + 0.5) * B * T / n) for k in range(n)], dtype=np.int64)
+        t0 = time.perf_counter()
+        o.prefill(q, c, wk, wv, g, pre["scale"], rows=rows)
+        return time.perf_counter() - t0, row_flops(rows), rows
+
+    dt, fl, _ = run(64)
+    n = int(min(B * T, max(64, 64 * target_s / max(dt, 1e-3))))
+    dt, fl, rows = run(n)
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} query rows (all {H} heads) evenly spaced over the {B}x{T} prefill workload, "
+                      f"{fl / 1e9:.1f} GFLOP in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--which", choices=["both", "prefill", "decode"], default="both")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's hot path only (got --gpus {args.gpus}); multi-GPU runs are not "
+              f"part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rank_latent_causal_amd as mla
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    mla.lib()
+
+    pw, dw = dg.WORKLOADS["full_prefill"], dg.WORKLOADS["full_decode"]
+    t_gen = time.perf_counter()
+    pre = dg.workload_inputs("full_prefill")
+    dec = dg.workload_inputs("full_decode")
+    print(f"# inputs generated in {time.perf_counter() - t_gen:.1f}s; decode cache rows "
+          f"{int(dec['cu_seqlens'][-1])}", file=sys.stderr, flush=True)
+
+    P = [dev(pre[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")]
+    B, T, H, dq, dv, r = pre["B"], pre["T"], pre["H"], pre["d_q"], pre["d_v"], pre["r"]
+    p_out = torch.empty((B, T, H * dv), dtype=torch.bfloat16, device="cuda")
+    p_ws = torch.empty(max(1, mla.prefill_workspace_size(B, T, H, dq, r, mla.DTYPE_BF16)), dtype=torch.uint8,
+                       device="cuda")
+    D = [dev(dec[k]) for k in ("q", "c_cache", "cu_seqlens", "w_uk", "w_uv", "gate")]
+    DB = dec["B"]
+    d_out = torch.empty((DB, H * dv), dtype=torch.bfloat16, device="cuda")
+    d_ws = torch.empty(max(1, mla.decode_workspace_size(DB, H, dq, r, 0, mla.DTYPE_BF16)), dtype=torch.uint8,
+                       device="cuda")
+
+    do_pre = args.which in ("both", "prefill")
+    do_dec = args.which in ("both", "decode")
+
+    def step(ev):
+        if do_pre:
+            ev[0].record()
+            mla.mla_absorb_prefill(*P, pre["scale"], out=p_out, workspace=p_ws)
+            ev[1].record()
+        if do_dec:
+            ev[2].record()
+            mla.mla_absorb_decode(*D, dec["scale"], out=d_out, workspace=d_ws)
+            ev[3].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(args.warmup):
+        step(warm)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"# timed {args.steps} steps in {wall:.3f}s", file=sys.stderr, flush=True)
+
+    pf = prefill_flops(B, T, H, dq, dv, r)
+    df = decode_flops(dec["lengths"], H, dq, dv, r)
+    dbytes = decode_bytes(dec["lengths"], H, dq, dv, r)
+    p_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) if do_pre else 0.0
+    d_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) if do_dec else 0.0
+    p_tflops = pf / (p_ms * 1e-3) / 1e12 if do_pre else None
+    d_gbs = dbytes / (d_ms * 1e-3) / 1e9 if do_dec else None
+
+    res = {
+        "metric": METRIC,
+        "value": round(p_tflops, 2) if do_pre else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(p_ms + d_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "full_prefill (B=1, T=8192, H=96, d_q=d_v=128, r=512, causal, scale 1/sqrt(128)) + "
+                        "full_decode (B=64 queries, cache lengths ~ U[1024,32768], H=96, d_q=d_v=128, r=512)",
+            "prefill_seed": pw["seed"], "decode_seed": dw["seed"],
+            "decode_cache_rows": int(dec["cu_seqlens"][-1]),
+        },
+    }
+    if do_pre:
+        res["roofline"] = {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                           "kernel": "mla_prefill_bf16_kernel<128,128,512>", "flop_per_launch": pf,
+                           "ms_per_launch": round(p_ms, 4)}
+    if do_dec:
+        res["decode"] = {"value": round(d_gbs, 1), "unit": "GB/s", "ms": round(d_ms, 4),
+                         "tflops": round(df / (d_ms * 1e-3) / 1e12, 2),
+                         "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                      "kernel": "mla_decode_split<512> + absorb + merge",
+                                      "bytes_per_launch": dbytes}}
+    if not args.no_cpu_baseline and do_pre:
+        res["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

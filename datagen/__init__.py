@@ -9,7 +9,8 @@ toy/full-size table of the "K3 混合架构" page):
 
 * every tensor is drawn from its own counter-based Philox4x64 stream, keyed by
   ``(seed, tensor_id << 32 | chunk)``, so a tensor never depends on the size or
-  order of the others and large tensors are drawn in independent row chunks;
+  order of the others; large tensors are drawn in independent chunks of
+  ``max(1, 2**21 // cols)`` rows;
 * ``q ~ N(0,1)`` with shape ``[B,T,H,d_q]`` (prefill) or ``[B,H,d_q]`` (decode);
 * ``c`` is a row-wise RMS-normalised ``N(0,1)`` draw over the last axis
   (gain 1, ``eps = 1e-6`` inside the square root), computed in float64;
@@ -36,7 +37,7 @@ F32 = "f32"
 BF16 = "bf16"
 
 _TID = {"q": 1, "c": 2, "w_uk": 3, "w_uv": 4, "gate": 5, "lens": 6}
-_CHUNK_ROWS = 1 << 15
+_CHUNK_ELEMS = 1 << 21
 _RMS_EPS = 1e-6
 
 
@@ -77,11 +78,12 @@ def _draw_rows(seed: int, name: str, rows: int, cols: int, std: float, dtype: st
                rms_norm: bool = False) -> np.ndarray:
     """rows x cols standard-normal draw (times std), chunked by rows."""
     out = np.empty((rows, cols), dtype=np.uint16 if dtype == BF16 else np.float32)
-    nchunks = max(1, -(-rows // _CHUNK_ROWS))
+    chunk_rows = max(1, _CHUNK_ELEMS // cols)
+    nchunks = max(1, -(-rows // chunk_rows))
 
     def work(ci: int) -> None:
-        r0 = ci * _CHUNK_ROWS
-        r1 = min(rows, r0 + _CHUNK_ROWS)
+        r0 = ci * chunk_rows
+        r1 = min(rows, r0 + chunk_rows)
         if r1 <= r0:
             return
         x = _gen(seed, _TID[name], ci).standard_normal((r1 - r0, cols))

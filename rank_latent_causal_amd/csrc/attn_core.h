@@ -35,37 +35,40 @@ constexpr int copies_per_wave(int nwaves) {
 }
 
 // Copies latent rows [row0, row0 + 32) into a swizzled LDS tile with raw
-// buffer loads.  The per-lane source offsets do not depend on the tile and
-// are computed once; rows at or past row_end read as zeros (their scores are
-// masked).  Copy qi (1 KiB of LDS) is issued by wave qi % NW, so each wave
-// issues either copies_per_wave(NW) copies or none.
+// buffer loads.  Copy qi (1 KiB of LDS, rows qi*RPI .. of the tile) is issued
+// by wave qi % NW, so each wave issues either copies_per_wave(NW) copies or
+// none.  Each copy gets its own scalar descriptor starting at its first row,
+// so rows at or past row_end read as zeros (their scores are masked) and the
+// per-lane offsets are small; they are recomputed from the lane id for every
+// tile instead of being kept live across the main loop.
 template <int R, int NW>
 struct TileCopier {
   static constexpr int COPIES = LatentTile<R>::COPIES;
   static constexpr int CPW = copies_per_wave<R>(NW);
-  unsigned voff[CPW];
+  static constexpr int CPR = R / 8;       // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;    // rows per copy
+  static_assert(64 % CPR == 0, "a copy covers whole rows");
   int w;
 
-  __device__ __forceinline__ void init(int wave, int lane) {
-    constexpr int CPR = R / 8;
-    w = wave;
-#pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const int P = (wave + NW * c) * 64 + lane;
-      const int s = P / CPR;
-      const int L = (P % CPR) ^ chunk_swizzle<R>(s);
-      voff[c] = (unsigned)((s * R + L * 8) * 2);
-    }
-  }
+  __device__ __forceinline__ void init(int wave, int) { w = wave; }
 
   __device__ __forceinline__ void issue(const bf16* __restrict__ base, long long row0, long long row_end,
                                         MLA_LDS char* stage) const {
-    const long long rows = row_end - row0 < LatentTile<R>::KT ? row_end - row0 : LatentTile<R>::KT;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (size_t)row0 * R, (unsigned)(rows * R * 2));
+    int l = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(l));  // opaque: keeps the offset math inside the loop
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int qi = w + NW * c;
-      if (qi < COPIES) buf2lds16(rs, voff[c], stage + qi * 1024);
+      if (qi < COPIES) {
+        const int srow = qi * RPI;
+        const int s = srow + l / CPR;
+        const int L = (l % CPR) ^ chunk_swizzle<R>(s);
+        const unsigned voff = (unsigned)(((l / CPR) * R + L * 8) * 2);
+        const long long first = row0 + srow;
+        long long rows = row_end - first;
+        rows = rows < 0 ? 0 : (rows > RPI ? RPI : rows);
+        buf2lds16(make_rsrc(base + (size_t)first * R, (unsigned)(rows * R * 2)), voff, stage + qi * 1024);
+      }
     }
   }
 };
@@ -102,28 +105,65 @@ __device__ __forceinline__ void absorb_rows(const bf16* __restrict__ qrow, const
   }
 }
 
-template <int R>
+// QCH / VCH: score k-steps / value tiles issued between scheduling barriers,
+// which bounds the LDS operand reads in flight (and their registers).
+template <int R, int QCH = 4, int VCH = 8>
 struct WaveAttn {
   static constexpr int NKK = R / 32;
   static constexpr int NJT = R / 16;
-  // The swizzle only permutes the low 4 bits of a chunk index, so operand
-  // addresses are a per-lane base (one per value of those bits) plus an
-  // immediate multiple of 256 bytes.
-  static constexpr int NQB = NKK < 4 ? NKK : 4;
-  static constexpr int NTB = NJT < 8 ? NJT : 8;
+  // The swizzle f(s) = 2 (s & 7) | ((s >> 3) & 1) only permutes the low 4
+  // bits of a chunk index, so for R >= 128 every operand address is one
+  // per-lane base plus a small XOR term and an immediate:
+  //  * score operand, row l16, chunk 4kk + kq:  with x = f(l16)
+  //      16 ((kq ^ x) & 3) + 64 ((kk & 3) ^ (x >> 2)) + 256 (kk >> 2)
+  //  * value operand, row r = 4kq + l16/4, chunk 2t + (l16%4)/2:
+  //      16 (((l16%4)/2) ^ ((r >> 3) & 1)) + 32 ((t & 7) ^ (r & 7)) + 256 (t >> 3)
+  // Smaller r keeps one precomputed base per k-step / value tile.
+  static constexpr bool XORADDR = (R / 8 >= 16);
+  static constexpr int NQB = XORADDR ? 1 : NKK;
+  static constexpr int NTB = XORADDR ? 1 : NJT;
   static constexpr int ROWB = R * 2;
   bf16x8 qT[NKK];
   f32x4 oT[NJT];
   float m_run, l_run;
-  int qk_base[NQB];  // score A operand: row l16, chunk 4u + kq
-  int tr_base[NTB];  // value A operand: row 4kq + l16/4, chunk 2u + (l16%4)/2, half l16%2
+  int qk_base[NQB];
+  int tr_base[NTB];
+  int qk_x, tr_rx;
 
   __device__ __forceinline__ void init_addressing(int l16, int kq) {
-#pragma unroll
-    for (int u = 0; u < NQB; ++u) qk_base[u] = tile_off<R>(l16, 4 * u + kq);
     const int r = 4 * kq + (l16 >> 2), q = l16 & 3;
+    if constexpr (XORADDR) {
+      const int x = chunk_swizzle<R>(l16);
+      qk_base[0] = l16 * ROWB + (((kq ^ x) & 3) << 4);
+      qk_x = x >> 2;
+      tr_base[0] = r * ROWB + ((((q >> 1) ^ ((r >> 3) & 1))) << 4) + (q & 1) * 8;
+      tr_rx = r & 7;
+    } else {
 #pragma unroll
-    for (int u = 0; u < NTB; ++u) tr_base[u] = tile_off<R>(r, 2 * u + (q >> 1)) + (q & 1) * 8;
+      for (int u = 0; u < NQB; ++u) qk_base[u] = tile_off<R>(l16, 4 * u + kq);
+#pragma unroll
+      for (int u = 0; u < NTB; ++u) tr_base[u] = tile_off<R>(r, 2 * u + (q >> 1)) + (q & 1) * 8;
+      qk_x = tr_rx = 0;
+    }
+  }
+
+  // b / x are per-tile opaque copies of the bases (see scores / update), so
+  // the compiler forms each address at its use instead of keeping all of
+  // them live across the main loop.
+  __device__ __forceinline__ int qk_off(int kk, int b, int x) const {
+    if constexpr (XORADDR) {
+      return b + (((kk & 3) ^ x) << 6) + (kk >> 2) * 256;
+    } else {
+      return qk_base[kk];
+    }
+  }
+
+  __device__ __forceinline__ int tr_off(int t, int b, int x) const {
+    if constexpr (XORADDR) {
+      return b + (((t & 7) ^ x) << 5) + (t >> 3) * 256;
+    } else {
+      return tr_base[t];
+    }
   }
 
   __device__ __forceinline__ void reset() {
@@ -137,12 +177,14 @@ struct WaveAttn {
   __device__ __forceinline__ void scores(const MLA_LDS char* tile, f32x4& s0, f32x4& s1) const {
     s0 = f32x4{};
     s1 = f32x4{};
-    constexpr int CH = NKK < 4 ? NKK : 4;  // bounds the operand reads in flight
+    int qb = qk_base[0], qx = qk_x;
+    asm volatile("" : "+v"(qb), "+v"(qx));
+    constexpr int CH = NKK < QCH ? NKK : QCH;
 #pragma unroll
     for (int k0 = 0; k0 < NKK; k0 += CH) {
 #pragma unroll
       for (int kk = k0; kk < k0 + CH; ++kk) {
-        const MLA_LDS char* p = tile + qk_base[kk % NQB] + (kk / NQB) * 256;
+        const MLA_LDS char* p = tile + qk_off(kk, qb, qx);
         s0 = mfma16(lds_read_b128(p), qT[kk], s0);
         s1 = mfma16(lds_read_b128(p + 16 * ROWB), qT[kk], s1);
       }
@@ -178,12 +220,14 @@ struct WaveAttn {
     // value operand: lane i of 16-lane group kq takes latent dim 16t + i and
     // keys {4kq+e} (lo) / {16+4kq+e} (hi); its tr16 source chunk is key row
     // 4kq + i/4 (+16), dims 16t + 4(i%4) .. +3.
-    constexpr int CH = NJT < 8 ? NJT : 8;
+    constexpr int CH = NJT < VCH ? NJT : VCH;
+    int tb = tr_base[0], tx = tr_rx;
+    asm volatile("" : "+v"(tb), "+v"(tx));
 #pragma unroll
     for (int t0 = 0; t0 < NJT; t0 += CH) {
 #pragma unroll
       for (int t = t0; t < t0 + CH; ++t) {
-        const MLA_LDS char* p = tile + tr_base[t % NTB] + (t / NTB) * 256;
+        const MLA_LDS char* p = tile + tr_off(t, tb, tx);
         const bf16x4 lo = lds_read_tr16(p);
         const bf16x4 hi = lds_read_tr16(p + 16 * ROWB);
         oT[t] = mfma16(cat4(lo, hi), pB, oT[t]);

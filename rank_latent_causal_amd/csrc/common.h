@@ -82,6 +82,19 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, unsigned vo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MLA_LDS void*)lds_base, 16, (int)voff, 0, 0, 0);
 }
 
+// Workgroup barrier without a memory fence.  __syncthreads() also waits for
+// every outstanding global access (vmcnt(0)), which would drain the tile
+// prefetches in flight; here the LDS hand-off is ordered explicitly instead:
+// a wave's own tile copies are waited for with wait_vmcnt<N>() before the
+// barrier, and a wave's LDS reads have returned (their values are consumed by
+// MFMAs) before it reaches the barrier that lets the stage be refilled.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // s_waitcnt vmcnt(N) leaving the other counters untouched (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

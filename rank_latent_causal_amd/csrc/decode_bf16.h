@@ -160,7 +160,7 @@ mla_decode_split(DecodeSplitArgs a) {
     } else {
       wait_vmcnt<0>();
     }
-    __syncthreads();
+    wg_barrier();
     const MLA_LDS char* tile = smem + (it % NS) * LT::BYTES;
     const long long r0 = lo + (long long)it * LT::KT;
     const long long r1 = min(r0 + LT::KT, hi);
@@ -172,12 +172,14 @@ mla_decode_split(DecodeSplitArgs a) {
       if (compute && a0 < a1) {
         f32x4 sa, sb;
         st.scores(tile, sa, sb);
-        if (a0 > r0 || a1 < r0 + LT::KT) {
+        // visible keys of this tile, as tile-relative offsets [k_lo, k_hi)
+        const int k_lo = (int)(a0 - r0), k_hi = (int)(a1 - r0);
+        if (k_lo > 0 || k_hi < LT::KT) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const long long ka = r0 + 4 * kq + e, kb = ka + 16;
-            if (ka < a0 || ka >= a1) sa[e] = -INFINITY;
-            if (kb < a0 || kb >= a1) sb[e] = -INFINITY;
+            const int ka = 4 * kq + e, kb = ka + 16;
+            if (ka < k_lo || ka >= k_hi) sa[e] = -INFINITY;
+            if (kb < k_lo || kb >= k_hi) sb[e] = -INFINITY;
           }
         }
         st.update(tile, sa, sb);
@@ -199,6 +201,8 @@ mla_decode_split(DecodeSplitArgs a) {
         }
       }
       if (seq_end >= hi || i + 1 >= a.B) break;  // range finished
+      // keep the next sequence's query loads after the partial stores
+      __builtin_amdgcn_sched_barrier(0);
       ++i;
       seq_lo = seq_end;
       seq_end = a.cu[i + 1];
@@ -206,7 +210,7 @@ mla_decode_split(DecodeSplitArgs a) {
       st.reset();
       if (seq_lo >= r1) break;  // the next sequence starts in a later tile
     }
-    __syncthreads();
+    wg_barrier();
   }
 }
 

@@ -96,7 +96,7 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
     } else {
       wait_vmcnt<0>();
     }
-    __syncthreads();
+    wg_barrier();
     const MLA_LDS char* tile = smem + (it & 1) * LT::BYTES;
     const int s0 = it * LT::KT;
     f32x4 sa, sb;
@@ -109,7 +109,7 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
       }
     }
     st.update(tile, sa, sb);
-    __syncthreads();  // this stage is refilled by the next iteration
+    wg_barrier();  // this stage is refilled by the next iteration
   }
 
   const float inv_l = 1.0f / col_sum(st.l_run);
