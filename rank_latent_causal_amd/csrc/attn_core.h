@@ -111,13 +111,13 @@ template <int R, int QCH = 4, int VCH = 8>
 struct WaveAttn {
   static constexpr int NKK = R / 32;
   static constexpr int NJT = R / 16;
-  // The swizzle f(s) = 2 (s & 7) | ((s >> 3) & 1) only permutes the low 4
-  // bits of a chunk index, so for R >= 128 every operand address is one
-  // per-lane base plus a small XOR term and an immediate:
+  // The swizzle f(s) only permutes the low 4 bits of a chunk index, so for
+  // R >= 128 every operand address is one per-lane base plus a small XOR term
+  // and an immediate:
   //  * score operand, row l16, chunk 4kk + kq:  with x = f(l16)
   //      16 ((kq ^ x) & 3) + 64 ((kk & 3) ^ (x >> 2)) + 256 (kk >> 2)
-  //  * value operand, row r = 4kq + l16/4, chunk 2t + (l16%4)/2:
-  //      16 (((l16%4)/2) ^ ((r >> 3) & 1)) + 32 ((t & 7) ^ (r & 7)) + 256 (t >> 3)
+  //  * value operand, row r = 4kq + l16/4, chunk 2t + (l16%4)/2: x = f(r)
+  //      16 (((l16%4)/2) ^ (x & 1)) + 32 ((t & 7) ^ (x >> 1)) + 256 (t >> 3)
   // Smaller r keeps one precomputed base per k-step / value tile.
   static constexpr bool XORADDR = (R / 8 >= 16);
   static constexpr int NQB = XORADDR ? 1 : NKK;
@@ -136,8 +136,9 @@ struct WaveAttn {
       const int x = chunk_swizzle<R>(l16);
       qk_base[0] = l16 * ROWB + (((kq ^ x) & 3) << 4);
       qk_x = x >> 2;
-      tr_base[0] = r * ROWB + ((((q >> 1) ^ ((r >> 3) & 1))) << 4) + (q & 1) * 8;
-      tr_rx = r & 7;
+      const int xr = chunk_swizzle<R>(r);
+      tr_base[0] = r * ROWB + ((((q >> 1) ^ (xr & 1))) << 4) + (q & 1) * 8;
+      tr_rx = xr >> 1;
     } else {
 #pragma unroll
       for (int u = 0; u < NQB; ++u) qk_base[u] = tile_off<R>(l16, 4 * u + kq);

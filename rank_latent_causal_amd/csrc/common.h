@@ -27,14 +27,16 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 }
 
 // XOR swizzle of the 16-byte chunks of a latent row held in LDS.  It keeps
-// both access patterns of a 32-row tile free of bank conflicts:
+// both access patterns of a 32-row tile free of bank conflicts (measured with
+// the LDS bank-conflict counter on gfx950, where simpler row XORs leave one
+// or the other pattern 2-way conflicted):
 //  * ds_read_b128 of one chunk from 16 consecutive rows (score operand), and
-//  * ds_read_b64_tr_b16 of 8 consecutive rows x 2 chunks per 32 lanes
-//    (value operand, both 8-byte halves of each chunk).
+//  * ds_read_b64_tr_b16 of 4 rows x 2 chunks per 16-lane group (value
+//    operand, both 8-byte halves of each chunk).
 template <int R>
 __device__ __host__ __forceinline__ constexpr int chunk_swizzle(int s) {
   if constexpr (R / 8 >= 16) {
-    return ((s & 7) << 1) | ((s >> 3) & 1);
+    return (s & 8) ^ ((s & 7) << 1) ^ ((s >> 3) & 1);
   } else if constexpr (R / 8 == 4) {
     return (((s >> 2) & 1) << 1) | ((s >> 3) & 1);
   } else {
