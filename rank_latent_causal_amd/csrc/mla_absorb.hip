@@ -137,7 +137,7 @@ mla_status mla_absorb_prefill(const void* q, const void* c, const void* w_uk, co
   const size_t need = mla_absorb_prefill_workspace_size(B, T, H, d_q, r, dtype);
   if (!workspace || !aligned16(workspace)) return need ? MLA_ERR_WORKSPACE : MLA_ERR_INVALID_ARG;
   if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
-  const long long ntb = (T + 31) / 32, nhg = (H + 3) / 4;
+  const long long ntb = (T + mla::kPrefillRows - 1) / mla::kPrefillRows, nhg = (H + 3) / 4;
   if ((long long)B * ntb * nhg >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
 
   bf16* wukT = (bf16*)workspace;

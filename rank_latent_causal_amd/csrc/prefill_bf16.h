@@ -26,12 +26,14 @@ struct PrefillArgs {
   bf16* out;         // [B, T, H*DV]
   int B, T, H;
   float qscale;      // softmax scale * log2(e), folded into q_abs
-  int ntb;           // ceil(T / 32) query blocks
+  int ntb;           // ceil(T / kPrefillRows) query blocks
   int nhg;           // ceil(H / 4) head groups
   int xcd_remap;     // 1: head group hg runs on XCD hg % 8 (weights stay in its L2)
 };
 
-constexpr int kPrefillWaves = 8;
+// waves per workgroup: 4 heads x (kPrefillWaves / 4) blocks of 16 positions
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRows = 16 * (kPrefillWaves / 4);  // query positions per workgroup
 
 template <int DQ, int DV, int R>
 __global__ void __launch_bounds__(64 * kPrefillWaves)
@@ -64,19 +66,19 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, kq = lane >> 4;
-  const int hw = w & 3, th = w >> 2;
+  const int hw = w & 3, th = w >> 2;  // head in group, 16-row block
   const int h = hg * 4 + hw;
   const bool hvalid = h < a.H;
   const int hc = hvalid ? h : a.H - 1;
   const int T = a.T, H = a.H;
-  const int t0 = tb * 32;
+  const int t0 = tb * kPrefillRows;
   const int tw = t0 + 16 * th;  // first row of this wave
   const int t = tw + l16;       // this lane's query row
   const bool tvalid = t < T;
   const int tc = tvalid ? t : T - 1;
   const bf16* __restrict__ cb = a.c + (size_t)b * T * R;
 
-  const int ntiles = (min(t0 + 32, T) + LT::KT - 1) / LT::KT;
+  const int ntiles = (min(t0 + kPrefillRows, T) + LT::KT - 1) / LT::KT;
 
   // stream the first latent tile while the absorb prologue runs
   TileCopier<R, kPrefillWaves> copier;
