@@ -38,9 +38,10 @@ constexpr int copies_per_wave(int nwaves) {
 // buffer loads.  Copy qi (1 KiB of LDS, rows qi*RPI .. of the tile) is issued
 // by wave qi % NW, so each wave issues either copies_per_wave(NW) copies or
 // none.  Each copy gets its own scalar descriptor starting at its first row,
-// so rows at or past row_end read as zeros (their scores are masked) and the
-// per-lane offsets are small; they are recomputed from the lane id for every
-// tile instead of being kept live across the main loop.
+// so rows at or past row_end read as zeros (their scores are masked).  The
+// swizzle is XOR-linear in the row bits and a copy's first row is a multiple
+// of its row count, so a lane's offset is a fixed per-lane base XOR a
+// wave-uniform term: one VALU op per copy, the rest is scalar.
 template <int R, int NW>
 struct TileCopier {
   static constexpr int COPIES = LatentTile<R>::COPIES;
@@ -49,23 +50,26 @@ struct TileCopier {
   static constexpr int RPI = 64 / CPR;    // rows per copy
   static_assert(64 % CPR == 0, "a copy covers whole rows");
   int w;
+  unsigned lane_base;
 
-  __device__ __forceinline__ void init(int wave, int) { w = wave; }
+  __device__ __forceinline__ void init(int wave, int lane) {
+    w = wave;
+    const int sl = lane / CPR;
+    lane_base = (unsigned)((sl * R + (((lane % CPR) ^ chunk_swizzle<R>(sl)) * 8)) * 2);
+  }
 
-  __device__ __forceinline__ void issue(const bf16* __restrict__ base, long long row0, long long row_end,
+  __device__ __forceinline__ void issue(const bf16* __restrict__ base, int row0, int row_end,
                                         MLA_LDS char* stage) const {
-    int l = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    asm volatile("" : "+v"(l));  // opaque: keeps the offset math inside the loop
+    unsigned lb = lane_base;
+    asm volatile("" : "+v"(lb));  // one live base; the per-copy XORs are formed here, not hoisted
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int qi = w + NW * c;
       if (qi < COPIES) {
         const int srow = qi * RPI;
-        const int s = srow + l / CPR;
-        const int L = (l % CPR) ^ chunk_swizzle<R>(s);
-        const unsigned voff = (unsigned)(((l / CPR) * R + L * 8) * 2);
-        const long long first = row0 + srow;
-        long long rows = row_end - first;
+        const unsigned voff = lb ^ (unsigned)(chunk_swizzle<R>(srow) << 4);
+        const int first = row0 + srow;
+        int rows = row_end - first;
         rows = rows < 0 ? 0 : (rows > RPI ? RPI : rows);
         buf2lds16(make_rsrc(base + (size_t)first * R, (unsigned)(rows * R * 2)), voff, stage + qi * 1024);
       }
@@ -268,5 +272,168 @@ __device__ __forceinline__ void project_gate_store(const f32x4 (&oT)[R / 16], fl
     }
   }
 }
+
+}  // namespace mla
+
+namespace mla {
+
+// ---------------------------------------------------------------------------
+// Wave-pair variant: two waves share 32 query columns (two 16-column groups)
+// and split the latent dimension r in halves.  Each latent operand read from
+// LDS then feeds two MFMAs (one per column group), halving LDS traffic per
+// FLOP, while each wave still holds only a [r/2 x 32] O^T accumulator.  The
+// score needs the full r, so the pair adds its two partial S^T tiles through
+// LDS once per key tile; both waves then run the same softmax.
+// ---------------------------------------------------------------------------
+
+// q_abs^T for two 16-row column groups, latent dims [jbase, jbase + R/2).
+template <int DQ, int R>
+__device__ __forceinline__ void absorb_pair(const bf16* __restrict__ qrow0, const bf16* __restrict__ qrow1,
+                                            const bf16* __restrict__ wkT, int jbase, float qscale, int l16,
+                                            int kq, bf16x8 (&qT)[2][R / 64]) {
+  constexpr int NKQ = (DQ + 31) / 32;
+  bf16x8 qb[2][NKQ];
+#pragma unroll
+  for (int k = 0; k < NKQ; ++k) {
+    const bool ok = 32 * k + 8 * kq < DQ;
+    qb[0][k] = ok ? *(const bf16x8*)(qrow0 + 32 * k + 8 * kq) : bf16x8{};
+    qb[1][k] = ok ? *(const bf16x8*)(qrow1 + 32 * k + 8 * kq) : bf16x8{};
+  }
+#pragma unroll
+  for (int kk = 0; kk < R / 64; ++kk) {
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      // A row rho loads latent dim jbase + 32kk + 8(rho/4) + 4u + rho%4, so C
+      // row 4kq + e of this fragment is dim jbase + 32kk + 8kq + 4u + e
+      const int j = jbase + 32 * kk + 8 * (l16 >> 2) + 4 * u + (l16 & 3);
+      const bf16* wrow = wkT + (size_t)j * DQ;
+      acc[0][u] = f32x4{};
+      acc[1][u] = f32x4{};
+#pragma unroll
+      for (int k = 0; k < NKQ; ++k) {
+        const bf16x8 av = (32 * k + 8 * kq < DQ) ? *(const bf16x8*)(wrow + 32 * k + 8 * kq) : bf16x8{};
+        acc[0][u] = mfma16(av, qb[0][k], acc[0][u]);
+        acc[1][u] = mfma16(av, qb[1][k], acc[1][u]);
+      }
+    }
+    qT[0][kk] = pack44(acc[0][0], acc[0][1], qscale);
+    qT[1][kk] = pack44(acc[1][0], acc[1][1], qscale);
+  }
+}
+
+template <int R, int QCH = 1, int VCH = 4>
+struct PairAttn {
+  static constexpr int RH = R / 2;     // latent dims owned by this wave
+  static constexpr int NKK = RH / 32;  // score k-steps
+  static constexpr int NJT = RH / 16;  // value tiles
+  static constexpr int ROWB = R * 2;
+  static_assert(R / 8 >= 16 && NKK % 4 == 0 && NJT % 8 == 0, "pair split needs r >= 256");
+  bf16x8 qT[2][NKK];
+  f32x4 oT[2][NJT];
+  float m_run[2], l_run[2];
+  // Operand addresses (latent half folded in): the score operand of k-step kk
+  // is qkb[kk & 3] + 256 (kk >> 2), the value operand of tile t is
+  // trb[t & 7] + 256 (t >> 3); the immediates fold into the ds_read offsets.
+  int qkb[4], trb[8];
+
+  __device__ __forceinline__ void init_addressing(int l16, int kq, int jh) {
+    const int x = chunk_swizzle<R>(l16);
+    const int qk_base = l16 * ROWB + (((kq ^ x) & 3) << 4) + jh * RH * 2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qkb[u] = qk_base + ((u ^ (x >> 2)) << 6);
+    const int r = 4 * kq + (l16 >> 2), q = l16 & 3;
+    const int xr = chunk_swizzle<R>(r);
+    const int tr_base = r * ROWB + (((q >> 1) ^ (xr & 1)) << 4) + (q & 1) * 8 + jh * RH * 2;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) trb[u] = tr_base + ((u ^ (xr >> 1)) << 5);
+  }
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int t = 0; t < NJT; ++t) oT[c][t] = f32x4{};
+      m_run[c] = -INFINITY;
+      l_run[c] = 0.0f;
+    }
+  }
+
+  // Partial S^T over this wave's latent half: s[cg][u] holds keys
+  // [16u, 16u+16) of the tile for column group cg.
+  __device__ __forceinline__ void partial_scores(const MLA_LDS char* tile, f32x4 (&s)[2][2]) const {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) s[c][0] = s[c][1] = f32x4{};
+    int b0 = qkb[0], b1 = qkb[1], b2 = qkb[2], b3 = qkb[3];
+    asm volatile("" : "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3));  // keep 4 bases, not 16 sums
+    const int bq[4] = {b0, b1, b2, b3};
+#pragma unroll
+    for (int k0 = 0; k0 < NKK; k0 += QCH) {
+#pragma unroll
+      for (int kk = k0; kk < k0 + QCH; ++kk) {
+        const MLA_LDS char* p = tile + bq[kk & 3] + (kk >> 2) * 256;
+        const bf16x8 a0 = lds_read_b128(p);
+        const bf16x8 a1 = lds_read_b128(p + 16 * ROWB);
+        s[0][0] = mfma16(a0, qT[0][kk], s[0][0]);
+        s[1][0] = mfma16(a0, qT[1][kk], s[1][0]);
+        s[0][1] = mfma16(a1, qT[0][kk], s[0][1]);
+        s[1][1] = mfma16(a1, qT[1][kk], s[1][1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Online softmax of both column groups over the full (masked, log2-domain)
+  // scores, then the value accumulation of this wave's latent half.
+  __device__ __forceinline__ void update(const MLA_LDS char* tile, const f32x4 (&s)[2][2]) {
+    float mx[2];
+    bool need[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const f32x4& a = s[c][0];
+      const f32x4& b = s[c][1];
+      mx[c] = col_max(fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3]))));
+      need[c] = mx[c] > m_run[c] + 8.0f;
+    }
+    if (__builtin_amdgcn_ballot_w64(need[0] || need[1])) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float m_new = need[c] ? mx[c] : m_run[c];
+        const float alpha = fast_exp2(m_run[c] - m_new);
+        l_run[c] *= alpha;
+#pragma unroll
+        for (int t = 0; t < NJT; ++t) oT[c][t] *= alpha;
+        m_run[c] = m_new;
+      }
+    }
+    bf16x8 pB[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      f32x4 p0, p1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p0[e] = fast_exp2(s[c][0][e] - m_run[c]);
+        p1[e] = fast_exp2(s[c][1][e] - m_run[c]);
+      }
+      l_run[c] += (p0[0] + p0[1]) + (p0[2] + p0[3]) + (p1[0] + p1[1]) + (p1[2] + p1[3]);
+      pB[c] = pack44(p0, p1, 1.0f);
+    }
+    int t0_ = trb[0], t1_ = trb[1], t2_ = trb[2], t3_ = trb[3], t4_ = trb[4], t5_ = trb[5], t6_ = trb[6],
+        t7_ = trb[7];
+    asm volatile("" : "+v"(t0_), "+v"(t1_), "+v"(t2_), "+v"(t3_), "+v"(t4_), "+v"(t5_), "+v"(t6_), "+v"(t7_));
+    const int bt[8] = {t0_, t1_, t2_, t3_, t4_, t5_, t6_, t7_};
+#pragma unroll
+    for (int t0 = 0; t0 < NJT; t0 += VCH) {
+#pragma unroll
+      for (int t = t0; t < t0 + VCH; ++t) {
+        const MLA_LDS char* p = tile + bt[t & 7] + (t >> 3) * 256;
+        const bf16x8 a = cat4(lds_read_tr16(p), lds_read_tr16(p + 16 * ROWB));
+        oT[0][t] = mfma16(a, pB[0], oT[0][t]);
+        oT[1][t] = mfma16(a, pB[1], oT[1][t]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
 
 }  // namespace mla

@@ -97,6 +97,12 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS writes have landed (before a barrier
+// that publishes them to the other waves).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
 // s_waitcnt vmcnt(N) leaving the other counters untouched (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

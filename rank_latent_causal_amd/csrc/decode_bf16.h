@@ -136,7 +136,7 @@ mla_decode_split(DecodeSplitArgs a) {
   copier.init(w, lane);
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
-    if (p < ntiles) copier.issue(a.cache, lo + (long long)p * LT::KT, hi, smem + p * LT::BYTES);
+    if (p < ntiles) copier.issue(a.cache, (int)(lo + p * LT::KT), (int)hi, smem + p * LT::BYTES);
 
   WaveAttn<R> st;
   auto load_q = [&](int seq) {
@@ -151,7 +151,7 @@ mla_decode_split(DecodeSplitArgs a) {
   for (int it = 0; it < ntiles; ++it) {
     const int nx = it + NS - 1;
     if (nx < ntiles) {
-      copier.issue(a.cache, lo + (long long)nx * LT::KT, hi, smem + (nx % NS) * LT::BYTES);
+      copier.issue(a.cache, (int)(lo + (long long)nx * LT::KT), (int)hi, smem + (nx % NS) * LT::BYTES);
       wait_vmcnt<(NS - 1) * LPW>();
     } else if (nx == ntiles) {
       wait_vmcnt<(NS - 2) * LPW>();

@@ -67,9 +67,22 @@ DecodeLayout decode_layout(int B, int H, int dq, int r, int G) {
   return L;
 }
 
+// r = 32: one wave per (head, 16 positions); r >= 256: wave pairs split r.
 template <int DQ, int DV, int R>
-void launch_prefill_bf16(const mla::PrefillArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((mla::mla_prefill_bf16_kernel<DQ, DV, R>), dim3(a.B * a.ntb * a.nhg), dim3(64 * mla::kPrefillWaves), 0, s, a);
+void launch_prefill_bf16(mla::PrefillArgs a, hipStream_t s) {
+  if constexpr (R >= 256) {
+    a.ntb = (a.T + 31) / 32;
+    a.nhg = (a.H + 1) / 2;
+    a.xcd_remap = (a.nhg % 8) == 0 ? 1 : 0;
+    hipLaunchKernelGGL((mla::mla_prefill_pair_kernel<DQ, DV, R>), dim3(a.B * a.ntb * a.nhg),
+                       dim3(64 * mla::kPairWaves), 0, s, a);
+  } else {
+    a.ntb = (a.T + mla::kPrefillRows - 1) / mla::kPrefillRows;
+    a.nhg = (a.H + 3) / 4;
+    a.xcd_remap = (a.nhg % 8) == 0 ? 1 : 0;
+    hipLaunchKernelGGL((mla::mla_prefill_bf16_kernel<DQ, DV, R>), dim3(a.B * a.ntb * a.nhg),
+                       dim3(64 * mla::kPrefillWaves), 0, s, a);
+  }
 }
 
 template <int DQ, int DV, int R>
@@ -137,8 +150,8 @@ mla_status mla_absorb_prefill(const void* q, const void* c, const void* w_uk, co
   const size_t need = mla_absorb_prefill_workspace_size(B, T, H, d_q, r, dtype);
   if (!workspace || !aligned16(workspace)) return need ? MLA_ERR_WORKSPACE : MLA_ERR_INVALID_ARG;
   if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
-  const long long ntb = (T + mla::kPrefillRows - 1) / mla::kPrefillRows, nhg = (H + 3) / 4;
-  if ((long long)B * ntb * nhg >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
+  // grid bound for the smaller of the two workgroup shapes (16 positions x 4 heads)
+  if ((long long)B * ((T + 15) / 16) * ((H + 1) / 2) >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
 
   bf16* wukT = (bf16*)workspace;
   launch_wuk_transpose((const bf16*)w_uk, wukT, H, d_q, r, s);
@@ -148,8 +161,6 @@ mla_status mla_absorb_prefill(const void* q, const void* c, const void* w_uk, co
   a.gate = (const bf16*)gate; a.out = (bf16*)out;
   a.B = B; a.T = T; a.H = H;
   a.qscale = scale * mla::kLog2e;
-  a.ntb = (int)ntb; a.nhg = (int)nhg;
-  a.xcd_remap = (nhg % 8) == 0 ? 1 : 0;
   if (d_q == 16) launch_prefill_bf16<16, 16, 32>(a, s);
   else if (d_q == 64) launch_prefill_bf16<64, 64, 256>(a, s);
   else launch_prefill_bf16<128, 128, 512>(a, s);

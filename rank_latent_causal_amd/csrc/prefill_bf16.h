@@ -93,7 +93,7 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
 
   for (int it = 0; it < ntiles; ++it) {
     if (it + 1 < ntiles) {
-      copier.issue(cb, (long long)(it + 1) * LT::KT, T, smem + ((it + 1) & 1) * LT::BYTES);
+      copier.issue(cb, (it + 1) * LT::KT, T, smem + ((it + 1) & 1) * LT::BYTES);
       wait_vmcnt<LPW>();
     } else {
       wait_vmcnt<0>();
@@ -118,6 +118,163 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
   const size_t orow = ((size_t)b * T + tc) * (size_t)H * DV + (size_t)hc * DV;
   project_gate_store<DV, R>(st.oT, inv_l, a.wuv + (size_t)hc * DV * R, a.gate + orow, a.out + orow,
                             tvalid && hvalid, l16, kq);
+}
+
+// ---------------------------------------------------------------------------
+// Wave-pair prefill for r >= 256: one workgroup = 4 waves = 2 heads x a block
+// of 32 positions.  Waves (2p, 2p+1) serve head 2hg + p, both 16-row column
+// groups, and latent halves 0 / 1.  Per 32-key tile: partial scores over the
+// wave's half, exchange through LDS, full causal softmax (identical in both
+// waves), values of the wave's half.  The epilogue adds the two halves' W_UV
+// products through LDS before the gate.
+// ---------------------------------------------------------------------------
+constexpr int kPairWaves = 4;
+
+template <int DQ, int DV, int R>
+__global__ void __launch_bounds__(64 * kPairWaves)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+mla_prefill_pair_kernel(PrefillArgs a) {
+  using LT = LatentTile<R>;
+  using PA = PairAttn<R>;
+  constexpr int NS = 2;
+  constexpr int LPW = copies_per_wave<R>(kPairWaves);
+  constexpr int NV = DV / 16;
+  static_assert(LT::COPIES % kPairWaves == 0, "copy split");
+  static_assert(DQ % 16 == 0 && DV % 16 == 0, "shape");
+  // epilogue partials of o^T reuse the stage memory
+  static_assert(kPairWaves * NV * 2 * 1024 <= NS * LT::BYTES, "epilogue exchange fits the stages");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * LT::BYTES];
+  __shared__ __attribute__((aligned(16))) f32x4 xbuf[kPairWaves][4][64];  // partial scores
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+
+  // ---- work item (32 positions x 2 heads), heaviest query blocks first
+  const int x = blockIdx.x;
+  int tb, b, hg;
+  if (a.xcd_remap) {
+    const int xcd = x & 7, pos = x >> 3, nh8 = a.nhg >> 3;
+    hg = (pos % nh8) * 8 + xcd;
+    const int rest = pos / nh8;
+    b = rest % a.B;
+    tb = a.ntb - 1 - rest / a.B;
+  } else {
+    hg = x % a.nhg;
+    const int rest = x / a.nhg;
+    b = rest % a.B;
+    tb = a.ntb - 1 - rest / a.B;
+  }
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int jh = w & 1, partner = w ^ 1;
+  const int h = hg * 2 + (w >> 1);
+  const bool hvalid = h < a.H;
+  const int hc = hvalid ? h : a.H - 1;
+  const int T = a.T, H = a.H;
+  const int t0 = tb * 32;
+  int tq[2];
+  bool tv[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    tq[c] = t0 + 16 * c + l16;
+    tv[c] = tq[c] < T;
+  }
+  const bf16* __restrict__ cb = a.c + (size_t)b * T * R;
+  const int ntiles = (min(t0 + 32, T) + LT::KT - 1) / LT::KT;
+
+  TileCopier<R, kPairWaves> copier;
+  copier.init(w, lane);
+  copier.issue(cb, 0, T, smem);
+
+  PA st;
+  {
+    const size_t q0 = (((size_t)b * T + (tv[0] ? tq[0] : T - 1)) * H + hc) * DQ;
+    const size_t q1 = (((size_t)b * T + (tv[1] ? tq[1] : T - 1)) * H + hc) * DQ;
+    absorb_pair<DQ, R>(a.q + q0, a.q + q1, a.wukT + (size_t)hc * R * DQ, jh * PA::RH, a.qscale, l16, kq, st.qT);
+  }
+  st.reset();
+  st.init_addressing(l16, kq, jh);
+
+  for (int it = 0; it < ntiles; ++it) {
+    wait_vmcnt<0>();  // this wave's copies of tile `it`
+    wg_barrier();     // tile visible; iteration it-1 finished (its stage and xbuf are free)
+    if (it + 1 < ntiles)
+      copier.issue(cb, (it + 1) * LT::KT, T, smem + ((it + 1) & 1) * LT::BYTES);
+    const MLA_LDS char* tile = smem + (it & 1) * LT::BYTES;
+
+    f32x4 sc[2][2];
+    st.partial_scores(tile, sc);
+    xbuf[w][0][lane] = sc[0][0];
+    xbuf[w][1][lane] = sc[0][1];
+    xbuf[w][2][lane] = sc[1][0];
+    xbuf[w][3][lane] = sc[1][1];
+    wait_lgkmcnt0();
+    wg_barrier();  // partial scores of both halves visible
+    {
+      const f32x4 o00 = xbuf[partner][0][lane], o01 = xbuf[partner][1][lane];
+      const f32x4 o10 = xbuf[partner][2][lane], o11 = xbuf[partner][3][lane];
+      // add in a fixed order (half 0 + half 1) so both waves get identical sums
+      if (jh == 0) {
+        sc[0][0] += o00; sc[0][1] += o01; sc[1][0] += o10; sc[1][1] += o11;
+      } else {
+        sc[0][0] = o00 + sc[0][0]; sc[0][1] = o01 + sc[0][1];
+        sc[1][0] = o10 + sc[1][0]; sc[1][1] = o11 + sc[1][1];
+      }
+    }
+    const int s0 = it * LT::KT;
+    if (s0 + LT::KT - 1 > t0) {  // causal mask on the diagonal tile (also hides keys past T)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (s0 + 4 * kq + e > tq[c]) sc[c][0][e] = -INFINITY;
+          if (s0 + 16 + 4 * kq + e > tq[c]) sc[c][1][e] = -INFINITY;
+        }
+      }
+    }
+    st.update(tile, sc);
+  }
+
+  // ---- epilogue: partial o^T = W_UV[h][:, half] (O^T_half / l), summed by the pair
+  bf16x8 ob[2][PA::NKK];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const float inv_l = 1.0f / col_sum(st.l_run[c]);
+#pragma unroll
+    for (int kk = 0; kk < PA::NKK; ++kk) ob[c][kk] = pack44(st.oT[c][2 * kk], st.oT[c][2 * kk + 1], inv_l);
+  }
+  wg_barrier();  // every wave is done with the stages: reuse them for the o^T partials
+  f32x4* obuf = (f32x4*)smem_raw;  // [wave][vt][cg][lane]
+  const bf16* wv = a.wuv + (size_t)hc * DV * R + jh * PA::RH;
+#pragma unroll
+  for (int vt = 0; vt < NV; ++vt) {
+    const bf16* wrow = wv + (size_t)(16 * vt + l16) * R + 4 * kq;
+    f32x4 acc0 = f32x4{}, acc1 = f32x4{};
+#pragma unroll
+    for (int kk = 0; kk < PA::NKK; ++kk) {
+      const bf16x8 av = cat4(*(const bf16x4*)(wrow + 32 * kk), *(const bf16x4*)(wrow + 32 * kk + 16));
+      acc0 = mfma16(av, ob[0][kk], acc0);
+      acc1 = mfma16(av, ob[1][kk], acc1);
+    }
+    obuf[((w * NV + vt) * 2 + 0) * 64 + lane] = acc0;
+    obuf[((w * NV + vt) * 2 + 1) * 64 + lane] = acc1;
+  }
+  wait_lgkmcnt0();
+  wg_barrier();
+  const int w0 = w & ~1, w1 = w0 + 1;  // half 0 and half 1 of this pair
+  for (int vt = jh; vt < NV; vt += 2) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const f32x4 o = obuf[((w0 * NV + vt) * 2 + c) * 64 + lane] + obuf[((w1 * NV + vt) * 2 + c) * 64 + lane];
+      if (tv[c] && hvalid) {
+        const size_t orow = ((size_t)b * T + tq[c]) * (size_t)H * DV + (size_t)h * DV + 16 * vt + 4 * kq;
+        const bf16x4 gv = *(const bf16x4*)(a.gate + orow);
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(o[e] * sigmoidf_((float)gv[e]));
+        *(bf16x4*)(a.out + orow) = ov;
+      }
+    }
+  }
 }
 
 }  // namespace mla
