@@ -89,7 +89,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--which", choices=["both", "prefill", "decode"], default="both")
@@ -181,7 +181,7 @@ def main():
     if do_pre:
         res["roofline"] = {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                           "kernel": "mla_prefill_bf16_kernel<128,128,512>", "flop_per_launch": pf,
+                           "kernel": "mla_prefill_pair_kernel<128,128,512> (+ W_UK transpose in the same call)", "flop_per_launch": pf,
                            "ms_per_launch": round(p_ms, 4)}
     if do_dec:
         res["decode"] = {"value": round(d_gbs, 1), "unit": "GB/s", "ms": round(d_ms, 4),

@@ -37,17 +37,19 @@ constexpr int copies_per_wave(int nwaves) {
 // Copies latent rows [row0, row0 + 32) into a swizzled LDS tile with raw
 // buffer loads.  Copy qi (1 KiB of LDS, rows qi*RPI .. of the tile) is issued
 // by wave qi % NW, so each wave issues either copies_per_wave(NW) copies or
-// none.  Each copy gets its own scalar descriptor starting at its first row,
-// so rows at or past row_end read as zeros (their scores are masked).  The
-// swizzle is XOR-linear in the row bits and a copy's first row is a multiple
-// of its row count, so a lane's offset is a fixed per-lane base XOR a
-// wave-uniform term: one VALU op per copy, the rest is scalar.
+// none.  One scalar descriptor covers the tile's valid rows, so rows at or
+// past row_end read as zeros (their scores are masked).  The swizzle is
+// XOR-linear in the row bits and a copy's first row is a multiple of its row
+// count, so a lane's byte offset is a fixed per-lane base XOR a wave-uniform
+// constant (swizzle term and row offset occupy disjoint bits): one VALU op
+// per copy.
 template <int R, int NW>
 struct TileCopier {
   static constexpr int COPIES = LatentTile<R>::COPIES;
   static constexpr int CPW = copies_per_wave<R>(NW);
   static constexpr int CPR = R / 8;       // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;    // rows per copy
+  static constexpr int KT = LatentTile<R>::KT;
   static_assert(64 % CPR == 0, "a copy covers whole rows");
   int w;
   unsigned lane_base;
@@ -62,16 +64,16 @@ struct TileCopier {
                                         MLA_LDS char* stage) const {
     unsigned lb = lane_base;
     asm volatile("" : "+v"(lb));  // one live base; the per-copy XORs are formed here, not hoisted
+    int rows = row_end - row0;
+    rows = rows > KT ? KT : rows;
+    const u32x4 rs = make_rsrc(base + (size_t)row0 * R, (unsigned)(rows * R * 2));
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int qi = w + NW * c;
       if (qi < COPIES) {
         const int srow = qi * RPI;
-        const unsigned voff = lb ^ (unsigned)(chunk_swizzle<R>(srow) << 4);
-        const int first = row0 + srow;
-        int rows = row_end - first;
-        rows = rows < 0 ? 0 : (rows > RPI ? RPI : rows);
-        buf2lds16(make_rsrc(base + (size_t)first * R, (unsigned)(rows * R * 2)), voff, stage + qi * 1024);
+        const unsigned k = (unsigned)((chunk_swizzle<R>(srow) << 4) | (srow * R * 2));
+        buf2lds16(rs, lb ^ k, stage + qi * 1024);
       }
     }
   }
@@ -322,6 +324,8 @@ __device__ __forceinline__ void absorb_pair(const bf16* __restrict__ qrow0, cons
   }
 }
 
+// QCH / VCH: k-steps / value tiles per scheduling chunk (each chunk issues its
+// LDS reads, then its MFMAs; sched_barrier keeps chunks in order).
 template <int R, int QCH = 1, int VCH = 4>
 struct PairAttn {
   static constexpr int RH = R / 2;     // latent dims owned by this wave
@@ -384,8 +388,8 @@ struct PairAttn {
   }
 
   // Online softmax of both column groups over the full (masked, log2-domain)
-  // scores, then the value accumulation of this wave's latent half.
-  __device__ __forceinline__ void update(const MLA_LDS char* tile, const f32x4 (&s)[2][2]) {
+  // scores; returns P^T as the value product's B operands.
+  __device__ __forceinline__ void softmax(const f32x4 (&s)[2][2], bf16x8 (&pB)[2]) {
     float mx[2];
     bool need[2];
 #pragma unroll
@@ -406,7 +410,6 @@ struct PairAttn {
         m_run[c] = m_new;
       }
     }
-    bf16x8 pB[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       f32x4 p0, p1;
@@ -418,6 +421,10 @@ struct PairAttn {
       l_run[c] += (p0[0] + p0[1]) + (p0[2] + p0[3]) + (p1[0] + p1[1]) + (p1[2] + p1[3]);
       pB[c] = pack44(p0, p1, 1.0f);
     }
+  }
+
+  // Value accumulation of this wave's latent half: O^T += c_tile^T P^T.
+  __device__ __forceinline__ void values(const MLA_LDS char* tile, const bf16x8 (&pB)[2]) {
     int t0_ = trb[0], t1_ = trb[1], t2_ = trb[2], t3_ = trb[3], t4_ = trb[4], t5_ = trb[5], t6_ = trb[6],
         t7_ = trb[7];
     asm volatile("" : "+v"(t0_), "+v"(t1_), "+v"(t2_), "+v"(t3_), "+v"(t4_), "+v"(t5_), "+v"(t6_), "+v"(t7_));

@@ -65,24 +65,46 @@ __device__ __forceinline__ bf16x8 cat4(const bf16x4& lo, const bf16x4& hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Direct 16-byte global -> LDS copy: lane l's 16 bytes land at lds_base + 16*l
-// (lds_base must be wave-uniform).  Completion is tracked by vmcnt.
-__device__ __forceinline__ void g2lds16(const void* gptr, MLA_LDS char* lds_base) {
-  __builtin_amdgcn_global_load_lds(gptr, (MLA_LDS void*)lds_base, 16, 0, 0);
-}
-
-// Buffer descriptor over `bytes` bytes at `base` (gfx9 raw buffer: stride 0,
-// reads at or past `bytes` return zero).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+// Raw buffer descriptor (gfx9 layout) over `bytes` bytes at `base`: stride 0,
+// so a lane whose offset is at or past `bytes` reads zeros.  Held in SGPRs.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, unsigned bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4 r;
+  r[0] = (unsigned)a;
+  r[1] = (unsigned)(a >> 32) & 0xFFFFu;
+  r[2] = bytes;
+  r[3] = 0x00020000u;
+  return r;
 }
 
 // Direct 16-byte buffer -> LDS copy at byte offset voff: lane l's 16 bytes
 // land at lds_base + 16*l (lds_base wave-uniform); out-of-range lanes write
-// zeros.  Completion is tracked by vmcnt.
-__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t rs, unsigned voff, MLA_LDS char* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MLA_LDS void*)lds_base, 16, (int)voff, 0, 0, 0);
+// zeros.  Completion is tracked by vmcnt, and callers wait for it explicitly
+// with wait_vmcnt<N>() before the barrier that publishes a tile.
+//
+// The copy is issued from inline assembly on purpose.  When the compiler sees
+// an LDS-DMA load it cannot tell which LDS bytes it writes, so it puts
+// vmcnt(0) in front of the next LDS read of any address, which drains every
+// prefetch in flight and serialises the copy of tile n+1 with the reads of
+// tile n.  Hidden in assembly, the copy is ordered only by the explicit waits
+// and barriers of the pipeline (the memory clobber keeps the compiler from
+// moving LDS accesses across it).  M0 is written here, with the one wait
+// state the hardware needs between an M0 write and an LDS-DMA instruction.
+// (The compiler reserves M0 and warns about the clobber; no other code in
+// these kernels reads M0, since gfx9 LDS instructions do not use it.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void buf2lds16(const u32x4& rs, unsigned voff, MLA_LDS char* lds_base) {
+  const unsigned m0v = (unsigned)(uintptr_t)lds_base;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rs), "s"(m0v)
+      : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Workgroup barrier without a memory fence.  __syncthreads() also waits for
 // every outstanding global access (vmcnt(0)), which would drain the tile

@@ -134,17 +134,21 @@ mla_decode_split(DecodeSplitArgs a) {
 
   TileCopier<R, kDecodeWaves> copier;
   copier.init(w, lane);
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < ntiles) copier.issue(a.cache, (int)(lo + p * LT::KT), (int)hi, smem + p * LT::BYTES);
-
   WaveAttn<R> st;
   auto load_q = [&](int seq) {
     const bf16* src = a.qabs + ((size_t)seq * a.H + hc) * R + 8 * kq;
 #pragma unroll
     for (int kk = 0; kk < R / 32; ++kk) st.qT[kk] = *(const bf16x8*)(src + 32 * kk);
   };
+  // Tile 0 and the first query are needed first: wait for both before the
+  // other prefetches go out, so no query load is still pending when the loop
+  // starts (the loop's own waits then only track tile copies).
+  copier.issue(a.cache, (int)lo, (int)hi, smem);
   if (compute) load_q(i);
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int p = 1; p < NS - 1; ++p)
+    if (p < ntiles) copier.issue(a.cache, (int)(lo + p * LT::KT), (int)hi, smem + p * LT::BYTES);
   st.reset();
   st.init_addressing(l16, kq);
 
@@ -207,6 +211,11 @@ mla_decode_split(DecodeSplitArgs a) {
       seq_lo = seq_end;
       seq_end = a.cu[i + 1];
       if (compute) load_q(i);
+      // Take the wait for the new query here, where the switch happens.  Left
+      // pending, the loads stay on the compiler's books across the loop back
+      // edge, and it then counts vmcnt down to zero inside every later
+      // iteration's score products, draining the tile prefetches each time.
+      wait_vmcnt<0>();
       st.reset();
       if (seq_lo >= r1) break;  // the next sequence starts in a later tile
     }

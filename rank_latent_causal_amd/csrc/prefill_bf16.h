@@ -231,7 +231,9 @@ mla_prefill_pair_kernel(PrefillArgs a) {
         }
       }
     }
-    st.update(tile, sc);
+    bf16x8 pB[2];
+    st.softmax(sc, pB);
+    st.values(tile, pB);
   }
 
   // ---- epilogue: partial o^T = W_UV[h][:, half] (O^T_half / l), summed by the pair
