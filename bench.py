@@ -50,6 +50,51 @@ def decode_bytes(lengths, H, dq, dv, r, elt=2):
     return int(elt * r * int(np.sum(lengths)) + elt * H * r * (dq + dv) + elt * B * H * (dq + 2 * dv) + 4 * (B + 1))
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_full_prefill_full_decode.md")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources and the ABI header, in a fixed order: the
+    key under which measured HBM traffic is stored."""
+    import hashlib
+    h = hashlib.sha256()
+    files = []
+    for d in (os.path.join(ROOT, "rank_latent_causal_amd", "csrc"), os.path.join(ROOT, "include")):
+        files += [os.path.join(d, f) for f in sorted(os.listdir(d)) if f.endswith((".h", ".hip"))]
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    the summary was taken on other kernel sources than the current ones."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("traffic-record: "):
+                    rec = json.loads(line[len("traffic-record: "):])
+                    return rec if rec.get("sources") == kernel_source_hash() else None
+    except OSError:
+        return None
+    return None
+
+
+def copy_probe(nbytes: int = 1 << 30):
+    """One plain device-to-device copy of nbytes: the reference kernel whose
+    FETCH_SIZE / WRITE_SIZE readings scale the counters to bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"# copy probe: {nbytes} bytes device to device", file=sys.stderr, flush=True)
+
+
 def dev(x):
     import torch
     if x.dtype == np.uint16:
@@ -93,6 +138,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--which", choices=["both", "prefill", "decode"], default="both")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's hot path only (got --gpus {args.gpus}); multi-GPU runs are not "
@@ -190,6 +237,14 @@ def main():
                                       "unit": "GB/s", "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": None,
                                       "kernel": "mla_decode_split<512> + absorb + merge",
                                       "bytes_per_launch": dbytes}}
+    traffic = measured_traffic()
+    if traffic is not None:
+        if do_pre:
+            res["roofline"]["traffic"] = traffic["prefill_bytes"]
+        if do_dec:
+            res["decode"]["roofline"]["traffic"] = traffic["decode_bytes"]
+    if args.copy_probe:
+        copy_probe()
     if not args.no_cpu_baseline and do_pre:
         res["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -58,12 +58,11 @@ class Oracle:
         fp, dp, i64p = ct.POINTER(ct.c_float), ct.POINTER(ct.c_double), ct.POINTER(ct.c_int64)
         I, I64, D = ct.c_int, ct.c_int64, ct.c_double
         L.oracle_mutant.restype = I
-        L.oracle_qabs.argtypes = [fp, fp, I64, I, I, I, dp, I]
         L.oracle_prefill.argtypes = [fp, fp, fp, fp, fp, I, I, I, I, I, I, D, i64p, I64, dp, I]
         L.oracle_decode.argtypes = [fp, fp, i64p, fp, fp, fp, I, I, I, I, I, D, i64p, I64, dp, I]
         L.oracle_prefill_decompressed.argtypes = [fp, fp, fp, fp, fp, I, I, I, I, I, I, D, dp, I]
         L.oracle_prefill_attn.argtypes = [fp, fp, fp, I, I, I, I, I, D, dp]
-        for f in ("oracle_qabs", "oracle_prefill", "oracle_decode", "oracle_prefill_decompressed",
+        for f in ("oracle_prefill", "oracle_decode", "oracle_prefill_decompressed",
                   "oracle_prefill_attn"):
             getattr(L, f).restype = I
 
@@ -75,17 +74,6 @@ class Oracle:
     def _check(rc: int, what: str) -> None:
         if rc != 0:
             raise ValueError(f"{what} failed with code {rc}")
-
-    def qabs(self, q, w_uk, threads: int = 0) -> np.ndarray:
-        """Step 1 alone.  q [..., H, dq] -> q_abs [..., H, r] (float64)."""
-        q, w_uk = _f32(q), _f32(w_uk)
-        H, dq, r = w_uk.shape
-        assert q.shape[-2:] == (H, dq)
-        N = int(np.prod(q.shape[:-2], dtype=np.int64))
-        out = np.empty(q.shape[:-1] + (r,), dtype=np.float64)
-        self._check(self.lib.oracle_qabs(_ptr(q, ct.c_float), _ptr(w_uk, ct.c_float), N, H, dq, r,
-                                         _ptr(out, ct.c_double), threads), "oracle_qabs")
-        return out
 
     def prefill(self, q, c, w_uk, w_uv, gate, scale: float, rows=None, threads: int = 0) -> np.ndarray:
         """Prefill.  rows: flattened b*T+t indices (None: all).  Returns

@@ -55,7 +55,7 @@
 
 int oracle_mutant(void) { return ORACLE_MUTANT; }
 
-/* Step 1 alone: q_abs[n,h,j] = sum_d q[n,h,d] W_UK[h,d,j] for n < N rows. */
+/* Step 1 for one (row, head): qa[j] = sum_d q[d] W_UK[h,d,j]. */
 static void absorb_row(const float* qh, const float* wuk_h, int dq, int r, double* qa) {
   for (int j = 0; j < r; ++j) qa[j] = 0.0;
   for (int d = 0; d < dq; ++d) {
@@ -69,18 +69,6 @@ static void absorb_row(const float* qh, const float* wuk_h, int dq, int r, doubl
 #endif
     }
   }
-}
-
-int oracle_qabs(const float* q, const float* w_uk, int64_t N, int H, int dq, int r,
-                double* q_abs, int nthreads) {
-  if (!q || !w_uk || !q_abs || N < 0 || H <= 0 || dq <= 0 || r <= 0) return ORACLE_EINVAL;
-  if (nthreads <= 0) nthreads = omp_get_max_threads();
-#pragma omp parallel for schedule(static) num_threads(nthreads)
-  for (int64_t n = 0; n < N; ++n)
-    for (int h = 0; h < H; ++h)
-      absorb_row(q + (n * H + h) * dq, w_uk + (int64_t)h * dq * r, dq, r,
-                 q_abs + (n * H + h) * r);
-  return ORACLE_OK;
 }
 
 /*
