@@ -126,33 +126,37 @@ def pin_reduces_to_sdpa(o):
 
 
 # ---------------------------------------------------------------- P6
-def literal_forward(q, c, w_uk, w_uv, gate, scale):
-    """The forward listing's core written out with float64 CPU tensors and the
-    einsum contractions of the Einsum 速查 table: materialised [B,H,T,T]
-    scores, -inf above the diagonal, softmax over the key axis, latent
-    weighted sum, W_UV contraction, head-major flatten, sigmoid gate."""
-    import torch
-
-    q, c, w_uk, w_uv, gate = [torch.from_numpy(np.asarray(x, dtype=np.float64)) for x in (q, c, w_uk, w_uv, gate)]
+def dense_forward(q, c, w_uk, w_uv, gate, scale):
+    """Brute force on tiny shapes, written independently of the oracle: for
+    each (batch, head) the whole T x T weight matrix is formed at once from
+    the definition on page "Gated MLA（矩阵吸收版）", section 完整计算流（四步）
+    (absorbed query times latent, keys after the query get weight zero, rows
+    normalised), then applied to the latent and projected by W_UV; output
+    columns h*d_v .. h*d_v + d_v - 1 of each row are gated by the sigmoid."""
+    q, c, w_uk, w_uv, gate = [np.asarray(x, dtype=np.float64) for x in (q, c, w_uk, w_uv, gate)]
     B, T, H, _ = q.shape
     dv = w_uv.shape[1]
-    q_abs = torch.einsum("bthd,hdj->bthj", q, w_uk)
-    scores = torch.einsum("bthj,bsj->bhts", q_abs, c) * scale
-    future = torch.triu(torch.ones(T, T, dtype=torch.bool), diagonal=1)
-    attn = torch.softmax(scores.masked_fill(future, float("-inf")), dim=-1)
-    lat = torch.einsum("bhts,bsj->bhtj", attn, c)
-    o = torch.einsum("bhtj,hvj->bhtv", lat, w_uv)
-    o = o.transpose(1, 2).reshape(B, T, H * dv)
-    return (torch.sigmoid(gate) * o).numpy()
+    allowed = np.arange(T)[None, :] <= np.arange(T)[:, None]  # [query, key]
+    out = np.zeros((B, T, H * dv))
+    for b in range(B):
+        for h in range(H):
+            logits = scale * ((q[b, :, h, :] @ w_uk[h]) @ c[b].T)
+            top = np.where(allowed, logits, -np.inf).max(axis=1, keepdims=True)
+            e = np.where(allowed, np.exp(np.where(allowed, logits - top, 0.0)), 0.0)
+            weights = e / e.sum(axis=1, keepdims=True)
+            o = (weights @ c[b]) @ w_uv[h].T  # [T, dv]
+            cols = slice(h * dv, (h + 1) * dv)
+            out[b, :, cols] = o / (1.0 + np.exp(-gate[b, :, cols]))
+    return out
 
 
-def pin_literal_brute_force(o):
-    """Plain-loop oracle equals the materialised einsum form on tiny shapes."""
+def pin_dense_brute_force(o):
+    """Plain-loop oracle equals the dense per-(batch, head) brute force."""
     for (B, T, H, dq, dv, r, scale, seed) in [(2, 16, 3, 4, 2, 8, 0.7, 61), (1, 5, 2, 1, 3, 2, 1.9, 62),
                                               (2, 1, 1, 2, 2, 3, 1.0, 63)]:
         d = dg.prefill_inputs(B, T, H, dq, dv, r, dtype=dg.F32, seed=seed)
-        _close(o.prefill(*_args(d), scale), literal_forward(*_args(d), scale), 1e-12, 1e-14,
-               f"literal einsum B{B} T{T} H{H}")
+        _close(o.prefill(*_args(d), scale), dense_forward(*_args(d), scale), 1e-12, 1e-14,
+               f"dense brute force B{B} T{T} H{H}")
 
 
 # ---------------------------------------------------------------- P7
@@ -250,7 +254,7 @@ ALL_PINS = [
     pin_first_position_closed_form,
     pin_zero_scale_prefix_mean,
     pin_reduces_to_sdpa,
-    pin_literal_brute_force,
+    pin_dense_brute_force,
     pin_decode_is_last_prefill_row,
     pin_decode_closed_forms,
     pin_causality_and_independence,
