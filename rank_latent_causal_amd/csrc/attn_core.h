@@ -70,7 +70,7 @@ struct TileCopier {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int qi = w + NW * c;
-      if (qi < COPIES) {
+      if (COPIES % NW == 0 || qi < COPIES) {
         const int srow = qi * RPI;
         const unsigned k = (unsigned)((chunk_swizzle<R>(srow) << 4) | (srow * R * 2));
         buf2lds16(rs, lb ^ k, stage + qi * 1024);
@@ -203,8 +203,7 @@ struct WaveAttn {
   // the value accumulation.  The reference max only moves when a score
   // exceeds it by more than 8, so the O^T rescale is rare and P <= 2^8.
   __device__ __forceinline__ void update(const MLA_LDS char* tile, const f32x4& s0, const f32x4& s1) {
-    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+    float mx = max8_nn(s0, s1);
     mx = col_max(mx);
     const bool need = mx > m_run + 8.0f;
     if (__builtin_amdgcn_ballot_w64(need)) {
@@ -365,12 +364,14 @@ struct PairAttn {
 
   // Partial S^T over this wave's latent half: s[cg][u] holds keys
   // [16u, 16u+16) of the tile for column group cg.
-  __device__ __forceinline__ void partial_scores(const MLA_LDS char* tile, f32x4 (&s)[2][2]) const {
+  __device__ __forceinline__ void partial_scores(const MLA_LDS char* tile, f32x4 (&s)[2][2]) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) s[c][0] = s[c][1] = f32x4{};
-    int b0 = qkb[0], b1 = qkb[1], b2 = qkb[2], b3 = qkb[3];
-    asm volatile("" : "+v"(b0), "+v"(b1), "+v"(b2), "+v"(b3));  // keep 4 bases, not 16 sums
-    const int bq[4] = {b0, b1, b2, b3};
+    // Launder the 4 bases in place each tile: the compiler then cannot hoist
+    // 16 base + offset sums out of the loop (they would stay live and
+    // spill), and every address is one base plus a ds_read immediate.
+    asm volatile("" : "+v"(qkb[0]), "+v"(qkb[1]), "+v"(qkb[2]), "+v"(qkb[3]));
+    const int* bq = qkb;
 #pragma unroll
     for (int k0 = 0; k0 < NKK; k0 += QCH) {
 #pragma unroll
@@ -396,7 +397,7 @@ struct PairAttn {
     for (int c = 0; c < 2; ++c) {
       const f32x4& a = s[c][0];
       const f32x4& b = s[c][1];
-      mx[c] = col_max(fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(b[0], b[1]), fmaxf(b[2], b[3]))));
+      mx[c] = col_max(max8_nn(a, b));
       need[c] = mx[c] > m_run[c] + 8.0f;
     }
     if (__builtin_amdgcn_ballot_w64(need[0] || need[1])) {
@@ -425,10 +426,9 @@ struct PairAttn {
 
   // Value accumulation of this wave's latent half: O^T += c_tile^T P^T.
   __device__ __forceinline__ void values(const MLA_LDS char* tile, const bf16x8 (&pB)[2]) {
-    int t0_ = trb[0], t1_ = trb[1], t2_ = trb[2], t3_ = trb[3], t4_ = trb[4], t5_ = trb[5], t6_ = trb[6],
-        t7_ = trb[7];
-    asm volatile("" : "+v"(t0_), "+v"(t1_), "+v"(t2_), "+v"(t3_), "+v"(t4_), "+v"(t5_), "+v"(t6_), "+v"(t7_));
-    const int bt[8] = {t0_, t1_, t2_, t3_, t4_, t5_, t6_, t7_};
+    asm volatile("" : "+v"(trb[0]), "+v"(trb[1]), "+v"(trb[2]), "+v"(trb[3]), "+v"(trb[4]), "+v"(trb[5]),
+                      "+v"(trb[6]), "+v"(trb[7]));  // as in partial_scores
+    const int* bt = trb;
 #pragma unroll
     for (int t0 = 0; t0 < NJT; t0 += VCH) {
 #pragma unroll

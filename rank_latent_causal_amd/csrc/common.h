@@ -132,12 +132,31 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// max of finite-or-(-inf) floats as one v_max / v_max3.  fmaxf must quiet
+// signalling NaNs, so the compiler puts a canonicalising v_max x, x in front
+// of every operand it cannot prove canonical (MFMA and LDS results); scores
+// are never NaN, so the plain instruction gives the same value.
+__device__ __forceinline__ float max_nn(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_nn(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// max of the 8 values of two C fragments (never NaN)
+__device__ __forceinline__ float max8_nn(const f32x4& a, const f32x4& b) {
+  return max3_nn(max3_nn(a[0], a[1], a[2]), max3_nn(a[3], b[0], b[1]), max3_nn(b[2], b[3], -INFINITY));
+}
+
 // Value of x from the lane in the other half of the wave (l ^ 32) combined
 // with x itself, via v_permlane32_swap.
 __device__ __forceinline__ float xhalf_max(float x) {
   unsigned u = __builtin_bit_cast(unsigned, x);
   auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
+  return max_nn(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
   unsigned u = __builtin_bit_cast(unsigned, x);
@@ -145,11 +164,12 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
 }
 
-// Combine x over the four lanes l, l^16, l^32, l^48 (one MFMA column).
+// Combine x over the four lanes l, l^16, l^32, l^48 (one MFMA column);
+// col_max takes values that are never NaN.
 __device__ __forceinline__ float col_max(float x) {
   unsigned u = __builtin_bit_cast(unsigned, x);
   auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  x = fmaxf(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
+  x = max_nn(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
   return xhalf_max(x);
 }
 __device__ __forceinline__ float col_sum(float x) {

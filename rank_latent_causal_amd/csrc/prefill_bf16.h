@@ -13,6 +13,8 @@
 // one c tile.  Two LDS stages let the copy of tile n+1 overlap tile n.
 #pragma once
 
+#include <type_traits>
+
 #include "attn_core.h"
 
 namespace mla {
@@ -194,12 +196,14 @@ mla_prefill_pair_kernel(PrefillArgs a) {
   st.reset();
   st.init_addressing(l16, kq, jh);
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One key tile; STG (the LDS stage of tile `it`) is a compile-time
+  // constant so every operand address is a per-lane base plus an immediate.
+  auto tile_step = [&](int it, auto stage_tag) {
+    constexpr int STG = decltype(stage_tag)::value;
     wait_vmcnt<0>();  // this wave's copies of tile `it`
     wg_barrier();     // tile visible; iteration it-1 finished (its stage and xbuf are free)
-    if (it + 1 < ntiles)
-      copier.issue(cb, (it + 1) * LT::KT, T, smem + ((it + 1) & 1) * LT::BYTES);
-    const MLA_LDS char* tile = smem + (it & 1) * LT::BYTES;
+    if (it + 1 < ntiles) copier.issue(cb, (it + 1) * LT::KT, T, smem + (STG ^ 1) * LT::BYTES);
+    const MLA_LDS char* tile = smem + STG * LT::BYTES;
 
     f32x4 sc[2][2];
     st.partial_scores(tile, sc);
@@ -234,6 +238,10 @@ mla_prefill_pair_kernel(PrefillArgs a) {
     bf16x8 pB[2];
     st.softmax(sc, pB);
     st.values(tile, pB);
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    tile_step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntiles) tile_step(it + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- epilogue: partial o^T = W_UV[h][:, half] (O^T_half / l), summed by the pair
