@@ -60,22 +60,45 @@ struct TileCopier {
     lane_base = (unsigned)((sl * R + (((lane % CPR) ^ chunk_swizzle<R>(sl)) * 8)) * 2);
   }
 
-  __device__ __forceinline__ void issue(const bf16* __restrict__ base, int row0, int row_end,
-                                        MLA_LDS char* stage) const {
-    unsigned lb = lane_base;
-    asm volatile("" : "+v"(lb));  // one live base; the per-copy XORs are formed here, not hoisted
+  // A tile's descriptor and this wave's copy offsets, formed once; the
+  // copies themselves can then be issued in several groups (issue_range), so
+  // a wave does not stall on a full vector-memory queue by sending all of
+  // them at once.
+  struct Pending {
+    u32x4 rs;
+    unsigned lb;
+    MLA_LDS char* stage;
+  };
+
+  __device__ __forceinline__ Pending prepare(const bf16* __restrict__ base, int row0, int row_end,
+                                             MLA_LDS char* stage) const {
+    Pending p;
+    p.lb = lane_base;
+    asm volatile("" : "+v"(p.lb));  // one live base; the per-copy XORs are formed at issue, not hoisted
     int rows = row_end - row0;
     rows = rows > KT ? KT : rows;
-    const u32x4 rs = make_rsrc(base + (size_t)row0 * R, (unsigned)(rows * R * 2));
+    p.rs = make_rsrc(base + (size_t)row0 * R, (unsigned)(rows * R * 2));
+    p.stage = stage;
+    return p;
+  }
+
+  // Copies c in [C0, C1) of this wave's CPW copies.
+  template <int C0, int C1>
+  __device__ __forceinline__ void issue_range(const Pending& p) const {
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
+    for (int c = C0; c < (C1 < CPW ? C1 : CPW); ++c) {
       const int qi = w + NW * c;
       if (COPIES % NW == 0 || qi < COPIES) {
         const int srow = qi * RPI;
         const unsigned k = (unsigned)((chunk_swizzle<R>(srow) << 4) | (srow * R * 2));
-        buf2lds16(rs, lb ^ k, stage + qi * 1024);
+        buf2lds16(p.rs, p.lb ^ k, p.stage + qi * 1024);
       }
     }
+  }
+
+  __device__ __forceinline__ void issue(const bf16* __restrict__ base, int row0, int row_end,
+                                        MLA_LDS char* stage) const {
+    issue_range<0, CPW>(prepare(base, row0, row_end, stage));
   }
 };
 
@@ -364,7 +387,10 @@ struct PairAttn {
 
   // Partial S^T over this wave's latent half: s[cg][u] holds keys
   // [16u, 16u+16) of the tile for column group cg.
-  __device__ __forceinline__ void partial_scores(const MLA_LDS char* tile, f32x4 (&s)[2][2]) {
+  // hook(k0) runs after the chunk that starts at k-step k0 (used to spread
+  // the next tile's copies over the score products).
+  template <typename Hook>
+  __device__ __forceinline__ void partial_scores(const MLA_LDS char* tile, f32x4 (&s)[2][2], Hook&& hook) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) s[c][0] = s[c][1] = f32x4{};
     // Launder the 4 bases in place each tile: the compiler then cannot hoist
@@ -385,6 +411,7 @@ struct PairAttn {
         s[1][1] = mfma16(a1, qT[1][kk], s[1][1]);
       }
       __builtin_amdgcn_sched_barrier(0);
+      hook(k0);
     }
   }
 

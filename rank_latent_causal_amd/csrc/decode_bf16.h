@@ -4,8 +4,8 @@
 // section 形状与参数对比).  The pages stop short of a decode path; this one
 // evaluates the same definition as prefill for the last position.
 //
-//  mla_wuk_transpose    W_UK [H, DQ, R] -> W_UK^T [H, R, DQ] (workspace)
-//  mla_decode_absorb    q_abs[i, h, :] = scale*log2e * q[i, h, :] W_UK[h]
+//  mla_decode_absorb    q_abs[i, h, :] = scale*log2e * q[i, h, :] W_UK[h], read
+//                       straight from W_UK [H, DQ, R] (no transposed copy)
 //  mla_decode_split     the packed cache rows are cut into G equal ranges, one
 //                       per workgroup; each range is streamed from HBM into
 //                       LDS once and scored against all H heads (heads are the
@@ -20,6 +20,8 @@
 // sequence i from range k is stored in slot k + i, which is unique because
 // the sequences met by consecutive ranges are consecutive.
 #pragma once
+
+#include <type_traits>
 
 #include "attn_core.h"
 
@@ -51,31 +53,62 @@ __global__ void __launch_bounds__(256) mla_wuk_transpose(const T* __restrict__ w
 
 // ----------------------------------------------------------------- absorb
 struct DecodeAbsorbArgs {
-  const bf16* q;     // [B, H, DQ]
-  const bf16* wukT;  // [H, R, DQ]
-  bf16* qabs;        // [B, H, R]
+  const bf16* q;    // [B, H, DQ]
+  const bf16* wuk;  // [H, DQ, R]
+  bf16* qabs;       // [B, H, R]
   int B, H;
   float qscale;
 };
 
-// Wave (head h, 16 sequences): q_abs^T = W_UK[h]^T q^T, stored row-major
-// [B, H, R] so that the split kernel loads its score B operands with 16-byte
-// reads.
+// Workgroup (head h, latent columns [J0, J0 + JC)), 4 waves; wave w owns the
+// 16 latent columns J0 + 16w .. and walks the sequences 16 at a time:
+// q_abs^T[j, i] = sum_d W_UK[h, d, j] q[i, h, d] on MFMA.  The W_UK slice
+// [DQ x JC] is staged in LDS as stored (d-major); the A operand (row j,
+// 8 consecutive d) comes from two transposing ds_read_b64_tr_b16 reads.
+// Output rows are stored in the plain [B, H, R] layout, scaled by qscale.
 template <int DQ, int R>
 __global__ void __launch_bounds__(256) mla_decode_absorb(DecodeAbsorbArgs a) {
+  constexpr int JC = R < 64 ? R : 64;    // latent columns per workgroup
+  constexpr int DP = DQ < 32 ? 32 : DQ;  // staged rows, zero-padded to a whole k-step
+  constexpr int NK = DP / 32;
+  constexpr int LD = JC + 8;             // padded row (elements): spreads the tr16 rows over banks
+  static_assert(R % JC == 0 && JC % 16 == 0 && DQ % 8 == 0, "absorb tiling");
+  __shared__ __attribute__((aligned(16))) bf16 wt[DP][LD];
+  const int h = blockIdx.x / (R / JC), J0 = (blockIdx.x % (R / JC)) * JC;
+  const bf16* __restrict__ src = a.wuk + (size_t)h * DQ * R + J0;
+  for (int e = threadIdx.x; e < DP * JC / 8; e += 256) {
+    const int d = e / (JC / 8), j8 = e % (JC / 8);
+    const bf16x8 v = d < DQ ? *(const bf16x8*)(src + (size_t)d * R + 8 * j8) : bf16x8{};
+    *(bf16x8*)&wt[d][8 * j8] = v;
+  }
+  __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (16 * w >= JC) return;
   const int l16 = lane & 15, kq = lane >> 4;
-  const int h = blockIdx.y * 4 + w;
-  if (h >= a.H) return;
-  const int i = blockIdx.x * 16 + l16;
-  const bool ivalid = i < a.B;
-  const int ic = ivalid ? i : a.B - 1;
-  bf16x8 qT[R / 32];
-  absorb_rows<DQ, R>(a.q + ((size_t)ic * a.H + h) * DQ, a.wukT + (size_t)h * R * DQ, a.qscale, l16, kq, qT);
-  if (ivalid) {
-    bf16* dst = a.qabs + ((size_t)ic * a.H + h) * R + 8 * kq;
+  const int e4 = l16 >> 2, q4 = l16 & 3;
+  bf16x8 af[NK];
 #pragma unroll
-    for (int kk = 0; kk < R / 32; ++kk) *(bf16x8*)(dst + 32 * kk) = qT[kk];
+  for (int k = 0; k < NK; ++k) {
+    const int d = 32 * k + 8 * kq + e4;
+    af[k] = cat4(lds_read_tr16((const MLA_LDS char*)&wt[d][16 * w + 4 * q4]),
+                 lds_read_tr16((const MLA_LDS char*)&wt[d + 4][16 * w + 4 * q4]));
+  }
+  for (int i0 = 0; i0 < a.B; i0 += 16) {
+    const int i = i0 + l16;
+    const bool ok = i < a.B;
+    const bf16* qrow = a.q + ((size_t)(ok ? i : a.B - 1) * a.H + h) * DQ;
+    f32x4 acc = f32x4{};
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const bf16x8 bq = (32 * k + 8 * kq < DQ) ? *(const bf16x8*)(qrow + 32 * k + 8 * kq) : bf16x8{};
+      acc = mfma16(af[k], bq, acc);
+    }
+    if (ok) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[e] * a.qscale);
+      *(bf16x4*)(a.qabs + ((size_t)i * a.H + h) * R + J0 + 16 * w + 4 * kq) = v;
+    }
   }
 }
 
@@ -241,86 +274,120 @@ __device__ __forceinline__ int range_of(long long x, long long N, long long G) {
 }
 
 // Workgroup (16 sequences, head h), 4 waves.  Phase 1: wave w merges latent
-// columns [w R/4, (w+1) R/4) of every sequence into LDS (bf16, normalised).
-// Phase 2: wave w computes v-tiles w, w+4, ... of o^T = W_UV[h] o_lat^T.
+// columns [w R/4, (w+1) R/4) of every sequence into LDS (bf16, normalised)
+// in one online pass over the sequence's partials, with the next partial's
+// loads in flight.  Phase 2: wave w computes v-tiles w, w+4, ... of
+// o^T = W_UV[h] o_lat^T; their W_UV operands and gate values are loaded
+// before phase 1 starts, so their latency hides behind the merge.
 template <int DV, int R>
 __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
   constexpr int JW = R / 4;   // latent columns merged per wave
   constexpr int JL = JW / 4;  // per lane (four lanes per sequence)
   static_assert(JL % 4 == 0 || JL == 2, "merge split");
-  constexpr int JV = JL >= 4 ? JL / 4 : 1;
+  constexpr int VW = JL >= 4 ? 4 : 2;  // floats per vector load
+  constexpr int NVV = JL / VW;
+  using VT = typename std::conditional<(JL >= 4), f32x4, f32x2>::type;
+  constexpr int NKK = R / 32;
   __shared__ __attribute__((aligned(16))) bf16 olat[16][R + 8];
 
-  const int h = blockIdx.y;
+  // 1-D grid of H x nb workgroups (nb = ceil(B / 16)).  With H % 8 == 0 the
+  // nb workgroups of head h get ids congruent to h mod 8, i.e. they run on
+  // one XCD and read W_UV[h] from HBM once.
+  const int nb = (a.B + 15) / 16;
+  int h, bb;
+  if ((a.H & 7) == 0) {
+    const int id = blockIdx.x;
+    h = (id / (8 * nb)) * 8 + (id & 7);
+    bb = (id >> 3) % nb;
+  } else {
+    h = blockIdx.x / nb;
+    bb = blockIdx.x % nb;
+  }
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l16 = lane & 15, kq = lane >> 4;
-  const int i = blockIdx.x * 16 + l16;
+  const int i = bb * 16 + l16;
   const bool ivalid = i < a.B;
   const int ic = ivalid ? i : a.B - 1;
+
+  // phase 2 operands: the first v-tile's are issued before the merge
+  const bf16* wv = a.wuv + (size_t)h * DV * R;
+  const size_t orow = (size_t)ic * a.H * DV + (size_t)h * DV;
+  auto load_w = [&](int vt, bf16x8 (&wa)[NKK], bf16x4& gv) {
+    const bf16* wrow = wv + (size_t)(16 * vt + l16) * R + 8 * kq;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) wa[kk] = *(const bf16x8*)(wrow + 32 * kk);
+    gv = *(const bf16x4*)(a.gate + orow + 16 * vt + 4 * kq);
+  };
+  bf16x8 wa[NKK];
+  bf16x4 gv;
+  if (w < DV / 16) load_w(w, wa, gv);
 
   {
     const long long s0 = a.cu[ic], s1 = a.cu[ic + 1];
     const int k0 = range_of(s0, a.N, a.G), k1 = range_of(s1 - 1, a.N, a.G);
-    float mstar = -INFINITY;
-    for (int k = k0; k <= k1; ++k) mstar = fmaxf(mstar, a.part_ml[((size_t)(k + ic) * a.H + h) * 2]);
-    float L = 0.0f;
+    const int j0 = w * JW + kq * JL;
+    auto load = [&](int k, float& mk, float& lk, VT (&o)[NVV]) {
+      const size_t base = (size_t)(k + ic) * a.H + h;
+      mk = a.part_ml[base * 2];
+      lk = a.part_ml[base * 2 + 1];
+      const float* src = a.part_o + base * R + j0;
+#pragma unroll
+      for (int u = 0; u < NVV; ++u) o[u] = *(const VT*)(src + VW * u);
+    };
+    // online log-sum-exp merge; every partial has a finite max (a range piece
+    // holds at least one key of the sequence)
+    float m = -INFINITY, L = 0.0f;
+    VT acc[NVV];
+#pragma unroll
+    for (int u = 0; u < NVV; ++u) acc[u] = VT{};
+    float mk, lk;
+    VT ok[NVV];
+    load(k0, mk, lk, ok);
     for (int k = k0; k <= k1; ++k) {
-      const float* ml = a.part_ml + ((size_t)(k + ic) * a.H + h) * 2;
-      L += fast_exp2(ml[0] - mstar) * ml[1];
+      float mn = 0.0f, ln = 0.0f;
+      VT on[NVV];
+      if (k < k1) load(k + 1, mn, ln, on);
+      const float m_new = fmaxf(m, mk);
+      const float sa = fast_exp2(m - m_new), sb = fast_exp2(mk - m_new);
+      L = L * sa + lk * sb;
+#pragma unroll
+      for (int u = 0; u < NVV; ++u) acc[u] = acc[u] * sa + ok[u] * sb;
+      m = m_new;
+      mk = mn;
+      lk = ln;
+#pragma unroll
+      for (int u = 0; u < NVV; ++u) ok[u] = on[u];
     }
     const float invL = 1.0f / L;
-    const int j0 = w * JW + kq * JL;
-    if constexpr (JL >= 4) {
-      f32x4 acc[JV];
 #pragma unroll
-      for (int u = 0; u < JV; ++u) acc[u] = f32x4{};
-      for (int k = k0; k <= k1; ++k) {
-        const size_t base = (size_t)(k + ic) * a.H + h;
-        const float wk = fast_exp2(a.part_ml[base * 2] - mstar) * invL;
-        const float* src = a.part_o + base * R + j0;
+    for (int u = 0; u < NVV; ++u) {
 #pragma unroll
-        for (int u = 0; u < JV; ++u) acc[u] += wk * *(const f32x4*)(src + 4 * u);
-      }
-#pragma unroll
-      for (int u = 0; u < JV; ++u) {
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[u][e];
-        *(bf16x4*)&olat[l16][j0 + 4 * u] = v;
-      }
-    } else {
-      float acc0 = 0.0f, acc1 = 0.0f;
-      for (int k = k0; k <= k1; ++k) {
-        const size_t base = (size_t)(k + ic) * a.H + h;
-        const float wk = fast_exp2(a.part_ml[base * 2] - mstar) * invL;
-        acc0 += wk * a.part_o[base * R + j0];
-        acc1 += wk * a.part_o[base * R + j0 + 1];
-      }
-      olat[l16][j0] = (bf16)acc0;
-      olat[l16][j0 + 1] = (bf16)acc1;
+      for (int e = 0; e < VW; ++e) olat[l16][j0 + VW * u + e] = (bf16)(acc[u][e] * invL);
     }
   }
   __syncthreads();
 
   // o_lat^T B operand for k-step kk: slot p <-> latent dim 32kk + 8kq + p
-  const bf16* wv = a.wuv + (size_t)h * DV * R;
   for (int vt = w; vt < DV / 16; vt += 4) {
-    const bf16* wrow = wv + (size_t)(16 * vt + l16) * R + 8 * kq;
+    bf16x8 wn[NKK];
+    bf16x4 gn;
+    if (vt + 4 < DV / 16) load_w(vt + 4, wn, gn);  // next v-tile's operands in flight
     f32x4 acc = f32x4{};
-#pragma unroll 4
-    for (int kk = 0; kk < R / 32; ++kk) {
-      const bf16x8 av = *(const bf16x8*)(wrow + 32 * kk);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
       const bf16x8 bv = *(const bf16x8*)&olat[l16][32 * kk + 8 * kq];
-      acc = mfma16(av, bv, acc);
+      acc = mfma16(wa[kk], bv, acc);
     }
     if (ivalid) {
-      const size_t orow = (size_t)i * a.H * DV + (size_t)h * DV;
-      const int v = 16 * vt + 4 * kq;
-      const bf16x4 gv = *(const bf16x4*)(a.gate + orow + v);
       bf16x4 ov;
 #pragma unroll
       for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[e] * sigmoidf_((float)gv[e]));
-      *(bf16x4*)(a.out + orow + v) = ov;
+      *(bf16x4*)(a.out + orow + 16 * vt + 4 * kq) = ov;
+    }
+    if (vt + 4 < DV / 16) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) wa[kk] = wn[kk];
+      gv = gn;
     }
   }
 }

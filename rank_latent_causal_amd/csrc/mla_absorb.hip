@@ -12,6 +12,13 @@
 #include "f32_kernels.h"
 #include "prefill_bf16.h"
 
+#ifndef MLA_PAIR_NW
+#define MLA_PAIR_NW 4
+#endif
+#ifndef MLA_PAIR_NS
+#define MLA_PAIR_NS 2
+#endif
+
 namespace {
 
 using mla::bf16;
@@ -49,14 +56,12 @@ int device_cu_count() {
 }
 
 struct DecodeLayout {
-  size_t wukT = 0, qabs = 0, part_o = 0, part_ml = 0, total = 0;
+  size_t qabs = 0, part_o = 0, part_ml = 0, total = 0;
 };
 
 DecodeLayout decode_layout(int B, int H, int dq, int r, int G) {
   DecodeLayout L;
   size_t off = 0;
-  L.wukT = off;
-  off = align_up(off + (size_t)H * r * dq * sizeof(bf16));
   L.qabs = off;
   off = align_up(off + (size_t)B * H * r * sizeof(bf16));
   L.part_o = off;
@@ -71,11 +76,12 @@ DecodeLayout decode_layout(int B, int H, int dq, int r, int G) {
 template <int DQ, int DV, int R>
 void launch_prefill_bf16(mla::PrefillArgs a, hipStream_t s) {
   if constexpr (R >= 256) {
+    constexpr int NW = MLA_PAIR_NW, NS = MLA_PAIR_NS;
     a.ntb = (a.T + 31) / 32;
-    a.nhg = (a.H + 1) / 2;
+    a.nhg = (a.H + NW / 2 - 1) / (NW / 2);
     a.xcd_remap = (a.nhg % 8) == 0 ? 1 : 0;
-    hipLaunchKernelGGL((mla::mla_prefill_pair_kernel<DQ, DV, R>), dim3(a.B * a.ntb * a.nhg),
-                       dim3(64 * mla::kPairWaves), 0, s, a);
+    hipLaunchKernelGGL((mla::mla_prefill_pair_kernel<DQ, DV, R, NW, NS>), dim3(a.B * a.ntb * a.nhg),
+                       dim3(64 * NW), 0, s, a);
   } else {
     a.ntb = (a.T + mla::kPrefillRows - 1) / mla::kPrefillRows;
     a.nhg = (a.H + 3) / 4;
@@ -88,9 +94,10 @@ void launch_prefill_bf16(mla::PrefillArgs a, hipStream_t s) {
 template <int DQ, int DV, int R>
 void launch_decode_bf16(const mla::DecodeAbsorbArgs& aa, const mla::DecodeSplitArgs& sa,
                         const mla::DecodeMergeArgs& ma, hipStream_t s) {
-  hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3((aa.B + 15) / 16, (aa.H + 3) / 4), dim3(256), 0, s, aa);
+  constexpr int JC = R < 64 ? R : 64;
+  hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(aa.H * (R / JC)), dim3(256), 0, s, aa);
   hipLaunchKernelGGL((mla::mla_decode_split<R>), dim3(sa.G), dim3(64 * mla::kDecodeWaves), 0, s, sa);
-  hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3((ma.B + 15) / 16, ma.H), dim3(256), 0, s, ma);
+  hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + 15) / 16) * ma.H), dim3(256), 0, s, ma);
 }
 
 void launch_wuk_transpose(const bf16* w, bf16* wt, int H, int dq, int r, hipStream_t s) {
@@ -216,11 +223,8 @@ mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* 
   const DecodeLayout L = decode_layout(B, H, d_q, r, G);
   char* ws = (char*)workspace;
 
-  bf16* wukT = (bf16*)(ws + L.wukT);
-  launch_wuk_transpose((const bf16*)w_uk, wukT, H, d_q, r, s);
-
   mla::DecodeAbsorbArgs aa{};
-  aa.q = (const bf16*)q; aa.wukT = wukT; aa.qabs = (bf16*)(ws + L.qabs);
+  aa.q = (const bf16*)q; aa.wuk = (const bf16*)w_uk; aa.qabs = (bf16*)(ws + L.qabs);
   aa.B = B; aa.H = H; aa.qscale = scale * mla::kLog2e;
   mla::DecodeSplitArgs sa{};
   sa.qabs = aa.qabs; sa.cache = (const bf16*)c_cache; sa.cu = cu_seqlens;

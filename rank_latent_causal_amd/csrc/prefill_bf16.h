@@ -123,33 +123,42 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave-pair prefill for r >= 256: one workgroup = 4 waves = 2 heads x a block
-// of 32 positions.  Waves (2p, 2p+1) serve head 2hg + p, both 16-row column
-// groups, and latent halves 0 / 1.  Per 32-key tile: partial scores over the
-// wave's half, exchange through LDS, full causal softmax (identical in both
-// waves), values of the wave's half.  The epilogue adds the two halves' W_UV
-// products through LDS before the gate.
+// Wave-pair prefill for r >= 256: one workgroup = NW waves = NW/2 heads x a
+// block of 32 positions.  Waves (2p, 2p+1) serve head (NW/2) hg + p, both
+// 16-row column groups, and latent halves 0 / 1.  Per 32-key tile: partial
+// scores over the wave's half, exchange through LDS, full causal softmax
+// (identical in both waves), values of the wave's half.  The epilogue adds
+// the two halves' W_UV products through LDS before the gate.  NS LDS stages
+// keep NS - 1 tiles in flight; every c tile is copied once per workgroup and
+// serves its NW/2 heads.
 // ---------------------------------------------------------------------------
-constexpr int kPairWaves = 4;
+template <int R, int NW, int NS>
+struct PairConfig {
+  static constexpr int XBUF = NW * 4 * 64 * 16;                  // partial-score exchange
+  static constexpr int LDS = NS * LatentTile<R>::BYTES + XBUF;   // bytes per workgroup
+};
 
-template <int DQ, int DV, int R>
-__global__ void __launch_bounds__(64 * kPairWaves)
+template <int DQ, int DV, int R, int NW, int NS>
+__global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 mla_prefill_pair_kernel(PrefillArgs a) {
   using LT = LatentTile<R>;
   using PA = PairAttn<R>;
-  constexpr int NS = 2;
-  constexpr int LPW = copies_per_wave<R>(kPairWaves);
+  using CFG = PairConfig<R, NW, NS>;
+  constexpr int CPW = copies_per_wave<R>(NW);
   constexpr int NV = DV / 16;
-  static_assert(LT::COPIES % kPairWaves == 0, "copy split");
+  constexpr int HPW = NW / 2;  // heads per workgroup
+  static_assert(NW % 2 == 0 && NS >= 2, "pairs and at least two stages");
+  static_assert(LT::COPIES % NW == 0, "copy split");
   static_assert(DQ % 16 == 0 && DV % 16 == 0, "shape");
-  // epilogue partials of o^T reuse the stage memory
-  static_assert(kPairWaves * NV * 2 * 1024 <= NS * LT::BYTES, "epilogue exchange fits the stages");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * LT::BYTES];
-  __shared__ __attribute__((aligned(16))) f32x4 xbuf[kPairWaves][4][64];  // partial scores
+  static_assert((NS - 2) * CPW < 64, "vmcnt range");
+  // epilogue partials of o^T reuse the stage and exchange memory
+  static_assert(NW * NV * 2 * 1024 <= CFG::LDS, "epilogue exchange fits the LDS");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+  f32x4* xbuf = (f32x4*)(smem_raw + NS * LT::BYTES);  // [wave][4][lane]
 
-  // ---- work item (32 positions x 2 heads), heaviest query blocks first
+  // ---- work item (32 positions x NW/2 heads), heaviest query blocks first
   const int x = blockIdx.x;
   int tb, b, hg;
   if (a.xcd_remap) {
@@ -168,7 +177,7 @@ mla_prefill_pair_kernel(PrefillArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, kq = lane >> 4;
   const int jh = w & 1, partner = w ^ 1;
-  const int h = hg * 2 + (w >> 1);
+  const int h = hg * HPW + (w >> 1);
   const bool hvalid = h < a.H;
   const int hc = hvalid ? h : a.H - 1;
   const int T = a.T, H = a.H;
@@ -183,9 +192,11 @@ mla_prefill_pair_kernel(PrefillArgs a) {
   const bf16* __restrict__ cb = a.c + (size_t)b * T * R;
   const int ntiles = (min(t0 + 32, T) + LT::KT - 1) / LT::KT;
 
-  TileCopier<R, kPairWaves> copier;
+  TileCopier<R, NW> copier;
   copier.init(w, lane);
-  copier.issue(cb, 0, T, smem);
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < ntiles) copier.issue(cb, p * LT::KT, T, smem + p * LT::BYTES);
 
   PA st;
   {
@@ -196,26 +207,46 @@ mla_prefill_pair_kernel(PrefillArgs a) {
   st.reset();
   st.init_addressing(l16, kq, jh);
 
-  // One key tile; STG (the LDS stage of tile `it`) is a compile-time
-  // constant so every operand address is a per-lane base plus an immediate.
+  // One key tile; STG (the LDS stage of tile `it`, it % NS) is a
+  // compile-time constant so every operand address is a per-lane base plus
+  // an immediate.
   auto tile_step = [&](int it, auto stage_tag) {
     constexpr int STG = decltype(stage_tag)::value;
-    wait_vmcnt<0>();  // this wave's copies of tile `it`
-    wg_barrier();     // tile visible; iteration it-1 finished (its stage and xbuf are free)
-    if (it + 1 < ntiles) copier.issue(cb, (it + 1) * LT::KT, T, smem + (STG ^ 1) * LT::BYTES);
+    // This wave's copies of tile `it` have landed once at most the copies of
+    // the younger tiles already issued (it+1 .. it+NS-2, those that exist)
+    // are outstanding.
+    {
+      const int younger = min(NS - 2, ntiles - 1 - it);
+      if constexpr (NS >= 4) {
+        if (younger >= 2) wait_vmcnt<2 * CPW>();
+        else if (younger == 1) wait_vmcnt<CPW>();
+        else wait_vmcnt<0>();
+      } else if constexpr (NS == 3) {
+        if (younger >= 1) wait_vmcnt<CPW>();
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
+    wg_barrier();  // tile visible; iteration it-1 finished (its stage and xbuf are free)
     const MLA_LDS char* tile = smem + STG * LT::BYTES;
 
     f32x4 sc[2][2];
-    st.partial_scores(tile, sc);
-    xbuf[w][0][lane] = sc[0][0];
-    xbuf[w][1][lane] = sc[0][1];
-    xbuf[w][2][lane] = sc[1][0];
-    xbuf[w][3][lane] = sc[1][1];
+    st.partial_scores(tile, sc, [](int) {});
+    xbuf[(w * 4 + 0) * 64 + lane] = sc[0][0];
+    xbuf[(w * 4 + 1) * 64 + lane] = sc[0][1];
+    xbuf[(w * 4 + 2) * 64 + lane] = sc[1][0];
+    xbuf[(w * 4 + 3) * 64 + lane] = sc[1][1];
     wait_lgkmcnt0();
     wg_barrier();  // partial scores of both halves visible
+    // The copies of tile it+NS-1 go out here, between the two barriers of
+    // this tile rather than right after the first one, where every wave of
+    // the workgroup would queue its copies at the same moment.
+    if (it + NS - 1 < ntiles)
+      copier.issue(cb, (it + NS - 1) * LT::KT, T, smem + ((STG + NS - 1) % NS) * LT::BYTES);
     {
-      const f32x4 o00 = xbuf[partner][0][lane], o01 = xbuf[partner][1][lane];
-      const f32x4 o10 = xbuf[partner][2][lane], o11 = xbuf[partner][3][lane];
+      const f32x4 o00 = xbuf[(partner * 4 + 0) * 64 + lane], o01 = xbuf[(partner * 4 + 1) * 64 + lane];
+      const f32x4 o10 = xbuf[(partner * 4 + 2) * 64 + lane], o11 = xbuf[(partner * 4 + 3) * 64 + lane];
       // add in a fixed order (half 0 + half 1) so both waves get identical sums
       if (jh == 0) {
         sc[0][0] += o00; sc[0][1] += o01; sc[1][0] += o10; sc[1][1] += o11;
@@ -239,10 +270,15 @@ mla_prefill_pair_kernel(PrefillArgs a) {
     st.softmax(sc, pB);
     st.values(tile, pB);
   };
-  for (int it = 0; it < ntiles; it += 2) {
+  for (int it = 0; it < ntiles; it += NS) {
     tile_step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < ntiles) tile_step(it + 1, std::integral_constant<int, 1>{});
+    if (it + 1 < ntiles) tile_step(it + 1, std::integral_constant<int, 1 % NS>{});
+    if constexpr (NS >= 3)
+      if (it + 2 < ntiles) tile_step(it + 2, std::integral_constant<int, 2 % NS>{});
+    if constexpr (NS >= 4)
+      if (it + 3 < ntiles) tile_step(it + 3, std::integral_constant<int, 3 % NS>{});
   }
+  static_assert(NS <= 4, "the loop above unrolls at most four stages");
 
   // ---- epilogue: partial o^T = W_UV[h][:, half] (O^T_half / l), summed by the pair
   bf16x8 ob[2][PA::NKK];
@@ -252,7 +288,7 @@ mla_prefill_pair_kernel(PrefillArgs a) {
 #pragma unroll
     for (int kk = 0; kk < PA::NKK; ++kk) ob[c][kk] = pack44(st.oT[c][2 * kk], st.oT[c][2 * kk + 1], inv_l);
   }
-  wg_barrier();  // every wave is done with the stages: reuse them for the o^T partials
+  wg_barrier();  // every wave is done with the stages and xbuf: reuse them for the o^T partials
   f32x4* obuf = (f32x4*)smem_raw;  // [wave][vt][cg][lane]
   const bf16* wv = a.wuv + (size_t)hc * DV * R + jh * PA::RH;
 #pragma unroll
