@@ -185,19 +185,19 @@ mla_decode_split(DecodeSplitArgs a) {
   st.reset();
   st.init_addressing(l16, kq);
 
+  static_assert(NS == 4, "the waits below assume four stages");
   for (int it = 0; it < ntiles; ++it) {
-    const int nx = it + NS - 1;
-    if (nx < ntiles) {
-      copier.issue(a.cache, (int)(lo + (long long)nx * LT::KT), (int)hi, smem + (nx % NS) * LT::BYTES);
-      wait_vmcnt<(NS - 1) * LPW>();
-    } else if (nx == ntiles) {
-      wait_vmcnt<(NS - 2) * LPW>();
-    } else if (nx == ntiles + 1) {
-      wait_vmcnt<(NS - 3) * LPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // Tile `it` has landed once at most the copies of the younger tiles
+    // already issued (it+1, it+2, those that exist) are outstanding.
+    const int younger = min(NS - 2, ntiles - 1 - it);
+    if (younger >= 2) wait_vmcnt<2 * LPW>();
+    else if (younger == 1) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
+    // One barrier per tile: it publishes tile `it` and shows that every wave
+    // has finished tile it-1, whose stage the copy below refills.
     wg_barrier();
+    const int nx = it + NS - 1;
+    if (nx < ntiles) copier.issue(a.cache, (int)(lo + (long long)nx * LT::KT), (int)hi, smem + (nx % NS) * LT::BYTES);
     const MLA_LDS char* tile = smem + (it % NS) * LT::BYTES;
     const long long r0 = lo + (long long)it * LT::KT;
     const long long r1 = min(r0 + LT::KT, hi);
@@ -252,7 +252,6 @@ mla_decode_split(DecodeSplitArgs a) {
       st.reset();
       if (seq_lo >= r1) break;  // the next sequence starts in a later tile
     }
-    wg_barrier();
   }
 }
 
