@@ -52,12 +52,19 @@ struct TileCopier {
   static constexpr int KT = LatentTile<R>::KT;
   static_assert(64 % CPR == 0, "a copy covers whole rows");
   int w;
-  unsigned lane_base;
 
-  __device__ __forceinline__ void init(int wave, int lane) {
-    w = wave;
-    const int sl = lane / CPR;
-    lane_base = (unsigned)((sl * R + (((lane % CPR) ^ chunk_swizzle<R>(sl)) * 8)) * 2);
+  __device__ __forceinline__ void init(int wave, int /*lane*/) { w = wave; }
+
+  // This lane's byte offset inside a copy.  The lane id is re-read with
+  // v_mbcnt at every tile (from asm, so the result is not hoisted): a base
+  // kept live across the whole key loop costs a VGPR in kernels that are at
+  // the register limit, and a spilled base reloads behind a vmcnt(0) that
+  // drains the tile prefetches.
+  __device__ __forceinline__ unsigned lane_base() const {
+    unsigned ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const unsigned sl = ln / CPR;
+    return (sl * R + (((ln % CPR) ^ (unsigned)chunk_swizzle<R>((int)sl)) * 8)) * 2;
   }
 
   // A tile's descriptor and this wave's copy offsets, formed once; the
@@ -73,8 +80,7 @@ struct TileCopier {
   __device__ __forceinline__ Pending prepare(const bf16* __restrict__ base, int row0, int row_end,
                                              MLA_LDS char* stage) const {
     Pending p;
-    p.lb = lane_base;
-    asm volatile("" : "+v"(p.lb));  // one live base; the per-copy XORs are formed at issue, not hoisted
+    p.lb = lane_base();
     int rows = row_end - row0;
     rows = rows > KT ? KT : rows;
     p.rs = make_rsrc(base + (size_t)row0 * R, (unsigned)(rows * R * 2));

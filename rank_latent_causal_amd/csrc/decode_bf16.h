@@ -154,6 +154,9 @@ mla_decode_split(DecodeSplitArgs a) {
   const int hc = hvalid ? h : a.H - 1;
 
   // first sequence with rows in [lo, hi): the largest i with cu[i] <= lo
+  // First sequence with rows in [lo, hi): the largest i with cu[i] <= lo.
+  // Sequence bookkeeping is wave-uniform and fits 32 bits (the host keeps
+  // the cache below 2^31 rows), so it lives in scalar registers.
   int i;
   {
     int l = 0, r = a.B - 1;
@@ -161,9 +164,9 @@ mla_decode_split(DecodeSplitArgs a) {
       const int mid = (l + r + 1) >> 1;
       if ((long long)a.cu[mid] <= lo) l = mid; else r = mid - 1;
     }
-    i = l;
+    i = __builtin_amdgcn_readfirstlane(l);
   }
-  long long seq_lo = a.cu[i], seq_end = a.cu[i + 1];
+  int seq_lo = __builtin_amdgcn_readfirstlane(a.cu[i]), seq_end = __builtin_amdgcn_readfirstlane(a.cu[i + 1]);
 
   TileCopier<R, kDecodeWaves> copier;
   copier.init(w, lane);
@@ -199,13 +202,13 @@ mla_decode_split(DecodeSplitArgs a) {
     const int nx = it + NS - 1;
     if (nx < ntiles) copier.issue(a.cache, (int)(lo + (long long)nx * LT::KT), (int)hi, smem + (nx % NS) * LT::BYTES);
     const MLA_LDS char* tile = smem + (it % NS) * LT::BYTES;
-    const long long r0 = lo + (long long)it * LT::KT;
-    const long long r1 = min(r0 + LT::KT, hi);
+    const int r0 = (int)lo + it * LT::KT;
+    const int r1 = min(r0 + LT::KT, (int)hi);
 
     // a tile may hold the end of one sequence and the start of the next
     while (true) {
-      const long long a0 = max(r0, seq_lo);
-      const long long a1 = min(r1, seq_end);
+      const int a0 = max(r0, seq_lo);
+      const int a1 = min(r1, seq_end);
       if (compute && a0 < a1) {
         f32x4 sa, sb;
         st.scores(tile, sa, sb);
@@ -242,7 +245,7 @@ mla_decode_split(DecodeSplitArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       ++i;
       seq_lo = seq_end;
-      seq_end = a.cu[i + 1];
+      seq_end = __builtin_amdgcn_readfirstlane(a.cu[i + 1]);
       if (compute) load_q(i);
       // Take the wait for the new query here, where the switch happens.  Left
       // pending, the loads stay on the compiler's books across the loop back

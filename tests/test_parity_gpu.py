@@ -111,6 +111,8 @@ def test_prefill_first_position_closed_form():
     ([31, 32, 33, 1, 200], 96, "full", 4),
     ([300, 1, 129], 96, "full", 0),
     ([1000, 17, 513, 64], 40, "full", 7),
+    ([1] * 37 + [45, 2], 96, "full", 3),  # tiles holding dozens of one-row sequences
+    ([65, 300], 128, "full", 0),          # the largest head count of one workgroup
 ])
 def test_decode_bf16_ragged(o, lens, H, shape, splits):
     dq, dv, r = SHAPES[shape]
