@@ -164,3 +164,77 @@ def test_decode_full_workload_sampled(o):
     got = to_host_f64(run_decode(d))
     seqs = np.array([0, 1, int(np.argmin(d["lengths"])), int(np.argmax(d["lengths"])), 31, 63], dtype=np.int64)
     assert_parity(got[seqs], oracle_decode(o, d, seqs=seqs), dg.BF16, "full decode sampled")
+
+
+# ------------------------------------------------------------------ edges
+@pytest.mark.parametrize("scale", [0.0, 0.35])
+def test_prefill_scale_extremes(o, scale):
+    """scale 0 (uniform weights over the prefix) and four times the default
+    1/sqrt(d_q) (a peakier softmax).  Far larger scales leave the bf16
+    regime: q_abs is rounded to bf16 for the MFMA, and a very peaky softmax
+    turns that rounding into weight shifts between near-tied keys."""
+    d = dg.prefill_inputs(1, 200, 4, 128, 128, 512, dtype=dg.BF16, seed=5100)
+    log(f"prefill full width scale={scale}")
+    got = to_host_f64(run_prefill(d, scale=scale))
+    assert_parity(got, oracle_prefill(o, d, scale=scale), dg.BF16, f"prefill scale={scale}")
+
+
+def test_prefill_running_max_rescale():
+    """Early latent rows shrunk (ramping to full size by position 100) with
+    four times the default scale: the running max jumps by more than 8
+    (log2 units) after the first tile on most query rows, so the
+    accumulator rescale runs, while outputs stay at unit scale."""
+    o = oracle.get()
+    T = 300
+    d = dg.prefill_inputs(1, T, 4, 128, 128, 512, dtype=dg.BF16, seed=5150)
+    ramp = np.minimum(1.0, 0.02 + np.arange(T, dtype=np.float32) / 100.0)[None, :, None]
+    d["c"] = dg.f32_to_bf16_bits(dg.as_f32(d["c"]) * ramp)
+    log("prefill ramped latent (rescale path)")
+    got = to_host_f64(run_prefill(d, scale=0.35))
+    assert_parity(got, oracle_prefill(o, d, scale=0.35), dg.BF16, "prefill rescale path")
+
+
+def test_prefill_long_sequence_sampled(o):
+    """T well beyond the full workload with a ragged last tile; rows at the
+    ends and around tile boundaries."""
+    T = 20001
+    d = dg.prefill_inputs(1, T, 2, 128, 128, 512, dtype=dg.BF16, seed=5200)
+    d["scale"] = 128 ** -0.5
+    log(f"prefill long T={T} H=2 (sampled rows)")
+    got = to_host_f64(run_prefill(d)).reshape(T, -1)
+    rows = np.array([0, 1, 31, 32, 33, 4095, 4096, 9999, 19967, 19968, 19999, 20000], dtype=np.int64)
+    assert_parity(got[rows], oracle_prefill(o, d, rows=rows), dg.BF16, "long prefill sampled")
+
+
+def test_decode_long_sequence(o):
+    """One sequence much longer than any range next to a three-row one."""
+    d = dg.decode_inputs(2, 8, 128, 128, 512, dtype=dg.BF16, seed=5300, lengths=[150000, 3])
+    d["scale"] = 128 ** -0.5
+    log("decode long sequence 150000 + 3 rows")
+    got = to_host_f64(run_decode(d))
+    assert_parity(got, oracle_decode(o, d), dg.BF16, "decode long sequence")
+
+
+def test_side_stream_and_workspace_reuse():
+    """Calls enqueued on a non-default stream with a caller workspace reused
+    across shapes give the same bits as default-stream calls."""
+    import torch
+    import rank_latent_causal_amd as mla
+    from gpu_util import to_dev
+    d = dg.prefill_inputs(2, 150, 6, 128, 128, 512, dtype=dg.BF16, seed=5400)
+    e = dg.decode_inputs(3, 20, 128, 128, 512, dtype=dg.BF16, seed=5401, lengths=[700, 2, 90])
+    P = [to_dev(d[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")]
+    D = [to_dev(e[k]) for k in ("q", "c_cache", "cu_seqlens", "w_uk", "w_uv", "gate")]
+    ref_p = mla.mla_absorb_prefill(*P, 0.1)
+    ref_d = mla.mla_absorb_decode(*D, 0.1)
+    torch.cuda.synchronize()
+    n = max(mla.prefill_workspace_size(2, 150, 6, 128, 512, mla.DTYPE_BF16),
+            mla.decode_workspace_size(3, 20, 128, 512, 0, mla.DTYPE_BF16))
+    ws = torch.empty(n + 4096, dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    log("side stream + shared workspace")
+    with torch.cuda.stream(side):
+        out_p = mla.mla_absorb_prefill(*P, 0.1, workspace=ws, stream=side)
+        out_d = mla.mla_absorb_decode(*D, 0.1, workspace=ws, stream=side)
+    side.synchronize()
+    assert torch.equal(out_p, ref_p) and torch.equal(out_d, ref_d)
