@@ -140,9 +140,11 @@ __device__ __forceinline__ void absorb_rows(const bf16* __restrict__ qrow, const
   }
 }
 
-// QCH / VCH: score k-steps / value tiles issued between scheduling barriers,
-// which bounds the LDS operand reads in flight (and their registers).
-template <int R, int QCH = 4, int VCH = 8>
+// PF > 0: the LDS operands of score k-step kk+PF (value tile t+PF) are read
+// while the MFMAs of step kk (tile t) run; two steps ahead measured 7% faster
+// than chunked reads on the full-width decode.  With PF = 0, QCH / VCH score
+// k-steps / value tiles form one chunk (its reads, then its MFMAs).
+template <int R, int QCH = 4, int VCH = 8, int PF = 2>
 struct WaveAttn {
   static constexpr int NKK = R / 32;
   static constexpr int NJT = R / 16;
@@ -215,6 +217,29 @@ struct WaveAttn {
     s1 = f32x4{};
     int qb = qk_base[0], qx = qk_x;
     asm volatile("" : "+v"(qb), "+v"(qx));
+    constexpr int SP = PF < NKK ? PF : NKK - 1;  // lookahead that exists
+    if constexpr (SP > 0) {
+      // operands of k-steps kk+1 .. kk+SP are read while k-step kk's MFMAs run
+      bf16x8 a[SP + 1][2];
+#pragma unroll
+      for (int u = 0; u < SP; ++u) {
+        const MLA_LDS char* p = tile + qk_off(u, qb, qx);
+        a[u][0] = lds_read_b128(p);
+        a[u][1] = lds_read_b128(p + 16 * ROWB);
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (kk + SP < NKK) {
+          const MLA_LDS char* p = tile + qk_off(kk + SP, qb, qx);
+          a[(kk + SP) % (SP + 1)][0] = lds_read_b128(p);
+          a[(kk + SP) % (SP + 1)][1] = lds_read_b128(p + 16 * ROWB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        s0 = mfma16(a[kk % (SP + 1)][0], qT[kk], s0);
+        s1 = mfma16(a[kk % (SP + 1)][1], qT[kk], s1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
     constexpr int CH = NKK < QCH ? NKK : QCH;
 #pragma unroll
     for (int k0 = 0; k0 < NKK; k0 += CH) {
@@ -225,6 +250,7 @@ struct WaveAttn {
         s1 = mfma16(lds_read_b128(p + 16 * ROWB), qT[kk], s1);
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
     }
   }
 
@@ -258,6 +284,24 @@ struct WaveAttn {
     constexpr int CH = NJT < VCH ? NJT : VCH;
     int tb = tr_base[0], tx = tr_rx;
     asm volatile("" : "+v"(tb), "+v"(tx));
+    constexpr int VP = PF < NJT ? PF : NJT - 1;  // lookahead that exists
+    if constexpr (VP > 0) {
+      // value tiles t+1 .. t+VP are read while tile t's MFMA runs
+      auto rd = [&](int t) {
+        const MLA_LDS char* p = tile + tr_off(t, tb, tx);
+        return cat4(lds_read_tr16(p), lds_read_tr16(p + 16 * ROWB));
+      };
+      bf16x8 a[VP + 1];
+#pragma unroll
+      for (int u = 0; u < VP; ++u) a[u] = rd(u);
+#pragma unroll
+      for (int t = 0; t < NJT; ++t) {
+        if (t + VP < NJT) a[(t + VP) % (VP + 1)] = rd(t + VP);
+        __builtin_amdgcn_sched_barrier(0);
+        oT[t] = mfma16(a[t % (VP + 1)], pB, oT[t]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
     for (int t0 = 0; t0 < NJT; t0 += CH) {
 #pragma unroll
@@ -268,6 +312,7 @@ struct WaveAttn {
         oT[t] = mfma16(cat4(lo, hi), pB, oT[t]);
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
     }
   }
 };
