@@ -258,6 +258,25 @@ struct WaveAttn {
   // the value accumulation.  The reference max only moves when a score
   // exceeds it by more than 8, so the O^T rescale is rare and P <= 2^8.
   __device__ __forceinline__ void update(const MLA_LDS char* tile, const f32x4& s0, const f32x4& s1) {
+    // value operand: lane i of 16-lane group kq takes latent dim 16t + i and
+    // keys {4kq+e} (lo) / {16+4kq+e} (hi); its tr16 source chunk is key row
+    // 4kq + i/4 (+16), dims 16t + 4(i%4) .. +3.
+    int tb = tr_base[0], tx = tr_rx;
+    asm volatile("" : "+v"(tb), "+v"(tx));
+    auto rd = [&](int t) {
+      const MLA_LDS char* p = tile + tr_off(t, tb, tx);
+      return cat4(lds_read_tr16(p), lds_read_tr16(p + 16 * ROWB));
+    };
+    constexpr int VP = PF < NJT ? PF : NJT - 1;  // lookahead that exists
+    // The first value operands do not depend on P: their reads go out before
+    // the softmax arithmetic.
+    bf16x8 a[VP + 1];
+    if constexpr (VP > 0) {
+#pragma unroll
+      for (int u = 0; u < VP; ++u) a[u] = rd(u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
     float mx = max8_nn(s0, s1);
     mx = col_max(mx);
     const bool need = mx > m_run + 8.0f;
@@ -278,22 +297,8 @@ struct WaveAttn {
     l_run += (p0[0] + p0[1]) + (p0[2] + p0[3]) + (p1[0] + p1[1]) + (p1[2] + p1[3]);
     const bf16x8 pB = pack44(p0, p1, 1.0f);
 
-    // value operand: lane i of 16-lane group kq takes latent dim 16t + i and
-    // keys {4kq+e} (lo) / {16+4kq+e} (hi); its tr16 source chunk is key row
-    // 4kq + i/4 (+16), dims 16t + 4(i%4) .. +3.
-    constexpr int CH = NJT < VCH ? NJT : VCH;
-    int tb = tr_base[0], tx = tr_rx;
-    asm volatile("" : "+v"(tb), "+v"(tx));
-    constexpr int VP = PF < NJT ? PF : NJT - 1;  // lookahead that exists
     if constexpr (VP > 0) {
       // value tiles t+1 .. t+VP are read while tile t's MFMA runs
-      auto rd = [&](int t) {
-        const MLA_LDS char* p = tile + tr_off(t, tb, tx);
-        return cat4(lds_read_tr16(p), lds_read_tr16(p + 16 * ROWB));
-      };
-      bf16x8 a[VP + 1];
-#pragma unroll
-      for (int u = 0; u < VP; ++u) a[u] = rd(u);
 #pragma unroll
       for (int t = 0; t < NJT; ++t) {
         if (t + VP < NJT) a[(t + VP) % (VP + 1)] = rd(t + VP);
@@ -302,17 +307,13 @@ struct WaveAttn {
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
+      constexpr int CH = NJT < VCH ? NJT : VCH;
 #pragma unroll
-    for (int t0 = 0; t0 < NJT; t0 += CH) {
+      for (int t0 = 0; t0 < NJT; t0 += CH) {
 #pragma unroll
-      for (int t = t0; t < t0 + CH; ++t) {
-        const MLA_LDS char* p = tile + tr_off(t, tb, tx);
-        const bf16x4 lo = lds_read_tr16(p);
-        const bf16x4 hi = lds_read_tr16(p + 16 * ROWB);
-        oT[t] = mfma16(cat4(lo, hi), pB, oT[t]);
+        for (int t = t0; t < t0 + CH; ++t) oT[t] = mfma16(rd(t), pB, oT[t]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
     }
   }
 };
@@ -529,24 +530,24 @@ struct PairAttn {
     }
   }
 
+  __device__ __forceinline__ bf16x8 value_operand(const MLA_LDS char* tile, int t) const {
+    const MLA_LDS char* p = tile + trb[t & 7] + (t >> 3) * 256;
+    return cat4(lds_read_tr16(p), lds_read_tr16(p + 16 * ROWB));
+  }
+
   // Value accumulation of this wave's latent half: O^T += c_tile^T P^T.
   __device__ __forceinline__ void values(const MLA_LDS char* tile, const bf16x8 (&pB)[2]) {
     asm volatile("" : "+v"(trb[0]), "+v"(trb[1]), "+v"(trb[2]), "+v"(trb[3]), "+v"(trb[4]), "+v"(trb[5]),
                       "+v"(trb[6]), "+v"(trb[7]));  // as in partial_scores
-    const int* bt = trb;
     if constexpr (VPF > 0) {
       // operands of value tiles t+1 .. t+VPF are read while the MFMAs of
       // tile t run
-      auto rd = [&](int t) {
-        const MLA_LDS char* p = tile + bt[t & 7] + (t >> 3) * 256;
-        return cat4(lds_read_tr16(p), lds_read_tr16(p + 16 * ROWB));
-      };
       bf16x8 a[VPF + 1];
 #pragma unroll
-      for (int u = 0; u < VPF; ++u) a[u] = rd(u);
+      for (int u = 0; u < VPF; ++u) a[u] = value_operand(tile, u);
 #pragma unroll
       for (int t = 0; t < NJT; ++t) {
-        if (t + VPF < NJT) a[(t + VPF) % (VPF + 1)] = rd(t + VPF);
+        if (t + VPF < NJT) a[(t + VPF) % (VPF + 1)] = value_operand(tile, t + VPF);
         __builtin_amdgcn_sched_barrier(0);
         oT[0][t] = mfma16(a[t % (VPF + 1)], pB[0], oT[0][t]);
         oT[1][t] = mfma16(a[t % (VPF + 1)], pB[1], oT[1][t]);
@@ -554,16 +555,15 @@ struct PairAttn {
       }
     } else {
 #pragma unroll
-    for (int t0 = 0; t0 < NJT; t0 += VCH) {
+      for (int t0 = 0; t0 < NJT; t0 += VCH) {
 #pragma unroll
-      for (int t = t0; t < t0 + VCH; ++t) {
-        const MLA_LDS char* p = tile + bt[t & 7] + (t >> 3) * 256;
-        const bf16x8 a = cat4(lds_read_tr16(p), lds_read_tr16(p + 16 * ROWB));
-        oT[0][t] = mfma16(a, pB[0], oT[0][t]);
-        oT[1][t] = mfma16(a, pB[1], oT[1][t]);
+        for (int t = t0; t < t0 + VCH; ++t) {
+          const bf16x8 a = value_operand(tile, t);
+          oT[0][t] = mfma16(a, pB[0], oT[0][t]);
+          oT[1][t] = mfma16(a, pB[1], oT[1][t]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
     }
   }
 };
