@@ -59,10 +59,11 @@ class Oracle:
         I, I64, D = ct.c_int, ct.c_int64, ct.c_double
         L.oracle_mutant.restype = I
         L.oracle_prefill.argtypes = [fp, fp, fp, fp, fp, I, I, I, I, I, I, D, i64p, I64, dp, I]
+        L.oracle_extend.argtypes = [fp, fp, fp, fp, fp, I, I, I, I, I, I, I, D, i64p, I64, dp, I]
         L.oracle_decode.argtypes = [fp, fp, i64p, fp, fp, fp, I, I, I, I, I, D, i64p, I64, dp, I]
         L.oracle_prefill_decompressed.argtypes = [fp, fp, fp, fp, fp, I, I, I, I, I, I, D, dp, I]
         L.oracle_prefill_attn.argtypes = [fp, fp, fp, I, I, I, I, I, D, dp]
-        for f in ("oracle_prefill", "oracle_decode", "oracle_prefill_decompressed",
+        for f in ("oracle_prefill", "oracle_extend", "oracle_decode", "oracle_prefill_decompressed",
                   "oracle_prefill_attn"):
             getattr(L, f).restype = I
 
@@ -95,6 +96,30 @@ class Oracle:
             _ptr(q, ct.c_float), _ptr(c, ct.c_float), _ptr(w_uk, ct.c_float), _ptr(w_uv, ct.c_float),
             _ptr(gate, ct.c_float), B, T, H, dq, dv, r, float(scale), rp, n,
             _ptr(out, ct.c_double), threads), "oracle_prefill")
+        return out
+
+    def extend(self, q, c, w_uk, w_uv, gate, scale: float, rows=None, threads: int = 0) -> np.ndarray:
+        """Chunked prefill: q [B,T,H,dq] are the last T positions of sequences
+        whose latent is c [B,S,r] (S >= T); query t attends to keys
+        0 .. S-T+t.  rows as for prefill.  Returns [B,T,H*dv] or
+        [len(rows), H*dv] (float64)."""
+        q, c, w_uk, w_uv, gate = map(_f32, (q, c, w_uk, w_uv, gate))
+        B, T, H, dq = q.shape
+        S, r = c.shape[1], c.shape[2]
+        dv = w_uv.shape[1]
+        assert c.shape == (B, S, r) and S >= T and w_uk.shape == (H, dq, r) and w_uv.shape == (H, dv, r)
+        assert gate.shape == (B, T, H * dv)
+        if rows is None:
+            out = np.empty((B, T, H * dv), dtype=np.float64)
+            rp, n = None, B * T
+        else:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            out = np.empty((rows.shape[0], H * dv), dtype=np.float64)
+            rp, n = _ptr(rows, ct.c_int64), rows.shape[0]
+        self._check(self.lib.oracle_extend(
+            _ptr(q, ct.c_float), _ptr(c, ct.c_float), _ptr(w_uk, ct.c_float), _ptr(w_uv, ct.c_float),
+            _ptr(gate, ct.c_float), B, T, S, H, dq, dv, r, float(scale), rp, n,
+            _ptr(out, ct.c_double), threads), "oracle_extend")
         return out
 
     def decode(self, q, c_cache, cu_seqlens, w_uk, w_uv, gate, scale: float, seqs=None,

@@ -31,6 +31,9 @@
  *               heads flattened head-major, the output projection is not applied)
  * The softmax scale is an explicit argument: the pages print none.
  *
+ * Chunked prefill (oracle_extend): the T queries of a chunk sit after a
+ * cached prefix of S - T positions and attend to it as well.
+ *
  * Decode: sequence i with cache rows c_cache[cu[i] .. cu[i+1]) is the same
  * computation for the query at position len_i - 1, which attends to all
  * len_i cached rows (its own latent included).
@@ -155,21 +158,27 @@ static void attend_row(const float* qrow, const float* keys, int64_t nkeys, cons
 }
 
 /*
- * Prefill.  q [B,T,H,dq], c [B,T,r], w_uk [H,dq,r], w_uv [H,dv,r],
- * gate [B,T,H*dv].  rows: nrows flattened indices b*T+t (NULL: every row in
- * order, nrows must be B*T).  out: [nrows, H*dv].
+ * Chunked prefill against a cached prefix (and, with S == T, plain prefill).
+ * Sequence b holds S latent rows c[b, 0..S); its T queries sit at positions
+ * P .. P+T-1 with P = S - T, and query t attends to keys 0 .. P+t (the
+ * causal mask of the MLA page, section 完整计算流（四步） step 2, measured
+ * from the chunk's first position).  q, gate and the output have T rows per
+ * sequence; rows[] (flattened b*T + t) selects which of them to compute, or
+ * all when rows == NULL.
  */
-int oracle_prefill(const float* q, const float* c, const float* w_uk, const float* w_uv,
-                   const float* gate, int B, int T, int H, int dq, int dv, int r, double scale,
-                   const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+int oracle_extend(const float* q, const float* c, const float* w_uk, const float* w_uv,
+                  const float* gate, int B, int T, int S, int H, int dq, int dv, int r, double scale,
+                  const int64_t* rows, int64_t nrows, double* out, int nthreads) {
   if (!q || !c || !w_uk || !w_uv || !gate || !out) return ORACLE_EINVAL;
-  if (B <= 0 || T <= 0 || H <= 0 || dq <= 0 || dv <= 0 || r <= 0 || nrows < 0) return ORACLE_EINVAL;
+  if (B <= 0 || T <= 0 || S < T || H <= 0 || dq <= 0 || dv <= 0 || r <= 0 || nrows < 0)
+    return ORACLE_EINVAL;
   if (!rows && nrows != (int64_t)B * T) return ORACLE_EINVAL;
   if (rows)
     for (int64_t i = 0; i < nrows; ++i)
       if (rows[i] < 0 || rows[i] >= (int64_t)B * T) return ORACLE_EINVAL;
   if (nthreads <= 0) nthreads = omp_get_max_threads();
-  const int64_t scratch_len = 2 * (int64_t)r + T;
+  const int64_t P = (int64_t)S - T;
+  const int64_t scratch_len = 2 * (int64_t)r + S;
   int err = ORACLE_OK;
 #pragma omp parallel num_threads(nthreads)
   {
@@ -185,17 +194,26 @@ int oracle_prefill(const float* q, const float* c, const float* w_uk, const floa
         const int64_t row = rows ? rows[i] : i;
         const int64_t b = row / T, t = row % T;
 #if ORACLE_MUTANT == 1
-        const int64_t nkeys = t; /* planted mistake: diagonal excluded */
+        const int64_t nkeys = P + t; /* planted mistake: diagonal excluded */
+#elif ORACLE_MUTANT == 11
+        const int64_t nkeys = t + 1; /* planted mistake: cached prefix ignored */
 #else
-        const int64_t nkeys = t + 1;
+        const int64_t nkeys = P + t + 1;
 #endif
-        attend_row(q + row * H * dq, c + b * (int64_t)T * r, nkeys, gate + row * H * dv, w_uk,
+        attend_row(q + row * H * dq, c + b * (int64_t)S * r, nkeys, gate + row * H * dv, w_uk,
                    w_uv, H, dq, dv, r, scale, scratch, out + i * (int64_t)H * dv);
       }
     }
     free(scratch);
   }
   return err;
+}
+
+/* Prefill: every position of B sequences of length T (no cached prefix). */
+int oracle_prefill(const float* q, const float* c, const float* w_uk, const float* w_uv,
+                   const float* gate, int B, int T, int H, int dq, int dv, int r, double scale,
+                   const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+  return oracle_extend(q, c, w_uk, w_uv, gate, B, T, T, H, dq, dv, r, scale, rows, nrows, out, nthreads);
 }
 
 /*

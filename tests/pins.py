@@ -248,6 +248,61 @@ def pin_golden_worked_examples(o):
         _close(got, expect, 1e-14, 1e-15, n)
 
 
+# ---------------------------------------------------------------- chunked prefill
+def dense_extend(q, c, w_uk, w_uv, gate, scale):
+    """dense_forward for a chunk of T queries after a cached prefix: c holds
+    S >= T rows per sequence and query t sits at position S - T + t."""
+    q, c, w_uk, w_uv, gate = [np.asarray(x, dtype=np.float64) for x in (q, c, w_uk, w_uv, gate)]
+    B, T, H, _ = q.shape
+    S = c.shape[1]
+    dv = w_uv.shape[1]
+    allowed = np.arange(S)[None, :] <= (S - T + np.arange(T))[:, None]  # [query, key]
+    out = np.zeros((B, T, H * dv))
+    for b in range(B):
+        for h in range(H):
+            logits = scale * ((q[b, :, h, :] @ w_uk[h]) @ c[b].T)
+            top = np.where(allowed, logits, -np.inf).max(axis=1, keepdims=True)
+            e = np.where(allowed, np.exp(np.where(allowed, logits - top, 0.0)), 0.0)
+            o = ((e / e.sum(axis=1, keepdims=True)) @ c[b]) @ w_uv[h].T
+            cols = slice(h * dv, (h + 1) * dv)
+            out[b, :, cols] = o / (1.0 + np.exp(-gate[b, :, cols]))
+    return out
+
+
+def pin_extend_matches_prefill_rows(o):
+    """A chunk of the last T positions over the whole latent equals rows
+    S-T .. S-1 of the prefill of the full sequence (T = S, 1 and between)."""
+    B, S, H, dq, dv, r = 2, 23, 3, 4, 5, 6
+    d = dg.prefill_inputs(B, S, H, dq, dv, r, dtype=dg.F32, seed=81)
+    full = o.prefill(*_args(d), 0.9)
+    q, c, wk, wv, g = _args(d)
+    for T in (S, 1, 9):
+        got = o.extend(q[:, S - T:], c, wk, wv, g[:, S - T:], 0.9)
+        _close(got, full[:, S - T:], 1e-13, 1e-15, f"extend T={T} vs prefill rows")
+
+
+def pin_extend_dense_brute_force(o):
+    """Chunked prefill equals the dense brute force with the prefix mask."""
+    for (B, T, S, H, dq, dv, r, scale, seed) in [(2, 5, 12, 2, 3, 4, 5, 0.7, 82), (1, 1, 7, 3, 2, 2, 4, 1.3, 83)]:
+        d = dg.prefill_inputs(B, S, H, dq, dv, r, dtype=dg.F32, seed=seed)
+        q, c, wk, wv, g = _args(d)
+        got = o.extend(q[:, S - T:], c, wk, wv, g[:, S - T:], scale)
+        _close(got, dense_extend(q[:, S - T:], c, wk, wv, g[:, S - T:], scale), 1e-12, 1e-14,
+               f"extend dense brute force T={T} S={S}")
+
+
+def pin_extend_one_query_is_decode(o):
+    """A one-query chunk is a decode step: it equals the decode routine over
+    the same latent laid out as a packed cache."""
+    B, S, H, dq, dv, r = 3, 11, 2, 4, 3, 5
+    d = dg.prefill_inputs(B, S, H, dq, dv, r, dtype=dg.F32, seed=84)
+    q, c, wk, wv, g = _args(d)
+    got = o.extend(q[:, S - 1:], c, wk, wv, g[:, S - 1:], 0.6)[:, 0]
+    cu = np.arange(B + 1, dtype=np.int64) * S
+    dec = o.decode(q[:, S - 1], c.reshape(B * S, r), cu, wk, wv, g[:, S - 1], 0.6)
+    _close(got, dec, 1e-13, 1e-15, "extend T=1 vs decode")
+
+
 ALL_PINS = [
     pin_absorbed_equals_decompressed,
     pin_attention_rows,
@@ -260,4 +315,7 @@ ALL_PINS = [
     pin_causality_and_independence,
     pin_head_permutation,
     pin_golden_worked_examples,
+    pin_extend_matches_prefill_rows,
+    pin_extend_dense_brute_force,
+    pin_extend_one_query_is_decode,
 ]

@@ -1,6 +1,7 @@
 """Each plausible mistake planted in the oracle (a dropped diagonal, a sign,
 a transposed weight, the flatten order, the gate sign, a missing scale or
-normalisation, the wrong key row, an off-by-one decode cache) must be caught
+normalisation, the wrong key row, an off-by-one decode cache, a chunk that ignores its
+cached prefix) must be caught
 by at least one pin.  Mutants are compiled on the CPU into a scratch dir."""
 import pytest
 
@@ -18,6 +19,7 @@ MUTANTS = {
     8: "softmax not normalised",
     9: "weighted sum uses the query's own latent row",
     10: "decode drops the newest cached row",
+    11: "chunked prefill ignores the cached prefix",
 }
 
 
