@@ -1,15 +1,16 @@
 """Benchmark of the absorbed Gated MLA hot path on one MI355X.
 
 One step = one full-width prefill call (B=1, T=8192, H=96, d_q=d_v=128,
-r=512, bf16, causal, scale 1/sqrt(d_q)) plus one full-width decode call
-(64 sequences with cache lengths ~ U[1024, 32768], same widths) on seeded
-synthetic inputs already resident in HBM.  Each call is bracketed by HIP
-events on the stream it runs on.
+r=512, bf16, causal, scale 1/sqrt(d_q)), one chunked-prefill call (the last
+2048 of those positions after the 6144 before them) and one full-width decode
+call (64 sequences with cache lengths ~ U[1024, 32768], same widths) on
+seeded synthetic inputs already resident in HBM.  Each call is bracketed by
+HIP events on the stream it runs on.
 
 Printed (one JSON line): prefill TFLOP/s as `value` (causal-triangle
-algorithmic FLOPs), decode latent-cache GB/s (algorithmic bytes), the
-roofline object of each against MI355X's published peaks, and the CPU oracle
-timed on a bounded row sample of the same workload.
+algorithmic FLOPs), chunked-prefill TFLOP/s, decode latent-cache GB/s
+(algorithmic bytes), the roofline object of each against MI355X's published
+peaks, and the CPU oracle timed on a bounded row sample of the prefill.
 """
 from __future__ import annotations
 
@@ -36,6 +37,14 @@ def prefill_flops(B, T, H, dq, dv, r):
     (b, t, h), and the score and latent-sum products on the causal triangle
     (diagonal included)."""
     pairs = B * H * T * (T + 1) // 2
+    return 2 * B * T * H * r * (dq + dv) + 4 * r * pairs
+
+
+def extend_flops(B, T, S, H, dq, dv, r):
+    """Algorithmic FLOPs of one chunked-prefill call: absorb + W_UV on the T
+    chunk rows, scores and latent sums over keys 0 .. S-T+t for each row."""
+    P = S - T
+    pairs = B * H * (T * P + T * (T + 1) // 2)
     return 2 * B * T * H * r * (dq + dv) + 4 * r * pairs
 
 
@@ -137,7 +146,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--which", choices=["both", "prefill", "decode"], default="both")
+    ap.add_argument("--which", choices=["both", "prefill", "decode"], default="both",
+                    help="both: prefill, chunked prefill and decode")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -168,6 +178,11 @@ def main():
                        device="cuda")
     D = [dev(dec[k]) for k in ("q", "c_cache", "cu_seqlens", "w_uk", "w_uv", "gate")]
     DB = dec["B"]
+    # chunked prefill: the last 2048 positions of the prefill workload as a
+    # chunk after 6144 cached positions
+    XT = 2048
+    X = [P[0][:, T - XT:].contiguous(), P[1], P[2], P[3], P[4][:, T - XT:].contiguous()]
+    x_out = torch.empty((B, XT, H * dv), dtype=torch.bfloat16, device="cuda")
     d_out = torch.empty((DB, H * dv), dtype=torch.bfloat16, device="cuda")
     d_ws = torch.empty(max(1, mla.decode_workspace_size(DB, H, dq, r, 0, mla.DTYPE_BF16)), dtype=torch.uint8,
                        device="cuda")
@@ -180,13 +195,17 @@ def main():
             ev[0].record()
             mla.mla_absorb_prefill(*P, pre["scale"], out=p_out, workspace=p_ws)
             ev[1].record()
+        if args.which == "both":
+            ev[4].record()
+            mla.mla_absorb_extend(*X, pre["scale"], out=x_out, workspace=p_ws)
+            ev[5].record()
         if do_dec:
             ev[2].record()
             mla.mla_absorb_decode(*D, dec["scale"], out=d_out, workspace=d_ws)
             ev[3].record()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    warm = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     for _ in range(args.warmup):
         step(warm)
     torch.cuda.synchronize()
@@ -212,7 +231,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(p_ms + d_ms, 4),
+        "ms_per_step": round(p_ms + d_ms + (float(np.mean([e[4].elapsed_time(e[5]) for e in evs]))
+                                           if args.which == "both" else 0.0), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -245,6 +265,16 @@ def main():
             res["decode"]["roofline"]["traffic"] = traffic["decode_bytes"]
     if args.copy_probe:
         copy_probe()
+    if args.which == "both":
+        x_ms = float(np.mean([e[4].elapsed_time(e[5]) for e in evs]))
+        xf = extend_flops(B, XT, T, H, dq, dv, r)
+        x_tf = xf / (x_ms * 1e-3) / 1e12
+        res["extend"] = {"value": round(x_tf, 2), "unit": "TFLOP/s", "ms": round(x_ms, 4),
+                         "workload": f"chunked prefill: {XT} queries after {T - XT} cached positions "
+                                     f"(S={T}), B={B}, H={H}, d_q=d_v={dq}, r={r}",
+                         "roofline": {"bound": "mfma", "achieved": round(x_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": round(x_tf / PEAK_BF16_TFLOPS, 4),
+                                      "traffic": None, "flop_per_launch": xf}}
     if not args.no_cpu_baseline and do_pre:
         res["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -88,6 +88,26 @@ mla_status mla_absorb_prefill(const void* q, const void* c, const void* w_uk, co
                               size_t workspace_bytes, void* stream);
 
 /*
+ * Chunked prefill against a cached prefix: the T queries of each sequence are
+ * its positions S-T .. S-1, and query t attends to latent rows 0 .. S-T+t
+ * (the causal softmax of page "Gated MLA（矩阵吸收版）", section
+ * 完整计算流（四步） step 2, for a chunk that follows S-T positions already in
+ * the latent cache; the pages cache only c, section 低秩压缩).  Prefill is the
+ * case S == T; a one-query chunk (T == 1) is a decode step.
+ *   q     [B, T, H, d_q]   queries of the chunk
+ *   c     [B, S, r]        latent of every position of each sequence,
+ *                          prefix first, the chunk's own rows last
+ *   gate, out [B, T, H*d_v]
+ *   w_uk, w_uv, scale      as for prefill
+ * Workspace: mla_absorb_prefill_workspace_size(B, T, H, d_q, r, dtype) bytes.
+ * Errors as for prefill; S < T is MLA_ERR_INVALID_ARG.
+ */
+mla_status mla_absorb_extend(const void* q, const void* c, const void* w_uk, const void* w_uv,
+                             const void* gate, void* out, int B, int T, int S, int H, int d_q, int d_v,
+                             int r, float scale, mla_dtype dtype, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of workspace mla_absorb_decode needs.  num_splits <= 0 selects the
  * library default (the device's compute-unit count, which queries the
  * current device).  Returns (size_t)-1 for invalid sizes.

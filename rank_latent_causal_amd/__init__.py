@@ -16,7 +16,8 @@ import os
 __all__ = [
     "LIB_PATH", "MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED", "MLA_ERR_WORKSPACE",
     "MLA_ERR_HIP", "DTYPE_F32", "DTYPE_BF16", "MLAError", "lib", "status_string",
-    "prefill_workspace_size", "decode_workspace_size", "mla_absorb_prefill", "mla_absorb_decode",
+    "prefill_workspace_size", "decode_workspace_size", "mla_absorb_prefill", "mla_absorb_extend",
+    "mla_absorb_decode",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_absorb.so")
@@ -28,6 +29,7 @@ EXPORTS = (
     "mla_status_string",
     "mla_absorb_prefill_workspace_size",
     "mla_absorb_prefill",
+    "mla_absorb_extend",
     "mla_absorb_decode_workspace_size",
     "mla_absorb_decode",
 )
@@ -55,6 +57,8 @@ def lib() -> ct.CDLL:
         L.mla_absorb_prefill_workspace_size.restype = sz
         L.mla_absorb_prefill.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, vp, sz, vp]
         L.mla_absorb_prefill.restype = I
+        L.mla_absorb_extend.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, I, F, I, vp, sz, vp]
+        L.mla_absorb_extend.restype = I
         L.mla_absorb_decode_workspace_size.argtypes = [I, I, I, I, I, I]
         L.mla_absorb_decode_workspace_size.restype = sz
         L.mla_absorb_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, I64, F, I, I, vp, sz, vp]
@@ -138,6 +142,34 @@ def mla_absorb_prefill(q, c, w_uk, w_uv, gate, scale: float, out=None, workspace
                                   _stream(stream))
     if st != MLA_OK:
         raise MLAError(st, "mla_absorb_prefill")
+    return out
+
+
+def mla_absorb_extend(q, c, w_uk, w_uv, gate, scale: float, out=None, workspace=None, stream=None):
+    """Chunked prefill against a cached prefix.  q [B,T,H,d_q] are positions
+    S-T .. S-1 of sequences whose latent is c [B,S,r] (S >= T), w_uk
+    [H,d_q,r], w_uv [H,d_v,r], gate [B,T,H*d_v] -> out [B,T,H*d_v]."""
+    torch = _torch()
+    B, T, H, dq = q.shape
+    S, r = c.shape[1], c.shape[2]
+    dv = w_uv.shape[1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    for t, shp, n in ((q, (B, T, H, dq), "q"), (c, (B, S, r), "c"), (w_uk, (H, dq, r), "w_uk"),
+                      (w_uv, (H, dv, r), "w_uv"), (gate, (B, T, H * dv), "gate")):
+        _check(t, shp, dt, n)
+    if out is None:
+        out = torch.empty((B, T, H * dv), dtype=dt, device=q.device)
+    _check(out, (B, T, H * dv), dt, "out")
+    need = prefill_workspace_size(B, T, H, dq, r, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().mla_absorb_extend(q.data_ptr(), c.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+                                 gate.data_ptr(), out.data_ptr(), B, T, S, H, dq, dv, r, float(scale),
+                                 code, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_absorb_extend")
     return out
 
 

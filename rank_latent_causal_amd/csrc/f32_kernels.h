@@ -14,13 +14,14 @@ namespace mla {
 
 struct F32Args {
   const float* q;      // prefill [B, T, H, DQ]   decode [B, H, DQ]
-  const float* c;      // prefill [B, T, R]       decode [N, R]
+  const float* c;      // prefill [B, S, R]       decode [N, R]
   const int* cu;       // decode only: [B + 1]
   const float* wuk;    // [H, DQ, R]
   const float* wuv;    // [H, DV, R]
   const float* gate;   // [rows, H*DV]
   float* out;          // [rows, H*DV]
   int B, T, H, DQ, DV, R;
+  int S;               // prefill: latent rows per sequence (S >= T; the T queries are the last T positions)
   long long N;         // decode: cache rows
   float scale;
   int decode;
@@ -48,8 +49,8 @@ __global__ void __launch_bounds__(64) mla_f32_kernel(F32Args a) {
   } else {
     const int b = row / a.T, t = row % a.T;
     key_lo = 0;
-    key_hi = t + 1;
-    keys = a.c + (size_t)b * a.T * R;
+    key_hi = (a.S - a.T) + t + 1;
+    keys = a.c + (size_t)b * a.S * R;
   }
   const float* qrow = a.q + ((size_t)row * H + h) * DQ;
   const float* wk = a.wuk + (size_t)h * DQ * R;

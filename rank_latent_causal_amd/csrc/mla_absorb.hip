@@ -127,14 +127,23 @@ mla_status mla_absorb_prefill(const void* q, const void* c, const void* w_uk, co
                               const void* gate, void* out, int B, int T, int H, int d_q, int d_v,
                               int r, float scale, mla_dtype dtype, void* workspace,
                               size_t workspace_bytes, void* stream) {
+  return mla_absorb_extend(q, c, w_uk, w_uv, gate, out, B, T, T, H, d_q, d_v, r, scale, dtype, workspace,
+                           workspace_bytes, stream);
+}
+
+mla_status mla_absorb_extend(const void* q, const void* c, const void* w_uk, const void* w_uv,
+                             const void* gate, void* out, int B, int T, int S, int H, int d_q, int d_v,
+                             int r, float scale, mla_dtype dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   if (!q || !c || !w_uk || !w_uv || !gate || !out) return MLA_ERR_INVALID_ARG;
-  if (B <= 0 || T <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || T <= 0 || S < T || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return MLA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(c) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(gate) ||
       !aligned16(out))
     return MLA_ERR_INVALID_ARG;
   if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return MLA_ERR_INVALID_ARG;
-  if (!fits(B, T, H, d_q > d_v ? (d_q > r ? d_q : r) : (d_v > r ? d_v : r))) return MLA_ERR_UNSUPPORTED;
+  if (!fits(B, T, H, d_q > d_v ? (d_q > r ? d_q : r) : (d_v > r ? d_v : r)) || !fits(B, S, r))
+    return MLA_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
 
   if (dtype == MLA_DTYPE_F32) {
@@ -144,7 +153,8 @@ mla_status mla_absorb_prefill(const void* q, const void* c, const void* w_uk, co
     a.q = (const float*)q; a.c = (const float*)c; a.cu = nullptr;
     a.wuk = (const float*)w_uk; a.wuv = (const float*)w_uv; a.gate = (const float*)gate;
     a.out = (float*)out;
-    a.B = B; a.T = T; a.H = H; a.DQ = d_q; a.DV = d_v; a.R = r; a.N = 0; a.scale = scale; a.decode = 0;
+    a.B = B; a.T = T; a.S = S; a.H = H; a.DQ = d_q; a.DV = d_v; a.R = r; a.N = 0; a.scale = scale;
+    a.decode = 0;
     hipLaunchKernelGGL(mla::mla_f32_kernel, dim3(B * T, H), dim3(64), 0, s, a);
     return launch_status();
   }
@@ -162,7 +172,7 @@ mla_status mla_absorb_prefill(const void* q, const void* c, const void* w_uk, co
   mla::PrefillArgs a{};
   a.q = (const bf16*)q; a.c = (const bf16*)c; a.wukT = wukT; a.wuv = (const bf16*)w_uv;
   a.gate = (const bf16*)gate; a.out = (bf16*)out;
-  a.B = B; a.T = T; a.H = H;
+  a.B = B; a.T = T; a.S = S; a.H = H;
   a.qscale = scale * mla::kLog2e;
   if (d_q == 16) launch_prefill_bf16<16, 16, 32>(a, s);
   else if (d_q == 64) launch_prefill_bf16<64, 64, 256>(a, s);

@@ -21,12 +21,13 @@ namespace mla {
 
 struct PrefillArgs {
   const bf16* q;     // [B, T, H, DQ]
-  const bf16* c;     // [B, T, R]
+  const bf16* c;     // [B, S, R]: the T queries are positions S-T .. S-1
   const bf16* wukT;  // [H, R, DQ]  (W_UK transposed per head, in the workspace)
   const bf16* wuv;   // [H, DV, R]
   const bf16* gate;  // [B, T, H*DV]
   bf16* out;         // [B, T, H*DV]
   int B, T, H;
+  int S;             // latent rows per sequence (S >= T; S - T cached prefix positions)
   float qscale;      // softmax scale * log2(e), folded into q_abs
   int ntb;           // ceil(T / kPrefillRows) query blocks
   int nhg;           // ceil(H / 4) head groups
@@ -78,14 +79,15 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
   const int t = tw + l16;       // this lane's query row
   const bool tvalid = t < T;
   const int tc = tvalid ? t : T - 1;
-  const bf16* __restrict__ cb = a.c + (size_t)b * T * R;
+  const int S = a.S, P = S - T;  // query t sits at position P + t
+  const bf16* __restrict__ cb = a.c + (size_t)b * S * R;
 
-  const int ntiles = (min(t0 + kPrefillRows, T) + LT::KT - 1) / LT::KT;
+  const int ntiles = (P + min(t0 + kPrefillRows, T) + LT::KT - 1) / LT::KT;
 
   // stream the first latent tile while the absorb prologue runs
   TileCopier<R, kPrefillWaves> copier;
   copier.init(w, lane);
-  copier.issue(cb, 0, T, smem);
+  copier.issue(cb, 0, S, smem);
 
   WaveAttn<R> st;
   absorb_rows<DQ, R>(a.q + (((size_t)b * T + tc) * H + hc) * DQ, a.wukT + (size_t)hc * R * DQ, a.qscale,
@@ -95,7 +97,7 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
 
   for (int it = 0; it < ntiles; ++it) {
     if (it + 1 < ntiles) {
-      copier.issue(cb, (it + 1) * LT::KT, T, smem + ((it + 1) & 1) * LT::BYTES);
+      copier.issue(cb, (it + 1) * LT::KT, S, smem + ((it + 1) & 1) * LT::BYTES);
       wait_vmcnt<LPW>();
     } else {
       wait_vmcnt<0>();
@@ -105,11 +107,11 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
     const int s0 = it * LT::KT;
     f32x4 sa, sb;
     st.scores(tile, sa, sb);
-    if (s0 + LT::KT - 1 > tw) {  // causal mask (also hides keys past T)
+    if (s0 + LT::KT - 1 > P + tw) {  // causal mask (also hides keys past S)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (s0 + 4 * kq + e > t) sa[e] = -INFINITY;
-        if (s0 + 16 + 4 * kq + e > t) sb[e] = -INFINITY;
+        if (s0 + 4 * kq + e > P + t) sa[e] = -INFINITY;
+        if (s0 + 16 + 4 * kq + e > P + t) sb[e] = -INFINITY;
       }
     }
     st.update(tile, sa, sb);
@@ -189,14 +191,15 @@ mla_prefill_pair_kernel(PrefillArgs a) {
     tq[c] = t0 + 16 * c + l16;
     tv[c] = tq[c] < T;
   }
-  const bf16* __restrict__ cb = a.c + (size_t)b * T * R;
-  const int ntiles = (min(t0 + 32, T) + LT::KT - 1) / LT::KT;
+  const int S = a.S, P = S - T;  // query t sits at position P + t
+  const bf16* __restrict__ cb = a.c + (size_t)b * S * R;
+  const int ntiles = (P + min(t0 + 32, T) + LT::KT - 1) / LT::KT;
 
   TileCopier<R, NW> copier;
   copier.init(w, lane);
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
-    if (p < ntiles) copier.issue(cb, p * LT::KT, T, smem + p * LT::BYTES);
+    if (p < ntiles) copier.issue(cb, p * LT::KT, S, smem + p * LT::BYTES);
 
   PA st;
   {
@@ -243,7 +246,7 @@ mla_prefill_pair_kernel(PrefillArgs a) {
     // this tile rather than right after the first one, where every wave of
     // the workgroup would queue its copies at the same moment.
     if (it + NS - 1 < ntiles)
-      copier.issue(cb, (it + NS - 1) * LT::KT, T, smem + ((STG + NS - 1) % NS) * LT::BYTES);
+      copier.issue(cb, (it + NS - 1) * LT::KT, S, smem + ((STG + NS - 1) % NS) * LT::BYTES);
     {
       const f32x4 o00 = xbuf[(partner * 4 + 0) * 64 + lane], o01 = xbuf[(partner * 4 + 1) * 64 + lane];
       const f32x4 o10 = xbuf[(partner * 4 + 2) * 64 + lane], o11 = xbuf[(partner * 4 + 3) * 64 + lane];
@@ -256,13 +259,13 @@ mla_prefill_pair_kernel(PrefillArgs a) {
       }
     }
     const int s0 = it * LT::KT;
-    if (s0 + LT::KT - 1 > t0) {  // causal mask on the diagonal tile (also hides keys past T)
+    if (s0 + LT::KT - 1 > P + t0) {  // causal mask on the diagonal tile (also hides keys past S)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (s0 + 4 * kq + e > tq[c]) sc[c][0][e] = -INFINITY;
-          if (s0 + 16 + 4 * kq + e > tq[c]) sc[c][1][e] = -INFINITY;
+          if (s0 + 4 * kq + e > P + tq[c]) sc[c][0][e] = -INFINITY;
+          if (s0 + 16 + 4 * kq + e > P + tq[c]) sc[c][1][e] = -INFINITY;
         }
       }
     }

@@ -47,6 +47,25 @@ def run_prefill(d, scale=None):
     return out
 
 
+def run_extend(d, T, scale=None):
+    """The last T positions of each sequence of prefill-shaped inputs d as a
+    chunk over the whole latent (S = d's T rows)."""
+    import rank_latent_causal_amd as mla
+    S = d["T"]
+    args = [to_dev(d["q"][:, S - T:]), to_dev(d["c"]), to_dev(d["w_uk"]), to_dev(d["w_uv"]),
+            to_dev(d["gate"][:, S - T:])]
+    out = mla.mla_absorb_extend(*args, d["scale"] if scale is None else scale)
+    torch().cuda.synchronize()
+    return out
+
+
+def oracle_extend(o, d, T, rows=None, scale=None):
+    f = dg.as_f32
+    S = d["T"]
+    return o.extend(f(d["q"])[:, S - T:], f(d["c"]), f(d["w_uk"]), f(d["w_uv"]), f(d["gate"])[:, S - T:],
+                    d["scale"] if scale is None else scale, rows=rows)
+
+
 def run_decode(d, scale=None, num_splits=0):
     import rank_latent_causal_amd as mla
     args = [to_dev(d["q"]), to_dev(d["c_cache"]), to_dev(d["cu_seqlens"]), to_dev(d["w_uk"]),

@@ -113,3 +113,24 @@ def test_prefill_rejects(kw, status):
 ])
 def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
+
+
+def _extend(**kw):
+    a = dict(q=FAKE, c=FAKE, w_uk=FAKE, w_uv=FAKE, gate=FAKE, out=FAKE, B=1, T=8, S=20, H=4, dq=128, dv=128,
+             r=512, scale=0.1, dtype=mla.DTYPE_BF16, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return mla.lib().mla_absorb_extend(a["q"], a["c"], a["w_uk"], a["w_uv"], a["gate"], a["out"], a["B"],
+                                       a["T"], a["S"], a["H"], a["dq"], a["dv"], a["r"], a["scale"],
+                                       a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=7), mla.MLA_ERR_INVALID_ARG),           # fewer latent rows than queries
+    (dict(T=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(c=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mla.MLA_ERR_INVALID_ARG),
+    (dict(dq=96, dv=96, r=384), mla.MLA_ERR_UNSUPPORTED),
+    (dict(wsb=16), mla.MLA_ERR_WORKSPACE),
+])
+def test_extend_rejects(kw, status):
+    assert _extend(**kw) == status

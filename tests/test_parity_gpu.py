@@ -9,8 +9,8 @@ import pytest
 
 import datagen as dg
 import oracle
-from gpu_util import (assert_parity, oracle_decode, oracle_prefill, run_decode, run_prefill, sample_rows,
-                      to_host_f64)
+from gpu_util import (assert_parity, oracle_decode, oracle_extend, oracle_prefill, run_decode, run_extend,
+                      run_prefill, sample_rows, to_host_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -238,3 +238,45 @@ def test_side_stream_and_workspace_reuse():
         out_d = mla.mla_absorb_decode(*D, 0.1, workspace=ws, stream=side)
     side.synchronize()
     assert torch.equal(out_p, ref_p) and torch.equal(out_d, ref_d)
+
+
+# ------------------------------------------------------------------ chunked prefill
+@pytest.mark.parametrize("B,T,S,H,shape", [
+    (1, 1, 1, 1, "toy"), (2, 37, 100, 3, "toy"),
+    (1, 45, 45, 2, "mid"), (2, 30, 161, 9, "mid"),
+    (2, 70, 200, 5, "full"), (1, 33, 1000, 8, "full"), (3, 1, 77, 4, "full"), (1, 130, 131, 8, "full"),
+])
+def test_extend_bf16_ragged(o, B, T, S, H, shape):
+    dq, dv, r = SHAPES[shape]
+    d = dg.prefill_inputs(B, S, H, dq, dv, r, dtype=dg.BF16, seed=6000 + B * 7 + T + S + H)
+    d["scale"] = dq ** -0.5
+    log(f"extend bf16 B={B} T={T} S={S} H={H} r={r}")
+    got = to_host_f64(run_extend(d, T))
+    assert_parity(got, oracle_extend(o, d, T), dg.BF16, f"extend {shape} B{B} T{T} S{S} H{H}")
+
+
+def test_extend_f32(o):
+    d = dg.prefill_inputs(2, 61, 3, 16, 16, 32, dtype=dg.F32, seed=6100)
+    log("extend f32 toy T=20 S=61")
+    got = to_host_f64(run_extend(d, 20, scale=0.7))
+    assert_parity(got, oracle_extend(o, d, 20, scale=0.7), dg.F32, "extend f32")
+
+
+def test_extend_without_prefix_is_prefill():
+    """S == T runs the prefill path: identical bits."""
+    d = dg.prefill_inputs(2, 90, 6, 128, 128, 512, dtype=dg.BF16, seed=6200)
+    d["scale"] = 128 ** -0.5
+    log("extend S == T vs prefill")
+    import torch
+    assert torch.equal(run_extend(d, 90), run_prefill(d))
+
+
+def test_extend_full_width_sampled(o):
+    """A 2048-query chunk after 6144 cached positions at the full widths."""
+    S, T = 8192, 2048
+    d = dg.prefill_inputs(1, S, 96, 128, 128, 512, dtype=dg.BF16, seed=6300)
+    d["scale"] = 128 ** -0.5
+    log(f"extend full width T={T} S={S} H=96 (sampled rows)")
+    got = to_host_f64(run_extend(d, T)).reshape(T, -1)
+    rows = sample_rows(1, T, 4, seed=7)
+    assert_parity(got[rows], oracle_extend(o, d, T, rows=rows), dg.BF16, "extend full sampled")
