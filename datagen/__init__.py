@@ -17,6 +17,11 @@ toy/full-size table of the "K3 混合架构" page):
 * ``W_UK [H,d_q,r]`` and ``W_UV [H,d_v,r]`` are ``N(0, 1/r)``;
 * ``gate`` (pre-sigmoid logits) ``~ N(0,1)`` with shape ``[B,T,H*d_v]`` or
   ``[B,H*d_v]``;
+* full-layer forward: ``x ~ N(0,1)`` ``[B,T,D]``; every projection weight
+  (``W_kv_down [r,D]``, ``W_q_down [q_rank,D]``, ``W_q_up [H*d_q,q_rank]``,
+  ``W_gate [H*d_v,D]``, ``W_o [D,H*d_v]``) is ``N(0, 1/in_features)``, so
+  the gate logits and q come out near ``N(0,1)`` as above; the two norm
+  gains are ``1 + N(0, 0.01)``;
 * decode cache lengths are i.i.d. uniform integers on ``[len_lo, len_hi]``;
   ``cu_seqlens`` is their int32 exclusive prefix sum;
 * float64 draws are rounded to float32 (round-to-nearest-even) and, for bf16
@@ -36,7 +41,8 @@ import numpy as np
 F32 = "f32"
 BF16 = "bf16"
 
-_TID = {"q": 1, "c": 2, "w_uk": 3, "w_uv": 4, "gate": 5, "lens": 6}
+_TID = {"q": 1, "c": 2, "w_uk": 3, "w_uv": 4, "gate": 5, "lens": 6, "x": 7, "w_kv_down": 8,
+        "kv_norm": 9, "w_q_down": 10, "q_norm": 11, "w_q_up": 12, "w_gate": 13, "w_o": 14}
 _CHUNK_ELEMS = 1 << 21
 _RMS_EPS = 1e-6
 
@@ -75,7 +81,7 @@ def _store(x64: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def _draw_rows(seed: int, name: str, rows: int, cols: int, std: float, dtype: str,
-               rms_norm: bool = False) -> np.ndarray:
+               rms_norm: bool = False, mean: float = 0.0) -> np.ndarray:
     """rows x cols standard-normal draw (times std), chunked by rows."""
     out = np.empty((rows, cols), dtype=np.uint16 if dtype == BF16 else np.float32)
     chunk_rows = max(1, _CHUNK_ELEMS // cols)
@@ -91,6 +97,8 @@ def _draw_rows(seed: int, name: str, rows: int, cols: int, std: float, dtype: st
             x = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + _RMS_EPS)
         elif std != 1.0:
             x = x * std
+        if mean != 0.0:
+            x = x + mean
         out[r0:r1] = _store(x, dtype)
 
     workers = min(nchunks, int(os.environ.get("DATAGEN_THREADS", "8")))
@@ -115,6 +123,30 @@ def prefill_inputs(B: int, T: int, H: int, d_q: int, d_v: int, r: int,
     gate = _draw_rows(seed, "gate", B * T, H * d_v, 1.0, dtype).reshape(B, T, H * d_v)
     return dict(q=q, c=c, w_uk=w_uk, w_uv=w_uv, gate=gate,
                 B=B, T=T, H=H, d_q=d_q, d_v=d_v, r=r, dtype=dtype, seed=seed)
+
+
+def forward_inputs(B: int, T: int, D: int, q_rank: int, H: int, d_q: int, d_v: int, r: int,
+                   dtype: str = BF16, seed: int = 0) -> dict:
+    """Inputs of one full-layer forward: the activations x and every weight,
+    laid out as linear layers (out_features x in_features)."""
+    if min(B, T, D, q_rank, H, d_q, d_v, r) <= 0:
+        raise ValueError("all sizes must be positive")
+    x = _draw_rows(seed, "x", B * T, D, 1.0, dtype).reshape(B, T, D)
+    w_kv_down = _draw_rows(seed, "w_kv_down", r, D, D ** -0.5, dtype)
+    kv_norm = _draw_rows(seed, "kv_norm", 1, r, 0.1, dtype, mean=1.0).reshape(r)
+    w_q_down = _draw_rows(seed, "w_q_down", q_rank, D, D ** -0.5, dtype)
+    q_norm = _draw_rows(seed, "q_norm", 1, q_rank, 0.1, dtype, mean=1.0).reshape(q_rank)
+    w_q_up = _draw_rows(seed, "w_q_up", H * d_q, q_rank, q_rank ** -0.5, dtype)
+    w_uk = _draw_rows(seed, "w_uk", H * d_q, r, r ** -0.5, dtype).reshape(H, d_q, r)
+    w_uv = _draw_rows(seed, "w_uv", H * d_v, r, r ** -0.5, dtype).reshape(H, d_v, r)
+    w_gate = _draw_rows(seed, "w_gate", H * d_v, D, D ** -0.5, dtype)
+    w_o = _draw_rows(seed, "w_o", D, H * d_v, (H * d_v) ** -0.5, dtype)
+    return dict(x=x, w_kv_down=w_kv_down, kv_norm=kv_norm, w_q_down=w_q_down, q_norm=q_norm,
+                w_q_up=w_q_up, w_uk=w_uk, w_uv=w_uv, w_gate=w_gate, w_o=w_o,
+                B=B, T=T, D=D, q_rank=q_rank, H=H, d_q=d_q, d_v=d_v, r=r, dtype=dtype, seed=seed)
+
+
+FORWARD_KEYS = ("x", "w_kv_down", "kv_norm", "w_q_down", "q_norm", "w_q_up", "w_uk", "w_uv", "w_gate", "w_o")
 
 
 def decode_lengths(B: int, len_lo: int, len_hi: int, seed: int = 0) -> np.ndarray:
@@ -163,6 +195,12 @@ WORKLOADS = {
                          dtype=BF16, scale=128 ** -0.5, seed=SEED_BASE + 3),
     "full_decode": dict(kind="decode", B=64, H=96, d_q=128, d_v=128, r=512, dtype=BF16,
                         len_lo=1024, len_hi=32768, scale=128 ** -0.5, seed=SEED_BASE + 4),
+    # the whole layer at the pages' toy and full widths (D, q_lora_rank from
+    # the toy/full table of the "K3 混合架构" page)
+    "toy_forward": dict(kind="forward", B=2, T=128, D=256, q_rank=64, H=8, d_q=16, d_v=16, r=32,
+                        dtype=BF16, scale=16 ** -0.5, eps=1e-6, seed=SEED_BASE + 5),
+    "full_forward": dict(kind="forward", B=1, T=8192, D=7168, q_rank=1536, H=96, d_q=128, d_v=128,
+                         r=512, dtype=BF16, scale=128 ** -0.5, eps=1e-6, seed=SEED_BASE + 6),
 }
 
 
@@ -170,8 +208,12 @@ def workload_inputs(name: str) -> dict:
     w = dict(WORKLOADS[name])
     kind = w.pop("kind")
     scale = w.pop("scale")
+    eps = w.pop("eps", None)
     if kind == "prefill":
         d = prefill_inputs(**w)
+    elif kind == "forward":
+        d = forward_inputs(**w)
+        d["eps"] = eps
     else:
         d = decode_inputs(**w)
     d["scale"] = scale

@@ -63,8 +63,10 @@ class Oracle:
         L.oracle_decode.argtypes = [fp, fp, i64p, fp, fp, fp, I, I, I, I, I, D, i64p, I64, dp, I]
         L.oracle_prefill_decompressed.argtypes = [fp, fp, fp, fp, fp, I, I, I, I, I, I, D, dp, I]
         L.oracle_prefill_attn.argtypes = [fp, fp, fp, I, I, I, I, I, D, dp]
+        L.oracle_round_bf16.argtypes = [dp, I64, dp]
+        L.oracle_forward.argtypes = [fp] * 10 + [I] * 8 + [D, D, I, i64p, I64] + [dp] * 5 + [I]
         for f in ("oracle_prefill", "oracle_extend", "oracle_decode", "oracle_prefill_decompressed",
-                  "oracle_prefill_attn"):
+                  "oracle_prefill_attn", "oracle_round_bf16", "oracle_forward"):
             getattr(L, f).restype = I
 
     @property
@@ -166,6 +168,53 @@ class Oracle:
             _ptr(q, ct.c_float), _ptr(c, ct.c_float), _ptr(w_uk, ct.c_float), B, T, H, dq, r,
             float(scale), _ptr(out, ct.c_double)), "oracle_prefill_attn")
         return out
+
+    def round_bf16(self, v) -> np.ndarray:
+        """Nearest bf16 value of each element (ties to even), as float64."""
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        out = np.empty_like(v)
+        self._check(self.lib.oracle_round_bf16(_ptr(v, ct.c_double), v.size, _ptr(out, ct.c_double)),
+                    "oracle_round_bf16")
+        return out
+
+    STAGE_F32 = 0
+    STAGE_BF16 = 1
+
+    def forward(self, x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o,
+                eps: float, scale: float, stage: int = 0, rows=None, stages: bool = False,
+                threads: int = 0):
+        """Full Gated MLA forward: x [B,T,D] -> y [B,T,D] (rows None) or
+        [len(rows), D] (float64).  stage: STAGE_F32 / STAGE_BF16, the
+        storage type of the stage results.  stages=True also returns a dict
+        with c [B*T,r], q [n,H*dq], gate [n,H*dv] and o [n,H*dv] as stored."""
+        x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o = map(
+            _f32, (x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o))
+        B, T, D = x.shape
+        r = w_kv_down.shape[0]
+        q_rank = w_q_down.shape[0]
+        H, dq, _ = w_uk.shape
+        dv = w_uv.shape[1]
+        assert w_kv_down.shape == (r, D) and kv_norm.shape == (r,)
+        assert w_q_down.shape == (q_rank, D) and q_norm.shape == (q_rank,)
+        assert w_q_up.shape == (H * dq, q_rank) and w_uk.shape == (H, dq, r) and w_uv.shape == (H, dv, r)
+        assert w_gate.shape == (H * dv, D) and w_o.shape == (D, H * dv)
+        if rows is None:
+            rp, n = None, B * T
+        else:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            rp, n = _ptr(rows, ct.c_int64), rows.shape[0]
+        y = np.empty((n, D), dtype=np.float64)
+        st = dict(c=np.empty((B * T, r)), q=np.empty((n, H * dq)), gate=np.empty((n, H * dv)),
+                  o=np.empty((n, H * dv))) if stages else None
+        sp = [(_ptr(st[k], ct.c_double) if stages else None) for k in ("c", "q", "gate", "o")]
+        self._check(self.lib.oracle_forward(
+            *[_ptr(a, ct.c_float) for a in (x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv,
+                                             w_gate, w_o)],
+            B, T, D, q_rank, H, dq, dv, r, float(eps), float(scale), int(stage), rp, n,
+            _ptr(y, ct.c_double), *sp, threads), "oracle_forward")
+        if rows is None:
+            y = y.reshape(B, T, D)
+        return (y, st) if stages else y
 
 
 _default = None

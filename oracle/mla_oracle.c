@@ -393,3 +393,235 @@ int oracle_prefill_attn(const float* q, const float* c, const float* w_uk, int B
   free(s);
   return ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * Full Gated MLA forward around the absorbed core ([MLA] section 低秩压缩 for
+ * the latent, section 完整计算流（四步） step 1 for the query low-rank path,
+ * step 4 for the gate and the output projection, the parameter table of
+ * section 形状与参数对比 for the weight layouts):
+ *
+ *   c    = RMSNorm_kv(x W_kv_down^T)       [N, r]        (N = B*T rows)
+ *   ql   = RMSNorm_q(x W_q_down^T)         [N, q_rank]
+ *   q    = ql W_q_up^T                     [N, H*dq], viewed [B, T, H, dq]
+ *   g    = x W_gate^T                      [N, H*dv]    (gate logits)
+ *   o    = steps 1-6 above on (q, c, g)    [N, H*dv]
+ *   y    = o W_o^T                         [N, D]
+ *
+ * Every weight is a linear layer without bias (the pages show none), laid out
+ * out_features x in_features.  RMSNorm(v) = v / sqrt(mean_j v_j^2 + eps),
+ * times a per-feature gain (the pages name the norm without writing it out;
+ * eps is an argument).
+ *
+ * Storage of the stage results: the core consumes stored values, as every
+ * other entry of this file does.  stage_dtype selects the activation type of
+ * the layer: ORACLE_STAGE_F32 rounds each stored stage result to float32,
+ * ORACLE_STAGE_BF16 to bf16 (round to nearest, ties to even).  Rounded are:
+ * the two down-projections (before their norms), the norms' outputs, q, g and
+ * o; y is returned unrounded.  Everything between two stores is float64.
+ */
+#define ORACLE_STAGE_F32 0
+#define ORACLE_STAGE_BF16 1
+
+#define BF16_MAX 3.3895313892515355e38 /* (2 - 2^-7) 2^127 */
+
+/* Nearest bf16 value of v, ties to even.  bf16 keeps 8 significant bits and
+ * float32's exponent range (quantum 2^-133 below 2^-126). */
+static double round_bf16(double v) {
+  if (!isfinite(v) || v == 0.0) return v;
+  int e;
+  const double m = frexp(v, &e); /* v = m 2^e, 0.5 <= |m| < 1 */
+  const int shift = (e - 8 < -133) ? e + 133 : 8;
+#if ORACLE_MUTANT == 19
+  const double n = round(ldexp(m, shift)); /* planted mistake: ties away from zero */
+#else
+  const double n = nearbyint(ldexp(m, shift)); /* the default mode rounds ties to even */
+#endif
+  const double r = ldexp(n, e - shift);
+  return fabs(r) > BF16_MAX ? copysign(INFINITY, v) : r;
+}
+
+static double store(double v, int stage_dtype) {
+  return stage_dtype == ORACLE_STAGE_BF16 ? round_bf16(v) : (double)(float)v;
+}
+
+int oracle_round_bf16(const double* in, int64_t n, double* out) {
+  if ((!in || !out) && n > 0) return ORACLE_EINVAL;
+  for (int64_t i = 0; i < n; ++i) out[i] = round_bf16(in[i]);
+  return ORACLE_OK;
+}
+
+/* out[i, n] = sum_k in[i, k] W[n, k] for N outputs over K inputs (a linear
+ * layer, weight [N, K]); `transposed` is only set by planted mistakes, which
+ * read W as [K, N]. */
+static void linear(const double* in, int64_t M, int K, const float* W, int N, int transposed,
+                   double* out, int nthreads) {
+#pragma omp parallel for collapse(2) schedule(static) num_threads(nthreads)
+  for (int64_t i = 0; i < M; ++i)
+    for (int n = 0; n < N; ++n) {
+      const double* xi = in + i * K;
+      double acc = 0.0;
+      if (transposed) {
+        for (int k = 0; k < K; ++k) acc += xi[k] * (double)W[(int64_t)k * N + n];
+      } else {
+        const float* wn = W + (int64_t)n * K;
+#pragma omp simd reduction(+ : acc)
+        for (int k = 0; k < K; ++k) acc += xi[k] * (double)wn[k];
+      }
+      out[i * N + n] = acc;
+    }
+}
+
+/* Row-wise RMSNorm with gain, in place on M rows of n features.  which: 0 for
+ * the latent's norm, 1 for the query's (planted mistakes pick one). */
+static void rmsnorm_rows(double* v, int64_t M, int n, const float* gain, double eps, int which) {
+  for (int64_t i = 0; i < M; ++i) {
+    double* row = v + i * n;
+#if ORACLE_MUTANT == 13
+    if (which == 0)
+      for (int j = 0; j < n; ++j) row[j] *= (double)gain[j]; /* planted: gain inside the norm */
+#endif
+    double ss = 0.0;
+    for (int j = 0; j < n; ++j) ss += row[j] * row[j];
+#if ORACLE_MUTANT == 18
+    const double inv = 1.0 / sqrt(ss + eps); /* planted mistake: sum instead of mean */
+#else
+    const double inv = 1.0 / sqrt(ss / n + eps);
+#endif
+#if ORACLE_MUTANT == 12
+    if (which == 0) {
+      for (int j = 0; j < n; ++j) row[j] *= (double)gain[j]; /* planted: latent not normalised */
+      continue;
+    }
+#elif ORACLE_MUTANT == 14
+    if (which == 1) {
+      for (int j = 0; j < n; ++j) row[j] *= (double)gain[j]; /* planted: query latent not normalised */
+      continue;
+    }
+#endif
+    for (int j = 0; j < n; ++j) {
+#if ORACLE_MUTANT == 13
+      row[j] = which == 0 ? row[j] * inv : row[j] * inv * (double)gain[j];
+#else
+      row[j] = row[j] * inv * (double)gain[j];
+#endif
+    }
+    (void)which;
+  }
+}
+
+static void store_all(double* v, int64_t n, int stage_dtype) {
+  for (int64_t i = 0; i < n; ++i) v[i] = store(v[i], stage_dtype);
+}
+
+/*
+ * x [B,T,D]; weights as listed above; rows[] (flattened b*T + t) selects the
+ * output rows (NULL: all B*T).  The latent c is formed for every position
+ * (it is every query's key set); q, g, o and y only for the selected rows.
+ * y: [nrows, D].  Optional stage outputs (NULL to skip): c_out [B*T, r],
+ * q_out [nrows, H*dq], g_out and o_out [nrows, H*dv], all as stored.
+ */
+int oracle_forward(const float* x, const float* w_kv_down, const float* kv_norm, const float* w_q_down,
+                   const float* q_norm, const float* w_q_up, const float* w_uk, const float* w_uv,
+                   const float* w_gate, const float* w_o, int B, int T, int D, int q_rank, int H, int dq,
+                   int dv, int r, double eps, double scale, int stage_dtype, const int64_t* rows,
+                   int64_t nrows, double* y, double* c_out, double* q_out, double* g_out, double* o_out,
+                   int nthreads) {
+  if (!x || !w_kv_down || !kv_norm || !w_q_down || !q_norm || !w_q_up || !w_uk || !w_uv || !w_gate ||
+      !w_o || !y)
+    return ORACLE_EINVAL;
+  if (B <= 0 || T <= 0 || D <= 0 || q_rank <= 0 || H <= 0 || dq <= 0 || dv <= 0 || r <= 0 || nrows < 0 ||
+      !(eps >= 0.0))
+    return ORACLE_EINVAL;
+  if (stage_dtype != ORACLE_STAGE_F32 && stage_dtype != ORACLE_STAGE_BF16) return ORACLE_EINVAL;
+  const int64_t N = (int64_t)B * T;
+  if (!rows && nrows != N) return ORACLE_EINVAL;
+  if (rows)
+    for (int64_t i = 0; i < nrows; ++i)
+      if (rows[i] < 0 || rows[i] >= N) return ORACLE_EINVAL;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  const int HQ = H * dq, HV = H * dv;
+
+  double* xd = (double*)malloc(sizeof(double) * (size_t)N * D);
+  double* xs = (double*)malloc(sizeof(double) * (size_t)(nrows ? nrows : 1) * D);
+  double* c = (double*)malloc(sizeof(double) * (size_t)N * r);
+  double* ql = (double*)malloc(sizeof(double) * (size_t)(nrows ? nrows : 1) * q_rank);
+  double* q = (double*)malloc(sizeof(double) * (size_t)(nrows ? nrows : 1) * HQ);
+  double* g = (double*)malloc(sizeof(double) * (size_t)(nrows ? nrows : 1) * HV);
+  double* o = (double*)malloc(sizeof(double) * (size_t)(nrows ? nrows : 1) * HV);
+  float* cf = (float*)malloc(sizeof(float) * (size_t)N * r);
+  float* qf = (float*)malloc(sizeof(float) * (size_t)B * T * HQ);
+  float* gf = (float*)malloc(sizeof(float) * (size_t)B * T * HV);
+  int err = ORACLE_OK;
+  if (!xd || !xs || !c || !ql || !q || !g || !o || !cf || !qf || !gf) {
+    err = ORACLE_ENOMEM;
+    goto done;
+  }
+  for (int64_t i = 0; i < N * D; ++i) xd[i] = (double)x[i];
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int64_t row = rows ? rows[i] : i;
+    memcpy(xs + i * D, xd + row * D, sizeof(double) * (size_t)D);
+  }
+
+  /* the latent of every position: c = RMSNorm_kv(W_kv_down x) */
+  linear(xd, N, D, w_kv_down, r, 0, c, nthreads);
+  store_all(c, N * r, stage_dtype);
+  rmsnorm_rows(c, N, r, kv_norm, eps, 0);
+  store_all(c, N * r, stage_dtype);
+
+  /* the query low-rank path of the selected rows: q = W_q_up RMSNorm_q(W_q_down x) */
+  linear(xs, nrows, D, w_q_down, q_rank, 0, ql, nthreads);
+  store_all(ql, nrows * q_rank, stage_dtype);
+  rmsnorm_rows(ql, nrows, q_rank, q_norm, eps, 1);
+  store_all(ql, nrows * q_rank, stage_dtype);
+#if ORACLE_MUTANT == 15
+  linear(ql, nrows, q_rank, w_q_up, HQ, 1, q, nthreads); /* planted: W_q_up read transposed */
+#else
+  linear(ql, nrows, q_rank, w_q_up, HQ, 0, q, nthreads);
+#endif
+  store_all(q, nrows * HQ, stage_dtype);
+
+  /* gate logits of the selected rows */
+#if ORACLE_MUTANT == 16
+  linear(xs, nrows, D, w_gate, HV, 1, g, nthreads); /* planted: W_gate read transposed */
+#else
+  linear(xs, nrows, D, w_gate, HV, 0, g, nthreads);
+#endif
+  store_all(g, nrows * HV, stage_dtype);
+
+  /* the core on the stored values; rows that were not selected stay zero */
+  for (int64_t i = 0; i < N * r; ++i) cf[i] = (float)c[i];
+  memset(qf, 0, sizeof(float) * (size_t)N * HQ);
+  memset(gf, 0, sizeof(float) * (size_t)N * HV);
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int64_t row = rows ? rows[i] : i;
+    for (int k = 0; k < HQ; ++k) qf[row * HQ + k] = (float)q[i * HQ + k];
+    for (int k = 0; k < HV; ++k) gf[row * HV + k] = (float)g[i * HV + k];
+  }
+  err = oracle_extend(qf, cf, w_uk, w_uv, gf, B, T, T, H, dq, dv, r, scale, rows, nrows, o, nthreads);
+  if (err != ORACLE_OK) goto done;
+  store_all(o, nrows * HV, stage_dtype);
+
+  /* output projection */
+#if ORACLE_MUTANT == 17
+  linear(o, nrows, HV, w_o, D, 1, y, nthreads); /* planted: W_o read transposed */
+#else
+  linear(o, nrows, HV, w_o, D, 0, y, nthreads);
+#endif
+
+  if (c_out) memcpy(c_out, c, sizeof(double) * (size_t)N * r);
+  if (q_out) memcpy(q_out, q, sizeof(double) * (size_t)nrows * HQ);
+  if (g_out) memcpy(g_out, g, sizeof(double) * (size_t)nrows * HV);
+  if (o_out) memcpy(o_out, o, sizeof(double) * (size_t)nrows * HV);
+done:
+  free(xd);
+  free(xs);
+  free(c);
+  free(ql);
+  free(q);
+  free(g);
+  free(o);
+  free(cf);
+  free(qf);
+  free(gf);
+  return err;
+}

@@ -303,6 +303,154 @@ def pin_extend_one_query_is_decode(o):
     _close(got, dec, 1e-13, 1e-15, "extend T=1 vs decode")
 
 
+# ---------------------------------------------------------------- full layer
+def _fwd(o, d, eps, scale, stage=0, **kw):
+    return o.forward(*[dg.as_f32(d[k]) for k in dg.FORWARD_KEYS], eps, scale, stage=stage, **kw)
+
+
+def pin_forward_closed_form_stages(o):
+    """Selection matrices for the two down-projections make every stage of
+    the full layer a closed form (page "Gated MLA（矩阵吸收版）", section 低秩压缩
+    and section 完整计算流（四步） steps 1 and 4, eps = 0):
+      * the latent input of a row is beta * s with beta > 0 and s_j = +-1, so
+        its mean square is beta^2 and c = s * kv_norm exactly;
+      * the query-latent input is alpha * e_k (one-hot), so the norm gives
+        sign(alpha) sqrt(q_rank) e_k and q = sign(alpha) sqrt(q_rank)
+        q_norm[k] * (column k of W_q_up);
+      * W_gate = 0 gives sigmoid(0) = 1/2, and W_o = [I; 0] copies the gated
+        core output into the first H*d_v outputs and zeroes the rest.
+    The expected output is the (separately pinned) core on those closed
+    forms."""
+    rng = np.random.default_rng(41)
+    B, T, H, dq, dv, r, q_rank = 2, 5, 2, 3, 2, 4, 6
+    D, HV = q_rank + r + 3, H * dv
+    k = rng.integers(0, q_rank, size=(B, T))
+    alpha = rng.choice([-1.0, 1.0], size=(B, T)) * rng.uniform(0.5, 4.0, size=(B, T))
+    beta = rng.uniform(0.5, 4.0, size=(B, T))
+    sgn = rng.choice([-1.0, 1.0], size=(B, T, r))
+    x = rng.standard_normal((B, T, D))
+    x[..., :q_rank] = 0.0
+    for b in range(B):
+        for t in range(T):
+            x[b, t, k[b, t]] = alpha[b, t]
+    x[..., q_rank:q_rank + r] = beta[..., None] * sgn
+    x = x.astype(np.float32)
+    alpha = x[np.arange(B)[:, None], np.arange(T)[None, :], k].astype(np.float64)
+    w_q_down = np.zeros((q_rank, D), np.float32)
+    w_q_down[:, :q_rank] = np.eye(q_rank)
+    w_kv_down = np.zeros((r, D), np.float32)
+    w_kv_down[:, q_rank:q_rank + r] = np.eye(r)
+    g_q = rng.uniform(0.5, 2.0, q_rank).astype(np.float32)
+    g_kv = rng.uniform(0.5, 2.0, r).astype(np.float32)
+    w_q_up = rng.standard_normal((H * dq, q_rank)).astype(np.float32)
+    w_uk = (rng.standard_normal((H, dq, r)) / 2).astype(np.float32)
+    w_uv = rng.standard_normal((H, dv, r)).astype(np.float32)
+    w_gate = np.zeros((HV, D), np.float32)
+    w_o = np.zeros((D, HV), np.float32)
+    w_o[:HV] = np.eye(HV)
+    scale = 0.45
+    y, st = o.forward(x, w_kv_down, g_kv, w_q_down, g_q, w_q_up, w_uk, w_uv, w_gate, w_o, 0.0, scale,
+                      stages=True)
+    c_exp = sgn * g_kv.astype(np.float64)
+    q_exp = (np.sign(alpha) * np.sqrt(q_rank) * g_q[k].astype(np.float64))[..., None] * \
+        w_q_up.T[k].astype(np.float64)
+    _close(st["c"].reshape(B, T, r), c_exp, 0.0, 0.0, "closed-form latent")
+    _close(st["q"].reshape(B, T, H * dq), q_exp, 2e-7, 1e-12, "closed-form query")
+    core = o.prefill(q_exp.reshape(B, T, H, dq), c_exp, w_uk, w_uv, np.zeros((B, T, HV)), scale)
+    y_exp = np.concatenate([core, np.zeros((B, T, D - HV))], axis=-1)
+    _close(y, y_exp, 2e-6, 1e-9, "closed-form full layer")
+
+
+def pin_forward_norm_scale_invariance(o):
+    """With eps = 0 an RMSNorm output does not change when its input is
+    scaled, so scaling W_kv_down or W_q_down by a power of two leaves the
+    layer's output bit-identical; q is linear in W_q_up, so doubling W_q_up
+    and halving the softmax scale does too (page "Gated MLA（矩阵吸收版）",
+    section 低秩压缩 and section 完整计算流（四步） steps 1-2)."""
+    d = dg.forward_inputs(2, 7, 64, 32, 3, 4, 5, 8, dtype=dg.F32, seed=71)
+    base = _fwd(o, d, 0.0, 0.6)
+    for key, f, sc in (("w_kv_down", 4.0, 0.6), ("w_q_down", 0.25, 0.6), ("w_q_up", 2.0, 0.3)):
+        e = dict(d)
+        e[key] = dg.as_f32(d[key]) * np.float32(f)
+        _close(_fwd(o, e, 0.0, sc), base, 1e-13, 1e-15, f"{key} scaled by {f}")
+
+
+def _brute_forward(d, eps, scale):
+    """The whole layer in plain Python loops on float64 scalars, attention
+    by the decompressed route (k = W_UK[h] c_u, v = W_UV[h] c_u per key),
+    written from page "Gated MLA（矩阵吸收版）": section 低秩压缩 (c), section
+    矩阵吸收的核心思路 (the standard route), section 完整计算流（四步） steps 1-4."""
+    import math
+    f = {k: dg.as_f32(d[k]).astype(np.float64).tolist() for k in dg.FORWARD_KEYS}
+    B, T, D, q_rank, H, dq, dv, r = (d[k] for k in ("B", "T", "D", "q_rank", "H", "d_q", "d_v", "r"))
+
+    def lin(vec, W):
+        return [sum(a * b for a, b in zip(vec, row)) for row in W]
+
+    def norm(vec, gain):
+        ms = sum(v * v for v in vec) / len(vec)
+        return [v / math.sqrt(ms + eps) * g for v, g in zip(vec, gain)]
+
+    y = np.zeros((B, T, D))
+    for b in range(B):
+        xs = f["x"][b]
+        c = [norm(lin(xs[u], f["w_kv_down"]), f["kv_norm"]) for u in range(T)]
+        for t in range(T):
+            qv = lin(norm(lin(xs[t], f["w_q_down"]), f["q_norm"]), f["w_q_up"])
+            gl = lin(xs[t], f["w_gate"])
+            gated = []
+            for h in range(H):
+                qh = qv[h * dq:(h + 1) * dq]
+                keys = [lin(c[u], f["w_uk"][h]) for u in range(t + 1)]
+                vals = [lin(c[u], f["w_uv"][h]) for u in range(t + 1)]
+                sc = [scale * sum(a * b for a, b in zip(qh, kk)) for kk in keys]
+                m = max(sc)
+                w = [math.exp(s_ - m) for s_ in sc]
+                z = sum(w)
+                for v in range(dv):
+                    ov = sum(w[u] * vals[u][v] for u in range(t + 1)) / z
+                    gated.append(ov / (1.0 + math.exp(-gl[h * dv + v])))
+            y[b, t] = lin(gated, f["w_o"])
+    return y
+
+
+def pin_forward_brute_force(o):
+    """The full layer equals a plain-loop brute force that takes the
+    decompressed route, with eps > 0 (float32 storage of the stage
+    results accounts for the tolerance)."""
+    for (B, T, D, q_rank, H, dq, dv, r, eps, scale, seed) in [(1, 4, 6, 4, 2, 2, 3, 5, 1e-3, 0.7, 81),
+                                                               (2, 3, 5, 3, 1, 3, 2, 4, 0.05, 1.3, 82)]:
+        d = dg.forward_inputs(B, T, D, q_rank, H, dq, dv, r, dtype=dg.F32, seed=seed)
+        _close(_fwd(o, d, eps, scale), _brute_forward(d, eps, scale), 2e-6, 1e-7,
+               f"full-layer brute force B{B} T{T} D{D}")
+
+
+def pin_round_bf16(o):
+    """The oracle's bf16 rounding (nearest, ties to even, from the float64
+    value) against fixed cases and two other implementations on float32
+    inputs (the bit-pattern rounding of the data generator and torch's
+    float32 -> bfloat16 conversion)."""
+    import torch
+    one = 1.0
+    u = 2.0 ** -8  # half a bf16 ulp at 1
+    cases = [(one + u, one), (one + 3 * u, one + 4 * u), (-(one + u), -one), (one + u + 2.0 ** -40, one + 2 * u),
+             (one + 0.99 * u, one), (0.0, 0.0), (1.5 * 2.0 ** -133, 2.0 * 2.0 ** -133),
+             (2.5 * 2.0 ** -133, 2.0 * 2.0 ** -133), (3.3895313892515355e38 + 2.0 ** 118, 3.3895313892515355e38),
+             (3.3895313892515355e38 + 2.0 ** 119, np.inf), (-7.0, -7.0), (1.0 / 3.0, 0.333984375)]
+    got = o.round_bf16(np.array([a for a, _ in cases]))
+    for (a, want), g in zip(cases, got):
+        assert g == want, f"round_bf16({a!r}) = {g!r}, expected {want!r}"
+    rng = np.random.default_rng(91)
+    v = (rng.standard_normal(20000) * np.exp2(rng.integers(-60, 60, 20000))).astype(np.float32)
+    v = np.concatenate([v, dg.bf16_bits_to_f32(rng.integers(0, 0x7F7F, 2000).astype(np.uint16)) *
+                        np.float32(1.0 + 2.0 ** -8)])
+    ref_bits = dg.bf16_bits_to_f32(dg.f32_to_bf16_bits(v)).astype(np.float64)
+    ref_torch = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = o.round_bf16(v.astype(np.float64))
+    assert np.array_equal(got, ref_bits), "round_bf16 differs from the bit-pattern rounding"
+    assert np.array_equal(got, ref_torch), "round_bf16 differs from torch's bfloat16 conversion"
+
+
 ALL_PINS = [
     pin_absorbed_equals_decompressed,
     pin_attention_rows,
@@ -318,4 +466,8 @@ ALL_PINS = [
     pin_extend_matches_prefill_rows,
     pin_extend_dense_brute_force,
     pin_extend_one_query_is_decode,
+    pin_forward_closed_form_stages,
+    pin_forward_norm_scale_invariance,
+    pin_forward_brute_force,
+    pin_round_bf16,
 ]

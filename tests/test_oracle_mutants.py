@@ -1,7 +1,8 @@
 """Each plausible mistake planted in the oracle (a dropped diagonal, a sign,
 a transposed weight, the flatten order, the gate sign, a missing scale or
 normalisation, the wrong key row, an off-by-one decode cache, a chunk that ignores its
-cached prefix) must be caught
+cached prefix; in the full layer a missing or misplaced norm, a transposed
+projection, a wrong rounding rule) must be caught
 by at least one pin.  Mutants are compiled on the CPU into a scratch dir."""
 import pytest
 
@@ -20,6 +21,14 @@ MUTANTS = {
     9: "weighted sum uses the query's own latent row",
     10: "decode drops the newest cached row",
     11: "chunked prefill ignores the cached prefix",
+    12: "latent not normalised",
+    13: "latent norm gain applied inside the norm",
+    14: "query latent not normalised",
+    15: "W_q_up read transposed",
+    16: "W_gate read transposed",
+    17: "W_o read transposed",
+    18: "RMSNorm over the sum of squares instead of the mean",
+    19: "bf16 rounding ties away from zero",
 }
 
 
