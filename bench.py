@@ -10,7 +10,10 @@ HIP events on the stream it runs on.
 Printed (one JSON line): prefill TFLOP/s as `value` (causal-triangle
 algorithmic FLOPs), chunked-prefill TFLOP/s, decode latent-cache GB/s
 (algorithmic bytes), the roofline object of each against MI355X's published
-peaks, and the CPU oracle timed on a bounded row sample of the prefill.
+peaks, and the CPU oracle timed on a bounded row sample of the prefill.  The
+full-layer forward (projections, norms, core, output projection at the full
+K3 widths, B=1, T=8192) is timed separately after the steps and reported
+under "forward"; it is not part of ms_per_step.
 """
 from __future__ import annotations
 
@@ -46,6 +49,15 @@ def extend_flops(B, T, S, H, dq, dv, r):
     P = S - T
     pairs = B * H * (T * P + T * (T + 1) // 2)
     return 2 * B * T * H * r * (dq + dv) + 4 * r * pairs
+
+
+def forward_flops(B, T, D, q_rank, H, dq, dv, r):
+    """Algorithmic FLOPs of one full-layer forward: the five projections
+    (latent and query down-projections, query up-projection, gate, output
+    projection) on every row, plus the core's prefill FLOPs."""
+    N = B * T
+    return 2 * N * (D * r + D * q_rank + q_rank * H * dq + D * H * dv + H * dv * D) + \
+        prefill_flops(B, T, H, dq, dv, r)
 
 
 def decode_flops(lengths, H, dq, dv, r):
@@ -139,6 +151,34 @@ def cpu_baseline(pre, target_s: float):
                       f"{fl / 1e9:.1f} GFLOP in {dt:.1f} s"}
 
 
+def bench_forward(torch, mla, steps, warmup):
+    """The whole layer (projections, norms, core, output projection) at the
+    full K3 widths, B=1, T=8192, timed on its own after the hot-path steps."""
+    fw = dg.WORKLOADS["full_forward"]
+    d = dg.workload_inputs("full_forward")
+    args = [dev(d[k]) for k in dg.FORWARD_KEYS]
+    B, T, D, qr, H, dq, dv, r = (d[k] for k in ("B", "T", "D", "q_rank", "H", "d_q", "d_v", "r"))
+    y = torch.empty((B, T, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.forward_workspace_size(B, T, qr, H, dq, dv, r, mla.DTYPE_BF16), dtype=torch.uint8,
+                     device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for _ in range(warmup):
+        mla.mla_gated_forward(*args, d["eps"], d["scale"], out=y, workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        mla.mla_gated_forward(*args, d["eps"], d["scale"], out=y, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    f = forward_flops(B, T, D, qr, H, dq, dv, r)
+    tf = f / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4), "seed": fw["seed"],
+            "workload": f"full_forward: B={B}, T={T}, D={D}, q_rank={qr}, H={H}, d_q=d_v={dq}, r={r}, eps 1e-6",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flop_per_launch": f}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,8 +186,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--which", choices=["both", "prefill", "decode"], default="both",
-                    help="both: prefill, chunked prefill and decode")
+    ap.add_argument("--which", choices=["both", "prefill", "decode", "forward"], default="both",
+                    help="both: prefill, chunked prefill and decode, then the full-layer forward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -275,6 +315,8 @@ def main():
                          "roofline": {"bound": "mfma", "achieved": round(x_tf, 2), "peak": PEAK_BF16_TFLOPS,
                                       "unit": "TFLOP/s", "frac": round(x_tf / PEAK_BF16_TFLOPS, 4),
                                       "traffic": None, "flop_per_launch": xf}}
+    if args.which in ("both", "forward"):
+        res["forward"] = bench_forward(torch, mla, args.steps, args.warmup)
     if not args.no_cpu_baseline and do_pre:
         res["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
     print(json.dumps(res), flush=True)

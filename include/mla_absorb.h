@@ -140,6 +140,37 @@ mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* 
                              int num_splits, mla_dtype dtype, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of workspace mla_gated_forward needs (bf16 only; (size_t)-1 for
+ * invalid sizes or dtypes).
+ */
+size_t mla_gated_forward_workspace_size(int B, int T, int q_rank, int H, int d_q, int d_v, int r,
+                                        mla_dtype dtype);
+
+/*
+ * Full Gated MLA forward around the absorbed core (page "Gated MLA（矩阵吸收版）":
+ * section 低秩压缩 for the latent, section 完整计算流（四步） steps 1-4):
+ *   c    = RMSNorm(x W_kv_down^T) * kv_norm            [B, T, r]
+ *   q    = (RMSNorm(x W_q_down^T) * q_norm) W_q_up^T    [B, T, H*d_q]
+ *   gate = x W_gate^T                                   [B, T, H*d_v]
+ *   o    = the absorbed core (mla_absorb_prefill) of q, c, W_UK, W_UV, gate
+ *   y    = o W_o^T                                      [B, T, D]
+ * with RMSNorm(v) = v / sqrt(mean(v^2) + eps) over the last axis.  Weights
+ * are laid out as linear layers (out_features x in_features):
+ *   w_kv_down [r, D], kv_norm [r], w_q_down [q_rank, D], q_norm [q_rank],
+ *   w_q_up [H*d_q, q_rank], w_uk [H, d_q, r], w_uv [H, d_v, r],
+ *   w_gate [H*d_v, D], w_o [D, H*d_v]; x and y are [B, T, D].
+ * bf16 only (MLA_ERR_UNSUPPORTED otherwise).  The projections run as 64-wide
+ * k tiles: D, q_rank and H*d_v must be multiples of 64, and r, q_rank <= 2048.
+ * Workspace: mla_gated_forward_workspace_size bytes.  Other conventions and
+ * errors as for mla_absorb_prefill.
+ */
+mla_status mla_gated_forward(const void* x, const void* w_kv_down, const void* kv_norm, const void* w_q_down,
+                             const void* q_norm, const void* w_q_up, const void* w_uk, const void* w_uv,
+                             const void* w_gate, const void* w_o, void* y, int B, int T, int D, int q_rank,
+                             int H, int d_q, int d_v, int r, float eps, float scale, mla_dtype dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,8 +16,8 @@ import os
 __all__ = [
     "LIB_PATH", "MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED", "MLA_ERR_WORKSPACE",
     "MLA_ERR_HIP", "DTYPE_F32", "DTYPE_BF16", "MLAError", "lib", "status_string",
-    "prefill_workspace_size", "decode_workspace_size", "mla_absorb_prefill", "mla_absorb_extend",
-    "mla_absorb_decode",
+    "prefill_workspace_size", "decode_workspace_size", "forward_workspace_size", "mla_absorb_prefill",
+    "mla_absorb_extend", "mla_absorb_decode", "mla_gated_forward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_absorb.so")
@@ -32,6 +32,8 @@ EXPORTS = (
     "mla_absorb_extend",
     "mla_absorb_decode_workspace_size",
     "mla_absorb_decode",
+    "mla_gated_forward_workspace_size",
+    "mla_gated_forward",
 )
 
 _lib = None
@@ -63,6 +65,10 @@ def lib() -> ct.CDLL:
         L.mla_absorb_decode_workspace_size.restype = sz
         L.mla_absorb_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, I64, F, I, I, vp, sz, vp]
         L.mla_absorb_decode.restype = I
+        L.mla_gated_forward_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+        L.mla_gated_forward_workspace_size.restype = sz
+        L.mla_gated_forward.argtypes = [vp] * 11 + [I] * 8 + [F, F, I, vp, sz, vp]
+        L.mla_gated_forward.restype = I
         _lib = L
     return _lib
 
@@ -85,6 +91,13 @@ def decode_workspace_size(B: int, H: int, d_q: int, r: int, num_splits: int, dty
     n = lib().mla_absorb_decode_workspace_size(B, H, d_q, r, num_splits, dtype)
     if n == _BAD:
         raise MLAError(MLA_ERR_INVALID_ARG, "mla_absorb_decode_workspace_size")
+    return n
+
+
+def forward_workspace_size(B: int, T: int, q_rank: int, H: int, d_q: int, d_v: int, r: int, dtype: int) -> int:
+    n = lib().mla_gated_forward_workspace_size(B, T, q_rank, H, d_q, d_v, r, dtype)
+    if n == _BAD:
+        raise MLAError(MLA_ERR_INVALID_ARG, "mla_gated_forward_workspace_size")
     return n
 
 
@@ -200,4 +213,39 @@ def mla_absorb_decode(q, c_cache, cu_seqlens, w_uk, w_uv, gate, scale: float, nu
                                  workspace.numel() * workspace.element_size(), _stream(stream))
     if st != MLA_OK:
         raise MLAError(st, "mla_absorb_decode")
+    return out
+
+
+def mla_gated_forward(x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o,
+                      eps: float, scale: float, out=None, workspace=None, stream=None):
+    """Full Gated MLA forward (bf16): x [B,T,D] -> y [B,T,D].  Weights as
+    linear layers: w_kv_down [r,D], kv_norm [r], w_q_down [q_rank,D],
+    q_norm [q_rank], w_q_up [H*d_q,q_rank], w_uk [H,d_q,r], w_uv [H,d_v,r],
+    w_gate [H*d_v,D], w_o [D,H*d_v]."""
+    torch = _torch()
+    B, T, D = x.shape
+    r = w_kv_down.shape[0]
+    q_rank = w_q_down.shape[0]
+    H, dq, _ = w_uk.shape
+    dv = w_uv.shape[1]
+    dt = x.dtype
+    code = _dtype_code(x)
+    for t, shp, n in ((x, (B, T, D), "x"), (w_kv_down, (r, D), "w_kv_down"), (kv_norm, (r,), "kv_norm"),
+                      (w_q_down, (q_rank, D), "w_q_down"), (q_norm, (q_rank,), "q_norm"),
+                      (w_q_up, (H * dq, q_rank), "w_q_up"), (w_uk, (H, dq, r), "w_uk"), (w_uv, (H, dv, r), "w_uv"),
+                      (w_gate, (H * dv, D), "w_gate"), (w_o, (D, H * dv), "w_o")):
+        _check(t, shp, dt, n)
+    if out is None:
+        out = torch.empty((B, T, D), dtype=dt, device=x.device)
+    _check(out, (B, T, D), dt, "out")
+    need = forward_workspace_size(B, T, q_rank, H, dq, dv, r, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib().mla_gated_forward(x.data_ptr(), w_kv_down.data_ptr(), kv_norm.data_ptr(), w_q_down.data_ptr(),
+                                 q_norm.data_ptr(), w_q_up.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+                                 w_gate.data_ptr(), w_o.data_ptr(), out.data_ptr(), B, T, D, q_rank, H, dq, dv,
+                                 r, float(eps), float(scale), code, workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_gated_forward")
     return out

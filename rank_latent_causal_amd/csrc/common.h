@@ -70,10 +70,12 @@ __device__ __forceinline__ bf16x8 cat4(const bf16x4& lo, const bf16x4& hi) {
 // so a lane whose offset is at or past `bytes` reads zeros.  Held in SGPRs.
 __device__ __forceinline__ u32x4 make_rsrc(const void* base, unsigned bytes) {
   const uint64_t a = (uint64_t)(uintptr_t)base;
+  // callers pass wave-uniform values; readfirstlane keeps the descriptor in
+  // SGPRs even where the compiler cannot prove that
   u32x4 r;
-  r[0] = (unsigned)a;
-  r[1] = (unsigned)(a >> 32) & 0xFFFFu;
-  r[2] = bytes;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xFFFFu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
   r[3] = 0x00020000u;
   return r;
 }

@@ -10,6 +10,8 @@
 #include "common.h"
 #include "decode_bf16.h"
 #include "f32_kernels.h"
+#include "forward_bf16.h"
+#include "gemm_bf16.h"
 #include "prefill_bf16.h"
 
 namespace {
@@ -99,6 +101,40 @@ void launch_decode_bf16(const mla::DecodeAbsorbArgs& aa, const mla::DecodeSplitA
 void launch_wuk_transpose(const bf16* w, bf16* wt, int H, int dq, int r, hipStream_t s) {
   hipLaunchKernelGGL((mla::mla_wuk_transpose<bf16>), dim3((r + 31) / 32, (dq + 31) / 32, H), dim3(256), 0, s,
                      w, wt, H, dq, r);
+}
+
+struct ForwardLayout {
+  size_t c = 0, ql = 0, q = 0, gate = 0, o = 0, core = 0, total = 0;
+};
+
+// Workspace of the full forward: the latent, the normalised query latent, q,
+// the gate pre-activations, the gated core output and the core's own workspace.
+ForwardLayout forward_layout(int B, int T, int q_rank, int H, int dq, int dv, int r) {
+  const size_t N = (size_t)B * T;
+  ForwardLayout L;
+  size_t off = 0;
+  L.c = off;    off = align_up(off + N * r * sizeof(bf16));
+  L.ql = off;   off = align_up(off + N * q_rank * sizeof(bf16));
+  L.q = off;    off = align_up(off + N * H * dq * sizeof(bf16));
+  L.gate = off; off = align_up(off + N * H * dv * sizeof(bf16));
+  L.o = off;    off = align_up(off + N * H * dv * sizeof(bf16));
+  L.core = off; off = align_up(off + (size_t)H * r * dq * sizeof(bf16));
+  L.total = off;
+  return L;
+}
+
+void launch_gemm(const bf16* x, const bf16* w, bf16* y, int M, int N, int K, hipStream_t s) {
+  mla::GemmArgs g{};
+  g.x = x; g.w = w; g.y = y; g.M = M; g.N = N; g.K = K;
+  g.tiles_n = (N + mla::kGemmTile - 1) / mla::kGemmTile;
+  const long long grid = (long long)g.tiles_n * ((M + mla::kGemmTile - 1) / mla::kGemmTile);
+  hipLaunchKernelGGL(mla::mla_gemm_nt, dim3((unsigned)grid), dim3(256), 0, s, g);
+}
+
+void launch_rmsnorm(bf16* x, const bf16* gain, int rows, int n, float eps, hipStream_t s) {
+  mla::RmsNormArgs a{};
+  a.x = x; a.gain = gain; a.rows = rows; a.n = n; a.eps = eps;
+  hipLaunchKernelGGL(mla::mla_rmsnorm_rows, dim3((rows + 3) / 4), dim3(256), 0, s, a);
 }
 
 }  // namespace
@@ -243,6 +279,64 @@ mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* 
   if (d_q == 16) launch_decode_bf16<16, 16, 32>(aa, sa, ma, s);
   else if (d_q == 64) launch_decode_bf16<64, 64, 256>(aa, sa, ma, s);
   else launch_decode_bf16<128, 128, 512>(aa, sa, ma, s);
+  return launch_status();
+}
+
+size_t mla_gated_forward_workspace_size(int B, int T, int q_rank, int H, int d_q, int d_v, int r,
+                                        mla_dtype dtype) {
+  if (B <= 0 || T <= 0 || q_rank <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return kBadSize;
+  if (dtype != MLA_DTYPE_BF16) return kBadSize;
+  return forward_layout(B, T, q_rank, H, d_q, d_v, r).total;
+}
+
+mla_status mla_gated_forward(const void* x, const void* w_kv_down, const void* kv_norm, const void* w_q_down,
+                             const void* q_norm, const void* w_q_up, const void* w_uk, const void* w_uv,
+                             const void* w_gate, const void* w_o, void* y, int B, int T, int D, int q_rank,
+                             int H, int d_q, int d_v, int r, float eps, float scale, mla_dtype dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !w_kv_down || !kv_norm || !w_q_down || !q_norm || !w_q_up || !w_uk || !w_uv || !w_gate || !w_o || !y)
+    return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || T <= 0 || D <= 0 || q_rank <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !std::isfinite(eps) || eps < 0.0f) return MLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o, y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (!bf16_shape_supported(d_q, d_v, r)) return MLA_ERR_UNSUPPORTED;
+  // projection contractions come in 64-wide k tiles; normalised rows fit one wave
+  if (D % 64 || q_rank % 64 || (H * d_v) % 64 || (H * d_q) % 8 || D % 8 || r % 8 || q_rank % 8)
+    return MLA_ERR_UNSUPPORTED;
+  if (r > 64 * 8 * mla::kNormMaxChunks || q_rank > 64 * 8 * mla::kNormMaxChunks) return MLA_ERR_UNSUPPORTED;
+  if (!fits(B, T, D) || !fits(B, T, H, d_q > d_v ? d_q : d_v) || (long long)B * T >= (1LL << 31))
+    return MLA_ERR_UNSUPPORTED;
+  const ForwardLayout L = forward_layout(B, T, q_rank, H, d_q, d_v, r);
+  if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+  if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int N = B * T;
+  const bf16* xb = (const bf16*)x;
+  bf16* c = (bf16*)(ws + L.c);
+  bf16* ql = (bf16*)(ws + L.ql);
+  bf16* q = (bf16*)(ws + L.q);
+  bf16* gate = (bf16*)(ws + L.gate);
+  bf16* o = (bf16*)(ws + L.o);
+  // latent: c = RMSNorm(W_down x)
+  launch_gemm(xb, (const bf16*)w_kv_down, c, N, r, D, s);
+  launch_rmsnorm(c, (const bf16*)kv_norm, N, r, eps, s);
+  // query low-rank path: q = W_q_up RMSNorm(W_q_down x)
+  launch_gemm(xb, (const bf16*)w_q_down, ql, N, q_rank, D, s);
+  launch_rmsnorm(ql, (const bf16*)q_norm, N, q_rank, eps, s);
+  launch_gemm(ql, (const bf16*)w_q_up, q, N, H * d_q, q_rank, s);
+  // gate pre-activations
+  launch_gemm(xb, (const bf16*)w_gate, gate, N, H * d_v, D, s);
+  // absorbed core: gated head outputs, flattened head-major
+  const mla_status st = mla_absorb_prefill(q, c, w_uk, w_uv, gate, o, B, T, H, d_q, d_v, r, scale, dtype,
+                                           ws + L.core, L.total - L.core, stream);
+  if (st != MLA_OK) return st;
+  // output projection
+  launch_gemm(o, (const bf16*)w_o, (bf16*)y, N, D, H * d_v, s);
   return launch_status();
 }
 

@@ -112,3 +112,18 @@ def sample_rows(B: int, T: int, n_random: int, seed: int) -> np.ndarray:
     ts |= set(int(x) for x in rng.integers(0, T, size=n_random))
     ts = sorted(t for t in ts if 0 <= t < T)
     return np.array([b * T + t for b in range(B) for t in ts], dtype=np.int64)
+
+
+def run_forward(d, eps=None, scale=None):
+    """Full-layer forward of forward-shaped inputs d (bf16) through the binding."""
+    import rank_latent_causal_amd as mla
+    args = [to_dev(d[k]) for k in dg.FORWARD_KEYS]
+    out = mla.mla_gated_forward(*args, d["eps"] if eps is None else eps, d["scale"] if scale is None else scale)
+    torch().cuda.synchronize()
+    return out
+
+
+def oracle_forward(o, d, rows=None, eps=None, scale=None):
+    """The oracle's full-layer forward with bf16 storage of the stage results."""
+    return o.forward(*[dg.as_f32(d[k]) for k in dg.FORWARD_KEYS], d["eps"] if eps is None else eps,
+                     d["scale"] if scale is None else scale, stage=o.STAGE_BF16, rows=rows)

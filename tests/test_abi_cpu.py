@@ -134,3 +134,42 @@ def _extend(**kw):
 ])
 def test_extend_rejects(kw, status):
     assert _extend(**kw) == status
+
+
+def test_forward_workspace_sizes():
+    n = mla.forward_workspace_size(1, 8192, 1536, 96, 128, 128, 512, mla.DTYPE_BF16)
+    rows = 8192
+    # c, the query latent, q, gate, the gated core output and the core's W_UK^T
+    assert n >= rows * (512 + 1536 + 3 * 96 * 128) * 2 + 96 * 512 * 128 * 2
+    with pytest.raises(mla.MLAError):
+        mla.forward_workspace_size(1, 8, 64, 8, 16, 16, 32, mla.DTYPE_F32)
+
+
+def _forward(**kw):
+    a = dict(x=FAKE, wkd=FAKE, kvn=FAKE, wqd=FAKE, qn=FAKE, wqu=FAKE, w_uk=FAKE, w_uv=FAKE, wg=FAKE, wo=FAKE,
+             y=FAKE, B=1, T=8, D=7168, q_rank=1536, H=96, dq=128, dv=128, r=512, eps=1e-6, scale=0.1,
+             dtype=mla.DTYPE_BF16, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return mla.lib().mla_gated_forward(a["x"], a["wkd"], a["kvn"], a["wqd"], a["qn"], a["wqu"], a["w_uk"],
+                                       a["w_uv"], a["wg"], a["wo"], a["y"], a["B"], a["T"], a["D"], a["q_rank"],
+                                       a["H"], a["dq"], a["dv"], a["r"], a["eps"], a["scale"], a["dtype"],
+                                       a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(wo=FAKE + 8), mla.MLA_ERR_INVALID_ARG),
+    (dict(T=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(eps=-1.0), mla.MLA_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), mla.MLA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), mla.MLA_ERR_INVALID_ARG),
+    (dict(dtype=mla.DTYPE_F32), mla.MLA_ERR_UNSUPPORTED),
+    (dict(D=7000), mla.MLA_ERR_UNSUPPORTED),          # not a multiple of 64
+    (dict(q_rank=1500), mla.MLA_ERR_UNSUPPORTED),
+    (dict(q_rank=4096), mla.MLA_ERR_UNSUPPORTED),     # beyond one wave's norm row
+    (dict(dq=96, dv=96, r=384), mla.MLA_ERR_UNSUPPORTED),
+    (dict(ws=None), mla.MLA_ERR_WORKSPACE),
+    (dict(wsb=1 << 20), mla.MLA_ERR_WORKSPACE),
+])
+def test_forward_rejects(kw, status):
+    assert _forward(**kw) == status
