@@ -180,6 +180,44 @@ def decode_inputs(B: int, H: int, d_q: int, d_v: int, r: int, dtype: str = BF16,
                 max_len=int(lens.max()))
 
 
+def paged_layout(lengths, page_size: int, seed: int = 0, spare_pages: int = 3) -> dict:
+    """A shuffled page assignment for sequences of the given lengths: sequence
+    i gets ceil(len_i / page_size) pages drawn without replacement from a pool
+    of (their total + spare_pages) pages.  block_table [B, max_pages] int32;
+    entries past a sequence's pages are -1."""
+    lens = np.asarray(lengths, dtype=np.int64)
+    need = -(-lens // page_size)
+    max_pages = int(need.max())
+    num_pages = int(need.sum()) + spare_pages
+    perm = _gen(seed, _TID["lens"], 1).permutation(num_pages)
+    bt = np.full((len(lens), max_pages), -1, dtype=np.int32)
+    o = 0
+    for i, n in enumerate(need):
+        bt[i, :n] = perm[o:o + n]
+        o += n
+    return dict(block_table=bt, num_pages=num_pages, max_pages=max_pages, page_size=page_size)
+
+
+def scatter_to_pages(rows: np.ndarray, cu, layout: dict, fill=np.nan) -> np.ndarray:
+    """Places packed rows [N, r] (storage dtype) of the sequences delimited by
+    cu into a page pool [num_pages, page_size, r] following layout; slots no
+    sequence owns hold `fill` (rounded to the storage dtype)."""
+    ps, npg = layout["page_size"], layout["num_pages"]
+    r = rows.shape[1]
+    if rows.dtype == np.uint16:
+        fb = f32_to_bf16_bits(np.array([fill], dtype=np.float32))[0]
+        pool = np.full((npg, ps, r), fb, dtype=np.uint16)
+    else:
+        pool = np.full((npg, ps, r), fill, dtype=rows.dtype)
+    bt = layout["block_table"]
+    for i in range(len(cu) - 1):
+        n = int(cu[i + 1] - cu[i])
+        for p in range(-(-n // ps)):
+            u0, u1 = p * ps, min(n, (p + 1) * ps)
+            pool[bt[i, p], :u1 - u0] = rows[cu[i] + u0:cu[i] + u1]
+    return pool
+
+
 # Named workloads: the pages' toy and full-scale shapes.  Seeds are
 # 0x4D4C41 + index so each workload draws independent data.
 SEED_BASE = 0x4D4C41

@@ -64,9 +64,15 @@ class Oracle:
         L.oracle_prefill_decompressed.argtypes = [fp, fp, fp, fp, fp, I, I, I, I, I, I, D, dp, I]
         L.oracle_prefill_attn.argtypes = [fp, fp, fp, I, I, I, I, I, D, dp]
         L.oracle_round_bf16.argtypes = [dp, I64, dp]
+        L.oracle_decode_paged.argtypes = [fp, fp, I64, I, i64p, I, i64p, fp, fp, fp, I, I, I, I, I, D, i64p, I64,
+                                          dp, I]
+        L.oracle_extend_paged.argtypes = [fp, fp, I64, I, i64p, I, fp, fp, fp, I, I, I, I, I, I, I, D, i64p, I64,
+                                          dp, I]
+        L.oracle_cache_append.argtypes = [fp, fp, I64, I, i64p, I, i64p, I, I]
         L.oracle_forward.argtypes = [fp] * 10 + [I] * 8 + [D, D, I, i64p, I64] + [dp] * 5 + [I]
         for f in ("oracle_prefill", "oracle_extend", "oracle_decode", "oracle_prefill_decompressed",
-                  "oracle_prefill_attn", "oracle_round_bf16", "oracle_forward"):
+                  "oracle_prefill_attn", "oracle_round_bf16", "oracle_forward", "oracle_decode_paged",
+                  "oracle_extend_paged", "oracle_cache_append"):
             getattr(L, f).restype = I
 
     @property
@@ -168,6 +174,68 @@ class Oracle:
             _ptr(q, ct.c_float), _ptr(c, ct.c_float), _ptr(w_uk, ct.c_float), B, T, H, dq, r,
             float(scale), _ptr(out, ct.c_double)), "oracle_prefill_attn")
         return out
+
+    def decode_paged(self, q, pages, block_table, seq_lens, w_uk, w_uv, gate, scale: float, seqs=None,
+                     threads: int = 0) -> np.ndarray:
+        """Decode against a paged cache: pages [num_pages, page_size, r],
+        block_table [B, max_pages], seq_lens [B].  Returns [B, H*dv] (or
+        [len(seqs), H*dv]) float64."""
+        q, pages, w_uk, w_uv, gate = map(_f32, (q, pages, w_uk, w_uv, gate))
+        bt = np.ascontiguousarray(block_table, dtype=np.int64)
+        lens = np.ascontiguousarray(seq_lens, dtype=np.int64)
+        B, H, dq = q.shape
+        npg, ps, r = pages.shape
+        dv = w_uv.shape[1]
+        assert bt.shape[0] == B and lens.shape == (B,) and gate.shape == (B, H * dv)
+        if seqs is None:
+            sp, n = None, B
+        else:
+            seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+            sp, n = _ptr(seqs, ct.c_int64), seqs.shape[0]
+        out = np.empty((n, H * dv), dtype=np.float64)
+        self._check(self.lib.oracle_decode_paged(
+            _ptr(q, ct.c_float), _ptr(pages, ct.c_float), npg, ps, _ptr(bt, ct.c_int64), bt.shape[1],
+            _ptr(lens, ct.c_int64), _ptr(w_uk, ct.c_float), _ptr(w_uv, ct.c_float), _ptr(gate, ct.c_float),
+            B, H, dq, dv, r, float(scale), sp, n, _ptr(out, ct.c_double), threads), "oracle_decode_paged")
+        return out
+
+    def extend_paged(self, q, pages, block_table, S: int, w_uk, w_uv, gate, scale: float, rows=None,
+                     threads: int = 0) -> np.ndarray:
+        """Chunked prefill against a paged cache holding S rows per
+        sequence.  Returns [B,T,H*dv] or [len(rows), H*dv] (float64)."""
+        q, pages, w_uk, w_uv, gate = map(_f32, (q, pages, w_uk, w_uv, gate))
+        bt = np.ascontiguousarray(block_table, dtype=np.int64)
+        B, T, H, dq = q.shape
+        npg, ps, r = pages.shape
+        dv = w_uv.shape[1]
+        assert bt.shape[0] == B and gate.shape == (B, T, H * dv)
+        if rows is None:
+            out = np.empty((B, T, H * dv), dtype=np.float64)
+            rp, n = None, B * T
+        else:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            out = np.empty((rows.shape[0], H * dv), dtype=np.float64)
+            rp, n = _ptr(rows, ct.c_int64), rows.shape[0]
+        self._check(self.lib.oracle_extend_paged(
+            _ptr(q, ct.c_float), _ptr(pages, ct.c_float), npg, ps, _ptr(bt, ct.c_int64), bt.shape[1],
+            _ptr(w_uk, ct.c_float), _ptr(w_uv, ct.c_float), _ptr(gate, ct.c_float), B, T, int(S), H, dq, dv, r,
+            float(scale), rp, n, _ptr(out, ct.c_double), threads), "oracle_extend_paged")
+        return out
+
+    def cache_append(self, c_new, pages, block_table, positions) -> np.ndarray:
+        """Returns a copy of pages [num_pages, page_size, r] (float32) with
+        row c_new[i] written at position positions[i] of sequence i."""
+        c_new = _f32(c_new)
+        pages = np.array(pages, dtype=np.float32, order="C", copy=True)
+        bt = np.ascontiguousarray(block_table, dtype=np.int64)
+        pos = np.ascontiguousarray(positions, dtype=np.int64)
+        npg, ps, r = pages.shape
+        B = c_new.shape[0]
+        assert c_new.shape == (B, r) and bt.shape[0] == B and pos.shape == (B,)
+        self._check(self.lib.oracle_cache_append(
+            _ptr(c_new, ct.c_float), _ptr(pages, ct.c_float), npg, ps, _ptr(bt, ct.c_int64), bt.shape[1],
+            _ptr(pos, ct.c_int64), B, r), "oracle_cache_append")
+        return pages
 
     def round_bf16(self, v) -> np.ndarray:
         """Nearest bf16 value of each element (ties to even), as float64."""

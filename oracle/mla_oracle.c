@@ -395,6 +395,96 @@ int oracle_prefill_attn(const float* q, const float* c, const float* w_uk, int B
 }
 
 /* ---------------------------------------------------------------------------
+ * Paged latent cache.  The pages cache only c ([MLA] section 低秩压缩); a
+ * paged cache stores each sequence's latent rows in fixed-size pages of a
+ * shared pool: row u of sequence b lives in page block_table[b, u / page_size]
+ * at slot u % page_size.  The paged entry points compute exactly what their
+ * packed counterparts compute on the rows gathered in order; the gather is
+ * written out here and the packed functions above do the rest.
+ */
+static int gather_rows(const float* pages, int64_t num_pages, int page_size, const int64_t* block_table,
+                       int max_pages, int64_t b, int64_t len, int r, float* dst) {
+  for (int64_t u = 0; u < len; ++u) {
+#if ORACLE_MUTANT == 20
+    const int64_t pg = block_table[b * page_size + u / page_size]; /* planted: wrong block-table stride */
+#else
+    const int64_t pg = block_table[b * max_pages + u / page_size];
+#endif
+    if (pg < 0 || pg >= num_pages) return ORACLE_EINVAL;
+#if ORACLE_MUTANT == 21
+    const int64_t slot = (u + 1) % page_size; /* planted mistake: slot off by one */
+#else
+    const int64_t slot = u % page_size;
+#endif
+    memcpy(dst + u * r, pages + (pg * page_size + slot) * (int64_t)r, sizeof(float) * (size_t)r);
+  }
+  return ORACLE_OK;
+}
+
+/* Decode against a paged cache: sequence i holds seq_lens[i] rows (>= 1). */
+int oracle_decode_paged(const float* q, const float* pages, int64_t num_pages, int page_size,
+                        const int64_t* block_table, int max_pages, const int64_t* seq_lens, const float* w_uk,
+                        const float* w_uv, const float* gate, int B, int H, int dq, int dv, int r, double scale,
+                        const int64_t* seqs, int64_t nseqs, double* out, int nthreads) {
+  if (!pages || !block_table || !seq_lens || B <= 0 || page_size <= 0 || max_pages <= 0 || r <= 0)
+    return ORACLE_EINVAL;
+  int64_t* cu = (int64_t*)malloc(sizeof(int64_t) * (size_t)(B + 1));
+  if (!cu) return ORACLE_ENOMEM;
+  cu[0] = 0;
+  for (int i = 0; i < B; ++i) {
+    if (seq_lens[i] < 1 || seq_lens[i] > (int64_t)max_pages * page_size) {
+      free(cu);
+      return ORACLE_EINVAL;
+    }
+    cu[i + 1] = cu[i] + seq_lens[i];
+  }
+  float* packed = (float*)malloc(sizeof(float) * (size_t)cu[B] * r);
+  int err = packed ? ORACLE_OK : ORACLE_ENOMEM;
+  for (int i = 0; i < B && err == ORACLE_OK; ++i)
+    err = gather_rows(pages, num_pages, page_size, block_table, max_pages, i, seq_lens[i], r, packed + cu[i] * r);
+  if (err == ORACLE_OK)
+    err = oracle_decode(q, packed, cu, w_uk, w_uv, gate, B, H, dq, dv, r, scale, seqs, nseqs, out, nthreads);
+  free(packed);
+  free(cu);
+  return err;
+}
+
+/* Chunked prefill against a paged cache: every sequence holds S rows, the
+ * chunk's T queries are its positions S-T .. S-1 (as oracle_extend). */
+int oracle_extend_paged(const float* q, const float* pages, int64_t num_pages, int page_size,
+                        const int64_t* block_table, int max_pages, const float* w_uk, const float* w_uv,
+                        const float* gate, int B, int T, int S, int H, int dq, int dv, int r, double scale,
+                        const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+  if (!pages || !block_table || B <= 0 || T <= 0 || S < T || page_size <= 0 || r <= 0 ||
+      (int64_t)max_pages * page_size < S)
+    return ORACLE_EINVAL;
+  float* packed = (float*)malloc(sizeof(float) * (size_t)B * S * r);
+  int err = packed ? ORACLE_OK : ORACLE_ENOMEM;
+  for (int b = 0; b < B && err == ORACLE_OK; ++b)
+    err = gather_rows(pages, num_pages, page_size, block_table, max_pages, b, S, r, packed + (int64_t)b * S * r);
+  if (err == ORACLE_OK)
+    err = oracle_extend(q, packed, w_uk, w_uv, gate, B, T, S, H, dq, dv, r, scale, rows, nrows, out, nthreads);
+  free(packed);
+  return err;
+}
+
+/* Cache append: row c_new[i] becomes row positions[i] of sequence i, i.e. it
+ * is written to page block_table[i, positions[i] / page_size], slot
+ * positions[i] % page_size, in place. */
+int oracle_cache_append(const float* c_new, float* pages, int64_t num_pages, int page_size,
+                        const int64_t* block_table, int max_pages, const int64_t* positions, int B, int r) {
+  if (!c_new || !pages || !block_table || !positions || B <= 0 || page_size <= 0 || r <= 0) return ORACLE_EINVAL;
+  for (int i = 0; i < B; ++i) {
+    const int64_t u = positions[i];
+    if (u < 0 || u >= (int64_t)max_pages * page_size) return ORACLE_EINVAL;
+    const int64_t pg = block_table[(int64_t)i * max_pages + u / page_size];
+    if (pg < 0 || pg >= num_pages) return ORACLE_EINVAL;
+    memcpy(pages + (pg * page_size + u % page_size) * (int64_t)r, c_new + (int64_t)i * r, sizeof(float) * (size_t)r);
+  }
+  return ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------------------
  * Full Gated MLA forward around the absorbed core ([MLA] section 低秩压缩 for
  * the latent, section 完整计算流（四步） step 1 for the query low-rank path,
  * step 4 for the gate and the output projection, the parameter table of

@@ -451,6 +451,69 @@ def pin_round_bf16(o):
     assert np.array_equal(got, ref_torch), "round_bf16 differs from torch's bfloat16 conversion"
 
 
+# ---------------------------------------------------------------- paged cache
+def _paged_case(seed, B, H, dq, dv, r, lens, page_size):
+    d = dg.decode_inputs(B, H, dq, dv, r, dtype=dg.F32, seed=seed, lengths=lens)
+    lay = dg.paged_layout(d["lengths"], page_size, seed=seed)
+    pool = dg.scatter_to_pages(d["c_cache"], d["cu_seqlens"], lay)
+    return d, lay, pool
+
+
+def pin_paged_decode_matches_packed(o):
+    """A paged cache holds the same rows as the packed one (the pages cache
+    only c; paging is storage): decode over shuffled pages, with NaN in every
+    slot no sequence owns, equals decode over the packed rows exactly."""
+    for (seed, B, H, dq, dv, r, lens, ps) in [(101, 4, 3, 4, 3, 8, [1, 9, 32, 70], 8),
+                                              (102, 3, 2, 2, 2, 5, [64, 5, 33], 32)]:
+        d, lay, pool = _paged_case(seed, B, H, dq, dv, r, lens, ps)
+        f = dg.as_f32
+        got = o.decode_paged(f(d["q"]), pool, lay["block_table"], d["lengths"], f(d["w_uk"]), f(d["w_uv"]),
+                             f(d["gate"]), 0.8)
+        ref = o.decode(f(d["q"]), f(d["c_cache"]), d["cu_seqlens"].astype(np.int64), f(d["w_uk"]),
+                       f(d["w_uv"]), f(d["gate"]), 0.8)
+        _close(got, ref, 0.0, 0.0, f"paged decode page_size {ps}")
+
+
+def pin_paged_extend_matches_packed(o):
+    """Chunked prefill over shuffled pages equals chunked prefill over the
+    contiguous latent."""
+    B, S, T, H, dq, dv, r, ps = 2, 21, 6, 2, 3, 2, 5, 8
+    d = dg.prefill_inputs(B, S, H, dq, dv, r, dtype=dg.F32, seed=103)
+    f = dg.as_f32
+    lay = dg.paged_layout([S] * B, ps, seed=103)
+    cu = np.arange(B + 1) * S
+    pool = dg.scatter_to_pages(f(d["c"]).reshape(B * S, r), cu, lay)
+    got = o.extend_paged(f(d["q"])[:, S - T:], pool, lay["block_table"], S, f(d["w_uk"]), f(d["w_uv"]),
+                         f(d["gate"])[:, S - T:], 0.7)
+    ref = o.extend(f(d["q"])[:, S - T:], f(d["c"]), f(d["w_uk"]), f(d["w_uv"]), f(d["gate"])[:, S - T:], 0.7)
+    _close(got, ref, 0.0, 0.0, "paged extend")
+
+
+def pin_cache_append_then_decode(o):
+    """Appending each sequence's new latent at position len_i and decoding
+    over len_i + 1 rows equals decoding over the packed rows with the new row
+    at the end of each sequence; no other slot of the pool changes."""
+    B, H, dq, dv, r, ps = 3, 2, 3, 2, 6, 8
+    lens = np.array([7, 8, 20])
+    full = dg.decode_inputs(B, H, dq, dv, r, dtype=dg.F32, seed=104, lengths=lens + 1)
+    f = dg.as_f32
+    cu_full = full["cu_seqlens"].astype(np.int64)
+    new_rows = f(full["c_cache"])[cu_full[1:] - 1]
+    keep = np.ones(cu_full[-1], bool)
+    keep[cu_full[1:] - 1] = False
+    old = f(full["c_cache"])[keep]
+    cu_old = np.concatenate([[0], np.cumsum(lens)])
+    lay = dg.paged_layout(lens + 1, ps, seed=104)
+    pool = dg.scatter_to_pages(old, cu_old, lay)
+    after = o.cache_append(new_rows, pool, lay["block_table"], lens)
+    changed = ~np.all((after == pool) | (np.isnan(after) & np.isnan(pool)), axis=-1)
+    assert changed.sum() == B, f"append changed {changed.sum()} slots, expected {B}"
+    got = o.decode_paged(f(full["q"]), after, lay["block_table"], lens + 1, f(full["w_uk"]), f(full["w_uv"]),
+                         f(full["gate"]), 0.9)
+    ref = o.decode(f(full["q"]), f(full["c_cache"]), cu_full, f(full["w_uk"]), f(full["w_uv"]), f(full["gate"]), 0.9)
+    _close(got, ref, 0.0, 0.0, "append then paged decode")
+
+
 ALL_PINS = [
     pin_absorbed_equals_decompressed,
     pin_attention_rows,
@@ -470,4 +533,7 @@ ALL_PINS = [
     pin_forward_norm_scale_invariance,
     pin_forward_brute_force,
     pin_round_bf16,
+    pin_paged_decode_matches_packed,
+    pin_paged_extend_matches_packed,
+    pin_cache_append_then_decode,
 ]

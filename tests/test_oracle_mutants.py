@@ -29,6 +29,8 @@ MUTANTS = {
     17: "W_o read transposed",
     18: "RMSNorm over the sum of squares instead of the mean",
     19: "bf16 rounding ties away from zero",
+    20: "paged cache: wrong block-table row stride",
+    21: "paged cache: slot within the page off by one",
 }
 
 
