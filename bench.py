@@ -12,8 +12,10 @@ algorithmic FLOPs), chunked-prefill TFLOP/s, decode latent-cache GB/s
 (algorithmic bytes), the roofline object of each against MI355X's published
 peaks, and the CPU oracle timed on a bounded row sample of the prefill.  The
 full-layer forward (projections, norms, core, output projection at the full
-K3 widths, B=1, T=8192) is timed separately after the steps and reported
-under "forward"; it is not part of ms_per_step.
+K3 widths, B=1, T=8192) and the decode over a paged cache (the decode
+workload in shuffled 64-row pages) are timed separately after the steps and
+reported under "forward" and "decode_paged"; they are not part of
+ms_per_step.
 """
 from __future__ import annotations
 
@@ -179,6 +181,34 @@ def bench_forward(torch, mla, steps, warmup):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flop_per_launch": f}}
 
 
+def bench_decode_paged(torch, mla, dec, steps, warmup, page_size=64):
+    """The full decode workload with its cache in shuffled 64-row pages."""
+    lay = dg.paged_layout(dec["lengths"], page_size, seed=dec["seed"])
+    pool = dg.scatter_to_pages(dec["c_cache"], dec["cu_seqlens"], lay)
+    args = [dev(dec["q"]), dev(pool), dev(lay["block_table"]), dev(dec["lengths"].astype(np.int32)),
+            dev(dec["w_uk"]), dev(dec["w_uv"]), dev(dec["gate"])]
+    B, H, dq, dv, r = dec["B"], dec["H"], dec["d_q"], dec["d_v"], dec["r"]
+    out = torch.empty((B, H * dv), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.decode_paged_workspace_size(B, H, dq, r, 0, mla.DTYPE_BF16), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(warmup):
+        mla.mla_absorb_decode_paged(*args, dec["scale"], out=out, workspace=ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        mla.mla_absorb_decode_paged(*args, dec["scale"], out=out, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = decode_bytes(dec["lengths"], H, dq, dv, r) + 4 * B * lay["max_pages"]
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
+            "workload": f"full_decode with the cache in {lay['num_pages']} shuffled pages of {page_size} rows",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "bytes_per_launch": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +345,8 @@ def main():
                          "roofline": {"bound": "mfma", "achieved": round(x_tf, 2), "peak": PEAK_BF16_TFLOPS,
                                       "unit": "TFLOP/s", "frac": round(x_tf / PEAK_BF16_TFLOPS, 4),
                                       "traffic": None, "flop_per_launch": xf}}
+    if args.which in ("both", "decode"):
+        res["decode_paged"] = bench_decode_paged(torch, mla, dec, args.steps, args.warmup)
     if args.which in ("both", "forward"):
         res["forward"] = bench_forward(torch, mla, args.steps, args.warmup)
     if not args.no_cpu_baseline and do_pre:

@@ -141,6 +141,56 @@ mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* 
                              size_t workspace_bytes, void* stream);
 
 /*
+ * Paged latent cache (the pages cache only c, page "Gated MLA（矩阵吸收版）",
+ * section 低秩压缩; how the cache is stored is not on the pages).  A pool
+ *   c_pages [num_pages, page_size, r]
+ * holds the rows of every sequence in fixed-size pages; row u of sequence i
+ * is page block_table[i * max_pages + u / page_size], slot u % page_size.
+ * block_table is an int32 device array [B, max_pages].  page_size is a power
+ * of two, at least 32 (the key tile, so no tile crosses a page).  Page
+ * indices are device data and are not read on the host: an entry outside
+ * [0, num_pages) that a call needs reads as zero rows (append: the row is
+ * skipped); nothing outside the pool is ever accessed.
+ *
+ * Chunked prefill over a paged cache: as mla_absorb_extend, with the S rows
+ * of each sequence in pages (S <= max_pages * page_size).  bf16 only (f32 is
+ * MLA_ERR_UNSUPPORTED).  Workspace: mla_absorb_prefill_workspace_size(B, T,
+ * H, d_q, r, dtype) bytes.
+ */
+mla_status mla_absorb_extend_paged(const void* q, const void* c_pages, const int32_t* block_table,
+                                   const void* w_uk, const void* w_uv, const void* gate, void* out, int B, int T,
+                                   int S, int H, int d_q, int d_v, int r, int64_t num_pages, int page_size,
+                                   int max_pages, float scale, mla_dtype dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mla_absorb_decode_paged needs ((size_t)-1: invalid). */
+size_t mla_absorb_decode_paged_workspace_size(int B, int H, int d_q, int r, int num_splits, mla_dtype dtype);
+
+/*
+ * Decode over a paged cache: as mla_absorb_decode, with sequence i's
+ * seq_lens[i] rows (int32 device array [B], the new token's own row
+ * included) in pages.  Lengths are clamped to [1, max_pages * page_size] on
+ * the device.  bf16 only.  The stream-K split works in 32-row tiles of each
+ * sequence; num_splits as for mla_absorb_decode.
+ */
+mla_status mla_absorb_decode_paged(const void* q, const void* c_pages, const int32_t* block_table,
+                                   const int32_t* seq_lens, const void* w_uk, const void* w_uv, const void* gate,
+                                   void* out, int B, int H, int d_q, int d_v, int r, int64_t num_pages,
+                                   int page_size, int max_pages, float scale, int num_splits, mla_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Cache append: writes row c_new[i] ([B, r], dtype) as row positions[i]
+ * (int32 device array [B]) of sequence i of the paged cache, in place; the
+ * row a decode step adds before it attends.  Any page size >= 1 works here;
+ * r * sizeof(dtype) must be a multiple of 16 bytes.  A position outside
+ * [0, max_pages * page_size) skips the row.  No workspace.
+ */
+mla_status mla_cache_append_paged(const void* c_new, void* c_pages, const int32_t* block_table,
+                                  const int32_t* positions, int B, int r, int64_t num_pages, int page_size,
+                                  int max_pages, mla_dtype dtype, void* stream);
+
+/*
  * Bytes of workspace mla_gated_forward needs (bf16 only; (size_t)-1 for
  * invalid sizes or dtypes).
  */

@@ -16,8 +16,9 @@ import os
 __all__ = [
     "LIB_PATH", "MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED", "MLA_ERR_WORKSPACE",
     "MLA_ERR_HIP", "DTYPE_F32", "DTYPE_BF16", "MLAError", "lib", "status_string",
-    "prefill_workspace_size", "decode_workspace_size", "forward_workspace_size", "mla_absorb_prefill",
-    "mla_absorb_extend", "mla_absorb_decode", "mla_gated_forward",
+    "prefill_workspace_size", "decode_workspace_size", "decode_paged_workspace_size", "forward_workspace_size",
+    "mla_absorb_prefill", "mla_absorb_extend", "mla_absorb_extend_paged", "mla_absorb_decode",
+    "mla_absorb_decode_paged", "mla_cache_append_paged", "mla_gated_forward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_absorb.so")
@@ -32,6 +33,10 @@ EXPORTS = (
     "mla_absorb_extend",
     "mla_absorb_decode_workspace_size",
     "mla_absorb_decode",
+    "mla_absorb_extend_paged",
+    "mla_absorb_decode_paged_workspace_size",
+    "mla_absorb_decode_paged",
+    "mla_cache_append_paged",
     "mla_gated_forward_workspace_size",
     "mla_gated_forward",
 )
@@ -65,6 +70,14 @@ def lib() -> ct.CDLL:
         L.mla_absorb_decode_workspace_size.restype = sz
         L.mla_absorb_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, I64, F, I, I, vp, sz, vp]
         L.mla_absorb_decode.restype = I
+        L.mla_absorb_extend_paged.argtypes = [vp] * 7 + [I] * 7 + [I64, I, I, F, I, vp, sz, vp]
+        L.mla_absorb_extend_paged.restype = I
+        L.mla_absorb_decode_paged_workspace_size.argtypes = [I, I, I, I, I, I]
+        L.mla_absorb_decode_paged_workspace_size.restype = sz
+        L.mla_absorb_decode_paged.argtypes = [vp] * 8 + [I] * 5 + [I64, I, I, F, I, I, vp, sz, vp]
+        L.mla_absorb_decode_paged.restype = I
+        L.mla_cache_append_paged.argtypes = [vp] * 4 + [I, I, I64, I, I, I, vp]
+        L.mla_cache_append_paged.restype = I
         L.mla_gated_forward_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
         L.mla_gated_forward_workspace_size.restype = sz
         L.mla_gated_forward.argtypes = [vp] * 11 + [I] * 8 + [F, F, I, vp, sz, vp]
@@ -91,6 +104,13 @@ def decode_workspace_size(B: int, H: int, d_q: int, r: int, num_splits: int, dty
     n = lib().mla_absorb_decode_workspace_size(B, H, d_q, r, num_splits, dtype)
     if n == _BAD:
         raise MLAError(MLA_ERR_INVALID_ARG, "mla_absorb_decode_workspace_size")
+    return n
+
+
+def decode_paged_workspace_size(B: int, H: int, d_q: int, r: int, num_splits: int, dtype: int) -> int:
+    n = lib().mla_absorb_decode_paged_workspace_size(B, H, d_q, r, num_splits, dtype)
+    if n == _BAD:
+        raise MLAError(MLA_ERR_INVALID_ARG, "mla_absorb_decode_paged_workspace_size")
     return n
 
 
@@ -214,6 +234,88 @@ def mla_absorb_decode(q, c_cache, cu_seqlens, w_uk, w_uv, gate, scale: float, nu
     if st != MLA_OK:
         raise MLAError(st, "mla_absorb_decode")
     return out
+
+
+def mla_absorb_extend_paged(q, c_pages, block_table, S: int, w_uk, w_uv, gate, scale: float, out=None,
+                            workspace=None, stream=None):
+    """Chunked prefill against a paged latent cache: c_pages
+    [num_pages, page_size, r], block_table [B, max_pages] int32 (device);
+    each sequence holds S rows, the T queries q [B,T,H,d_q] are its last
+    positions.  gate, out [B,T,H*d_v]."""
+    torch = _torch()
+    B, T, H, dq = q.shape
+    npg, ps, r = c_pages.shape
+    dv = w_uv.shape[1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    for t, shp, n in ((q, (B, T, H, dq), "q"), (c_pages, (npg, ps, r), "c_pages"), (w_uk, (H, dq, r), "w_uk"),
+                      (w_uv, (H, dv, r), "w_uv"), (gate, (B, T, H * dv), "gate")):
+        _check(t, shp, dt, n)
+    _check(block_table, (B, block_table.shape[1]), torch.int32, "block_table")
+    if out is None:
+        out = torch.empty((B, T, H * dv), dtype=dt, device=q.device)
+    _check(out, (B, T, H * dv), dt, "out")
+    need = prefill_workspace_size(B, T, H, dq, r, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().mla_absorb_extend_paged(q.data_ptr(), c_pages.data_ptr(), block_table.data_ptr(), w_uk.data_ptr(),
+                                       w_uv.data_ptr(), gate.data_ptr(), out.data_ptr(), B, T, int(S), H, dq, dv, r,
+                                       npg, ps, block_table.shape[1], float(scale), code, workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_absorb_extend_paged")
+    return out
+
+
+def mla_absorb_decode_paged(q, c_pages, block_table, seq_lens, w_uk, w_uv, gate, scale: float,
+                            num_splits: int = 0, out=None, workspace=None, stream=None):
+    """Decode against a paged latent cache: c_pages [num_pages, page_size, r],
+    block_table [B, max_pages] int32, seq_lens [B] int32 (device, the new
+    token's own row included).  q [B,H,d_q], gate [B,H*d_v] -> [B,H*d_v]."""
+    torch = _torch()
+    B, H, dq = q.shape
+    npg, ps, r = c_pages.shape
+    dv = w_uv.shape[1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    for t, shp, n in ((q, (B, H, dq), "q"), (c_pages, (npg, ps, r), "c_pages"), (w_uk, (H, dq, r), "w_uk"),
+                      (w_uv, (H, dv, r), "w_uv"), (gate, (B, H * dv), "gate")):
+        _check(t, shp, dt, n)
+    _check(block_table, (B, block_table.shape[1]), torch.int32, "block_table")
+    _check(seq_lens, (B,), torch.int32, "seq_lens")
+    if out is None:
+        out = torch.empty((B, H * dv), dtype=dt, device=q.device)
+    _check(out, (B, H * dv), dt, "out")
+    need = decode_paged_workspace_size(B, H, dq, r, num_splits, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().mla_absorb_decode_paged(q.data_ptr(), c_pages.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+                                       w_uk.data_ptr(), w_uv.data_ptr(), gate.data_ptr(), out.data_ptr(), B, H, dq,
+                                       dv, r, npg, ps, block_table.shape[1], float(scale), int(num_splits), code,
+                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                       _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_absorb_decode_paged")
+    return out
+
+
+def mla_cache_append_paged(c_new, c_pages, block_table, positions, stream=None):
+    """Writes row c_new[i] ([B, r]) at position positions[i] (int32, device)
+    of sequence i of the paged cache c_pages (in place)."""
+    torch = _torch()
+    B, r = c_new.shape
+    npg, ps, _ = c_pages.shape
+    dt = c_new.dtype
+    _check(c_new, (B, r), dt, "c_new")
+    _check(c_pages, (npg, ps, r), dt, "c_pages")
+    _check(block_table, (B, block_table.shape[1]), torch.int32, "block_table")
+    _check(positions, (B,), torch.int32, "positions")
+    st = lib().mla_cache_append_paged(c_new.data_ptr(), c_pages.data_ptr(), block_table.data_ptr(),
+                                      positions.data_ptr(), B, r, npg, ps, block_table.shape[1], _dtype_code(c_new),
+                                      _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_cache_append_paged")
+    return c_pages
 
 
 def mla_gated_forward(x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o,

@@ -124,6 +124,22 @@ __device__ __forceinline__ void wg_barrier() {
 
 // s_waitcnt lgkmcnt(0): this wave's LDS writes have landed (before a barrier
 // that publishes them to the other waves).
+// Scalar (SMEM) load of a wave-uniform int.  A plain load of a value the
+// compiler cannot prove read-only becomes a vector load, and waiting for it
+// (vmcnt) would also wait for every LDS-DMA tile copy in flight.  The SMEM
+// load is tracked by lgkmcnt instead; it waits for itself before returning.
+__device__ __forceinline__ int sload_i32(const int* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  // readfirstlane returns int: widen through unsigned, or a low word with
+  // bit 31 set would sign-extend over the high word
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)a);
+  const uint64_t s = ((uint64_t)hi << 32) | (uint64_t)lo;
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(s) : "memory");
+  return v;
+}
+
 __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }

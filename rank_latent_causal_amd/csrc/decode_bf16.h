@@ -268,6 +268,8 @@ struct DecodeMergeArgs {
   bf16* out;             // [B, H*DV]
   int B, H, G;
   long long N;
+  const int* n_dev;      // if set, N and G are read from n_dev[0] and n_dev[1] (paged decode:
+                         // cu holds tile counts, G the number of non-empty ranges)
 };
 
 // index of the range that holds cache row x (every range is non-empty)
@@ -325,8 +327,10 @@ __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
   if (w < DV / 16) load_w(w, wa, gv);
 
   {
+    const long long N = a.n_dev ? (long long)a.n_dev[0] : a.N;
+    const long long G = a.n_dev ? (long long)a.n_dev[1] : a.G;
     const long long s0 = a.cu[ic], s1 = a.cu[ic + 1];
-    const int k0 = range_of(s0, a.N, a.G), k1 = range_of(s1 - 1, a.N, a.G);
+    const int k0 = range_of(s0, N, G), k1 = range_of(s1 - 1, N, G);
     const int j0 = w * JW + kq * JL;
     auto load = [&](int k, float& mk, float& lk, VT (&o)[NVV]) {
       const size_t base = (size_t)(k + ic) * a.H + h;
@@ -392,6 +396,214 @@ __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
       gv = gn;
     }
   }
+}
+
+// ----------------------------------------------------------------- paged
+// Decode against a paged latent cache: sequence i's row u lives in page
+// block_table[i, u / page_size] at slot u % page_size of a page pool
+// [num_pages, page_size, R].  page_size is a power of two of at least the
+// 32-row tile, so a tile never crosses a page.  The split works in tile units: sequence i
+// owns ceil(len_i / 32) consecutive tiles of a virtual tile sequence, range
+// k of G covers tiles [floor(k NT / G), floor((k+1) NT / G)), and a tile
+// belongs to exactly one sequence.  Partial slots, the merge and its
+// range arithmetic are those of the packed decode, in tile units.
+
+// One workgroup: clamps the lengths to [1, max_pages * page_size] and writes
+// them, the exclusive prefix sums of the tile counts (cu_t[B] = NT) and the
+// number of ranges cu_t[B + 1] = min(G, NT), so that no range is empty (the
+// merge walks every range between a sequence's first and last).
+__global__ void __launch_bounds__(256) mla_paged_prepare(const int* __restrict__ seq_lens, int B, int max_rows,
+                                                         int G, int* __restrict__ lens, int* __restrict__ cu_t) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int carry = 0;
+  if (tid == 0) cu_t[0] = 0;
+  for (int base = 0; base < B; base += 256) {
+    const int i = base + tid;
+    int len = 0, tiles = 0;
+    if (i < B) {
+      len = seq_lens[i];
+      len = len < 1 ? 1 : (len > max_rows ? max_rows : len);
+      tiles = (len + 31) / 32;
+      lens[i] = len;
+    }
+    int incl = tiles;  // inclusive scan inside the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int before = carry;
+    for (int u = 0; u < w; ++u) before += wsum[u];
+    if (i < B) cu_t[i + 1] = before + incl;
+    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  if (tid == 0) cu_t[B + 1] = min(G, carry);
+}
+
+struct DecodePagedArgs {
+  const bf16* qabs;         // [B, H, R]
+  const bf16* pages;        // [num_pages, page_size, R]
+  const int* block_table;   // [B, max_pages]
+  const int* lens;          // [B] clamped lengths (mla_paged_prepare)
+  const int* cu_t;          // [B + 2] tile prefix sums, then the range count (mla_paged_prepare)
+  float* part_o;            // [(G + B), H, R]
+  float* part_ml;           // [(G + B), H, 2]
+  int B, H, G;                           // G: workgroups launched (>= the range count)
+  int page_shift, max_pages, num_pages;  // pages of 2^page_shift rows
+};
+
+template <int R>
+__global__ void __launch_bounds__(64 * kDecodeWaves)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+mla_decode_split_paged(DecodePagedArgs a) {
+  using LT = LatentTile<R>;
+  constexpr int NS = kDecodeStages;
+  constexpr int LPW = copies_per_wave<R>(kDecodeWaves);
+  static_assert(LT::COPIES % kDecodeWaves == 0 || LT::COPIES < kDecodeWaves, "copy split");
+  static_assert(LT::KT == 32, "tile rows");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * LT::BYTES];
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+
+  const int k = blockIdx.x;
+  const int NT = __builtin_amdgcn_readfirstlane(a.cu_t[a.B]);
+  const int G = __builtin_amdgcn_readfirstlane(a.cu_t[a.B + 1]);  // min(launched, NT): ranges are non-empty
+  if (k >= G) return;  // the whole workgroup leaves
+  const int lo = (int)((long long)k * NT / G), hi = (int)((long long)(k + 1) * NT / G);
+  const int ntiles = hi - lo;
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int h = 16 * w + l16;
+  const bool compute = 16 * w < a.H;  // wave-uniform
+  const bool hvalid = h < a.H;
+  const int hc = hvalid ? h : a.H - 1;
+
+  // the sequence of tile lo: the largest i with cu_t[i] <= lo
+  int i;
+  {
+    int l = 0, r = a.B - 1;
+    while (l < r) {
+      const int mid = (l + r + 1) >> 1;
+      if (a.cu_t[mid] <= lo) l = mid; else r = mid - 1;
+    }
+    i = __builtin_amdgcn_readfirstlane(l);
+  }
+  int seq_t0 = __builtin_amdgcn_readfirstlane(a.cu_t[i]);
+  int seq_t1 = __builtin_amdgcn_readfirstlane(a.cu_t[i + 1]);
+  int len = __builtin_amdgcn_readfirstlane(a.lens[i]);
+
+  TileCopier<R, kDecodeWaves> copier;
+  copier.init(w, lane);
+  // The copy cursor runs NS - 1 tiles ahead of the compute cursor and keeps
+  // its own sequence bookkeeping (scalar registers).
+  int pi = i, p_t0 = seq_t0, p_t1 = seq_t1;
+  auto issue_tile = [&](int t, MLA_LDS char* stage) {
+    while (t >= p_t1) {  // every sequence owns at least one tile
+      ++pi;
+      p_t0 = p_t1;
+      p_t1 = sload_i32(a.cu_t + pi + 1);
+    }
+    const int pos = (t - p_t0) * LT::KT;
+    int pg = sload_i32(a.block_table + (size_t)pi * a.max_pages + (pos >> a.page_shift));
+    int valid = min(sload_i32(a.lens + pi) - pos, LT::KT);
+    if ((unsigned)pg >= (unsigned)a.num_pages) {
+      pg = 0;
+      valid = 0;
+    }
+    const size_t row = ((size_t)pg << a.page_shift) + (pos & ((1 << a.page_shift) - 1));
+    copier.issue(a.pages + row * R, 0, valid, stage);
+  };
+
+  WaveAttn<R> st;
+  auto load_q = [&](int seq) {
+    const bf16* src = a.qabs + ((size_t)seq * a.H + hc) * R + 8 * kq;
+#pragma unroll
+    for (int kk = 0; kk < R / 32; ++kk) st.qT[kk] = *(const bf16x8*)(src + 32 * kk);
+  };
+  issue_tile(lo, smem);
+  if (compute) load_q(i);
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int p = 1; p < NS - 1; ++p)
+    if (p < ntiles) issue_tile(lo + p, smem + p * LT::BYTES);
+  st.reset();
+  st.init_addressing(l16, kq);
+
+  static_assert(NS == 4, "the waits below assume four stages");
+  for (int it = 0; it < ntiles; ++it) {
+    const int younger = min(NS - 2, ntiles - 1 - it);
+    if (younger >= 2) wait_vmcnt<2 * LPW>();
+    else if (younger == 1) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
+    wg_barrier();  // tile `it` visible; every wave is done with tile it-1
+    const int nx = it + NS - 1;
+    if (nx < ntiles) issue_tile(lo + nx, smem + (nx % NS) * LT::BYTES);
+    const MLA_LDS char* tile = smem + (it % NS) * LT::BYTES;
+    const int t = lo + it;
+    if (t == seq_t1) {
+      // the previous tile ended a sequence (its partial is out): start the next
+      ++i;
+      seq_t0 = seq_t1;
+      seq_t1 = sload_i32(a.cu_t + i + 1);
+      len = sload_i32(a.lens + i);
+      if (compute) load_q(i);
+      wait_vmcnt<0>();  // see the packed kernel: no query load stays pending across the back edge
+      st.reset();
+    }
+
+    if (compute) {
+      f32x4 sa, sb;
+      st.scores(tile, sa, sb);
+      const int k_hi = len - (t - seq_t0) * LT::KT;  // rows of this sequence in the tile
+      if (k_hi < LT::KT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (4 * kq + e >= k_hi) sa[e] = -INFINITY;
+          if (16 + 4 * kq + e >= k_hi) sb[e] = -INFINITY;
+        }
+      }
+      st.update(tile, sa, sb);
+      if (t + 1 == seq_t1 || t + 1 == hi) {
+        // this range's piece of sequence i ends here: emit its partial
+        const int slot = k + i;
+        const float l_tot = col_sum(st.l_run);
+        if (hvalid) {
+          float* dst = a.part_o + ((size_t)slot * a.H + h) * R + 4 * kq;
+#pragma unroll
+          for (int u = 0; u < R / 16; ++u) *(f32x4*)(dst + 16 * u) = st.oT[u];
+          if (kq == 0) {
+            a.part_ml[((size_t)slot * a.H + h) * 2 + 0] = st.m_run;
+            a.part_ml[((size_t)slot * a.H + h) * 2 + 1] = l_tot;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Cache append: row c_new[i] becomes row positions[i] of sequence i.  One
+// wave per row, 16-byte chunks; a position or page index out of range skips
+// the row (nothing is written).
+__global__ void __launch_bounds__(256) mla_cache_append_paged(const char* __restrict__ c_new,
+                                                              char* __restrict__ pages,
+                                                              const int* __restrict__ block_table,
+                                                              const int* __restrict__ positions, int B,
+                                                              int row_bytes, int page_size, int max_pages,
+                                                              int num_pages) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (i >= B) return;
+  const int u = positions[i];
+  if (u < 0 || u >= max_pages * page_size) return;
+  const int pg = block_table[(size_t)i * max_pages + u / page_size];
+  if (pg < 0 || pg >= num_pages) return;
+  const char* src = c_new + (size_t)i * row_bytes;
+  char* dst = pages + ((size_t)pg * page_size + u % page_size) * row_bytes;
+  for (int off = 16 * lane; off < row_bytes; off += 16 * 64)
+    *(u32x4*)(dst + off) = *(const u32x4*)(src + off);
 }
 
 }  // namespace mla

@@ -68,7 +68,7 @@ DecodeLayout decode_layout(int B, int H, int dq, int r, int G) {
 }
 
 // r = 32: one wave per (head, 16 positions); r >= 256: wave pairs split r.
-template <int DQ, int DV, int R>
+template <int DQ, int DV, int R, bool PAGED = false>
 void launch_prefill_bf16(mla::PrefillArgs a, hipStream_t s) {
   if constexpr (R >= 256) {
     // Two 4-wave workgroups per CU (80 KiB of LDS each), one tile of
@@ -78,13 +78,13 @@ void launch_prefill_bf16(mla::PrefillArgs a, hipStream_t s) {
     a.ntb = (a.T + 31) / 32;
     a.nhg = (a.H + NW / 2 - 1) / (NW / 2);
     a.xcd_remap = (a.nhg % 8) == 0 ? 1 : 0;
-    hipLaunchKernelGGL((mla::mla_prefill_pair_kernel<DQ, DV, R, NW, NS>), dim3(a.B * a.ntb * a.nhg),
+    hipLaunchKernelGGL((mla::mla_prefill_pair_kernel<DQ, DV, R, NW, NS, PAGED>), dim3(a.B * a.ntb * a.nhg),
                        dim3(64 * NW), 0, s, a);
   } else {
     a.ntb = (a.T + mla::kPrefillRows - 1) / mla::kPrefillRows;
     a.nhg = (a.H + 3) / 4;
     a.xcd_remap = (a.nhg % 8) == 0 ? 1 : 0;
-    hipLaunchKernelGGL((mla::mla_prefill_bf16_kernel<DQ, DV, R>), dim3(a.B * a.ntb * a.nhg),
+    hipLaunchKernelGGL((mla::mla_prefill_bf16_kernel<DQ, DV, R, PAGED>), dim3(a.B * a.ntb * a.nhg),
                        dim3(64 * mla::kPrefillWaves), 0, s, a);
   }
 }
@@ -96,6 +96,48 @@ void launch_decode_bf16(const mla::DecodeAbsorbArgs& aa, const mla::DecodeSplitA
   hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(aa.H * (R / JC)), dim3(256), 0, s, aa);
   hipLaunchKernelGGL((mla::mla_decode_split<R>), dim3(sa.G), dim3(64 * mla::kDecodeWaves), 0, s, sa);
   hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + 15) / 16) * ma.H), dim3(256), 0, s, ma);
+}
+
+template <int DQ, int DV, int R>
+void launch_decode_paged_bf16(const mla::DecodeAbsorbArgs& aa, const int* seq_lens, int max_rows,
+                              const mla::DecodePagedArgs& sa, const mla::DecodeMergeArgs& ma, hipStream_t s) {
+  constexpr int JC = R < 64 ? R : 64;
+  hipLaunchKernelGGL(mla::mla_paged_prepare, dim3(1), dim3(256), 0, s, seq_lens, sa.B, max_rows, sa.G,
+                     const_cast<int*>(sa.lens), const_cast<int*>(sa.cu_t));
+  hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(aa.H * (R / JC)), dim3(256), 0, s, aa);
+  hipLaunchKernelGGL((mla::mla_decode_split_paged<R>), dim3(sa.G), dim3(64 * mla::kDecodeWaves), 0, s, sa);
+  hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + 15) / 16) * ma.H), dim3(256), 0, s, ma);
+}
+
+struct PagedDecodeLayout {
+  DecodeLayout d;
+  size_t lens = 0, cu_t = 0, total = 0;
+};
+
+PagedDecodeLayout paged_decode_layout(int B, int H, int dq, int r, int G) {
+  PagedDecodeLayout L;
+  L.d = decode_layout(B, H, dq, r, G);
+  size_t off = L.d.total;
+  L.lens = off;
+  off = align_up(off + (size_t)B * sizeof(int));
+  L.cu_t = off;
+  off = align_up(off + (size_t)(B + 2) * sizeof(int));
+  L.total = off;
+  return L;
+}
+
+// page pool geometry shared by the paged entry points
+int log2_exact(int v) {
+  int k = 0;
+  while ((1 << k) < v) ++k;
+  return (1 << k) == v ? k : -1;
+}
+
+bool paged_geometry_ok(int B, int r, long long num_pages, int page_size, int max_pages) {
+  if (num_pages <= 0 || page_size < 32 || max_pages <= 0 || log2_exact(page_size) < 0) return false;
+  return num_pages < (1LL << 31) && fits(num_pages, page_size, r) &&
+         (long long)max_pages * page_size < (1LL << 31) && fits(B, max_pages) &&
+         (long long)B * max_pages * page_size / 32 < (1LL << 31);
 }
 
 void launch_wuk_transpose(const bf16* w, bf16* wt, int H, int dq, int r, hipStream_t s) {
@@ -167,10 +209,12 @@ mla_status mla_absorb_prefill(const void* q, const void* c, const void* w_uk, co
                            workspace_bytes, stream);
 }
 
-mla_status mla_absorb_extend(const void* q, const void* c, const void* w_uk, const void* w_uv,
-                             const void* gate, void* out, int B, int T, int S, int H, int d_q, int d_v,
-                             int r, float scale, mla_dtype dtype, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+// Chunked prefill over a contiguous latent [B, S, r] (block_table null) or a
+// paged one (pool c of num_pages pages, geometry checked by the caller).
+static mla_status extend_impl(const void* q, const void* c, const int32_t* block_table, long long num_pages,
+                       int page_size, int max_pages, const void* w_uk, const void* w_uv, const void* gate,
+                       void* out, int B, int T, int S, int H, int d_q, int d_v, int r, float scale,
+                       mla_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !c || !w_uk || !w_uv || !gate || !out) return MLA_ERR_INVALID_ARG;
   if (B <= 0 || T <= 0 || S < T || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return MLA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
@@ -180,6 +224,7 @@ mla_status mla_absorb_extend(const void* q, const void* c, const void* w_uk, con
   if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return MLA_ERR_INVALID_ARG;
   if (!fits(B, T, H, d_q > d_v ? (d_q > r ? d_q : r) : (d_v > r ? d_v : r)) || !fits(B, S, r))
     return MLA_ERR_UNSUPPORTED;
+  const bool paged = block_table != nullptr;
   hipStream_t s = (hipStream_t)stream;
 
   if (dtype == MLA_DTYPE_F32) {
@@ -210,10 +255,42 @@ mla_status mla_absorb_extend(const void* q, const void* c, const void* w_uk, con
   a.gate = (const bf16*)gate; a.out = (bf16*)out;
   a.B = B; a.T = T; a.S = S; a.H = H;
   a.qscale = scale * mla::kLog2e;
-  if (d_q == 16) launch_prefill_bf16<16, 16, 32>(a, s);
-  else if (d_q == 64) launch_prefill_bf16<64, 64, 256>(a, s);
-  else launch_prefill_bf16<128, 128, 512>(a, s);
+  a.block_table = block_table; a.max_pages = max_pages; a.num_pages = (int)num_pages;
+  a.page_shift = paged ? log2_exact(page_size) : 0;
+  if (paged) {
+    if (d_q == 16) launch_prefill_bf16<16, 16, 32, true>(a, s);
+    else if (d_q == 64) launch_prefill_bf16<64, 64, 256, true>(a, s);
+    else launch_prefill_bf16<128, 128, 512, true>(a, s);
+  } else {
+    if (d_q == 16) launch_prefill_bf16<16, 16, 32>(a, s);
+    else if (d_q == 64) launch_prefill_bf16<64, 64, 256>(a, s);
+    else launch_prefill_bf16<128, 128, 512>(a, s);
+  }
   return launch_status();
+}
+
+
+mla_status mla_absorb_extend(const void* q, const void* c, const void* w_uk, const void* w_uv,
+                             const void* gate, void* out, int B, int T, int S, int H, int d_q, int d_v,
+                             int r, float scale, mla_dtype dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return extend_impl(q, c, nullptr, 0, 0, 0, w_uk, w_uv, gate, out, B, T, S, H, d_q, d_v, r, scale, dtype,
+                     workspace, workspace_bytes, stream);
+}
+
+mla_status mla_absorb_extend_paged(const void* q, const void* c_pages, const int32_t* block_table,
+                                   const void* w_uk, const void* w_uv, const void* gate, void* out, int B, int T,
+                                   int S, int H, int d_q, int d_v, int r, int64_t num_pages, int page_size,
+                                   int max_pages, float scale, mla_dtype dtype, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!c_pages || !block_table || !aligned16(block_table)) return MLA_ERR_INVALID_ARG;
+  if (num_pages <= 0 || page_size <= 0 || max_pages <= 0) return MLA_ERR_INVALID_ARG;
+  if (page_size < 32 || log2_exact(page_size) < 0 || (long long)max_pages * page_size < S)
+    return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_DTYPE_BF16) return dtype == MLA_DTYPE_F32 ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (!paged_geometry_ok(B, r, num_pages, page_size, max_pages)) return MLA_ERR_UNSUPPORTED;
+  return extend_impl(q, c_pages, block_table, num_pages, page_size, max_pages, w_uk, w_uv, gate, out, B, T, S, H,
+                     d_q, d_v, r, scale, dtype, workspace, workspace_bytes, stream);
 }
 
 size_t mla_absorb_decode_workspace_size(int B, int H, int d_q, int r, int num_splits, mla_dtype dtype) {
@@ -279,6 +356,78 @@ mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* 
   if (d_q == 16) launch_decode_bf16<16, 16, 32>(aa, sa, ma, s);
   else if (d_q == 64) launch_decode_bf16<64, 64, 256>(aa, sa, ma, s);
   else launch_decode_bf16<128, 128, 512>(aa, sa, ma, s);
+  return launch_status();
+}
+
+size_t mla_absorb_decode_paged_workspace_size(int B, int H, int d_q, int r, int num_splits, mla_dtype dtype) {
+  if (B <= 0 || H <= 0 || d_q <= 0 || r <= 0) return kBadSize;
+  if (dtype != MLA_DTYPE_BF16) return kBadSize;
+  const int G = num_splits > 0 ? num_splits : device_cu_count();
+  if (G <= 0) return kBadSize;
+  return paged_decode_layout(B, H, d_q, r, G).total;
+}
+
+mla_status mla_absorb_decode_paged(const void* q, const void* c_pages, const int32_t* block_table,
+                                   const int32_t* seq_lens, const void* w_uk, const void* w_uv, const void* gate,
+                                   void* out, int B, int H, int d_q, int d_v, int r, int64_t num_pages,
+                                   int page_size, int max_pages, float scale, int num_splits, mla_dtype dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !c_pages || !block_table || !seq_lens || !w_uk || !w_uv || !gate || !out) return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return MLA_ERR_INVALID_ARG;
+  if (num_pages <= 0 || max_pages <= 0 || page_size < 32 || log2_exact(page_size) < 0) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, c_pages, block_table, seq_lens, w_uk, w_uv, gate, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_DTYPE_BF16) return dtype == MLA_DTYPE_F32 ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (!bf16_shape_supported(d_q, d_v, r) || H > 16 * mla::kDecodeWaves) return MLA_ERR_UNSUPPORTED;
+  if (!paged_geometry_ok(B, r, num_pages, page_size, max_pages) || !fits(B, H, d_q > d_v ? d_q : d_v))
+    return MLA_ERR_UNSUPPORTED;
+  const int G = num_splits > 0 ? num_splits : device_cu_count();
+  if (G <= 0) return MLA_ERR_HIP;
+  const PagedDecodeLayout L = paged_decode_layout(B, H, d_q, r, G);
+  if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+  if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  mla::DecodeAbsorbArgs aa{};
+  aa.q = (const bf16*)q; aa.wuk = (const bf16*)w_uk; aa.qabs = (bf16*)(ws + L.d.qabs);
+  aa.B = B; aa.H = H; aa.qscale = scale * mla::kLog2e;
+  mla::DecodePagedArgs sa{};
+  sa.qabs = aa.qabs; sa.pages = (const bf16*)c_pages; sa.block_table = block_table;
+  sa.lens = (const int*)(ws + L.lens); sa.cu_t = (const int*)(ws + L.cu_t);
+  sa.part_o = (float*)(ws + L.d.part_o); sa.part_ml = (float*)(ws + L.d.part_ml);
+  sa.B = B; sa.H = H; sa.G = G;
+  sa.page_shift = log2_exact(page_size); sa.max_pages = max_pages; sa.num_pages = (int)num_pages;
+  mla::DecodeMergeArgs ma{};
+  ma.part_o = sa.part_o; ma.part_ml = sa.part_ml; ma.cu = sa.cu_t; ma.n_dev = sa.cu_t + B;
+  ma.wuv = (const bf16*)w_uv; ma.gate = (const bf16*)gate; ma.out = (bf16*)out;
+  ma.B = B; ma.H = H; ma.G = G; ma.N = 0;
+  const int max_rows = max_pages * page_size;
+  if (d_q == 16) launch_decode_paged_bf16<16, 16, 32>(aa, seq_lens, max_rows, sa, ma, s);
+  else if (d_q == 64) launch_decode_paged_bf16<64, 64, 256>(aa, seq_lens, max_rows, sa, ma, s);
+  else launch_decode_paged_bf16<128, 128, 512>(aa, seq_lens, max_rows, sa, ma, s);
+  return launch_status();
+}
+
+mla_status mla_cache_append_paged(const void* c_new, void* c_pages, const int32_t* block_table,
+                                  const int32_t* positions, int B, int r, int64_t num_pages, int page_size,
+                                  int max_pages, mla_dtype dtype, void* stream) {
+  if (!c_new || !c_pages || !block_table || !positions) return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || r <= 0 || num_pages <= 0 || page_size <= 0 || max_pages <= 0) return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_DTYPE_F32 && dtype != MLA_DTYPE_BF16) return MLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {c_new, c_pages, block_table, positions};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MLA_ERR_INVALID_ARG;
+  const int row_bytes = r * (dtype == MLA_DTYPE_F32 ? 4 : 2);
+  if (row_bytes % 16) return MLA_ERR_UNSUPPORTED;
+  if (num_pages >= (1LL << 31) || (long long)max_pages * page_size >= (1LL << 31) || !fits(B, max_pages) ||
+      !fits(num_pages, page_size, row_bytes) || B >= (1 << 30))
+    return MLA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(mla::mla_cache_append_paged, dim3((B + 3) / 4), dim3(256), 0, (hipStream_t)stream,
+                     (const char*)c_new, (char*)c_pages, block_table, positions, B, row_bytes, page_size, max_pages,
+                     (int)num_pages);
   return launch_status();
 }
 

@@ -32,13 +32,41 @@ struct PrefillArgs {
   int ntb;           // ceil(T / kPrefillRows) query blocks
   int nhg;           // ceil(H / 4) head groups
   int xcd_remap;     // 1: head group hg runs on XCD hg % 8 (weights stay in its L2)
+  // paged latent (the kernels' PAGED instantiations): c is a pool of
+  // num_pages pages of 2^page_shift rows (at least the 32-row key tile);
+  // row u of sequence b is page block_table[b, u >> page_shift], slot
+  // u & (2^page_shift - 1).  A page index outside [0, num_pages) reads as
+  // zero rows.
+  const int* block_table;  // [B, max_pages]
+  int page_shift, max_pages, num_pages;
 };
+
+// Issues the copies of key tile j (rows 32j .. 32j+31 of sequence b) into an
+// LDS stage: from the contiguous latent [B, S, R], or through the block table.
+template <bool PAGED, int R, int NW>
+__device__ __forceinline__ void issue_key_tile(const TileCopier<R, NW>& copier, const PrefillArgs& a, int b,
+                                               int j, MLA_LDS char* stage) {
+  constexpr int KT = LatentTile<R>::KT;
+  if constexpr (PAGED) {
+    const int pos = j * KT;
+    int pg = sload_i32(a.block_table + (size_t)b * a.max_pages + (pos >> a.page_shift));
+    int valid = min(a.S - pos, KT);
+    if ((unsigned)pg >= (unsigned)a.num_pages) {
+      pg = 0;
+      valid = 0;
+    }
+    const size_t row = ((size_t)pg << a.page_shift) + (pos & ((1 << a.page_shift) - 1));
+    copier.issue(a.c + row * R, 0, valid, stage);
+  } else {
+    copier.issue(a.c + (size_t)b * a.S * R, j * KT, a.S, stage);
+  }
+}
 
 // waves per workgroup: 4 heads x (kPrefillWaves / 4) blocks of 16 positions
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRows = 16 * (kPrefillWaves / 4);  // query positions per workgroup
 
-template <int DQ, int DV, int R>
+template <int DQ, int DV, int R, bool PAGED = false>
 __global__ void __launch_bounds__(64 * kPrefillWaves)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 mla_prefill_bf16_kernel(PrefillArgs a) {
@@ -80,14 +108,13 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
   const bool tvalid = t < T;
   const int tc = tvalid ? t : T - 1;
   const int S = a.S, P = S - T;  // query t sits at position P + t
-  const bf16* __restrict__ cb = a.c + (size_t)b * S * R;
 
   const int ntiles = (P + min(t0 + kPrefillRows, T) + LT::KT - 1) / LT::KT;
 
   // stream the first latent tile while the absorb prologue runs
   TileCopier<R, kPrefillWaves> copier;
   copier.init(w, lane);
-  copier.issue(cb, 0, S, smem);
+  issue_key_tile<PAGED>(copier, a, b, 0, smem);
 
   WaveAttn<R> st;
   absorb_rows<DQ, R>(a.q + (((size_t)b * T + tc) * H + hc) * DQ, a.wukT + (size_t)hc * R * DQ, a.qscale,
@@ -97,7 +124,7 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
 
   for (int it = 0; it < ntiles; ++it) {
     if (it + 1 < ntiles) {
-      copier.issue(cb, (it + 1) * LT::KT, S, smem + ((it + 1) & 1) * LT::BYTES);
+      issue_key_tile<PAGED>(copier, a, b, it + 1, smem + ((it + 1) & 1) * LT::BYTES);
       wait_vmcnt<LPW>();
     } else {
       wait_vmcnt<0>();
@@ -140,7 +167,7 @@ struct PairConfig {
   static constexpr int LDS = NS * LatentTile<R>::BYTES + XBUF;   // bytes per workgroup
 };
 
-template <int DQ, int DV, int R, int NW, int NS>
+template <int DQ, int DV, int R, int NW, int NS, bool PAGED = false>
 __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 mla_prefill_pair_kernel(PrefillArgs a) {
@@ -192,14 +219,13 @@ mla_prefill_pair_kernel(PrefillArgs a) {
     tv[c] = tq[c] < T;
   }
   const int S = a.S, P = S - T;  // query t sits at position P + t
-  const bf16* __restrict__ cb = a.c + (size_t)b * S * R;
   const int ntiles = (P + min(t0 + 32, T) + LT::KT - 1) / LT::KT;
 
   TileCopier<R, NW> copier;
   copier.init(w, lane);
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
-    if (p < ntiles) copier.issue(cb, p * LT::KT, S, smem + p * LT::BYTES);
+    if (p < ntiles) issue_key_tile<PAGED>(copier, a, b, p, smem + p * LT::BYTES);
 
   PA st;
   {
@@ -246,7 +272,7 @@ mla_prefill_pair_kernel(PrefillArgs a) {
     // this tile rather than right after the first one, where every wave of
     // the workgroup would queue its copies at the same moment.
     if (it + NS - 1 < ntiles)
-      copier.issue(cb, (it + NS - 1) * LT::KT, S, smem + ((STG + NS - 1) % NS) * LT::BYTES);
+      issue_key_tile<PAGED>(copier, a, b, it + NS - 1, smem + ((STG + NS - 1) % NS) * LT::BYTES);
     {
       const f32x4 o00 = xbuf[(partner * 4 + 0) * 64 + lane], o01 = xbuf[(partner * 4 + 1) * 64 + lane];
       const f32x4 o10 = xbuf[(partner * 4 + 2) * 64 + lane], o11 = xbuf[(partner * 4 + 3) * 64 + lane];

@@ -173,3 +173,80 @@ def _forward(**kw):
 ])
 def test_forward_rejects(kw, status):
     assert _forward(**kw) == status
+
+
+def test_paged_decode_workspace_size():
+    n = mla.decode_paged_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_BF16)
+    assert n >= mla.decode_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_BF16) + 4 * (2 * 64 + 1)
+    with pytest.raises(mla.MLAError):
+        mla.decode_paged_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_F32)
+
+
+def _decode_paged(**kw):
+    a = dict(q=FAKE, c=FAKE, bt=FAKE, lens=FAKE, w_uk=FAKE, w_uv=FAKE, gate=FAKE, out=FAKE, B=2, H=96, dq=128,
+             dv=128, r=512, npg=100, ps=64, mp=10, scale=0.1, splits=8, dtype=mla.DTYPE_BF16, ws=FAKE,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return mla.lib().mla_absorb_decode_paged(a["q"], a["c"], a["bt"], a["lens"], a["w_uk"], a["w_uv"], a["gate"],
+                                             a["out"], a["B"], a["H"], a["dq"], a["dv"], a["r"], a["npg"], a["ps"],
+                                             a["mp"], a["scale"], a["splits"], a["dtype"], a["ws"], a["wsb"],
+                                             a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(lens=FAKE + 4), mla.MLA_ERR_INVALID_ARG),
+    (dict(ps=48), mla.MLA_ERR_INVALID_ARG),       # not a power of two
+    (dict(ps=16), mla.MLA_ERR_INVALID_ARG),       # smaller than the 32-row tile
+    (dict(npg=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mla.MLA_ERR_INVALID_ARG),
+    (dict(dtype=mla.DTYPE_F32), mla.MLA_ERR_UNSUPPORTED),
+    (dict(H=200), mla.MLA_ERR_UNSUPPORTED),
+    (dict(mp=1 << 26), mla.MLA_ERR_UNSUPPORTED),  # max_pages * page_size beyond int32
+    (dict(ws=None), mla.MLA_ERR_WORKSPACE),
+    (dict(wsb=4096), mla.MLA_ERR_WORKSPACE),
+])
+def test_decode_paged_rejects(kw, status):
+    assert _decode_paged(**kw) == status
+
+
+def _extend_paged(**kw):
+    a = dict(q=FAKE, c=FAKE, bt=FAKE, w_uk=FAKE, w_uv=FAKE, gate=FAKE, out=FAKE, B=1, T=8, S=20, H=4, dq=128,
+             dv=128, r=512, npg=10, ps=32, mp=4, scale=0.1, dtype=mla.DTYPE_BF16, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return mla.lib().mla_absorb_extend_paged(a["q"], a["c"], a["bt"], a["w_uk"], a["w_uv"], a["gate"], a["out"],
+                                             a["B"], a["T"], a["S"], a["H"], a["dq"], a["dv"], a["r"], a["npg"],
+                                             a["ps"], a["mp"], a["scale"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(S=200), mla.MLA_ERR_INVALID_ARG),       # more rows than max_pages * page_size
+    (dict(ps=96), mla.MLA_ERR_INVALID_ARG),
+    (dict(S=7), mla.MLA_ERR_INVALID_ARG),
+    (dict(dtype=mla.DTYPE_F32), mla.MLA_ERR_UNSUPPORTED),
+    (dict(dq=96, dv=96, r=384), mla.MLA_ERR_UNSUPPORTED),
+    (dict(wsb=16), mla.MLA_ERR_WORKSPACE),
+])
+def test_extend_paged_rejects(kw, status):
+    assert _extend_paged(**kw) == status
+
+
+def _append(**kw):
+    a = dict(c_new=FAKE, c=FAKE, bt=FAKE, pos=FAKE, B=2, r=512, npg=10, ps=64, mp=4, dtype=mla.DTYPE_BF16,
+             stream=None)
+    a.update(kw)
+    return mla.lib().mla_cache_append_paged(a["c_new"], a["c"], a["bt"], a["pos"], a["B"], a["r"], a["npg"],
+                                            a["ps"], a["mp"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(c=FAKE + 8), mla.MLA_ERR_INVALID_ARG),
+    (dict(B=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(dtype=9), mla.MLA_ERR_INVALID_ARG),
+    (dict(r=4), mla.MLA_ERR_UNSUPPORTED),          # 8-byte rows: not whole 16-byte chunks
+    (dict(npg=1 << 31), mla.MLA_ERR_UNSUPPORTED),
+])
+def test_cache_append_rejects(kw, status):
+    assert _append(**kw) == status
