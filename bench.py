@@ -12,10 +12,10 @@ algorithmic FLOPs), chunked-prefill TFLOP/s, decode latent-cache GB/s
 (algorithmic bytes), the roofline object of each against MI355X's published
 peaks, and the CPU oracle timed on a bounded row sample of the prefill.  The
 full-layer forward (projections, norms, core, output projection at the full
-K3 widths, B=1, T=8192) and the decode over a paged cache (the decode
-workload in shuffled 64-row pages) are timed separately after the steps and
-reported under "forward" and "decode_paged"; they are not part of
-ms_per_step.
+K3 widths, B=1, T=8192) is timed separately after the steps and reported
+under "forward".  The decode over a paged cache (the decode workload in
+shuffled 64-row pages) runs in each step right after the packed decode and
+is reported under "decode_paged".  Neither is part of ms_per_step.
 """
 from __future__ import annotations
 
@@ -181,8 +181,11 @@ def bench_forward(torch, mla, steps, warmup):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flop_per_launch": f}}
 
 
-def bench_decode_paged(torch, mla, dec, steps, warmup, page_size=64):
-    """The full decode workload with its cache in shuffled 64-row pages."""
+def setup_decode_paged(torch, mla, dec, page_size=64):
+    """The full decode workload with its cache in shuffled 64-row pages.
+    Returns (launch, report): launch() enqueues one call; report(ms) builds
+    the JSON object.  The calls run inside the timed steps, right after the
+    packed decode, so both see the same clock state."""
     lay = dg.paged_layout(dec["lengths"], page_size, seed=dec["seed"])
     pool = dg.scatter_to_pages(dec["c_cache"], dec["cu_seqlens"], lay)
     args = [dev(dec["q"]), dev(pool), dev(lay["block_table"]), dev(dec["lengths"].astype(np.int32)),
@@ -191,22 +194,18 @@ def bench_decode_paged(torch, mla, dec, steps, warmup, page_size=64):
     out = torch.empty((B, H * dv), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(mla.decode_paged_workspace_size(B, H, dq, r, 0, mla.DTYPE_BF16), dtype=torch.uint8,
                      device="cuda")
-    for _ in range(warmup):
-        mla.mla_absorb_decode_paged(*args, dec["scale"], out=out, workspace=ws)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for a, b in ev:
-        a.record()
-        mla.mla_absorb_decode_paged(*args, dec["scale"], out=out, workspace=ws)
-        b.record()
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     nbytes = decode_bytes(dec["lengths"], H, dq, dv, r) + 4 * B * lay["max_pages"]
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
-            "workload": f"full_decode with the cache in {lay['num_pages']} shuffled pages of {page_size} rows",
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "bytes_per_launch": nbytes}}
+
+    def launch():
+        mla.mla_absorb_decode_paged(*args, dec["scale"], out=out, workspace=ws)
+
+    def report(ms):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
+                "workload": f"full_decode with the cache in {lay['num_pages']} shuffled pages of {page_size} rows",
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "bytes_per_launch": nbytes}}
+    return launch, report
 
 
 def main():
@@ -260,6 +259,8 @@ def main():
     do_pre = args.which in ("both", "prefill")
     do_dec = args.which in ("both", "decode")
 
+    paged = setup_decode_paged(torch, mla, dec) if do_dec else None
+
     def step(ev):
         if do_pre:
             ev[0].record()
@@ -273,9 +274,12 @@ def main():
             ev[2].record()
             mla.mla_absorb_decode(*D, dec["scale"], out=d_out, workspace=d_ws)
             ev[3].record()
+            ev[6].record()
+            paged[0]()
+            ev[7].record()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    warm = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
     for _ in range(args.warmup):
         step(warm)
     torch.cuda.synchronize()
@@ -345,8 +349,8 @@ def main():
                          "roofline": {"bound": "mfma", "achieved": round(x_tf, 2), "peak": PEAK_BF16_TFLOPS,
                                       "unit": "TFLOP/s", "frac": round(x_tf / PEAK_BF16_TFLOPS, 4),
                                       "traffic": None, "flop_per_launch": xf}}
-    if args.which in ("both", "decode"):
-        res["decode_paged"] = bench_decode_paged(torch, mla, dec, args.steps, args.warmup)
+    if do_dec:
+        res["decode_paged"] = paged[1](float(np.mean([e[6].elapsed_time(e[7]) for e in evs])))
     if args.which in ("both", "forward"):
         res["forward"] = bench_forward(torch, mla, args.steps, args.warmup)
     if not args.no_cpu_baseline and do_pre:

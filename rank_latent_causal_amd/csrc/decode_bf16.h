@@ -500,16 +500,25 @@ mla_decode_split_paged(DecodePagedArgs a) {
   copier.init(w, lane);
   // The copy cursor runs NS - 1 tiles ahead of the compute cursor and keeps
   // its own sequence bookkeeping (scalar registers).
-  int pi = i, p_t0 = seq_t0, p_t1 = seq_t1;
+  // The page index is looked up once per page and the length once per
+  // sequence; every lookup is a scalar load that waits for itself.
+  int pi = i, p_t0 = seq_t0, p_t1 = seq_t1, p_len = len;
+  int p_page = -1, p_pg = 0;
   auto issue_tile = [&](int t, MLA_LDS char* stage) {
     while (t >= p_t1) {  // every sequence owns at least one tile
       ++pi;
       p_t0 = p_t1;
       p_t1 = sload_i32(a.cu_t + pi + 1);
+      p_len = sload_i32(a.lens + pi);
+      p_page = -1;
     }
     const int pos = (t - p_t0) * LT::KT;
-    int pg = sload_i32(a.block_table + (size_t)pi * a.max_pages + (pos >> a.page_shift));
-    int valid = min(sload_i32(a.lens + pi) - pos, LT::KT);
+    if ((pos >> a.page_shift) != p_page) {
+      p_page = pos >> a.page_shift;
+      p_pg = sload_i32(a.block_table + (size_t)pi * a.max_pages + p_page);
+    }
+    int pg = p_pg;
+    int valid = min(p_len - pos, LT::KT);
     if ((unsigned)pg >= (unsigned)a.num_pages) {
       pg = 0;
       valid = 0;
