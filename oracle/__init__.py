@@ -69,10 +69,11 @@ class Oracle:
         L.oracle_extend_paged.argtypes = [fp, fp, I64, I, i64p, I, fp, fp, fp, I, I, I, I, I, I, I, D, i64p, I64,
                                           dp, I]
         L.oracle_cache_append.argtypes = [fp, fp, I64, I, i64p, I, i64p, I, I]
+        L.oracle_prefill_backward.argtypes = [fp] * 6 + [I] * 6 + [D] + [dp] * 5 + [I]
         L.oracle_forward.argtypes = [fp] * 10 + [I] * 8 + [D, D, I, i64p, I64] + [dp] * 5 + [I]
         for f in ("oracle_prefill", "oracle_extend", "oracle_decode", "oracle_prefill_decompressed",
                   "oracle_prefill_attn", "oracle_round_bf16", "oracle_forward", "oracle_decode_paged",
-                  "oracle_extend_paged", "oracle_cache_append"):
+                  "oracle_extend_paged", "oracle_cache_append", "oracle_prefill_backward"):
             getattr(L, f).restype = I
 
     @property
@@ -236,6 +237,24 @@ class Oracle:
             _ptr(c_new, ct.c_float), _ptr(pages, ct.c_float), npg, ps, _ptr(bt, ct.c_int64), bt.shape[1],
             _ptr(pos, ct.c_int64), B, r), "oracle_cache_append")
         return pages
+
+    def prefill_backward(self, q, c, w_uk, w_uv, gate, dout, scale: float, threads: int = 0) -> dict:
+        """Gradients of the prefill core given dout [B,T,H*dv]: dict with dq
+        [B,T,H,dq], dc [B,T,r], dw_uk [H,dq,r], dw_uv [H,dv,r], dgate
+        [B,T,H*dv] (float64)."""
+        q, c, w_uk, w_uv, gate, dout = map(_f32, (q, c, w_uk, w_uv, gate, dout))
+        B, T, H, dq = q.shape
+        r = c.shape[-1]
+        dv = w_uv.shape[1]
+        assert c.shape == (B, T, r) and w_uk.shape == (H, dq, r) and w_uv.shape == (H, dv, r)
+        assert gate.shape == (B, T, H * dv) and dout.shape == gate.shape
+        g = dict(dq=np.empty((B, T, H, dq)), dc=np.empty((B, T, r)), dw_uk=np.empty((H, dq, r)),
+                 dw_uv=np.empty((H, dv, r)), dgate=np.empty((B, T, H * dv)))
+        self._check(self.lib.oracle_prefill_backward(
+            *[_ptr(a, ct.c_float) for a in (q, c, w_uk, w_uv, gate, dout)], B, T, H, dq, dv, r, float(scale),
+            *[_ptr(g[k], ct.c_double) for k in ("dq", "dc", "dw_uk", "dw_uv", "dgate")], threads),
+            "oracle_prefill_backward")
+        return g
 
     def round_bf16(self, v) -> np.ndarray:
         """Nearest bf16 value of each element (ties to even), as float64."""

@@ -421,31 +421,45 @@ static int gather_rows(const float* pages, int64_t num_pages, int page_size, con
   return ORACLE_OK;
 }
 
-/* Decode against a paged cache: sequence i holds seq_lens[i] rows (>= 1). */
+/* Decode against a paged cache: sequence i holds seq_lens[i] rows (>= 1).
+ * Only the selected sequences (seqs, or all) are gathered. */
 int oracle_decode_paged(const float* q, const float* pages, int64_t num_pages, int page_size,
                         const int64_t* block_table, int max_pages, const int64_t* seq_lens, const float* w_uk,
                         const float* w_uv, const float* gate, int B, int H, int dq, int dv, int r, double scale,
                         const int64_t* seqs, int64_t nseqs, double* out, int nthreads) {
-  if (!pages || !block_table || !seq_lens || B <= 0 || page_size <= 0 || max_pages <= 0 || r <= 0)
+  if (!q || !pages || !block_table || !seq_lens || !gate || B <= 0 || H <= 0 || dq <= 0 || dv <= 0 ||
+      page_size <= 0 || max_pages <= 0 || r <= 0 || nseqs < 0 || (!seqs && nseqs != B))
     return ORACLE_EINVAL;
-  int64_t* cu = (int64_t*)malloc(sizeof(int64_t) * (size_t)(B + 1));
-  if (!cu) return ORACLE_ENOMEM;
-  cu[0] = 0;
-  for (int i = 0; i < B; ++i) {
-    if (seq_lens[i] < 1 || seq_lens[i] > (int64_t)max_pages * page_size) {
-      free(cu);
-      return ORACLE_EINVAL;
-    }
-    cu[i + 1] = cu[i] + seq_lens[i];
+  for (int i = 0; i < B; ++i)
+    if (seq_lens[i] < 1 || seq_lens[i] > (int64_t)max_pages * page_size) return ORACLE_EINVAL;
+  if (seqs)
+    for (int64_t k = 0; k < nseqs; ++k)
+      if (seqs[k] < 0 || seqs[k] >= B) return ORACLE_EINVAL;
+  if (nseqs == 0) return ORACLE_OK;
+  int64_t* cu = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nseqs + 1));
+  float* qs = (float*)malloc(sizeof(float) * (size_t)nseqs * H * dq);
+  float* gs = (float*)malloc(sizeof(float) * (size_t)nseqs * H * dv);
+  int err = (cu && qs && gs) ? ORACLE_OK : ORACLE_ENOMEM;
+  float* packed = NULL;
+  if (err == ORACLE_OK) {
+    cu[0] = 0;
+    for (int64_t k = 0; k < nseqs; ++k) cu[k + 1] = cu[k] + seq_lens[seqs ? seqs[k] : k];
+    packed = (float*)malloc(sizeof(float) * (size_t)cu[nseqs] * r);
+    if (!packed) err = ORACLE_ENOMEM;
   }
-  float* packed = (float*)malloc(sizeof(float) * (size_t)cu[B] * r);
-  int err = packed ? ORACLE_OK : ORACLE_ENOMEM;
-  for (int i = 0; i < B && err == ORACLE_OK; ++i)
-    err = gather_rows(pages, num_pages, page_size, block_table, max_pages, i, seq_lens[i], r, packed + cu[i] * r);
+  for (int64_t k = 0; k < nseqs && err == ORACLE_OK; ++k) {
+    const int64_t i = seqs ? seqs[k] : k;
+    memcpy(qs + k * H * dq, q + i * H * dq, sizeof(float) * (size_t)H * dq);
+    memcpy(gs + k * H * dv, gate + i * H * dv, sizeof(float) * (size_t)H * dv);
+    err = gather_rows(pages, num_pages, page_size, block_table, max_pages, i, seq_lens[i], r, packed + cu[k] * r);
+  }
   if (err == ORACLE_OK)
-    err = oracle_decode(q, packed, cu, w_uk, w_uv, gate, B, H, dq, dv, r, scale, seqs, nseqs, out, nthreads);
+    err = oracle_decode(qs, packed, cu, w_uk, w_uv, gs, (int)nseqs, H, dq, dv, r, scale, NULL, nseqs, out,
+                        nthreads);
   free(packed);
   free(cu);
+  free(qs);
+  free(gs);
   return err;
 }
 
@@ -713,5 +727,172 @@ done:
   free(cf);
   free(qf);
   free(gf);
+  return err;
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward of the absorbed core (prefill).  The pages train the model with a
+ * cross-entropy loss and backpropagation ([MLA] describes only the forward);
+ * the gradients below are the chain rule applied to steps 1-6 above, for
+ * every batch b and head h (a_t = q_t W_UK[h] is the absorbed query, S the
+ * scaled scores, P the causal softmax, ol_t the latent output, o_t = W_UV[h]
+ * ol_t and out_t = sigmoid(g_t) o_t), given dout = dLoss/dout:
+ *
+ *   dg_t    = dout_t * o_t * s (1 - s),  s = sigmoid(g_t)
+ *   do_t    = dout_t * s
+ *   dW_UV  += do_t ol_t^T
+ *   dol_t   = W_UV^T do_t
+ *   dP_ts   = dol_t . c_s                         (s <= t)
+ *   dS_ts   = P_ts (dP_ts - sum_u P_tu dP_tu)
+ *   da_t    = scale sum_s dS_ts c_s
+ *   dc_s   += scale dS_ts a_t + P_ts dol_t        (c is both key and value)
+ *   dq_t    = W_UK da_t
+ *   dW_UK  += q_t da_t^T
+ *
+ * Weight gradients and dc sum over batches and heads.  Everything is
+ * float64; outputs: dq [B,T,H,dq], dc [B,T,r], dw_uk [H,dq,r], dw_uv [H,dv,r],
+ * dgate [B,T,H*dv].
+ */
+int oracle_prefill_backward(const float* q, const float* c, const float* w_uk, const float* w_uv,
+                            const float* gate, const float* dout, int B, int T, int H, int dq, int dv, int r,
+                            double scale, double* dq_out, double* dc_out, double* dwuk_out, double* dwuv_out,
+                            double* dgate_out, int nthreads) {
+  if (!q || !c || !w_uk || !w_uv || !gate || !dout || !dq_out || !dc_out || !dwuk_out || !dwuv_out || !dgate_out)
+    return ORACLE_EINVAL;
+  if (B <= 0 || T <= 0 || H <= 0 || dq <= 0 || dv <= 0 || r <= 0) return ORACLE_EINVAL;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  const int64_t ndc = (int64_t)B * T * r, nwk = (int64_t)H * dq * r, nwv = (int64_t)H * dv * r;
+  memset(dc_out, 0, sizeof(double) * (size_t)ndc);
+  memset(dwuk_out, 0, sizeof(double) * (size_t)nwk);
+  memset(dwuv_out, 0, sizeof(double) * (size_t)nwv);
+  int err = ORACLE_OK;
+#pragma omp parallel num_threads(nthreads)
+  {
+    /* private accumulators for the sums over (b, h) */
+    double* dc_p = (double*)calloc((size_t)ndc, sizeof(double));
+    double* wk_p = (double*)calloc((size_t)nwk, sizeof(double));
+    double* wv_p = (double*)calloc((size_t)nwv, sizeof(double));
+    double* a = (double*)malloc(sizeof(double) * (size_t)T * r);
+    double* P = (double*)malloc(sizeof(double) * (size_t)T);
+    double* dS = (double*)malloc(sizeof(double) * (size_t)T);
+    double* ol = (double*)malloc(sizeof(double) * (size_t)r);
+    double* dol = (double*)malloc(sizeof(double) * (size_t)r);
+    double* da = (double*)malloc(sizeof(double) * (size_t)r);
+    double* dov = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!dc_p || !wk_p || !wv_p || !a || !P || !dS || !ol || !dol || !da || !dov) {
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+    }
+#pragma omp barrier
+    if (err == ORACLE_OK) {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        const int64_t b = bh / H, h = bh % H;
+        const float* wk = w_uk + h * (int64_t)dq * r;
+        const float* wv = w_uv + h * (int64_t)dv * r;
+        const float* cb = c + b * (int64_t)T * r;
+        for (int t = 0; t < T; ++t)
+          absorb_row(q + ((b * T + t) * H + h) * dq, wk, dq, r, a + (int64_t)t * r);
+        for (int t = 0; t < T; ++t) {
+          const double* at = a + (int64_t)t * r;
+          const int64_t row = b * T + t;
+          /* forward quantities of row t */
+          double m = -INFINITY;
+          for (int s = 0; s <= t; ++s) {
+            double acc = 0.0;
+            for (int j = 0; j < r; ++j) acc += at[j] * (double)cb[(int64_t)s * r + j];
+            P[s] = scale * acc;
+            m = P[s] > m ? P[s] : m;
+          }
+          double z = 0.0;
+          for (int s = 0; s <= t; ++s) {
+            P[s] = exp(P[s] - m);
+            z += P[s];
+          }
+          for (int s = 0; s <= t; ++s) P[s] /= z;
+          for (int j = 0; j < r; ++j) ol[j] = 0.0;
+          for (int s = 0; s <= t; ++s)
+            for (int j = 0; j < r; ++j) ol[j] += P[s] * (double)cb[(int64_t)s * r + j];
+          /* gate, output and W_UV */
+          for (int v = 0; v < dv; ++v) {
+            double o = 0.0;
+            for (int j = 0; j < r; ++j) o += (double)wv[(int64_t)v * r + j] * ol[j];
+            const int64_t col = row * H * dv + h * dv + v;
+            const double sg = 1.0 / (1.0 + exp(-(double)gate[col]));
+            const double g = (double)dout[col];
+#if ORACLE_MUTANT == 24
+            dgate_out[col] = g * o * sg; /* planted mistake: sigmoid instead of its derivative */
+#else
+            dgate_out[col] = g * o * sg * (1.0 - sg);
+#endif
+            dov[v] = g * sg;
+            for (int j = 0; j < r; ++j) wv_p[(h * dv + v) * (int64_t)r + j] += dov[v] * ol[j];
+          }
+          for (int j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int v = 0; v < dv; ++v) acc += (double)wv[(int64_t)v * r + j] * dov[v];
+            dol[j] = acc;
+          }
+          /* softmax backward */
+          double D = 0.0;
+          for (int s = 0; s <= t; ++s) {
+            double acc = 0.0;
+            for (int j = 0; j < r; ++j) acc += dol[j] * (double)cb[(int64_t)s * r + j];
+            dS[s] = acc; /* dP for now */
+            D += P[s] * acc;
+          }
+          for (int s = 0; s <= t; ++s) {
+#if ORACLE_MUTANT == 22
+            dS[s] = P[s] * dS[s]; /* planted mistake: the row term of the softmax Jacobian dropped */
+#else
+            dS[s] = P[s] * (dS[s] - D);
+#endif
+          }
+          /* query side */
+          for (int j = 0; j < r; ++j) da[j] = 0.0;
+          for (int s = 0; s <= t; ++s)
+            for (int j = 0; j < r; ++j) da[j] += dS[s] * (double)cb[(int64_t)s * r + j];
+#if ORACLE_MUTANT != 25
+          for (int j = 0; j < r; ++j) da[j] *= scale;
+#endif
+          /* (mutant 25 plants a missing scale on the query-side gradient) */
+          for (int d = 0; d < dq; ++d) {
+            double acc = 0.0;
+            for (int j = 0; j < r; ++j) acc += (double)wk[(int64_t)d * r + j] * da[j];
+            dq_out[((b * T + t) * H + h) * dq + d] = acc;
+            const double qd = (double)q[((b * T + t) * H + h) * dq + d];
+            for (int j = 0; j < r; ++j) wk_p[(h * dq + d) * (int64_t)r + j] += qd * da[j];
+          }
+          /* key and value side: c enters as both */
+          for (int s = 0; s <= t; ++s) {
+            double* dcs = dc_p + (b * T + s) * (int64_t)r;
+            for (int j = 0; j < r; ++j) {
+#if ORACLE_MUTANT == 23
+              dcs[j] += scale * dS[s] * at[j]; /* planted mistake: the value path of c dropped */
+#else
+              dcs[j] += scale * dS[s] * at[j] + P[s] * dol[j];
+#endif
+            }
+          }
+        }
+      }
+#pragma omp critical
+      {
+        for (int64_t i = 0; i < ndc; ++i) dc_out[i] += dc_p[i];
+        for (int64_t i = 0; i < nwk; ++i) dwuk_out[i] += wk_p[i];
+        for (int64_t i = 0; i < nwv; ++i) dwuv_out[i] += wv_p[i];
+      }
+    }
+    free(dc_p);
+    free(wk_p);
+    free(wv_p);
+    free(a);
+    free(P);
+    free(dS);
+    free(ol);
+    free(dol);
+    free(da);
+    free(dov);
+  }
   return err;
 }

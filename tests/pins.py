@@ -514,6 +514,58 @@ def pin_cache_append_then_decode(o):
     _close(got, ref, 0.0, 0.0, "append then paged decode")
 
 
+# ---------------------------------------------------------------- backward
+def pin_backward_finite_differences(o):
+    """Every element of every gradient of the core against a central finite
+    difference of the loss sum(dout * out), the forward evaluated by the
+    independent float64 brute force above (dense_forward): calculus, not
+    the oracle's own arithmetic.  Two tiny shapes, scales 0.7 and 1.6."""
+    for (B, T, H, dq, dv, r, scale, seed) in [(2, 5, 2, 3, 2, 4, 0.7, 111), (1, 4, 3, 2, 3, 5, 1.6, 112)]:
+        d = dg.prefill_inputs(B, T, H, dq, dv, r, dtype=dg.F32, seed=seed)
+        args = {k: _f(d, k).astype(np.float64) for k in ("q", "c", "w_uk", "w_uv", "gate")}
+        dout = np.random.default_rng(seed).standard_normal((B, T, H * dv))
+        g = o.prefill_backward(*[args[k] for k in ("q", "c", "w_uk", "w_uv", "gate")],
+                               dout.astype(np.float32), scale)
+        dout64 = dout.astype(np.float32).astype(np.float64)
+
+        def loss(a):
+            return float(np.sum(dout64 * dense_forward(a["q"], a["c"], a["w_uk"], a["w_uv"], a["gate"], scale)))
+
+        eps = 1e-6
+        for key, gk in (("q", "dq"), ("c", "dc"), ("w_uk", "dw_uk"), ("w_uv", "dw_uv"), ("gate", "dgate")):
+            x = args[key]
+            fd = np.empty(x.size)
+            for i in range(x.size):
+                orig = x.flat[i]
+                x.flat[i] = orig + eps
+                lp = loss(args)
+                x.flat[i] = orig - eps
+                lm = loss(args)
+                x.flat[i] = orig
+                fd[i] = (lp - lm) / (2 * eps)
+            got = g[gk].reshape(-1)
+            _close(got, fd, 1e-6, 1e-8, f"d{key} vs finite differences (B{B} T{T} H{H})")
+
+
+def pin_backward_special_cases(o):
+    """Closed forms: with scale 0 the scores carry no gradient, so dq and
+    dW_UK vanish exactly; at T = 1 the softmax is the constant 1, so
+    dc_0 = sum_h W_UV[h]^T (dout_h * sigmoid(g_h)) and dq vanishes."""
+    B, T, H, dq, dv, r = 2, 6, 3, 4, 2, 5
+    d = dg.prefill_inputs(B, T, H, dq, dv, r, dtype=dg.F32, seed=113)
+    dout = np.random.default_rng(113).standard_normal((B, T, H * dv)).astype(np.float32)
+    g = o.prefill_backward(*_args(d), dout, 0.0)
+    assert np.all(g["dq"] == 0.0) and np.all(g["dw_uk"] == 0.0), "scale 0: query gradients must vanish"
+    d1 = dg.prefill_inputs(B, 1, H, dq, dv, r, dtype=dg.F32, seed=114)
+    dout1 = np.random.default_rng(114).standard_normal((B, 1, H * dv)).astype(np.float32)
+    g1 = o.prefill_backward(*_args(d1), dout1, 0.9)
+    wv = _f(d1, "w_uv").astype(np.float64)
+    s = _sigmoid(_f(d1, "gate").astype(np.float64)).reshape(B, H, dv)
+    want = np.einsum("hvj,bhv->bj", wv, dout1.astype(np.float64).reshape(B, H, dv) * s)
+    _close(g1["dc"][:, 0], want, 1e-12, 1e-14, "T=1 dc closed form")
+    _close(g1["dq"], np.zeros_like(g1["dq"]), 0.0, 1e-14, "T=1 dq")
+
+
 ALL_PINS = [
     pin_absorbed_equals_decompressed,
     pin_attention_rows,
@@ -536,4 +588,6 @@ ALL_PINS = [
     pin_paged_decode_matches_packed,
     pin_paged_extend_matches_packed,
     pin_cache_append_then_decode,
+    pin_backward_finite_differences,
+    pin_backward_special_cases,
 ]

@@ -31,6 +31,10 @@ MUTANTS = {
     19: "bf16 rounding ties away from zero",
     20: "paged cache: wrong block-table row stride",
     21: "paged cache: slot within the page off by one",
+    22: "backward: softmax Jacobian row term dropped",
+    23: "backward: value path of c dropped from dc",
+    24: "backward: gate gradient uses the sigmoid, not its derivative",
+    25: "backward: query-side gradient missing the softmax scale",
 }
 
 
