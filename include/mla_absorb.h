@@ -191,6 +191,41 @@ mla_status mla_cache_append_paged(const void* c_new, void* c_pages, const int32_
                                   int max_pages, mla_dtype dtype, void* stream);
 
 /*
+ * Training forward: mla_absorb_prefill that also writes, for the backward,
+ *   lse [B, H, T] float32   log sum_{s<=t} exp(scale * q_abs[b,t,h,:] . c[b,s,:])
+ * (natural log; the normaliser of the causal softmax).  bf16 only.  Other
+ * arguments, workspace and errors as for mla_absorb_prefill.
+ */
+mla_status mla_absorb_prefill_train(const void* q, const void* c, const void* w_uk, const void* w_uv,
+                                    const void* gate, void* out, float* lse, int B, int T, int H, int d_q, int d_v,
+                                    int r, float scale, mla_dtype dtype, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* Bytes of workspace mla_absorb_prefill_backward needs ((size_t)-1: invalid). */
+size_t mla_absorb_prefill_backward_workspace_size(int B, int T, int H, int d_q, int d_v, int r, mla_dtype dtype);
+
+/*
+ * Backward of the prefill core.  The pages train the layer with a
+ * cross-entropy loss; these are the gradients of the forward above (chain
+ * rule through absorb, latent score, causal softmax, latent sum, W_UV and the
+ * sigmoid gate) given dout = dLoss/dout.  c is both the key and the value of
+ * the latent attention, so dc carries both paths, summed over heads.
+ *   inputs:  q, c, w_uk, w_uv, gate as for the forward; out [B, T, H*d_v] and
+ *            lse [B, H, T] from mla_absorb_prefill_train; dout [B, T, H*d_v]
+ *   outputs: dq [B, T, H, d_q], dc [B, T, r], dgate [B, T, H*d_v] (bf16) and
+ *            dw_uk [H, d_q, r], dw_uv [H, d_v, r] (float32, overwritten)
+ * bf16 only, (d_q, d_v, r) in the compiled set; the head-major intermediates
+ * must stay below 2 GB each (H * B * T * r * 2 bytes), else
+ * MLA_ERR_UNSUPPORTED.  Workspace: mla_absorb_prefill_backward_workspace_size
+ * bytes (about 4 * H * B * T * r * 2 bytes).  Other conventions as above.
+ */
+mla_status mla_absorb_prefill_backward(const void* q, const void* c, const void* w_uk, const void* w_uv,
+                                       const void* gate, const void* out, const float* lse, const void* dout,
+                                       void* dq, void* dc, float* dw_uk, float* dw_uv, void* dgate, int B, int T,
+                                       int H, int d_q, int d_v, int r, float scale, mla_dtype dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of workspace mla_gated_forward needs (bf16 only; (size_t)-1 for
  * invalid sizes or dtypes).
  */

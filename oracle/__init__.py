@@ -70,10 +70,12 @@ class Oracle:
                                           dp, I]
         L.oracle_cache_append.argtypes = [fp, fp, I64, I, i64p, I, i64p, I, I]
         L.oracle_prefill_backward.argtypes = [fp] * 6 + [I] * 6 + [D] + [dp] * 5 + [I]
+        L.oracle_prefill_lse.argtypes = [fp, fp, fp, I, I, I, I, I, D, dp, I]
         L.oracle_forward.argtypes = [fp] * 10 + [I] * 8 + [D, D, I, i64p, I64] + [dp] * 5 + [I]
         for f in ("oracle_prefill", "oracle_extend", "oracle_decode", "oracle_prefill_decompressed",
                   "oracle_prefill_attn", "oracle_round_bf16", "oracle_forward", "oracle_decode_paged",
-                  "oracle_extend_paged", "oracle_cache_append", "oracle_prefill_backward"):
+                  "oracle_extend_paged", "oracle_cache_append", "oracle_prefill_backward",
+                  "oracle_prefill_lse"):
             getattr(L, f).restype = I
 
     @property
@@ -255,6 +257,17 @@ class Oracle:
             *[_ptr(g[k], ct.c_double) for k in ("dq", "dc", "dw_uk", "dw_uv", "dgate")], threads),
             "oracle_prefill_backward")
         return g
+
+    def prefill_lse(self, q, c, w_uk, scale: float, threads: int = 0) -> np.ndarray:
+        """Natural-log log-sum-exp of each causal score row, [B, H, T]."""
+        q, c, w_uk = map(_f32, (q, c, w_uk))
+        B, T, H, dq = q.shape
+        r = c.shape[-1]
+        out = np.empty((B, H, T), dtype=np.float64)
+        self._check(self.lib.oracle_prefill_lse(_ptr(q, ct.c_float), _ptr(c, ct.c_float), _ptr(w_uk, ct.c_float),
+                                                B, T, H, dq, r, float(scale), _ptr(out, ct.c_double), threads),
+                    "oracle_prefill_lse")
+        return out
 
     def round_bf16(self, v) -> np.ndarray:
         """Nearest bf16 value of each element (ties to even), as float64."""

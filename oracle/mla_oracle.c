@@ -896,3 +896,45 @@ int oracle_prefill_backward(const float* q, const float* c, const float* w_uk, c
   }
   return err;
 }
+
+/* Log-sum-exp of each causal score row, natural log: lse[b,h,t] =
+ * log sum_{s<=t} exp(scale * a_t . c_s) with a_t = q_t W_UK[h], the
+ * normaliser of step 3's softmax (what a training forward keeps for its
+ * backward).  Max-subtracted, float64. */
+int oracle_prefill_lse(const float* q, const float* c, const float* w_uk, int B, int T, int H, int dq, int r,
+                       double scale, double* lse, int nthreads) {
+  if (!q || !c || !w_uk || !lse || B <= 0 || T <= 0 || H <= 0 || dq <= 0 || r <= 0) return ORACLE_EINVAL;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  int err = ORACLE_OK;
+#pragma omp parallel num_threads(nthreads)
+  {
+    double* qa = (double*)malloc(sizeof(double) * (size_t)r);
+    double* s = (double*)malloc(sizeof(double) * (size_t)T);
+    if (!qa || !s) {
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+    }
+#pragma omp barrier
+    if (err == ORACLE_OK) {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t bht = 0; bht < (int64_t)B * H * T; ++bht) {
+        const int64_t b = bht / ((int64_t)H * T), h = (bht / T) % H, t = bht % T;
+        absorb_row(q + ((b * T + t) * H + h) * dq, w_uk + h * (int64_t)dq * r, dq, r, qa);
+        double m = -INFINITY;
+        for (int64_t u = 0; u <= t; ++u) {
+          const float* cu = c + (b * T + u) * (int64_t)r;
+          double acc = 0.0;
+          for (int j = 0; j < r; ++j) acc += qa[j] * (double)cu[j];
+          s[u] = scale * acc;
+          m = s[u] > m ? s[u] : m;
+        }
+        double z = 0.0;
+        for (int64_t u = 0; u <= t; ++u) z += exp(s[u] - m);
+        lse[bht] = m + log(z);
+      }
+    }
+    free(qa);
+    free(s);
+  }
+  return err;
+}

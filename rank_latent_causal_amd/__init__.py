@@ -18,7 +18,8 @@ __all__ = [
     "MLA_ERR_HIP", "DTYPE_F32", "DTYPE_BF16", "MLAError", "lib", "status_string",
     "prefill_workspace_size", "decode_workspace_size", "decode_paged_workspace_size", "forward_workspace_size",
     "mla_absorb_prefill", "mla_absorb_extend", "mla_absorb_extend_paged", "mla_absorb_decode",
-    "mla_absorb_decode_paged", "mla_cache_append_paged", "mla_gated_forward",
+    "mla_absorb_decode_paged", "mla_cache_append_paged", "mla_gated_forward", "mla_absorb_prefill_train",
+    "backward_workspace_size", "mla_absorb_prefill_backward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_absorb.so")
@@ -37,6 +38,9 @@ EXPORTS = (
     "mla_absorb_decode_paged_workspace_size",
     "mla_absorb_decode_paged",
     "mla_cache_append_paged",
+    "mla_absorb_prefill_train",
+    "mla_absorb_prefill_backward_workspace_size",
+    "mla_absorb_prefill_backward",
     "mla_gated_forward_workspace_size",
     "mla_gated_forward",
 )
@@ -78,6 +82,12 @@ def lib() -> ct.CDLL:
         L.mla_absorb_decode_paged.restype = I
         L.mla_cache_append_paged.argtypes = [vp] * 4 + [I, I, I64, I, I, I, vp]
         L.mla_cache_append_paged.restype = I
+        L.mla_absorb_prefill_train.argtypes = [vp] * 7 + [I] * 6 + [F, I, vp, sz, vp]
+        L.mla_absorb_prefill_train.restype = I
+        L.mla_absorb_prefill_backward_workspace_size.argtypes = [I] * 7
+        L.mla_absorb_prefill_backward_workspace_size.restype = sz
+        L.mla_absorb_prefill_backward.argtypes = [vp] * 13 + [I] * 6 + [F, I, vp, sz, vp]
+        L.mla_absorb_prefill_backward.restype = I
         L.mla_gated_forward_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
         L.mla_gated_forward_workspace_size.restype = sz
         L.mla_gated_forward.argtypes = [vp] * 11 + [I] * 8 + [F, F, I, vp, sz, vp]
@@ -111,6 +121,13 @@ def decode_paged_workspace_size(B: int, H: int, d_q: int, r: int, num_splits: in
     n = lib().mla_absorb_decode_paged_workspace_size(B, H, d_q, r, num_splits, dtype)
     if n == _BAD:
         raise MLAError(MLA_ERR_INVALID_ARG, "mla_absorb_decode_paged_workspace_size")
+    return n
+
+
+def backward_workspace_size(B: int, T: int, H: int, d_q: int, d_v: int, r: int, dtype: int) -> int:
+    n = lib().mla_absorb_prefill_backward_workspace_size(B, T, H, d_q, d_v, r, dtype)
+    if n == _BAD:
+        raise MLAError(MLA_ERR_INVALID_ARG, "mla_absorb_prefill_backward_workspace_size")
     return n
 
 
@@ -316,6 +333,70 @@ def mla_cache_append_paged(c_new, c_pages, block_table, positions, stream=None):
     if st != MLA_OK:
         raise MLAError(st, "mla_cache_append_paged")
     return c_pages
+
+
+def mla_absorb_prefill_train(q, c, w_uk, w_uv, gate, scale: float, out=None, lse=None, workspace=None,
+                             stream=None):
+    """Prefill that also returns the log-sum-exp [B,H,T] (float32) the
+    backward needs.  Returns (out, lse)."""
+    torch = _torch()
+    B, T, H, dq = q.shape
+    r = c.shape[-1]
+    dv = w_uv.shape[1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    for t, shp, n in ((q, (B, T, H, dq), "q"), (c, (B, T, r), "c"), (w_uk, (H, dq, r), "w_uk"),
+                      (w_uv, (H, dv, r), "w_uv"), (gate, (B, T, H * dv), "gate")):
+        _check(t, shp, dt, n)
+    if out is None:
+        out = torch.empty((B, T, H * dv), dtype=dt, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    _check(out, (B, T, H * dv), dt, "out")
+    _check(lse, (B, H, T), torch.float32, "lse")
+    need = prefill_workspace_size(B, T, H, dq, r, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().mla_absorb_prefill_train(q.data_ptr(), c.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(), gate.data_ptr(),
+                                        out.data_ptr(), lse.data_ptr(), B, T, H, dq, dv, r, float(scale), code,
+                                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                        _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_absorb_prefill_train")
+    return out, lse
+
+
+def mla_absorb_prefill_backward(q, c, w_uk, w_uv, gate, out, lse, dout, scale: float, workspace=None, stream=None):
+    """Gradients of the prefill core given dout [B,T,H*d_v]: returns a dict
+    with dq [B,T,H,d_q], dc [B,T,r], dgate [B,T,H*d_v] (input dtype) and
+    dw_uk [H,d_q,r], dw_uv [H,d_v,r] (float32)."""
+    torch = _torch()
+    B, T, H, dq = q.shape
+    r = c.shape[-1]
+    dv = w_uv.shape[1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    for t, shp, n in ((q, (B, T, H, dq), "q"), (c, (B, T, r), "c"), (w_uk, (H, dq, r), "w_uk"),
+                      (w_uv, (H, dv, r), "w_uv"), (gate, (B, T, H * dv), "gate"), (out, (B, T, H * dv), "out"),
+                      (dout, (B, T, H * dv), "dout")):
+        _check(t, shp, dt, n)
+    _check(lse, (B, H, T), torch.float32, "lse")
+    g = dict(dq=torch.empty((B, T, H, dq), dtype=dt, device=q.device),
+             dc=torch.empty((B, T, r), dtype=dt, device=q.device),
+             dgate=torch.empty((B, T, H * dv), dtype=dt, device=q.device),
+             dw_uk=torch.empty((H, dq, r), dtype=torch.float32, device=q.device),
+             dw_uv=torch.empty((H, dv, r), dtype=torch.float32, device=q.device))
+    need = backward_workspace_size(B, T, H, dq, dv, r, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().mla_absorb_prefill_backward(
+        q.data_ptr(), c.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(), gate.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        dout.data_ptr(), g["dq"].data_ptr(), g["dc"].data_ptr(), g["dw_uk"].data_ptr(), g["dw_uv"].data_ptr(),
+        g["dgate"].data_ptr(), B, T, H, dq, dv, r, float(scale), code, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_absorb_prefill_backward")
+    return g
 
 
 def mla_gated_forward(x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o,

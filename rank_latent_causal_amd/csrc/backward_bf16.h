@@ -1,0 +1,419 @@
+// bf16 backward of the absorbed Gated MLA prefill core on gfx950.  The pages
+// train the layer with a cross-entropy loss; the gradients are the chain rule
+// through the forward of page "Gated MLA（矩阵吸收版）", section
+// 完整计算流（四步） (absorb, latent score, causal softmax, latent sum, W_UV,
+// sigmoid gate).  With a = q W_UK (absorbed query), P the causal softmax of
+// S = scale a c^T, ol = P c and o = ol W_UV^T, given dout:
+//
+//   dg = dout * out * (1 - sigmoid(g))          do = dout * sigmoid(g)
+//   dol = do W_UV                               D_t = sum_v dout out  (= dol . ol)
+//   dS = P (dol c^T - D)                        da = scale dS c
+//   dc = scale dS^T a + P^T dol                 dq = da W_UK^T
+//   dW_UK = sum_t q_t^T da_t                    dW_UV = sum_t do_t^T ol_t
+//
+// Kernels (in call order):
+//   mla_bwd_prep     dg, do and the per-row pair {lse log2 e, D}
+//   absorb (decode)  q_abs2 = scale log2e q W_UK and dol = do W_UV, head-major
+//   mla_bwd_query    per (32 queries, head): da and ol over the key tiles
+//   mla_bwd_key      per (32 keys, head group): partial dc over the query
+//                    blocks at or after the keys
+//   mla_bwd_dc_sum   dc = sum of the head-group partials
+//   GEMMs            dq = da W_UK^T (NT), dW_UK and dW_UV (TN)
+//
+// Head-major rows: q_abs2, dol, da and ol are [H, B*T, R], so the 32 rows of
+// one (head, block) are one contiguous 32-row tile, copied like a latent
+// tile.  The scores of the forward are recomputed from q_abs2 and c with the
+// forward's log-sum-exp, P = exp2(S2 - lse log2 e).
+#pragma once
+
+#include "attn_core.h"
+
+namespace mla {
+
+struct BwdArgs {
+  const bf16* c;      // [B, T, R]
+  const bf16* qabs;   // [H, B*T, R]  scale * log2(e) * q W_UK
+  const bf16* dolat;  // [H, B*T, R]  do W_UV
+  const float* ld;    // [H, B*T, 2]  {lse * log2(e), D}
+  bf16* da;           // [H, B*T, R]
+  bf16* ol;           // [H, B*T, R]
+  float* dc_part;     // [nhg, B*T, R]
+  int B, T, H;
+  float scale;
+  int ntb;            // ceil(T / 32)
+  int nhg, hpg;       // head groups of mla_bwd_key and heads per group
+};
+
+constexpr int kBwdWaves = 8;
+constexpr int kXPitch = 33;  // fp32 exchange rows (floats)
+constexpr int kPPitch = 40;  // bf16 P / dS rows (elements): 80-byte rows keep b128 reads aligned
+
+// Exchange buffers after the tile stages: S and dP (fp32 [32][33] each), P and
+// dS (bf16 [32][40] each).
+constexpr int kBwdXBytes = 2 * 32 * kXPitch * 4 + 2 * 32 * kPPitch * 2;
+
+// Transposed operand of a stored 32-row tile (rows = the reduction index):
+// lane l gets rows 8 (l/16) + 0..7 of column 16 jt + l % 16.
+template <int R>
+__device__ __forceinline__ bf16x8 tile_column_operand(const MLA_LDS char* tile, int jt, int l16, int kq) {
+  const int e = l16 >> 2, q = l16 & 3;
+  const int chunk = 2 * jt + (q >> 1), half = (q & 1) * 8;
+  const MLA_LDS char* p0 = tile + tile_off<R>(8 * kq + e, chunk) + half;
+  const MLA_LDS char* p1 = tile + tile_off<R>(8 * kq + 4 + e, chunk) + half;
+  return cat4(lds_read_tr16(p0), lds_read_tr16(p1));
+}
+
+// ----------------------------------------------------------------- prep
+struct BwdPrepArgs {
+  const bf16* gate;   // [B*T, H*DV]
+  const bf16* out;    // [B*T, H*DV]  forward output
+  const bf16* dout;   // [B*T, H*DV]
+  const float* lse;   // [B, H, T]    forward log-sum-exp (natural log)
+  bf16* dgate;        // [B*T, H*DV]
+  bf16* dov;          // [B*T, H, DV] do = dout * sigmoid(g)
+  float* ld;          // [H, B*T, 2]
+  int B, T, H, DV;
+};
+
+// One workgroup per token row; wave w takes heads w, w+4, ...; lanes walk the
+// DV values of a head.
+__global__ void __launch_bounds__(256) mla_bwd_prep(BwdPrepArgs a) {
+  const int bt = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = bt / a.T, t = bt % a.T;
+  const size_t row = (size_t)bt * a.H * a.DV;
+  for (int h = w; h < a.H; h += 4) {
+    float dsum = 0.0f;
+    for (int v = lane; v < a.DV; v += 64) {
+      const size_t i = row + (size_t)h * a.DV + v;
+      const float g = (float)a.gate[i], o = (float)a.out[i], d = (float)a.dout[i];
+      const float s = sigmoidf_(g);
+      a.dgate[i] = (bf16)(d * o * (1.0f - s));
+      a.dov[i] = (bf16)(d * s);
+      dsum += d * o;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, 64);
+    if (lane == 0) {
+      float* dst = a.ld + ((size_t)h * a.B * a.T + bt) * 2;
+      dst[0] = a.lse[((size_t)b * a.H + h) * a.T + t] * kLog2e;
+      dst[1] = dsum;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- query side
+// Workgroup (batch b, 32 queries t0.., head h), 8 waves, heaviest blocks
+// first.  Per key tile: waves 0-3 form the four 16x16 tiles of S2 = q_abs2
+// c^T and waves 4-7 those of dP = dol c^T (the query rows are MFMA A operands
+// held in VGPRs); every thread then turns two of the 32x32 elements into P and
+// dS (bf16 in LDS); wave w accumulates da^T and ol^T for latent tiles w,
+// w+8, ... with c^T from transposing reads.  Two LDS stages, one tile of
+// lookahead.
+template <int R>
+__global__ void __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mla_bwd_query(BwdArgs a) {
+  using LT = LatentTile<R>;
+  constexpr int NKK = R / 32, NJT = R / 16;
+  constexpr int JPW = (NJT + kBwdWaves - 1) / kBwdWaves;
+  static_assert(LT::COPIES % kBwdWaves == 0 || LT::COPIES < kBwdWaves, "copy split");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * LT::BYTES + kBwdXBytes];
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+  float* xS = (float*)(smem_raw + 2 * LT::BYTES);
+  float* xP = xS + 32 * kXPitch;
+  bf16* Pb = (bf16*)(xP + 32 * kXPitch);
+  bf16* dSb = Pb + 32 * kPPitch;
+
+  const int x = blockIdx.x;
+  const int h = x % a.H, rest = x / a.H;
+  const int b = rest % a.B, tb = a.ntb - 1 - rest / a.B;
+  const int T = a.T, t0 = tb * 32;
+  const int ntiles = (min(t0 + 32, T) + LT::KT - 1) / LT::KT;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int role = w >> 2, qt = (w >> 1) & 1, kt = w & 1;
+  const size_t hrow = (size_t)h * a.B * T + (size_t)b * T;  // head-major row of (b, t = 0)
+
+  // the A operand rows (query qt*16 + l16) of this wave's product
+  bf16x8 aop[NKK];
+  {
+    const int tq = min(t0 + 16 * qt + l16, T - 1);
+    const bf16* src = (role ? a.dolat : a.qabs) + (hrow + tq) * R + 8 * kq;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) aop[kk] = *(const bf16x8*)(src + 32 * kk);
+  }
+  // elementwise phase: thread -> query eq, keys ek, ek + 1 of the tile
+  const int eq = threadIdx.x >> 4, ek = 2 * (threadIdx.x & 15);
+  const int tq_e = t0 + eq;
+  float L2, Dq;
+  {
+    const float* p = a.ld + (hrow + min(tq_e, T - 1)) * 2;
+    L2 = p[0];
+    Dq = p[1];
+  }
+
+  f32x4 accd[JPW][2], acco[JPW][2];
+#pragma unroll
+  for (int j = 0; j < JPW; ++j)
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) accd[j][c2] = acco[j][c2] = f32x4{};
+
+  TileCopier<R, kBwdWaves> copier;
+  copier.init(w, lane);
+  const bf16* cb = a.c + (size_t)b * T * R;
+  copier.issue(cb, 0, T, smem);
+
+  for (int it = 0; it < ntiles; ++it) {
+    wait_vmcnt<0>();
+    wg_barrier();  // tile it visible; the previous tile's update is done everywhere
+    if (it + 1 < ntiles) copier.issue(cb, (it + 1) * LT::KT, T, smem + ((it + 1) & 1) * LT::BYTES);
+    const MLA_LDS char* tile = smem + (it & 1) * LT::BYTES;
+
+    // S2 or dP tile (qt, kt): rows query qt*16 + 4kq + i, column key kt*16 + l16
+    f32x4 sacc = f32x4{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const bf16x8 bk = lds_read_b128(tile + tile_off<R>(16 * kt + l16, 4 * kk + kq));
+      sacc = mfma16(aop[kk], bk, sacc);
+    }
+    {
+      float* xd = role ? xP : xS;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xd[(16 * qt + 4 * kq + i) * kXPitch + 16 * kt + l16] = sacc[i];
+    }
+    wait_lgkmcnt0();
+    wg_barrier();
+
+    {
+      const int s0 = it * LT::KT;
+      bf16 pv[2], dv2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int k = ek + u;
+        const float s2 = xS[eq * kXPitch + k], dp = xP[eq * kXPitch + k];
+        const float p = (s0 + k <= tq_e) ? fast_exp2(s2 - L2) : 0.0f;
+        pv[u] = (bf16)p;
+        dv2[u] = (bf16)(p * (dp - Dq));
+      }
+      Pb[eq * kPPitch + ek] = pv[0];
+      Pb[eq * kPPitch + ek + 1] = pv[1];
+      dSb[eq * kPPitch + ek] = dv2[0];
+      dSb[eq * kPPitch + ek + 1] = dv2[1];
+    }
+    wait_lgkmcnt0();
+    wg_barrier();
+
+    // da^T, ol^T += c^T [16 latent x 32 keys] x {dS, P}^T [32 keys x 16 queries]
+    bf16x8 bS[2], bP[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      bS[c2] = *(const bf16x8*)&dSb[(16 * c2 + l16) * kPPitch + 8 * kq];
+      bP[c2] = *(const bf16x8*)&Pb[(16 * c2 + l16) * kPPitch + 8 * kq];
+    }
+#pragma unroll
+    for (int j = 0; j < JPW; ++j) {
+      const int jt = w + kBwdWaves * j;
+      if (jt < NJT) {
+        const bf16x8 ac = tile_column_operand<R>(tile, jt, l16, kq);
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          accd[j][c2] = mfma16(ac, bS[c2], accd[j][c2]);
+          acco[j][c2] = mfma16(ac, bP[c2], acco[j][c2]);
+        }
+      }
+    }
+  }
+
+  // epilogue: fragment (j, c2) holds latent dims 16 jt + 4 kq + e of query 16 c2 + l16
+#pragma unroll
+  for (int j = 0; j < JPW; ++j) {
+    const int jt = w + kBwdWaves * j;
+    if (jt >= NJT) continue;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int tq = t0 + 16 * c2 + l16;
+      if (tq >= T) continue;
+      bf16x4 vd, vo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vd[e] = (bf16)(accd[j][c2][e] * a.scale);
+        vo[e] = (bf16)acco[j][c2][e];
+      }
+      const size_t off = (hrow + tq) * R + 16 * jt + 4 * kq;
+      *(bf16x4*)(a.da + off) = vd;
+      *(bf16x4*)(a.ol + off) = vo;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- key side
+// Workgroup (batch b, 32 keys k0.., head group hg), 8 waves, blocks with the
+// most query blocks first.  Steps run over (head h of the group, query block
+// qb >= the key block); a step stages the q_abs2 and dol tiles of (h, qb) and
+// their {lse log2 e, D} pairs in LDS (two stages, one step of lookahead).
+// Waves 0-3 form S2^T tiles and waves 4-7 dP^T tiles, with the key rows of c
+// as A operands held in VGPRs; every thread makes two elements of P and
+// dS ln 2 (key-major bf16 rows); wave w accumulates dc^T for latent tiles w,
+// w+8, ...:  dc^T += q_abs2^T dS^T + dol^T P^T  (q_abs2 carries
+// scale log2 e, so dS ln 2 gives the scale dS a term).
+template <int R>
+struct BwdKeyConfig {
+  static constexpr int LDB = 256;                                    // {L2, D} x 32 queries
+  static constexpr int STAGE = 2 * LatentTile<R>::BYTES + LDB;
+  static constexpr int LDS = 2 * STAGE + kBwdXBytes;
+};
+
+template <int R>
+__global__ void __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mla_bwd_key(BwdArgs a) {
+  using LT = LatentTile<R>;
+  using CFG = BwdKeyConfig<R>;
+  constexpr int NKK = R / 32, NJT = R / 16;
+  constexpr int JPW = (NJT + kBwdWaves - 1) / kBwdWaves;
+  constexpr int CPW = copies_per_wave<R>(kBwdWaves);
+  static_assert(LT::COPIES % kBwdWaves == 0 || LT::COPIES < kBwdWaves, "copy split");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS];
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+  float* xS = (float*)(smem_raw + 2 * CFG::STAGE);
+  float* xP = xS + 32 * kXPitch;
+  bf16* Pb = (bf16*)(xP + 32 * kXPitch);
+  bf16* dSb = Pb + 32 * kPPitch;
+
+  const int x = blockIdx.x;
+  const int hg = x % a.nhg, rest = x / a.nhg;
+  const int b = rest % a.B, kb = rest / a.B;
+  const int T = a.T, k0 = kb * 32;
+  const int h0 = hg * a.hpg, nh = min(a.hpg, a.H - h0);
+  const int nq = a.ntb - kb;
+  const int nsteps = nh * nq;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int role = w >> 2, kt = (w >> 1) & 1, qt = w & 1;
+  const size_t BT = (size_t)a.B * T;
+
+  // A operand: key rows kt*16 + l16 of c
+  bf16x8 aop[NKK];
+  {
+    const int tk = min(k0 + 16 * kt + l16, T - 1);
+    const bf16* src = a.c + ((size_t)b * T + tk) * R + 8 * kq;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) aop[kk] = *(const bf16x8*)(src + 32 * kk);
+  }
+  const int ek = threadIdx.x >> 4, eq = 2 * (threadIdx.x & 15);
+
+  f32x4 acc[JPW][2];
+#pragma unroll
+  for (int j = 0; j < JPW; ++j) acc[j][0] = acc[j][1] = f32x4{};
+
+  TileCopier<R, kBwdWaves> copier;
+  copier.init(w, lane);
+  auto stage = [&](int st) { return smem + st * CFG::STAGE; };
+  auto issue_step = [&](int s, MLA_LDS char* dst) {
+    const int h = h0 + s / nq, qb = kb + s % nq;
+    const size_t r0 = (size_t)h * BT + (size_t)b * T;  // row t = 0 of (h, b)
+    copier.issue(a.qabs + r0 * R, qb * 32, T, dst);
+    copier.issue(a.dolat + r0 * R, qb * 32, T, dst + LT::BYTES);
+    if (w == 0 && lane < 16) {
+      const int rows = min(32, T - qb * 32);
+      const u32x4 rs = make_rsrc(a.ld + (r0 + qb * 32) * 2, (unsigned)(rows * 8));
+      buf2lds16(rs, (unsigned)(lane * 16), dst + 2 * LT::BYTES);
+    }
+  };
+  (void)CPW;
+  if (nsteps > 0) issue_step(0, stage(0));
+
+  for (int s = 0; s < nsteps; ++s) {
+    wait_vmcnt<0>();
+    wg_barrier();  // step s staged; step s-1 done everywhere (its stage and the exchange are free)
+    if (s + 1 < nsteps) issue_step(s + 1, stage((s + 1) & 1));
+    const MLA_LDS char* tq_tile = stage(s & 1);
+    const MLA_LDS char* td_tile = tq_tile + LT::BYTES;
+    const float* ldst = (const float*)(smem_raw + (s & 1) * CFG::STAGE + 2 * LT::BYTES);
+    const int qb = kb + s % nq;
+
+    // S2^T or dP^T tile (kt, qt): rows key kt*16 + 4kq + i, column query qt*16 + l16
+    const MLA_LDS char* src = role ? td_tile : tq_tile;
+    f32x4 sacc = f32x4{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const bf16x8 bq = lds_read_b128(src + tile_off<R>(16 * qt + l16, 4 * kk + kq));
+      sacc = mfma16(aop[kk], bq, sacc);
+    }
+    {
+      float* xd = role ? xP : xS;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xd[(16 * kt + 4 * kq + i) * kXPitch + 16 * qt + l16] = sacc[i];
+    }
+    wait_lgkmcnt0();
+    wg_barrier();
+
+    {
+      const int kpos = k0 + ek;
+      bf16 pv[2], dv2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int q = eq + u, qpos = qb * 32 + q;
+        const float s2 = xS[ek * kXPitch + q], dp = xP[ek * kXPitch + q];
+        const float L2 = ldst[2 * q], Dq = ldst[2 * q + 1];
+        const float p = (kpos <= qpos && qpos < T) ? fast_exp2(s2 - L2) : 0.0f;
+        pv[u] = (bf16)p;
+        dv2[u] = (bf16)(p * (dp - Dq) * 0.69314718055994531f);
+      }
+      Pb[ek * kPPitch + eq] = pv[0];
+      Pb[ek * kPPitch + eq + 1] = pv[1];
+      dSb[ek * kPPitch + eq] = dv2[0];
+      dSb[ek * kPPitch + eq + 1] = dv2[1];
+    }
+    wait_lgkmcnt0();
+    wg_barrier();
+
+    bf16x8 bS[2], bP[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      bS[c2] = *(const bf16x8*)&dSb[(16 * c2 + l16) * kPPitch + 8 * kq];
+      bP[c2] = *(const bf16x8*)&Pb[(16 * c2 + l16) * kPPitch + 8 * kq];
+    }
+#pragma unroll
+    for (int j = 0; j < JPW; ++j) {
+      const int jt = w + kBwdWaves * j;
+      if (jt < NJT) {
+        const bf16x8 aq = tile_column_operand<R>(tq_tile, jt, l16, kq);
+        const bf16x8 ad = tile_column_operand<R>(td_tile, jt, l16, kq);
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          acc[j][c2] = mfma16(aq, bS[c2], acc[j][c2]);
+          acc[j][c2] = mfma16(ad, bP[c2], acc[j][c2]);
+        }
+      }
+    }
+  }
+
+  // epilogue: fragment (j, c2) holds latent dims 16 jt + 4 kq + e of key 16 c2 + l16
+#pragma unroll
+  for (int j = 0; j < JPW; ++j) {
+    const int jt = w + kBwdWaves * j;
+    if (jt >= NJT) continue;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int tk = k0 + 16 * c2 + l16;
+      if (tk >= T) continue;
+      *(f32x4*)(a.dc_part + ((size_t)hg * BT + (size_t)b * T + tk) * R + 16 * jt + 4 * kq) = acc[j][c2];
+    }
+  }
+}
+
+// dc[row, :] = sum over head groups of the partials (bf16 out); one thread
+// per 4 latent values.
+__global__ void __launch_bounds__(256) mla_bwd_dc_sum(const float* __restrict__ part, bf16* __restrict__ dc,
+                                                      long long rows, int R, int nhg) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // index of 4 values
+  const long long n4 = rows * R / 4;
+  if (i >= n4) return;
+  f32x4 s = f32x4{};
+  for (int g = 0; g < nhg; ++g) s += *(const f32x4*)(part + ((long long)g * rows * R) + 4 * i);
+  bf16x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = (bf16)s[e];
+  *(bf16x4*)(dc + 4 * i) = v;
+}
+
+}  // namespace mla

@@ -55,9 +55,10 @@ __global__ void __launch_bounds__(256) mla_wuk_transpose(const T* __restrict__ w
 struct DecodeAbsorbArgs {
   const bf16* q;    // [B, H, DQ]
   const bf16* wuk;  // [H, DQ, R]
-  bf16* qabs;       // [B, H, R]
+  bf16* qabs;       // [B, H, R], or [H, B, R] with head_major
   int B, H;
   float qscale;
+  int head_major;
 };
 
 // Workgroup (head h, latent columns [J0, J0 + JC)), 4 waves; wave w owns the
@@ -107,7 +108,8 @@ __global__ void __launch_bounds__(256) mla_decode_absorb(DecodeAbsorbArgs a) {
       bf16x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[e] * a.qscale);
-      *(bf16x4*)(a.qabs + ((size_t)i * a.H + h) * R + J0 + 16 * w + 4 * kq) = v;
+      const size_t row = a.head_major ? (size_t)h * a.B + i : (size_t)i * a.H + h;
+      *(bf16x4*)(a.qabs + row * R + J0 + 16 * w + 4 * kq) = v;
     }
   }
 }

@@ -6,7 +6,9 @@
 //   Y[m, n] = sum_k X[m, k] * W[n, k]        X [M, K], W [N, K], Y [M, N]
 //
 // (row-major, K contiguous in both operands, the weight laid out as
-// out_features x in_features), bf16 storage with fp32 accumulation.
+// out_features x in_features), bf16 storage with fp32 accumulation.  Rows
+// may be strided (lda, ldw, ldy) and blockIdx.y indexes a batch (per-head
+// products of the backward).
 //
 // Workgroup: 4 waves, a 128 (n) x 128 (m) tile of Y^T, 64-wide k tiles in
 // two LDS stages.  The MFMA computes Y^T = W X^T, so its A operand rows are
@@ -26,11 +28,13 @@
 namespace mla {
 
 struct GemmArgs {
-  const bf16* x;  // [M, K]
-  const bf16* w;  // [N, K]
-  bf16* y;        // [M, N]
-  int M, N, K;    // K % 64 == 0
+  const bf16* x;  // [M, K], rows lda apart
+  const bf16* w;  // [N, K], rows ldw apart
+  bf16* y;        // [M, N], rows ldy apart
+  int M, N, K;    // K % 8 == 0; a last partial k tile reads zeros past K
   int tiles_n;    // ceil(N / 128)
+  int lda, ldw, ldy;
+  long long bsx, bsw, bsy;  // element offsets between the batches of blockIdx.y
 };
 
 constexpr int kGemmTile = 128;
@@ -43,19 +47,21 @@ __device__ __forceinline__ int gemm_chunk(int s, int c) { return c ^ ((s >> 1) &
 // operand into a swizzled LDS tile.  Copy i (1 KiB = 8 rows) is issued by
 // wave i % 4; lane l of a copy fills LDS bytes 16 l .. of it, which is row
 // 8 i + l / 8, physical chunk l % 8.
-__device__ __forceinline__ void gemm_copy(const bf16* __restrict__ base, int rows_total, int row0, int K,
-                                          int k0, MLA_LDS char* tile, int w) {
+__device__ __forceinline__ void gemm_copy(const bf16* __restrict__ base, int rows_total, int row0, int ld,
+                                          int K, int k0, MLA_LDS char* tile, int w) {
   unsigned ln;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
   int rows = rows_total - row0;
   rows = rows > kGemmTile ? kGemmTile : rows;
-  const u32x4 rs = make_rsrc(base + (size_t)row0 * K, (unsigned)((size_t)(rows > 0 ? rows : 0) * K * 2));
+  // the descriptor ends at the last valid row's row start + ld: rows past it read as zeros
+  const u32x4 rs = make_rsrc(base + (size_t)row0 * ld, (unsigned)((size_t)(rows > 0 ? rows : 0) * ld * 2));
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int i = w + 4 * c;  // copy index 0..15
     const int s = 8 * i + (int)(ln >> 3);
     const int logical = gemm_chunk(s, (int)(ln & 7));
-    const unsigned voff = (unsigned)((s * K + k0 + 8 * logical) * 2);
+    const int k = k0 + 8 * logical;  // columns past K read as zeros
+    const unsigned voff = k < K ? (unsigned)(((size_t)s * ld + k) * 2) : 0xFFFFFFF0u;
     buf2lds16(rs, voff, tile + i * 1024);
   }
 }
@@ -67,16 +73,19 @@ mla_gemm_nt(GemmArgs a) {
 
   const int tn = blockIdx.x % a.tiles_n, tm = blockIdx.x / a.tiles_n;
   const int n0 = tn * kGemmTile, m0 = tm * kGemmTile;
+  const bf16* __restrict__ X = a.x + (size_t)blockIdx.y * a.bsx;
+  const bf16* __restrict__ W = a.w + (size_t)blockIdx.y * a.bsw;
+  bf16* __restrict__ Y = a.y + (size_t)blockIdx.y * a.bsy;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, kq = lane >> 4;
   const int wn = w & 1, wm = w >> 1;  // this wave's 64 x 64 block
-  const int nk = a.K / kGemmKT;
+  const int nk = (a.K + kGemmKT - 1) / kGemmKT;
 
   auto stage_w = [&](int st) { return smem + st * 2 * kGemmTileBytes; };
   auto stage_x = [&](int st) { return smem + st * 2 * kGemmTileBytes + kGemmTileBytes; };
 
-  gemm_copy(a.w, a.N, n0, a.K, 0, stage_w(0), w);
-  gemm_copy(a.x, a.M, m0, a.K, 0, stage_x(0), w);
+  gemm_copy(W, a.N, n0, a.ldw, a.K, 0, stage_w(0), w);
+  gemm_copy(X, a.M, m0, a.lda, a.K, 0, stage_x(0), w);
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -92,8 +101,8 @@ mla_gemm_nt(GemmArgs a) {
     wait_vmcnt<0>();
     wg_barrier();  // tile kt visible; every wave is done with tile kt-1
     if (kt + 1 < nk) {
-      gemm_copy(a.w, a.N, n0, a.K, (kt + 1) * kGemmKT, stage_w((kt + 1) & 1), w);
-      gemm_copy(a.x, a.M, m0, a.K, (kt + 1) * kGemmKT, stage_x((kt + 1) & 1), w);
+      gemm_copy(W, a.N, n0, a.ldw, a.K, (kt + 1) * kGemmKT, stage_w((kt + 1) & 1), w);
+      gemm_copy(X, a.M, m0, a.lda, a.K, (kt + 1) * kGemmKT, stage_x((kt + 1) & 1), w);
     }
     const MLA_LDS char* tw = stage_w(kt & 1);
     const MLA_LDS char* tx = stage_x(kt & 1);
@@ -123,7 +132,7 @@ mla_gemm_nt(GemmArgs a) {
       bf16x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[i][j][e];
-      bf16* dst = a.y + (size_t)m * a.N + n;
+      bf16* dst = Y + (size_t)m * a.ldy + n;
       if (n + 3 < a.N) {
         *(bf16x4*)dst = v;
       } else {
@@ -133,6 +142,117 @@ mla_gemm_nt(GemmArgs a) {
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// C[z][m][n] = sum_k A[k][m] B[k][n] for the weight gradients of the
+// backward (the reduction runs over token rows): A and B are row-major with
+// the m / n index contiguous (rows lda / ldb apart, batch z at element
+// offsets bsa / bsb), C is fp32 [M, N] per batch (written, not added).
+// Workgroup: 4 waves, a 128 x 128 tile of C, 64-row k tiles in two LDS
+// stages, each wave 64 x 64.  Both MFMA operands need 8 consecutive k per
+// lane, i.e. columns of the stored tiles: they come from transposing
+// ds_read_b64_tr_b16 reads.  Tiles are copied from global memory with
+// LDS-DMA buffer loads; columns m0..m0+127 of every row are read (the caller
+// keeps them inside the allocation, whose byte size bounds the descriptor),
+// and k rows past K read as zeros.
+struct GemmTNArgs {
+  const bf16* a;
+  const bf16* b;
+  float* c;
+  int M, N, K;
+  int lda, ldb;
+  long long bsa, bsb, bsc;
+  unsigned a_bytes, b_bytes;  // allocation sizes from the a / b pointers
+  int tiles_n;
+};
+
+// rows k0 .. k0+63 x columns col0 .. col0+127 of a row-major operand into a
+// 16 KiB LDS tile, row pitch 256 bytes, unswizzled.  Copy i (1 KiB = 4 rows)
+// is issued by wave i % 4.
+__device__ __forceinline__ void gemm_tn_copy(const bf16* __restrict__ base, unsigned bytes, int ld, int K, int k0,
+                                             long long col0, MLA_LDS char* tile, int w) {
+  unsigned ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  const u32x4 rs = make_rsrc(base, bytes);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int i = w + 4 * c;  // copy index 0..15
+    const int row = 4 * i + (int)(ln >> 4);
+    const int k = k0 + row;
+    const unsigned voff = k < K ? (unsigned)((((long long)k * ld) + col0 + 8 * (ln & 15)) * 2) : 0xFFFFFFF0u;
+    buf2lds16(rs, voff, tile + i * 1024);
+  }
+}
+
+// Operand fragment for rows 16 t + (lane % 16) of the stored columns and the
+// k-step's 32 rows: lane l gets tile rows 8 (l/16) + 0..7 of column
+// col0 + l % 16 (two transposing reads of four rows each).
+__device__ __forceinline__ bf16x8 gemm_tn_operand(const MLA_LDS char* tile, int ks, int col0, int l16, int kq) {
+  const int e = l16 >> 2, q = l16 & 3;
+  const MLA_LDS char* p = tile + (32 * ks + 8 * kq + e) * 256 + (col0 + 4 * q) * 2;
+  return cat4(lds_read_tr16(p), lds_read_tr16(p + 4 * 256));
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mla_gemm_tn(GemmTNArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * kGemmTileBytes];
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+  const int tn = blockIdx.x % a.tiles_n, tm = blockIdx.x / a.tiles_n;
+  const int n0 = tn * kGemmTile, m0 = tm * kGemmTile;
+  const long long ca = (long long)blockIdx.y * a.bsa + m0, cb = (long long)blockIdx.y * a.bsb + n0;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int wn = w & 1, wm = w >> 1;
+  const int nk = (a.K + kGemmKT - 1) / kGemmKT;
+  auto stage_a = [&](int st) { return smem + st * 2 * kGemmTileBytes; };
+  auto stage_b = [&](int st) { return smem + st * 2 * kGemmTileBytes + kGemmTileBytes; };
+
+  gemm_tn_copy(a.a, a.a_bytes, a.lda, a.K, 0, ca, stage_a(0), w);
+  gemm_tn_copy(a.b, a.b_bytes, a.ldb, a.K, 0, cb, stage_b(0), w);
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
+
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<0>();
+    wg_barrier();
+    if (kt + 1 < nk) {
+      gemm_tn_copy(a.a, a.a_bytes, a.lda, a.K, (kt + 1) * kGemmKT, ca, stage_a((kt + 1) & 1), w);
+      gemm_tn_copy(a.b, a.b_bytes, a.ldb, a.K, (kt + 1) * kGemmKT, cb, stage_b((kt + 1) & 1), w);
+    }
+    const MLA_LDS char* ta = stage_a(kt & 1);
+    const MLA_LDS char* tb = stage_b(kt & 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        fa[t] = gemm_tn_operand(ta, ks, 64 * wm + 16 * t, l16, kq);
+        fb[t] = gemm_tn_operand(tb, ks, 64 * wn + 16 * t, l16, kq);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(fa[i], fb[j], acc[i][j]);
+    }
+  }
+  // C fragment (i, j): rows m0 + 64 wm + 16 i + 4 kq + e, column n0 + 64 wn + 16 j + l16
+  float* C = a.c + (size_t)blockIdx.y * a.bsc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 64 * wn + 16 * j + l16;
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 64 * wm + 16 * i + 4 * kq + e;
+        if (m < a.M) C[(size_t)m * a.N + n] = acc[i][j][e];
+      }
+    }
 }
 
 }  // namespace mla

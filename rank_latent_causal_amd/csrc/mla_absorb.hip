@@ -8,6 +8,7 @@
 #include <cstdint>
 
 #include "common.h"
+#include "backward_bf16.h"
 #include "decode_bf16.h"
 #include "f32_kernels.h"
 #include "forward_bf16.h"
@@ -165,18 +166,66 @@ ForwardLayout forward_layout(int B, int T, int q_rank, int H, int dq, int dv, in
   return L;
 }
 
+// Y = X W^T, every operand dense row-major (one batch)
 void launch_gemm(const bf16* x, const bf16* w, bf16* y, int M, int N, int K, hipStream_t s) {
   mla::GemmArgs g{};
   g.x = x; g.w = w; g.y = y; g.M = M; g.N = N; g.K = K;
+  g.lda = K; g.ldw = K; g.ldy = N;
   g.tiles_n = (N + mla::kGemmTile - 1) / mla::kGemmTile;
   const long long grid = (long long)g.tiles_n * ((M + mla::kGemmTile - 1) / mla::kGemmTile);
-  hipLaunchKernelGGL(mla::mla_gemm_nt, dim3((unsigned)grid), dim3(256), 0, s, g);
+  hipLaunchKernelGGL(mla::mla_gemm_nt, dim3((unsigned)grid, 1), dim3(256), 0, s, g);
 }
 
 void launch_rmsnorm(bf16* x, const bf16* gain, int rows, int n, float eps, hipStream_t s) {
   mla::RmsNormArgs a{};
   a.x = x; a.gain = gain; a.rows = rows; a.n = n; a.eps = eps;
   hipLaunchKernelGGL(mla::mla_rmsnorm_rows, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+}
+
+struct BackwardLayout {
+  size_t dov = 0, ld = 0, qabs = 0, dolat = 0, da = 0, ol = 0, part = 0, total = 0;
+  int nhg = 0, hpg = 0;
+};
+
+BackwardLayout backward_layout(int B, int T, int H, int dv, int r) {
+  BackwardLayout L;
+  const size_t BT = (size_t)B * T;
+  // at most 8 head groups, none of them empty
+  L.hpg = (H + 7) / 8;
+  L.nhg = (H + L.hpg - 1) / L.hpg;
+  size_t off = 0;
+  L.dov = off;   off = align_up(off + BT * H * dv * sizeof(bf16));
+  L.ld = off;    off = align_up(off + (size_t)H * BT * 2 * sizeof(float));
+  L.qabs = off;  off = align_up(off + (size_t)H * BT * r * sizeof(bf16));
+  L.dolat = off; off = align_up(off + (size_t)H * BT * r * sizeof(bf16));
+  L.da = off;    off = align_up(off + (size_t)H * BT * r * sizeof(bf16));
+  L.ol = off;    off = align_up(off + (size_t)H * BT * r * sizeof(bf16));
+  L.part = off;  off = align_up(off + (size_t)L.nhg * BT * r * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+// C[z] = A[z]^T B[z] over K token rows (weight gradients, fp32 out)
+void launch_gemm_tn(const bf16* A, size_t a_bytes, int lda, long long bsa, const bf16* Bm, size_t b_bytes, int ldb,
+                    long long bsb, float* C, long long bsc, int M, int N, int K, int batch, hipStream_t s) {
+  mla::GemmTNArgs g{};
+  g.a = A; g.b = Bm; g.c = C; g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb;
+  g.bsa = bsa; g.bsb = bsb; g.bsc = bsc;
+  g.a_bytes = (unsigned)a_bytes; g.b_bytes = (unsigned)b_bytes;
+  g.tiles_n = (N + mla::kGemmTile - 1) / mla::kGemmTile;
+  const int tiles = g.tiles_n * ((M + mla::kGemmTile - 1) / mla::kGemmTile);
+  hipLaunchKernelGGL(mla::mla_gemm_tn, dim3(tiles, batch), dim3(256), 0, s, g);
+}
+
+template <int DQ, int DV, int R>
+void launch_backward_bf16(const mla::BwdPrepArgs& pa, const mla::DecodeAbsorbArgs& qa, const mla::DecodeAbsorbArgs& va,
+                          const mla::BwdArgs& ba, hipStream_t s) {
+  constexpr int JC = R < 64 ? R : 64;
+  hipLaunchKernelGGL(mla::mla_bwd_prep, dim3(pa.B * pa.T), dim3(256), 0, s, pa);
+  hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(qa.H * (R / JC)), dim3(256), 0, s, qa);
+  hipLaunchKernelGGL((mla::mla_decode_absorb<DV, R>), dim3(va.H * (R / JC)), dim3(256), 0, s, va);
+  hipLaunchKernelGGL((mla::mla_bwd_query<R>), dim3(ba.B * ba.ntb * ba.H), dim3(64 * mla::kBwdWaves), 0, s, ba);
+  hipLaunchKernelGGL((mla::mla_bwd_key<R>), dim3(ba.B * ba.ntb * ba.nhg), dim3(64 * mla::kBwdWaves), 0, s, ba);
 }
 
 }  // namespace
@@ -213,7 +262,7 @@ mla_status mla_absorb_prefill(const void* q, const void* c, const void* w_uk, co
 // paged one (pool c of num_pages pages, geometry checked by the caller).
 static mla_status extend_impl(const void* q, const void* c, const int32_t* block_table, long long num_pages,
                        int page_size, int max_pages, const void* w_uk, const void* w_uv, const void* gate,
-                       void* out, int B, int T, int S, int H, int d_q, int d_v, int r, float scale,
+                       void* out, float* lse, int B, int T, int S, int H, int d_q, int d_v, int r, float scale,
                        mla_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !c || !w_uk || !w_uv || !gate || !out) return MLA_ERR_INVALID_ARG;
   if (B <= 0 || T <= 0 || S < T || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return MLA_ERR_INVALID_ARG;
@@ -257,6 +306,7 @@ static mla_status extend_impl(const void* q, const void* c, const int32_t* block
   a.qscale = scale * mla::kLog2e;
   a.block_table = block_table; a.max_pages = max_pages; a.num_pages = (int)num_pages;
   a.page_shift = paged ? log2_exact(page_size) : 0;
+  a.lse = lse;
   if (paged) {
     if (d_q == 16) launch_prefill_bf16<16, 16, 32, true>(a, s);
     else if (d_q == 64) launch_prefill_bf16<64, 64, 256, true>(a, s);
@@ -274,7 +324,18 @@ mla_status mla_absorb_extend(const void* q, const void* c, const void* w_uk, con
                              const void* gate, void* out, int B, int T, int S, int H, int d_q, int d_v,
                              int r, float scale, mla_dtype dtype, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return extend_impl(q, c, nullptr, 0, 0, 0, w_uk, w_uv, gate, out, B, T, S, H, d_q, d_v, r, scale, dtype,
+  return extend_impl(q, c, nullptr, 0, 0, 0, w_uk, w_uv, gate, out, nullptr, B, T, S, H, d_q, d_v, r, scale, dtype,
+                     workspace, workspace_bytes, stream);
+}
+
+mla_status mla_absorb_prefill_train(const void* q, const void* c, const void* w_uk, const void* w_uv,
+                                    const void* gate, void* out, float* lse, int B, int T, int H, int d_q, int d_v,
+                                    int r, float scale, mla_dtype dtype, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (!lse || !aligned16(lse)) return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_DTYPE_BF16) return dtype == MLA_DTYPE_F32 ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (!fits(B, H, T)) return MLA_ERR_UNSUPPORTED;
+  return extend_impl(q, c, nullptr, 0, 0, 0, w_uk, w_uv, gate, out, lse, B, T, T, H, d_q, d_v, r, scale, dtype,
                      workspace, workspace_bytes, stream);
 }
 
@@ -289,8 +350,8 @@ mla_status mla_absorb_extend_paged(const void* q, const void* c_pages, const int
     return MLA_ERR_INVALID_ARG;
   if (dtype != MLA_DTYPE_BF16) return dtype == MLA_DTYPE_F32 ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
   if (!paged_geometry_ok(B, r, num_pages, page_size, max_pages)) return MLA_ERR_UNSUPPORTED;
-  return extend_impl(q, c_pages, block_table, num_pages, page_size, max_pages, w_uk, w_uv, gate, out, B, T, S, H,
-                     d_q, d_v, r, scale, dtype, workspace, workspace_bytes, stream);
+  return extend_impl(q, c_pages, block_table, num_pages, page_size, max_pages, w_uk, w_uv, gate, out, nullptr, B, T,
+                     S, H, d_q, d_v, r, scale, dtype, workspace, workspace_bytes, stream);
 }
 
 size_t mla_absorb_decode_workspace_size(int B, int H, int d_q, int r, int num_splits, mla_dtype dtype) {
@@ -428,6 +489,77 @@ mla_status mla_cache_append_paged(const void* c_new, void* c_pages, const int32_
   hipLaunchKernelGGL(mla::mla_cache_append_paged, dim3((B + 3) / 4), dim3(256), 0, (hipStream_t)stream,
                      (const char*)c_new, (char*)c_pages, block_table, positions, B, row_bytes, page_size, max_pages,
                      (int)num_pages);
+  return launch_status();
+}
+
+size_t mla_absorb_prefill_backward_workspace_size(int B, int T, int H, int d_q, int d_v, int r, mla_dtype dtype) {
+  if (B <= 0 || T <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return kBadSize;
+  if (dtype != MLA_DTYPE_BF16) return kBadSize;
+  return backward_layout(B, T, H, d_v, r).total;
+}
+
+mla_status mla_absorb_prefill_backward(const void* q, const void* c, const void* w_uk, const void* w_uv,
+                                       const void* gate, const void* out, const float* lse, const void* dout,
+                                       void* dq, void* dc, float* dw_uk, float* dw_uv, void* dgate, int B, int T,
+                                       int H, int d_q, int d_v, int r, float scale, mla_dtype dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const void* ptrs[] = {q, c, w_uk, w_uv, gate, out, lse, dout, dq, dc, dw_uk, dw_uv, dgate};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || T <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_DTYPE_BF16) return dtype == MLA_DTYPE_F32 ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (!bf16_shape_supported(d_q, d_v, r)) return MLA_ERR_UNSUPPORTED;
+  // 32-bit offsets inside the weight-gradient GEMM descriptors
+  const long long BT = (long long)B * T;
+  if (BT >= (1LL << 31) || (long double)H * BT * r * 2 >= 2.0e9L || (long double)H * BT * d_q * 2 >= 2.0e9L ||
+      (long double)H * BT * d_v * 2 >= 2.0e9L)
+    return MLA_ERR_UNSUPPORTED;
+  const BackwardLayout L = backward_layout(B, T, H, d_v, r);
+  if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+  if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  mla::BwdPrepArgs pa{};
+  pa.gate = (const bf16*)gate; pa.out = (const bf16*)out; pa.dout = (const bf16*)dout; pa.lse = lse;
+  pa.dgate = (bf16*)dgate; pa.dov = (bf16*)(ws + L.dov); pa.ld = (float*)(ws + L.ld);
+  pa.B = B; pa.T = T; pa.H = H; pa.DV = d_v;
+  mla::DecodeAbsorbArgs qa{};
+  qa.q = (const bf16*)q; qa.wuk = (const bf16*)w_uk; qa.qabs = (bf16*)(ws + L.qabs);
+  qa.B = (int)BT; qa.H = H; qa.qscale = scale * mla::kLog2e; qa.head_major = 1;
+  mla::DecodeAbsorbArgs va{};
+  va.q = pa.dov; va.wuk = (const bf16*)w_uv; va.qabs = (bf16*)(ws + L.dolat);
+  va.B = (int)BT; va.H = H; va.qscale = 1.0f; va.head_major = 1;
+  mla::BwdArgs ba{};
+  ba.c = (const bf16*)c; ba.qabs = qa.qabs; ba.dolat = va.qabs; ba.ld = pa.ld;
+  ba.da = (bf16*)(ws + L.da); ba.ol = (bf16*)(ws + L.ol); ba.dc_part = (float*)(ws + L.part);
+  ba.B = B; ba.T = T; ba.H = H; ba.scale = scale; ba.ntb = (T + 31) / 32; ba.nhg = L.nhg; ba.hpg = L.hpg;
+  if (d_q == 16) launch_backward_bf16<16, 16, 32>(pa, qa, va, ba, s);
+  else if (d_q == 64) launch_backward_bf16<64, 64, 256>(pa, qa, va, ba, s);
+  else launch_backward_bf16<128, 128, 512>(pa, qa, va, ba, s);
+
+  // dc: sum of the head-group partials
+  const long long n4 = BT * r / 4;
+  hipLaunchKernelGGL(mla::mla_bwd_dc_sum, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, ba.dc_part,
+                     (bf16*)dc, BT, r, L.nhg);
+  // dq[:, h, :] = da[h] W_UK[h]^T
+  {
+    mla::GemmArgs g{};
+    g.x = ba.da; g.w = (const bf16*)w_uk; g.y = (bf16*)dq;
+    g.M = (int)BT; g.N = d_q; g.K = r; g.lda = r; g.ldw = r; g.ldy = H * d_q;
+    g.bsx = BT * r; g.bsw = (long long)d_q * r; g.bsy = d_q;
+    g.tiles_n = (d_q + mla::kGemmTile - 1) / mla::kGemmTile;
+    const long long grid = (long long)g.tiles_n * ((BT + mla::kGemmTile - 1) / mla::kGemmTile);
+    hipLaunchKernelGGL(mla::mla_gemm_nt, dim3((unsigned)grid, H), dim3(256), 0, s, g);
+  }
+  // dW_UK[h] = q[:, h, :]^T da[h];  dW_UV[h] = do[:, h, :]^T ol[h]
+  const size_t q_bytes = (size_t)BT * H * d_q * 2, hr_bytes = (size_t)H * BT * r * 2,
+               do_bytes = (size_t)BT * H * d_v * 2;
+  launch_gemm_tn((const bf16*)q, q_bytes, H * d_q, d_q, ba.da, hr_bytes, r, BT * r, dw_uk, (long long)d_q * r, d_q,
+                 r, (int)BT, H, s);
+  launch_gemm_tn(pa.dov, do_bytes, H * d_v, d_v, ba.ol, hr_bytes, r, BT * r, dw_uv, (long long)d_v * r, d_v, r,
+                 (int)BT, H, s);
   return launch_status();
 }
 

@@ -39,6 +39,9 @@ struct PrefillArgs {
   // zero rows.
   const int* block_table;  // [B, max_pages]
   int page_shift, max_pages, num_pages;
+  // training: the natural-log log-sum-exp of each row's scaled scores,
+  // [B, H, T] (written when non-null; the backward recomputes P from it)
+  float* lse;
 };
 
 // Issues the copies of key tile j (rows 32j .. 32j+31 of sequence b) into an
@@ -145,7 +148,10 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
     wg_barrier();  // this stage is refilled by the next iteration
   }
 
-  const float inv_l = 1.0f / col_sum(st.l_run);
+  const float l_tot = col_sum(st.l_run);
+  const float inv_l = 1.0f / l_tot;
+  if (a.lse && kq == 0 && tvalid && hvalid)
+    a.lse[((size_t)b * H + h) * T + t] = (st.m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
   const size_t orow = ((size_t)b * T + tc) * (size_t)H * DV + (size_t)hc * DV;
   project_gate_store<DV, R>(st.oT, inv_l, a.wuv + (size_t)hc * DV * R, a.gate + orow, a.out + orow,
                             tvalid && hvalid, l16, kq);
@@ -313,7 +319,10 @@ mla_prefill_pair_kernel(PrefillArgs a) {
   bf16x8 ob[2][PA::NKK];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const float inv_l = 1.0f / col_sum(st.l_run[c]);
+    const float l_tot = col_sum(st.l_run[c]);
+    const float inv_l = 1.0f / l_tot;
+    if (a.lse && jh == 0 && kq == 0 && tv[c] && hvalid)
+      a.lse[((size_t)b * H + h) * T + tq[c]] = (st.m_run[c] + __builtin_log2f(l_tot)) * 0.69314718055994531f;
 #pragma unroll
     for (int kk = 0; kk < PA::NKK; ++kk) ob[c][kk] = pack44(st.oT[c][2 * kk], st.oT[c][2 * kk + 1], inv_l);
   }

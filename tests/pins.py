@@ -566,6 +566,22 @@ def pin_backward_special_cases(o):
     _close(g1["dq"], np.zeros_like(g1["dq"]), 0.0, 1e-14, "T=1 dq")
 
 
+def pin_lse_matches_library(o):
+    """The log-sum-exp of each causal score row equals scipy's logsumexp of
+    the scores formed densely in numpy (a library routine)."""
+    from scipy.special import logsumexp
+    B, T, H, dq, dv, r, scale = 2, 7, 3, 4, 2, 5, 0.8
+    d = dg.prefill_inputs(B, T, H, dq, dv, r, dtype=dg.F32, seed=115)
+    q, c, wk = (_f(d, k).astype(np.float64) for k in ("q", "c", "w_uk"))
+    want = np.empty((B, H, T))
+    for b in range(B):
+        for h in range(H):
+            sc = scale * (q[b, :, h, :] @ wk[h]) @ c[b].T
+            for t in range(T):
+                want[b, h, t] = logsumexp(sc[t, :t + 1])
+    _close(o.prefill_lse(_f(d, "q"), _f(d, "c"), _f(d, "w_uk"), scale), want, 1e-13, 1e-13, "lse")
+
+
 ALL_PINS = [
     pin_absorbed_equals_decompressed,
     pin_attention_rows,
@@ -590,4 +606,5 @@ ALL_PINS = [
     pin_cache_append_then_decode,
     pin_backward_finite_differences,
     pin_backward_special_cases,
+    pin_lse_matches_library,
 ]

@@ -1,0 +1,145 @@
+"""GPU parity of the training path: the forward's log-sum-exp and the
+backward of the prefill core, through the C ABI, against the oracle.
+
+The backward is fed the oracle's forward output (rounded to bf16) and
+log-sum-exp, so the comparison measures the backward alone.  Tolerance (bf16
+operands, fp32 accumulation), per gradient tensor:
+  * relative Frobenius error ||gpu - oracle|| / ||oracle|| at most 1e-2;
+  * every element within 2^-7 |oracle| + 25% of the tensor's RMS + 1e-3.
+The chain rounds q_abs, dol, P, dS, c and the stored da / ol to bf16, each at
+most 2^-9 relative, so a term carries about 1% relative error and a long sum
+less.  The bf16 outputs add their own rounding (2^-9 relative, doubled for
+headroom in the first term).  Single elements can sit further from the
+oracle where a gradient is a small difference: in the first positions dS =
+P (dP - D) is a difference of two values near 7 at full width (dP formed from
+bf16 dol, about 0.5% off), against an exact zero at t = 0, which puts dq of
+rows 0-1 at 10-13% of the tensor's RMS; the element bar allows that, and an
+indexing mistake would not pass the Frobenius bar.  The log-sum-exp is
+compared at 2e-2 absolute (it is formed from bf16 q_abs).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import datagen as dg
+import oracle
+from gpu_util import to_dev, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {"toy": (16, 16, 32), "mid": (64, 64, 256), "full": (128, 128, 512)}
+FROB_REL, REL_ELEM, RMS_FRAC, ABS_FLOOR = 1e-2, 2.0 ** -7, 0.25, 1e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.get()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rank_latent_causal_amd as mla
+    mla.lib()
+    return torch
+
+
+def _grad_close(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    frob = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    assert frob <= FROB_REL, f"{what}: relative Frobenius error {frob:.3g} > {FROB_REL}"
+    bar = REL_ELEM * np.abs(ref) + RMS_FRAC * rms + ABS_FLOOR
+    err = np.abs(got - ref)
+    if (err > bar).any():
+        idx = np.unravel_index(np.argmax(err), err.shape)
+        raise AssertionError(f"{what}: {(err > bar).sum()} of {err.size} beyond the bar (rms {rms:.3g}); "
+                             f"max err {err.max():.3g} at {idx} (gpu {got[idx]:.5g}, oracle {ref[idx]:.5g})")
+    return float(err.max() / max(rms, 1e-30))
+
+
+def _case(B, T, H, shape, seed):
+    dq, dv, r = SHAPES[shape]
+    d = dg.prefill_inputs(B, T, H, dq, dv, r, dtype=dg.BF16, seed=seed)
+    d["scale"] = dq ** -0.5
+    dout = dg.f32_to_bf16_bits(np.random.default_rng(seed).standard_normal((B, T, H * dv)).astype(np.float32))
+    return d, dout
+
+
+def test_train_forward_lse(o):
+    """The training forward's output is the plain forward's, bit for bit, and
+    its log-sum-exp matches the oracle's."""
+    import torch
+    import rank_latent_causal_amd as mla
+    for (B, T, H, shape) in [(2, 77, 3, "toy"), (1, 130, 5, "mid"), (2, 70, 9, "full")]:
+        d, _ = _case(B, T, H, shape, seed=9000 + T)
+        args = [to_dev(d[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")]
+        out, lse = mla.mla_absorb_prefill_train(*args, d["scale"])
+        ref_out = mla.mla_absorb_prefill(*args, d["scale"])
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"{shape}: training forward output differs"
+        f = dg.as_f32
+        want = o.prefill_lse(f(d["q"]), f(d["c"]), f(d["w_uk"]), d["scale"])
+        got = lse.cpu().numpy().astype(np.float64)
+        err = np.abs(got - want).max()
+        assert err <= 2e-2, f"{shape}: lse max err {err:.3g}"
+
+
+@pytest.mark.parametrize("B,T,H,shape", [
+    (2, 100, 3, "toy"),
+    (1, 33, 2, "toy"),
+    (1, 130, 5, "mid"),
+    (2, 70, 9, "full"),
+    (1, 200, 8, "full"),
+    (1, 64, 96, "full"),
+])
+def test_backward_parity(o, B, T, H, shape):
+    import torch
+    import rank_latent_causal_amd as mla
+    d, dout = _case(B, T, H, shape, seed=9100 + 7 * T + H)
+    f = dg.as_f32
+    args64 = [f(d[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")]
+    ref_out = o.prefill(*args64, d["scale"])
+    ref_lse = o.prefill_lse(f(d["q"]), f(d["c"]), f(d["w_uk"]), d["scale"])
+    want = o.prefill_backward(*args64, f(dout), d["scale"])
+    log(f"backward {shape} B={B} T={T} H={H}")
+    out_b = dg.f32_to_bf16_bits(ref_out.astype(np.float32))
+    g = mla.mla_absorb_prefill_backward(*[to_dev(d[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")], to_dev(out_b),
+                                        to_dev(ref_lse.astype(np.float32)), to_dev(dout), d["scale"])
+    torch.cuda.synchronize()
+    for k in ("dgate", "dq", "dc", "dw_uk", "dw_uv"):
+        _grad_close(to_host_f64(g[k]), want[k], f"{k} ({shape} B{B} T{T} H{H})")
+
+
+def test_backward_workspace_reuse_and_repeat():
+    """Two calls on the same inputs give identical bits, also after a larger
+    call has left its intermediates in the workspace."""
+    import torch
+    import rank_latent_causal_amd as mla
+    big, dbig = _case(2, 150, 5, "mid", seed=9200)
+    small, dsmall = _case(1, 60, 5, "mid", seed=9201)
+    ws = torch.empty(mla.backward_workspace_size(2, 150, 5, 64, 64, 256, mla.DTYPE_BF16), dtype=torch.uint8,
+                     device="cuda")
+
+    def run(d, dout, workspace=None):
+        args = [to_dev(d[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")]
+        out, lse = mla.mla_absorb_prefill_train(*args, d["scale"])
+        return mla.mla_absorb_prefill_backward(*args, out, lse, to_dev(dout), d["scale"], workspace=workspace)
+
+    run(big, dbig, ws)
+    a = run(small, dsmall, ws)
+    b = run(small, dsmall)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
