@@ -13,7 +13,8 @@ algorithmic FLOPs), chunked-prefill TFLOP/s, decode latent-cache GB/s
 peaks, and the CPU oracle timed on a bounded row sample of the prefill.  The
 full-layer forward (projections, norms, core, output projection at the full
 K3 widths, B=1, T=8192) is timed separately after the steps and reported
-under "forward".  The decode over a paged cache (the decode workload in
+under "forward"; the backward of the prefill core (with the log-sum-exp of a
+training forward run before it) likewise under "backward".  The decode over a paged cache (the decode workload in
 shuffled 64-row pages) runs in each step right after the packed decode and
 is reported under "decode_paged".  Neither is part of ms_per_step.
 """
@@ -181,6 +182,46 @@ def bench_forward(torch, mla, steps, warmup):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flop_per_launch": f}}
 
 
+def backward_flops(B, T, H, dq, dv, r):
+    """Algorithmic FLOPs of one backward of the prefill core: five latent
+    products per causal (query, key, head) triple (the recomputed scores,
+    dP = dol c^T, da = dS c, and c's key and value gradients), 2 r FLOP
+    each, plus the per-row projections (q W_UK, do W_UV, da W_UK^T and the
+    two weight gradients)."""
+    pairs = B * H * T * (T + 1) // 2
+    return 10 * r * pairs + 2 * B * T * H * r * (3 * dq + 2 * dv)
+
+
+def bench_backward(torch, mla, steps, warmup):
+    """The backward of the full-width prefill (B=1, T=8192), its forward
+    (with the log-sum-exp) run once before the timed calls."""
+    d = dg.workload_inputs("full_prefill")
+    args = [dev(d[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")]
+    B, T, H, dq, dv, r = d["B"], d["T"], d["H"], d["d_q"], d["d_v"], d["r"]
+    out, lse = mla.mla_absorb_prefill_train(*args, d["scale"])
+    g = torch.Generator(device="cuda").manual_seed(d["seed"])
+    dout = torch.randn(out.shape, generator=g, device="cuda").to(torch.bfloat16)
+    ws = torch.empty(mla.backward_workspace_size(B, T, H, dq, dv, r, mla.DTYPE_BF16), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(max(1, warmup // 4)):
+        mla.mla_absorb_prefill_backward(*args, out, lse, dout, d["scale"], workspace=ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(max(1, steps // 4))]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        mla.mla_absorb_prefill_backward(*args, out, lse, dout, d["scale"], workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    f = backward_flops(B, T, H, dq, dv, r)
+    tf = f / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4), "calls": len(ev),
+            "workload": "backward of full_prefill (B=1, T=8192, H=96, d_q=d_v=128, r=512), dout ~ N(0,1)",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flop_per_launch": f}}
+
+
 def setup_decode_paged(torch, mla, dec, page_size=64):
     """The full decode workload with its cache in shuffled 64-row pages.
     Returns (launch, report): launch() enqueues one call; report(ms) builds
@@ -215,8 +256,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--which", choices=["both", "prefill", "decode", "forward"], default="both",
-                    help="both: prefill, chunked prefill and decode, then the full-layer forward")
+    ap.add_argument("--which", choices=["both", "prefill", "decode", "forward", "backward"], default="both",
+                    help="both: prefill, chunked prefill and decode, then the full-layer forward and the backward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -353,6 +394,8 @@ def main():
         res["decode_paged"] = paged[1](float(np.mean([e[6].elapsed_time(e[7]) for e in evs])))
     if args.which in ("both", "forward"):
         res["forward"] = bench_forward(torch, mla, args.steps, args.warmup)
+    if args.which in ("both", "backward"):
+        res["backward"] = bench_backward(torch, mla, args.steps, args.warmup)
     if not args.no_cpu_baseline and do_pre:
         res["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
     print(json.dumps(res), flush=True)
