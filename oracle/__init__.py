@@ -71,11 +71,13 @@ class Oracle:
         L.oracle_cache_append.argtypes = [fp, fp, I64, I, i64p, I, i64p, I, I]
         L.oracle_prefill_backward.argtypes = [fp] * 6 + [I] * 6 + [D] + [dp] * 5 + [I]
         L.oracle_prefill_lse.argtypes = [fp, fp, fp, I, I, I, I, I, D, dp, I]
+        L.oracle_extend_varlen_paged.argtypes = [fp, fp, I64, I, i64p, I, i64p, i64p, fp, fp, fp, I, I, I, I, I, D,
+                                                 dp, I]
         L.oracle_forward.argtypes = [fp] * 10 + [I] * 8 + [D, D, I, i64p, I64] + [dp] * 5 + [I]
         for f in ("oracle_prefill", "oracle_extend", "oracle_decode", "oracle_prefill_decompressed",
                   "oracle_prefill_attn", "oracle_round_bf16", "oracle_forward", "oracle_decode_paged",
                   "oracle_extend_paged", "oracle_cache_append", "oracle_prefill_backward",
-                  "oracle_prefill_lse"):
+                  "oracle_prefill_lse", "oracle_extend_varlen_paged"):
             getattr(L, f).restype = I
 
     @property
@@ -223,6 +225,28 @@ class Oracle:
             _ptr(q, ct.c_float), _ptr(pages, ct.c_float), npg, ps, _ptr(bt, ct.c_int64), bt.shape[1],
             _ptr(w_uk, ct.c_float), _ptr(w_uv, ct.c_float), _ptr(gate, ct.c_float), B, T, int(S), H, dq, dv, r,
             float(scale), rp, n, _ptr(out, ct.c_double), threads), "oracle_extend_paged")
+        return out
+
+    def extend_varlen_paged(self, q, pages, block_table, cu_q, seq_lens, w_uk, w_uv, gate, scale: float,
+                            threads: int = 0) -> np.ndarray:
+        """Varlen chunked prefill: q [Nq,H,dq] packed by cu_q [B+1], seq_lens
+        [B] cache rows per sequence (the chunk is the last T_b of them).
+        Returns [Nq, H*dv] float64."""
+        q, pages, w_uk, w_uv, gate = map(_f32, (q, pages, w_uk, w_uv, gate))
+        bt = np.ascontiguousarray(block_table, dtype=np.int64)
+        cu = np.ascontiguousarray(cu_q, dtype=np.int64)
+        lens = np.ascontiguousarray(seq_lens, dtype=np.int64)
+        Nq, H, dq = q.shape
+        npg, ps, r = pages.shape
+        dv = w_uv.shape[1]
+        B = lens.shape[0]
+        assert cu.shape == (B + 1,) and cu[-1] == Nq and bt.shape[0] == B and gate.shape == (Nq, H * dv)
+        out = np.zeros((Nq, H * dv), dtype=np.float64)
+        self._check(self.lib.oracle_extend_varlen_paged(
+            _ptr(q, ct.c_float), _ptr(pages, ct.c_float), npg, ps, _ptr(bt, ct.c_int64), bt.shape[1],
+            _ptr(cu, ct.c_int64), _ptr(lens, ct.c_int64), _ptr(w_uk, ct.c_float), _ptr(w_uv, ct.c_float),
+            _ptr(gate, ct.c_float), B, H, dq, dv, r, float(scale), _ptr(out, ct.c_double), threads),
+            "oracle_extend_varlen_paged")
         return out
 
     def cache_append(self, c_new, pages, block_table, positions) -> np.ndarray:

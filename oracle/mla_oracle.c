@@ -482,6 +482,41 @@ int oracle_extend_paged(const float* q, const float* pages, int64_t num_pages, i
   return err;
 }
 
+/* Varlen chunked prefill against a paged cache: sequence b owns the
+ * T_b = cu_q[b+1] - cu_q[b] packed query rows cu_q[b] .. (q [Nq, H, dq], gate
+ * and out [Nq, H*dv]) and seq_lens[b] = S_b >= T_b cache rows; its chunk is
+ * positions S_b - T_b .. S_b - 1.  A batch that mixes prefill chunks
+ * (S_b = T_b), chunks after a cached prefix and decode steps (T_b = 1) is one
+ * call.  Each sequence is oracle_extend on its gathered rows. */
+int oracle_extend_varlen_paged(const float* q, const float* pages, int64_t num_pages, int page_size,
+                               const int64_t* block_table, int max_pages, const int64_t* cu_q, const int64_t* seq_lens,
+                               const float* w_uk, const float* w_uv, const float* gate, int B, int H, int dq, int dv,
+                               int r, double scale, double* out, int nthreads) {
+  if (!q || !pages || !block_table || !cu_q || !seq_lens || !gate || !out || B <= 0 || H <= 0 || dq <= 0 ||
+      dv <= 0 || r <= 0 || page_size <= 0 || max_pages <= 0 || cu_q[0] != 0)
+    return ORACLE_EINVAL;
+  int err = ORACLE_OK;
+  for (int b = 0; b < B && err == ORACLE_OK; ++b) {
+    const int64_t T = cu_q[b + 1] - cu_q[b], S = seq_lens[b];
+    if (T < 0 || S < T || S > (int64_t)max_pages * page_size) return ORACLE_EINVAL;
+    if (T == 0) continue;
+    float* rows = (float*)malloc(sizeof(float) * (size_t)S * r);
+    if (!rows) return ORACLE_ENOMEM;
+    err = gather_rows(pages, num_pages, page_size, block_table, max_pages, b, S, r, rows);
+    if (err == ORACLE_OK)
+#if ORACLE_MUTANT == 26
+      /* planted mistake: the chunk placed at the start of the sequence */
+      err = oracle_extend(q + cu_q[b] * H * dq, rows, w_uk, w_uv, gate + cu_q[b] * H * dv, 1, (int)T, (int)T, H, dq,
+                          dv, r, scale, NULL, T, out + cu_q[b] * H * dv, nthreads);
+#else
+      err = oracle_extend(q + cu_q[b] * H * dq, rows, w_uk, w_uv, gate + cu_q[b] * H * dv, 1, (int)T, (int)S, H, dq,
+                          dv, r, scale, NULL, T, out + cu_q[b] * H * dv, nthreads);
+#endif
+    free(rows);
+  }
+  return err;
+}
+
 /* Cache append: row c_new[i] becomes row positions[i] of sequence i, i.e. it
  * is written to page block_table[i, positions[i] / page_size], slot
  * positions[i] % page_size, in place. */

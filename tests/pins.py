@@ -582,6 +582,35 @@ def pin_lse_matches_library(o):
     _close(o.prefill_lse(_f(d, "q"), _f(d, "c"), _f(d, "w_uk"), scale), want, 1e-13, 1e-13, "lse")
 
 
+def pin_varlen_mixed_batch(o):
+    """A varlen batch mixing a full prefill (S = T), a chunk after a cached
+    prefix, a decode step (T = 1) and an empty chunk over one shuffled page
+    pool equals, sequence by sequence, the separately written prefill and
+    decode routines (and chunked prefill, itself pinned against both)."""
+    H, dq, dv, r, ps = 2, 3, 2, 5, 8
+    S = [13, 20, 9, 6]
+    T = [13, 7, 1, 0]
+    parts = [dg.prefill_inputs(1, s_, H, dq, dv, r, dtype=dg.F32, seed=120 + i) for i, s_ in enumerate(S)]
+    f = dg.as_f32
+    c_rows = np.concatenate([f(p["c"])[0] for p in parts])
+    cu_k = np.concatenate([[0], np.cumsum(S)])
+    lay = dg.paged_layout(S, ps, seed=120)
+    pool = dg.scatter_to_pages(c_rows, cu_k, lay)
+    q = np.concatenate([f(p["q"])[0, s_ - t_:] for p, s_, t_ in zip(parts, S, T)])
+    g = np.concatenate([f(p["gate"])[0, s_ - t_:] for p, s_, t_ in zip(parts, S, T)])
+    cu_q = np.concatenate([[0], np.cumsum(T)])
+    wk, wv = f(parts[0]["w_uk"]), f(parts[0]["w_uv"])
+    got = o.extend_varlen_paged(q, pool, lay["block_table"], cu_q, S, wk, wv, g, 0.6)
+    full = o.prefill(f(parts[0]["q"]), f(parts[0]["c"]), wk, wv, f(parts[0]["gate"]), 0.6)[0]
+    _close(got[cu_q[0]:cu_q[1]], full, 1e-13, 1e-15, "varlen prefill sequence")
+    part1 = o.extend(f(parts[1]["q"])[:, S[1] - T[1]:], f(parts[1]["c"]), wk, wv, f(parts[1]["gate"])[:, S[1] - T[1]:],
+                     0.6)[0]
+    _close(got[cu_q[1]:cu_q[2]], part1, 1e-13, 1e-15, "varlen chunk after a prefix")
+    dec = o.decode(f(parts[2]["q"])[:, S[2] - 1], f(parts[2]["c"])[0], np.array([0, S[2]]), wk, wv,
+                   f(parts[2]["gate"])[:, S[2] - 1], 0.6)
+    _close(got[cu_q[2]:cu_q[3]], dec, 1e-13, 1e-15, "varlen decode step")
+
+
 ALL_PINS = [
     pin_absorbed_equals_decompressed,
     pin_attention_rows,
@@ -607,4 +636,5 @@ ALL_PINS = [
     pin_backward_finite_differences,
     pin_backward_special_cases,
     pin_lse_matches_library,
+    pin_varlen_mixed_batch,
 ]

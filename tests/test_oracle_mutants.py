@@ -35,6 +35,7 @@ MUTANTS = {
     23: "backward: value path of c dropped from dc",
     24: "backward: gate gradient uses the sigmoid, not its derivative",
     25: "backward: query-side gradient missing the softmax scale",
+    26: "varlen: the chunk placed at the start of its sequence",
 }
 
 
