@@ -163,6 +163,33 @@ mla_status mla_absorb_extend_paged(const void* q, const void* c_pages, const int
                                    int max_pages, float scale, mla_dtype dtype, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace mla_absorb_extend_varlen_paged needs ((size_t)-1: invalid). */
+size_t mla_absorb_extend_varlen_workspace_size(int B, int Nq, int H, int d_q, int r, mla_dtype dtype);
+
+/*
+ * Varlen chunked prefill over a paged cache: one call for a batch that mixes
+ * full prefills, chunks after a cached prefix and single decode steps.
+ * Sequence b owns the packed query rows cu_q[b] .. cu_q[b+1]-1 (T_b rows,
+ * possibly none) and seq_lens[b] = S_b cache rows, its chunk being positions
+ * S_b - T_b .. S_b - 1 (so query t attends to rows 0 .. S_b - T_b + t):
+ *   q     [Nq, H, d_q]     queries of all chunks, sequence by sequence
+ *   cu_q  [B + 1] int32    device array, cu_q[0] = 0, cu_q[B] = Nq, non-decreasing
+ *   seq_lens [B] int32     device array, T_b <= S_b <= max_pages * page_size
+ *   gate, out [Nq, H*d_v]
+ *   c_pages, block_table   as for the paged calls (the chunk's own rows are in
+ *                          the cache already, e.g. through mla_cache_append_paged)
+ * cu_q and seq_lens are read on the device only: ranges are clamped into
+ * [0, Nq) and [0, max_pages * page_size] before use, so a violated
+ * precondition yields unspecified values for the affected rows, never an
+ * access outside the buffers.  bf16 only.  Workspace:
+ * mla_absorb_extend_varlen_workspace_size bytes.
+ */
+mla_status mla_absorb_extend_varlen_paged(const void* q, const void* c_pages, const int32_t* block_table,
+                                          const int32_t* cu_q, const int32_t* seq_lens, const void* w_uk,
+                                          const void* w_uv, const void* gate, void* out, int B, int Nq, int H, int d_q,
+                                          int d_v, int r, int64_t num_pages, int page_size, int max_pages, float scale,
+                                          mla_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace mla_absorb_decode_paged needs ((size_t)-1: invalid). */
 size_t mla_absorb_decode_paged_workspace_size(int B, int H, int d_q, int r, int num_splits, mla_dtype dtype);
 

@@ -19,7 +19,8 @@ __all__ = [
     "prefill_workspace_size", "decode_workspace_size", "decode_paged_workspace_size", "forward_workspace_size",
     "mla_absorb_prefill", "mla_absorb_extend", "mla_absorb_extend_paged", "mla_absorb_decode",
     "mla_absorb_decode_paged", "mla_cache_append_paged", "mla_gated_forward", "mla_absorb_prefill_train",
-    "backward_workspace_size", "mla_absorb_prefill_backward",
+    "backward_workspace_size", "mla_absorb_prefill_backward", "varlen_workspace_size",
+    "mla_absorb_extend_varlen_paged",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_absorb.so")
@@ -35,6 +36,8 @@ EXPORTS = (
     "mla_absorb_decode_workspace_size",
     "mla_absorb_decode",
     "mla_absorb_extend_paged",
+    "mla_absorb_extend_varlen_workspace_size",
+    "mla_absorb_extend_varlen_paged",
     "mla_absorb_decode_paged_workspace_size",
     "mla_absorb_decode_paged",
     "mla_cache_append_paged",
@@ -76,6 +79,10 @@ def lib() -> ct.CDLL:
         L.mla_absorb_decode.restype = I
         L.mla_absorb_extend_paged.argtypes = [vp] * 7 + [I] * 7 + [I64, I, I, F, I, vp, sz, vp]
         L.mla_absorb_extend_paged.restype = I
+        L.mla_absorb_extend_varlen_workspace_size.argtypes = [I] * 6
+        L.mla_absorb_extend_varlen_workspace_size.restype = sz
+        L.mla_absorb_extend_varlen_paged.argtypes = [vp] * 9 + [I] * 6 + [I64, I, I, F, I, vp, sz, vp]
+        L.mla_absorb_extend_varlen_paged.restype = I
         L.mla_absorb_decode_paged_workspace_size.argtypes = [I, I, I, I, I, I]
         L.mla_absorb_decode_paged_workspace_size.restype = sz
         L.mla_absorb_decode_paged.argtypes = [vp] * 8 + [I] * 5 + [I64, I, I, F, I, I, vp, sz, vp]
@@ -114,6 +121,13 @@ def decode_workspace_size(B: int, H: int, d_q: int, r: int, num_splits: int, dty
     n = lib().mla_absorb_decode_workspace_size(B, H, d_q, r, num_splits, dtype)
     if n == _BAD:
         raise MLAError(MLA_ERR_INVALID_ARG, "mla_absorb_decode_workspace_size")
+    return n
+
+
+def varlen_workspace_size(B: int, Nq: int, H: int, d_q: int, r: int, dtype: int) -> int:
+    n = lib().mla_absorb_extend_varlen_workspace_size(B, Nq, H, d_q, r, dtype)
+    if n == _BAD:
+        raise MLAError(MLA_ERR_INVALID_ARG, "mla_absorb_extend_varlen_workspace_size")
     return n
 
 
@@ -281,6 +295,41 @@ def mla_absorb_extend_paged(q, c_pages, block_table, S: int, w_uk, w_uv, gate, s
                                        workspace.numel() * workspace.element_size(), _stream(stream))
     if st != MLA_OK:
         raise MLAError(st, "mla_absorb_extend_paged")
+    return out
+
+
+def mla_absorb_extend_varlen_paged(q, c_pages, block_table, cu_q, seq_lens, w_uk, w_uv, gate, scale: float,
+                                   out=None, workspace=None, stream=None):
+    """Varlen chunked prefill over a paged cache (a mixed prefill / chunk /
+    decode batch in one call): q [Nq,H,d_q] packed by cu_q [B+1] (int32,
+    device), seq_lens [B] (int32, device) cache rows per sequence; gate and
+    out [Nq,H*d_v]."""
+    torch = _torch()
+    Nq, H, dq = q.shape
+    npg, ps, r = c_pages.shape
+    dv = w_uv.shape[1]
+    B = seq_lens.shape[0]
+    dt = q.dtype
+    code = _dtype_code(q)
+    for t, shp, n in ((q, (Nq, H, dq), "q"), (c_pages, (npg, ps, r), "c_pages"), (w_uk, (H, dq, r), "w_uk"),
+                      (w_uv, (H, dv, r), "w_uv"), (gate, (Nq, H * dv), "gate")):
+        _check(t, shp, dt, n)
+    _check(block_table, (B, block_table.shape[1]), torch.int32, "block_table")
+    _check(cu_q, (B + 1,), torch.int32, "cu_q")
+    _check(seq_lens, (B,), torch.int32, "seq_lens")
+    if out is None:
+        out = torch.empty((Nq, H * dv), dtype=dt, device=q.device)
+    _check(out, (Nq, H * dv), dt, "out")
+    need = varlen_workspace_size(B, Nq, H, dq, r, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().mla_absorb_extend_varlen_paged(
+        q.data_ptr(), c_pages.data_ptr(), block_table.data_ptr(), cu_q.data_ptr(), seq_lens.data_ptr(),
+        w_uk.data_ptr(), w_uv.data_ptr(), gate.data_ptr(), out.data_ptr(), B, Nq, H, dq, dv, r, npg, ps,
+        block_table.shape[1], float(scale), code, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_absorb_extend_varlen_paged")
     return out
 
 

@@ -228,6 +228,35 @@ void launch_backward_bf16(const mla::BwdPrepArgs& pa, const mla::DecodeAbsorbArg
   hipLaunchKernelGGL((mla::mla_bwd_key<R>), dim3(ba.B * ba.ntb * ba.nhg), dim3(64 * mla::kBwdWaves), 0, s, ba);
 }
 
+// Varlen: the prepare kernel, then the paged prefill kernels over its block
+// list (max_blocks = ceil(Nq / rows per block) + B workgroups per head group).
+template <int DQ, int DV, int R>
+void launch_varlen_bf16(mla::PrefillArgs a, const int* cu_q, const int* seq_lens, int Nq, int max_rows,
+                        hipStream_t s) {
+  constexpr bool PAIR = R >= 256;
+  constexpr int BR = PAIR ? 32 : mla::kPrefillRows;
+  const int max_blocks = (Nq + BR - 1) / BR + a.B;
+  hipLaunchKernelGGL(mla::mla_varlen_prepare, dim3(1), dim3(256), 0, s, cu_q, seq_lens, a.B, Nq, max_rows, BR,
+                     max_blocks, const_cast<int4*>(a.seq), const_cast<int2*>(a.blocks), const_cast<int*>(a.nblocks));
+  if constexpr (PAIR) {
+    constexpr int NW = 4, NS = 2;
+    a.nhg = (a.H + NW / 2 - 1) / (NW / 2);
+    a.xcd_remap = 0;
+    hipLaunchKernelGGL((mla::mla_prefill_pair_kernel<DQ, DV, R, NW, NS, true, true>), dim3(max_blocks * a.nhg),
+                       dim3(64 * NW), 0, s, a);
+  } else {
+    a.nhg = (a.H + 3) / 4;
+    a.xcd_remap = 0;
+    hipLaunchKernelGGL((mla::mla_prefill_bf16_kernel<DQ, DV, R, true, true>), dim3(max_blocks * a.nhg),
+                       dim3(64 * mla::kPrefillWaves), 0, s, a);
+  }
+}
+
+size_t varlen_meta_bytes(int B, int Nq) {
+  const int max_blocks = (Nq + mla::kPrefillRows - 1) / mla::kPrefillRows + B;  // the larger count (16-row blocks)
+  return align_up((size_t)B * sizeof(int4)) + align_up((size_t)max_blocks * sizeof(int2)) + align_up(sizeof(int));
+}
+
 }  // namespace
 
 extern "C" {
@@ -352,6 +381,56 @@ mla_status mla_absorb_extend_paged(const void* q, const void* c_pages, const int
   if (!paged_geometry_ok(B, r, num_pages, page_size, max_pages)) return MLA_ERR_UNSUPPORTED;
   return extend_impl(q, c_pages, block_table, num_pages, page_size, max_pages, w_uk, w_uv, gate, out, nullptr, B, T,
                      S, H, d_q, d_v, r, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+size_t mla_absorb_extend_varlen_workspace_size(int B, int Nq, int H, int d_q, int r, mla_dtype dtype) {
+  if (B <= 0 || Nq <= 0 || H <= 0 || d_q <= 0 || r <= 0 || dtype != MLA_DTYPE_BF16) return kBadSize;
+  return align_up((size_t)H * r * d_q * sizeof(bf16)) + varlen_meta_bytes(B, Nq);
+}
+
+mla_status mla_absorb_extend_varlen_paged(const void* q, const void* c_pages, const int32_t* block_table,
+                                          const int32_t* cu_q, const int32_t* seq_lens, const void* w_uk,
+                                          const void* w_uv, const void* gate, void* out, int B, int Nq, int H, int d_q,
+                                          int d_v, int r, int64_t num_pages, int page_size, int max_pages, float scale,
+                                          mla_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const void* ptrs[] = {q, c_pages, block_table, cu_q, seq_lens, w_uk, w_uv, gate, out};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return MLA_ERR_INVALID_ARG;
+  if (B <= 0 || Nq <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return MLA_ERR_INVALID_ARG;
+  if (num_pages <= 0 || max_pages <= 0 || page_size < 32 || log2_exact(page_size) < 0) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_DTYPE_BF16) return dtype == MLA_DTYPE_F32 ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  if (!bf16_shape_supported(d_q, d_v, r)) return MLA_ERR_UNSUPPORTED;
+  if (!paged_geometry_ok(B, r, num_pages, page_size, max_pages) || !fits(Nq, H, d_q > d_v ? d_q : d_v))
+    return MLA_ERR_UNSUPPORTED;
+  if (((long long)Nq / 16 + B) * ((H + 1) / 2) >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
+  const size_t wt = align_up((size_t)H * r * d_q * sizeof(bf16));
+  const size_t need = wt + varlen_meta_bytes(B, Nq);
+  if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  bf16* wukT = (bf16*)ws;
+  launch_wuk_transpose((const bf16*)w_uk, wukT, H, d_q, r, s);
+
+  mla::PrefillArgs a{};
+  a.q = (const bf16*)q; a.c = (const bf16*)c_pages; a.wukT = wukT; a.wuv = (const bf16*)w_uv;
+  a.gate = (const bf16*)gate; a.out = (bf16*)out;
+  a.B = B; a.T = 0; a.S = 0; a.H = H;
+  a.qscale = scale * mla::kLog2e;
+  a.block_table = block_table; a.max_pages = max_pages; a.num_pages = (int)num_pages;
+  a.page_shift = log2_exact(page_size);
+  size_t off = wt;
+  a.seq = (const int4*)(ws + off);
+  off += align_up((size_t)B * sizeof(int4));
+  a.blocks = (const int2*)(ws + off);
+  off += align_up((size_t)((Nq + mla::kPrefillRows - 1) / mla::kPrefillRows + B) * sizeof(int2));
+  a.nblocks = (const int*)(ws + off);
+  const int max_rows = max_pages * page_size;
+  if (d_q == 16) launch_varlen_bf16<16, 16, 32>(a, cu_q, seq_lens, Nq, max_rows, s);
+  else if (d_q == 64) launch_varlen_bf16<64, 64, 256>(a, cu_q, seq_lens, Nq, max_rows, s);
+  else launch_varlen_bf16<128, 128, 512>(a, cu_q, seq_lens, Nq, max_rows, s);
+  return launch_status();
 }
 
 size_t mla_absorb_decode_workspace_size(int B, int H, int d_q, int r, int num_splits, mla_dtype dtype) {

@@ -42,18 +42,63 @@ struct PrefillArgs {
   // training: the natural-log log-sum-exp of each row's scaled scores,
   // [B, H, T] (written when non-null; the backward recomputes P from it)
   float* lse;
+  // varlen (the VARLEN instantiations, always paged): query blocks come from
+  // a list built by mla_varlen_prepare; sequence b owns packed query rows
+  // seq[b].x .. seq[b].x + seq[b].y - 1 and seq[b].z cache rows
+  const int4* seq;      // [B] {first query row, T_b, S_b, 0}
+  const int2* blocks;   // [max blocks] {b, query block}
+  const int* nblocks;   // number of valid blocks
 };
+
+// One workgroup: sanitises the varlen description (query ranges inside
+// [0, Nq), cache lengths inside [0, max_rows)) and lists the query blocks of
+// BR rows, each sequence's heaviest (last) block first.  At most max_blocks
+// entries are written.
+__global__ void __launch_bounds__(256) mla_varlen_prepare(const int* __restrict__ cu_q,
+                                                          const int* __restrict__ seq_lens, int B, int Nq,
+                                                          int max_rows, int BR, int max_blocks, int4* __restrict__ seq,
+                                                          int2* __restrict__ blocks, int* __restrict__ nblocks) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < B; base += 256) {
+    const int b = base + tid;
+    int nb = 0, q0 = 0, T = 0, S = 0;
+    if (b < B) {
+      q0 = min(max(cu_q[b], 0), Nq);
+      T = max(0, min(max(cu_q[b + 1], 0), Nq) - q0);
+      S = min(max(seq_lens[b], 0), max_rows);
+      nb = (T + BR - 1) / BR;
+      seq[b] = make_int4(q0, T, S, 0);
+    }
+    int incl = nb;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    int off = carry + incl - nb;
+    for (int u = 0; u < w; ++u) off += wsum[u];
+    for (int k = 0; k < nb; ++k)
+      if (off + k < max_blocks) blocks[off + k] = make_int2(b, nb - 1 - k);
+    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  if (tid == 0) *nblocks = min(carry, max_blocks);
+}
 
 // Issues the copies of key tile j (rows 32j .. 32j+31 of sequence b) into an
 // LDS stage: from the contiguous latent [B, S, R], or through the block table.
 template <bool PAGED, int R, int NW>
-__device__ __forceinline__ void issue_key_tile(const TileCopier<R, NW>& copier, const PrefillArgs& a, int b,
+__device__ __forceinline__ void issue_key_tile(const TileCopier<R, NW>& copier, const PrefillArgs& a, int b, int S,
                                                int j, MLA_LDS char* stage) {
   constexpr int KT = LatentTile<R>::KT;
   if constexpr (PAGED) {
     const int pos = j * KT;
     int pg = sload_i32(a.block_table + (size_t)b * a.max_pages + (pos >> a.page_shift));
-    int valid = min(a.S - pos, KT);
+    int valid = min(S - pos, KT);
     if ((unsigned)pg >= (unsigned)a.num_pages) {
       pg = 0;
       valid = 0;
@@ -61,7 +106,7 @@ __device__ __forceinline__ void issue_key_tile(const TileCopier<R, NW>& copier, 
     const size_t row = ((size_t)pg << a.page_shift) + (pos & ((1 << a.page_shift) - 1));
     copier.issue(a.c + row * R, 0, valid, stage);
   } else {
-    copier.issue(a.c + (size_t)b * a.S * R, j * KT, a.S, stage);
+    copier.issue(a.c + (size_t)b * S * R, j * KT, S, stage);
   }
 }
 
@@ -69,7 +114,7 @@ __device__ __forceinline__ void issue_key_tile(const TileCopier<R, NW>& copier, 
 constexpr int kPrefillWaves = 4;
 constexpr int kPrefillRows = 16 * (kPrefillWaves / 4);  // query positions per workgroup
 
-template <int DQ, int DV, int R, bool PAGED = false>
+template <int DQ, int DV, int R, bool PAGED = false, bool VARLEN = false>
 __global__ void __launch_bounds__(64 * kPrefillWaves)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 mla_prefill_bf16_kernel(PrefillArgs a) {
@@ -84,7 +129,14 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
   // ---- work item: heaviest query blocks first
   const int x = blockIdx.x;
   int tb, b, hg;
-  if (a.xcd_remap) {
+  if constexpr (VARLEN) {
+    hg = x % a.nhg;
+    const int i = x / a.nhg;
+    if (i >= __builtin_amdgcn_readfirstlane(*a.nblocks)) return;  // the whole workgroup
+    const int2 e = a.blocks[i];
+    b = __builtin_amdgcn_readfirstlane(e.x);
+    tb = __builtin_amdgcn_readfirstlane(e.y);
+  } else if (a.xcd_remap) {
     // gridDim.x = 8 * per; XCD x % 8 owns head groups hg = x % 8 (mod 8)
     const int xcd = x & 7, pos = x >> 3, nh8 = a.nhg >> 3;
     hg = (pos % nh8) * 8 + xcd;
@@ -104,30 +156,38 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
   const int h = hg * 4 + hw;
   const bool hvalid = h < a.H;
   const int hc = hvalid ? h : a.H - 1;
-  const int T = a.T, H = a.H;
+  const int H = a.H;
+  int T = a.T, S = a.S;
+  size_t qr0 = (size_t)b * a.T;  // packed row of query 0 of sequence b
+  if constexpr (VARLEN) {
+    const int4 sq = a.seq[b];
+    qr0 = (size_t)__builtin_amdgcn_readfirstlane(sq.x);
+    T = __builtin_amdgcn_readfirstlane(sq.y);
+    S = __builtin_amdgcn_readfirstlane(sq.z);
+  }
   const int t0 = tb * kPrefillRows;
   const int tw = t0 + 16 * th;  // first row of this wave
   const int t = tw + l16;       // this lane's query row
   const bool tvalid = t < T;
   const int tc = tvalid ? t : T - 1;
-  const int S = a.S, P = S - T;  // query t sits at position P + t
+  const int P = S - T;  // query t sits at position P + t
 
   const int ntiles = (P + min(t0 + kPrefillRows, T) + LT::KT - 1) / LT::KT;
 
   // stream the first latent tile while the absorb prologue runs
   TileCopier<R, kPrefillWaves> copier;
   copier.init(w, lane);
-  issue_key_tile<PAGED>(copier, a, b, 0, smem);
+  issue_key_tile<PAGED>(copier, a, b, S, 0, smem);
 
   WaveAttn<R> st;
-  absorb_rows<DQ, R>(a.q + (((size_t)b * T + tc) * H + hc) * DQ, a.wukT + (size_t)hc * R * DQ, a.qscale,
+  absorb_rows<DQ, R>(a.q + ((qr0 + tc) * H + hc) * DQ, a.wukT + (size_t)hc * R * DQ, a.qscale,
                      l16, kq, st.qT);
   st.reset();
   st.init_addressing(l16, kq);
 
   for (int it = 0; it < ntiles; ++it) {
     if (it + 1 < ntiles) {
-      issue_key_tile<PAGED>(copier, a, b, it + 1, smem + ((it + 1) & 1) * LT::BYTES);
+      issue_key_tile<PAGED>(copier, a, b, S, it + 1, smem + ((it + 1) & 1) * LT::BYTES);
       wait_vmcnt<LPW>();
     } else {
       wait_vmcnt<0>();
@@ -152,7 +212,7 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
   const float inv_l = 1.0f / l_tot;
   if (a.lse && kq == 0 && tvalid && hvalid)
     a.lse[((size_t)b * H + h) * T + t] = (st.m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
-  const size_t orow = ((size_t)b * T + tc) * (size_t)H * DV + (size_t)hc * DV;
+  const size_t orow = (qr0 + tc) * (size_t)H * DV + (size_t)hc * DV;
   project_gate_store<DV, R>(st.oT, inv_l, a.wuv + (size_t)hc * DV * R, a.gate + orow, a.out + orow,
                             tvalid && hvalid, l16, kq);
 }
@@ -173,7 +233,7 @@ struct PairConfig {
   static constexpr int LDS = NS * LatentTile<R>::BYTES + XBUF;   // bytes per workgroup
 };
 
-template <int DQ, int DV, int R, int NW, int NS, bool PAGED = false>
+template <int DQ, int DV, int R, int NW, int NS, bool PAGED = false, bool VARLEN = false>
 __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 mla_prefill_pair_kernel(PrefillArgs a) {
@@ -196,7 +256,14 @@ mla_prefill_pair_kernel(PrefillArgs a) {
   // ---- work item (32 positions x NW/2 heads), heaviest query blocks first
   const int x = blockIdx.x;
   int tb, b, hg;
-  if (a.xcd_remap) {
+  if constexpr (VARLEN) {
+    hg = x % a.nhg;
+    const int i = x / a.nhg;
+    if (i >= __builtin_amdgcn_readfirstlane(*a.nblocks)) return;  // the whole workgroup
+    const int2 e = a.blocks[i];
+    b = __builtin_amdgcn_readfirstlane(e.x);
+    tb = __builtin_amdgcn_readfirstlane(e.y);
+  } else if (a.xcd_remap) {
     const int xcd = x & 7, pos = x >> 3, nh8 = a.nhg >> 3;
     hg = (pos % nh8) * 8 + xcd;
     const int rest = pos / nh8;
@@ -215,7 +282,15 @@ mla_prefill_pair_kernel(PrefillArgs a) {
   const int h = hg * HPW + (w >> 1);
   const bool hvalid = h < a.H;
   const int hc = hvalid ? h : a.H - 1;
-  const int T = a.T, H = a.H;
+  const int H = a.H;
+  int T = a.T, S = a.S;
+  size_t qr0 = (size_t)b * a.T;  // packed row of query 0 of sequence b
+  if constexpr (VARLEN) {
+    const int4 sq = a.seq[b];
+    qr0 = (size_t)__builtin_amdgcn_readfirstlane(sq.x);
+    T = __builtin_amdgcn_readfirstlane(sq.y);
+    S = __builtin_amdgcn_readfirstlane(sq.z);
+  }
   const int t0 = tb * 32;
   int tq[2];
   bool tv[2];
@@ -224,19 +299,19 @@ mla_prefill_pair_kernel(PrefillArgs a) {
     tq[c] = t0 + 16 * c + l16;
     tv[c] = tq[c] < T;
   }
-  const int S = a.S, P = S - T;  // query t sits at position P + t
+  const int P = S - T;  // query t sits at position P + t
   const int ntiles = (P + min(t0 + 32, T) + LT::KT - 1) / LT::KT;
 
   TileCopier<R, NW> copier;
   copier.init(w, lane);
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
-    if (p < ntiles) issue_key_tile<PAGED>(copier, a, b, p, smem + p * LT::BYTES);
+    if (p < ntiles) issue_key_tile<PAGED>(copier, a, b, S, p, smem + p * LT::BYTES);
 
   PA st;
   {
-    const size_t q0 = (((size_t)b * T + (tv[0] ? tq[0] : T - 1)) * H + hc) * DQ;
-    const size_t q1 = (((size_t)b * T + (tv[1] ? tq[1] : T - 1)) * H + hc) * DQ;
+    const size_t q0 = ((qr0 + (tv[0] ? tq[0] : T - 1)) * H + hc) * DQ;
+    const size_t q1 = ((qr0 + (tv[1] ? tq[1] : T - 1)) * H + hc) * DQ;
     absorb_pair<DQ, R>(a.q + q0, a.q + q1, a.wukT + (size_t)hc * R * DQ, jh * PA::RH, a.qscale, l16, kq, st.qT);
   }
   st.reset();
@@ -278,7 +353,7 @@ mla_prefill_pair_kernel(PrefillArgs a) {
     // this tile rather than right after the first one, where every wave of
     // the workgroup would queue its copies at the same moment.
     if (it + NS - 1 < ntiles)
-      issue_key_tile<PAGED>(copier, a, b, it + NS - 1, smem + ((STG + NS - 1) % NS) * LT::BYTES);
+      issue_key_tile<PAGED>(copier, a, b, S, it + NS - 1, smem + ((STG + NS - 1) % NS) * LT::BYTES);
     {
       const f32x4 o00 = xbuf[(partner * 4 + 0) * 64 + lane], o01 = xbuf[(partner * 4 + 1) * 64 + lane];
       const f32x4 o10 = xbuf[(partner * 4 + 2) * 64 + lane], o11 = xbuf[(partner * 4 + 3) * 64 + lane];
@@ -350,7 +425,7 @@ mla_prefill_pair_kernel(PrefillArgs a) {
     for (int c = 0; c < 2; ++c) {
       const f32x4 o = obuf[((w0 * NV + vt) * 2 + c) * 64 + lane] + obuf[((w1 * NV + vt) * 2 + c) * 64 + lane];
       if (tv[c] && hvalid) {
-        const size_t orow = ((size_t)b * T + tq[c]) * (size_t)H * DV + (size_t)h * DV + 16 * vt + 4 * kq;
+        const size_t orow = (qr0 + tq[c]) * (size_t)H * DV + (size_t)h * DV + 16 * vt + 4 * kq;
         const bf16x4 gv = *(const bf16x4*)(a.gate + orow);
         bf16x4 ov;
 #pragma unroll

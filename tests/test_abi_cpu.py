@@ -250,3 +250,36 @@ def _append(**kw):
 ])
 def test_cache_append_rejects(kw, status):
     assert _append(**kw) == status
+
+
+def _varlen(**kw):
+    a = dict(q=FAKE, c=FAKE, bt=FAKE, cu=FAKE, lens=FAKE, w_uk=FAKE, w_uv=FAKE, gate=FAKE, out=FAKE, B=3, Nq=100, H=8,
+             dq=128, dv=128, r=512, npg=64, ps=64, mp=8, scale=0.1, dtype=mla.DTYPE_BF16, ws=FAKE, wsb=1 << 30,
+             stream=None)
+    a.update(kw)
+    return mla.lib().mla_absorb_extend_varlen_paged(a["q"], a["c"], a["bt"], a["cu"], a["lens"], a["w_uk"], a["w_uv"],
+                                                    a["gate"], a["out"], a["B"], a["Nq"], a["H"], a["dq"], a["dv"],
+                                                    a["r"], a["npg"], a["ps"], a["mp"], a["scale"], a["dtype"], a["ws"],
+                                                    a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(lens=FAKE + 4), mla.MLA_ERR_INVALID_ARG),
+    (dict(Nq=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(ps=100), mla.MLA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), mla.MLA_ERR_INVALID_ARG),
+    (dict(dtype=mla.DTYPE_F32), mla.MLA_ERR_UNSUPPORTED),
+    (dict(dq=96, dv=96, r=384), mla.MLA_ERR_UNSUPPORTED),
+    (dict(ws=None), mla.MLA_ERR_WORKSPACE),
+    (dict(wsb=1024), mla.MLA_ERR_WORKSPACE),
+])
+def test_extend_varlen_rejects(kw, status):
+    assert _varlen(**kw) == status
+
+
+def test_varlen_workspace_size():
+    n = mla.varlen_workspace_size(4, 1000, 96, 128, 512, mla.DTYPE_BF16)
+    assert n >= mla.prefill_workspace_size(1, 1, 96, 128, 512, mla.DTYPE_BF16) + 8 * (1000 // 16 + 4)
+    with pytest.raises(mla.MLAError):
+        mla.varlen_workspace_size(4, 1000, 96, 128, 512, mla.DTYPE_F32)

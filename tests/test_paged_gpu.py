@@ -204,3 +204,61 @@ def test_paged_tables_at_high_low_word_addresses(o):
     torch.cuda.synchronize()
     assert_parity(to_host_f64(out), _oracle_decode_paged(o, d, lay, pool), dg.BF16, "high-address tables")
     del buf
+
+
+def _varlen_case(S, T, H, shape, page_size, seed):
+    """Sequences with cache lengths S and chunk lengths T (T_b <= S_b) in one
+    shuffled page pool; returns packed queries, gates, the pool and tables."""
+    dq, dv, r = SHAPES[shape]
+    parts = [dg.prefill_inputs(1, s_, H, dq, dv, r, dtype=dg.BF16, seed=seed + i) for i, s_ in enumerate(S)]
+    rows = np.concatenate([p["c"][0] for p in parts])
+    lay = dg.paged_layout(S, page_size, seed=seed)
+    pool = dg.scatter_to_pages(rows, np.concatenate([[0], np.cumsum(S)]), lay)
+    q = np.ascontiguousarray(np.concatenate([p["q"][0, s_ - t_:] for p, s_, t_ in zip(parts, S, T)]))
+    g = np.ascontiguousarray(np.concatenate([p["gate"][0, s_ - t_:] for p, s_, t_ in zip(parts, S, T)]))
+    cu_q = np.concatenate([[0], np.cumsum(T)]).astype(np.int32)
+    return dict(q=q, gate=g, pool=pool, lay=lay, cu_q=cu_q, S=np.array(S, dtype=np.int32), w_uk=parts[0]["w_uk"],
+                w_uv=parts[0]["w_uv"], scale=dq ** -0.5)
+
+
+@pytest.mark.parametrize("S,T,H,shape,page_size", [
+    ([300, 1000, 5000, 64, 129], [300, 77, 1, 0, 33], 8, "full", 64),
+    ([40, 17, 100, 33], [40, 1, 60, 33], 4, "toy", 32),
+    ([257, 70, 1], [100, 70, 1], 9, "mid", 128),
+    ([4096] * 3 + [2000] * 8, [1] * 3 + [300] * 8, 96, "full", 256),
+])
+def test_extend_varlen_mixed_batch(o, S, T, H, shape, page_size):
+    """One call over a batch mixing prefills (S = T), chunks after a cached
+    prefix, decode steps (T = 1) and empty chunks."""
+    import torch
+    import rank_latent_causal_amd as mla
+    v = _varlen_case(S, T, H, shape, page_size, seed=8600 + sum(S) % 991)
+    log(f"varlen {shape} H={H} S={S[:5]} T={T[:5]} page {page_size}")
+    out = mla.mla_absorb_extend_varlen_paged(to_dev(v["q"]), to_dev(v["pool"]), to_dev(v["lay"]["block_table"]),
+                                             to_dev(v["cu_q"]), to_dev(v["S"]), to_dev(v["w_uk"]), to_dev(v["w_uv"]),
+                                             to_dev(v["gate"]), v["scale"])
+    torch.cuda.synchronize()
+    f = dg.as_f32
+    ref = o.extend_varlen_paged(f(v["q"]), f(v["pool"]), v["lay"]["block_table"], v["cu_q"], v["S"], f(v["w_uk"]),
+                                f(v["w_uv"]), f(v["gate"]), v["scale"])
+    assert_parity(to_host_f64(out), ref, dg.BF16, "varlen")
+
+
+def test_extend_varlen_clamps_bad_ranges(o):
+    """Descriptions that break the preconditions (a query range past Nq, a
+    cache length past the table) are clamped on the device: the call stays
+    inside its buffers and the well-formed sequences are unaffected."""
+    import torch
+    import rank_latent_causal_amd as mla
+    v = _varlen_case([100, 64], [30, 20], 8, "mid", 64, seed=8700)
+    cap = v["lay"]["max_pages"] * 64
+    cu_bad = np.array([0, 30, 50 + 1000], dtype=np.int32)  # the last range runs past Nq = 50
+    S_bad = np.array([100, cap + 500], dtype=np.int32)
+    out = mla.mla_absorb_extend_varlen_paged(to_dev(v["q"]), to_dev(v["pool"]), to_dev(v["lay"]["block_table"]),
+                                             to_dev(cu_bad), to_dev(S_bad), to_dev(v["w_uk"]), to_dev(v["w_uv"]),
+                                             to_dev(v["gate"]), v["scale"])
+    torch.cuda.synchronize()
+    f = dg.as_f32
+    ref = o.extend_varlen_paged(f(v["q"]), f(v["pool"]), v["lay"]["block_table"], v["cu_q"], v["S"], f(v["w_uk"]),
+                                f(v["w_uv"]), f(v["gate"]), v["scale"])
+    assert_parity(to_host_f64(out)[:30], ref[:30], dg.BF16, "well-formed sequence next to bad ranges")
