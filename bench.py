@@ -13,7 +13,8 @@ algorithmic FLOPs), chunked-prefill TFLOP/s, decode latent-cache GB/s
 peaks, and the CPU oracle timed on a bounded row sample of the prefill.  The
 full-layer forward (projections, norms, core, output projection at the full
 K3 widths, B=1, T=8192) is timed separately after the steps and reported
-under "forward"; the backward of the prefill core (with the log-sum-exp of a
+under "forward"; a varlen batch of four chunks over a paged cache under
+"extend_varlen"; the backward of the prefill core (with the log-sum-exp of a
 training forward run before it) likewise under "backward".  The decode over a paged cache (the decode workload in
 shuffled 64-row pages) runs in each step right after the packed decode and
 is reported under "decode_paged".  Neither is part of ms_per_step.
@@ -222,6 +223,45 @@ def bench_backward(torch, mla, steps, warmup):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flop_per_launch": f}}
 
 
+def bench_varlen(torch, mla, steps, warmup, page_size=64):
+    """A mixed chunk batch at full width in one varlen call over a paged
+    cache: chunks of 2048, 1024, 512 and 256 queries after 6144, 3072, 7680
+    and 1792 cached positions (H=96, d=128, r=512), pages of 64 rows."""
+    S = [8192, 4096, 8192, 2048]
+    T = [2048, 1024, 512, 256]
+    H, dq, dv, r = 96, 128, 128, 512
+    seed = dg.WORKLOADS["full_prefill"]["seed"] + 100
+    parts = [dg.prefill_inputs(1, s_, H, dq, dv, r, dtype=dg.BF16, seed=seed + i) for i, s_ in enumerate(S)]
+    lay = dg.paged_layout(S, page_size, seed=seed)
+    pool = dg.scatter_to_pages(np.concatenate([p["c"][0] for p in parts]), np.concatenate([[0], np.cumsum(S)]), lay)
+    q = np.concatenate([p["q"][0, s_ - t_:] for p, s_, t_ in zip(parts, S, T)])
+    g = np.concatenate([p["gate"][0, s_ - t_:] for p, s_, t_ in zip(parts, S, T)])
+    cu = np.concatenate([[0], np.cumsum(T)]).astype(np.int32)
+    args = [dev(q), dev(pool), dev(lay["block_table"]), dev(cu), dev(np.array(S, dtype=np.int32)),
+            dev(parts[0]["w_uk"]), dev(parts[0]["w_uv"]), dev(g)]
+    scale = dq ** -0.5
+    out = torch.empty((int(cu[-1]), H * dv), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.varlen_workspace_size(len(S), int(cu[-1]), H, dq, r, mla.DTYPE_BF16), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(warmup):
+        mla.mla_absorb_extend_varlen_paged(*args, scale, out=out, workspace=ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        mla.mla_absorb_extend_varlen_paged(*args, scale, out=out, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    f = sum(extend_flops(1, t_, s_, H, dq, dv, r) for s_, t_ in zip(S, T))
+    tf = f / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+            "workload": "varlen chunk batch T=[2048,1024,512,256] after S-T cached of S=[8192,4096,8192,2048], "
+                        "H=96, d_q=d_v=128, r=512, 64-row shuffled pages",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flop_per_launch": f}}
+
+
 def setup_decode_paged(torch, mla, dec, page_size=64):
     """The full decode workload with its cache in shuffled 64-row pages.
     Returns (launch, report): launch() enqueues one call; report(ms) builds
@@ -392,6 +432,8 @@ def main():
                                       "traffic": None, "flop_per_launch": xf}}
     if do_dec:
         res["decode_paged"] = paged[1](float(np.mean([e[6].elapsed_time(e[7]) for e in evs])))
+    if args.which in ("both", "prefill"):
+        res["extend_varlen"] = bench_varlen(torch, mla, args.steps, args.warmup)
     if args.which in ("both", "forward"):
         res["forward"] = bench_forward(torch, mla, args.steps, args.warmup)
     if args.which in ("both", "backward"):
