@@ -246,20 +246,25 @@ mla_bwd_query(BwdArgs a) {
 }
 
 // ----------------------------------------------------------------- key side
-// Workgroup (batch b, 32 keys k0.., head group hg), 8 waves, blocks with the
-// most query blocks first.  Steps run over (head h of the group, query block
-// qb >= the key block); a step stages the q_abs2 and dol tiles of (h, qb) and
-// their {lse log2 e, D} pairs in LDS (two stages, one step of lookahead).
-// Waves 0-3 form S2^T tiles and waves 4-7 dP^T tiles, with the key rows of c
-// as A operands held in VGPRs; every thread makes two elements of P and
-// dS ln 2 (key-major bf16 rows); wave w accumulates dc^T for latent tiles w,
-// w+8, ...:  dc^T += q_abs2^T dS^T + dol^T P^T  (q_abs2 carries
-// scale log2 e, so dS ln 2 gives the scale dS a term).
+// Workgroup (batch b, 64 keys k0.., head group hg), 8 waves, blocks with the
+// most query blocks first.  Steps run over (head h of the group, 32-query
+// block qb from the one holding key k0 on); a step stages the q_abs2 and dol
+// tiles of (h, qb) and their {lse log2 e, D} pairs in LDS (two stages, one
+// step of lookahead).  Wave w owns the 16x16 tile (keys 16 (w/2) .., queries
+// 16 (w%2) ..) of both S2^T and dP^T: the key rows of c are its MFMA A
+// operand for both products (held in VGPRs), so P and dS ln 2 are formed in
+// registers and written once as key-major bf16 rows.  Wave w then
+// accumulates dc^T for latent tiles w, w+8, ... over all 64 keys:
+//   dc^T += q_abs2^T (dS ln 2)^T + dol^T P^T
+// (q_abs2 carries scale log2 e, so dS ln 2 gives the scale dS a term).
+constexpr int kBwdKeys = 64;
+
 template <int R>
 struct BwdKeyConfig {
   static constexpr int LDB = 256;                                    // {L2, D} x 32 queries
   static constexpr int STAGE = 2 * LatentTile<R>::BYTES + LDB;
-  static constexpr int LDS = 2 * STAGE + kBwdXBytes;
+  static constexpr int PBYTES = kBwdKeys * kPPitch * 2;             // one bf16 [64][40] array
+  static constexpr int LDS = 2 * STAGE + 2 * PBYTES;
 };
 
 template <int R>
@@ -269,28 +274,28 @@ mla_bwd_key(BwdArgs a) {
   using CFG = BwdKeyConfig<R>;
   constexpr int NKK = R / 32, NJT = R / 16;
   constexpr int JPW = (NJT + kBwdWaves - 1) / kBwdWaves;
-  constexpr int CPW = copies_per_wave<R>(kBwdWaves);
+  constexpr int KTS = kBwdKeys / 16;  // 16-key tiles
   static_assert(LT::COPIES % kBwdWaves == 0 || LT::COPIES < kBwdWaves, "copy split");
+  static_assert(KTS * 2 == kBwdWaves, "one (key tile, query tile) pair per wave");
   __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
-  float* xS = (float*)(smem_raw + 2 * CFG::STAGE);
-  float* xP = xS + 32 * kXPitch;
-  bf16* Pb = (bf16*)(xP + 32 * kXPitch);
-  bf16* dSb = Pb + 32 * kPPitch;
+  bf16* Pb = (bf16*)(smem_raw + 2 * CFG::STAGE);
+  bf16* dSb = Pb + kBwdKeys * kPPitch;
 
   const int x = blockIdx.x;
   const int hg = x % a.nhg, rest = x / a.nhg;
   const int b = rest % a.B, kb = rest / a.B;
-  const int T = a.T, k0 = kb * 32;
+  const int T = a.T, k0 = kb * kBwdKeys;
   const int h0 = hg * a.hpg, nh = min(a.hpg, a.H - h0);
-  const int nq = a.ntb - kb;
+  const int qb0 = k0 / 32;
+  const int nq = a.ntb - qb0;
   const int nsteps = nh * nq;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, kq = lane >> 4;
-  const int role = w >> 2, kt = (w >> 1) & 1, qt = w & 1;
+  const int kt = w >> 1, qt = w & 1;
   const size_t BT = (size_t)a.B * T;
 
-  // A operand: key rows kt*16 + l16 of c
+  // A operand: key rows 16 kt + l16 of c
   bf16x8 aop[NKK];
   {
     const int tk = min(k0 + 16 * kt + l16, T - 1);
@@ -298,17 +303,18 @@ mla_bwd_key(BwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) aop[kk] = *(const bf16x8*)(src + 32 * kk);
   }
-  const int ek = threadIdx.x >> 4, eq = 2 * (threadIdx.x & 15);
 
-  f32x4 acc[JPW][2];
+  f32x4 acc[JPW][KTS];
 #pragma unroll
-  for (int j = 0; j < JPW; ++j) acc[j][0] = acc[j][1] = f32x4{};
+  for (int j = 0; j < JPW; ++j)
+#pragma unroll
+    for (int t = 0; t < KTS; ++t) acc[j][t] = f32x4{};
 
   TileCopier<R, kBwdWaves> copier;
   copier.init(w, lane);
   auto stage = [&](int st) { return smem + st * CFG::STAGE; };
   auto issue_step = [&](int s, MLA_LDS char* dst) {
-    const int h = h0 + s / nq, qb = kb + s % nq;
+    const int h = h0 + s / nq, qb = qb0 + s % nq;
     const size_t r0 = (size_t)h * BT + (size_t)b * T;  // row t = 0 of (h, b)
     copier.issue(a.qabs + r0 * R, qb * 32, T, dst);
     copier.issue(a.dolat + r0 * R, qb * 32, T, dst + LT::BYTES);
@@ -318,59 +324,44 @@ mla_bwd_key(BwdArgs a) {
       buf2lds16(rs, (unsigned)(lane * 16), dst + 2 * LT::BYTES);
     }
   };
-  (void)CPW;
   if (nsteps > 0) issue_step(0, stage(0));
 
   for (int s = 0; s < nsteps; ++s) {
     wait_vmcnt<0>();
-    wg_barrier();  // step s staged; step s-1 done everywhere (its stage and the exchange are free)
+    wg_barrier();  // step s staged; step s-1 done everywhere (its stage and the P / dS rows are free)
     if (s + 1 < nsteps) issue_step(s + 1, stage((s + 1) & 1));
     const MLA_LDS char* tq_tile = stage(s & 1);
     const MLA_LDS char* td_tile = tq_tile + LT::BYTES;
     const float* ldst = (const float*)(smem_raw + (s & 1) * CFG::STAGE + 2 * LT::BYTES);
-    const int qb = kb + s % nq;
+    const int qb = qb0 + s % nq;
 
-    // S2^T or dP^T tile (kt, qt): rows key kt*16 + 4kq + i, column query qt*16 + l16
-    const MLA_LDS char* src = role ? td_tile : tq_tile;
-    f32x4 sacc = f32x4{};
+    // S2^T and dP^T tile (kt, qt): rows key 16 kt + 4 kq + i, column query 16 qt + l16
+    f32x4 sacc = f32x4{}, dacc = f32x4{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const bf16x8 bq = lds_read_b128(src + tile_off<R>(16 * qt + l16, 4 * kk + kq));
-      sacc = mfma16(aop[kk], bq, sacc);
+      const int off = tile_off<R>(16 * qt + l16, 4 * kk + kq);
+      sacc = mfma16(aop[kk], lds_read_b128(tq_tile + off), sacc);
+      dacc = mfma16(aop[kk], lds_read_b128(td_tile + off), dacc);
     }
     {
-      float* xd = role ? xP : xS;
+      const int q = 16 * qt + l16, qpos = qb * 32 + q;
+      const float L2 = ldst[2 * q], Dq = ldst[2 * q + 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xd[(16 * kt + 4 * kq + i) * kXPitch + 16 * qt + l16] = sacc[i];
-    }
-    wait_lgkmcnt0();
-    wg_barrier();
-
-    {
-      const int kpos = k0 + ek;
-      bf16 pv[2], dv2[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int q = eq + u, qpos = qb * 32 + q;
-        const float s2 = xS[ek * kXPitch + q], dp = xP[ek * kXPitch + q];
-        const float L2 = ldst[2 * q], Dq = ldst[2 * q + 1];
-        const float p = (kpos <= qpos && qpos < T) ? fast_exp2(s2 - L2) : 0.0f;
-        pv[u] = (bf16)p;
-        dv2[u] = (bf16)(p * (dp - Dq) * 0.69314718055994531f);
+      for (int i = 0; i < 4; ++i) {
+        const int kr = 16 * kt + 4 * kq + i, kpos = k0 + kr;
+        const float p = (kpos <= qpos && qpos < T) ? fast_exp2(sacc[i] - L2) : 0.0f;
+        Pb[kr * kPPitch + q] = (bf16)p;
+        dSb[kr * kPPitch + q] = (bf16)(p * (dacc[i] - Dq) * 0.69314718055994531f);
       }
-      Pb[ek * kPPitch + eq] = pv[0];
-      Pb[ek * kPPitch + eq + 1] = pv[1];
-      dSb[ek * kPPitch + eq] = dv2[0];
-      dSb[ek * kPPitch + eq + 1] = dv2[1];
     }
     wait_lgkmcnt0();
     wg_barrier();
 
-    bf16x8 bS[2], bP[2];
+    bf16x8 bS[KTS], bP[KTS];
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      bS[c2] = *(const bf16x8*)&dSb[(16 * c2 + l16) * kPPitch + 8 * kq];
-      bP[c2] = *(const bf16x8*)&Pb[(16 * c2 + l16) * kPPitch + 8 * kq];
+    for (int t = 0; t < KTS; ++t) {
+      bS[t] = *(const bf16x8*)&dSb[(16 * t + l16) * kPPitch + 8 * kq];
+      bP[t] = *(const bf16x8*)&Pb[(16 * t + l16) * kPPitch + 8 * kq];
     }
 #pragma unroll
     for (int j = 0; j < JPW; ++j) {
@@ -379,24 +370,24 @@ mla_bwd_key(BwdArgs a) {
         const bf16x8 aq = tile_column_operand<R>(tq_tile, jt, l16, kq);
         const bf16x8 ad = tile_column_operand<R>(td_tile, jt, l16, kq);
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          acc[j][c2] = mfma16(aq, bS[c2], acc[j][c2]);
-          acc[j][c2] = mfma16(ad, bP[c2], acc[j][c2]);
+        for (int t = 0; t < KTS; ++t) {
+          acc[j][t] = mfma16(aq, bS[t], acc[j][t]);
+          acc[j][t] = mfma16(ad, bP[t], acc[j][t]);
         }
       }
     }
   }
 
-  // epilogue: fragment (j, c2) holds latent dims 16 jt + 4 kq + e of key 16 c2 + l16
+  // epilogue: fragment (j, t) holds latent dims 16 jt + 4 kq + e of key 16 t + l16
 #pragma unroll
   for (int j = 0; j < JPW; ++j) {
     const int jt = w + kBwdWaves * j;
     if (jt >= NJT) continue;
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const int tk = k0 + 16 * c2 + l16;
+    for (int t = 0; t < KTS; ++t) {
+      const int tk = k0 + 16 * t + l16;
       if (tk >= T) continue;
-      *(f32x4*)(a.dc_part + ((size_t)hg * BT + (size_t)b * T + tk) * R + 16 * jt + 4 * kq) = acc[j][c2];
+      *(f32x4*)(a.dc_part + ((size_t)hg * BT + (size_t)b * T + tk) * R + 16 * jt + 4 * kq) = acc[j][t];
     }
   }
 }

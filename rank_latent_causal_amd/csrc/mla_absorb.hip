@@ -225,7 +225,8 @@ void launch_backward_bf16(const mla::BwdPrepArgs& pa, const mla::DecodeAbsorbArg
   hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(qa.H * (R / JC)), dim3(256), 0, s, qa);
   hipLaunchKernelGGL((mla::mla_decode_absorb<DV, R>), dim3(va.H * (R / JC)), dim3(256), 0, s, va);
   hipLaunchKernelGGL((mla::mla_bwd_query<R>), dim3(ba.B * ba.ntb * ba.H), dim3(64 * mla::kBwdWaves), 0, s, ba);
-  hipLaunchKernelGGL((mla::mla_bwd_key<R>), dim3(ba.B * ba.ntb * ba.nhg), dim3(64 * mla::kBwdWaves), 0, s, ba);
+  const int nkb = (ba.T + mla::kBwdKeys - 1) / mla::kBwdKeys;
+  hipLaunchKernelGGL((mla::mla_bwd_key<R>), dim3(ba.B * nkb * ba.nhg), dim3(64 * mla::kBwdWaves), 0, s, ba);
 }
 
 // Varlen: the prepare kernel, then the paged prefill kernels over its block
