@@ -9,20 +9,21 @@
 //   dol = do W_UV                               D_t = sum_v dout out  (= dol . ol)
 //   dS = P (dol c^T - D)                        da = scale dS c
 //   dc = scale dS^T a + P^T dol                 dq = da W_UK^T
-//   dW_UK = sum_t q_t^T da_t                    dW_UV = sum_t do_t^T ol_t
+//   dW_UK = sum_t q_t^T da_t                    dW_UV = sum_t do_t^T ol_t = sum_s dV_s^T c_s
+// with dV_s = sum_t P_ts do_t (the value gradient of the decompressed form).
 //
 // Kernels (in call order):
 //   mla_bwd_prep     dg, do and the per-row pair {lse log2 e, D}
 //   absorb (decode)  q_abs2 = scale log2e q W_UK and dol = do W_UV, head-major
-//   mla_bwd_query    per (32 queries, head): da and ol over the key tiles
-//   mla_bwd_key      per (32 keys, head group): partial dc over the query
-//                    blocks at or after the keys
+//   mla_bwd_query    per (32 queries, head): da over the key tiles
+//   mla_bwd_key      per (64 keys, head group): partial dc and, per head, dV
+//                    over the query blocks at or after the keys
 //   mla_bwd_dc_sum   dc = sum of the head-group partials
-//   GEMMs            dq = da W_UK^T (NT), dW_UK and dW_UV (TN)
+//   GEMMs            dq = da W_UK^T (NT), dW_UK = q^T da and dW_UV = dV^T c (TN)
 //
-// Head-major rows: q_abs2, dol, da and ol are [H, B*T, R], so the 32 rows of
-// one (head, block) are one contiguous 32-row tile, copied like a latent
-// tile.  The scores of the forward are recomputed from q_abs2 and c with the
+// Head-major rows: q_abs2, dol and da are [H, B*T, R], do and dV [H, B*T, DV],
+// so the 32 rows of one (head, block) are one contiguous 32-row tile, copied
+// like a latent tile.  The scores of the forward are recomputed from q_abs2 and c with the
 // forward's log-sum-exp, P = exp2(S2 - lse log2 e).
 #pragma once
 
@@ -35,8 +36,9 @@ struct BwdArgs {
   const bf16* qabs;   // [H, B*T, R]  scale * log2(e) * q W_UK
   const bf16* dolat;  // [H, B*T, R]  do W_UV
   const float* ld;    // [H, B*T, 2]  {lse * log2(e), D}
+  const bf16* dov;    // [H, B*T, DV] do = dout * sigmoid(g)
   bf16* da;           // [H, B*T, R]
-  bf16* ol;           // [H, B*T, R]
+  bf16* dv;           // [H, B*T, DV] dV
   float* dc_part;     // [nhg, B*T, R]
   int B, T, H;
   float scale;
@@ -70,7 +72,7 @@ struct BwdPrepArgs {
   const bf16* dout;   // [B*T, H*DV]
   const float* lse;   // [B, H, T]    forward log-sum-exp (natural log)
   bf16* dgate;        // [B*T, H*DV]
-  bf16* dov;          // [B*T, H, DV] do = dout * sigmoid(g)
+  bf16* dov;          // [H, B*T, DV] do = dout * sigmoid(g)
   float* ld;          // [H, B*T, 2]
   int B, T, H, DV;
 };
@@ -88,7 +90,7 @@ __global__ void __launch_bounds__(256) mla_bwd_prep(BwdPrepArgs a) {
       const float g = (float)a.gate[i], o = (float)a.out[i], d = (float)a.dout[i];
       const float s = sigmoidf_(g);
       a.dgate[i] = (bf16)(d * o * (1.0f - s));
-      a.dov[i] = (bf16)(d * s);
+      a.dov[((size_t)h * a.B * a.T + bt) * a.DV + v] = (bf16)(d * s);
       dsum += d * o;
     }
 #pragma unroll
@@ -103,121 +105,113 @@ __global__ void __launch_bounds__(256) mla_bwd_prep(BwdPrepArgs a) {
 
 // ----------------------------------------------------------------- query side
 // Workgroup (batch b, 32 queries t0.., head h), 8 waves, heaviest blocks
-// first.  Per key tile: waves 0-3 form the four 16x16 tiles of S2 = q_abs2
-// c^T and waves 4-7 those of dP = dol c^T (the query rows are MFMA A operands
-// held in VGPRs); every thread then turns two of the 32x32 elements into P and
-// dS (bf16 in LDS); wave w accumulates da^T and ol^T for latent tiles w,
-// w+8, ... with c^T from transposing reads.  Two LDS stages, one tile of
-// lookahead.
+// first.  A step covers 64 keys (two 32-row latent tiles per LDS stage, two
+// stages, one step of lookahead).  Wave w owns the 16x16 tile (queries
+// 16 (w%2) .., keys 16 (w/2) ..) of both S2 = q_abs2 c^T and dP = dol c^T:
+// the key rows of c are the shared B operand, the wave's q_abs2 and dol rows
+// are its A operands (held in VGPRs), so P and dS are formed in registers and
+// written once as query-major bf16 rows.  Wave w then accumulates da^T for
+// latent tiles w, w+8, ...: da^T += c^T dS^T over the 64 keys, c^T from
+// transposing reads of the tiles.
+constexpr int kBwdQKeys = 64;
+constexpr int kDSPitch = kBwdQKeys + 8;  // bf16 dS rows (elements), 144 bytes
+
 template <int R>
 __global__ void __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mla_bwd_query(BwdArgs a) {
   using LT = LatentTile<R>;
   constexpr int NKK = R / 32, NJT = R / 16;
   constexpr int JPW = (NJT + kBwdWaves - 1) / kBwdWaves;
+  constexpr int SUB = kBwdQKeys / LT::KT;  // latent tiles per step
+  constexpr int STAGE = SUB * LT::BYTES;
   static_assert(LT::COPIES % kBwdWaves == 0 || LT::COPIES < kBwdWaves, "copy split");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * LT::BYTES + kBwdXBytes];
+  static_assert(SUB == 2, "two 32-row tiles per step");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE + 32 * kDSPitch * 2];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
-  float* xS = (float*)(smem_raw + 2 * LT::BYTES);
-  float* xP = xS + 32 * kXPitch;
-  bf16* Pb = (bf16*)(xP + 32 * kXPitch);
-  bf16* dSb = Pb + 32 * kPPitch;
+  bf16* dSb = (bf16*)(smem_raw + 2 * STAGE);
 
   const int x = blockIdx.x;
   const int h = x % a.H, rest = x / a.H;
   const int b = rest % a.B, tb = a.ntb - 1 - rest / a.B;
   const int T = a.T, t0 = tb * 32;
-  const int ntiles = (min(t0 + 32, T) + LT::KT - 1) / LT::KT;
+  const int nsteps = (min(t0 + 32, T) + kBwdQKeys - 1) / kBwdQKeys;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l16 = lane & 15, kq = lane >> 4;
-  const int role = w >> 2, qt = (w >> 1) & 1, kt = w & 1;
+  const int qt = w & 1, kt = w >> 1;  // query tile, 16-key tile of the step
   const size_t hrow = (size_t)h * a.B * T + (size_t)b * T;  // head-major row of (b, t = 0)
 
-  // the A operand rows (query qt*16 + l16) of this wave's product
-  bf16x8 aop[NKK];
+  // A operands: query rows 16 qt + l16 of q_abs2 and dol
+  bf16x8 aq[NKK], ad[NKK];
   {
-    const int tq = min(t0 + 16 * qt + l16, T - 1);
-    const bf16* src = (role ? a.dolat : a.qabs) + (hrow + tq) * R + 8 * kq;
+    const size_t row = (hrow + min(t0 + 16 * qt + l16, T - 1)) * R + 8 * kq;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) aop[kk] = *(const bf16x8*)(src + 32 * kk);
+    for (int kk = 0; kk < NKK; ++kk) {
+      aq[kk] = *(const bf16x8*)(a.qabs + row + 32 * kk);
+      ad[kk] = *(const bf16x8*)(a.dolat + row + 32 * kk);
+    }
   }
-  // elementwise phase: thread -> query eq, keys ek, ek + 1 of the tile
-  const int eq = threadIdx.x >> 4, ek = 2 * (threadIdx.x & 15);
-  const int tq_e = t0 + eq;
-  float L2, Dq;
-  {
-    const float* p = a.ld + (hrow + min(tq_e, T - 1)) * 2;
-    L2 = p[0];
-    Dq = p[1];
+  // {lse log2 e, D} of this lane's fragment rows: queries 16 qt + 4 kq + i
+  float L2[4], Dq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float* p = a.ld + (hrow + min(t0 + 16 * qt + 4 * kq + i, T - 1)) * 2;
+    L2[i] = p[0];
+    Dq[i] = p[1];
   }
 
-  f32x4 accd[JPW][2], acco[JPW][2];
+  f32x4 acc[JPW][2];
 #pragma unroll
-  for (int j = 0; j < JPW; ++j)
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) accd[j][c2] = acco[j][c2] = f32x4{};
+  for (int j = 0; j < JPW; ++j) acc[j][0] = acc[j][1] = f32x4{};
 
   TileCopier<R, kBwdWaves> copier;
   copier.init(w, lane);
   const bf16* cb = a.c + (size_t)b * T * R;
-  copier.issue(cb, 0, T, smem);
+  auto issue_step = [&](int it, MLA_LDS char* dst) {
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) copier.issue(cb, it * kBwdQKeys + u * LT::KT, T, dst + u * LT::BYTES);
+  };
+  issue_step(0, smem);
 
-  for (int it = 0; it < ntiles; ++it) {
+  for (int it = 0; it < nsteps; ++it) {
     wait_vmcnt<0>();
-    wg_barrier();  // tile it visible; the previous tile's update is done everywhere
-    if (it + 1 < ntiles) copier.issue(cb, (it + 1) * LT::KT, T, smem + ((it + 1) & 1) * LT::BYTES);
-    const MLA_LDS char* tile = smem + (it & 1) * LT::BYTES;
+    wg_barrier();  // step it staged; the previous step's update is done everywhere
+    if (it + 1 < nsteps) issue_step(it + 1, smem + ((it + 1) & 1) * STAGE);
+    const MLA_LDS char* st = smem + (it & 1) * STAGE;
+    const MLA_LDS char* ktile = st + (kt >> 1) * LT::BYTES;  // the 32-row tile holding key tile kt
 
-    // S2 or dP tile (qt, kt): rows query qt*16 + 4kq + i, column key kt*16 + l16
-    f32x4 sacc = f32x4{};
+    // S2 and dP tile (qt, kt): rows query 16 qt + 4 kq + i, column key 16 kt + l16
+    f32x4 sacc = f32x4{}, dacc = f32x4{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const bf16x8 bk = lds_read_b128(tile + tile_off<R>(16 * kt + l16, 4 * kk + kq));
-      sacc = mfma16(aop[kk], bk, sacc);
+      const bf16x8 bk = lds_read_b128(ktile + tile_off<R>(16 * (kt & 1) + l16, 4 * kk + kq));
+      sacc = mfma16(aq[kk], bk, sacc);
+      dacc = mfma16(ad[kk], bk, dacc);
     }
     {
-      float* xd = role ? xP : xS;
+      const int kc = 16 * kt + l16, kpos = it * kBwdQKeys + kc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xd[(16 * qt + 4 * kq + i) * kXPitch + 16 * kt + l16] = sacc[i];
-    }
-    wait_lgkmcnt0();
-    wg_barrier();
-
-    {
-      const int s0 = it * LT::KT;
-      bf16 pv[2], dv2[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int k = ek + u;
-        const float s2 = xS[eq * kXPitch + k], dp = xP[eq * kXPitch + k];
-        const float p = (s0 + k <= tq_e) ? fast_exp2(s2 - L2) : 0.0f;
-        pv[u] = (bf16)p;
-        dv2[u] = (bf16)(p * (dp - Dq));
+      for (int i = 0; i < 4; ++i) {
+        const int qr = 16 * qt + 4 * kq + i, qpos = t0 + qr;
+        const float p = (kpos <= qpos) ? fast_exp2(sacc[i] - L2[i]) : 0.0f;
+        dSb[qr * kDSPitch + kc] = (bf16)(p * (dacc[i] - Dq[i]));
       }
-      Pb[eq * kPPitch + ek] = pv[0];
-      Pb[eq * kPPitch + ek + 1] = pv[1];
-      dSb[eq * kPPitch + ek] = dv2[0];
-      dSb[eq * kPPitch + ek + 1] = dv2[1];
     }
     wait_lgkmcnt0();
     wg_barrier();
 
-    // da^T, ol^T += c^T [16 latent x 32 keys] x {dS, P}^T [32 keys x 16 queries]
-    bf16x8 bS[2], bP[2];
+    // da^T += c^T [16 latent x 32 keys] x dS^T [32 keys x 16 queries], two key halves
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      bS[c2] = *(const bf16x8*)&dSb[(16 * c2 + l16) * kPPitch + 8 * kq];
-      bP[c2] = *(const bf16x8*)&Pb[(16 * c2 + l16) * kPPitch + 8 * kq];
-    }
+    for (int u = 0; u < SUB; ++u) {
+      bf16x8 bS[2];
 #pragma unroll
-    for (int j = 0; j < JPW; ++j) {
-      const int jt = w + kBwdWaves * j;
-      if (jt < NJT) {
-        const bf16x8 ac = tile_column_operand<R>(tile, jt, l16, kq);
+      for (int c2 = 0; c2 < 2; ++c2) bS[c2] = *(const bf16x8*)&dSb[(16 * c2 + l16) * kDSPitch + 32 * u + 8 * kq];
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          accd[j][c2] = mfma16(ac, bS[c2], accd[j][c2]);
-          acco[j][c2] = mfma16(ac, bP[c2], acco[j][c2]);
+      for (int j = 0; j < JPW; ++j) {
+        const int jt = w + kBwdWaves * j;
+        if (jt < NJT) {
+          const bf16x8 ac = tile_column_operand<R>(st + u * LT::BYTES, jt, l16, kq);
+          acc[j][0] = mfma16(ac, bS[0], acc[j][0]);
+          acc[j][1] = mfma16(ac, bS[1], acc[j][1]);
         }
       }
     }
@@ -232,15 +226,10 @@ mla_bwd_query(BwdArgs a) {
     for (int c2 = 0; c2 < 2; ++c2) {
       const int tq = t0 + 16 * c2 + l16;
       if (tq >= T) continue;
-      bf16x4 vd, vo;
+      bf16x4 vd;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vd[e] = (bf16)(accd[j][c2][e] * a.scale);
-        vo[e] = (bf16)acco[j][c2][e];
-      }
-      const size_t off = (hrow + tq) * R + 16 * jt + 4 * kq;
-      *(bf16x4*)(a.da + off) = vd;
-      *(bf16x4*)(a.ol + off) = vo;
+      for (int e = 0; e < 4; ++e) vd[e] = (bf16)(acc[j][c2][e] * a.scale);
+      *(bf16x4*)(a.da + (hrow + tq) * R + 16 * jt + 4 * kq) = vd;
     }
   }
 }
@@ -256,27 +245,34 @@ mla_bwd_query(BwdArgs a) {
 // registers and written once as key-major bf16 rows.  Wave w then
 // accumulates dc^T for latent tiles w, w+8, ... over all 64 keys:
 //   dc^T += q_abs2^T (dS ln 2)^T + dol^T P^T
-// (q_abs2 carries scale log2 e, so dS ln 2 gives the scale dS a term).
+// (q_abs2 carries scale log2 e, so dS ln 2 gives the scale dS a term), and
+// dV^T for value tile w: dV^T += do^T P^T, stored per head when the head's
+// last query block is done (do is staged with the step's tiles).
 constexpr int kBwdKeys = 64;
 
-template <int R>
+template <int DV, int R>
 struct BwdKeyConfig {
   static constexpr int LDB = 256;                                    // {L2, D} x 32 queries
-  static constexpr int STAGE = 2 * LatentTile<R>::BYTES + LDB;
+  static constexpr int DOB = LatentTile<DV>::BYTES;                  // do tile, 32 x DV
+  static constexpr int STAGE = 2 * LatentTile<R>::BYTES + DOB + LDB;
   static constexpr int PBYTES = kBwdKeys * kPPitch * 2;             // one bf16 [64][40] array
   static constexpr int LDS = 2 * STAGE + 2 * PBYTES;
 };
 
-template <int R>
+template <int DV, int R>
 __global__ void __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mla_bwd_key(BwdArgs a) {
   using LT = LatentTile<R>;
-  using CFG = BwdKeyConfig<R>;
+  using LV = LatentTile<DV>;
+  using CFG = BwdKeyConfig<DV, R>;
+  constexpr int NVT = DV / 16;  // value tiles: wave w < NVT owns tile w
   constexpr int NKK = R / 32, NJT = R / 16;
   constexpr int JPW = (NJT + kBwdWaves - 1) / kBwdWaves;
   constexpr int KTS = kBwdKeys / 16;  // 16-key tiles
   static_assert(LT::COPIES % kBwdWaves == 0 || LT::COPIES < kBwdWaves, "copy split");
   static_assert(KTS * 2 == kBwdWaves, "one (key tile, query tile) pair per wave");
+  static_assert(NVT <= kBwdWaves, "one value tile per wave at most");
+  static_assert(LV::COPIES % kBwdWaves == 0 || LV::COPIES < kBwdWaves, "copy split");
   __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
   bf16* Pb = (bf16*)(smem_raw + 2 * CFG::STAGE);
@@ -304,24 +300,29 @@ mla_bwd_key(BwdArgs a) {
     for (int kk = 0; kk < NKK; ++kk) aop[kk] = *(const bf16x8*)(src + 32 * kk);
   }
 
-  f32x4 acc[JPW][KTS];
+  f32x4 acc[JPW][KTS], accv[KTS];
 #pragma unroll
   for (int j = 0; j < JPW; ++j)
 #pragma unroll
     for (int t = 0; t < KTS; ++t) acc[j][t] = f32x4{};
+#pragma unroll
+  for (int t = 0; t < KTS; ++t) accv[t] = f32x4{};
 
   TileCopier<R, kBwdWaves> copier;
   copier.init(w, lane);
+  TileCopier<DV, kBwdWaves> vcopier;
+  vcopier.init(w, lane);
   auto stage = [&](int st) { return smem + st * CFG::STAGE; };
   auto issue_step = [&](int s, MLA_LDS char* dst) {
     const int h = h0 + s / nq, qb = qb0 + s % nq;
     const size_t r0 = (size_t)h * BT + (size_t)b * T;  // row t = 0 of (h, b)
     copier.issue(a.qabs + r0 * R, qb * 32, T, dst);
     copier.issue(a.dolat + r0 * R, qb * 32, T, dst + LT::BYTES);
+    vcopier.issue(a.dov + r0 * DV, qb * 32, T, dst + 2 * LT::BYTES);
     if (w == 0 && lane < 16) {
       const int rows = min(32, T - qb * 32);
       const u32x4 rs = make_rsrc(a.ld + (r0 + qb * 32) * 2, (unsigned)(rows * 8));
-      buf2lds16(rs, (unsigned)(lane * 16), dst + 2 * LT::BYTES);
+      buf2lds16(rs, (unsigned)(lane * 16), dst + 2 * LT::BYTES + CFG::DOB);
     }
   };
   if (nsteps > 0) issue_step(0, stage(0));
@@ -332,7 +333,8 @@ mla_bwd_key(BwdArgs a) {
     if (s + 1 < nsteps) issue_step(s + 1, stage((s + 1) & 1));
     const MLA_LDS char* tq_tile = stage(s & 1);
     const MLA_LDS char* td_tile = tq_tile + LT::BYTES;
-    const float* ldst = (const float*)(smem_raw + (s & 1) * CFG::STAGE + 2 * LT::BYTES);
+    const MLA_LDS char* tv_tile = td_tile + LT::BYTES;
+    const float* ldst = (const float*)(smem_raw + (s & 1) * CFG::STAGE + 2 * LT::BYTES + CFG::DOB);
     const int qb = qb0 + s % nq;
 
     // S2^T and dP^T tile (kt, qt): rows key 16 kt + 4 kq + i, column query 16 qt + l16
@@ -373,6 +375,28 @@ mla_bwd_key(BwdArgs a) {
         for (int t = 0; t < KTS; ++t) {
           acc[j][t] = mfma16(aq, bS[t], acc[j][t]);
           acc[j][t] = mfma16(ad, bP[t], acc[j][t]);
+        }
+      }
+    }
+    if (w < NVT) {
+      // dV^T [16 values x 64 keys] += do^T [16 values x 32 queries] P^T
+      const bf16x8 av = tile_column_operand<DV>(tv_tile, w, l16, kq);
+#pragma unroll
+      for (int t = 0; t < KTS; ++t) accv[t] = mfma16(av, bP[t], accv[t]);
+      if (s % nq == nq - 1) {
+        // the head's last query block: store its dV rows (values 16 w + 4 kq + e of key 16 t + l16)
+        const int h = h0 + s / nq;
+        const size_t r0 = (size_t)h * BT + (size_t)b * T;
+#pragma unroll
+        for (int t = 0; t < KTS; ++t) {
+          const int tk = k0 + 16 * t + l16;
+          if (tk < T) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (bf16)accv[t][e];
+            *(bf16x4*)(a.dv + (r0 + tk) * DV + 16 * w + 4 * kq) = v;
+          }
+          accv[t] = f32x4{};
         }
       }
     }

@@ -59,6 +59,7 @@ struct DecodeAbsorbArgs {
   int B, H;
   float qscale;
   int head_major;
+  int in_head_major;  // q is [H, B, DQ]
 };
 
 // Workgroup (head h, latent columns [J0, J0 + JC)), 4 waves; wave w owns the
@@ -97,7 +98,8 @@ __global__ void __launch_bounds__(256) mla_decode_absorb(DecodeAbsorbArgs a) {
   for (int i0 = 0; i0 < a.B; i0 += 16) {
     const int i = i0 + l16;
     const bool ok = i < a.B;
-    const bf16* qrow = a.q + ((size_t)(ok ? i : a.B - 1) * a.H + h) * DQ;
+    const size_t qi = ok ? i : a.B - 1;
+    const bf16* qrow = a.q + (a.in_head_major ? (size_t)h * a.B + qi : qi * a.H + h) * DQ;
     f32x4 acc = f32x4{};
 #pragma unroll
     for (int k = 0; k < NK; ++k) {

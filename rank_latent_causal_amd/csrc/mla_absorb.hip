@@ -183,7 +183,7 @@ void launch_rmsnorm(bf16* x, const bf16* gain, int rows, int n, float eps, hipSt
 }
 
 struct BackwardLayout {
-  size_t dov = 0, ld = 0, qabs = 0, dolat = 0, da = 0, ol = 0, part = 0, total = 0;
+  size_t dov = 0, ld = 0, qabs = 0, dolat = 0, da = 0, dv = 0, part = 0, total = 0;
   int nhg = 0, hpg = 0;
 };
 
@@ -199,7 +199,7 @@ BackwardLayout backward_layout(int B, int T, int H, int dv, int r) {
   L.qabs = off;  off = align_up(off + (size_t)H * BT * r * sizeof(bf16));
   L.dolat = off; off = align_up(off + (size_t)H * BT * r * sizeof(bf16));
   L.da = off;    off = align_up(off + (size_t)H * BT * r * sizeof(bf16));
-  L.ol = off;    off = align_up(off + (size_t)H * BT * r * sizeof(bf16));
+  L.dv = off;    off = align_up(off + (size_t)H * BT * dv * sizeof(bf16));
   L.part = off;  off = align_up(off + (size_t)L.nhg * BT * r * sizeof(float));
   L.total = off;
   return L;
@@ -226,7 +226,7 @@ void launch_backward_bf16(const mla::BwdPrepArgs& pa, const mla::DecodeAbsorbArg
   hipLaunchKernelGGL((mla::mla_decode_absorb<DV, R>), dim3(va.H * (R / JC)), dim3(256), 0, s, va);
   hipLaunchKernelGGL((mla::mla_bwd_query<R>), dim3(ba.B * ba.ntb * ba.H), dim3(64 * mla::kBwdWaves), 0, s, ba);
   const int nkb = (ba.T + mla::kBwdKeys - 1) / mla::kBwdKeys;
-  hipLaunchKernelGGL((mla::mla_bwd_key<R>), dim3(ba.B * nkb * ba.nhg), dim3(64 * mla::kBwdWaves), 0, s, ba);
+  hipLaunchKernelGGL((mla::mla_bwd_key<DV, R>), dim3(ba.B * nkb * ba.nhg), dim3(64 * mla::kBwdWaves), 0, s, ba);
 }
 
 // Varlen: the prepare kernel, then the paged prefill kernels over its block
@@ -610,10 +610,10 @@ mla_status mla_absorb_prefill_backward(const void* q, const void* c, const void*
   qa.B = (int)BT; qa.H = H; qa.qscale = scale * mla::kLog2e; qa.head_major = 1;
   mla::DecodeAbsorbArgs va{};
   va.q = pa.dov; va.wuk = (const bf16*)w_uv; va.qabs = (bf16*)(ws + L.dolat);
-  va.B = (int)BT; va.H = H; va.qscale = 1.0f; va.head_major = 1;
+  va.B = (int)BT; va.H = H; va.qscale = 1.0f; va.head_major = 1; va.in_head_major = 1;
   mla::BwdArgs ba{};
   ba.c = (const bf16*)c; ba.qabs = qa.qabs; ba.dolat = va.qabs; ba.ld = pa.ld;
-  ba.da = (bf16*)(ws + L.da); ba.ol = (bf16*)(ws + L.ol); ba.dc_part = (float*)(ws + L.part);
+  ba.dov = pa.dov; ba.da = (bf16*)(ws + L.da); ba.dv = (bf16*)(ws + L.dv); ba.dc_part = (float*)(ws + L.part);
   ba.B = B; ba.T = T; ba.H = H; ba.scale = scale; ba.ntb = (T + 31) / 32; ba.nhg = L.nhg; ba.hpg = L.hpg;
   if (d_q == 16) launch_backward_bf16<16, 16, 32>(pa, qa, va, ba, s);
   else if (d_q == 64) launch_backward_bf16<64, 64, 256>(pa, qa, va, ba, s);
@@ -633,12 +633,12 @@ mla_status mla_absorb_prefill_backward(const void* q, const void* c, const void*
     const long long grid = (long long)g.tiles_n * ((BT + mla::kGemmTile - 1) / mla::kGemmTile);
     hipLaunchKernelGGL(mla::mla_gemm_nt, dim3((unsigned)grid, H), dim3(256), 0, s, g);
   }
-  // dW_UK[h] = q[:, h, :]^T da[h];  dW_UV[h] = do[:, h, :]^T ol[h]
+  // dW_UK[h] = q[:, h, :]^T da[h];  dW_UV[h] = dV[h]^T c
   const size_t q_bytes = (size_t)BT * H * d_q * 2, hr_bytes = (size_t)H * BT * r * 2,
-               do_bytes = (size_t)BT * H * d_v * 2;
+               dv_bytes = (size_t)H * BT * d_v * 2, c_bytes = (size_t)BT * r * 2;
   launch_gemm_tn((const bf16*)q, q_bytes, H * d_q, d_q, ba.da, hr_bytes, r, BT * r, dw_uk, (long long)d_q * r, d_q,
                  r, (int)BT, H, s);
-  launch_gemm_tn(pa.dov, do_bytes, H * d_v, d_v, ba.ol, hr_bytes, r, BT * r, dw_uv, (long long)d_v * r, d_v, r,
+  launch_gemm_tn(ba.dv, dv_bytes, d_v, BT * d_v, (const bf16*)c, c_bytes, r, 0, dw_uv, (long long)d_v * r, d_v, r,
                  (int)BT, H, s);
   return launch_status();
 }
