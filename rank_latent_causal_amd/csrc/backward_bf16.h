@@ -14,7 +14,7 @@
 //
 // Kernels (in call order):
 //   mla_bwd_prep     dg, do and the per-row pair {lse log2 e, D}
-//   absorb (decode)  q_abs2 = scale log2e q W_UK and dol = do W_UV, head-major
+//   GEMMs            q_abs2 = scale log2e q W_UK and dol = do W_UV, head-major
 //   mla_bwd_query    per (32 queries, head): da over the key tiles
 //   mla_bwd_key      per (64 keys, head group): partial dc and, per head, dV
 //                    over the query blocks at or after the keys

@@ -55,11 +55,9 @@ __global__ void __launch_bounds__(256) mla_wuk_transpose(const T* __restrict__ w
 struct DecodeAbsorbArgs {
   const bf16* q;    // [B, H, DQ]
   const bf16* wuk;  // [H, DQ, R]
-  bf16* qabs;       // [B, H, R], or [H, B, R] with head_major
+  bf16* qabs;       // [B, H, R]
   int B, H;
   float qscale;
-  int head_major;
-  int in_head_major;  // q is [H, B, DQ]
 };
 
 // Workgroup (head h, latent columns [J0, J0 + JC)), 4 waves; wave w owns the
@@ -98,8 +96,7 @@ __global__ void __launch_bounds__(256) mla_decode_absorb(DecodeAbsorbArgs a) {
   for (int i0 = 0; i0 < a.B; i0 += 16) {
     const int i = i0 + l16;
     const bool ok = i < a.B;
-    const size_t qi = ok ? i : a.B - 1;
-    const bf16* qrow = a.q + (a.in_head_major ? (size_t)h * a.B + qi : qi * a.H + h) * DQ;
+    const bf16* qrow = a.q + ((size_t)(ok ? i : a.B - 1) * a.H + h) * DQ;
     f32x4 acc = f32x4{};
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
@@ -110,8 +107,7 @@ __global__ void __launch_bounds__(256) mla_decode_absorb(DecodeAbsorbArgs a) {
       bf16x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[e] * a.qscale);
-      const size_t row = a.head_major ? (size_t)h * a.B + i : (size_t)i * a.H + h;
-      *(bf16x4*)(a.qabs + row * R + J0 + 16 * w + 4 * kq) = v;
+      *(bf16x4*)(a.qabs + ((size_t)i * a.H + h) * R + J0 + 16 * w + 4 * kq) = v;
     }
   }
 }

@@ -35,6 +35,7 @@ struct GemmArgs {
   int tiles_n;    // ceil(N / 128)
   int lda, ldw, ldy;
   long long bsx, bsw, bsy;  // element offsets between the batches of blockIdx.y
+  float alpha;              // Y = alpha X W^T
 };
 
 constexpr int kGemmTile = 128;
@@ -131,7 +132,7 @@ mla_gemm_nt(GemmArgs a) {
       const int n = n0 + 64 * wn + 16 * i + 4 * kq;
       bf16x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (bf16)acc[i][j][e];
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[i][j][e] * a.alpha);
       bf16* dst = Y + (size_t)m * a.ldy + n;
       if (n + 3 < a.N) {
         *(bf16x4*)dst = v;

@@ -170,7 +170,7 @@ ForwardLayout forward_layout(int B, int T, int q_rank, int H, int dq, int dv, in
 void launch_gemm(const bf16* x, const bf16* w, bf16* y, int M, int N, int K, hipStream_t s) {
   mla::GemmArgs g{};
   g.x = x; g.w = w; g.y = y; g.M = M; g.N = N; g.K = K;
-  g.lda = K; g.ldw = K; g.ldy = N;
+  g.lda = K; g.ldw = K; g.ldy = N; g.alpha = 1.0f;
   g.tiles_n = (N + mla::kGemmTile - 1) / mla::kGemmTile;
   const long long grid = (long long)g.tiles_n * ((M + mla::kGemmTile - 1) / mla::kGemmTile);
   hipLaunchKernelGGL(mla::mla_gemm_nt, dim3((unsigned)grid, 1), dim3(256), 0, s, g);
@@ -183,17 +183,19 @@ void launch_rmsnorm(bf16* x, const bf16* gain, int rows, int n, float eps, hipSt
 }
 
 struct BackwardLayout {
-  size_t dov = 0, ld = 0, qabs = 0, dolat = 0, da = 0, dv = 0, part = 0, total = 0;
+  size_t wukT = 0, wuvT = 0, dov = 0, ld = 0, qabs = 0, dolat = 0, da = 0, dv = 0, part = 0, total = 0;
   int nhg = 0, hpg = 0;
 };
 
-BackwardLayout backward_layout(int B, int T, int H, int dv, int r) {
+BackwardLayout backward_layout(int B, int T, int H, int dq, int dv, int r) {
   BackwardLayout L;
   const size_t BT = (size_t)B * T;
   // at most 8 head groups, none of them empty
   L.hpg = (H + 7) / 8;
   L.nhg = (H + L.hpg - 1) / L.hpg;
   size_t off = 0;
+  L.wukT = off;  off = align_up(off + (size_t)H * r * dq * sizeof(bf16));
+  L.wuvT = off;  off = align_up(off + (size_t)H * r * dv * sizeof(bf16));
   L.dov = off;   off = align_up(off + BT * H * dv * sizeof(bf16));
   L.ld = off;    off = align_up(off + (size_t)H * BT * 2 * sizeof(float));
   L.qabs = off;  off = align_up(off + (size_t)H * BT * r * sizeof(bf16));
@@ -217,13 +219,33 @@ void launch_gemm_tn(const bf16* A, size_t a_bytes, int lda, long long bsa, const
   hipLaunchKernelGGL(mla::mla_gemm_tn, dim3(tiles, batch), dim3(256), 0, s, g);
 }
 
+// Y[z] = alpha X[z] W[z]^T for z < batch, every operand strided
+void launch_gemm_batched(const bf16* x, int lda, long long bsx, const bf16* w, int ldw, long long bsw, bf16* y, int ldy,
+                         long long bsy, int M, int N, int K, float alpha, int batch, hipStream_t s) {
+  mla::GemmArgs g{};
+  g.x = x; g.w = w; g.y = y; g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldw = ldw; g.ldy = ldy;
+  g.bsx = bsx; g.bsw = bsw; g.bsy = bsy; g.alpha = alpha;
+  g.tiles_n = (N + mla::kGemmTile - 1) / mla::kGemmTile;
+  const long long grid = (long long)g.tiles_n * ((M + mla::kGemmTile - 1) / mla::kGemmTile);
+  hipLaunchKernelGGL(mla::mla_gemm_nt, dim3((unsigned)grid, batch), dim3(256), 0, s, g);
+}
+
+// q_abs2[h] = scale log2e q[:, h, :] W_UK[h] and dol[h] = do[h] W_UV[h], as GEMMs
+// against the transposed weights (head-major outputs)
+void launch_backward_projections(const bf16* q, const bf16* wukT, const bf16* dov, const bf16* wuvT, bf16* qabs,
+                                 bf16* dolat, int BT, int H, int dq, int dv, int r, float qscale, hipStream_t s) {
+  launch_gemm_batched(q, H * dq, dq, wukT, dq, (long long)r * dq, qabs, r, (long long)BT * r, BT, r, dq, qscale, H,
+                      s);
+  launch_gemm_batched(dov, dv, (long long)BT * dv, wuvT, dv, (long long)r * dv, dolat, r, (long long)BT * r, BT, r, dv,
+                      1.0f, H, s);
+}
+
 template <int DQ, int DV, int R>
-void launch_backward_bf16(const mla::BwdPrepArgs& pa, const mla::DecodeAbsorbArgs& qa, const mla::DecodeAbsorbArgs& va,
-                          const mla::BwdArgs& ba, hipStream_t s) {
-  constexpr int JC = R < 64 ? R : 64;
+void launch_backward_bf16(const mla::BwdPrepArgs& pa, const mla::BwdArgs& ba, const bf16* q, const bf16* wukT,
+                          const bf16* wuvT, hipStream_t s) {
   hipLaunchKernelGGL(mla::mla_bwd_prep, dim3(pa.B * pa.T), dim3(256), 0, s, pa);
-  hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(qa.H * (R / JC)), dim3(256), 0, s, qa);
-  hipLaunchKernelGGL((mla::mla_decode_absorb<DV, R>), dim3(va.H * (R / JC)), dim3(256), 0, s, va);
+  launch_backward_projections(q, wukT, pa.dov, wuvT, const_cast<bf16*>(ba.qabs), const_cast<bf16*>(ba.dolat),
+                              pa.B * pa.T, ba.H, DQ, DV, R, ba.scale * mla::kLog2e, s);
   hipLaunchKernelGGL((mla::mla_bwd_query<R>), dim3(ba.B * ba.ntb * ba.H), dim3(64 * mla::kBwdWaves), 0, s, ba);
   const int nkb = (ba.T + mla::kBwdKeys - 1) / mla::kBwdKeys;
   hipLaunchKernelGGL((mla::mla_bwd_key<DV, R>), dim3(ba.B * nkb * ba.nhg), dim3(64 * mla::kBwdWaves), 0, s, ba);
@@ -575,7 +597,7 @@ mla_status mla_cache_append_paged(const void* c_new, void* c_pages, const int32_
 size_t mla_absorb_prefill_backward_workspace_size(int B, int T, int H, int d_q, int d_v, int r, mla_dtype dtype) {
   if (B <= 0 || T <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return kBadSize;
   if (dtype != MLA_DTYPE_BF16) return kBadSize;
-  return backward_layout(B, T, H, d_v, r).total;
+  return backward_layout(B, T, H, d_q, d_v, r).total;
 }
 
 mla_status mla_absorb_prefill_backward(const void* q, const void* c, const void* w_uk, const void* w_uv,
@@ -595,7 +617,7 @@ mla_status mla_absorb_prefill_backward(const void* q, const void* c, const void*
   if (BT >= (1LL << 31) || (long double)H * BT * r * 2 >= 2.0e9L || (long double)H * BT * d_q * 2 >= 2.0e9L ||
       (long double)H * BT * d_v * 2 >= 2.0e9L)
     return MLA_ERR_UNSUPPORTED;
-  const BackwardLayout L = backward_layout(B, T, H, d_v, r);
+  const BackwardLayout L = backward_layout(B, T, H, d_q, d_v, r);
   if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
   if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
@@ -605,34 +627,25 @@ mla_status mla_absorb_prefill_backward(const void* q, const void* c, const void*
   pa.gate = (const bf16*)gate; pa.out = (const bf16*)out; pa.dout = (const bf16*)dout; pa.lse = lse;
   pa.dgate = (bf16*)dgate; pa.dov = (bf16*)(ws + L.dov); pa.ld = (float*)(ws + L.ld);
   pa.B = B; pa.T = T; pa.H = H; pa.DV = d_v;
-  mla::DecodeAbsorbArgs qa{};
-  qa.q = (const bf16*)q; qa.wuk = (const bf16*)w_uk; qa.qabs = (bf16*)(ws + L.qabs);
-  qa.B = (int)BT; qa.H = H; qa.qscale = scale * mla::kLog2e; qa.head_major = 1;
-  mla::DecodeAbsorbArgs va{};
-  va.q = pa.dov; va.wuk = (const bf16*)w_uv; va.qabs = (bf16*)(ws + L.dolat);
-  va.B = (int)BT; va.H = H; va.qscale = 1.0f; va.head_major = 1; va.in_head_major = 1;
+  bf16* wukT = (bf16*)(ws + L.wukT);
+  bf16* wuvT = (bf16*)(ws + L.wuvT);
+  launch_wuk_transpose((const bf16*)w_uk, wukT, H, d_q, r, s);
+  launch_wuk_transpose((const bf16*)w_uv, wuvT, H, d_v, r, s);
   mla::BwdArgs ba{};
-  ba.c = (const bf16*)c; ba.qabs = qa.qabs; ba.dolat = va.qabs; ba.ld = pa.ld;
+  ba.c = (const bf16*)c; ba.qabs = (bf16*)(ws + L.qabs); ba.dolat = (bf16*)(ws + L.dolat); ba.ld = pa.ld;
   ba.dov = pa.dov; ba.da = (bf16*)(ws + L.da); ba.dv = (bf16*)(ws + L.dv); ba.dc_part = (float*)(ws + L.part);
   ba.B = B; ba.T = T; ba.H = H; ba.scale = scale; ba.ntb = (T + 31) / 32; ba.nhg = L.nhg; ba.hpg = L.hpg;
-  if (d_q == 16) launch_backward_bf16<16, 16, 32>(pa, qa, va, ba, s);
-  else if (d_q == 64) launch_backward_bf16<64, 64, 256>(pa, qa, va, ba, s);
-  else launch_backward_bf16<128, 128, 512>(pa, qa, va, ba, s);
+  if (d_q == 16) launch_backward_bf16<16, 16, 32>(pa, ba, (const bf16*)q, wukT, wuvT, s);
+  else if (d_q == 64) launch_backward_bf16<64, 64, 256>(pa, ba, (const bf16*)q, wukT, wuvT, s);
+  else launch_backward_bf16<128, 128, 512>(pa, ba, (const bf16*)q, wukT, wuvT, s);
 
   // dc: sum of the head-group partials
   const long long n4 = BT * r / 4;
   hipLaunchKernelGGL(mla::mla_bwd_dc_sum, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, ba.dc_part,
                      (bf16*)dc, BT, r, L.nhg);
   // dq[:, h, :] = da[h] W_UK[h]^T
-  {
-    mla::GemmArgs g{};
-    g.x = ba.da; g.w = (const bf16*)w_uk; g.y = (bf16*)dq;
-    g.M = (int)BT; g.N = d_q; g.K = r; g.lda = r; g.ldw = r; g.ldy = H * d_q;
-    g.bsx = BT * r; g.bsw = (long long)d_q * r; g.bsy = d_q;
-    g.tiles_n = (d_q + mla::kGemmTile - 1) / mla::kGemmTile;
-    const long long grid = (long long)g.tiles_n * ((BT + mla::kGemmTile - 1) / mla::kGemmTile);
-    hipLaunchKernelGGL(mla::mla_gemm_nt, dim3((unsigned)grid, H), dim3(256), 0, s, g);
-  }
+  launch_gemm_batched(ba.da, r, BT * r, (const bf16*)w_uk, r, (long long)d_q * r, (bf16*)dq, H * d_q, d_q, (int)BT, d_q,
+                      r, 1.0f, H, s);
   // dW_UK[h] = q[:, h, :]^T da[h];  dW_UV[h] = dV[h]^T c
   const size_t q_bytes = (size_t)BT * H * d_q * 2, hr_bytes = (size_t)H * BT * r * 2,
                dv_bytes = (size_t)H * BT * d_v * 2, c_bytes = (size_t)BT * r * 2;
