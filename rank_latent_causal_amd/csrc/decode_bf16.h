@@ -11,8 +11,8 @@
 //                       LDS once and scored against all H heads (heads are the
 //                       MFMA columns, 16 per wave, up to 8 waves).  Every
 //                       sequence piece in a range leaves an unnormalised
-//                       partial (m, l, O[r]).
-//  mla_decode_merge     per (head, 16 sequences): log-sum-exp merge of the
+//                       partial (m, l in fp32, O[r] in bf16).
+//  mla_decode_merge     per (head, 8 sequences): log-sum-exp merge of the
 //                       partials, then o = o_lat W_UV[h]^T on MFMA, the
 //                       sigmoid gate and the store.
 //
@@ -117,7 +117,7 @@ struct DecodeSplitArgs {
   const bf16* qabs;     // [B, H, R]
   const bf16* cache;    // [N, R]
   const int* cu;        // [B + 1]
-  float* part_o;        // [(G + B), H, R]
+  bf16* part_o;         // [(G + B), H, R]  unnormalised O, bf16
   float* part_ml;       // [(G + B), H, 2]
   int B, H, G;
   long long N;          // cache rows (total_len)
@@ -231,9 +231,14 @@ mla_decode_split(DecodeSplitArgs a) {
         const float l_tot = col_sum(st.l_run);
         if (hvalid) {
           // O^T fragment t holds latent dims 16t + 4kq + e
-          float* dst = a.part_o + ((size_t)slot * a.H + h) * R + 4 * kq;
+          bf16* dst = a.part_o + ((size_t)slot * a.H + h) * R + 4 * kq;
 #pragma unroll
-          for (int t = 0; t < R / 16; ++t) *(f32x4*)(dst + 16 * t) = st.oT[t];
+          for (int t = 0; t < R / 16; ++t) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (bf16)st.oT[t][e];
+            *(bf16x4*)(dst + 16 * t) = v;
+          }
           if (kq == 0) {
             a.part_ml[((size_t)slot * a.H + h) * 2 + 0] = st.m_run;
             a.part_ml[((size_t)slot * a.H + h) * 2 + 1] = l_tot;
@@ -260,7 +265,7 @@ mla_decode_split(DecodeSplitArgs a) {
 
 // ----------------------------------------------------------------- merge
 struct DecodeMergeArgs {
-  const float* part_o;   // [(G + B), H, R]
+  const bf16* part_o;    // [(G + B), H, R]  unnormalised O, bf16
   const float* part_ml;  // [(G + B), H, 2]
   const int* cu;         // [B + 1]
   const bf16* wuv;       // [H, DV, R]
@@ -277,27 +282,27 @@ __device__ __forceinline__ int range_of(long long x, long long N, long long G) {
   return (int)(((x + 1) * G - 1) / N);
 }
 
-// Workgroup (16 sequences, head h), 4 waves.  Phase 1: wave w merges latent
-// columns [w R/4, (w+1) R/4) of every sequence into LDS (bf16, normalised)
-// in one online pass over the sequence's partials, with the next partial's
-// loads in flight.  Phase 2: wave w computes v-tiles w, w+4, ... of
-// o^T = W_UV[h] o_lat^T; their W_UV operands and gate values are loaded
-// before phase 1 starts, so their latency hides behind the merge.
+// Workgroup (head h, 8 sequences), 4 waves.  Phase 1: wave w merges the
+// partials of sequences 2w and 2w+1 of the group (half a wave each, 32 lanes
+// over the R latent columns), loading the partials of up to kMergeChunk ranges
+// at once, and writes o_lat = O / l (bf16) to LDS.  Phase 2: wave w computes
+// v-tiles w, w+4, ... of o^T = W_UV[h] o_lat^T on MFMA (the 16 MFMA columns
+// are the group's sequences, 8 of them used), gates and stores; the first
+// v-tile's W_UV operands and gate values are loaded before phase 1.
+constexpr int kMergeSeqs = 8;
+constexpr int kMergeChunk = 4;
+
 template <int DV, int R>
 __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
-  constexpr int JW = R / 4;   // latent columns merged per wave
-  constexpr int JL = JW / 4;  // per lane (four lanes per sequence)
-  static_assert(JL % 4 == 0 || JL == 2, "merge split");
-  constexpr int VW = JL >= 4 ? 4 : 2;  // floats per vector load
-  constexpr int NVV = JL / VW;
-  using VT = typename std::conditional<(JL >= 4), f32x4, f32x2>::type;
+  constexpr int CPL = R / 32;  // latent columns per lane (32 lanes per sequence)
   constexpr int NKK = R / 32;
+  static_assert(CPL == 1 || CPL % 4 == 0, "merge split");
   __shared__ __attribute__((aligned(16))) bf16 olat[16][R + 8];
 
-  // 1-D grid of H x nb workgroups (nb = ceil(B / 16)).  With H % 8 == 0 the
+  // 1-D grid of H x nb workgroups (nb = ceil(B / 8)).  With H % 8 == 0 the
   // nb workgroups of head h get ids congruent to h mod 8, i.e. they run on
   // one XCD and read W_UV[h] from HBM once.
-  const int nb = (a.B + 15) / 16;
+  const int nb = (a.B + kMergeSeqs - 1) / kMergeSeqs;
   int h, bb;
   if ((a.H & 7) == 0) {
     const int id = blockIdx.x;
@@ -309,13 +314,13 @@ __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
   }
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l16 = lane & 15, kq = lane >> 4;
-  const int i = bb * 16 + l16;
-  const bool ivalid = i < a.B;
-  const int ic = ivalid ? i : a.B - 1;
 
-  // phase 2 operands: the first v-tile's are issued before the merge
+  // phase 2 operands (MFMA column l16 = sequence bb*8 + l16 for l16 < 8)
+  const int ip = bb * kMergeSeqs + (l16 & (kMergeSeqs - 1));
+  const bool pvalid = l16 < kMergeSeqs && ip < a.B;
+  const int ipc = ip < a.B ? ip : a.B - 1;
   const bf16* wv = a.wuv + (size_t)h * DV * R;
-  const size_t orow = (size_t)ic * a.H * DV + (size_t)h * DV;
+  const size_t orow = (size_t)ipc * a.H * DV + (size_t)h * DV;
   auto load_w = [&](int vt, bf16x8 (&wa)[NKK], bf16x4& gv) {
     const bf16* wrow = wv + (size_t)(16 * vt + l16) * R + 8 * kq;
 #pragma unroll
@@ -329,71 +334,72 @@ __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
   {
     const long long N = a.n_dev ? (long long)a.n_dev[0] : a.N;
     const long long G = a.n_dev ? (long long)a.n_dev[1] : a.G;
+    const int sl = 2 * w + (lane >> 5);  // sequence of this half wave in the group
+    const int l32 = lane & 31;
+    const int i = bb * kMergeSeqs + sl;
+    const int ic = i < a.B ? i : a.B - 1;
     const long long s0 = a.cu[ic], s1 = a.cu[ic + 1];
     const int k0 = range_of(s0, N, G), k1 = range_of(s1 - 1, N, G);
-    const int j0 = w * JW + kq * JL;
-    auto load = [&](int k, float& mk, float& lk, VT (&o)[NVV]) {
-      const size_t base = (size_t)(k + ic) * a.H + h;
-      mk = a.part_ml[base * 2];
-      lk = a.part_ml[base * 2 + 1];
-      const float* src = a.part_o + base * R + j0;
-#pragma unroll
-      for (int u = 0; u < NVV; ++u) o[u] = *(const VT*)(src + VW * u);
-    };
-    // online log-sum-exp merge; every partial has a finite max (a range piece
-    // holds at least one key of the sequence)
+    const int j0 = CPL * l32;
     float m = -INFINITY, L = 0.0f;
-    VT acc[NVV];
+    float acc[CPL];
 #pragma unroll
-    for (int u = 0; u < NVV; ++u) acc[u] = VT{};
-    float mk, lk;
-    VT ok[NVV];
-    load(k0, mk, lk, ok);
-    for (int k = k0; k <= k1; ++k) {
-      float mn = 0.0f, ln = 0.0f;
-      VT on[NVV];
-      if (k < k1) load(k + 1, mn, ln, on);
-      const float m_new = fmaxf(m, mk);
-      const float sa = fast_exp2(m - m_new), sb = fast_exp2(mk - m_new);
-      L = L * sa + lk * sb;
+    for (int u = 0; u < CPL; ++u) acc[u] = 0.0f;
+    for (int kc = k0; kc <= k1; kc += kMergeChunk) {
+      // every partial of the chunk is in flight at once
+      float mk[kMergeChunk], lk[kMergeChunk], ok[kMergeChunk][CPL];
 #pragma unroll
-      for (int u = 0; u < NVV; ++u) acc[u] = acc[u] * sa + ok[u] * sb;
-      m = m_new;
-      mk = mn;
-      lk = ln;
+      for (int c = 0; c < kMergeChunk; ++c) {
+        const int k = min(kc + c, k1);
+        const size_t base = (size_t)(k + ic) * a.H + h;
+        mk[c] = a.part_ml[base * 2];
+        lk[c] = a.part_ml[base * 2 + 1];
+        const bf16* src = a.part_o + base * R + j0;
+        if constexpr (CPL % 4 == 0) {
 #pragma unroll
-      for (int u = 0; u < NVV; ++u) ok[u] = on[u];
+          for (int u = 0; u < CPL; u += 4) {
+            const bf16x4 v = *(const bf16x4*)(src + u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ok[c][u + e] = (float)v[e];
+          }
+        } else {
+          ok[c][0] = (float)src[0];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < kMergeChunk; ++c) {
+        if (kc + c > k1) break;  // partials past the last range are repeats
+        const float m_new = fmaxf(m, mk[c]);
+        const float sa = fast_exp2(m - m_new), sb = fast_exp2(mk[c] - m_new);
+        L = L * sa + lk[c] * sb;
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) acc[u] = acc[u] * sa + ok[c][u] * sb;
+        m = m_new;
+      }
     }
     const float invL = 1.0f / L;
 #pragma unroll
-    for (int u = 0; u < NVV; ++u) {
+    for (int u = 0; u < CPL; ++u) olat[sl][j0 + u] = (bf16)(acc[u] * invL);
+    // rows 8..15 are the unused MFMA columns: keep them finite
 #pragma unroll
-      for (int e = 0; e < VW; ++e) olat[l16][j0 + VW * u + e] = (bf16)(acc[u][e] * invL);
-    }
+    for (int u = 0; u < CPL; ++u) olat[kMergeSeqs + sl][j0 + u] = (bf16)0.0f;
   }
   __syncthreads();
 
   // o_lat^T B operand for k-step kk: slot p <-> latent dim 32kk + 8kq + p
   for (int vt = w; vt < DV / 16; vt += 4) {
-    bf16x8 wn[NKK];
-    bf16x4 gn;
-    if (vt + 4 < DV / 16) load_w(vt + 4, wn, gn);  // next v-tile's operands in flight
+    if (vt != w) load_w(vt, wa, gv);
     f32x4 acc = f32x4{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const bf16x8 bv = *(const bf16x8*)&olat[l16][32 * kk + 8 * kq];
       acc = mfma16(wa[kk], bv, acc);
     }
-    if (ivalid) {
+    if (pvalid) {
       bf16x4 ov;
 #pragma unroll
       for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[e] * sigmoidf_((float)gv[e]));
       *(bf16x4*)(a.out + orow + 16 * vt + 4 * kq) = ov;
-    }
-    if (vt + 4 < DV / 16) {
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) wa[kk] = wn[kk];
-      gv = gn;
     }
   }
 }
@@ -450,7 +456,7 @@ struct DecodePagedArgs {
   const int* block_table;   // [B, max_pages]
   const int* lens;          // [B] clamped lengths (mla_paged_prepare)
   const int* cu_t;          // [B + 2] tile prefix sums, then the range count (mla_paged_prepare)
-  float* part_o;            // [(G + B), H, R]
+  bf16* part_o;             // [(G + B), H, R]  unnormalised O, bf16
   float* part_ml;           // [(G + B), H, 2]
   int B, H, G;                           // G: workgroups launched (>= the range count)
   int page_shift, max_pages, num_pages;  // pages of 2^page_shift rows
@@ -581,9 +587,14 @@ mla_decode_split_paged(DecodePagedArgs a) {
         const int slot = k + i;
         const float l_tot = col_sum(st.l_run);
         if (hvalid) {
-          float* dst = a.part_o + ((size_t)slot * a.H + h) * R + 4 * kq;
+          bf16* dst = a.part_o + ((size_t)slot * a.H + h) * R + 4 * kq;
 #pragma unroll
-          for (int u = 0; u < R / 16; ++u) *(f32x4*)(dst + 16 * u) = st.oT[u];
+          for (int u = 0; u < R / 16; ++u) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (bf16)st.oT[u][e];
+            *(bf16x4*)(dst + 16 * u) = v;
+          }
           if (kq == 0) {
             a.part_ml[((size_t)slot * a.H + h) * 2 + 0] = st.m_run;
             a.part_ml[((size_t)slot * a.H + h) * 2 + 1] = l_tot;

@@ -61,7 +61,7 @@ DecodeLayout decode_layout(int B, int H, int dq, int r, int G) {
   L.qabs = off;
   off = align_up(off + (size_t)B * H * r * sizeof(bf16));
   L.part_o = off;
-  off = align_up(off + (size_t)(G + B) * H * r * sizeof(float));
+  off = align_up(off + (size_t)(G + B) * H * r * sizeof(bf16));
   L.part_ml = off;
   off = align_up(off + (size_t)(G + B) * H * 2 * sizeof(float));
   L.total = off;
@@ -96,7 +96,8 @@ void launch_decode_bf16(const mla::DecodeAbsorbArgs& aa, const mla::DecodeSplitA
   constexpr int JC = R < 64 ? R : 64;
   hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(aa.H * (R / JC)), dim3(256), 0, s, aa);
   hipLaunchKernelGGL((mla::mla_decode_split<R>), dim3(sa.G), dim3(64 * mla::kDecodeWaves), 0, s, sa);
-  hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + 15) / 16) * ma.H), dim3(256), 0, s, ma);
+  hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + mla::kMergeSeqs - 1) / mla::kMergeSeqs) * ma.H),
+                     dim3(256), 0, s, ma);
 }
 
 template <int DQ, int DV, int R>
@@ -107,7 +108,8 @@ void launch_decode_paged_bf16(const mla::DecodeAbsorbArgs& aa, const int* seq_le
                      const_cast<int*>(sa.lens), const_cast<int*>(sa.cu_t));
   hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(aa.H * (R / JC)), dim3(256), 0, s, aa);
   hipLaunchKernelGGL((mla::mla_decode_split_paged<R>), dim3(sa.G), dim3(64 * mla::kDecodeWaves), 0, s, sa);
-  hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + 15) / 16) * ma.H), dim3(256), 0, s, ma);
+  hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + mla::kMergeSeqs - 1) / mla::kMergeSeqs) * ma.H),
+                     dim3(256), 0, s, ma);
 }
 
 struct PagedDecodeLayout {
@@ -510,7 +512,7 @@ mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* 
   aa.B = B; aa.H = H; aa.qscale = scale * mla::kLog2e;
   mla::DecodeSplitArgs sa{};
   sa.qabs = aa.qabs; sa.cache = (const bf16*)c_cache; sa.cu = cu_seqlens;
-  sa.part_o = (float*)(ws + L.part_o); sa.part_ml = (float*)(ws + L.part_ml);
+  sa.part_o = (bf16*)(ws + L.part_o); sa.part_ml = (float*)(ws + L.part_ml);
   sa.B = B; sa.H = H; sa.G = G; sa.N = total_len;
   mla::DecodeMergeArgs ma{};
   ma.part_o = sa.part_o; ma.part_ml = sa.part_ml; ma.cu = cu_seqlens;
@@ -560,7 +562,7 @@ mla_status mla_absorb_decode_paged(const void* q, const void* c_pages, const int
   mla::DecodePagedArgs sa{};
   sa.qabs = aa.qabs; sa.pages = (const bf16*)c_pages; sa.block_table = block_table;
   sa.lens = (const int*)(ws + L.lens); sa.cu_t = (const int*)(ws + L.cu_t);
-  sa.part_o = (float*)(ws + L.d.part_o); sa.part_ml = (float*)(ws + L.d.part_ml);
+  sa.part_o = (bf16*)(ws + L.d.part_o); sa.part_ml = (float*)(ws + L.d.part_ml);
   sa.B = B; sa.H = H; sa.G = G;
   sa.page_shift = log2_exact(page_size); sa.max_pages = max_pages; sa.num_pages = (int)num_pages;
   mla::DecodeMergeArgs ma{};

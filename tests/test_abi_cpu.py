@@ -54,8 +54,8 @@ def test_prefill_workspace_sizes():
 def test_decode_workspace_sizes_explicit_splits():
     assert mla.decode_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_F32) == 0
     n = mla.decode_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_BF16)
-    # q_abs + (G+B) partial rows of r floats + (m, l)
-    assert n >= 64 * 96 * 512 * 2 + (256 + 64) * 96 * (512 + 2) * 4
+    # q_abs + (G+B) partial rows of r bf16 values + (m, l) in fp32
+    assert n >= 64 * 96 * 512 * 2 + (256 + 64) * 96 * (512 * 2 + 2 * 4)
     assert mla.decode_workspace_size(64, 96, 128, 512, 512, mla.DTYPE_BF16) > n
     with pytest.raises(mla.MLAError):
         mla.decode_workspace_size(64, 96, 128, 512, 256, 7)
