@@ -146,6 +146,108 @@ mla_gemm_nt(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// The same product with a 256 x 256 tile of Y^T per workgroup of 8 waves
+// (each wave 128 n x 64 m: 8 x 4 MFMA tiles), for products with enough
+// tiles to fill the chip.  Per k-step a wave reads 12 operand fragments for 32
+// MFMAs (the 128 x 128 kernel: 8 for 16), and every staged byte serves twice
+// the FLOPs.  Two 64 KiB stages, one workgroup per CU.
+constexpr int kGemmBig = 256;
+
+__device__ __forceinline__ void gemm_copy_big(const bf16* __restrict__ base, int rows_total, int row0, int ld, int K,
+                                              int k0, MLA_LDS char* tile, int w) {
+  unsigned ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+  int rows = rows_total - row0;
+  rows = rows > kGemmBig ? kGemmBig : rows;
+  const u32x4 rs = make_rsrc(base + (size_t)row0 * ld, (unsigned)((size_t)(rows > 0 ? rows : 0) * ld * 2));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int i = w + 8 * c;  // copy index 0..31, 8 rows each
+    const int s = 8 * i + (int)(ln >> 3);
+    const int logical = gemm_chunk(s, (int)(ln & 7));
+    const int k = k0 + 8 * logical;
+    const unsigned voff = k < K ? (unsigned)(((size_t)s * ld + k) * 2) : 0xFFFFFFF0u;
+    buf2lds16(rs, voff, tile + i * 1024);
+  }
+}
+
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mla_gemm_nt_big(GemmArgs a) {
+  constexpr int TB = kGemmBig * kGemmKT * 2;  // 32 KiB per operand per stage
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * TB];
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;  // [stage][W tile, X tile]
+
+  const int tn = blockIdx.x % a.tiles_n, tm = blockIdx.x / a.tiles_n;
+  const int n0 = tn * kGemmBig, m0 = tm * kGemmBig;
+  const bf16* __restrict__ X = a.x + (size_t)blockIdx.y * a.bsx;
+  const bf16* __restrict__ W = a.w + (size_t)blockIdx.y * a.bsw;
+  bf16* __restrict__ Y = a.y + (size_t)blockIdx.y * a.bsy;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int wn = w & 1, wm = w >> 1;  // this wave's 128 (n) x 64 (m) block
+  const int nk = (a.K + kGemmKT - 1) / kGemmKT;
+
+  auto stage_w = [&](int st) { return smem + st * 2 * TB; };
+  auto stage_x = [&](int st) { return smem + st * 2 * TB + TB; };
+
+  gemm_copy_big(W, a.N, n0, a.ldw, a.K, 0, stage_w(0), w);
+  gemm_copy_big(X, a.M, m0, a.lda, a.K, 0, stage_x(0), w);
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
+
+  auto off = [&](int row, int chunk) { return row * 128 + (gemm_chunk(row, chunk) << 4); };
+
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<0>();
+    wg_barrier();  // tile kt visible; every wave is done with tile kt-1
+    if (kt + 1 < nk) {
+      gemm_copy_big(W, a.N, n0, a.ldw, a.K, (kt + 1) * kGemmKT, stage_w((kt + 1) & 1), w);
+      gemm_copy_big(X, a.M, m0, a.lda, a.K, (kt + 1) * kGemmKT, stage_x((kt + 1) & 1), w);
+    }
+    const MLA_LDS char* tw = stage_w(kt & 1);
+    const MLA_LDS char* tx = stage_x(kt & 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 fa[8], fb[4];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) fa[t] = lds_read_b128(tw + off(128 * wn + 16 * t + l16, 4 * ks + kq));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) fb[t] = lds_read_b128(tx + off(64 * wm + 16 * t + l16, 4 * ks + kq));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(fa[i], fb[j], acc[i][j]);
+    }
+  }
+
+  // C fragment (i, j): rows n0 + 128 wn + 16 i + 4 kq + e, column m0 + 64 wm + 16 j + l16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + 64 * wm + 16 * j + l16;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = n0 + 128 * wn + 16 * i + 4 * kq;
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[i][j][e] * a.alpha);
+      bf16* dst = Y + (size_t)m * a.ldy + n;
+      if (n + 3 < a.N) {
+        *(bf16x4*)dst = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) dst[e] = v[e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // C[z][m][n] = sum_k A[k][m] B[k][n] for the weight gradients of the
 // backward (the reduction runs over token rows): A and B are row-major with
 // the m / n index contiguous (rows lda / ldb apart, batch z at element

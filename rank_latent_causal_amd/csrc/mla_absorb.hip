@@ -168,14 +168,29 @@ ForwardLayout forward_layout(int B, int T, int q_rank, int H, int dq, int dv, in
   return L;
 }
 
+// Y[z] = alpha X[z] W[z]^T for z < batch, every operand strided.  The
+// 256 x 256 tile when it still gives at least one workgroup per CU (256),
+// else 128 x 128.
+void launch_gemm_batched(const bf16* x, int lda, long long bsx, const bf16* w, int ldw, long long bsw, bf16* y, int ldy,
+                         long long bsy, int M, int N, int K, float alpha, int batch, hipStream_t s) {
+  mla::GemmArgs g{};
+  g.x = x; g.w = w; g.y = y; g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldw = ldw; g.ldy = ldy;
+  g.bsx = bsx; g.bsw = bsw; g.bsy = bsy; g.alpha = alpha;
+  const long long big = (long long)((N + mla::kGemmBig - 1) / mla::kGemmBig) *
+                        ((M + mla::kGemmBig - 1) / mla::kGemmBig) * batch;
+  if (big >= 256) {
+    g.tiles_n = (N + mla::kGemmBig - 1) / mla::kGemmBig;
+    hipLaunchKernelGGL(mla::mla_gemm_nt_big, dim3((unsigned)(big / batch), batch), dim3(512), 0, s, g);
+  } else {
+    g.tiles_n = (N + mla::kGemmTile - 1) / mla::kGemmTile;
+    const long long grid = (long long)g.tiles_n * ((M + mla::kGemmTile - 1) / mla::kGemmTile);
+    hipLaunchKernelGGL(mla::mla_gemm_nt, dim3((unsigned)grid, batch), dim3(256), 0, s, g);
+  }
+}
+
 // Y = X W^T, every operand dense row-major (one batch)
 void launch_gemm(const bf16* x, const bf16* w, bf16* y, int M, int N, int K, hipStream_t s) {
-  mla::GemmArgs g{};
-  g.x = x; g.w = w; g.y = y; g.M = M; g.N = N; g.K = K;
-  g.lda = K; g.ldw = K; g.ldy = N; g.alpha = 1.0f;
-  g.tiles_n = (N + mla::kGemmTile - 1) / mla::kGemmTile;
-  const long long grid = (long long)g.tiles_n * ((M + mla::kGemmTile - 1) / mla::kGemmTile);
-  hipLaunchKernelGGL(mla::mla_gemm_nt, dim3((unsigned)grid, 1), dim3(256), 0, s, g);
+  launch_gemm_batched(x, K, 0, w, K, 0, y, N, 0, M, N, K, 1.0f, 1, s);
 }
 
 void launch_rmsnorm(bf16* x, const bf16* gain, int rows, int n, float eps, hipStream_t s) {
@@ -219,17 +234,6 @@ void launch_gemm_tn(const bf16* A, size_t a_bytes, int lda, long long bsa, const
   g.tiles_n = (N + mla::kGemmTile - 1) / mla::kGemmTile;
   const int tiles = g.tiles_n * ((M + mla::kGemmTile - 1) / mla::kGemmTile);
   hipLaunchKernelGGL(mla::mla_gemm_tn, dim3(tiles, batch), dim3(256), 0, s, g);
-}
-
-// Y[z] = alpha X[z] W[z]^T for z < batch, every operand strided
-void launch_gemm_batched(const bf16* x, int lda, long long bsx, const bf16* w, int ldw, long long bsw, bf16* y, int ldy,
-                         long long bsy, int M, int N, int K, float alpha, int batch, hipStream_t s) {
-  mla::GemmArgs g{};
-  g.x = x; g.w = w; g.y = y; g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldw = ldw; g.ldy = ldy;
-  g.bsx = bsx; g.bsw = bsw; g.bsy = bsy; g.alpha = alpha;
-  g.tiles_n = (N + mla::kGemmTile - 1) / mla::kGemmTile;
-  const long long grid = (long long)g.tiles_n * ((M + mla::kGemmTile - 1) / mla::kGemmTile);
-  hipLaunchKernelGGL(mla::mla_gemm_nt, dim3((unsigned)grid, batch), dim3(256), 0, s, g);
 }
 
 // q_abs2[h] = scale log2e q[:, h, :] W_UK[h] and dol[h] = do[h] W_UV[h], as GEMMs
