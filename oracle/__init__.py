@@ -71,13 +71,14 @@ class Oracle:
         L.oracle_cache_append.argtypes = [fp, fp, I64, I, i64p, I, i64p, I, I]
         L.oracle_prefill_backward.argtypes = [fp] * 6 + [I] * 6 + [D] + [dp] * 5 + [I]
         L.oracle_prefill_lse.argtypes = [fp, fp, fp, I, I, I, I, I, D, dp, I]
+        L.oracle_forward_backward.argtypes = [fp] * 11 + [I] * 8 + [D, D] + [dp] * 10 + [I]
         L.oracle_extend_varlen_paged.argtypes = [fp, fp, I64, I, i64p, I, i64p, i64p, fp, fp, fp, I, I, I, I, I, D,
                                                  dp, I]
         L.oracle_forward.argtypes = [fp] * 10 + [I] * 8 + [D, D, I, i64p, I64] + [dp] * 5 + [I]
         for f in ("oracle_prefill", "oracle_extend", "oracle_decode", "oracle_prefill_decompressed",
                   "oracle_prefill_attn", "oracle_round_bf16", "oracle_forward", "oracle_decode_paged",
                   "oracle_extend_paged", "oracle_cache_append", "oracle_prefill_backward",
-                  "oracle_prefill_lse", "oracle_extend_varlen_paged"):
+                  "oracle_prefill_lse", "oracle_extend_varlen_paged", "oracle_forward_backward"):
             getattr(L, f).restype = I
 
     @property
@@ -292,6 +293,32 @@ class Oracle:
                                                 B, T, H, dq, r, float(scale), _ptr(out, ct.c_double), threads),
                     "oracle_prefill_lse")
         return out
+
+    GRAD_KEYS = ("dx", "dw_kv_down", "dkv_norm", "dw_q_down", "dq_norm", "dw_q_up", "dw_uk", "dw_uv", "dw_gate",
+                 "dw_o")
+
+    def forward_backward(self, x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o, dy,
+                         eps: float, scale: float, threads: int = 0) -> dict:
+        """Gradients of the full layer given dy [B,T,D] (stage results of
+        the forward stored as float32): dict keyed by GRAD_KEYS, float64."""
+        x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o, dy = map(
+            _f32, (x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o, dy))
+        B, T, D = x.shape
+        r = w_kv_down.shape[0]
+        q_rank = w_q_down.shape[0]
+        H, dq, _ = w_uk.shape
+        dv = w_uv.shape[1]
+        assert dy.shape == x.shape
+        shapes = dict(dx=x.shape, dw_kv_down=w_kv_down.shape, dkv_norm=kv_norm.shape, dw_q_down=w_q_down.shape,
+                      dq_norm=q_norm.shape, dw_q_up=w_q_up.shape, dw_uk=w_uk.shape, dw_uv=w_uv.shape,
+                      dw_gate=w_gate.shape, dw_o=w_o.shape)
+        g = {k: np.empty(shapes[k], dtype=np.float64) for k in self.GRAD_KEYS}
+        self._check(self.lib.oracle_forward_backward(
+            *[_ptr(a, ct.c_float) for a in (x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate,
+                                             w_o, dy)],
+            B, T, D, q_rank, H, dq, dv, r, float(eps), float(scale), *[_ptr(g[k], ct.c_double) for k in self.GRAD_KEYS],
+            threads), "oracle_forward_backward")
+        return g
 
     def round_bf16(self, v) -> np.ndarray:
         """Nearest bf16 value of each element (ties to even), as float64."""

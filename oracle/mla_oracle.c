@@ -973,3 +973,162 @@ int oracle_prefill_lse(const float* q, const float* c, const float* w_uk, int B,
   }
   return err;
 }
+
+/* ---------------------------------------------------------------------------
+ * Backward of the full Gated MLA layer (the forward of oracle_forward, stage
+ * results stored as float32), given dy = dLoss/dy [B,T,D]: the chain rule
+ * through the output projection, the core (oracle_prefill_backward), the gate
+ * projection, the query up- and down-projections with the query norm, and the
+ * latent down-projection with the latent norm.  For RMSNorm
+ * u = g * v / rms(v), rms = sqrt(mean(v^2) + eps):
+ *   dg   = sum over rows of du * v / rms
+ *   dv_i = (du_i g_i - n_i * mean_j(du_j g_j n_j)) / rms,   n = v / rms
+ * Outputs (float64): dx [B,T,D], dw_kv_down [r,D], dkv_norm [r],
+ * dw_q_down [q_rank,D], dq_norm [q_rank], dw_q_up [H*dq,q_rank],
+ * dw_uk [H,dq,r], dw_uv [H,dv,r], dw_gate [H*dv,D], dw_o [D,H*dv].
+ */
+static void rmsnorm_backward(const double* pre, int64_t M, int n, const float* gain, double eps,
+                             const double* du, double* dpre, double* dgain) {
+  for (int j = 0; j < n; ++j) dgain[j] = 0.0;
+  for (int64_t i = 0; i < M; ++i) {
+    const double* v = pre + i * n;
+    const double* g_ = du + i * n;
+    double ss = 0.0;
+    for (int j = 0; j < n; ++j) ss += v[j] * v[j];
+    const double rms = sqrt(ss / n + eps);
+    double dot = 0.0;
+    for (int j = 0; j < n; ++j) {
+      const double nj = v[j] / rms;
+      dgain[j] += g_[j] * nj;
+      dot += g_[j] * (double)gain[j] * nj;
+    }
+    dot /= n;
+    for (int j = 0; j < n; ++j) {
+#if ORACLE_MUTANT == 27
+      dpre[i * n + j] = g_[j] * (double)gain[j] / rms; /* planted mistake: the norm's projection term dropped */
+#else
+      dpre[i * n + j] = (g_[j] * (double)gain[j] - (v[j] / rms) * dot) / rms;
+#endif
+    }
+  }
+}
+
+/* out[i, k] += sum_n g[i, n] W[n, k] (input gradient of a linear layer, weight [N, K]) */
+static void linear_dx(const double* g, int64_t M, int N, const float* W, int K, double* out) {
+  for (int64_t i = 0; i < M; ++i)
+    for (int n = 0; n < N; ++n) {
+      const double gi = g[i * N + n];
+      if (gi == 0.0) continue;
+      const float* wn = W + (int64_t)n * K;
+      for (int k = 0; k < K; ++k) out[i * K + k] += gi * (double)wn[k];
+    }
+}
+
+/* dW[n, k] = sum_i g[i, n] in[i, k] (weight gradient of a linear layer) */
+static void linear_dw(const double* g, int64_t M, int N, const double* in, int K, double* dW) {
+  memset(dW, 0, sizeof(double) * (size_t)N * K);
+  for (int64_t i = 0; i < M; ++i)
+    for (int n = 0; n < N; ++n) {
+      const double gi = g[i * N + n];
+      for (int k = 0; k < K; ++k) dW[(int64_t)n * K + k] += gi * in[i * K + k];
+    }
+}
+
+int oracle_forward_backward(const float* x, const float* w_kv_down, const float* kv_norm, const float* w_q_down,
+                            const float* q_norm, const float* w_q_up, const float* w_uk, const float* w_uv,
+                            const float* w_gate, const float* w_o, const float* dy, int B, int T, int D, int q_rank,
+                            int H, int dq, int dv, int r, double eps, double scale, double* dx, double* dw_kv_down,
+                            double* dkv_norm, double* dw_q_down, double* dq_norm, double* dw_q_up, double* dw_uk,
+                            double* dw_uv, double* dw_gate, double* dw_o, int nthreads) {
+  if (!x || !w_kv_down || !kv_norm || !w_q_down || !q_norm || !w_q_up || !w_uk || !w_uv || !w_gate || !w_o || !dy ||
+      !dx || !dw_kv_down || !dkv_norm || !dw_q_down || !dq_norm || !dw_q_up || !dw_uk || !dw_uv || !dw_gate || !dw_o)
+    return ORACLE_EINVAL;
+  if (B <= 0 || T <= 0 || D <= 0 || q_rank <= 0 || H <= 0 || dq <= 0 || dv <= 0 || r <= 0 || !(eps >= 0.0))
+    return ORACLE_EINVAL;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  const int64_t N = (int64_t)B * T;
+  const int HQ = H * dq, HV = H * dv;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)N * D);
+  double* c_pre = (double*)malloc(sizeof(double) * (size_t)N * r);
+  double* c = (double*)malloc(sizeof(double) * (size_t)N * r);
+  double* ql_pre = (double*)malloc(sizeof(double) * (size_t)N * q_rank);
+  double* ql = (double*)malloc(sizeof(double) * (size_t)N * q_rank);
+  double* q = (double*)malloc(sizeof(double) * (size_t)N * HQ);
+  double* g = (double*)malloc(sizeof(double) * (size_t)N * HV);
+  double* o = (double*)malloc(sizeof(double) * (size_t)N * HV);
+  double* dyd = (double*)malloc(sizeof(double) * (size_t)N * D);
+  double* dout = (double*)malloc(sizeof(double) * (size_t)N * HV);
+  float* qf = (float*)malloc(sizeof(float) * (size_t)N * HQ);
+  float* cf = (float*)malloc(sizeof(float) * (size_t)N * r);
+  float* gf = (float*)malloc(sizeof(float) * (size_t)N * HV);
+  float* doutf = (float*)malloc(sizeof(float) * (size_t)N * HV);
+  double* dqv = (double*)malloc(sizeof(double) * (size_t)N * HQ);
+  double* dcv = (double*)malloc(sizeof(double) * (size_t)N * r);
+  double* dgv = (double*)malloc(sizeof(double) * (size_t)N * HV);
+  double* dql = (double*)malloc(sizeof(double) * (size_t)N * q_rank);
+  double* dql_pre = (double*)malloc(sizeof(double) * (size_t)N * q_rank);
+  double* dc_pre = (double*)malloc(sizeof(double) * (size_t)N * r);
+  int err = ORACLE_OK;
+  if (!xd || !c_pre || !c || !ql_pre || !ql || !q || !g || !o || !dyd || !dout || !qf || !cf || !gf || !doutf || !dqv ||
+      !dcv || !dgv || !dql || !dql_pre || !dc_pre) {
+    err = ORACLE_ENOMEM;
+    goto done;
+  }
+  for (int64_t i = 0; i < N * D; ++i) {
+    xd[i] = (double)x[i];
+    dyd[i] = (double)dy[i];
+  }
+  /* forward stages, stored as float32 as oracle_forward does */
+  linear(xd, N, D, w_kv_down, r, 0, c_pre, nthreads);
+  store_all(c_pre, N * r, ORACLE_STAGE_F32);
+  memcpy(c, c_pre, sizeof(double) * (size_t)N * r);
+  rmsnorm_rows(c, N, r, kv_norm, eps, 0);
+  store_all(c, N * r, ORACLE_STAGE_F32);
+  linear(xd, N, D, w_q_down, q_rank, 0, ql_pre, nthreads);
+  store_all(ql_pre, N * q_rank, ORACLE_STAGE_F32);
+  memcpy(ql, ql_pre, sizeof(double) * (size_t)N * q_rank);
+  rmsnorm_rows(ql, N, q_rank, q_norm, eps, 1);
+  store_all(ql, N * q_rank, ORACLE_STAGE_F32);
+  linear(ql, N, q_rank, w_q_up, HQ, 0, q, nthreads);
+  store_all(q, N * HQ, ORACLE_STAGE_F32);
+  linear(xd, N, D, w_gate, HV, 0, g, nthreads);
+  store_all(g, N * HV, ORACLE_STAGE_F32);
+  for (int64_t i = 0; i < N * HQ; ++i) qf[i] = (float)q[i];
+  for (int64_t i = 0; i < N * r; ++i) cf[i] = (float)c[i];
+  for (int64_t i = 0; i < N * HV; ++i) gf[i] = (float)g[i];
+  err = oracle_extend(qf, cf, w_uk, w_uv, gf, B, T, T, H, dq, dv, r, scale, NULL, N, o, nthreads);
+  if (err != ORACLE_OK) goto done;
+  store_all(o, N * HV, ORACLE_STAGE_F32);
+
+  /* output projection y = o W_o^T */
+  linear_dw(dyd, N, D, o, HV, dw_o);
+  memset(dout, 0, sizeof(double) * (size_t)N * HV);
+  linear_dx(dyd, N, D, w_o, HV, dout);
+  /* the core */
+  for (int64_t i = 0; i < N * HV; ++i) doutf[i] = (float)dout[i];
+  err = oracle_prefill_backward(qf, cf, w_uk, w_uv, gf, doutf, B, T, H, dq, dv, r, scale, dqv, dcv, dw_uk, dw_uv, dgv,
+                                nthreads);
+  if (err != ORACLE_OK) goto done;
+  /* gate projection */
+  memset(dx, 0, sizeof(double) * (size_t)N * D);
+  linear_dw(dgv, N, HV, xd, D, dw_gate);
+  linear_dx(dgv, N, HV, w_gate, D, dx);
+  /* query path */
+  linear_dw(dqv, N, HQ, ql, q_rank, dw_q_up);
+  memset(dql, 0, sizeof(double) * (size_t)N * q_rank);
+  linear_dx(dqv, N, HQ, w_q_up, q_rank, dql);
+  rmsnorm_backward(ql_pre, N, q_rank, q_norm, eps, dql, dql_pre, dq_norm);
+  linear_dw(dql_pre, N, q_rank, xd, D, dw_q_down);
+#if ORACLE_MUTANT != 28
+  linear_dx(dql_pre, N, q_rank, w_q_down, D, dx);
+#endif
+  /* (mutant 28 plants an input gradient without the query path) */
+  /* latent path */
+  rmsnorm_backward(c_pre, N, r, kv_norm, eps, dcv, dc_pre, dkv_norm);
+  linear_dw(dc_pre, N, r, xd, D, dw_kv_down);
+  linear_dx(dc_pre, N, r, w_kv_down, D, dx);
+done:
+  free(xd); free(c_pre); free(c); free(ql_pre); free(ql); free(q); free(g); free(o); free(dyd); free(dout);
+  free(qf); free(cf); free(gf); free(doutf); free(dqv); free(dcv); free(dgv); free(dql); free(dql_pre); free(dc_pre);
+  return err;
+}

@@ -375,13 +375,15 @@ def pin_forward_norm_scale_invariance(o):
         _close(_fwd(o, e, 0.0, sc), base, 1e-13, 1e-15, f"{key} scaled by {f}")
 
 
-def _brute_forward(d, eps, scale):
+def _brute_forward(d, eps, scale, f64=False):
     """The whole layer in plain Python loops on float64 scalars, attention
     by the decompressed route (k = W_UK[h] c_u, v = W_UV[h] c_u per key),
     written from page "Gated MLA（矩阵吸收版）": section 低秩压缩 (c), section
     矩阵吸收的核心思路 (the standard route), section 完整计算流（四步） steps 1-4."""
     import math
-    f = {k: dg.as_f32(d[k]).astype(np.float64).tolist() for k in dg.FORWARD_KEYS}
+    # f64: take the values as float64 (finite differences), else as float32
+    f = {k: (np.asarray(d[k], np.float64) if f64 else dg.as_f32(d[k]).astype(np.float64)).tolist()
+         for k in dg.FORWARD_KEYS}
     B, T, D, q_rank, H, dq, dv, r = (d[k] for k in ("B", "T", "D", "q_rank", "H", "d_q", "d_v", "r"))
 
     def lin(vec, W):
@@ -611,6 +613,42 @@ def pin_varlen_mixed_batch(o):
     _close(got[cu_q[2]:cu_q[3]], dec, 1e-13, 1e-15, "varlen decode step")
 
 
+def pin_layer_backward_finite_differences(o):
+    """Every element of every gradient of the full layer (dx and the ten
+    parameter tensors) against a central finite difference of sum(dy * y),
+    y from the plain-loop float64 brute force of the layer above
+    (_brute_forward, decompressed attention route), with eps > 0.  The
+    oracle stores the forward's stage results as float32, which the
+    tolerance covers."""
+    B, T, D, q_rank, H, dq, dv, r, eps, scale = 1, 3, 6, 4, 2, 2, 3, 5, 1e-2, 0.7
+    d = dg.forward_inputs(B, T, D, q_rank, H, dq, dv, r, dtype=dg.F32, seed=131)
+    dy = np.random.default_rng(131).standard_normal((B, T, D)).astype(np.float32)
+    g = o.forward_backward(*[dg.as_f32(d[k]) for k in dg.FORWARD_KEYS], dy, eps, scale)
+    base = {k: dg.as_f32(d[k]).astype(np.float64) for k in dg.FORWARD_KEYS}
+    dy64 = dy.astype(np.float64)
+
+    def loss(p):
+        e = dict(d)
+        e.update(p)
+        return float(np.sum(dy64 * _brute_forward(e, eps, scale, f64=True)))
+
+    step = 1e-5
+    names = dict(x="dx", w_kv_down="dw_kv_down", kv_norm="dkv_norm", w_q_down="dw_q_down", q_norm="dq_norm",
+                 w_q_up="dw_q_up", w_uk="dw_uk", w_uv="dw_uv", w_gate="dw_gate", w_o="dw_o")
+    for key, gk in names.items():
+        xv = base[key]
+        fd = np.empty(xv.size)
+        for i in range(xv.size):
+            orig = xv.flat[i]
+            xv.flat[i] = orig + step
+            lp = loss(base)
+            xv.flat[i] = orig - step
+            lm = loss(base)
+            xv.flat[i] = orig
+            fd[i] = (lp - lm) / (2 * step)
+        _close(g[gk].reshape(-1), fd, 2e-5, 2e-6, f"{gk} vs finite differences")
+
+
 ALL_PINS = [
     pin_absorbed_equals_decompressed,
     pin_attention_rows,
@@ -637,4 +675,5 @@ ALL_PINS = [
     pin_backward_special_cases,
     pin_lse_matches_library,
     pin_varlen_mixed_batch,
+    pin_layer_backward_finite_differences,
 ]

@@ -36,6 +36,8 @@ MUTANTS = {
     24: "backward: gate gradient uses the sigmoid, not its derivative",
     25: "backward: query-side gradient missing the softmax scale",
     26: "varlen: the chunk placed at the start of its sequence",
+    27: "layer backward: the norm's projection term dropped",
+    28: "layer backward: input gradient without the query path",
 }
 
 
