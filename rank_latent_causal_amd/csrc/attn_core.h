@@ -83,6 +83,7 @@ struct TileCopier {
     p.lb = lane_base();
     int rows = row_end - row0;
     rows = rows > KT ? KT : rows;
+    rows = rows < 0 ? 0 : rows;  // a tile wholly past row_end reads as zeros
     p.rs = make_rsrc(base + (size_t)row0 * R, (unsigned)(rows * R * 2));
     p.stage = stage;
     return p;

@@ -71,10 +71,10 @@ struct BwdPrepArgs {
   const bf16* out;    // [B*T, H*DV]  forward output
   const bf16* dout;   // [B*T, H*DV]
   const float* lse;   // [B, H, T]    forward log-sum-exp (natural log)
-  bf16* dgate;        // [B*T, H*DV]
+  bf16* dgate;        // [B*T, H*DV], rows ldg apart
   bf16* dov;          // [H, B*T, DV] do = dout * sigmoid(g)
   float* ld;          // [H, B*T, 2]
-  int B, T, H, DV;
+  int B, T, H, DV, ldg;
 };
 
 // One workgroup per token row; wave w takes heads w, w+4, ...; lanes walk the
@@ -89,7 +89,7 @@ __global__ void __launch_bounds__(256) mla_bwd_prep(BwdPrepArgs a) {
       const size_t i = row + (size_t)h * a.DV + v;
       const float g = (float)a.gate[i], o = (float)a.out[i], d = (float)a.dout[i];
       const float s = sigmoidf_(g);
-      a.dgate[i] = (bf16)(d * o * (1.0f - s));
+      a.dgate[(size_t)bt * a.ldg + (size_t)h * a.DV + v] = (bf16)(d * o * (1.0f - s));
       a.dov[((size_t)h * a.B * a.T + bt) * a.DV + v] = (bf16)(d * s);
       dsum += d * o;
     }
@@ -351,9 +351,12 @@ mla_bwd_key(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kr = 16 * kt + 4 * kq + i, kpos = k0 + kr;
-        const float p = (kpos <= qpos && qpos < T) ? fast_exp2(sacc[i] - L2) : 0.0f;
+        // a query past T has no {lse, D} pair of its own: the staged bytes
+        // there may be anything, so both products are selected, not scaled, to zero
+        const bool live = kpos <= qpos && qpos < T;
+        const float p = live ? fast_exp2(sacc[i] - L2) : 0.0f;
         Pb[kr * kPPitch + q] = (bf16)p;
-        dSb[kr * kPPitch + q] = (bf16)(p * (dacc[i] - Dq) * 0.69314718055994531f);
+        dSb[kr * kPPitch + q] = live ? (bf16)(p * (dacc[i] - Dq) * 0.69314718055994531f) : (bf16)0.0f;
       }
     }
     wait_lgkmcnt0();

@@ -143,3 +143,45 @@ def test_backward_workspace_reuse_and_repeat():
     torch.cuda.synchronize()
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("B,T,H,shape", [(1, 1, 8, "toy"), (1, 33, 3, "full"), (2, 1, 5, "mid")])
+def test_backward_poisoned_workspace(o, B, T, H, shape):
+    """Every workspace byte set to 0xFF (NaN in bf16 and fp32) before the
+    call: a read of a byte the call did not write first shows up as a
+    non-finite or wrong gradient.  The last query block holds an odd number
+    of rows here, where the staged {lse, D} pairs end mid-copy.  At T = 1 the
+    single key's softmax weight is 1 whatever the score, so dq and dW_UK are
+    exactly zero in the oracle and rounding noise of P (dP - D) in the
+    library: they must be finite and under 2^-7 of the size dq has at the
+    same inputs' T = 2; the other gradients meet the usual bar."""
+    import torch
+    import rank_latent_causal_amd as mla
+    d, dout = _case(B, T, H, shape, seed=9300 + T + H)
+    dq_, dv_, r_ = SHAPES[shape]
+    ws = torch.full((mla.backward_workspace_size(B, T, H, dq_, dv_, r_, mla.DTYPE_BF16),), 255, dtype=torch.uint8,
+                    device="cuda")
+    f = dg.as_f32
+    args64 = [f(d[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")]
+    ref_out = o.prefill(*args64, d["scale"])
+    ref_lse = o.prefill_lse(f(d["q"]), f(d["c"]), f(d["w_uk"]), d["scale"])
+    want = o.prefill_backward(*args64, f(dout), d["scale"])
+    log(f"backward poisoned workspace {shape} B={B} T={T} H={H}")
+    out_b = dg.f32_to_bf16_bits(ref_out.astype(np.float32))
+    g = mla.mla_absorb_prefill_backward(*[to_dev(d[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")], to_dev(out_b),
+                                        to_dev(ref_lse.astype(np.float32)), to_dev(dout), d["scale"], workspace=ws)
+    torch.cuda.synchronize()
+    for k in ("dgate", "dq", "dc", "dw_uk", "dw_uv"):
+        got = to_host_f64(g[k])
+        assert np.all(np.isfinite(got)), f"{k}: non-finite values"
+        if T == 1 and k in ("dq", "dw_uk"):
+            assert np.all(want[k] == 0.0), f"oracle {k} at T=1 is not zero"
+            continue
+        _grad_close(got, want[k], f"{k} ({shape} B{B} T{T} H{H}, poisoned workspace)")
+    if T == 1:
+        # the query-side noise against the size of dq one position later
+        d2, dout2 = _case(B, 2, H, shape, seed=9300 + T + H)
+        want2 = o.prefill_backward(*[f(d2[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")], f(dout2), d2["scale"])
+        for k in ("dq", "dw_uk"):
+            noise = np.linalg.norm(to_host_f64(g[k]))
+            assert noise <= 2.0 ** -7 * np.linalg.norm(want2[k]), f"{k}: T=1 noise {noise:.3g}"
