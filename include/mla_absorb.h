@@ -283,6 +283,63 @@ mla_status mla_gated_forward(const void* x, const void* w_kv_down, const void* k
                              int H, int d_q, int d_v, int r, float eps, float scale, mla_dtype dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of the saved state mla_gated_forward_train keeps for
+ * mla_gated_backward (bf16 only; (size_t)-1 for invalid sizes or dtypes).
+ */
+size_t mla_gated_train_state_size(int B, int T, int q_rank, int H, int d_q, int d_v, int r, mla_dtype dtype);
+
+/*
+ * Training form of mla_gated_forward: the same y (same arithmetic, same
+ * conventions and errors), and the caller-owned buffer `state`
+ * (mla_gated_train_state_size bytes, 16-byte aligned) receives what the
+ * backward reads: the inputs of the two RMSNorms and their 1/rms, their
+ * outputs, q, the gate pre-activations, the gated core output and the
+ * core's log-sum-exp (as mla_absorb_prefill_train).  The layout of `state`
+ * is private to this library; it stays valid until the caller overwrites
+ * it.  MLA_ERR_WORKSPACE if state is null, misaligned or too small.
+ */
+mla_status mla_gated_forward_train(const void* x, const void* w_kv_down, const void* kv_norm, const void* w_q_down,
+                                   const void* q_norm, const void* w_q_up, const void* w_uk, const void* w_uv,
+                                   const void* w_gate, const void* w_o, void* y, int B, int T, int D, int q_rank,
+                                   int H, int d_q, int d_v, int r, float eps, float scale, mla_dtype dtype,
+                                   void* state, size_t state_bytes, void* stream);
+
+/*
+ * Bytes of workspace mla_gated_backward needs (bf16 only; (size_t)-1 for
+ * invalid sizes or dtypes).
+ */
+size_t mla_gated_backward_workspace_size(int B, int T, int D, int q_rank, int H, int d_q, int d_v, int r,
+                                         mla_dtype dtype);
+
+/*
+ * Backward of the full Gated MLA layer (page "Gated MLA（矩阵吸收版）":
+ * section 低秩压缩 and section 完整计算流（四步） steps 1-4, differentiated by
+ * the chain rule) given dy = dLoss/dy [B, T, D] and the `state` that
+ * mla_gated_forward_train left for the same x and weights:
+ *   output projection  dO = dy W_o,           dW_o = dy^T o
+ *   core               dq, dc, dgate, dW_UK, dW_UV as mla_absorb_prefill_backward
+ *   query path         dql = dq W_q_up,       dW_q_up = dq^T ql
+ *   the two RMSNorms   u = g v rstd:  dv = (du g - n mean(du g n)) rstd with
+ *                      n = v rstd, and dg = sum over tokens of du n
+ *   products of x      dx = dgate W_gate + dql_pre W_q_down + dc_pre W_kv_down,
+ *                      dW_gate = dgate^T x, dW_q_down = dql_pre^T x,
+ *                      dW_kv_down = dc_pre^T x.
+ * Weights and x as for mla_gated_forward; dy and dx bf16 [B, T, D]; every
+ * parameter gradient is float32 in the shape of its parameter (dkv_norm [r],
+ * dq_norm [q_rank]), written, not accumulated.  bf16 only; shape limits of
+ * mla_gated_forward and of mla_absorb_prefill_backward.  MLA_ERR_INVALID_ARG
+ * also for a null, misaligned or too small state; workspace:
+ * mla_gated_backward_workspace_size bytes, 16-byte aligned.
+ */
+mla_status mla_gated_backward(const void* x, const void* w_kv_down, const void* kv_norm, const void* w_q_down,
+                              const void* q_norm, const void* w_q_up, const void* w_uk, const void* w_uv,
+                              const void* w_gate, const void* w_o, const void* dy, const void* state,
+                              size_t state_bytes, void* dx, float* dw_kv_down, float* dkv_norm, float* dw_q_down,
+                              float* dq_norm, float* dw_q_up, float* dw_uk, float* dw_uv, float* dw_gate,
+                              float* dw_o, int B, int T, int D, int q_rank, int H, int d_q, int d_v, int r,
+                              float scale, mla_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1015,6 +1015,7 @@ static void rmsnorm_backward(const double* pre, int64_t M, int n, const float* g
 
 /* out[i, k] += sum_n g[i, n] W[n, k] (input gradient of a linear layer, weight [N, K]) */
 static void linear_dx(const double* g, int64_t M, int N, const float* W, int K, double* out) {
+#pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < M; ++i)
     for (int n = 0; n < N; ++n) {
       const double gi = g[i * N + n];
@@ -1027,9 +1028,11 @@ static void linear_dx(const double* g, int64_t M, int N, const float* W, int K, 
 /* dW[n, k] = sum_i g[i, n] in[i, k] (weight gradient of a linear layer) */
 static void linear_dw(const double* g, int64_t M, int N, const double* in, int K, double* dW) {
   memset(dW, 0, sizeof(double) * (size_t)N * K);
-  for (int64_t i = 0; i < M; ++i)
-    for (int n = 0; n < N; ++n) {
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n)
+    for (int64_t i = 0; i < M; ++i) {
       const double gi = g[i * N + n];
+      if (gi == 0.0) continue;
       for (int k = 0; k < K; ++k) dW[(int64_t)n * K + k] += gi * in[i * K + k];
     }
 }

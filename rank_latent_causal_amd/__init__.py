@@ -20,7 +20,8 @@ __all__ = [
     "mla_absorb_prefill", "mla_absorb_extend", "mla_absorb_extend_paged", "mla_absorb_decode",
     "mla_absorb_decode_paged", "mla_cache_append_paged", "mla_gated_forward", "mla_absorb_prefill_train",
     "backward_workspace_size", "mla_absorb_prefill_backward", "varlen_workspace_size",
-    "mla_absorb_extend_varlen_paged",
+    "mla_absorb_extend_varlen_paged", "train_state_size", "mla_gated_forward_train",
+    "layer_backward_workspace_size", "mla_gated_backward", "LAYER_GRAD_KEYS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_absorb.so")
@@ -46,6 +47,10 @@ EXPORTS = (
     "mla_absorb_prefill_backward",
     "mla_gated_forward_workspace_size",
     "mla_gated_forward",
+    "mla_gated_train_state_size",
+    "mla_gated_forward_train",
+    "mla_gated_backward_workspace_size",
+    "mla_gated_backward",
 )
 
 _lib = None
@@ -99,6 +104,14 @@ def lib() -> ct.CDLL:
         L.mla_gated_forward_workspace_size.restype = sz
         L.mla_gated_forward.argtypes = [vp] * 11 + [I] * 8 + [F, F, I, vp, sz, vp]
         L.mla_gated_forward.restype = I
+        L.mla_gated_train_state_size.argtypes = [I] * 8
+        L.mla_gated_train_state_size.restype = sz
+        L.mla_gated_forward_train.argtypes = [vp] * 11 + [I] * 8 + [F, F, I, vp, sz, vp]
+        L.mla_gated_forward_train.restype = I
+        L.mla_gated_backward_workspace_size.argtypes = [I] * 9
+        L.mla_gated_backward_workspace_size.restype = sz
+        L.mla_gated_backward.argtypes = [vp] * 12 + [sz] + [vp] * 10 + [I] * 8 + [F, I, vp, sz, vp]
+        L.mla_gated_backward.restype = I
         _lib = L
     return _lib
 
@@ -149,6 +162,21 @@ def forward_workspace_size(B: int, T: int, q_rank: int, H: int, d_q: int, d_v: i
     n = lib().mla_gated_forward_workspace_size(B, T, q_rank, H, d_q, d_v, r, dtype)
     if n == _BAD:
         raise MLAError(MLA_ERR_INVALID_ARG, "mla_gated_forward_workspace_size")
+    return n
+
+
+def train_state_size(B: int, T: int, q_rank: int, H: int, d_q: int, d_v: int, r: int, dtype: int) -> int:
+    n = lib().mla_gated_train_state_size(B, T, q_rank, H, d_q, d_v, r, dtype)
+    if n == _BAD:
+        raise MLAError(MLA_ERR_INVALID_ARG, "mla_gated_train_state_size")
+    return n
+
+
+def layer_backward_workspace_size(B: int, T: int, D: int, q_rank: int, H: int, d_q: int, d_v: int, r: int,
+                                  dtype: int) -> int:
+    n = lib().mla_gated_backward_workspace_size(B, T, D, q_rank, H, d_q, d_v, r, dtype)
+    if n == _BAD:
+        raise MLAError(MLA_ERR_INVALID_ARG, "mla_gated_backward_workspace_size")
     return n
 
 
@@ -481,3 +509,77 @@ def mla_gated_forward(x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_u
     if st != MLA_OK:
         raise MLAError(st, "mla_gated_forward")
     return out
+
+
+def _layer_dims(x, w_kv_down, w_q_down, w_uk, w_uv):
+    B, T, D = x.shape
+    return B, T, D, w_q_down.shape[0], w_uk.shape[0], w_uk.shape[1], w_uv.shape[1], w_kv_down.shape[0]
+
+
+def _check_layer_weights(x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o):
+    B, T, D, q_rank, H, dq, dv, r = _layer_dims(x, w_kv_down, w_q_down, w_uk, w_uv)
+    dt = x.dtype
+    for t, shp, n in ((x, (B, T, D), "x"), (w_kv_down, (r, D), "w_kv_down"), (kv_norm, (r,), "kv_norm"),
+                      (w_q_down, (q_rank, D), "w_q_down"), (q_norm, (q_rank,), "q_norm"),
+                      (w_q_up, (H * dq, q_rank), "w_q_up"), (w_uk, (H, dq, r), "w_uk"), (w_uv, (H, dv, r), "w_uv"),
+                      (w_gate, (H * dv, D), "w_gate"), (w_o, (D, H * dv), "w_o")):
+        _check(t, shp, dt, n)
+
+
+def mla_gated_forward_train(x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o,
+                            eps: float, scale: float, out=None, state=None, stream=None):
+    """Training form of mla_gated_forward: returns (y, state), state a uint8
+    device buffer that mla_gated_backward reads."""
+    torch = _torch()
+    _check_layer_weights(x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o)
+    B, T, D, q_rank, H, dq, dv, r = _layer_dims(x, w_kv_down, w_q_down, w_uk, w_uv)
+    code = _dtype_code(x)
+    if out is None:
+        out = torch.empty((B, T, D), dtype=x.dtype, device=x.device)
+    _check(out, (B, T, D), x.dtype, "out")
+    need = train_state_size(B, T, q_rank, H, dq, dv, r, code)
+    if state is None:
+        state = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib().mla_gated_forward_train(x.data_ptr(), w_kv_down.data_ptr(), kv_norm.data_ptr(), w_q_down.data_ptr(),
+                                       q_norm.data_ptr(), w_q_up.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+                                       w_gate.data_ptr(), w_o.data_ptr(), out.data_ptr(), B, T, D, q_rank, H, dq, dv,
+                                       r, float(eps), float(scale), code, state.data_ptr(),
+                                       state.numel() * state.element_size(), _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_gated_forward_train")
+    return out, state
+
+
+LAYER_GRAD_KEYS = ("dx", "dw_kv_down", "dkv_norm", "dw_q_down", "dq_norm", "dw_q_up", "dw_uk", "dw_uv", "dw_gate",
+                   "dw_o")
+
+
+def mla_gated_backward(x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o, dy, state,
+                       scale: float, grads=None, workspace=None, stream=None) -> dict:
+    """Backward of the full layer: dict keyed by LAYER_GRAD_KEYS (dx bf16
+    like x, every parameter gradient float32 in its parameter's shape)."""
+    torch = _torch()
+    _check_layer_weights(x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o)
+    B, T, D, q_rank, H, dq, dv, r = _layer_dims(x, w_kv_down, w_q_down, w_uk, w_uv)
+    _check(dy, (B, T, D), x.dtype, "dy")
+    code = _dtype_code(x)
+    shapes = dict(dx=(B, T, D), dw_kv_down=(r, D), dkv_norm=(r,), dw_q_down=(q_rank, D), dq_norm=(q_rank,),
+                  dw_q_up=(H * dq, q_rank), dw_uk=(H, dq, r), dw_uv=(H, dv, r), dw_gate=(H * dv, D), dw_o=(D, H * dv))
+    if grads is None:
+        grads = {k: torch.empty(shapes[k], dtype=x.dtype if k == "dx" else torch.float32, device=x.device)
+                 for k in LAYER_GRAD_KEYS}
+    for k in LAYER_GRAD_KEYS:
+        _check(grads[k], shapes[k], x.dtype if k == "dx" else torch.float32, k)
+    need = layer_backward_workspace_size(B, T, D, q_rank, H, dq, dv, r, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    st = lib().mla_gated_backward(x.data_ptr(), w_kv_down.data_ptr(), kv_norm.data_ptr(), w_q_down.data_ptr(),
+                                  q_norm.data_ptr(), w_q_up.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+                                  w_gate.data_ptr(), w_o.data_ptr(), dy.data_ptr(), state.data_ptr(),
+                                  state.numel() * state.element_size(),
+                                  *[grads[k].data_ptr() for k in LAYER_GRAD_KEYS], B, T, D, q_rank, H, dq, dv, r,
+                                  float(scale), code, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_gated_backward")
+    return grads

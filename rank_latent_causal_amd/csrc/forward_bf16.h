@@ -9,8 +9,10 @@
 namespace mla {
 
 struct RmsNormArgs {
-  bf16* x;           // [rows, n], normalised in place
+  const bf16* x;     // [rows, n]
+  bf16* y;           // [rows, n] the normalised rows (may be x itself)
   const bf16* gain;  // [n]
+  float* rstd;       // [rows] 1 / sqrt(mean(x^2) + eps), kept for the backward (null: not kept)
   int rows, n;
   float eps;         // added to the mean square inside the square root
 };
@@ -22,7 +24,8 @@ constexpr int kNormMaxChunks = 4;  // n <= 2048
 __global__ void __launch_bounds__(256) mla_rmsnorm_rows(RmsNormArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= a.rows) return;
-  bf16* xr = a.x + (size_t)row * a.n;
+  const bf16* xr = a.x + (size_t)row * a.n;
+  bf16* yr = a.y + (size_t)row * a.n;
   bf16x8 v[kNormMaxChunks];
   float ss = 0.0f;
 #pragma unroll
@@ -35,6 +38,7 @@ __global__ void __launch_bounds__(256) mla_rmsnorm_rows(RmsNormArgs a) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
   const float inv = 1.0f / __builtin_sqrtf(ss / (float)a.n + a.eps);
+  if (a.rstd && lane == 0) a.rstd[row] = inv;
 #pragma unroll
   for (int u = 0; u < kNormMaxChunks; ++u) {
     const int j = 8 * (lane + 64 * u);
@@ -43,7 +47,7 @@ __global__ void __launch_bounds__(256) mla_rmsnorm_rows(RmsNormArgs a) {
       bf16x8 o;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = (bf16)((float)v[u][e] * inv * (float)g[e]);
-      *(bf16x8*)(xr + j) = o;
+      *(bf16x8*)(yr + j) = o;
     }
   }
 }

@@ -13,6 +13,7 @@
 #include "f32_kernels.h"
 #include "forward_bf16.h"
 #include "gemm_bf16.h"
+#include "layer_backward_bf16.h"
 #include "prefill_bf16.h"
 
 namespace {
@@ -193,9 +194,11 @@ void launch_gemm(const bf16* x, const bf16* w, bf16* y, int M, int N, int K, hip
   launch_gemm_batched(x, K, 0, w, K, 0, y, N, 0, M, N, K, 1.0f, 1, s);
 }
 
-void launch_rmsnorm(bf16* x, const bf16* gain, int rows, int n, float eps, hipStream_t s) {
+// y = RMSNorm(x) * gain row by row (y may be x); rstd (or null) receives 1/rms
+void launch_rmsnorm(const bf16* x, bf16* y, const bf16* gain, float* rstd, int rows, int n, float eps,
+                    hipStream_t s) {
   mla::RmsNormArgs a{};
-  a.x = x; a.gain = gain; a.rows = rows; a.n = n; a.eps = eps;
+  a.x = x; a.y = y; a.gain = gain; a.rstd = rstd; a.rows = rows; a.n = n; a.eps = eps;
   hipLaunchKernelGGL(mla::mla_rmsnorm_rows, dim3((rows + 3) / 4), dim3(256), 0, s, a);
 }
 
@@ -279,6 +282,80 @@ void launch_varlen_bf16(mla::PrefillArgs a, const int* cu_q, const int* seq_lens
     hipLaunchKernelGGL((mla::mla_prefill_bf16_kernel<DQ, DV, R, true, true>), dim3(max_blocks * a.nhg),
                        dim3(64 * mla::kPrefillWaves), 0, s, a);
   }
+}
+
+// Saved state of a training forward of the full layer: what the backward
+// reads (the norms' inputs and 1/rms, their outputs, q, the gate, the gated
+// core output and the core's log-sum-exp) plus the core's own workspace.
+struct TrainLayout {
+  size_t c_pre = 0, c = 0, rstd_c = 0, ql_pre = 0, ql = 0, rstd_q = 0, q = 0, gate = 0, o = 0, lse = 0, core = 0,
+         total = 0;
+};
+
+TrainLayout train_layout(int B, int T, int q_rank, int H, int dq, int dv, int r) {
+  const size_t N = (size_t)B * T;
+  TrainLayout L;
+  size_t off = 0;
+  L.c_pre = off;  off = align_up(off + N * r * sizeof(bf16));
+  L.c = off;      off = align_up(off + N * r * sizeof(bf16));
+  L.rstd_c = off; off = align_up(off + N * sizeof(float));
+  L.ql_pre = off; off = align_up(off + N * q_rank * sizeof(bf16));
+  L.ql = off;     off = align_up(off + N * q_rank * sizeof(bf16));
+  L.rstd_q = off; off = align_up(off + N * sizeof(float));
+  L.q = off;      off = align_up(off + N * H * dq * sizeof(bf16));
+  L.gate = off;   off = align_up(off + N * H * dv * sizeof(bf16));
+  L.o = off;      off = align_up(off + N * H * dv * sizeof(bf16));
+  L.lse = off;    off = align_up(off + N * H * sizeof(float));
+  L.core = off;   off = align_up(off + (size_t)H * r * dq * sizeof(bf16));
+  L.total = off;
+  return L;
+}
+
+constexpr int kNormBwdGroups = 256;  // workgroups of the RMSNorm backward (partial rows of the gain gradient)
+
+// Workspace of the layer backward.  gcat [N, Kc] holds, side by side, the
+// gradients of the three products of x (gate pre-activations, query and
+// latent down-projections before their norms), Kc = H dv + q_rank + r, so
+// that dx is one product with the matching transposed weights wcatT [D, Kc].
+struct LayerBwdLayout {
+  size_t gcat = 0, dout = 0, dq = 0, dc = 0, dql = 0, woT = 0, wqupT = 0, wcatT = 0, part = 0, core = 0, total = 0;
+  int Kc = 0;
+};
+
+LayerBwdLayout layer_bwd_layout(int B, int T, int D, int q_rank, int H, int dq, int dv, int r) {
+  const size_t N = (size_t)B * T;
+  LayerBwdLayout L;
+  L.Kc = H * dv + q_rank + r;
+  size_t off = 0;
+  L.gcat = off;  off = align_up(off + N * L.Kc * sizeof(bf16));
+  L.dout = off;  off = align_up(off + N * H * dv * sizeof(bf16));
+  L.dq = off;    off = align_up(off + N * H * dq * sizeof(bf16));
+  L.dc = off;    off = align_up(off + N * r * sizeof(bf16));
+  L.dql = off;   off = align_up(off + N * q_rank * sizeof(bf16));
+  L.woT = off;   off = align_up(off + (size_t)H * dv * D * sizeof(bf16));
+  L.wqupT = off; off = align_up(off + (size_t)q_rank * H * dq * sizeof(bf16));
+  L.wcatT = off; off = align_up(off + (size_t)D * L.Kc * sizeof(bf16));
+  L.part = off;  off = align_up(off + (size_t)kNormBwdGroups * (q_rank > r ? q_rank : r) * sizeof(float));
+  L.core = off;  off = align_up(off + backward_layout(B, T, H, dq, dv, r).total);
+  L.total = off;
+  return L;
+}
+
+// dst[:, col0 + i] = src[i, :]^T for src [rows, cols]: dst rows ld_dst apart
+void launch_transpose_into(const bf16* src, int rows, int cols, bf16* dst, long long ld_dst, hipStream_t s) {
+  hipLaunchKernelGGL(mla::mla_transpose_into, dim3((cols + 31) / 32, (rows + 31) / 32), dim3(256), 0, s, src, rows,
+                     cols, dst, ld_dst);
+}
+
+// RMSNorm backward of rows [rows, n] and the gain gradient dgain [n]
+void launch_rmsnorm_backward(const bf16* du, int ld_du, const bf16* v, const float* rstd, const bf16* gain, bf16* dv,
+                             int ld_dv, float* part, float* dgain, int rows, int n, hipStream_t s) {
+  mla::RmsNormBwdArgs a{};
+  a.du = du; a.v = v; a.rstd = rstd; a.gain = gain; a.dv = dv; a.part = part;
+  a.rows = rows; a.n = n; a.ld_du = ld_du; a.ld_dv = ld_dv;
+  const int groups = (rows + 3) / 4 < kNormBwdGroups ? (rows + 3) / 4 : kNormBwdGroups;
+  hipLaunchKernelGGL(mla::mla_rmsnorm_backward, dim3(groups), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(mla::mla_colsum_f32, dim3((n + 255) / 256), dim3(256), 0, s, part, groups, n, dgain);
 }
 
 size_t varlen_meta_bytes(int B, int Nq) {
@@ -606,11 +683,13 @@ size_t mla_absorb_prefill_backward_workspace_size(int B, int T, int H, int d_q, 
   return backward_layout(B, T, H, d_q, d_v, r).total;
 }
 
-mla_status mla_absorb_prefill_backward(const void* q, const void* c, const void* w_uk, const void* w_uv,
-                                       const void* gate, const void* out, const float* lse, const void* dout,
-                                       void* dq, void* dc, float* dw_uk, float* dw_uv, void* dgate, int B, int T,
-                                       int H, int d_q, int d_v, int r, float scale, mla_dtype dtype, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
+// The core backward; dgate rows are ldg elements apart (H d_v for the
+// entry point, wider inside the layer backward's side-by-side gradients).
+static mla_status prefill_backward_impl(const void* q, const void* c, const void* w_uk, const void* w_uv,
+                                        const void* gate, const void* out, const float* lse, const void* dout,
+                                        void* dq, void* dc, float* dw_uk, float* dw_uv, void* dgate, int ldg, int B,
+                                        int T, int H, int d_q, int d_v, int r, float scale, mla_dtype dtype,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
   const void* ptrs[] = {q, c, w_uk, w_uv, gate, out, lse, dout, dq, dc, dw_uk, dw_uv, dgate};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return MLA_ERR_INVALID_ARG;
@@ -632,7 +711,7 @@ mla_status mla_absorb_prefill_backward(const void* q, const void* c, const void*
   mla::BwdPrepArgs pa{};
   pa.gate = (const bf16*)gate; pa.out = (const bf16*)out; pa.dout = (const bf16*)dout; pa.lse = lse;
   pa.dgate = (bf16*)dgate; pa.dov = (bf16*)(ws + L.dov); pa.ld = (float*)(ws + L.ld);
-  pa.B = B; pa.T = T; pa.H = H; pa.DV = d_v;
+  pa.B = B; pa.T = T; pa.H = H; pa.DV = d_v; pa.ldg = ldg;
   bf16* wukT = (bf16*)(ws + L.wukT);
   bf16* wuvT = (bf16*)(ws + L.wuvT);
   launch_wuk_transpose((const bf16*)w_uk, wukT, H, d_q, r, s);
@@ -660,6 +739,15 @@ mla_status mla_absorb_prefill_backward(const void* q, const void* c, const void*
   launch_gemm_tn(ba.dv, dv_bytes, d_v, BT * d_v, (const bf16*)c, c_bytes, r, 0, dw_uv, (long long)d_v * r, d_v, r,
                  (int)BT, H, s);
   return launch_status();
+}
+
+mla_status mla_absorb_prefill_backward(const void* q, const void* c, const void* w_uk, const void* w_uv,
+                                       const void* gate, const void* out, const float* lse, const void* dout,
+                                       void* dq, void* dc, float* dw_uk, float* dw_uv, void* dgate, int B, int T,
+                                       int H, int d_q, int d_v, int r, float scale, mla_dtype dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return prefill_backward_impl(q, c, w_uk, w_uv, gate, out, lse, dout, dq, dc, dw_uk, dw_uv, dgate, H * d_v, B, T, H,
+                               d_q, d_v, r, scale, dtype, workspace, workspace_bytes, stream);
 }
 
 size_t mla_gated_forward_workspace_size(int B, int T, int q_rank, int H, int d_q, int d_v, int r,
@@ -704,10 +792,10 @@ mla_status mla_gated_forward(const void* x, const void* w_kv_down, const void* k
   bf16* o = (bf16*)(ws + L.o);
   // latent: c = RMSNorm(W_down x)
   launch_gemm(xb, (const bf16*)w_kv_down, c, N, r, D, s);
-  launch_rmsnorm(c, (const bf16*)kv_norm, N, r, eps, s);
+  launch_rmsnorm(c, c, (const bf16*)kv_norm, nullptr, N, r, eps, s);
   // query low-rank path: q = W_q_up RMSNorm(W_q_down x)
   launch_gemm(xb, (const bf16*)w_q_down, ql, N, q_rank, D, s);
-  launch_rmsnorm(ql, (const bf16*)q_norm, N, q_rank, eps, s);
+  launch_rmsnorm(ql, ql, (const bf16*)q_norm, nullptr, N, q_rank, eps, s);
   launch_gemm(ql, (const bf16*)w_q_up, q, N, H * d_q, q_rank, s);
   // gate pre-activations
   launch_gemm(xb, (const bf16*)w_gate, gate, N, H * d_v, D, s);
@@ -717,6 +805,150 @@ mla_status mla_gated_forward(const void* x, const void* w_kv_down, const void* k
   if (st != MLA_OK) return st;
   // output projection
   launch_gemm(o, (const bf16*)w_o, (bf16*)y, N, D, H * d_v, s);
+  return launch_status();
+}
+
+
+// Shape checks shared by the full-layer forward, its training form and its backward.
+static mla_status layer_shape_check(int B, int T, int D, int q_rank, int H, int d_q, int d_v, int r) {
+  if (B <= 0 || T <= 0 || D <= 0 || q_rank <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!bf16_shape_supported(d_q, d_v, r)) return MLA_ERR_UNSUPPORTED;
+  // projection contractions come in 64-wide k tiles; normalised rows fit one wave
+  if (D % 64 || q_rank % 64 || (H * d_v) % 64 || (H * d_q) % 8 || D % 8 || r % 8 || q_rank % 8)
+    return MLA_ERR_UNSUPPORTED;
+  if (r > 64 * 8 * mla::kNormMaxChunks || q_rank > 64 * 8 * mla::kNormMaxChunks) return MLA_ERR_UNSUPPORTED;
+  if (!fits(B, T, D) || !fits(B, T, H, d_q > d_v ? d_q : d_v) || (long long)B * T >= (1LL << 31))
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+size_t mla_gated_train_state_size(int B, int T, int q_rank, int H, int d_q, int d_v, int r, mla_dtype dtype) {
+  if (B <= 0 || T <= 0 || q_rank <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return kBadSize;
+  if (dtype != MLA_DTYPE_BF16) return kBadSize;
+  return train_layout(B, T, q_rank, H, d_q, d_v, r).total;
+}
+
+mla_status mla_gated_forward_train(const void* x, const void* w_kv_down, const void* kv_norm, const void* w_q_down,
+                                   const void* q_norm, const void* w_q_up, const void* w_uk, const void* w_uv,
+                                   const void* w_gate, const void* w_o, void* y, int B, int T, int D, int q_rank,
+                                   int H, int d_q, int d_v, int r, float eps, float scale, mla_dtype dtype,
+                                   void* state, size_t state_bytes, void* stream) {
+  const void* ptrs[] = {x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o, y};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !std::isfinite(eps) || eps < 0.0f) return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_DTYPE_BF16) return dtype == MLA_DTYPE_F32 ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  const mla_status st0 = layer_shape_check(B, T, D, q_rank, H, d_q, d_v, r);
+  if (st0 != MLA_OK) return st0;
+  if (!fits(B, H, T)) return MLA_ERR_UNSUPPORTED;
+  const TrainLayout L = train_layout(B, T, q_rank, H, d_q, d_v, r);
+  if (!state || !aligned16(state)) return MLA_ERR_WORKSPACE;
+  if (state_bytes < L.total) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* st = (char*)state;
+  const int N = B * T;
+  const bf16* xb = (const bf16*)x;
+  bf16* c_pre = (bf16*)(st + L.c_pre);
+  bf16* c = (bf16*)(st + L.c);
+  bf16* ql_pre = (bf16*)(st + L.ql_pre);
+  bf16* ql = (bf16*)(st + L.ql);
+  bf16* q = (bf16*)(st + L.q);
+  bf16* gate = (bf16*)(st + L.gate);
+  bf16* o = (bf16*)(st + L.o);
+  launch_gemm(xb, (const bf16*)w_kv_down, c_pre, N, r, D, s);
+  launch_rmsnorm(c_pre, c, (const bf16*)kv_norm, (float*)(st + L.rstd_c), N, r, eps, s);
+  launch_gemm(xb, (const bf16*)w_q_down, ql_pre, N, q_rank, D, s);
+  launch_rmsnorm(ql_pre, ql, (const bf16*)q_norm, (float*)(st + L.rstd_q), N, q_rank, eps, s);
+  launch_gemm(ql, (const bf16*)w_q_up, q, N, H * d_q, q_rank, s);
+  launch_gemm(xb, (const bf16*)w_gate, gate, N, H * d_v, D, s);
+  const mla_status st1 = mla_absorb_prefill_train(q, c, w_uk, w_uv, gate, o, (float*)(st + L.lse), B, T, H, d_q,
+                                                  d_v, r, scale, dtype, st + L.core, L.total - L.core, stream);
+  if (st1 != MLA_OK) return st1;
+  launch_gemm(o, (const bf16*)w_o, (bf16*)y, N, D, H * d_v, s);
+  return launch_status();
+}
+
+size_t mla_gated_backward_workspace_size(int B, int T, int D, int q_rank, int H, int d_q, int d_v, int r,
+                                         mla_dtype dtype) {
+  if (B <= 0 || T <= 0 || D <= 0 || q_rank <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return kBadSize;
+  if (dtype != MLA_DTYPE_BF16) return kBadSize;
+  return layer_bwd_layout(B, T, D, q_rank, H, d_q, d_v, r).total;
+}
+
+mla_status mla_gated_backward(const void* x, const void* w_kv_down, const void* kv_norm, const void* w_q_down,
+                              const void* q_norm, const void* w_q_up, const void* w_uk, const void* w_uv,
+                              const void* w_gate, const void* w_o, const void* dy, const void* state,
+                              size_t state_bytes, void* dx, float* dw_kv_down, float* dkv_norm, float* dw_q_down,
+                              float* dq_norm, float* dw_q_up, float* dw_uk, float* dw_uv, float* dw_gate,
+                              float* dw_o, int B, int T, int D, int q_rank, int H, int d_q, int d_v, int r,
+                              float scale, mla_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  const void* ptrs[] = {x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o, dy, dx,
+                        dw_kv_down, dkv_norm, dw_q_down, dq_norm, dw_q_up, dw_uk, dw_uv, dw_gate, dw_o};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
+  if (dtype != MLA_DTYPE_BF16) return dtype == MLA_DTYPE_F32 ? MLA_ERR_UNSUPPORTED : MLA_ERR_INVALID_ARG;
+  const mla_status st0 = layer_shape_check(B, T, D, q_rank, H, d_q, d_v, r);
+  if (st0 != MLA_OK) return st0;
+  const long long N = (long long)B * T;
+  const int HQ = H * d_q, HV = H * d_v;
+  const LayerBwdLayout L = layer_bwd_layout(B, T, D, q_rank, H, d_q, d_v, r);
+  // the weight-gradient products address each token-major operand with 32-bit offsets
+  if ((long double)N * L.Kc * 2 >= 2.0e9L || (long double)N * D * 2 >= 2.0e9L || (long double)N * HQ * 2 >= 2.0e9L ||
+      (long double)N * HV * 2 >= 2.0e9L)
+    return MLA_ERR_UNSUPPORTED;
+  const TrainLayout TL = train_layout(B, T, q_rank, H, d_q, d_v, r);
+  if (!state || !aligned16(state) || state_bytes < TL.total) return MLA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
+  if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const char* st = (const char*)state;
+  char* ws = (char*)workspace;
+  const bf16* xb = (const bf16*)x;
+  const bf16* dyb = (const bf16*)dy;
+  const bf16* o = (const bf16*)(st + TL.o);
+  bf16* gcat = (bf16*)(ws + L.gcat);
+  bf16* dout = (bf16*)(ws + L.dout);
+  bf16* dqb = (bf16*)(ws + L.dq);
+  bf16* dcb = (bf16*)(ws + L.dc);
+  bf16* dql = (bf16*)(ws + L.dql);
+  bf16* woT = (bf16*)(ws + L.woT);
+  bf16* wqupT = (bf16*)(ws + L.wqupT);
+  bf16* wcatT = (bf16*)(ws + L.wcatT);
+  float* part = (float*)(ws + L.part);
+  const int Kc = L.Kc;
+
+  // output projection y = o W_o^T: dout = dy W_o, dW_o = dy^T o
+  launch_transpose_into((const bf16*)w_o, D, HV, woT, D, s);
+  launch_gemm(dyb, woT, dout, (int)N, HV, D, s);
+  launch_gemm_tn(dyb, (size_t)N * D * 2, D, 0, o, (size_t)N * HV * 2, HV, 0, dw_o, 0, D, HV, (int)N, 1, s);
+  // the core: dq, dc, dW_UK, dW_UV and the gate gradient into gcat[:, 0:HV]
+  const mla_status st1 = prefill_backward_impl(st + TL.q, st + TL.c, w_uk, w_uv, st + TL.gate, o,
+                                               (const float*)(st + TL.lse), dout, dqb, dcb, dw_uk, dw_uv, gcat, Kc, B,
+                                               T, H, d_q, d_v, r, scale, dtype, ws + L.core, L.total - L.core, stream);
+  if (st1 != MLA_OK) return st1;
+  // query up-projection q = ql W_q_up^T: dql = dq W_q_up, dW_q_up = dq^T ql
+  launch_transpose_into((const bf16*)w_q_up, HQ, q_rank, wqupT, HQ, s);
+  launch_gemm(dqb, wqupT, dql, (int)N, q_rank, HQ, s);
+  launch_gemm_tn(dqb, (size_t)N * HQ * 2, HQ, 0, (const bf16*)(st + TL.ql), (size_t)N * q_rank * 2, q_rank, 0, dw_q_up,
+                 0, HQ, q_rank, (int)N, 1, s);
+  // the two norms: gradients of their inputs into gcat, gain gradients
+  launch_rmsnorm_backward(dql, q_rank, (const bf16*)(st + TL.ql_pre), (const float*)(st + TL.rstd_q),
+                          (const bf16*)q_norm, gcat + HV, Kc, part, dq_norm, (int)N, q_rank, s);
+  launch_rmsnorm_backward(dcb, r, (const bf16*)(st + TL.c_pre), (const float*)(st + TL.rstd_c), (const bf16*)kv_norm,
+                          gcat + HV + q_rank, Kc, part, dkv_norm, (int)N, r, s);
+  // the three products of x: dx = gcat [W_gate; W_q_down; W_kv_down], and their weight gradients
+  launch_transpose_into((const bf16*)w_gate, HV, D, wcatT, Kc, s);
+  launch_transpose_into((const bf16*)w_q_down, q_rank, D, wcatT + HV, Kc, s);
+  launch_transpose_into((const bf16*)w_kv_down, r, D, wcatT + HV + q_rank, Kc, s);
+  launch_gemm_batched(gcat, Kc, 0, wcatT, Kc, 0, (bf16*)dx, D, 0, (int)N, D, Kc, 1.0f, 1, s);
+  const size_t gcat_bytes = (size_t)N * Kc * 2, x_bytes = (size_t)N * D * 2;
+  launch_gemm_tn(gcat, gcat_bytes, Kc, 0, xb, x_bytes, D, 0, dw_gate, 0, HV, D, (int)N, 1, s);
+  launch_gemm_tn(gcat + HV, gcat_bytes - (size_t)HV * 2, Kc, 0, xb, x_bytes, D, 0, dw_q_down, 0, q_rank, D, (int)N, 1,
+                 s);
+  launch_gemm_tn(gcat + HV + q_rank, gcat_bytes - (size_t)(HV + q_rank) * 2, Kc, 0, xb, x_bytes, D, 0, dw_kv_down, 0,
+                 r, D, (int)N, 1, s);
   return launch_status();
 }
 

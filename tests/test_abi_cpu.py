@@ -175,6 +175,81 @@ def test_forward_rejects(kw, status):
     assert _forward(**kw) == status
 
 
+def _forward_train(**kw):
+    a = dict(x=FAKE, wkd=FAKE, kvn=FAKE, wqd=FAKE, qn=FAKE, wqu=FAKE, w_uk=FAKE, w_uv=FAKE, wg=FAKE, wo=FAKE,
+             y=FAKE, B=1, T=8, D=7168, q_rank=1536, H=96, dq=128, dv=128, r=512, eps=1e-6, scale=0.1,
+             dtype=mla.DTYPE_BF16, st=FAKE, stb=1 << 40, stream=None)
+    a.update(kw)
+    return mla.lib().mla_gated_forward_train(a["x"], a["wkd"], a["kvn"], a["wqd"], a["qn"], a["wqu"], a["w_uk"],
+                                             a["w_uv"], a["wg"], a["wo"], a["y"], a["B"], a["T"], a["D"],
+                                             a["q_rank"], a["H"], a["dq"], a["dv"], a["r"], a["eps"], a["scale"],
+                                             a["dtype"], a["st"], a["stb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(y=FAKE + 2), mla.MLA_ERR_INVALID_ARG),
+    (dict(B=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(eps=-1.0), mla.MLA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mla.MLA_ERR_INVALID_ARG),
+    (dict(dtype=mla.DTYPE_F32), mla.MLA_ERR_UNSUPPORTED),
+    (dict(dtype=9), mla.MLA_ERR_INVALID_ARG),
+    (dict(D=7000), mla.MLA_ERR_UNSUPPORTED),
+    (dict(r=4096, dq=128), mla.MLA_ERR_UNSUPPORTED),
+    (dict(st=None), mla.MLA_ERR_WORKSPACE),
+    (dict(st=FAKE + 8), mla.MLA_ERR_WORKSPACE),
+    (dict(stb=1 << 20), mla.MLA_ERR_WORKSPACE),
+])
+def test_forward_train_rejects(kw, status):
+    assert _forward_train(**kw) == status
+
+
+def _layer_backward(**kw):
+    a = dict(x=FAKE, wkd=FAKE, kvn=FAKE, wqd=FAKE, qn=FAKE, wqu=FAKE, w_uk=FAKE, w_uv=FAKE, wg=FAKE, wo=FAKE,
+             dy=FAKE, st=FAKE, stb=1 << 40, dx=FAKE, g=[FAKE] * 9, B=1, T=8, D=7168, q_rank=1536, H=96, dq=128,
+             dv=128, r=512, scale=0.1, dtype=mla.DTYPE_BF16, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return mla.lib().mla_gated_backward(a["x"], a["wkd"], a["kvn"], a["wqd"], a["qn"], a["wqu"], a["w_uk"],
+                                        a["w_uv"], a["wg"], a["wo"], a["dy"], a["st"], a["stb"], a["dx"], *a["g"],
+                                        a["B"], a["T"], a["D"], a["q_rank"], a["H"], a["dq"], a["dv"], a["r"],
+                                        a["scale"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dy=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(dx=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(g=[FAKE] * 8 + [None]), mla.MLA_ERR_INVALID_ARG),
+    (dict(g=[FAKE + 4] + [FAKE] * 8), mla.MLA_ERR_INVALID_ARG),
+    (dict(st=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(stb=1 << 20), mla.MLA_ERR_INVALID_ARG),
+    (dict(T=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), mla.MLA_ERR_INVALID_ARG),
+    (dict(dtype=mla.DTYPE_F32), mla.MLA_ERR_UNSUPPORTED),
+    (dict(q_rank=1500), mla.MLA_ERR_UNSUPPORTED),
+    (dict(dq=96, dv=96, r=384), mla.MLA_ERR_UNSUPPORTED),
+    (dict(T=1 << 18), mla.MLA_ERR_UNSUPPORTED),       # token-major operands beyond 32-bit offsets
+    (dict(ws=None), mla.MLA_ERR_WORKSPACE),
+    (dict(wsb=1 << 20), mla.MLA_ERR_WORKSPACE),
+    (dict(ws=FAKE + 8), mla.MLA_ERR_WORKSPACE),
+])
+def test_layer_backward_rejects(kw, status):
+    assert _layer_backward(**kw) == status
+
+
+def test_layer_training_sizes():
+    B, T, D, qr, H, dq, dv, r = 1, 8192, 7168, 1536, 96, 128, 128, 512
+    n = mla.train_state_size(B, T, qr, H, dq, dv, r, mla.DTYPE_BF16)
+    # two copies of each norm's rows, q, gate, the core output, lse and the two 1/rms
+    assert n >= T * (2 * (r + qr) + 3 * H * dq) * 2 + T * (H + 2) * 4
+    w = mla.layer_backward_workspace_size(B, T, D, qr, H, dq, dv, r, mla.DTYPE_BF16)
+    core = mla.backward_workspace_size(B, T, H, dq, dv, r, mla.DTYPE_BF16)
+    assert w >= core + T * (H * dv + qr + r) * 2 + D * (H * dv + qr + r) * 2
+    for f in (lambda: mla.train_state_size(B, T, qr, H, dq, dv, r, mla.DTYPE_F32),
+              lambda: mla.layer_backward_workspace_size(B, 0, D, qr, H, dq, dv, r, mla.DTYPE_BF16)):
+        with pytest.raises(mla.MLAError):
+            f()
+
+
 def test_paged_decode_workspace_size():
     n = mla.decode_paged_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_BF16)
     assert n >= mla.decode_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_BF16) + 4 * (2 * 64 + 1)

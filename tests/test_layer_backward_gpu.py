@@ -1,0 +1,197 @@
+"""GPU parity of the full layer's training path through the C ABI:
+mla_gated_forward_train (whose y must equal mla_gated_forward's bit for
+bit) and mla_gated_backward against the oracle's layer backward.
+
+Tolerance, per gradient tensor, as for the core backward: relative
+Frobenius error at most 1e-2, and every element within 2^-7 |oracle| + 25%
+of the tensor's RMS + 1e-3.  The oracle keeps the forward's stage results
+in float32 and every gradient in float64; the library stores the stage
+results (the norms' inputs and outputs, q, the gate, the core output) and
+the intermediate gradients (dO, dq, dc, the gate gradient, dql, the norms'
+input gradients) in bf16, 2^-9 relative each, and accumulates in fp32.  A
+gradient reached through k such roundings carries about sqrt(k) 2^-9 of
+noise per term, far inside 1e-2 for the chains here (at most six), while a
+dropped term, a wrong sign or a transposed operand moves the Frobenius
+error to order one.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import datagen as dg
+import oracle
+from gpu_util import to_dev, to_host_f64
+
+pytestmark = pytest.mark.gpu
+
+WIDTHS = {"toy": dict(D=256, q_rank=64, H=8, d_q=16, d_v=16, r=32),
+          "mid": dict(D=1024, q_rank=384, H=32, d_q=64, d_v=64, r=256),
+          "full": dict(D=7168, q_rank=1536, H=96, d_q=128, d_v=128, r=512)}
+FROB_REL, REL_ELEM, RMS_FRAC, ABS_FLOOR = 1e-2, 2.0 ** -7, 0.25, 1e-3
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.get()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rank_latent_causal_amd as mla
+    mla.lib()
+    return torch
+
+
+def _inputs(B, T, width, seed, eps=1e-6):
+    w = WIDTHS[width]
+    d = dg.forward_inputs(B, T, dtype=dg.BF16, seed=seed, **w)
+    d["eps"] = eps
+    d["scale"] = w["d_q"] ** -0.5
+    rng = np.random.default_rng(seed + 1)
+    d["dy"] = dg.f32_to_bf16_bits(rng.standard_normal((B, T, w["D"])).astype(np.float32))
+    return d
+
+
+def _train(d, poison=False):
+    """Training forward and backward; poison: state and workspace start as
+    0xFF bytes (NaN in bf16 and fp32), so a read of a byte that the calls did
+    not write first shows up."""
+    import torch
+    import rank_latent_causal_amd as mla
+    args = [to_dev(d[k]) for k in dg.FORWARD_KEYS]
+    B, T, D = d["x"].shape
+    q_rank, H, dq, dv, r = d["w_q_down"].shape[0], d["w_uk"].shape[0], d["w_uk"].shape[1], d["w_uv"].shape[1], \
+        d["w_kv_down"].shape[0]
+    fill = 255 if poison else 0
+    state = torch.full((mla.train_state_size(B, T, q_rank, H, dq, dv, r, mla.DTYPE_BF16),), fill, dtype=torch.uint8,
+                       device="cuda")
+    ws = torch.full((mla.layer_backward_workspace_size(B, T, D, q_rank, H, dq, dv, r, mla.DTYPE_BF16),), fill,
+                    dtype=torch.uint8, device="cuda")
+    y, state = mla.mla_gated_forward_train(*args, d["eps"], d["scale"], state=state)
+    g = mla.mla_gated_backward(*args, to_dev(d["dy"]), state, d["scale"], workspace=ws)
+    torch.cuda.synchronize()
+    return y, g
+
+
+def _grad_close(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    frob = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    assert frob <= FROB_REL, f"{what}: relative Frobenius error {frob:.3g} > {FROB_REL}"
+    bar = REL_ELEM * np.abs(ref) + RMS_FRAC * rms + ABS_FLOOR
+    err = np.abs(got - ref)
+    if (err > bar).any():
+        idx = np.unravel_index(np.argmax(err), err.shape)
+        raise AssertionError(f"{what}: {(err > bar).sum()} of {err.size} beyond the bar (rms {rms:.3g}); "
+                             f"max err {err.max():.3g} at {idx} (gpu {got[idx]:.5g}, oracle {ref[idx]:.5g})")
+    return frob
+
+
+@pytest.mark.parametrize("B,T,width", [(2, 64, "toy"), (1, 130, "mid")])
+def test_train_forward_equals_forward(B, T, width):
+    import torch
+    import rank_latent_causal_amd as mla
+    d = _inputs(B, T, width, seed=9100 + T)
+    log(f"train forward vs forward {width} B={B} T={T}")
+    args = [to_dev(d[k]) for k in dg.FORWARD_KEYS]
+    y, _ = mla.mla_gated_forward_train(*args, d["eps"], d["scale"])
+    ref = mla.mla_gated_forward(*args, d["eps"], d["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
+
+
+@pytest.mark.parametrize("B,T,width,poison", [(2, 77, "toy", False), (3, 33, "toy", True), (2, 130, "mid", False),
+                                              (1, 48, "full", False), (1, 65, "full", True)])
+def test_layer_backward_parity(o, B, T, width, poison):
+    """Ragged row counts (partial 32-row attention tiles and 128-row GEMM
+    tiles) and the full K3 widths; two cases start from poisoned state and
+    workspace."""
+    d = _inputs(B, T, width, seed=9200 + 10 * B + T)
+    log(f"layer backward {width} B={B} T={T} poison={poison}")
+    _, g = _train(d, poison)
+    ref = o.forward_backward(*[dg.as_f32(d[k]) for k in dg.FORWARD_KEYS], dg.as_f32(d["dy"]), d["eps"], d["scale"])
+    errs = {}
+    for k in o.GRAD_KEYS:
+        errs[k] = _grad_close(to_host_f64(g[k]), ref[k], f"{width} B{B} T{T} {k}")
+    log("  relative Frobenius errors: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+
+
+Q_PATH = ("dw_q_down", "dq_norm", "dw_q_up", "dw_uk")
+
+
+def test_layer_backward_single_position(o):
+    """T = 1: the one key gets softmax weight 1 whatever the scores, so every
+    gradient reached only through the scores (the query path and W_UK) is
+    exactly zero; the oracle must give zeros.  The library forms dS = P (dP -
+    D) from two bf16-derived values that agree to rounding, so its query-path
+    gradients are rounding noise.  dP comes from bf16 dol and c, D from bf16
+    dO and O: about four roundings of 2^-9, up to 2^-7 of |D| when they
+    align; the noise must stay under 2^-6 (twice that) of the same tensors'
+    size one position later (T = 2, same first row), where dP - D is of the
+    order of D.  Every other gradient meets the usual bar."""
+    import rank_latent_causal_amd as mla  # noqa: F401
+    d2 = _inputs(1, 2, "toy", seed=9250)
+    d1 = dict(d2)
+    d1["x"] = d2["x"][:, :1].copy()
+    d1["dy"] = d2["dy"][:, :1].copy()
+    log("layer backward toy B=1 T=1")
+    _, g1 = _train(d1, poison=True)
+    ref1 = o.forward_backward(*[dg.as_f32(d1[k]) for k in dg.FORWARD_KEYS], dg.as_f32(d1["dy"]), d1["eps"],
+                              d1["scale"])
+    ref2 = o.forward_backward(*[dg.as_f32(d2[k]) for k in dg.FORWARD_KEYS], dg.as_f32(d2["dy"]), d2["eps"],
+                              d2["scale"])
+    for k in o.GRAD_KEYS:
+        if k in Q_PATH:
+            assert np.all(ref1[k] == 0.0), f"oracle {k} at T=1 is not zero"
+            got = to_host_f64(g1[k])
+            assert np.all(np.isfinite(got)), k
+            scale2 = np.linalg.norm(ref2[k])
+            assert np.linalg.norm(got) <= 2.0 ** -6 * scale2, \
+                f"{k}: T=1 noise {np.linalg.norm(got):.3g} vs {scale2:.3g}"
+        else:
+            _grad_close(to_host_f64(g1[k]), ref1[k], f"T=1 {k}")
+
+
+def test_layer_backward_large_eps(o):
+    """eps comparable to the mean square, where the norms' 1/rms depends on
+    eps and a mistake in how eps enters the saved 1/rms would show."""
+    d = _inputs(2, 40, "toy", seed=9300, eps=0.5)
+    log("layer backward toy eps=0.5")
+    _, g = _train(d)
+    ref = o.forward_backward(*[dg.as_f32(d[k]) for k in dg.FORWARD_KEYS], dg.as_f32(d["dy"]), d["eps"], d["scale"])
+    for k in o.GRAD_KEYS:
+        _grad_close(to_host_f64(g[k]), ref[k], f"eps 0.5 {k}")
+
+
+def test_layer_backward_repeat_is_deterministic():
+    """Two runs on the same inputs (the second with the first's workspace and
+    gradient buffers) give identical bits: every reduction has a fixed order."""
+    import torch
+    import rank_latent_causal_amd as mla
+    d = _inputs(1, 100, "mid", seed=9400)
+    log("layer backward repeat mid B=1 T=100")
+    args = [to_dev(d[k]) for k in dg.FORWARD_KEYS]
+    dy = to_dev(d["dy"])
+    _, state = mla.mla_gated_forward_train(*args, d["eps"], d["scale"])
+    B, T, D = d["x"].shape
+    w = WIDTHS["mid"]
+    ws = torch.empty(mla.layer_backward_workspace_size(B, T, D, w["q_rank"], w["H"], w["d_q"], w["d_v"], w["r"],
+                                                       mla.DTYPE_BF16), dtype=torch.uint8, device="cuda")
+    a = mla.mla_gated_backward(*args, dy, state, d["scale"], workspace=ws)
+    a = {k: v.clone() for k, v in a.items()}
+    b = mla.mla_gated_backward(*args, dy, state, d["scale"], workspace=ws)
+    torch.cuda.synchronize()
+    for k in mla.LAYER_GRAD_KEYS:
+        assert torch.equal(a[k], b[k]), k
