@@ -15,7 +15,9 @@ full-layer forward (projections, norms, core, output projection at the full
 K3 widths, B=1, T=8192) is timed separately after the steps and reported
 under "forward"; a varlen batch of four chunks over a paged cache under
 "extend_varlen"; the backward of the prefill core (with the log-sum-exp of a
-training forward run before it) likewise under "backward".  The decode over a paged cache (the decode workload in
+training forward run before it) likewise under "backward"; one training
+step of the whole layer (training forward, then the layer backward) under
+"layer_train".  The decode over a paged cache (the decode workload in
 shuffled 64-row pages) runs in each step right after the packed decode and
 is reported under "decode_paged".  Neither is part of ms_per_step.
 """
@@ -223,6 +225,62 @@ def bench_backward(torch, mla, steps, warmup):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flop_per_launch": f}}
 
 
+def layer_train_flops(B, T, D, q_rank, H, dq, dv, r):
+    """Algorithmic FLOPs of one training step of the full layer: the forward,
+    then the core's backward and, for each of the five projections, its input
+    and weight gradients (twice the projection's forward FLOPs; the latent
+    and query down-projections' input gradients included, since x needs
+    them)."""
+    N = B * T
+    proj = 2 * N * (D * r + D * q_rank + q_rank * H * dq + D * H * dv + H * dv * D)
+    return forward_flops(B, T, D, q_rank, H, dq, dv, r) + 2 * proj + backward_flops(B, T, H, dq, dv, r)
+
+
+def bench_layer_train(torch, mla, steps, warmup):
+    """One training step of the whole layer at the full K3 widths, B=1,
+    T=8192: mla_gated_forward_train then mla_gated_backward with dy ~ N(0,1)."""
+    fw = dg.WORKLOADS["full_forward"]
+    d = dg.workload_inputs("full_forward")
+    args = [dev(d[k]) for k in dg.FORWARD_KEYS]
+    B, T, D, qr, H, dq, dv, r = (d[k] for k in ("B", "T", "D", "q_rank", "H", "d_q", "d_v", "r"))
+    y = torch.empty((B, T, D), dtype=torch.bfloat16, device="cuda")
+    state = torch.empty(mla.train_state_size(B, T, qr, H, dq, dv, r, mla.DTYPE_BF16), dtype=torch.uint8,
+                        device="cuda")
+    ws = torch.empty(mla.layer_backward_workspace_size(B, T, D, qr, H, dq, dv, r, mla.DTYPE_BF16), dtype=torch.uint8,
+                     device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(fw["seed"])
+    dy = torch.randn((B, T, D), generator=g, device="cuda").to(torch.bfloat16)
+    grads = None
+
+    def step():
+        nonlocal grads
+        mla.mla_gated_forward_train(*args, d["eps"], d["scale"], out=y, state=state)
+        grads = mla.mla_gated_backward(*args, dy, state, d["scale"], grads=grads, workspace=ws)
+
+    n = max(1, steps // 4)
+    for _ in range(max(1, warmup // 4)):
+        step()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, m, b in ev:
+        a.record()
+        mla.mla_gated_forward_train(*args, d["eps"], d["scale"], out=y, state=state)
+        m.record()
+        grads = mla.mla_gated_backward(*args, dy, state, d["scale"], grads=grads, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, _, b in ev]))
+    ms_f = float(np.mean([a.elapsed_time(m) for a, m, _ in ev]))
+    f = layer_train_flops(B, T, D, qr, H, dq, dv, r)
+    tf = f / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4), "ms_forward_train": round(ms_f, 4),
+            "ms_backward": round(ms - ms_f, 4), "calls": n, "seed": fw["seed"],
+            "workload": f"training step of full_forward: B={B}, T={T}, D={D}, q_rank={qr}, H={H}, d_q=d_v={dq}, "
+                        f"r={r}, dy ~ N(0,1)",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flop_per_launch": f}}
+
+
 def bench_varlen(torch, mla, steps, warmup, page_size=64):
     """A mixed chunk batch at full width in one varlen call over a paged
     cache: chunks of 2048, 1024, 512 and 256 queries after 6144, 3072, 7680
@@ -296,7 +354,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--which", choices=["both", "prefill", "decode", "forward", "backward"], default="both",
+    ap.add_argument("--which", choices=["both", "prefill", "decode", "forward", "backward", "layer_train"],
+                    default="both",
                     help="both: prefill, chunked prefill and decode, then the full-layer forward and the backward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration)")
@@ -438,6 +497,8 @@ def main():
         res["forward"] = bench_forward(torch, mla, args.steps, args.warmup)
     if args.which in ("both", "backward"):
         res["backward"] = bench_backward(torch, mla, args.steps, args.warmup)
+    if args.which in ("both", "layer_train"):
+        res["layer_train"] = bench_layer_train(torch, mla, args.steps, args.warmup)
     if not args.no_cpu_baseline and do_pre:
         res["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
     print(json.dumps(res), flush=True)

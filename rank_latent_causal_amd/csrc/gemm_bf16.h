@@ -256,9 +256,10 @@ mla_gemm_nt_big(GemmArgs a) {
 // stages, each wave 64 x 64.  Both MFMA operands need 8 consecutive k per
 // lane, i.e. columns of the stored tiles: they come from transposing
 // ds_read_b64_tr_b16 reads.  Tiles are copied from global memory with
-// LDS-DMA buffer loads; columns m0..m0+127 of every row are read (the caller
-// keeps them inside the allocation, whose byte size bounds the descriptor),
-// and k rows past K read as zeros.
+// LDS-DMA buffer loads; every column of the tile is read, also past M or N
+// (inside the allocation, whose byte size bounds the descriptor, those bytes
+// only reach accumulators that are not stored), and k rows past K read as
+// zeros.
 struct GemmTNArgs {
   const bf16* a;
   const bf16* b;
@@ -270,31 +271,53 @@ struct GemmTNArgs {
   int tiles_n;
 };
 
-// rows k0 .. k0+63 x columns col0 .. col0+127 of a row-major operand into a
-// 16 KiB LDS tile, row pitch 256 bytes, unswizzled.  Copy i (1 KiB = 4 rows)
-// is issued by wave i % 4.
+// The k tiles of these products hold 64 token rows of WIDTH (128 or 256)
+// columns, row pitch 2 WIDTH bytes.  A transposing read takes 8 bytes of
+// 16 rows (8 kq + e, e < 4) at the same columns, and every row of the tile
+// starts on bank 0: unswizzled, those 16 rows share 8 banks.  The 16-byte
+// chunk L of row s is therefore stored at chunk L ^ gemm_tn_swz(s), an even
+// value (the two chunks of a 16-column fragment stay one aligned pair) that
+// takes 8 different values over the rows one half-wave reads, so its 32
+// lanes cover all 64 banks.
+__device__ __forceinline__ int gemm_tn_swz(int s) { return 2 * ((s & 3) | (((s >> 3) & 1) << 2)); }
+
+// Rows k0 .. k0+63 x columns col0 .. col0+WIDTH-1 of a row-major operand
+// into a swizzled LDS tile.  Copy i (1 KiB) covers 1024 / (2 WIDTH) rows
+// and is issued by wave i % NW; lane l's 16 bytes land at byte 16 l of the
+// copy, the row's physical chunk l % (WIDTH / 8), so the lane fetches the
+// logical chunk that the swizzle puts there.  k rows past K read as zeros.
+template <int WIDTH, int NW>
 __device__ __forceinline__ void gemm_tn_copy(const bf16* __restrict__ base, unsigned bytes, int ld, int K, int k0,
                                              long long col0, MLA_LDS char* tile, int w) {
+  constexpr int CPR = WIDTH / 8;     // chunks per row
+  constexpr int RPC = 64 / CPR;      // rows per copy
+  constexpr int COPIES = 64 / RPC;   // copies per tile
+  static_assert(COPIES % NW == 0, "copies split evenly over the waves");
   unsigned ln;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
   const u32x4 rs = make_rsrc(base, bytes);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int i = w + 4 * c;  // copy index 0..15
-    const int row = 4 * i + (int)(ln >> 4);
+  for (int c = 0; c < COPIES / NW; ++c) {
+    const int i = w + NW * c;
+    const int row = RPC * i + (int)(ln / CPR);
+    const int logical = (int)(ln % CPR) ^ gemm_tn_swz(row);
     const int k = k0 + row;
-    const unsigned voff = k < K ? (unsigned)((((long long)k * ld) + col0 + 8 * (ln & 15)) * 2) : 0xFFFFFFF0u;
+    const unsigned voff = k < K ? (unsigned)((((long long)k * ld) + col0 + 8 * logical) * 2) : 0xFFFFFFF0u;
     buf2lds16(rs, voff, tile + i * 1024);
   }
 }
 
-// Operand fragment for rows 16 t + (lane % 16) of the stored columns and the
-// k-step's 32 rows: lane l gets tile rows 8 (l/16) + 0..7 of column
-// col0 + l % 16 (two transposing reads of four rows each).
-__device__ __forceinline__ bf16x8 gemm_tn_operand(const MLA_LDS char* tile, int ks, int col0, int l16, int kq) {
+// Operand fragment for columns col .. col+15 (col a multiple of 16) and the
+// k-step's 32 rows: lane l gets rows 32 ks + 8 (l/16) + 0..7 of column
+// col + l % 16 (two transposing reads of four rows each).
+template <int WIDTH>
+__device__ __forceinline__ bf16x8 gemm_tn_operand(const MLA_LDS char* tile, int ks, int col, int l16, int kq) {
   const int e = l16 >> 2, q = l16 & 3;
-  const MLA_LDS char* p = tile + (32 * ks + 8 * kq + e) * 256 + (col0 + 4 * q) * 2;
-  return cat4(lds_read_tr16(p), lds_read_tr16(p + 4 * 256));
+  const int r0 = 32 * ks + 8 * kq + e, r1 = r0 + 4;
+  const int lc = (col >> 3) + (q >> 1), half = (q & 1) * 8;
+  const MLA_LDS char* p0 = tile + r0 * (2 * WIDTH) + ((lc ^ gemm_tn_swz(r0)) << 4) + half;
+  const MLA_LDS char* p1 = tile + r1 * (2 * WIDTH) + ((lc ^ gemm_tn_swz(r1)) << 4) + half;
+  return cat4(lds_read_tr16(p0), lds_read_tr16(p1));
 }
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -311,8 +334,8 @@ mla_gemm_tn(GemmTNArgs a) {
   auto stage_a = [&](int st) { return smem + st * 2 * kGemmTileBytes; };
   auto stage_b = [&](int st) { return smem + st * 2 * kGemmTileBytes + kGemmTileBytes; };
 
-  gemm_tn_copy(a.a, a.a_bytes, a.lda, a.K, 0, ca, stage_a(0), w);
-  gemm_tn_copy(a.b, a.b_bytes, a.ldb, a.K, 0, cb, stage_b(0), w);
+  gemm_tn_copy<kGemmTile, 4>(a.a, a.a_bytes, a.lda, a.K, 0, ca, stage_a(0), w);
+  gemm_tn_copy<kGemmTile, 4>(a.b, a.b_bytes, a.ldb, a.K, 0, cb, stage_b(0), w);
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -323,8 +346,8 @@ mla_gemm_tn(GemmTNArgs a) {
     wait_vmcnt<0>();
     wg_barrier();
     if (kt + 1 < nk) {
-      gemm_tn_copy(a.a, a.a_bytes, a.lda, a.K, (kt + 1) * kGemmKT, ca, stage_a((kt + 1) & 1), w);
-      gemm_tn_copy(a.b, a.b_bytes, a.ldb, a.K, (kt + 1) * kGemmKT, cb, stage_b((kt + 1) & 1), w);
+      gemm_tn_copy<kGemmTile, 4>(a.a, a.a_bytes, a.lda, a.K, (kt + 1) * kGemmKT, ca, stage_a((kt + 1) & 1), w);
+      gemm_tn_copy<kGemmTile, 4>(a.b, a.b_bytes, a.ldb, a.K, (kt + 1) * kGemmKT, cb, stage_b((kt + 1) & 1), w);
     }
     const MLA_LDS char* ta = stage_a(kt & 1);
     const MLA_LDS char* tb = stage_b(kt & 1);
@@ -333,8 +356,8 @@ mla_gemm_tn(GemmTNArgs a) {
       bf16x8 fa[4], fb[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        fa[t] = gemm_tn_operand(ta, ks, 64 * wm + 16 * t, l16, kq);
-        fb[t] = gemm_tn_operand(tb, ks, 64 * wn + 16 * t, l16, kq);
+        fa[t] = gemm_tn_operand<kGemmTile>(ta, ks, 64 * wm + 16 * t, l16, kq);
+        fb[t] = gemm_tn_operand<kGemmTile>(tb, ks, 64 * wn + 16 * t, l16, kq);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -353,6 +376,70 @@ mla_gemm_tn(GemmTNArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = m0 + 64 * wm + 16 * i + 4 * kq + e;
+        if (m < a.M) C[(size_t)m * a.N + n] = acc[i][j][e];
+      }
+    }
+}
+
+// The same product with a 256 x 256 tile of C per workgroup of 8 waves, each
+// wave 128 (m) x 64 (n): 8 x 4 MFMA tiles, 12 operand fragments per 32
+// MFMAs.  Two 64 KiB stages, one workgroup per CU.
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mla_gemm_tn_big(GemmTNArgs a) {
+  constexpr int TB = kGemmBig * kGemmKT * 2;  // 32 KiB per operand per stage
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * 2 * TB];
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+  const int tn = blockIdx.x % a.tiles_n, tm = blockIdx.x / a.tiles_n;
+  const int n0 = tn * kGemmBig, m0 = tm * kGemmBig;
+  const long long ca = (long long)blockIdx.y * a.bsa + m0, cb = (long long)blockIdx.y * a.bsb + n0;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int wn = w & 3, wm = w >> 2;  // this wave's 128 (m) x 64 (n) block
+  const int nk = (a.K + kGemmKT - 1) / kGemmKT;
+  auto stage_a = [&](int st) { return smem + st * 2 * TB; };
+  auto stage_b = [&](int st) { return smem + st * 2 * TB + TB; };
+
+  gemm_tn_copy<kGemmBig, 8>(a.a, a.a_bytes, a.lda, a.K, 0, ca, stage_a(0), w);
+  gemm_tn_copy<kGemmBig, 8>(a.b, a.b_bytes, a.ldb, a.K, 0, cb, stage_b(0), w);
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
+
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmcnt<0>();
+    wg_barrier();
+    if (kt + 1 < nk) {
+      gemm_tn_copy<kGemmBig, 8>(a.a, a.a_bytes, a.lda, a.K, (kt + 1) * kGemmKT, ca, stage_a((kt + 1) & 1), w);
+      gemm_tn_copy<kGemmBig, 8>(a.b, a.b_bytes, a.ldb, a.K, (kt + 1) * kGemmKT, cb, stage_b((kt + 1) & 1), w);
+    }
+    const MLA_LDS char* ta = stage_a(kt & 1);
+    const MLA_LDS char* tb = stage_b(kt & 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 fa[8], fb[4];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) fa[t] = gemm_tn_operand<kGemmBig>(ta, ks, 128 * wm + 16 * t, l16, kq);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) fb[t] = gemm_tn_operand<kGemmBig>(tb, ks, 64 * wn + 16 * t, l16, kq);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(fa[i], fb[j], acc[i][j]);
+    }
+  }
+  // C fragment (i, j): rows m0 + 128 wm + 16 i + 4 kq + e, column n0 + 64 wn + 16 j + l16
+  float* C = a.c + (size_t)blockIdx.y * a.bsc;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 64 * wn + 16 * j + l16;
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = m0 + 128 * wm + 16 * i + 4 * kq + e;
         if (m < a.M) C[(size_t)m * a.N + n] = acc[i][j][e];
       }
     }

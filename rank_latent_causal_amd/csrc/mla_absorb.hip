@@ -234,6 +234,14 @@ void launch_gemm_tn(const bf16* A, size_t a_bytes, int lda, long long bsa, const
   g.a = A; g.b = Bm; g.c = C; g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb;
   g.bsa = bsa; g.bsb = bsb; g.bsc = bsc;
   g.a_bytes = (unsigned)a_bytes; g.b_bytes = (unsigned)b_bytes;
+  // the 256 x 256 tile when it still gives at least one workgroup per CU
+  const long long big = (long long)((N + mla::kGemmBig - 1) / mla::kGemmBig) *
+                        ((M + mla::kGemmBig - 1) / mla::kGemmBig) * batch;
+  if (big >= 256) {
+    g.tiles_n = (N + mla::kGemmBig - 1) / mla::kGemmBig;
+    hipLaunchKernelGGL(mla::mla_gemm_tn_big, dim3((unsigned)(big / batch), batch), dim3(512), 0, s, g);
+    return;
+  }
   g.tiles_n = (N + mla::kGemmTile - 1) / mla::kGemmTile;
   const int tiles = g.tiles_n * ((M + mla::kGemmTile - 1) / mla::kGemmTile);
   hipLaunchKernelGGL(mla::mla_gemm_tn, dim3(tiles, batch), dim3(256), 0, s, g);
