@@ -81,13 +81,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_full_prefill_full_dec
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources and the ABI header, in a fixed order: the
-    key under which measured HBM traffic is stored."""
+    """sha256 over the MLA library's HIP sources and its ABI header, in a
+    fixed order: the key under which measured HBM traffic is stored.  The
+    KDA sources (files named kda*) build separate kernels and are left out."""
     import hashlib
     h = hashlib.sha256()
     files = []
     for d in (os.path.join(ROOT, "rank_latent_causal_amd", "csrc"), os.path.join(ROOT, "include")):
-        files += [os.path.join(d, f) for f in sorted(os.listdir(d)) if f.endswith((".h", ".hip"))]
+        files += [os.path.join(d, f) for f in sorted(os.listdir(d))
+                  if f.endswith((".h", ".hip")) and not f.startswith("kda")]
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
         with open(f, "rb") as fh:
