@@ -22,6 +22,14 @@ toy/full-size table of the "K3 混合架构" page):
   ``W_gate [H*d_v,D]``, ``W_o [D,H*d_v]``) is ``N(0, 1/in_features)``, so
   the gate logits and q come out near ``N(0,1)`` as above; the two norm
   gains are ``1 + N(0, 0.01)``;
+* KDA (variable table of the "符号表" page: q, k ``[B,T,H,K]``, v
+  ``[B,T,H_V,V]``, the log-space decay g ``[B,T,H_V,K]``, the write strength
+  beta ``[B,T,H_V]``, the state ``[B,H_V,K,V]``): q and k rows are
+  ``N(0,1)`` draws normalised to unit L2 norm (float64), q then times
+  ``K**-0.5`` (the table's q already carries the scale); ``v ~ N(0,1)``;
+  ``g = max(gate_low, -exp(N(-2, 1)))`` with ``gate_low = -5`` (the gate's
+  lower bound on the same page), float32; ``beta = sigmoid(N(0,1))``,
+  float32; an initial state, when asked for, ``N(0, 1/K)`` float32;
 * decode cache lengths are i.i.d. uniform integers on ``[len_lo, len_hi]``;
   ``cu_seqlens`` is their int32 exclusive prefix sum;
 * float64 draws are rounded to float32 (round-to-nearest-even) and, for bf16
@@ -42,7 +50,8 @@ F32 = "f32"
 BF16 = "bf16"
 
 _TID = {"q": 1, "c": 2, "w_uk": 3, "w_uv": 4, "gate": 5, "lens": 6, "x": 7, "w_kv_down": 8,
-        "kv_norm": 9, "w_q_down": 10, "q_norm": 11, "w_q_up": 12, "w_gate": 13, "w_o": 14}
+        "kv_norm": 9, "w_q_down": 10, "q_norm": 11, "w_q_up": 12, "w_gate": 13, "w_o": 14,
+        "kda_q": 15, "kda_k": 16, "kda_v": 17, "kda_g": 18, "kda_beta": 19, "kda_s0": 20}
 _CHUNK_ELEMS = 1 << 21
 _RMS_EPS = 1e-6
 
@@ -149,6 +158,36 @@ def forward_inputs(B: int, T: int, D: int, q_rank: int, H: int, d_q: int, d_v: i
 FORWARD_KEYS = ("x", "w_kv_down", "kv_norm", "w_q_down", "q_norm", "w_q_up", "w_uk", "w_uv", "w_gate", "w_o")
 
 
+def _draw_f32(seed: int, name: str, shape, fn) -> np.ndarray:
+    """float32 array of the given shape from fn(standard-normal float64 draw)."""
+    n = int(np.prod(shape))
+    x = _gen(seed, _TID[name], 0).standard_normal(n)
+    return _store(fn(x), F32).reshape(shape)
+
+
+def kda_inputs(B: int, T: int, H: int, G: int, K: int, V: int, dtype: str = BF16, seed: int = 0,
+               gate_low: float = -5.0, init_state: bool = False) -> dict:
+    """Inputs of one chunk_kda call: H query/key heads, H_V = G H value heads."""
+    if min(B, T, H, G, K, V) <= 0:
+        raise ValueError("all sizes must be positive")
+    HV = G * H
+
+    def unit_rows(name, rows, cols, mult):
+        out = np.empty((rows, cols), dtype=np.uint16 if dtype == BF16 else np.float32)
+        x = _gen(seed, _TID[name], 0).standard_normal((rows, cols))
+        x = x / np.sqrt(np.sum(x * x, axis=1, keepdims=True)) * mult
+        out[:] = _store(x, dtype)
+        return out
+
+    q = unit_rows("kda_q", B * T * H, K, K ** -0.5).reshape(B, T, H, K)
+    k = unit_rows("kda_k", B * T * H, K, 1.0).reshape(B, T, H, K)
+    v = _draw_rows(seed, "kda_v", B * T * HV, V, 1.0, dtype).reshape(B, T, HV, V)
+    g = _draw_f32(seed, "kda_g", (B, T, HV, K), lambda x: np.maximum(gate_low, -np.exp(x - 2.0)))
+    beta = _draw_f32(seed, "kda_beta", (B, T, HV), lambda x: 1.0 / (1.0 + np.exp(-x)))
+    s0 = _draw_f32(seed, "kda_s0", (B, HV, K, V), lambda x: x * K ** -0.5) if init_state else None
+    return dict(q=q, k=k, v=v, g=g, beta=beta, s0=s0, B=B, T=T, H=H, G=G, K=K, V=V, dtype=dtype, seed=seed)
+
+
 def decode_lengths(B: int, len_lo: int, len_hi: int, seed: int = 0) -> np.ndarray:
     """i.i.d. uniform integer cache lengths on [len_lo, len_hi] (inclusive)."""
     if not (1 <= len_lo <= len_hi):
@@ -239,12 +278,21 @@ WORKLOADS = {
                         dtype=BF16, scale=16 ** -0.5, eps=1e-6, seed=SEED_BASE + 5),
     "full_forward": dict(kind="forward", B=1, T=8192, D=7168, q_rank=1536, H=96, d_q=128, d_v=128,
                          r=512, dtype=BF16, scale=128 ** -0.5, eps=1e-6, seed=SEED_BASE + 6),
+    # chunk_kda at the pages' toy widths (H = H_V = 8, K = V = 16, T in the
+    # 128-2048 range of the shape table) and the full K3 widths (H = H_V = 96,
+    # K = V = 128) over the same 8192 positions as the MLA workloads
+    "toy_kda": dict(kind="kda", B=2, T=512, H=8, G=1, K=16, V=16, dtype=BF16, seed=SEED_BASE + 7),
+    "full_kda": dict(kind="kda", B=1, T=8192, H=96, G=1, K=128, V=128, dtype=BF16, seed=SEED_BASE + 8),
 }
 
 
 def workload_inputs(name: str) -> dict:
     w = dict(WORKLOADS[name])
     kind = w.pop("kind")
+    if kind == "kda":
+        d = kda_inputs(**w)
+        d["kind"] = kind
+        return d
     scale = w.pop("scale")
     eps = w.pop("eps", None)
     if kind == "prefill":

@@ -1,4 +1,5 @@
-"""Plain CPU oracle for the absorbed Gated MLA layer (ctypes wrapper).
+"""Plain CPU oracle for the absorbed Gated MLA layer and chunk_kda's
+recurrence (ctypes wrapper).
 
 TEST INFRASTRUCTURE: only the tests, the smoke check and the CPU-baseline leg
 of the benchmark may import this package.  The product library never loads
@@ -72,13 +73,14 @@ class Oracle:
         L.oracle_prefill_backward.argtypes = [fp] * 6 + [I] * 6 + [D] + [dp] * 5 + [I]
         L.oracle_prefill_lse.argtypes = [fp, fp, fp, I, I, I, I, I, D, dp, I]
         L.oracle_forward_backward.argtypes = [fp] * 11 + [I] * 8 + [D, D] + [dp] * 10 + [I]
+        L.oracle_kda.argtypes = [fp] * 6 + [I] * 6 + [dp, dp, I]
         L.oracle_extend_varlen_paged.argtypes = [fp, fp, I64, I, i64p, I, i64p, i64p, fp, fp, fp, I, I, I, I, I, D,
                                                  dp, I]
         L.oracle_forward.argtypes = [fp] * 10 + [I] * 8 + [D, D, I, i64p, I64] + [dp] * 5 + [I]
         for f in ("oracle_prefill", "oracle_extend", "oracle_decode", "oracle_prefill_decompressed",
                   "oracle_prefill_attn", "oracle_round_bf16", "oracle_forward", "oracle_decode_paged",
                   "oracle_extend_paged", "oracle_cache_append", "oracle_prefill_backward",
-                  "oracle_prefill_lse", "oracle_extend_varlen_paged", "oracle_forward_backward"):
+                  "oracle_prefill_lse", "oracle_extend_varlen_paged", "oracle_forward_backward", "oracle_kda"):
             getattr(L, f).restype = I
 
     @property
@@ -319,6 +321,28 @@ class Oracle:
             B, T, D, q_rank, H, dq, dv, r, float(eps), float(scale), *[_ptr(g[k], ct.c_double) for k in self.GRAD_KEYS],
             threads), "oracle_forward_backward")
         return g
+
+    def kda(self, q, k, v, g, beta, s0=None, G: int = 1, threads: int = 0):
+        """chunk_kda's recurrence: returns (o [B,T,G*H,V], final state
+        [B,G*H,K,V]), float64; q, k [B,T,H,K], v [B,T,G*H,V], g [B,T,G*H,K],
+        beta [B,T,G*H], s0 [B,G*H,K,V] or None (zero state)."""
+        q, k, v, g, beta = map(_f32, (q, k, v, g, beta))
+        B, T, H, K = q.shape
+        V = v.shape[3]
+        HV = G * H
+        assert k.shape == q.shape and v.shape == (B, T, HV, V) and g.shape == (B, T, HV, K)
+        assert beta.shape == (B, T, HV)
+        s0p = None
+        if s0 is not None:
+            s0 = _f32(s0)
+            assert s0.shape == (B, HV, K, V)
+            s0p = _ptr(s0, ct.c_float)
+        o = np.empty((B, T, HV, V), dtype=np.float64)
+        st = np.empty((B, HV, K, V), dtype=np.float64)
+        self._check(self.lib.oracle_kda(_ptr(q, ct.c_float), _ptr(k, ct.c_float), _ptr(v, ct.c_float),
+                                        _ptr(g, ct.c_float), _ptr(beta, ct.c_float), s0p, B, T, H, G, K, V,
+                                        _ptr(o, ct.c_double), _ptr(st, ct.c_double), threads), "oracle_kda")
+        return o, st
 
     def round_bf16(self, v) -> np.ndarray:
         """Nearest bf16 value of each element (ties to even), as float64."""

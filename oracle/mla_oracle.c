@@ -1,5 +1,6 @@
 /*
- * Plain CPU oracle for the matrix-absorbed, NoPE Gated MLA attention layer.
+ * Plain CPU oracle for the matrix-absorbed, NoPE Gated MLA attention layer
+ * (and, at the end of the file, for chunk_kda's recurrence).
  *
  * TEST INFRASTRUCTURE.  Only the test-suite, the smoke check and the CPU
  * baseline leg of the benchmark load this library.  It shares no code, header,
@@ -1133,5 +1134,105 @@ int oracle_forward_backward(const float* x, const float* w_kv_down, const float*
 done:
   free(xd); free(c_pre); free(c); free(ql_pre); free(ql); free(q); free(g); free(o); free(dyd); free(dout);
   free(qf); free(cf); free(gf); free(doutf); free(dqv); free(dcv); free(dgv); free(dql); free(dql_pre); free(dc_pre);
+  return err;
+}
+
+/* ---------------------------------------------------------------------------
+ * chunk_kda's recurrence (page "符号表": section KDA 变量 for the variables
+ * and section Einsum 速查 for the three contractions; the summary list on the
+ * same page states that the chunked form equals this step-by-step one).  Per
+ * batch b and value head hv (query/key head hv / G, the GVA expansion), with
+ * the state S [K, V] starting at S0 (zero when s0 is NULL), for t = 0..T-1:
+ *   S_dec = diag(exp(g_t)) S          decay per key channel (log-space g)
+ *   p_t   = k_t^T S_dec               the old state's prediction for k_t
+ *   r_t   = v_t - p_t                 delta-rule residual
+ *   a_t   = beta_t k_t                write vector
+ *   S     = S_dec + a_t r_t^T         outer-product write
+ *   o_t   = q_t^T S                   read-out after the write
+ * Layouts: q, k [B,T,H,K]; v [B,T,HV,V]; g [B,T,HV,K]; beta [B,T,HV];
+ * s0 and s_out [B,HV,K,V]; o [B,T,HV,V]; HV = G H.  float64 throughout.
+ */
+int oracle_kda(const float* q, const float* k, const float* v, const float* g, const float* beta, const float* s0,
+               int B, int T, int H, int G, int K, int V, double* o, double* s_out, int nthreads) {
+  if (!q || !k || !v || !g || !beta || !o) return ORACLE_EINVAL;
+  if (B <= 0 || T < 0 || H <= 0 || G <= 0 || K <= 0 || V <= 0) return ORACLE_EINVAL;
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+  const int HV = G * H;
+  int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+  for (int64_t bh = 0; bh < (int64_t)B * HV; ++bh) {
+    const int64_t b = bh / HV;
+    const int hv = (int)(bh % HV);
+#if ORACLE_MUTANT == 33
+    const int h = hv % H; /* planted mistake: GVA heads interleaved instead of repeated */
+#else
+    const int h = hv / G;
+#endif
+    double* S = (double*)malloc(sizeof(double) * (size_t)K * V);
+    double* p = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!S || !p) {
+      free(S);
+      free(p);
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+      continue;
+    }
+    for (int64_t i = 0; i < (int64_t)K * V; ++i) S[i] = s0 ? (double)s0[bh * K * V + i] : 0.0;
+    for (int t = 0; t < T; ++t) {
+      const float* qt = q + ((b * T + t) * H + h) * (int64_t)K;
+      const float* kt = k + ((b * T + t) * H + h) * (int64_t)K;
+      const float* vt = v + ((b * T + t) * HV + hv) * (int64_t)V;
+      const float* gt = g + ((b * T + t) * HV + hv) * (int64_t)K;
+      const double bt = (double)beta[(b * T + t) * HV + hv];
+#if ORACLE_MUTANT != 29
+      for (int i = 0; i < K; ++i) {
+#if ORACLE_MUTANT == 32
+        const double dcy = exp(-(double)gt[i]); /* planted mistake: decay sign flipped */
+#else
+        const double dcy = exp((double)gt[i]);
+#endif
+        for (int j = 0; j < V; ++j) S[i * V + j] *= dcy;
+      }
+#endif
+      double* ot = o + ((b * T + t) * HV + hv) * (int64_t)V;
+#if ORACLE_MUTANT == 30
+      for (int j = 0; j < V; ++j) { /* planted mistake: read-out before the write */
+        double acc = 0.0;
+        for (int i = 0; i < K; ++i) acc += (double)qt[i] * S[i * V + j];
+        ot[j] = acc;
+      }
+#endif
+      for (int j = 0; j < V; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < K; ++i) acc += (double)kt[i] * S[i * V + j];
+        p[j] = acc;
+      }
+      for (int i = 0; i < K; ++i) {
+#if ORACLE_MUTANT == 31
+        const double ai = (double)kt[i]; /* planted mistake: write strength ignored */
+#else
+        const double ai = bt * (double)kt[i];
+#endif
+        for (int j = 0; j < V; ++j) S[i * V + j] += ai * ((double)vt[j] - p[j]);
+      }
+#if ORACLE_MUTANT == 29
+      for (int i = 0; i < K; ++i) { /* planted mistake: decay after the write */
+        const double dcy = exp((double)gt[i]);
+        for (int j = 0; j < V; ++j) S[i * V + j] *= dcy;
+      }
+#endif
+#if ORACLE_MUTANT != 30
+      for (int j = 0; j < V; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < K; ++i) acc += (double)qt[i] * S[i * V + j];
+        ot[j] = acc;
+      }
+#endif
+    }
+    if (s_out)
+      for (int64_t i = 0; i < (int64_t)K * V; ++i) s_out[bh * K * V + i] = S[i];
+    free(S);
+    free(p);
+  }
   return err;
 }

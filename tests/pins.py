@@ -649,6 +649,119 @@ def pin_layer_backward_finite_differences(o):
         _close(g[gk].reshape(-1), fd, 2e-5, 2e-6, f"{gk} vs finite differences")
 
 
+# ----------------------------------------------------------------- chunk_kda
+def _kda_arrays(d, s0=True):
+    f = lambda x: dg.as_f32(x).astype(np.float64)
+    return (f(d["q"]), f(d["k"]), f(d["v"]), np.asarray(d["g"], np.float64), np.asarray(d["beta"], np.float64),
+            (np.asarray(d["s0"], np.float64) if (s0 and d["s0"] is not None) else None))
+
+
+def _kda_global_solve(q, k, v, g, beta, s0, G):
+    """The recurrence of chunk_kda unrolled over the whole sequence as one
+    block (numpy, float64).  With Gam_t = sum_{u<=t} g_u per key channel and
+    a_u = beta_u k_u, the state after step t is
+      S_t = e^{Gam_t} * S0 + sum_{u<=t} (a_u * e^{Gam_t - Gam_u}) r_u^T,
+    so the residuals r_t = v_t - k_t^T S_dec,t solve the unit lower-triangular
+    system (I + A) R = V - (K * e^Gam) S0 with A_tu = sum_c k_t[c] a_u[c]
+    e^{Gam_t[c] - Gam_u[c]} for u < t; then O = (Q * e^Gam) S0 + Bm R with
+    Bm_tu of the same form with q_t, for u <= t.  Written from that
+    derivation, independent of the step-by-step loop."""
+    B, T, H, K = q.shape
+    HV, V = v.shape[2], v.shape[3]
+    o = np.zeros((B, T, HV, V))
+    st = np.zeros((B, HV, K, V))
+    for b in range(B):
+        for hv in range(HV):
+            h = hv // G
+            qs, ks, vs, gs, bs = q[b, :, h], k[b, :, h], v[b, :, hv], g[b, :, hv], beta[b, :, hv]
+            S0 = s0[b, hv] if s0 is not None else np.zeros((K, V))
+            Gam = np.cumsum(gs, axis=0)                          # [T, K]
+            a = bs[:, None] * ks                                  # [T, K]
+            E = np.exp(Gam[:, None, :] - Gam[None, :, :])         # [t, u, K], e^{Gam_t - Gam_u}
+            A = np.einsum("tc,uc,tuc->tu", ks, a, E) * np.tril(np.ones((T, T)), -1)
+            Bm = np.einsum("tc,uc,tuc->tu", qs, a, E) * np.tril(np.ones((T, T)), 0)
+            R = np.linalg.solve(np.eye(T) + A, vs - (ks * np.exp(Gam)) @ S0)
+            o[b, :, hv] = (qs * np.exp(Gam)) @ S0 + Bm @ R
+            st[b, hv] = np.exp(Gam[-1])[:, None] * S0 + (a * np.exp(Gam[-1] - Gam)).T @ R
+    return o, st
+
+
+def pin_kda_global_solve(o):
+    """The oracle's step-by-step recurrence equals the one-block triangular
+    solve above (GVA with G = 2, K != V, an initial state, ragged T)."""
+    d = dg.kda_inputs(2, 37, 2, 2, 8, 6, dtype=dg.F32, seed=41, init_state=True)
+    q, k, v, g, beta, s0 = _kda_arrays(d)
+    got_o, got_s = o.kda(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], G=2)
+    want_o, want_s = _kda_global_solve(q, k, v, g, beta, s0, 2)
+    _close(got_o, want_o, 1e-10, 1e-12, "kda o vs the global solve")
+    _close(got_s, want_s, 1e-10, 1e-12, "kda final state vs the global solve")
+
+
+def pin_kda_overwrite_memory(o):
+    """No decay (g = 0), full write strength (beta = 1) and one-hot keys: the
+    delta rule overwrites row idx_t of the state with v_t, so after step t
+    the state is S0 with each written row replaced by its latest value, and
+    o_t = q_t^T of that table (a dictionary walk, not the recurrence)."""
+    B, T, H, K, V = 1, 24, 1, 6, 4
+    rng = np.random.default_rng(43)
+    idx = rng.integers(0, K, size=T)
+    kk = np.zeros((B, T, H, K), np.float32)
+    kk[0, np.arange(T), 0, idx] = 1.0
+    q = rng.standard_normal((B, T, H, K)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, V)).astype(np.float32)
+    s0 = rng.standard_normal((B, H, K, V)).astype(np.float32)
+    g = np.zeros((B, T, H, K), np.float32)
+    beta = np.ones((B, T, H), np.float32)
+    got, st = o.kda(q, kk, v, g, beta, s0)
+    table = s0[0, 0].astype(np.float64).copy()
+    for t in range(T):
+        table[idx[t]] = v[0, t, 0]
+        _close(got[0, t, 0], q[0, t, 0].astype(np.float64) @ table, 1e-12, 1e-12, f"overwrite o_{t}")
+    _close(st[0, 0], table, 1e-12, 1e-12, "overwrite final state")
+
+
+def pin_kda_decay_only(o):
+    """beta = 0: nothing is written, the state is S0 decayed per key channel:
+    o_t = sum_c q_t[c] e^{Gam_t[c]} S0[c, :] and S_T = e^{Gam_T} * S0."""
+    d = dg.kda_inputs(1, 19, 3, 1, 5, 7, dtype=dg.F32, seed=47, init_state=True)
+    d["beta"] = np.zeros_like(d["beta"])
+    q, k, v, g, beta, s0 = _kda_arrays(d)
+    got_o, got_s = o.kda(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+    Gam = np.cumsum(g, axis=1)                                   # [B, T, HV, K]
+    want_o = np.einsum("bthc,bthc,bhcv->bthv", q, np.exp(Gam), s0)
+    _close(got_o, want_o, 1e-12, 1e-14, "decay-only o")
+    _close(got_s, np.exp(Gam[:, -1])[..., None] * s0, 1e-12, 1e-14, "decay-only state")
+
+
+def pin_kda_state_passing(o):
+    """Running T1 positions, then the next T2 from the returned state, equals
+    one run over T1 + T2 (the state is the whole carry between chunks)."""
+    d = dg.kda_inputs(2, 30, 2, 2, 8, 8, dtype=dg.F32, seed=53, init_state=True)
+    T1 = 13
+    full_o, full_s = o.kda(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], G=2)
+    cut = lambda x, a, b: np.ascontiguousarray(x[:, a:b])
+    o1, s1 = o.kda(cut(d["q"], 0, T1), cut(d["k"], 0, T1), cut(d["v"], 0, T1), cut(d["g"], 0, T1),
+                   cut(d["beta"], 0, T1), d["s0"], G=2)
+    o2, s2 = o.kda(cut(d["q"], T1, 30), cut(d["k"], T1, 30), cut(d["v"], T1, 30), cut(d["g"], T1, 30),
+                   cut(d["beta"], T1, 30), s1.astype(np.float32), G=2)
+    # the carried state passes through float32 at the cut: compare at float32 precision
+    _close(np.concatenate([o1, o2], axis=1), full_o, 1e-5, 1e-6, "state passing o")
+    _close(s2, full_s, 1e-5, 1e-6, "state passing final state")
+
+
+def pin_kda_gva_and_linearity(o):
+    """GVA: G = 2 value heads per query/key head equals G = 1 with q and k
+    repeated per value head.  Linearity: doubling v and S0 doubles o and the
+    final state exactly (every step is linear in them)."""
+    d = dg.kda_inputs(1, 21, 2, 2, 6, 5, dtype=dg.F32, seed=59, init_state=True)
+    o2, s2 = o.kda(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], G=2)
+    rep = lambda x: np.ascontiguousarray(np.repeat(x, 2, axis=2))
+    o1, s1 = o.kda(rep(d["q"]), rep(d["k"]), d["v"], d["g"], d["beta"], d["s0"], G=1)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2), "GVA expansion differs"
+    od, sd = o.kda(d["q"], d["k"], d["v"] * 2, d["g"], d["beta"], d["s0"] * 2, G=2)
+    assert np.array_equal(od, 2 * o2) and np.array_equal(sd, 2 * s2), "not linear in (v, S0)"
+
+
 ALL_PINS = [
     pin_absorbed_equals_decompressed,
     pin_attention_rows,
@@ -676,4 +789,9 @@ ALL_PINS = [
     pin_lse_matches_library,
     pin_varlen_mixed_batch,
     pin_layer_backward_finite_differences,
+    pin_kda_global_solve,
+    pin_kda_overwrite_memory,
+    pin_kda_decay_only,
+    pin_kda_state_passing,
+    pin_kda_gva_and_linearity,
 ]

@@ -38,6 +38,11 @@ MUTANTS = {
     26: "varlen: the chunk placed at the start of its sequence",
     27: "layer backward: the norm's projection term dropped",
     28: "layer backward: input gradient without the query path",
+    29: "kda: decay applied after the write",
+    30: "kda: read-out before the write",
+    31: "kda: write strength ignored",
+    32: "kda: decay sign flipped",
+    33: "kda: GVA heads interleaved instead of repeated",
 }
 
 
