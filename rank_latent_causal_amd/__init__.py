@@ -21,7 +21,8 @@ __all__ = [
     "mla_absorb_decode_paged", "mla_cache_append_paged", "mla_gated_forward", "mla_absorb_prefill_train",
     "backward_workspace_size", "mla_absorb_prefill_backward", "varlen_workspace_size",
     "mla_absorb_extend_varlen_paged", "train_state_size", "mla_gated_forward_train",
-    "layer_backward_workspace_size", "mla_gated_backward", "LAYER_GRAD_KEYS",
+    "layer_backward_workspace_size", "mla_gated_backward", "LAYER_GRAD_KEYS", "kda_workspace_size",
+    "kda_chunk_forward",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_absorb.so")
@@ -51,6 +52,8 @@ EXPORTS = (
     "mla_gated_forward_train",
     "mla_gated_backward_workspace_size",
     "mla_gated_backward",
+    "kda_chunk_workspace_size",
+    "kda_chunk_forward",
 )
 
 _lib = None
@@ -112,6 +115,10 @@ def lib() -> ct.CDLL:
         L.mla_gated_backward_workspace_size.restype = sz
         L.mla_gated_backward.argtypes = [vp] * 12 + [sz] + [vp] * 10 + [I] * 8 + [F, I, vp, sz, vp]
         L.mla_gated_backward.restype = I
+        L.kda_chunk_workspace_size.argtypes = [I] * 7
+        L.kda_chunk_workspace_size.restype = sz
+        L.kda_chunk_forward.argtypes = [vp] * 8 + [I] * 6 + [I, vp, sz, vp]
+        L.kda_chunk_forward.restype = I
         _lib = L
     return _lib
 
@@ -177,6 +184,13 @@ def layer_backward_workspace_size(B: int, T: int, D: int, q_rank: int, H: int, d
     n = lib().mla_gated_backward_workspace_size(B, T, D, q_rank, H, d_q, d_v, r, dtype)
     if n == _BAD:
         raise MLAError(MLA_ERR_INVALID_ARG, "mla_gated_backward_workspace_size")
+    return n
+
+
+def kda_workspace_size(B: int, T: int, H: int, G: int, K: int, V: int, dtype: int = DTYPE_BF16) -> int:
+    n = lib().kda_chunk_workspace_size(B, T, H, G, K, V, dtype)
+    if n == _BAD:
+        raise MLAError(MLA_ERR_INVALID_ARG, "kda_chunk_workspace_size")
     return n
 
 
@@ -583,3 +597,35 @@ def mla_gated_backward(x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_
     if st != MLA_OK:
         raise MLAError(st, "mla_gated_backward")
     return grads
+
+
+def kda_chunk_forward(q, k, v, g, beta, G: int = 1, initial_state=None, final_state: bool = False, out=None,
+                      workspace=None, stream=None):
+    """chunk_kda (bf16): q, k [B,T,H,K], v [B,T,G*H,V] bf16; g [B,T,G*H,K] and
+    beta [B,T,G*H] float32; initial_state [B,G*H,K,V] float32 or None.
+    Returns (o [B,T,G*H,V] bf16, final state float32 or None)."""
+    torch = _torch()
+    B, T, H, K = q.shape
+    HV = G * H
+    V = v.shape[3]
+    _check(q, (B, T, H, K), torch.bfloat16, "q")
+    _check(k, (B, T, H, K), torch.bfloat16, "k")
+    _check(v, (B, T, HV, V), torch.bfloat16, "v")
+    _check(g, (B, T, HV, K), torch.float32, "g")
+    _check(beta, (B, T, HV), torch.float32, "beta")
+    if initial_state is not None:
+        _check(initial_state, (B, HV, K, V), torch.float32, "initial_state")
+    if out is None:
+        out = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=q.device)
+    _check(out, (B, T, HV, V), torch.bfloat16, "out")
+    st = torch.empty((B, HV, K, V), dtype=torch.float32, device=q.device) if final_state else None
+    need = kda_workspace_size(B, T, H, G, K, V, DTYPE_BF16)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = lib().kda_chunk_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+                                 initial_state.data_ptr() if initial_state is not None else None, out.data_ptr(),
+                                 st.data_ptr() if st is not None else None, B, T, H, G, K, V, DTYPE_BF16,
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != MLA_OK:
+        raise MLAError(rc, "kda_chunk_forward")
+    return out, st

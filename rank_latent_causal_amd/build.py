@@ -7,7 +7,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "mla_absorb.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("mla_absorb.hip", "kda.hip")]
 HEADERS = [os.path.join(HERE, "csrc", f) for f in os.listdir(os.path.join(HERE, "csrc")) if f.endswith(".h")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmla_absorb.so")
@@ -25,7 +25,7 @@ def build(out_path: str = LIB, verbose: bool = False) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed fp32 VALU forms are kept out of every kernel
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           f"-I{INCLUDE}", SRC, "-o", out_path + ".tmp"]
+           f"-I{INCLUDE}", *SRCS, "-o", out_path + ".tmp"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "not a recognized feature" not in l)
     if res.returncode != 0:

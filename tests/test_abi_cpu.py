@@ -11,7 +11,7 @@ import pytest
 import rank_latent_causal_amd as mla
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mla_absorb.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in ("mla_absorb.h", "kda.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(mla.LIB_PATH), reason="libmla_absorb.so not built")
 
@@ -19,9 +19,11 @@ FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:mla|kda)_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_exactly_the_bound_functions():
@@ -33,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(L, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", mla.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r" T (mla_\w+)", out))
+    exported = set(re.findall(r" T ((?:mla|kda)_\w+)", out))
     assert set(declared_functions()) <= exported
 
 
@@ -358,3 +360,45 @@ def test_varlen_workspace_size():
     assert n >= mla.prefill_workspace_size(1, 1, 96, 128, 512, mla.DTYPE_BF16) + 8 * (1000 // 16 + 4)
     with pytest.raises(mla.MLAError):
         mla.varlen_workspace_size(4, 1000, 96, 128, 512, mla.DTYPE_F32)
+
+
+def test_kda_workspace_size():
+    n = mla.kda_workspace_size(1, 8192, 96, 1, 128, 128)
+    # per (batch, value head, 64 positions): W and q e^Gam [64][136], A_hat^T [128][72], Bm [64][72],
+    # U^T [128][72] bf16 and the chunk decay [128] fp32
+    assert n == 96 * 128 * (((2 * 64 * 136 + 128 * 72 + 64 * 72 + 128 * 72) * 2 + 128 * 4 + 255) // 256 * 256)
+    assert mla.kda_workspace_size(2, 65, 4, 2, 16, 16) == 2 * 8 * 2 * mla.kda_workspace_size(1, 64, 1, 1, 16, 16)
+    for bad in (dict(K=96, V=96), dict(K=128, V=64), dict(T=0), dict(G=0)):
+        kw = dict(B=1, T=64, H=2, G=1, K=128, V=128)
+        kw.update(bad)
+        with pytest.raises(mla.MLAError):
+            mla.kda_workspace_size(**kw)
+
+
+def _kda(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, s0=None, o=FAKE, sT=None, B=1, T=100, H=2, G=2, K=128,
+             V=128, dtype=mla.DTYPE_BF16, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return mla.lib().kda_chunk_forward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["s0"], a["o"], a["sT"],
+                                       a["B"], a["T"], a["H"], a["G"], a["K"], a["V"], a["dtype"], a["ws"],
+                                       a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(beta=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(o=FAKE + 2), mla.MLA_ERR_INVALID_ARG),
+    (dict(s0=FAKE + 4), mla.MLA_ERR_INVALID_ARG),
+    (dict(sT=FAKE + 8), mla.MLA_ERR_INVALID_ARG),
+    (dict(T=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(G=-1), mla.MLA_ERR_INVALID_ARG),
+    (dict(dtype=mla.DTYPE_F32), mla.MLA_ERR_UNSUPPORTED),
+    (dict(dtype=7), mla.MLA_ERR_INVALID_ARG),
+    (dict(K=96, V=96), mla.MLA_ERR_UNSUPPORTED),
+    (dict(K=128, V=64), mla.MLA_ERR_UNSUPPORTED),
+    (dict(ws=None), mla.MLA_ERR_WORKSPACE),
+    (dict(ws=FAKE + 8), mla.MLA_ERR_WORKSPACE),
+    (dict(wsb=1 << 12), mla.MLA_ERR_WORKSPACE),     # far below the 653 KB these sizes need
+])
+def test_kda_rejects(kw, status):
+    assert _kda(**kw) == status
