@@ -17,7 +17,7 @@ under "forward"; a varlen batch of four chunks over a paged cache under
 "extend_varlen"; the backward of the prefill core (with the log-sum-exp of a
 training forward run before it) likewise under "backward"; one training
 step of the whole layer (training forward, then the layer backward) under
-"layer_train".  The decode over a paged cache (the decode workload in
+"layer_train"; chunk_kda over B=1, T=8192, H=96, K=V=128 under "kda".  The decode over a paged cache (the decode workload in
 shuffled 64-row pages) runs in each step right after the packed decode and
 is reported under "decode_paged".  Neither is part of ms_per_step.
 """
@@ -283,6 +283,48 @@ def bench_layer_train(torch, mla, steps, warmup):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flop_per_launch": f}}
 
 
+def kda_bytes(B, T, H, G, K, V):
+    """Bytes chunk_kda must move: q and k (bf16) per query/key head, v and o
+    (bf16), g (fp32) and beta (fp32) per value head, once each."""
+    HV = G * H
+    return B * T * (2 * H * K * 2 + HV * V * 2 * 2 + HV * K * 4 + HV * 4)
+
+
+def kda_flops(B, T, H, G, K, V):
+    """FLOPs of the step-by-step recurrence: per position and value head the
+    decay (K V), the prediction k^T S (2 K V), the write (2 K V) and the
+    read-out q^T S (2 K V)."""
+    return 7 * B * T * G * H * K * V
+
+
+def bench_kda(torch, mla, steps, warmup):
+    """chunk_kda over the full workload (B=1, T=8192, H=H_V=96, K=V=128), a
+    zero initial state, no final state: both kernels of one call."""
+    d = dg.workload_inputs("full_kda")
+    B, T, H, G, K, V = (d[k] for k in ("B", "T", "H", "G", "K", "V"))
+    args = [dev(d[k]) for k in ("q", "k", "v", "g", "beta")]
+    out = torch.empty((B, T, G * H, V), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mla.kda_workspace_size(B, T, H, G, K, V), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        mla.kda_chunk_forward(*args, G=G, out=out, workspace=ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        mla.kda_chunk_forward(*args, G=G, out=out, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nb = kda_bytes(B, T, H, G, K, V)
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {"value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
+            "tflops": round(kda_flops(B, T, H, G, K, V) / (ms * 1e-3) / 1e12, 2), "seed": d["seed"],
+            "workload": f"full_kda: B={B}, T={T}, H=H_V={G * H}, K=V={K}, chunks of 64, g in [-5, 0], zero state",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "bytes_per_launch": nb,
+                         "kernel": "kda_intra + kda_state"}}
+
+
 def bench_varlen(torch, mla, steps, warmup, page_size=64):
     """A mixed chunk batch at full width in one varlen call over a paged
     cache: chunks of 2048, 1024, 512 and 256 queries after 6144, 3072, 7680
@@ -356,7 +398,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--which", choices=["both", "prefill", "decode", "forward", "backward", "layer_train"],
+    ap.add_argument("--which", choices=["both", "prefill", "decode", "forward", "backward", "layer_train", "kda"],
                     default="both",
                     help="both: prefill, chunked prefill and decode, then the full-layer forward and the backward")
     ap.add_argument("--copy-probe", action="store_true",
@@ -501,6 +543,8 @@ def main():
         res["backward"] = bench_backward(torch, mla, args.steps, args.warmup)
     if args.which in ("both", "layer_train"):
         res["layer_train"] = bench_layer_train(torch, mla, args.steps, args.warmup)
+    if args.which in ("both", "kda"):
+        res["kda"] = bench_kda(torch, mla, args.steps, args.warmup)
     if not args.no_cpu_baseline and do_pre:
         res["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -27,7 +27,7 @@ size_t slot_bytes(int K) {
 template <int DK, int DV, int VB>
 void launch(kda::KdaArgs a, hipStream_t s) {
   const long long slots = (long long)a.B * a.HV * a.NC;
-  hipLaunchKernelGGL((kda::kda_intra<DK, DV>), dim3((unsigned)slots), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((kda::kda_intra<DK, DV>), dim3((unsigned)slots), dim3(64 * kda::intra_waves<DK>()), 0, s, a);
   constexpr int NVB = DV / VB;
   const long long heads = (long long)a.B * a.HV;
   a.xcd_map = (NVB > 1 && heads % 8 == 0) ? 1 : 0;
@@ -61,6 +61,8 @@ mla_status kda_chunk_forward(const void* q, const void* k, const void* v, const 
   const long long HV = (long long)G * H, NC = (T + kda::kC - 1) / kda::kC;
   if (HV >= (1LL << 20) || (long double)B * HV * NC >= 2.0e9L || (long double)B * T * HV * (K > V ? K : V) >= 4.0e18L)
     return MLA_ERR_UNSUPPORTED;
+  // the in-chunk kernel copies q, k and g with 32-bit offsets inside one batch
+  if ((long double)T * H * K * 2 >= 2.0e9L || (long double)T * HV * K * 4 >= 2.0e9L) return MLA_ERR_UNSUPPORTED;
   const size_t need = kda_chunk_workspace_size(B, T, H, G, K, V, dtype);
   if (need == kBad) return MLA_ERR_UNSUPPORTED;
   if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;

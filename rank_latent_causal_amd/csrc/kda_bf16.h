@@ -93,36 +93,67 @@ __device__ __forceinline__ bf16x8 lds8(const MLA_LDS char* base, int byte_off) {
 template <int DK, int DV>
 struct IntraLds {
   using D = KdaDims<DK, DV>;
-  static constexpr int X_BYTES = kC * D::WP * 2;                   // one [64][WP] bf16 operand
-  static constexpr int A_PITCH = 68;                               // fp32 A rows, 16-byte aligned
-  static constexpr int RX = 2 * X_BYTES > kC * A_PITCH * 4 ? 2 * X_BYTES : kC * A_PITCH * 4;
-  static constexpr int RY = X_BYTES > kC * D::TP * 2 ? X_BYTES : kC * D::TP * 2;
-  static constexpr int OFF_XK = 0, OFF_XQ = X_BYTES, OFF_A = 0;    // A replaces XK / XQ after use
-  static constexpr int OFF_Y = RX, OFF_T = RX;                     // Tm replaces Y after use
-  static constexpr int OFF_F = RX + RY;
-  static constexpr int OFF_KT = OFF_F + 10 * D::DKP * 4;
-  static constexpr int OFF_VT = OFF_KT + D::DKP * D::TP * 2;
-  static constexpr int OFF_BETA = OFF_VT + DV * D::TP * 2;
+  static constexpr int X_BYTES = kC * D::DKP * 2;  // X_K / X_Q: [64][DKP] bf16, chunk-swizzled rows
+  static constexpr int Y_BYTES = kC * D::WP * 2;   // Y: [64][WP] bf16
+  static constexpr int A_PITCH = 68;               // fp32 A / Tm rows, 16-byte aligned
+  static constexpr int A_BYTES = kC * A_PITCH * 4;
+  static constexpr int P_BYTES = 4 * 16 * 16 * 4;  // one 16 x 16 fp32 product per wave
+  static constexpr int T_BYTES = kC * D::TP * 2;   // bf16 Tm [64][TP]
+  static constexpr int max2(int x, int y) { return x > y ? x : y; }
+  // Region lifetimes (phases 0-4):
+  //   R1: raw k -> X_K (0-2), A (3), K~^T (4, spilling into R2)
+  //   R2: raw q -> X_Q (0-2), fp32 Tm (3)
+  //   R3: raw decays (0-1a), Y and F (1b-2), the solve's products then bf16 Tm (3-4), V^T (4)
+  static constexpr int R1 = max2(X_BYTES, A_BYTES), R2 = max2(X_BYTES, A_BYTES);
+  static constexpr int OFF_R1 = 0, OFF_R2 = R1, OFF_R3 = R1 + R2;
+  static constexpr int R3 = max2(max2(kC * D::DKP * 4, Y_BYTES + 10 * D::DKP * 4), max2(P_BYTES, T_BYTES) + DV * D::TP * 2);
+  static constexpr int OFF_XK = OFF_R1, OFF_A = OFF_R1, OFF_KT = OFF_R1;
+  static constexpr int OFF_XQ = OFF_R2, OFF_TF = OFF_R2;
+  static constexpr int OFF_G = OFF_R3, OFF_Y = OFF_R3, OFF_F = OFF_R3 + Y_BYTES;
+  static constexpr int OFF_P = OFF_R3, OFF_T = OFF_R3, OFF_VT = OFF_R3 + max2(P_BYTES, T_BYTES);
+  static constexpr int OFF_BETA = OFF_R3 + R3;
   static constexpr int BYTES = OFF_BETA + kC * 4;
+  static_assert(D::DKP * D::TP * 2 <= R1 + R2, "K~^T fits over A and Tm");
 };
 
-// One workgroup (4 waves) per (batch, value head, chunk).
+// X_K / X_Q rows are 2 DKP bytes, unpadded, so the LDS-DMA copy can fill
+// whole rows; the 16-byte chunk L of row i sits at chunk L ^ xswz(i), which
+// spreads the 16 consecutive rows of an MFMA operand read over all banks.
+template <int DKP>
+__device__ __forceinline__ int xswz(int i) {
+  constexpr int CPR = DKP / 8, RPB = 256 / (2 * DKP);  // chunks per row, rows per 256 bytes
+  return (i / RPB) % CPR;
+}
+template <int DKP>
+__device__ __forceinline__ int xoff(int i, int ch) {  // byte offset of element (i, ch)
+  return i * (2 * DKP) + ((((ch >> 3) ^ xswz<DKP>(i))) << 4) + (ch & 7) * 2;
+}
+
+// Waves of kda_intra: 8 at K = 128 (four threads per key channel in the
+// scaling phase, A and Bm on separate waves), 4 for the narrower heads.
+template <int DK>
+constexpr int intra_waves() { return DK >= 128 ? 8 : 4; }
+
+// One workgroup per (batch, value head, chunk); two fit on a CU.
 template <int DK, int DV>
-__global__ void __launch_bounds__(256) kda_intra(KdaArgs a) {
+__global__ void __launch_bounds__(64 * intra_waves<DK>()) kda_intra(KdaArgs a) {
+  constexpr int NW = intra_waves<DK>(), NT = 64 * NW;
   using D = KdaDims<DK, DV>;
   using L = IntraLds<DK, DV>;
-  constexpr int DKP = D::DKP, WP = D::WP, TP = D::TP;
+  constexpr int DKP = D::DKP, WP = D::WP, TP = D::TP, AP = L::A_PITCH;
   __shared__ __attribute__((aligned(16))) char smem_raw[L::BYTES];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
   bf16* sXK = (bf16*)(smem_raw + L::OFF_XK);
   bf16* sXQ = (bf16*)(smem_raw + L::OFF_XQ);
   bf16* sY = (bf16*)(smem_raw + L::OFF_Y);
   float* sF = (float*)(smem_raw + L::OFF_F);
+  float* sG = (float*)(smem_raw + L::OFF_G);
+  float* sA = (float*)(smem_raw + L::OFF_A);
+  float* sTf = (float*)(smem_raw + L::OFF_TF);
+  bf16* sT = (bf16*)(smem_raw + L::OFF_T);
   bf16* sKt = (bf16*)(smem_raw + L::OFF_KT);
   bf16* sVt = (bf16*)(smem_raw + L::OFF_VT);
   float* sBeta = (float*)(smem_raw + L::OFF_BETA);
-  float* sA = (float*)(smem_raw + L::OFF_A);
-  bf16* sT = (bf16*)(smem_raw + L::OFF_T);
 
   const int slot = blockIdx.x;
   const int ci = slot % a.NC, bh = slot / a.NC;
@@ -137,142 +168,232 @@ __global__ void __launch_bounds__(256) kda_intra(KdaArgs a) {
   bf16* Utimg = (bf16*)(out + D::OFF_UT);
   float* Gimg = (float*)(out + D::OFF_G);
   const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l16 = lane & 15, kq = lane >> 4;
 
-  if (tid < kC) sBeta[tid] = tid < nvalid ? a.beta[((size_t)b * a.T + t0 + tid) * a.HV + hv] : 0.0f;
+  // ---- phase 0: k and q rows (chunk-swizzled) and the decays go straight
+  // from global memory into LDS with LDS-DMA copies (rows past the chunk's
+  // end and channels past K read as zeros); v is loaded into registers and
+  // written transposed once the solve is done
+  constexpr int VCH = DV / 8, NV = kC * VCH, VPER = (NV + NT - 1) / NT;
+  bf16x8 vreg[VPER];
+  {
+    constexpr int CPR = DKP / 8, RPK = 1024 / (2 * DKP);        // key rows per 1 KiB copy
+    constexpr int GPR = DKP / 4, GRK = 1024 / (4 * DKP);        // decay chunks per row, rows per copy
+    constexpr int NKC = kC / RPK, NGC = kC / GRK;               // copies per key tensor, for the decays
+    const u32x4 rk = mla::make_rsrc(a.k + (size_t)b * a.T * a.H * DK, (unsigned)((size_t)a.T * a.H * DK * 2));
+    const u32x4 rq = mla::make_rsrc(a.q + (size_t)b * a.T * a.H * DK, (unsigned)((size_t)a.T * a.H * DK * 2));
+    const u32x4 rg = mla::make_rsrc(a.g + (size_t)b * a.T * a.HV * DK, (unsigned)((size_t)a.T * a.HV * DK * 4));
+    for (int c = w; c < 2 * NKC + NGC; c += NW) {
+      if (c < 2 * NKC) {
+        const int cc = c % NKC, i = RPK * cc + lane / CPR;
+        const int L = (lane % CPR) ^ xswz<DKP>(i);
+        const unsigned voff = (i < nvalid && 8 * L < DK)
+                                  ? (unsigned)(((size_t)(t0 + i) * a.H + h) * DK * 2 + 16 * L) : 0xFFFFFFF0u;
+        mla::buf2lds16(c < NKC ? rk : rq, voff, smem + (c < NKC ? L::OFF_XK : L::OFF_XQ) + cc * 1024);
+      } else {
+        const int cc = c - 2 * NKC, i = GRK * cc + lane / GPR, c4 = 4 * (lane % GPR);
+        const unsigned voff = (i < nvalid && c4 < DK)
+                                  ? (unsigned)((((size_t)(t0 + i) * a.HV + hv) * DK + c4) * 4) : 0xFFFFFFF0u;
+        mla::buf2lds16(rg, voff, smem + L::OFF_G + cc * 1024);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VPER; ++u) {
+      const int r = tid + NT * u, i = r / VCH, c8 = 8 * (r % VCH);
+      vreg[u] = (r < NV && i < nvalid) ? *(const bf16x8*)(a.v + (((size_t)b * a.T + t0 + i) * a.HV + hv) * DV + c8)
+                                       : bf16x8{};
+    }
+    if (tid < kC) sBeta[tid] = tid < nvalid ? a.beta[((size_t)b * a.T + t0 + tid) * a.HV + hv] : 0.0f;
+    mla::wait_vmcnt<0>();
+  }
   __syncthreads();
 
-  // ---- phase 1: one thread per key channel (Gam down the chunk, every
-  // per-element scaling), one per value channel (V^T)
-  if (tid < DKP) {
-    const int ch = tid;
-    const bool live = ch < DK;
-    float gam[kC];
+  // ---- phase 1: NT / DKP threads per key channel, each over RPT rows.  The
+  // running Gam is kept for the thread's own rows, the 16-row block bounds
+  // of those rows, the chunk end and (part 0) every block bound.
+  constexpr int TPC = NT / DKP, RPT = kC / TPC;
+  static_assert(NT % DKP == 0 && RPT % 8 == 0 && (RPT % 16 == 0 || 16 % RPT == 0), "row runs");
+  const int ch = tid % DKP, part = tid / DKP;
+  const int blk = (part * RPT) / 16;  // the 16-row block holding this thread's rows
+  float own[RPT], ref0 = 0.0f, ref15 = 0.0f, gl = 0.0f, gs[4], ge[4];
+  {
     float run = 0.0f;
 #pragma unroll
     for (int i = 0; i < kC; ++i) {
-      float gi = 0.0f;
-      if (live && i < nvalid) gi = a.g[(((size_t)b * a.T + t0 + i) * a.HV + hv) * DK + ch];
-      run += gi;
-      gam[i] = run;
+      run += sG[i * DKP + ch];
+      if (i / RPT == part) own[i % RPT] = run;
+      if (i % 16 == 0) {
+        gs[i / 16] = run;
+        if (i / 16 == blk) ref0 = run;
+      }
+      if (i % 16 == 15) {
+        ge[i / 16] = run;
+        if (i / 16 == blk) ref15 = run;
+      }
     }
-    const float gl = gam[kC - 1];
-    Gimg[ch] = live ? exp_(gl) : 1.0f;
+    gl = run;
+  }
+  __syncthreads();  // R3 is free: Y and F may be written
+  bf16x8 ktreg[RPT / 8];
+  {
+    const bool live = ch < DK;
+    if (part == 0) Gimg[ch] = live ? exp_(gl) : 1.0f;
 #pragma unroll
-    for (int i8 = 0; i8 < kC / 8; ++i8) {
-      bf16x8 kt8, at8;
+    for (int i8 = 0; i8 < RPT / 8; ++i8) {
+      bf16x8 at8;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int i = 8 * i8 + u;
-        float kk = 0.0f, qq = 0.0f;
-        if (live && i < nvalid) {
-          const size_t idx = (((size_t)b * a.T + t0 + i) * a.H + h) * DK + ch;
-          kk = (float)a.k[idx];
-          qq = (float)a.q[idx];
-        }
+        const int r = 8 * i8 + u, i = part * RPT + r;
+        const float gm = own[r];
+        bf16* pk = (bf16*)(smem_raw + L::OFF_XK + xoff<DKP>(i, ch));
+        bf16* pq = (bf16*)(smem_raw + L::OFF_XQ + xoff<DKP>(i, ch));
+        const float kk = (float)*pk, qq = (float)*pq;
         const float bi = sBeta[i];
-        const float e = exp_(gam[i]);
-        kt8[u] = (bf16)(kk * e);
-        at8[u] = (bf16)(bi * kk * exp_(gl - gam[i]));
-        const int r0 = 16 * (i / 16);
-        const float eb = exp_(gam[i] - gam[r0]);
-        sXK[i * WP + ch] = (bf16)(kk * eb);
-        sXQ[i * WP + ch] = (bf16)(qq * eb);
-        sY[i * WP + ch] = (bf16)(bi * kk * exp_(gam[r0 + 15] - gam[i]));
+        const float e = exp_(gm);
+        ktreg[i8][u] = (bf16)(kk * e);
+        at8[u] = (bf16)(bi * kk * exp_(gl - gm));
+        const float eb = exp_(gm - ref0);
+        *pk = (bf16)(kk * eb);
+        *pq = (bf16)(qq * eb);
+        sY[i * WP + ch] = (bf16)(bi * kk * exp_(ref15 - gm));
         Qimg[i * WP + ch] = (bf16)(qq * e);
       }
-      *(bf16x8*)&sKt[ch * TP + 8 * i8] = kt8;
-      *(bf16x8*)&Atimg[ch * TP + 8 * i8] = at8;
+      *(bf16x8*)&Atimg[ch * TP + part * RPT + 8 * i8] = at8;
     }
-    int p = 0;
+    if (part == 0) {
+      int p = 0;
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
+      for (int I = 0; I < 4; ++I)
 #pragma unroll
-      for (int J = 0; J <= I; ++J) sF[(p++) * DKP + ch] = exp_(gam[16 * I] - gam[16 * J + 15]);
-  } else if (tid < DKP + DV) {
-    const int ch = tid - DKP;
-#pragma unroll
-    for (int i8 = 0; i8 < kC / 8; ++i8) {
-      bf16x8 v8;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = 8 * i8 + u;
-        v8[u] = i < nvalid ? a.v[(((size_t)b * a.T + t0 + i) * a.HV + hv) * DV + ch] : (bf16)0.0f;
-      }
-      *(bf16x8*)&sVt[ch * TP + 8 * i8] = v8;
+        for (int J = 0; J <= I; ++J) sF[(p++) * DKP + ch] = exp_(gs[I] - ge[J]);
     }
   }
   __syncthreads();
 
-  // ---- phase 2: A and Bm, wave w owns block row I = w (blocks J <= I)
-  const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, kq = lane >> 4;
+  // ---- phase 2: A and Bm by 16-row block rows I (blocks J <= I).  With 8
+  // waves, wave I forms A's row I and wave 4 + I Bm's; with 4, wave I both.
+  const int bw = w & 3;
+  const bool doA = NW == 4 || w < 4, doB = NW == 4 || w >= 4;
   f32x4 accA[4], accB[4];
 #pragma unroll
   for (int J = 0; J < 4; ++J) accA[J] = accB[J] = f32x4{};
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
-    if (J > w) continue;
-    const int pair = w * (w + 1) / 2 + J;
+    if (J > bw) continue;
+    const int pair = bw * (bw + 1) / 2 + J;
 #pragma unroll
     for (int ks = 0; ks < DKP / 32; ++ks) {
       const int c0 = 32 * ks + 8 * kq;
-      const bf16x8 xk = lds8(smem, L::OFF_XK + ((16 * w + l16) * WP + c0) * 2);
-      const bf16x8 xq = lds8(smem, L::OFF_XQ + ((16 * w + l16) * WP + c0) * 2);
       const bf16x8 y = lds8(smem, L::OFF_Y + ((16 * J + l16) * WP + c0) * 2);
       const f32x4 f0 = *(const f32x4*)&sF[pair * DKP + c0];
       const f32x4 f1 = *(const f32x4*)&sF[pair * DKP + c0 + 4];
-      bf16x8 xk2, xq2;
+      if (doA) {
+        const bf16x8 xk = lds8(smem, L::OFF_XK + xoff<DKP>(16 * bw + l16, c0));
+        bf16x8 xk2;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float f = u < 4 ? f0[u] : f1[u - 4];
-        xk2[u] = (bf16)((float)xk[u] * f);
-        xq2[u] = (bf16)((float)xq[u] * f);
+        for (int u = 0; u < 8; ++u) xk2[u] = (bf16)((float)xk[u] * (u < 4 ? f0[u] : f1[u - 4]));
+        accA[J] = mla::mfma16(xk2, y, accA[J]);
       }
-      accA[J] = mla::mfma16(xk2, y, accA[J]);
-      accB[J] = mla::mfma16(xq2, y, accB[J]);
+      if (doB) {
+        const bf16x8 xq = lds8(smem, L::OFF_XQ + xoff<DKP>(16 * bw + l16, c0));
+        bf16x8 xq2;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) xq2[u] = (bf16)((float)xq[u] * (u < 4 ? f0[u] : f1[u - 4]));
+        accB[J] = mla::mfma16(xq2, y, accB[J]);
+      }
     }
   }
-  // Bm image (rows i = 16 w + 4 kq + e, column j = 16 J + l16), zero above the diagonal
+  // Bm image (rows i = 16 bw + 4 kq + e, column j = 16 J + l16), zero above the diagonal
+  if (doB) {
 #pragma unroll
-  for (int J = 0; J < 4; ++J)
+    for (int J = 0; J < 4; ++J)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * kq + e, j = 16 * J + l16;
-      Bimg[i * TP + j] = (bf16)(j <= i ? accB[J][e] : 0.0f);
-    }
-  __syncthreads();  // every wave is done with XK / XQ / Y
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * bw + 4 * kq + e, j = 16 * J + l16;
+        Bimg[i * TP + j] = (bf16)(j <= i ? accB[J][e] : 0.0f);
+      }
+  }
+  __syncthreads();  // every wave is done with XK / XQ / Y / F
+  if (doA) {
 #pragma unroll
-  for (int J = 0; J < 4; ++J)
+    for (int J = 0; J < 4; ++J)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * w + 4 * kq + e, j = 16 * J + l16;
-      sA[i * L::A_PITCH + j] = j < i ? accA[J][e] : 0.0f;
-    }
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * bw + 4 * kq + e, j = 16 * J + l16;
+        sA[i * AP + j] = j < i ? accA[J][e] : 0.0f;
+      }
+  }
   __syncthreads();
 
-  // ---- phase 3: Tm = (I + A)^{-1}, lane c solves column c by forward substitution
-  if (w == 0) {
-    float x[kC];
+  // ---- phase 3: Tm = (I + A)^{-1} by 16 x 16 blocks, fp32.  Waves 0-3
+  // invert their diagonal block by forward substitution (lane c < 16:
+  // column c); then, by distance d = I - J = 1, 2, 3, wave J forms
+  //   T_IJ = -T_II sum_{M=J}^{I-1} A_IM T_MJ
+  // (each lane 4 of the 256 elements, the sum staged in the wave's scratch).
+  if (w < 4) {
+    float x[16];
 #pragma unroll
-    for (int i = 0; i < kC; ++i) {
-      float acc = (i == lane) ? 1.0f : 0.0f;
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == l16) ? 1.0f : 0.0f;
 #pragma unroll
-      for (int j4 = 0; j4 < i / 4; ++j4) {
-        const f32x4 av = *(const f32x4*)&sA[i * L::A_PITCH + 4 * j4];
-        acc -= av[0] * x[4 * j4] + av[1] * x[4 * j4 + 1] + av[2] * x[4 * j4 + 2] + av[3] * x[4 * j4 + 3];
-      }
-#pragma unroll
-      for (int j = 4 * (i / 4); j < i; ++j) acc -= sA[i * L::A_PITCH + j] * x[j];
-      x[i] = acc;
+      for (int s2 = 0; s2 < r; ++s2) acc -= sA[(16 * w + r) * AP + 16 * w + s2] * x[s2];
+      x[r] = acc;
     }
+    if (lane < 16) {
 #pragma unroll
-    for (int i = 0; i < kC; ++i) sT[i * TP + lane] = (bf16)x[i];
+      for (int r = 0; r < 16; ++r) sTf[(16 * w + r) * AP + 16 * w + lane] = x[r];
+    }
+  }
+  __syncthreads();
+  float* sP = (float*)(smem_raw + L::OFF_P) + (w & 3) * 256;
+#pragma unroll
+  for (int d = 1; d < 4; ++d) {
+    if (w < 4 - d) {
+      const int J = w, I = w + d;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int e = lane + 64 * m, i = e >> 4, j = e & 15;
+        float acc = 0.0f;
+        for (int M = J; M < I; ++M)
+#pragma unroll
+          for (int k2 = 0; k2 < 16; ++k2) acc += sA[(16 * I + i) * AP + 16 * M + k2] * sTf[(16 * M + k2) * AP + 16 * J + j];
+        sP[e] = acc;
+      }
+      mla::wait_lgkmcnt0();
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int e = lane + 64 * m, i = e >> 4, j = e & 15;
+        float acc = 0.0f;
+#pragma unroll
+        for (int k2 = 0; k2 < 16; ++k2) acc += sTf[(16 * I + i) * AP + 16 * I + k2] * sP[k2 * 16 + j];
+        sTf[(16 * I + i) * AP + 16 * J + j] = -acc;
+      }
+    }
+    __syncthreads();
+  }
+  // bf16 Tm for the MFMA products (zero above the diagonal blocks)
+  for (int e = tid; e < kC * kC; e += NT) {
+    const int i = e >> 6, j = e & 63;
+    sT[i * TP + j] = (bf16)((j >> 4) > (i >> 4) ? 0.0f : sTf[i * AP + j]);
+  }
+  __syncthreads();  // A and the fp32 Tm are dead: K~^T and V^T may be written
+#pragma unroll
+  for (int i8 = 0; i8 < RPT / 8; ++i8) *(bf16x8*)&sKt[ch * TP + part * RPT + 8 * i8] = ktreg[i8];
+#pragma unroll
+  for (int u = 0; u < VPER; ++u) {
+    const int r = tid + NT * u, i = r / VCH, c8 = 8 * (r % VCH);
+    if (r < NV) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sVt[(c8 + e) * TP + i] = vreg[u][e];
+    }
   }
   __syncthreads();
 
   // ---- phase 4: W^T = (k e^Gam)^T Tm^T (tiles: 16 channels x 16 rows) and
   // U = Tm V (tiles: 16 rows x 16 value channels)
   constexpr int NWT = (DKP / 16) * 4, NUT = 4 * (DV / 16);
-  for (int tile = w; tile < NWT + NUT; tile += 4) {
+  for (int tile = w; tile < NWT + NUT; tile += NW) {
     f32x4 acc = f32x4{};
     if (tile < NWT) {
       const int C = tile / 4, I = tile % 4;

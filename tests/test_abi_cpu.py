@@ -396,6 +396,7 @@ def _kda(**kw):
     (dict(dtype=7), mla.MLA_ERR_INVALID_ARG),
     (dict(K=96, V=96), mla.MLA_ERR_UNSUPPORTED),
     (dict(K=128, V=64), mla.MLA_ERR_UNSUPPORTED),
+    (dict(T=1 << 21, H=2, G=1), mla.MLA_ERR_UNSUPPORTED),   # one batch's g beyond 32-bit offsets
     (dict(ws=None), mla.MLA_ERR_WORKSPACE),
     (dict(ws=FAKE + 8), mla.MLA_ERR_WORKSPACE),
     (dict(wsb=1 << 12), mla.MLA_ERR_WORKSPACE),     # far below the 653 KB these sizes need
