@@ -76,7 +76,7 @@ mla_status kda_chunk_forward(const void* q, const void* k, const void* v, const 
   hipStream_t s = (hipStream_t)stream;
   if (K == 16) launch<16, 16, 16>(a, s);
   else if (K == 64) launch<64, 64, 32>(a, s);
-  else launch<128, 128, 32>(a, s);
+  else launch<128, 128, 64>(a, s);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

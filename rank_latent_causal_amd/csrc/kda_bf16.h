@@ -444,17 +444,20 @@ __device__ __forceinline__ void copy_image(const char* src, MLA_LDS char* dst, i
 template <int DK, int DV, int VB>
 struct StateLds {
   using D = KdaDims<DK, DV>;
+  // double-buffered per chunk: W, q e^Gam, A_hat^T, Bm, the chunk decay
   static constexpr int S_W = 0;
   static constexpr int S_Q = S_W + D::W_BYTES;
   static constexpr int S_AT = S_Q + D::W_BYTES;
   static constexpr int S_B = S_AT + D::AT_BYTES;
-  static constexpr int S_UT = S_B + D::B_BYTES;
-  static constexpr int UT_SLICE = VB * D::TP * 2;
-  static constexpr int S_G = S_UT + UT_SLICE;
+  static constexpr int S_G = S_B + D::B_BYTES;
   static constexpr int STAGE = round_up(S_G + D::G_BYTES, 16);
-  static constexpr int OFF_ST = 2 * STAGE;                      // S^T bf16 [VB][WP]
+  // single-buffered: this block's U^T rows (refilled once R has used them)
+  static constexpr int UT_SLICE = VB * D::TP * 2;
+  static constexpr int OFF_UT = 2 * STAGE;
+  static constexpr int OFF_ST = OFF_UT + UT_SLICE;              // S^T bf16 [VB][WP]
   static constexpr int OFF_RT = OFF_ST + VB * D::WP * 2;        // R^T bf16 [VB][TP]
   static constexpr int BYTES = OFF_RT + VB * D::TP * 2;
+  static_assert(BYTES <= 163840, "LDS");
 };
 
 // One workgroup (4 waves) per (batch, value head, VB value columns); wave w
@@ -487,17 +490,21 @@ __global__ void __launch_bounds__(256) kda_state(KdaArgs a) {
   const int l16 = lane & 15, kq = lane >> 4;
   const int v0 = vb * VB;
 
-  auto issue = [&](int ci, int st) {
-    const char* slot = a.ws + ((size_t)bh * a.NC + ci) * D::SLOT;
+  auto slot_of = [&](int ci) { return a.ws + ((size_t)bh * a.NC + ci) * D::SLOT; };
+  auto issue_main = [&](int ci, int st) {
+    const char* slot = slot_of(ci);
     MLA_LDS char* dst = smem + st * L::STAGE;
     copy_image<D::W_BYTES>(slot + D::OFF_W, dst + L::S_W, w, lane);
     copy_image<D::W_BYTES>(slot + D::OFF_Q, dst + L::S_Q, w, lane);
     copy_image<D::AT_BYTES>(slot + D::OFF_AT, dst + L::S_AT, w, lane);
     copy_image<D::B_BYTES>(slot + D::OFF_B, dst + L::S_B, w, lane);
-    copy_image<L::UT_SLICE>(slot + D::OFF_UT + v0 * TP * 2, dst + L::S_UT, w, lane);
     copy_image<D::G_BYTES>(slot + D::OFF_G, dst + L::S_G, w, lane);
   };
-  issue(0, 0);
+  auto issue_ut = [&](int ci) {
+    copy_image<L::UT_SLICE>(slot_of(ci) + D::OFF_UT + v0 * TP * 2, smem + L::OFF_UT, w, lane);
+  };
+  issue_main(0, 0);
+  issue_ut(0);
 
   // the state: fragment (m, V) holds channels 16 (w + 4 m) + 4 kq + e of value column 16 V + l16
   f32x4 S[CPW][NVT];
@@ -526,7 +533,7 @@ __global__ void __launch_bounds__(256) kda_state(KdaArgs a) {
     mla::wait_vmcnt<0>();
     mla::wait_lgkmcnt0();
     mla::wg_barrier();  // chunk ci staged, S^T of the previous chunk written, R^T free
-    if (ci + 1 < a.NC) issue(ci + 1, (ci + 1) & 1);
+    if (ci + 1 < a.NC) issue_main(ci + 1, (ci + 1) & 1);
     const int so = (ci & 1) * L::STAGE;
 
     // R = U - W S and P = (q e^Gam) S: rows 16 w + 4 kq + e, value column 16 V + l16
@@ -547,14 +554,15 @@ __global__ void __launch_bounds__(256) kda_state(KdaArgs a) {
     }
 #pragma unroll
     for (int V = 0; V < NVT; ++V) {
-      const bf16x4 u4 = *(const MLA_LDS bf16x4*)(smem + so + L::S_UT + ((16 * V + l16) * TP + 16 * w + 4 * kq) * 2);
+      const bf16x4 u4 = *(const MLA_LDS bf16x4*)(smem + L::OFF_UT + ((16 * V + l16) * TP + 16 * w + 4 * kq) * 2);
       bf16x4 r4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) r4[e] = (bf16)((float)u4[e] - accR[V][e]);
       *(bf16x4*)&sRt[(16 * V + l16) * TP + 16 * w + 4 * kq] = r4;
     }
     mla::wait_lgkmcnt0();
-    mla::wg_barrier();  // R^T complete; every wave is done reading S^T
+    mla::wg_barrier();  // R^T complete; every wave is done reading S^T and U^T
+    if (ci + 1 < a.NC) issue_ut(ci + 1);
 
     // O = P + Bm R
 #pragma unroll
