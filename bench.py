@@ -111,6 +111,38 @@ def measured_traffic():
     return None
 
 
+KDA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_full_kda.md")
+
+
+def kda_source_hash() -> str:
+    """sha256 over the sources chunk_kda's kernels are built from (the KDA
+    files and the device helpers they include), in a fixed order: the key
+    of the KDA traffic record."""
+    import hashlib
+    h = hashlib.sha256()
+    files = [os.path.join(ROOT, "include", "kda.h")] + [
+        os.path.join(ROOT, "rank_latent_causal_amd", "csrc", f) for f in ("common.h", "kda_bf16.h", "kda.hip")]
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_kda_traffic():
+    """The KDA traffic record (bytes per call) if it was taken from the
+    current KDA sources, else None."""
+    try:
+        with open(KDA_TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("traffic-record: "):
+                    rec = json.loads(line[len("traffic-record: "):])
+                    return rec if rec.get("sources") == kda_source_hash() else None
+    except OSError:
+        return None
+    return None
+
+
 def copy_probe(nbytes: int = 1 << 30):
     """One plain device-to-device copy of nbytes: the reference kernel whose
     FETCH_SIZE / WRITE_SIZE readings scale the counters to bytes."""
@@ -317,12 +349,13 @@ def bench_kda(torch, mla, steps, warmup):
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     nb = kda_bytes(B, T, H, G, K, V)
     gbs = nb / (ms * 1e-3) / 1e9
+    rec = measured_kda_traffic()
     return {"value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
             "tflops": round(kda_flops(B, T, H, G, K, V) / (ms * 1e-3) / 1e12, 2), "seed": d["seed"],
             "workload": f"full_kda: B={B}, T={T}, H=H_V={G * H}, K=V={K}, chunks of 64, g in [-5, 0], zero state",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "bytes_per_launch": nb,
-                         "kernel": "kda_intra + kda_state"}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": rec["call_bytes"] if rec else None,
+                         "bytes_per_launch": nb, "kernel": "kda_intra + kda_state"}}
 
 
 def bench_varlen(torch, mla, steps, warmup, page_size=64):

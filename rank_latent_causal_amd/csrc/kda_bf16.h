@@ -129,6 +129,14 @@ __device__ __forceinline__ int xoff(int i, int ch) {  // byte offset of element 
   return i * (2 * DKP) + ((((ch >> 3) ^ xswz<DKP>(i))) << 4) + (ch & 7) * 2;
 }
 
+// Workgroup barrier that orders LDS only: this wave's LDS accesses have
+// completed, then s_barrier.  __syncthreads() would also wait for every
+// global store still in flight (the images written to the workspace).
+__device__ __forceinline__ void lds_barrier() {
+  mla::wait_lgkmcnt0();
+  mla::wg_barrier();
+}
+
 // Waves of kda_intra: 8 at K = 128 (four threads per key channel in the
 // scaling phase, A and Bm on separate waves), 4 for the narrower heads.
 template <int DK>
@@ -197,16 +205,18 @@ __global__ void __launch_bounds__(64 * intra_waves<DK>()) kda_intra(KdaArgs a) {
         mla::buf2lds16(rg, voff, smem + L::OFF_G + cc * 1024);
       }
     }
+    // item r: row r % 64, channels 8 (r / 64) .. (consecutive lanes take consecutive
+    // rows, so the transposed LDS writes below fall in distinct banks)
 #pragma unroll
     for (int u = 0; u < VPER; ++u) {
-      const int r = tid + NT * u, i = r / VCH, c8 = 8 * (r % VCH);
+      const int r = tid + NT * u, i = r % kC, c8 = 8 * (r / kC);
       vreg[u] = (r < NV && i < nvalid) ? *(const bf16x8*)(a.v + (((size_t)b * a.T + t0 + i) * a.HV + hv) * DV + c8)
                                        : bf16x8{};
     }
     if (tid < kC) sBeta[tid] = tid < nvalid ? a.beta[((size_t)b * a.T + t0 + tid) * a.HV + hv] : 0.0f;
     mla::wait_vmcnt<0>();
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- phase 1: NT / DKP threads per key channel, each over RPT rows.  The
   // running Gam is kept for the thread's own rows, the 16-row block bounds
@@ -233,11 +243,20 @@ __global__ void __launch_bounds__(64 * intra_waves<DK>()) kda_intra(KdaArgs a) {
     }
     gl = run;
   }
-  __syncthreads();  // R3 is free: Y and F may be written
+  lds_barrier();  // R3 is free: Y and F may be written
   bf16x8 ktreg[RPT / 8];
   {
     const bool live = ch < DK;
     if (part == 0) Gimg[ch] = live ? exp_(gl) : 1.0f;
+    // every read of this thread's k and q values goes out before the first
+    // in-place write (the writes would otherwise order each row's reads)
+    bf16 kraw[RPT], qraw[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int i = part * RPT + r;
+      kraw[r] = *(const bf16*)(smem_raw + L::OFF_XK + xoff<DKP>(i, ch));
+      qraw[r] = *(const bf16*)(smem_raw + L::OFF_XQ + xoff<DKP>(i, ch));
+    }
 #pragma unroll
     for (int i8 = 0; i8 < RPT / 8; ++i8) {
       bf16x8 at8;
@@ -247,7 +266,7 @@ __global__ void __launch_bounds__(64 * intra_waves<DK>()) kda_intra(KdaArgs a) {
         const float gm = own[r];
         bf16* pk = (bf16*)(smem_raw + L::OFF_XK + xoff<DKP>(i, ch));
         bf16* pq = (bf16*)(smem_raw + L::OFF_XQ + xoff<DKP>(i, ch));
-        const float kk = (float)*pk, qq = (float)*pq;
+        const float kk = (float)kraw[r], qq = (float)qraw[r];
         const float bi = sBeta[i];
         const float e = exp_(gm);
         ktreg[i8][u] = (bf16)(kk * e);
@@ -268,7 +287,7 @@ __global__ void __launch_bounds__(64 * intra_waves<DK>()) kda_intra(KdaArgs a) {
         for (int J = 0; J <= I; ++J) sF[(p++) * DKP + ch] = exp_(gs[I] - ge[J]);
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- phase 2: A and Bm by 16-row block rows I (blocks J <= I).  With 8
   // waves, wave I forms A's row I and wave 4 + I Bm's; with 4, wave I both.
@@ -313,7 +332,7 @@ __global__ void __launch_bounds__(64 * intra_waves<DK>()) kda_intra(KdaArgs a) {
         Bimg[i * TP + j] = (bf16)(j <= i ? accB[J][e] : 0.0f);
       }
   }
-  __syncthreads();  // every wave is done with XK / XQ / Y / F
+  lds_barrier();  // every wave is done with XK / XQ / Y / F
   if (doA) {
 #pragma unroll
     for (int J = 0; J < 4; ++J)
@@ -323,7 +342,7 @@ __global__ void __launch_bounds__(64 * intra_waves<DK>()) kda_intra(KdaArgs a) {
         sA[i * AP + j] = j < i ? accA[J][e] : 0.0f;
       }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- phase 3: Tm = (I + A)^{-1} by 16 x 16 blocks, fp32.  Waves 0-3
   // invert their diagonal block by forward substitution (lane c < 16:
@@ -344,7 +363,7 @@ __global__ void __launch_bounds__(64 * intra_waves<DK>()) kda_intra(KdaArgs a) {
       for (int r = 0; r < 16; ++r) sTf[(16 * w + r) * AP + 16 * w + lane] = x[r];
     }
   }
-  __syncthreads();
+  lds_barrier();
   float* sP = (float*)(smem_raw + L::OFF_P) + (w & 3) * 256;
 #pragma unroll
   for (int d = 1; d < 4; ++d) {
@@ -370,25 +389,25 @@ __global__ void __launch_bounds__(64 * intra_waves<DK>()) kda_intra(KdaArgs a) {
         sTf[(16 * I + i) * AP + 16 * J + j] = -acc;
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   // bf16 Tm for the MFMA products (zero above the diagonal blocks)
   for (int e = tid; e < kC * kC; e += NT) {
     const int i = e >> 6, j = e & 63;
     sT[i * TP + j] = (bf16)((j >> 4) > (i >> 4) ? 0.0f : sTf[i * AP + j]);
   }
-  __syncthreads();  // A and the fp32 Tm are dead: K~^T and V^T may be written
+  lds_barrier();  // A and the fp32 Tm are dead: K~^T and V^T may be written
 #pragma unroll
   for (int i8 = 0; i8 < RPT / 8; ++i8) *(bf16x8*)&sKt[ch * TP + part * RPT + 8 * i8] = ktreg[i8];
 #pragma unroll
   for (int u = 0; u < VPER; ++u) {
-    const int r = tid + NT * u, i = r / VCH, c8 = 8 * (r % VCH);
+    const int r = tid + NT * u, i = r % kC, c8 = 8 * (r / kC);
     if (r < NV) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) sVt[(c8 + e) * TP + i] = vreg[u][e];
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- phase 4: W^T = (k e^Gam)^T Tm^T (tiles: 16 channels x 16 rows) and
   // U = Tm V (tiles: 16 rows x 16 value channels)
