@@ -155,3 +155,24 @@ def test_kda_poisoned_workspace_and_repeat(o):
     assert torch.equal(a, b) and torch.equal(sa, sb)
     ref_o, ref_s = _oracle(o, d)
     _close(to_host_f64(a), ref_o, "o (poisoned workspace)")
+
+
+def test_kda_single_steps_chained(o):
+    """Decode-style use: five one-position calls, each starting from the
+    state the previous one returned, equal one call over the five positions
+    and the oracle (full head width, GVA)."""
+    import torch
+    import rank_latent_causal_amd as mla
+    d = dg.kda_inputs(2, 5, 2, 2, 128, 128, dtype=dg.BF16, seed=11700, init_state=True)
+    log("kda five chained single steps, K=V=128")
+    one = lambda x, t: to_dev(np.ascontiguousarray(x[:, t:t + 1]))
+    st = to_dev(d["s0"])
+    outs = []
+    for t in range(5):
+        ot, st = mla.kda_chunk_forward(*[one(d[k], t) for k in ("q", "k", "v", "g", "beta")], G=2,
+                                       initial_state=st, final_state=True)
+        outs.append(ot)
+    torch.cuda.synchronize()
+    ref_o, ref_s = _oracle(o, d)
+    _close(to_host_f64(torch.cat(outs, dim=1)), ref_o, "chained single steps o")
+    _close(st.cpu().numpy(), ref_s, "chained single steps final state")
