@@ -10,7 +10,9 @@ HIP events on the stream it runs on.
 Printed (one JSON line): prefill TFLOP/s as `value` (causal-triangle
 algorithmic FLOPs), chunked-prefill TFLOP/s, decode latent-cache GB/s
 (algorithmic bytes), the roofline object of each against MI355X's published
-peaks, and the CPU oracle timed on a bounded row sample of the prefill.  The
+peaks (and, as `measured_peak` / `frac_measured`, against the rates the probe
+kernels sustain on the same device, also printed under "measured_peaks"),
+and the CPU oracle timed on a bounded row sample of the prefill.  The
 full-layer forward (projections, norms, core, output projection at the full
 K3 widths, B=1, T=8192) is timed separately after the steps and reported
 under "forward"; a varlen batch of four chunks over a paged cache under
@@ -89,7 +91,7 @@ def kernel_source_hash() -> str:
     files = []
     for d in (os.path.join(ROOT, "rank_latent_causal_amd", "csrc"), os.path.join(ROOT, "include")):
         files += [os.path.join(d, f) for f in sorted(os.listdir(d))
-                  if f.endswith((".h", ".hip")) and not f.startswith("kda")]
+                  if f.endswith((".h", ".hip")) and not f.startswith(("kda", "probes"))]
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
         with open(f, "rb") as fh:
@@ -141,6 +143,66 @@ def measured_kda_traffic():
     except OSError:
         return None
     return None
+
+
+PROBE_LIB = os.path.join(ROOT, "rank_latent_causal_amd", "libmla_probes.so")
+
+
+def measure_peaks(torch):
+    """Sustained rates of this device from the probe kernels of
+    libmla_probes.so: bf16 MFMA TFLOP/s (16x16x32 MFMA chains on random
+    operands, 8 waves on every CU) and HBM read GB/s (one streaming read of
+    4 GiB, far past the 256 MiB infinity cache).  None if the probe library
+    is not built."""
+    import ctypes as ct
+    if not os.path.exists(PROBE_LIB):
+        return None
+    L = ct.CDLL(PROBE_LIB)
+    L.probe_mfma_bf16.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_void_p]
+    L.probe_stream_read.argtypes = [ct.c_void_p, ct.c_size_t, ct.c_void_p, ct.c_int, ct.c_void_p]
+    stream = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    g = torch.Generator(device="cuda").manual_seed(12345)
+    src = (torch.rand(4096 * 8, generator=g, device="cuda") * 2 - 1).to(torch.bfloat16)
+    sink = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    iters = 4000
+    assert L.probe_mfma_bf16(src.data_ptr(), sink.data_ptr(), cus, 200, stream) == 0
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    assert L.probe_mfma_bf16(src.data_ptr(), sink.data_ptr(), cus, iters, stream) == 0
+    ev[1].record()
+    torch.cuda.synchronize()
+    mfma = cus * 8 * iters * 32 * 16384.0 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    usink = torch.empty(cus * 16, dtype=torch.int32, device="cuda")
+    assert L.probe_stream_read(buf.data_ptr(), nbytes, usink.data_ptr(), cus * 16, stream) == 0
+    ts = []
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        assert L.probe_stream_read(buf.data_ptr(), nbytes, usink.data_ptr(), cus * 16, stream) == 0
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    del buf
+    hbm = nbytes / (min(ts) * 1e-3) / 1e9
+    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbs": round(hbm, 1)}
+
+
+def add_measured_peaks(res, peaks):
+    """Adds to every roofline object of res the measured peak of its bound
+    and the achieved fraction of it (next to the published `peak`)."""
+    def visit(o):
+        if isinstance(o, dict):
+            r = o.get("roofline")
+            if isinstance(r, dict) and r.get("achieved") is not None:
+                mp = peaks["mfma_bf16_tflops"] if r.get("bound") == "mfma" else peaks["hbm_read_gbs"]
+                r["measured_peak"] = mp
+                r["frac_measured"] = round(r["achieved"] / mp, 4)
+            for v in o.values():
+                visit(v)
+    visit(res)
 
 
 def copy_probe(nbytes: int = 1 << 30):
@@ -431,6 +493,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the probe kernels that measure this device's sustained MFMA and HBM read rates")
     ap.add_argument("--which", choices=["both", "prefill", "decode", "forward", "backward", "layer_train", "kda"],
                     default="both",
                     help="both: prefill, chunked prefill and decode, then the full-layer forward and the backward")
@@ -578,6 +642,11 @@ def main():
         res["layer_train"] = bench_layer_train(torch, mla, args.steps, args.warmup)
     if args.which in ("both", "kda"):
         res["kda"] = bench_kda(torch, mla, args.steps, args.warmup)
+    if not args.no_peaks:
+        peaks = measure_peaks(torch)
+        if peaks is not None:
+            res["measured_peaks"] = peaks
+            add_measured_peaks(res, peaks)
     if not args.no_cpu_baseline and do_pre:
         res["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
     print(json.dumps(res), flush=True)

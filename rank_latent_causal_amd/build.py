@@ -11,6 +11,9 @@ SRCS = [os.path.join(HERE, "csrc", f) for f in ("mla_absorb.hip", "kda.hip")]
 HEADERS = [os.path.join(HERE, "csrc", f) for f in os.listdir(os.path.join(HERE, "csrc")) if f.endswith(".h")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmla_absorb.so")
+# measurement probes used by bench.py only (not part of the C ABI)
+PROBE_SRC = os.path.join(HERE, "csrc", "probes.hip")
+PROBE_LIB = os.path.join(HERE, "libmla_probes.so")
 ARCH = "gfx950"
 
 
@@ -21,11 +24,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(out_path: str = LIB, verbose: bool = False) -> str:
+def _compile(srcs, out_path: str, verbose: bool) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed fp32 VALU forms are kept out of every kernel
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           f"-I{INCLUDE}", *SRCS, "-o", out_path + ".tmp"]
+           f"-I{INCLUDE}", *srcs, "-o", out_path + ".tmp"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "not a recognized feature" not in l)
     if res.returncode != 0:
@@ -33,6 +36,13 @@ def build(out_path: str = LIB, verbose: bool = False) -> str:
     if verbose and msgs.strip():
         print(msgs)
     os.replace(out_path + ".tmp", out_path)
+    return out_path
+
+
+def build(out_path: str = LIB, verbose: bool = False) -> str:
+    """The MLA / KDA library, then the measurement probes."""
+    _compile(SRCS, out_path, verbose)
+    _compile([PROBE_SRC], PROBE_LIB, verbose)
     return out_path
 
 
