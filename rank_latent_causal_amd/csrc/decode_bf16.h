@@ -30,8 +30,8 @@ namespace mla {
 // ----------------------------------------------------------------- W_UK^T
 template <typename T>
 __global__ void __launch_bounds__(256) mla_wuk_transpose(const T* __restrict__ w, T* __restrict__ wt,
-                                                         int H, int DQ, int R) {
-  // one 32 (d) x 32 (j) tile per workgroup: read rows of W_UK[h], write rows of W_UK^T[h]
+                                                         int DQ, int R) {
+  // one 32 (d) x 32 (j) tile per workgroup (head blockIdx.z): read rows of W_UK[h], write rows of W_UK^T[h]
   __shared__ T tile[32][33];
   const int h = blockIdx.z;
   const int j0 = blockIdx.x * 32, d0 = blockIdx.y * 32;

@@ -151,8 +151,6 @@ __global__ void __launch_bounds__(64 * intra_waves<DK>()) kda_intra(KdaArgs a) {
   constexpr int DKP = D::DKP, WP = D::WP, TP = D::TP, AP = L::A_PITCH;
   __shared__ __attribute__((aligned(16))) char smem_raw[L::BYTES];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
-  bf16* sXK = (bf16*)(smem_raw + L::OFF_XK);
-  bf16* sXQ = (bf16*)(smem_raw + L::OFF_XQ);
   bf16* sY = (bf16*)(smem_raw + L::OFF_Y);
   float* sF = (float*)(smem_raw + L::OFF_F);
   float* sG = (float*)(smem_raw + L::OFF_G);

@@ -56,7 +56,7 @@ struct DecodeLayout {
   size_t qabs = 0, part_o = 0, part_ml = 0, total = 0;
 };
 
-DecodeLayout decode_layout(int B, int H, int dq, int r, int G) {
+DecodeLayout decode_layout(int B, int H, int r, int G) {
   DecodeLayout L;
   size_t off = 0;
   L.qabs = off;
@@ -118,9 +118,9 @@ struct PagedDecodeLayout {
   size_t lens = 0, cu_t = 0, total = 0;
 };
 
-PagedDecodeLayout paged_decode_layout(int B, int H, int dq, int r, int G) {
+PagedDecodeLayout paged_decode_layout(int B, int H, int r, int G) {
   PagedDecodeLayout L;
-  L.d = decode_layout(B, H, dq, r, G);
+  L.d = decode_layout(B, H, r, G);
   size_t off = L.d.total;
   L.lens = off;
   off = align_up(off + (size_t)B * sizeof(int));
@@ -146,7 +146,7 @@ bool paged_geometry_ok(int B, int r, long long num_pages, int page_size, int max
 
 void launch_wuk_transpose(const bf16* w, bf16* wt, int H, int dq, int r, hipStream_t s) {
   hipLaunchKernelGGL((mla::mla_wuk_transpose<bf16>), dim3((r + 31) / 32, (dq + 31) / 32, H), dim3(256), 0, s,
-                     w, wt, H, dq, r);
+                     w, wt, dq, r);
 }
 
 struct ForwardLayout {
@@ -553,7 +553,7 @@ size_t mla_absorb_decode_workspace_size(int B, int H, int d_q, int r, int num_sp
   if (dtype != MLA_DTYPE_BF16) return kBadSize;
   int G = num_splits > 0 ? num_splits : device_cu_count();
   if (G <= 0) return kBadSize;
-  return decode_layout(B, H, d_q, r, G).total;
+  return decode_layout(B, H, r, G).total;
 }
 
 mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* cu_seqlens,
@@ -588,12 +588,12 @@ mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* 
   if (H > 16 * mla::kDecodeWaves) return MLA_ERR_UNSUPPORTED;  // 16 heads per wave
   int G = num_splits > 0 ? num_splits : device_cu_count();
   if (G <= 0) return MLA_ERR_HIP;
-  const size_t need = decode_layout(B, H, d_q, r, G).total;
+  const size_t need = decode_layout(B, H, r, G).total;
   if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
   if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
   // every range must own at least one cache row (the merge relies on it)
   if ((long long)G > total_len) G = (int)total_len;
-  const DecodeLayout L = decode_layout(B, H, d_q, r, G);
+  const DecodeLayout L = decode_layout(B, H, r, G);
   char* ws = (char*)workspace;
 
   mla::DecodeAbsorbArgs aa{};
@@ -618,7 +618,7 @@ size_t mla_absorb_decode_paged_workspace_size(int B, int H, int d_q, int r, int 
   if (dtype != MLA_DTYPE_BF16) return kBadSize;
   const int G = num_splits > 0 ? num_splits : device_cu_count();
   if (G <= 0) return kBadSize;
-  return paged_decode_layout(B, H, d_q, r, G).total;
+  return paged_decode_layout(B, H, r, G).total;
 }
 
 mla_status mla_absorb_decode_paged(const void* q, const void* c_pages, const int32_t* block_table,
@@ -639,7 +639,7 @@ mla_status mla_absorb_decode_paged(const void* q, const void* c_pages, const int
     return MLA_ERR_UNSUPPORTED;
   const int G = num_splits > 0 ? num_splits : device_cu_count();
   if (G <= 0) return MLA_ERR_HIP;
-  const PagedDecodeLayout L = paged_decode_layout(B, H, d_q, r, G);
+  const PagedDecodeLayout L = paged_decode_layout(B, H, r, G);
   if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
   if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
@@ -758,6 +758,20 @@ mla_status mla_absorb_prefill_backward(const void* q, const void* c, const void*
                                d_q, d_v, r, scale, dtype, workspace, workspace_bytes, stream);
 }
 
+// Shape checks shared by the full-layer forward, its training form and its backward.
+static mla_status layer_shape_check(int B, int T, int D, int q_rank, int H, int d_q, int d_v, int r) {
+  if (B <= 0 || T <= 0 || D <= 0 || q_rank <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!bf16_shape_supported(d_q, d_v, r)) return MLA_ERR_UNSUPPORTED;
+  // projection contractions come in 64-wide k tiles; normalised rows fit one wave
+  if (D % 64 || q_rank % 64 || (H * d_v) % 64 || (H * d_q) % 8 || D % 8 || r % 8 || q_rank % 8)
+    return MLA_ERR_UNSUPPORTED;
+  if (r > 64 * 8 * mla::kNormMaxChunks || q_rank > 64 * 8 * mla::kNormMaxChunks) return MLA_ERR_UNSUPPORTED;
+  if (!fits(B, T, D) || !fits(B, T, H, d_q > d_v ? d_q : d_v) || (long long)B * T >= (1LL << 31))
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
 size_t mla_gated_forward_workspace_size(int B, int T, int q_rank, int H, int d_q, int d_v, int r,
                                         mla_dtype dtype) {
   if (B <= 0 || T <= 0 || q_rank <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return kBadSize;
@@ -770,22 +784,15 @@ mla_status mla_gated_forward(const void* x, const void* w_kv_down, const void* k
                              const void* w_gate, const void* w_o, void* y, int B, int T, int D, int q_rank,
                              int H, int d_q, int d_v, int r, float eps, float scale, mla_dtype dtype,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  if (!x || !w_kv_down || !kv_norm || !w_q_down || !q_norm || !w_q_up || !w_uk || !w_uv || !w_gate || !w_o || !y)
-    return MLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o, y};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return MLA_ERR_INVALID_ARG;
   if (B <= 0 || T <= 0 || D <= 0 || q_rank <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0)
     return MLA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !std::isfinite(eps) || eps < 0.0f) return MLA_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, w_kv_down, kv_norm, w_q_down, q_norm, w_q_up, w_uk, w_uv, w_gate, w_o, y};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return MLA_ERR_INVALID_ARG;
   if (dtype != MLA_DTYPE_BF16) return MLA_ERR_UNSUPPORTED;
-  if (!bf16_shape_supported(d_q, d_v, r)) return MLA_ERR_UNSUPPORTED;
-  // projection contractions come in 64-wide k tiles; normalised rows fit one wave
-  if (D % 64 || q_rank % 64 || (H * d_v) % 64 || (H * d_q) % 8 || D % 8 || r % 8 || q_rank % 8)
-    return MLA_ERR_UNSUPPORTED;
-  if (r > 64 * 8 * mla::kNormMaxChunks || q_rank > 64 * 8 * mla::kNormMaxChunks) return MLA_ERR_UNSUPPORTED;
-  if (!fits(B, T, D) || !fits(B, T, H, d_q > d_v ? d_q : d_v) || (long long)B * T >= (1LL << 31))
-    return MLA_ERR_UNSUPPORTED;
+  const mla_status st0 = layer_shape_check(B, T, D, q_rank, H, d_q, d_v, r);
+  if (st0 != MLA_OK) return st0;
   const ForwardLayout L = forward_layout(B, T, q_rank, H, d_q, d_v, r);
   if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
   if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
@@ -816,20 +823,6 @@ mla_status mla_gated_forward(const void* x, const void* w_kv_down, const void* k
   return launch_status();
 }
 
-
-// Shape checks shared by the full-layer forward, its training form and its backward.
-static mla_status layer_shape_check(int B, int T, int D, int q_rank, int H, int d_q, int d_v, int r) {
-  if (B <= 0 || T <= 0 || D <= 0 || q_rank <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0)
-    return MLA_ERR_INVALID_ARG;
-  if (!bf16_shape_supported(d_q, d_v, r)) return MLA_ERR_UNSUPPORTED;
-  // projection contractions come in 64-wide k tiles; normalised rows fit one wave
-  if (D % 64 || q_rank % 64 || (H * d_v) % 64 || (H * d_q) % 8 || D % 8 || r % 8 || q_rank % 8)
-    return MLA_ERR_UNSUPPORTED;
-  if (r > 64 * 8 * mla::kNormMaxChunks || q_rank > 64 * 8 * mla::kNormMaxChunks) return MLA_ERR_UNSUPPORTED;
-  if (!fits(B, T, D) || !fits(B, T, H, d_q > d_v ? d_q : d_v) || (long long)B * T >= (1LL << 31))
-    return MLA_ERR_UNSUPPORTED;
-  return MLA_OK;
-}
 
 size_t mla_gated_train_state_size(int B, int T, int q_rank, int H, int d_q, int d_v, int r, mla_dtype dtype) {
   if (B <= 0 || T <= 0 || q_rank <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0) return kBadSize;
