@@ -47,9 +47,8 @@ size_t kda_chunk_workspace_size(int B, int T, int H, int G, int K, int V, mla_dt
  *   o              [B, T, G*H, V]  bf16 output (written)
  *   final_state    [B, G*H, K, V]  float32 (written), or NULL
  * Supported head widths: K = V in {16, 64, 128}; dtype MLA_DTYPE_BF16 only;
- * one batch's g must stay under 2e9 bytes (MLA_ERR_UNSUPPORTED otherwise).
- * Positions are processed in chunks of 64 (the last one may be partial).
- * The caller owns every buffer; workspace is
+ * one batch's g must stay under 2e9 bytes (MLA_ERR_UNSUPPORTED otherwise).  Positions are processed in chunks of 64
+ * (the last one may be partial).  The caller owns every buffer; workspace is
  * kda_chunk_workspace_size bytes, 16-byte aligned (MLA_ERR_WORKSPACE
  * otherwise).  All pointers are device pointers, 16-byte aligned
  * (MLA_ERR_INVALID_ARG for a null or misaligned required pointer or a
