@@ -31,7 +31,9 @@ void launch(kda::KdaArgs a, hipStream_t s) {
   constexpr int NVB = DV / VB;
   const long long heads = (long long)a.B * a.HV;
   a.xcd_map = (NVB > 1 && heads % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL((kda::kda_state<DK, DV, VB>), dim3((unsigned)(heads * NVB)), dim3(256), 0, s, a);
+  // two waves per SIMD where the value tiles of a block split evenly
+  constexpr int NW = (VB / 16) % 2 == 0 ? 8 : 4;
+  hipLaunchKernelGGL((kda::kda_state<DK, DV, VB, NW>), dim3((unsigned)(heads * NVB)), dim3(64 * NW), 0, s, a);
 }
 
 }  // namespace

@@ -443,17 +443,26 @@ __global__ void __launch_bounds__(64 * intra_waves<DK>()) kda_intra(KdaArgs a) {
 }
 
 // ------------------------------------------------------------------ state
+// One bf16 store through a raw buffer descriptor: an offset at or past the
+// descriptor's size writes nothing.  Issued from assembly so that every call
+// is exactly one vector memory operation (the state kernel's wait counts rely
+// on it).
+__device__ __forceinline__ void buf_store_b16(const u32x4& rs, unsigned voff, bf16 v) {
+  const unsigned d = (unsigned)__builtin_bit_cast(unsigned short, v);
+  asm volatile("buffer_store_short %0, %1, %2, 0 offen" : : "v"(d), "v"(voff), "s"(rs) : "memory");
+}
+
 // Copies NB bytes (a multiple of 16) from global src into LDS dst: 1 KiB
-// pieces, piece p issued by wave p % 4, the lanes of a last partial piece
+// pieces, piece p issued by wave p % NW, the lanes of a last partial piece
 // past NB masked off (so nothing past dst + NB is written).
-template <int NB>
+template <int NB, int NW>
 __device__ __forceinline__ void copy_image(const char* src, MLA_LDS char* dst, int w, int lane) {
   static_assert(NB % 16 == 0, "16-byte pieces");
   constexpr int PIECES = (NB + 1023) / 1024;
   const u32x4 rs = mla::make_rsrc(src, (unsigned)NB);
 #pragma unroll
   for (int p = 0; p < PIECES; ++p) {
-    if (p % 4 != w) continue;
+    if (p % NW != w) continue;
     if (p * 1024 + 16 * lane < NB) mla::buf2lds16(rs, (unsigned)(p * 1024 + 16 * lane), dst + p * 1024);
   }
 }
@@ -477,15 +486,20 @@ struct StateLds {
   static_assert(BYTES <= 163840, "LDS");
 };
 
-// One workgroup (4 waves) per (batch, value head, VB value columns); wave w
-// owns rows 16 w .. of R and O and channel tiles w, w+4, ... of S.
-template <int DK, int DV, int VB>
-__global__ void __launch_bounds__(256) kda_state(KdaArgs a) {
+// One workgroup (NW = 4 or 8 waves) per (batch, value head, VB value
+// columns).  Wave w owns rows 16 (w % 4) .. of R and O and channel tiles
+// w % 4, w % 4 + 4, ... of S, over the value tiles of its share: all of them
+// with 4 waves, half (w / 4 picks which) with 8.  Eight waves put two on each
+// SIMD, so one wave's LDS reads and MFMA chains run while the other waits.
+template <int DK, int DV, int VB, int NW>
+__global__ void __launch_bounds__(64 * NW) kda_state(KdaArgs a) {
   using D = KdaDims<DK, DV>;
   using L = StateLds<DK, DV, VB>;
   constexpr int DKP = D::DKP, WP = D::WP, TP = D::TP;
   constexpr int NVB = DV / VB, NVT = VB / 16, NCT = DKP / 16, CPW = (NCT + 3) / 4;
+  constexpr int NVW = NVT / (NW / 4);  // value tiles per wave
   static_assert(DV % VB == 0 && VB % 16 == 0, "value blocks");
+  static_assert((NW == 4 || NW == 8) && NVT % (NW / 4) == 0, "waves split the value tiles evenly");
   __shared__ __attribute__((aligned(1024))) char smem_raw[L::BYTES];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
   bf16* sSt = (bf16*)(smem_raw + L::OFF_ST);
@@ -504,6 +518,7 @@ __global__ void __launch_bounds__(256) kda_state(KdaArgs a) {
   }
   const int hv = bh % a.HV, b = bh / a.HV;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int wr = w & 3, V0 = (w >> 2) * NVW;  // row block / channel tile base; first value tile
   const int l16 = lane & 15, kq = lane >> 4;
   const int v0 = vb * VB;
 
@@ -511,71 +526,83 @@ __global__ void __launch_bounds__(256) kda_state(KdaArgs a) {
   auto issue_main = [&](int ci, int st) {
     const char* slot = slot_of(ci);
     MLA_LDS char* dst = smem + st * L::STAGE;
-    copy_image<D::W_BYTES>(slot + D::OFF_W, dst + L::S_W, w, lane);
-    copy_image<D::W_BYTES>(slot + D::OFF_Q, dst + L::S_Q, w, lane);
-    copy_image<D::AT_BYTES>(slot + D::OFF_AT, dst + L::S_AT, w, lane);
-    copy_image<D::B_BYTES>(slot + D::OFF_B, dst + L::S_B, w, lane);
-    copy_image<D::G_BYTES>(slot + D::OFF_G, dst + L::S_G, w, lane);
+    copy_image<D::W_BYTES, NW>(slot + D::OFF_W, dst + L::S_W, w, lane);
+    copy_image<D::W_BYTES, NW>(slot + D::OFF_Q, dst + L::S_Q, w, lane);
+    copy_image<D::AT_BYTES, NW>(slot + D::OFF_AT, dst + L::S_AT, w, lane);
+    copy_image<D::B_BYTES, NW>(slot + D::OFF_B, dst + L::S_B, w, lane);
+    copy_image<D::G_BYTES, NW>(slot + D::OFF_G, dst + L::S_G, w, lane);
   };
   auto issue_ut = [&](int ci) {
-    copy_image<L::UT_SLICE>(slot_of(ci) + D::OFF_UT + v0 * TP * 2, smem + L::OFF_UT, w, lane);
+    copy_image<L::UT_SLICE, NW>(slot_of(ci) + D::OFF_UT + v0 * TP * 2, smem + L::OFF_UT, w, lane);
   };
   issue_main(0, 0);
   issue_ut(0);
 
-  // the state: fragment (m, V) holds channels 16 (w + 4 m) + 4 kq + e of value column 16 V + l16
-  f32x4 S[CPW][NVT];
+  // the state: fragment (m, vv) holds channels 16 (wr + 4 m) + 4 kq + e of
+  // value column 16 (V0 + vv) + l16
+  f32x4 S[CPW][NVW];
 #pragma unroll
   for (int m = 0; m < CPW; ++m) {
-    const int C = w + 4 * m;
+    const int C = wr + 4 * m;
 #pragma unroll
-    for (int V = 0; V < NVT; ++V) {
+    for (int vv = 0; vv < NVW; ++vv) {
+      const int V = V0 + vv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = 16 * C + 4 * kq + e;
-        S[m][V][e] = (a.s0 && C < NCT && c < DK)
+        S[m][vv][e] = (a.s0 && C < NCT && c < DK)
                          ? a.s0[(((size_t)b * a.HV + hv) * DK + c) * DV + v0 + 16 * V + l16]
                          : 0.0f;
       }
       if (C < NCT) {
         bf16x4 s4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s4[e] = (bf16)S[m][V][e];
+        for (int e = 0; e < 4; ++e) s4[e] = (bf16)S[m][vv][e];
         *(bf16x4*)&sSt[(16 * V + l16) * WP + 16 * C + 4 * kq] = s4;
       }
     }
   }
 
+  // O is written with NVW * 4 buffer stores per wave and chunk, always issued
+  // (rows past T fall outside the descriptor and are dropped), so the wait
+  // for chunk ci's copies can leave the previous chunk's stores in flight:
+  // vector memory operations complete in issue order, and those stores are
+  // the youngest.
+  constexpr int OST = NVW * 4;
+  static_assert(OST < 64, "vmcnt range");
   for (int ci = 0; ci < a.NC; ++ci) {
-    mla::wait_vmcnt<0>();
+    if (ci == 0) mla::wait_vmcnt<0>();
+    else mla::wait_vmcnt<OST>();
     mla::wait_lgkmcnt0();
     mla::wg_barrier();  // chunk ci staged, S^T of the previous chunk written, R^T free
     if (ci + 1 < a.NC) issue_main(ci + 1, (ci + 1) & 1);
     const int so = (ci & 1) * L::STAGE;
 
-    // R = U - W S and P = (q e^Gam) S: rows 16 w + 4 kq + e, value column 16 V + l16
-    f32x4 accR[NVT], accP[NVT];
+    // R = U - W S and P = (q e^Gam) S: rows 16 wr + 4 kq + e, value column
+    // 16 (V0 + vv) + l16
+    f32x4 accR[NVW], accP[NVW];
 #pragma unroll
-    for (int V = 0; V < NVT; ++V) accR[V] = accP[V] = f32x4{};
+    for (int vv = 0; vv < NVW; ++vv) accR[vv] = accP[vv] = f32x4{};
 #pragma unroll
     for (int ks = 0; ks < DKP / 32; ++ks) {
       const int c0 = 32 * ks + 8 * kq;
-      const bf16x8 aw = lds8(smem, so + L::S_W + ((16 * w + l16) * WP + c0) * 2);
-      const bf16x8 aq = lds8(smem, so + L::S_Q + ((16 * w + l16) * WP + c0) * 2);
+      const bf16x8 aw = lds8(smem, so + L::S_W + ((16 * wr + l16) * WP + c0) * 2);
+      const bf16x8 aq = lds8(smem, so + L::S_Q + ((16 * wr + l16) * WP + c0) * 2);
 #pragma unroll
-      for (int V = 0; V < NVT; ++V) {
-        const bf16x8 bs = lds8(smem, L::OFF_ST + ((16 * V + l16) * WP + c0) * 2);
-        accR[V] = mla::mfma16(aw, bs, accR[V]);
-        accP[V] = mla::mfma16(aq, bs, accP[V]);
+      for (int vv = 0; vv < NVW; ++vv) {
+        const bf16x8 bs = lds8(smem, L::OFF_ST + ((16 * (V0 + vv) + l16) * WP + c0) * 2);
+        accR[vv] = mla::mfma16(aw, bs, accR[vv]);
+        accP[vv] = mla::mfma16(aq, bs, accP[vv]);
       }
     }
 #pragma unroll
-    for (int V = 0; V < NVT; ++V) {
-      const bf16x4 u4 = *(const MLA_LDS bf16x4*)(smem + L::OFF_UT + ((16 * V + l16) * TP + 16 * w + 4 * kq) * 2);
+    for (int vv = 0; vv < NVW; ++vv) {
+      const int V = V0 + vv;
+      const bf16x4 u4 = *(const MLA_LDS bf16x4*)(smem + L::OFF_UT + ((16 * V + l16) * TP + 16 * wr + 4 * kq) * 2);
       bf16x4 r4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r4[e] = (bf16)((float)u4[e] - accR[V][e]);
-      *(bf16x4*)&sRt[(16 * V + l16) * TP + 16 * w + 4 * kq] = r4;
+      for (int e = 0; e < 4; ++e) r4[e] = (bf16)((float)u4[e] - accR[vv][e]);
+      *(bf16x4*)&sRt[(16 * V + l16) * TP + 16 * wr + 4 * kq] = r4;
     }
     mla::wait_lgkmcnt0();
     mla::wg_barrier();  // R^T complete; every wave is done reading S^T and U^T
@@ -585,44 +612,50 @@ __global__ void __launch_bounds__(256) kda_state(KdaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int j0 = 32 * ks + 8 * kq;
-      const bf16x8 ab = lds8(smem, so + L::S_B + ((16 * w + l16) * TP + j0) * 2);
+      const bf16x8 ab = lds8(smem, so + L::S_B + ((16 * wr + l16) * TP + j0) * 2);
 #pragma unroll
-      for (int V = 0; V < NVT; ++V)
-        accP[V] = mla::mfma16(ab, lds8(smem, L::OFF_RT + ((16 * V + l16) * TP + j0) * 2), accP[V]);
+      for (int vv = 0; vv < NVW; ++vv)
+        accP[vv] = mla::mfma16(ab, lds8(smem, L::OFF_RT + ((16 * (V0 + vv) + l16) * TP + j0) * 2), accP[vv]);
     }
-    const int t0 = ci * kC;
+    {
+      // rows t0 .. min(t0 + 64, T) - 1 of this head; a row at or past T lies
+      // past the descriptor's last byte
+      const int t0 = ci * kC;
+      const int rows = min(kC, a.T - t0);
+      const u32x4 rs = mla::make_rsrc(a.o + ((size_t)b * a.T + t0) * a.HV * DV, (unsigned)(rows * a.HV * DV * 2));
 #pragma unroll
-    for (int V = 0; V < NVT; ++V)
+      for (int vv = 0; vv < NVW; ++vv)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = t0 + 16 * w + 4 * kq + e;
-        if (t < a.T) a.o[(((size_t)b * a.T + t) * a.HV + hv) * DV + v0 + 16 * V + l16] = (bf16)accP[V][e];
-      }
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * wr + 4 * kq + e;
+          buf_store_b16(rs, (unsigned)(((r * a.HV + hv) * DV + v0 + 16 * (V0 + vv) + l16) * 2), (bf16)accP[vv][e]);
+        }
+    }
 
     // S = e^{Gam_63} S + A_hat^T R
 #pragma unroll
     for (int m = 0; m < CPW; ++m) {
-      const int C = w + 4 * m;
+      const int C = wr + 4 * m;
       if (C >= NCT) continue;
       const f32x4 gc = *(const MLA_LDS f32x4*)(smem + so + L::S_G + (16 * C + 4 * kq) * 4);
 #pragma unroll
-      for (int V = 0; V < NVT; ++V)
+      for (int vv = 0; vv < NVW; ++vv)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[m][V][e] *= gc[e];
+        for (int e = 0; e < 4; ++e) S[m][vv][e] *= gc[e];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int j0 = 32 * ks + 8 * kq;
         const bf16x8 aa = lds8(smem, so + L::S_AT + ((16 * C + l16) * TP + j0) * 2);
 #pragma unroll
-        for (int V = 0; V < NVT; ++V)
-          S[m][V] = mla::mfma16(aa, lds8(smem, L::OFF_RT + ((16 * V + l16) * TP + j0) * 2), S[m][V]);
+        for (int vv = 0; vv < NVW; ++vv)
+          S[m][vv] = mla::mfma16(aa, lds8(smem, L::OFF_RT + ((16 * (V0 + vv) + l16) * TP + j0) * 2), S[m][vv]);
       }
 #pragma unroll
-      for (int V = 0; V < NVT; ++V) {
+      for (int vv = 0; vv < NVW; ++vv) {
         bf16x4 s4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s4[e] = (bf16)S[m][V][e];
-        *(bf16x4*)&sSt[(16 * V + l16) * WP + 16 * C + 4 * kq] = s4;
+        for (int e = 0; e < 4; ++e) s4[e] = (bf16)S[m][vv][e];
+        *(bf16x4*)&sSt[(16 * (V0 + vv) + l16) * WP + 16 * C + 4 * kq] = s4;
       }
     }
   }
@@ -630,14 +663,14 @@ __global__ void __launch_bounds__(256) kda_state(KdaArgs a) {
   if (a.s_out) {
 #pragma unroll
     for (int m = 0; m < CPW; ++m) {
-      const int C = w + 4 * m;
+      const int C = wr + 4 * m;
       if (C >= NCT) continue;
 #pragma unroll
-      for (int V = 0; V < NVT; ++V)
+      for (int vv = 0; vv < NVW; ++vv)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int c = 16 * C + 4 * kq + e;
-          if (c < DK) a.s_out[(((size_t)b * a.HV + hv) * DK + c) * DV + v0 + 16 * V + l16] = S[m][V][e];
+          if (c < DK) a.s_out[(((size_t)b * a.HV + hv) * DK + c) * DV + v0 + 16 * (V0 + vv) + l16] = S[m][vv][e];
         }
     }
   }
