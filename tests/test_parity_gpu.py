@@ -1,7 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
 same seeded inputs, element by element, plus structural invariants that
 hold at any size."""
-import os
 import sys
 
 import numpy as np
