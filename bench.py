@@ -502,8 +502,8 @@ def main():
                     help="also run one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU's hot path only (got --gpus {args.gpus}); multi-GPU runs are not "
-              f"part of this build", file=sys.stderr)
+        print(f"bench.py measures one GPU's hot path only (got --gpus {args.gpus}); the library has no "
+              f"multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
