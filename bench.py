@@ -9,19 +9,22 @@ HIP events on the stream it runs on.
 
 Printed (one JSON line): prefill TFLOP/s as `value` (causal-triangle
 algorithmic FLOPs), chunked-prefill TFLOP/s, decode latent-cache GB/s
-(algorithmic bytes), the roofline object of each against MI355X's published
-peaks (and, as `measured_peak` / `frac_measured`, against the rates the probe
-kernels sustain on the same device, also printed under "measured_peaks"),
-and the CPU oracle timed on a bounded row sample of the prefill.  The
-full-layer forward (projections, norms, core, output projection at the full
-K3 widths, B=1, T=8192) is timed separately after the steps and reported
-under "forward"; a varlen batch of four chunks over a paged cache under
-"extend_varlen"; the backward of the prefill core (with the log-sum-exp of a
-training forward run before it) likewise under "backward"; one training
-step of the whole layer (training forward, then the layer backward) under
-"layer_train"; chunk_kda over B=1, T=8192, H=96, K=V=128 under "kda".  The decode over a paged cache (the decode workload in
+(algorithmic bytes), each with a roofline object against MI355X's published
+peaks (2.5 PFLOP/s dense bf16 MFMA, 8 TB/s HBM3E, 157.3 TFLOP/s fp32
+vector), and the CPU oracle (cpu_baseline): a bounded row sample of the
+full prefill, plus the whole decode call and the whole toy and mid-scale
+prefill calls.  The smaller prefill workloads (toy fp32, toy-max B=4
+T=2048, mid-scale B=4 T=4096 H=32 r=256) are timed whole under their names.
+The full-layer forward (projections, norms, core, output projection at the
+full K3 widths, B=1, T=8192) is timed separately after the steps and
+reported under "forward"; a varlen batch of four chunks over a paged cache
+under "extend_varlen"; the backward of the prefill core (with the
+log-sum-exp of a training forward run before it) likewise under
+"backward"; one training step of the whole layer (training forward, then
+the layer backward) under "layer_train"; chunk_kda over B=1, T=8192, H=96,
+K=V=128 under "kda".  The decode over a paged cache (the decode workload in
 shuffled 64-row pages) runs in each step right after the packed decode and
-is reported under "decode_paged".  Neither is part of ms_per_step.
+is reported under "decode_paged".  None of these is part of ms_per_step.
 """
 from __future__ import annotations
 
@@ -41,6 +44,7 @@ import datagen as dg  # noqa: E402
 METRIC = "absorbed-MLA prefill TFLOP/s + decode latent-cache GB/s (% of roofline), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs x 2.4 GHz)
 
 
 def prefill_flops(B, T, H, dq, dv, r):
@@ -91,7 +95,7 @@ def kernel_source_hash() -> str:
     files = []
     for d in (os.path.join(ROOT, "rank_latent_causal_amd", "csrc"), os.path.join(ROOT, "include")):
         files += [os.path.join(d, f) for f in sorted(os.listdir(d))
-                  if f.endswith((".h", ".hip")) and not f.startswith(("kda", "probes"))]
+                  if f.endswith((".h", ".hip")) and not f.startswith("kda")]
     for f in files:
         h.update(os.path.relpath(f, ROOT).encode())
         with open(f, "rb") as fh:
@@ -145,66 +149,6 @@ def measured_kda_traffic():
     return None
 
 
-PROBE_LIB = os.path.join(ROOT, "rank_latent_causal_amd", "libmla_probes.so")
-
-
-def measure_peaks(torch):
-    """Sustained rates of this device from the probe kernels of
-    libmla_probes.so: bf16 MFMA TFLOP/s (16x16x32 MFMA chains on random
-    operands, 8 waves on every CU) and HBM read GB/s (one streaming read of
-    4 GiB, far past the 256 MiB infinity cache).  None if the probe library
-    is not built."""
-    import ctypes as ct
-    if not os.path.exists(PROBE_LIB):
-        return None
-    L = ct.CDLL(PROBE_LIB)
-    L.probe_mfma_bf16.argtypes = [ct.c_void_p, ct.c_void_p, ct.c_int, ct.c_int, ct.c_void_p]
-    L.probe_stream_read.argtypes = [ct.c_void_p, ct.c_size_t, ct.c_void_p, ct.c_int, ct.c_void_p]
-    stream = ct.c_void_p(torch.cuda.current_stream().cuda_stream)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    g = torch.Generator(device="cuda").manual_seed(12345)
-    src = (torch.rand(4096 * 8, generator=g, device="cuda") * 2 - 1).to(torch.bfloat16)
-    sink = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
-    iters = 4000
-    assert L.probe_mfma_bf16(src.data_ptr(), sink.data_ptr(), cus, 200, stream) == 0
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record()
-    assert L.probe_mfma_bf16(src.data_ptr(), sink.data_ptr(), cus, iters, stream) == 0
-    ev[1].record()
-    torch.cuda.synchronize()
-    mfma = cus * 8 * iters * 32 * 16384.0 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12
-    nbytes = 4 << 30
-    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    usink = torch.empty(cus * 16, dtype=torch.int32, device="cuda")
-    assert L.probe_stream_read(buf.data_ptr(), nbytes, usink.data_ptr(), cus * 16, stream) == 0
-    ts = []
-    for _ in range(3):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        assert L.probe_stream_read(buf.data_ptr(), nbytes, usink.data_ptr(), cus * 16, stream) == 0
-        b.record()
-        torch.cuda.synchronize()
-        ts.append(a.elapsed_time(b))
-    del buf
-    hbm = nbytes / (min(ts) * 1e-3) / 1e9
-    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbs": round(hbm, 1)}
-
-
-def add_measured_peaks(res, peaks):
-    """Adds to every roofline object of res the measured peak of its bound
-    and the achieved fraction of it (next to the published `peak`)."""
-    def visit(o):
-        if isinstance(o, dict):
-            r = o.get("roofline")
-            if isinstance(r, dict) and r.get("achieved") is not None:
-                mp = peaks["mfma_bf16_tflops"] if r.get("bound") == "mfma" else peaks["hbm_read_gbs"]
-                r["measured_peak"] = mp
-                r["frac_measured"] = round(r["achieved"] / mp, 4)
-            for v in o.values():
-                visit(v)
-    visit(res)
-
-
 def copy_probe(nbytes: int = 1 << 30):
     """One plain device-to-device copy of nbytes: the reference kernel whose
     FETCH_SIZE / WRITE_SIZE readings scale the counters to bytes."""
@@ -225,9 +169,14 @@ def dev(x):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def cpu_baseline(pre, target_s: float):
-    """The oracle on a sample of query rows of the prefill workload, sized to
-    take about target_s seconds; reported in TFLOP/s of the same count."""
+def cpu_baseline(pre, dec, target_s: float, small: dict):
+    """The oracle as it stands, on the host threads OpenMP gives it.
+
+    Headline (value): a sample of query rows of the full-width prefill,
+    sized to take about target_s seconds, in TFLOP/s of the same algorithmic
+    count.  Also timed, each as a whole call: the full decode workload (all
+    64 sequences, GB/s of the same algorithmic bytes) and the prefill
+    workloads small enough to finish in seconds (`small`: name -> inputs)."""
     import oracle
     o = oracle.get()
     f = dg.as_f32
@@ -248,9 +197,68 @@ def cpu_baseline(pre, target_s: float):
     n = int(min(B * T, max(64, 64 * target_s / max(dt, 1e-3))))
     dt, fl, rows = run(n)
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} query rows (all {H} heads) evenly spaced over the {B}x{T} prefill workload, "
-                      f"{fl / 1e9:.1f} GFLOP in {dt:.1f} s"}
+    res = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+           "sample": f"{n} query rows (all {H} heads) evenly spaced over the {B}x{T} prefill workload, "
+                     f"{fl / 1e9:.1f} GFLOP in {dt:.1f} s"}
+    for name, d in small.items():
+        args = [f(d[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")]
+        t0 = time.perf_counter()
+        o.prefill(*args, d["scale"])
+        sec = time.perf_counter() - t0
+        fl = prefill_flops(d["B"], d["T"], d["H"], d["d_q"], d["d_v"], d["r"])
+        res[name] = {"value": fl / sec / 1e12, "unit": "TFLOP/s", "seconds": round(sec, 3),
+                     "sample": "the whole call"}
+    if dec is not None:
+        cc = f(dec["c_cache"])
+        args = [f(dec["q"]), cc, dec["cu_seqlens"].astype(np.int64), f(dec["w_uk"]), f(dec["w_uv"]),
+                f(dec["gate"])]
+        t0 = time.perf_counter()
+        o.decode(*args, dec["scale"])
+        sec = time.perf_counter() - t0
+        nb = decode_bytes(dec["lengths"], dec["H"], dec["d_q"], dec["d_v"], dec["r"])
+        res["full_decode"] = {"value": nb / sec / 1e9, "unit": "GB/s", "seconds": round(sec, 3),
+                              "sample": f"the whole call: all {dec['B']} sequences, "
+                                        f"{int(dec['cu_seqlens'][-1])} cache rows"}
+        del cc
+    return res
+
+
+def bench_prefill_workload(torch, mla, name, calls, warmup):
+    """One named prefill workload (its whole call: the W_UK transpose and the
+    prefill kernel for bf16, the fp32 kernel for fp32), timed by HIP events
+    around each call on the current stream."""
+    d = dg.workload_inputs(name)
+    args = [dev(d[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")]
+    B, T, H, dq, dv, r = d["B"], d["T"], d["H"], d["d_q"], d["d_v"], d["r"]
+    bf = d["dtype"] == dg.BF16
+    dt = mla.DTYPE_BF16 if bf else mla.DTYPE_F32
+    out = torch.empty((B, T, H * dv), dtype=torch.bfloat16 if bf else torch.float32, device="cuda")
+    ws = torch.empty(max(1, mla.prefill_workspace_size(B, T, H, dq, r, dt)), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        mla.mla_absorb_prefill(*args, d["scale"], out=out, workspace=ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        mla.mla_absorb_prefill(*args, d["scale"], out=out, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    fl = prefill_flops(B, T, H, dq, dv, r)
+    tf = fl / (ms * 1e-3) / 1e12
+    if bf:
+        kernel = ("mla_prefill_bf16_kernel<16,16,32>" if r == 32 else
+                  f"mla_prefill_pair_kernel<{dq},{dv},{r}>") + " (+ W_UK transpose in the same call)"
+        roof = {"bound": "mfma", "peak": PEAK_BF16_TFLOPS}
+    else:
+        kernel = "mla_f32_kernel"
+        roof = {"bound": "alu", "peak": PEAK_F32_VALU_TFLOPS}
+    roof.update({"achieved": round(tf, 3), "unit": "TFLOP/s", "frac": round(tf / roof["peak"], 5),
+                 "traffic": None, "kernel": kernel, "flop_per_launch": fl})
+    return {"value": round(tf, 3), "unit": "TFLOP/s", "ms": round(ms, 5), "calls": calls, "seed": d["seed"],
+            "workload": f"{name}: B={B}, T={T}, H={H}, d_q=d_v={dq}, r={r}, {d['dtype']}, causal, "
+                        f"scale {d['scale']:.4g}",
+            "roofline": roof}
 
 
 def bench_forward(torch, mla, steps, warmup):
@@ -493,8 +501,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-peaks", action="store_true",
-                    help="skip the probe kernels that measure this device's sustained MFMA and HBM read rates")
     ap.add_argument("--which", choices=["both", "prefill", "decode", "forward", "backward", "layer_train", "kda"],
                     default="both",
                     help="both: prefill, chunked prefill and decode, then the full-layer forward and the backward")
@@ -642,13 +648,14 @@ def main():
         res["layer_train"] = bench_layer_train(torch, mla, args.steps, args.warmup)
     if args.which in ("both", "kda"):
         res["kda"] = bench_kda(torch, mla, args.steps, args.warmup)
-    if not args.no_peaks:
-        peaks = measure_peaks(torch)
-        if peaks is not None:
-            res["measured_peaks"] = peaks
-            add_measured_peaks(res, peaks)
+    if args.which in ("both", "prefill"):
+        # the smaller prefill workloads (toy fp32, toy-max, mid-scale): whole
+        # calls, each with its roofline object; not part of ms_per_step
+        for name, calls in (("toy_f32", 200), ("toy_max", 200), ("mid", max(20, args.steps))):
+            res[name] = bench_prefill_workload(torch, mla, name, calls, max(10, args.warmup))
     if not args.no_cpu_baseline and do_pre:
-        res["cpu_baseline"] = cpu_baseline(pre, args.cpu_seconds)
+        small = {name: dg.workload_inputs(name) for name in ("toy_f32", "toy_max", "mid")}
+        res["cpu_baseline"] = cpu_baseline(pre, dec if do_dec else None, args.cpu_seconds, small)
     print(json.dumps(res), flush=True)
 
 

@@ -116,6 +116,20 @@ size_t mla_absorb_decode_workspace_size(int B, int H, int d_q, int r, int num_sp
                                         mla_dtype dtype);
 
 /*
+ * Workspace of mla_absorb_prefill (is_decode = 0, T_or_max_len = T) or of
+ * mla_absorb_decode with the default split count (is_decode != 0;
+ * T_or_max_len, the longest cache, bounds nothing there and only has to be
+ * positive, because decode splits the packed cache rows evenly whatever the
+ * lengths).  d_q is implied by r: the compiled bf16 set pairs r = 32, 256,
+ * 512 with d_q = 16, 64, 128.  Returns 0 for MLA_DTYPE_F32 and (size_t)-1
+ * for invalid sizes, an r outside the compiled set, or (decode) when no
+ * device can be queried for its compute-unit count.  The calls with explicit
+ * head widths and split counts are mla_absorb_prefill_workspace_size and
+ * mla_absorb_decode_workspace_size.
+ */
+size_t mla_absorb_workspace_size(int is_decode, int B, int T_or_max_len, int H, int r, mla_dtype dtype);
+
+/*
  * Decode: one new query per sequence against a packed latent cache.
  *   q          [B, H, d_q]      the query of each sequence, at position len_i - 1
  *   c_cache    [total_len, r]   latents of all sequences back to back; sequence
@@ -133,6 +147,10 @@ size_t mla_absorb_decode_workspace_size(int B, int H, int d_q, int r, int num_sp
  *   num_splits                  workgroups sharing the cache rows evenly
  *                               (<= 0: library default); any value gives the
  *                               same result up to rounding order
+ * The split is stream-K over the packed rows (each workgroup takes
+ * total_len / num_splits consecutive rows, across sequence boundaries), so
+ * the grid depends on total_len and not on the longest sequence: the call
+ * takes total_len, where a per-sequence split would take the maximum length.
  */
 mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* cu_seqlens,
                              const void* w_uk, const void* w_uv, const void* gate, void* out,

@@ -27,9 +27,19 @@ _CFLAGS = ["-O3", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-mavx2", "-mfma",
            "-fno-fast-math", "-Wall", "-Wextra"]
 
 
-def build(out_path: str = LIB, mutant: int = 0, quiet: bool = True) -> str:
-    """Compile the oracle with gcc; mutant != 0 plants one known mistake."""
-    cmd = ["gcc", *_CFLAGS, f"-DORACLE_MUTANT={int(mutant)}", SRC, "-o", out_path + ".tmp", "-lm"]
+LIB_SANITIZED = os.path.join(_HERE, "liboracle_san.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build: any out-of-bounds
+# access, use after free, signed overflow, misaligned or null access, or bad
+# shift aborts the process (the library must then be loaded into a process
+# started with libasan preloaded; see tests/test_oracle_sanitized.py).
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(out_path: str = LIB, mutant: int = 0, quiet: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc; mutant != 0 plants one known mistake;
+    sanitize builds it with ASan and UBSan instead of -O3."""
+    flags = [f for f in _CFLAGS if f != "-O3"] + ["-O1"] + _SAN_FLAGS if sanitize else list(_CFLAGS)
+    cmd = ["gcc", *flags, f"-DORACLE_MUTANT={int(mutant)}", SRC, "-o", out_path + ".tmp", "-lm"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("oracle build failed:\n" + res.stdout + res.stderr)
@@ -396,12 +406,15 @@ _default = None
 
 
 def get() -> Oracle:
-    """The default (non-mutant) oracle, built on first use if missing."""
+    """The default (non-mutant) oracle, built on first use if missing.  With
+    ORACLE_SANITIZE=1 in the environment, the ASan/UBSan build instead."""
     global _default
     if _default is None:
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-            build()
-        _default = Oracle(LIB)
+        san = os.environ.get("ORACLE_SANITIZE") == "1"
+        path = LIB_SANITIZED if san else LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(SRC):
+            build(path, sanitize=san)
+        _default = Oracle(path)
     return _default
 
 

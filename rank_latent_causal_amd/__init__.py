@@ -16,7 +16,7 @@ import os
 __all__ = [
     "LIB_PATH", "MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED", "MLA_ERR_WORKSPACE",
     "MLA_ERR_HIP", "DTYPE_F32", "DTYPE_BF16", "MLAError", "lib", "status_string",
-    "prefill_workspace_size", "decode_workspace_size", "decode_paged_workspace_size", "forward_workspace_size",
+    "prefill_workspace_size", "workspace_size", "decode_workspace_size", "decode_paged_workspace_size", "forward_workspace_size",
     "mla_absorb_prefill", "mla_absorb_extend", "mla_absorb_extend_paged", "mla_absorb_decode",
     "mla_absorb_decode_paged", "mla_cache_append_paged", "mla_gated_forward", "mla_absorb_prefill_train",
     "backward_workspace_size", "mla_absorb_prefill_backward", "varlen_workspace_size",
@@ -33,6 +33,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 EXPORTS = (
     "mla_status_string",
     "mla_absorb_prefill_workspace_size",
+    "mla_absorb_workspace_size",
     "mla_absorb_prefill",
     "mla_absorb_extend",
     "mla_absorb_decode_workspace_size",
@@ -77,6 +78,8 @@ def lib() -> ct.CDLL:
         L.mla_status_string.restype = ct.c_char_p
         L.mla_absorb_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
         L.mla_absorb_prefill_workspace_size.restype = sz
+        L.mla_absorb_workspace_size.argtypes = [I, I, I, I, I, I]
+        L.mla_absorb_workspace_size.restype = sz
         L.mla_absorb_prefill.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, F, I, vp, sz, vp]
         L.mla_absorb_prefill.restype = I
         L.mla_absorb_extend.argtypes = [vp, vp, vp, vp, vp, vp, I, I, I, I, I, I, I, F, I, vp, sz, vp]
@@ -134,6 +137,14 @@ def prefill_workspace_size(B: int, T: int, H: int, d_q: int, r: int, dtype: int)
     n = lib().mla_absorb_prefill_workspace_size(B, T, H, d_q, r, dtype)
     if n == _BAD:
         raise MLAError(MLA_ERR_INVALID_ARG, "mla_absorb_prefill_workspace_size")
+    return n
+
+
+def workspace_size(is_decode: bool, B: int, T_or_max_len: int, H: int, r: int, dtype: int) -> int:
+    """Workspace bytes of a prefill (T) or a default-split decode call."""
+    n = lib().mla_absorb_workspace_size(int(bool(is_decode)), B, T_or_max_len, H, r, dtype)
+    if n == _BAD:
+        raise MLAError(MLA_ERR_INVALID_ARG, "mla_absorb_workspace_size")
     return n
 
 

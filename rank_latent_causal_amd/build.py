@@ -11,9 +11,6 @@ SRCS = [os.path.join(HERE, "csrc", f) for f in ("mla_absorb.hip", "kda.hip")]
 HEADERS = [os.path.join(HERE, "csrc", f) for f in os.listdir(os.path.join(HERE, "csrc")) if f.endswith(".h")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmla_absorb.so")
-# measurement probes used by bench.py only (not part of the C ABI)
-PROBE_SRC = os.path.join(HERE, "csrc", "probes.hip")
-PROBE_LIB = os.path.join(HERE, "libmla_probes.so")
 ARCH = "gfx950"
 
 
@@ -40,9 +37,8 @@ def _compile(srcs, out_path: str, verbose: bool) -> str:
 
 
 def build(out_path: str = LIB, verbose: bool = False) -> str:
-    """The MLA / KDA library, then the measurement probes."""
+    """The MLA / KDA library."""
     _compile(SRCS, out_path, verbose)
-    _compile([PROBE_SRC], PROBE_LIB, verbose)
     return out_path
 
 

@@ -130,11 +130,11 @@ PagedDecodeLayout paged_decode_layout(int B, int H, int r, int G) {
   return L;
 }
 
-// page pool geometry shared by the paged entry points
+// page pool geometry shared by the paged entry points: log2 of a positive
+// power of two, -1 for anything else (no loop, no shift past bit 30)
 int log2_exact(int v) {
-  int k = 0;
-  while ((1 << k) < v) ++k;
-  return (1 << k) == v ? k : -1;
+  if (v <= 0 || (v & (v - 1)) != 0) return -1;
+  return __builtin_ctz((unsigned)v);
 }
 
 bool paged_geometry_ok(int B, int r, long long num_pages, int page_size, int max_pages) {
@@ -545,6 +545,17 @@ mla_status mla_absorb_extend_varlen_paged(const void* q, const void* c_pages, co
   else if (d_q == 64) launch_varlen_bf16<64, 64, 256>(a, cu_q, seq_lens, Nq, max_rows, s);
   else launch_varlen_bf16<128, 128, 512>(a, cu_q, seq_lens, Nq, max_rows, s);
   return launch_status();
+}
+
+size_t mla_absorb_workspace_size(int is_decode, int B, int T_or_max_len, int H, int r, mla_dtype dtype) {
+  if (B <= 0 || T_or_max_len <= 0 || H <= 0 || r <= 0) return kBadSize;
+  if (dtype == MLA_DTYPE_F32) return 0;
+  if (dtype != MLA_DTYPE_BF16) return kBadSize;
+  // the compiled bf16 set pairs each latent width with one head width
+  const int d_q = r == 32 ? 16 : r == 256 ? 64 : r == 512 ? 128 : 0;
+  if (d_q == 0) return kBadSize;
+  return is_decode ? mla_absorb_decode_workspace_size(B, H, d_q, r, 0, dtype)
+                   : mla_absorb_prefill_workspace_size(B, T_or_max_len, H, d_q, r, dtype);
 }
 
 size_t mla_absorb_decode_workspace_size(int B, int H, int d_q, int r, int num_splits, mla_dtype dtype) {

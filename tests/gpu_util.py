@@ -4,6 +4,19 @@ through the binding, and the parity bars.
 Tolerances: bf16 storage with fp32 accumulation is compared element by
 element with |gpu - oracle| <= 2e-2 (absolute); fp32 with
 |gpu - oracle| <= 1e-4 * |oracle| + 1e-6.
+
+At the full widths the outputs have an RMS near 0.025, about the size of
+the absolute bar, so the element bar alone would pass a kernel that is a
+few percent off everywhere.  Every comparison therefore also bounds the
+normwise relative error of each output row (the last axis: one (b, t)
+position, or one decode sequence) and, where the caller names the head
+width, of each head's d_v block of a row:
+  ||gpu - oracle||_2 / ||oracle||_2 <= 1e-2 (bf16), 1e-4 (fp32).
+The bf16 chain rounds q_abs, P and o_lat / l to bf16 (2^-9 relative each)
+and the output itself, which gives normwise errors of a few 1e-3; a head
+scaled 3% off, a wrong row or a dropped term fails the bar.  The achieved
+maximum absolute error and maximum row / head normwise error are printed
+(and appended as JSON lines to the file named by MLA_PARITY_LOG, if set).
 """
 from __future__ import annotations
 
@@ -13,6 +26,8 @@ import datagen as dg
 
 BF16_ATOL = 2e-2
 F32_RTOL, F32_ATOL = 1e-4, 1e-6
+BF16_NORM_REL = 1e-2   # per row / per head block, normwise
+F32_NORM_REL = 1e-4
 
 
 def torch():
@@ -87,21 +102,65 @@ def oracle_decode(o, d, seqs=None, scale=None):
                     f(d["w_uv"]), f(d["gate"]), d["scale"] if scale is None else scale, seqs=seqs)
 
 
-def assert_parity(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
+def _normwise(got: np.ndarray, ref: np.ndarray, width: int) -> np.ndarray:
+    """||gpu - oracle|| / ||oracle|| over consecutive groups of `width`
+    elements of the last axis (a group whose oracle norm is zero is measured
+    against 1, i.e. absolutely)."""
+    g = got.reshape(-1, width)
+    r = ref.reshape(-1, width)
+    den = np.linalg.norm(r, axis=1)
+    return np.linalg.norm(g - r, axis=1) / np.where(den > 0, den, 1.0)
+
+
+def assert_parity(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, block: int | None = None):
+    """Element bar plus the normwise bars per row (last axis) and, with
+    `block` (the head width d_v), per head block of each row."""
     assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - ref)
     if dtype == dg.BF16:
         bad = err > BF16_ATOL
         bar = f"atol {BF16_ATOL}"
+        nbar = BF16_NORM_REL
     else:
         bad = err > F32_RTOL * np.abs(ref) + F32_ATOL
         bar = f"rtol {F32_RTOL} + atol {F32_ATOL}"
+        nbar = F32_NORM_REL
+    width = got.shape[-1] if got.ndim else 1
+    row_rel = _normwise(got, ref, width) if got.size else np.zeros(1)
+    blk_rel = None
+    if block is not None and got.size:
+        assert width % block == 0, f"{what}: row width {width} is not a multiple of {block}"
+        blk_rel = _normwise(got, ref, block)
+    stats = dict(what=what, dtype=dtype, elements=int(got.size), max_abs=float(err.max()) if got.size else 0.0,
+                 max_row_rel=float(row_rel.max()),
+                 max_head_rel=None if blk_rel is None else float(blk_rel.max()),
+                 ref_rms=float(np.sqrt(np.mean(ref * ref))) if got.size else 0.0)
+    _report(stats)
     if bad.any():
         idx = np.unravel_index(np.argmax(err), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} of {err.size} elements beyond {bar}; "
                              f"max err {err.max():.4g} at {idx} (gpu {got[idx]:.6g}, oracle {ref[idx]:.6g})")
-    return float(err.max())
+    if row_rel.max() > nbar:
+        i = int(np.argmax(row_rel))
+        raise AssertionError(f"{what}: row {i} normwise error {row_rel[i]:.3g} > {nbar} "
+                             f"({int((row_rel > nbar).sum())} of {row_rel.size} rows)")
+    if blk_rel is not None and blk_rel.max() > nbar:
+        i = int(np.argmax(blk_rel))
+        raise AssertionError(f"{what}: head block {i} (row {i * block // width}, head {i % (width // block)}) "
+                             f"normwise error {blk_rel[i]:.3g} > {nbar} ({int((blk_rel > nbar).sum())} of "
+                             f"{blk_rel.size} blocks)")
+    return float(err.max()) if got.size else 0.0
+
+
+def _report(stats: dict) -> None:
+    import json
+    import os
+    print("PARITY " + json.dumps(stats), flush=True)
+    path = os.environ.get("MLA_PARITY_LOG")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps(stats) + "\n")
 
 
 def sample_rows(B: int, T: int, n_random: int, seed: int) -> np.ndarray:
@@ -127,3 +186,54 @@ def oracle_forward(o, d, rows=None, eps=None, scale=None):
     """The oracle's full-layer forward with bf16 storage of the stage results."""
     return o.forward(*[dg.as_f32(d[k]) for k in dg.FORWARD_KEYS], d["eps"] if eps is None else eps,
                      d["scale"] if scale is None else scale, stage=o.STAGE_BF16, rows=rows)
+
+
+# ---------------------------------------------------------------- gradients
+GRAD_FROB_REL = 1e-2   # whole tensor and every slice, normwise
+GRAD_FLOOR = 0.5       # a slice is measured against at least this fraction of a typical slice's norm
+
+
+def assert_tensor_close(got, ref, what: str, slices=(), frob_rel: float = GRAD_FROB_REL,
+                        floor: float = GRAD_FLOOR) -> float:
+    """Normwise comparison of a computed tensor (a gradient, a recurrent
+    state) with the oracle's, as a whole and slice by slice.
+
+    `slices` lists (label, shape, axes): the tensors are viewed with `shape`
+    (None keeps theirs) and every index combination of `axes` is one slice
+    (e.g. one token row, or one head).  Each slice s must satisfy
+        ||gpu_s - oracle_s|| <= frob_rel * max(||oracle_s||, floor * rms * sqrt(n_s)),
+    rms being the whole tensor's RMS and n_s the slice's element count: a
+    slice as large as a typical one is held to frob_rel of its own norm, and
+    a slice whose exact value is (near) zero -- where a gradient is a small
+    difference, e.g. the first positions' query gradient -- to frob_rel of
+    `floor` typical slices.  A wrong head, a wrong row or a few wrong rows of
+    a large tensor fail here even when the whole-tensor error stays small.
+    Returns the whole-tensor relative error; every figure is printed."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    frob = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    stats = dict(what=what, elements=int(got.size), ref_rms=rms, frob_rel=frob)
+    fails = []
+    if frob > frob_rel:
+        fails.append(f"relative Frobenius error {frob:.3g} > {frob_rel}")
+    for label, shape, axes in slices:
+        g = got.reshape(shape) if shape is not None else got
+        r = ref.reshape(shape) if shape is not None else ref
+        other = tuple(a for a in range(g.ndim) if a not in axes)
+        n_s = int(np.prod([g.shape[a] for a in other])) if other else 1
+        en = np.sqrt(np.sum((g - r) ** 2, axis=other)).ravel()
+        rn = np.sqrt(np.sum(r * r, axis=other)).ravel()
+        den = np.maximum(rn, floor * rms * np.sqrt(n_s))
+        ratio = en / np.where(den > 0, den, 1.0)
+        stats[f"max_{label}_rel"] = float(ratio.max())
+        if ratio.max() > frob_rel:
+            i = int(np.argmax(ratio))
+            idx = np.unravel_index(i, [g.shape[a] for a in axes])
+            fails.append(f"{label} {tuple(int(x) for x in idx)}: normwise error {ratio[i]:.3g} > {frob_rel} "
+                         f"({int((ratio > frob_rel).sum())} of {ratio.size} {label}s)")
+    _report(stats)
+    assert not fails, f"{what}: " + "; ".join(fails)
+    return frob

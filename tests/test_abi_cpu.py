@@ -53,6 +53,28 @@ def test_prefill_workspace_sizes():
         mla.prefill_workspace_size(0, 1, 1, 16, 32, mla.DTYPE_BF16)
 
 
+def test_unified_workspace_size():
+    """mla_absorb_workspace_size(is_decode, B, T_or_max_len, H, r, dtype):
+    prefill equals the explicit call with the d_q the compiled set pairs
+    with r; fp32 needs none; sizes outside the set are rejected."""
+    for r, dq in ((32, 16), (256, 64), (512, 128)):
+        assert mla.workspace_size(False, 1, 8192, 96, r, mla.DTYPE_BF16) == \
+            mla.prefill_workspace_size(1, 8192, 96, dq, r, mla.DTYPE_BF16)
+    assert mla.workspace_size(False, 2, 128, 8, 32, mla.DTYPE_F32) == 0
+    assert mla.workspace_size(True, 64, 32768, 96, 512, mla.DTYPE_F32) == 0
+    for args in ((False, 1, 8, 4, 128, mla.DTYPE_BF16), (False, 0, 8, 4, 512, mla.DTYPE_BF16),
+                 (True, 4, 0, 4, 512, mla.DTYPE_BF16), (False, 1, 8, 4, 512, 5)):
+        with pytest.raises(mla.MLAError):
+            mla.workspace_size(*args)
+    # decode with the default split count queries the device: without one the
+    # answer is the invalid size, with one it is the explicit call's
+    try:
+        n = mla.workspace_size(True, 64, 32768, 96, 512, mla.DTYPE_BF16)
+    except mla.MLAError:
+        return
+    assert n == mla.decode_workspace_size(64, 96, 128, 512, 0, mla.DTYPE_BF16)
+
+
 def test_decode_workspace_sizes_explicit_splits():
     assert mla.decode_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_F32) == 0
     n = mla.decode_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_BF16)
@@ -275,6 +297,9 @@ def _decode_paged(**kw):
     (dict(lens=FAKE + 4), mla.MLA_ERR_INVALID_ARG),
     (dict(ps=48), mla.MLA_ERR_INVALID_ARG),       # not a power of two
     (dict(ps=16), mla.MLA_ERR_INVALID_ARG),       # smaller than the 32-row tile
+    (dict(ps=(1 << 30) + 1), mla.MLA_ERR_INVALID_ARG),  # above 2^30 and not a power of two
+    (dict(ps=2 ** 31 - 1), mla.MLA_ERR_INVALID_ARG),    # the largest int: no unbounded search
+    (dict(ps=1 << 30), mla.MLA_ERR_UNSUPPORTED),        # a power of two, but the pool overflows int32 rows
     (dict(npg=0), mla.MLA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), mla.MLA_ERR_INVALID_ARG),
     (dict(dtype=mla.DTYPE_F32), mla.MLA_ERR_UNSUPPORTED),
@@ -300,6 +325,7 @@ def _extend_paged(**kw):
     (dict(bt=None), mla.MLA_ERR_INVALID_ARG),
     (dict(S=200), mla.MLA_ERR_INVALID_ARG),       # more rows than max_pages * page_size
     (dict(ps=96), mla.MLA_ERR_INVALID_ARG),
+    (dict(ps=2 ** 31 - 1), mla.MLA_ERR_INVALID_ARG),
     (dict(S=7), mla.MLA_ERR_INVALID_ARG),
     (dict(dtype=mla.DTYPE_F32), mla.MLA_ERR_UNSUPPORTED),
     (dict(dq=96, dv=96, r=384), mla.MLA_ERR_UNSUPPORTED),
@@ -345,6 +371,7 @@ def _varlen(**kw):
     (dict(lens=FAKE + 4), mla.MLA_ERR_INVALID_ARG),
     (dict(Nq=0), mla.MLA_ERR_INVALID_ARG),
     (dict(ps=100), mla.MLA_ERR_INVALID_ARG),
+    (dict(ps=2 ** 31 - 1), mla.MLA_ERR_INVALID_ARG),
     (dict(scale=float("inf")), mla.MLA_ERR_INVALID_ARG),
     (dict(dtype=mla.DTYPE_F32), mla.MLA_ERR_UNSUPPORTED),
     (dict(dq=96, dv=96, r=384), mla.MLA_ERR_UNSUPPORTED),

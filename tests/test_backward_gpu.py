@@ -3,18 +3,19 @@ backward of the prefill core, through the C ABI, against the oracle.
 
 The backward is fed the oracle's forward output (rounded to bf16) and
 log-sum-exp, so the comparison measures the backward alone.  Tolerance (bf16
-operands, fp32 accumulation), per gradient tensor:
-  * relative Frobenius error ||gpu - oracle|| / ||oracle|| at most 1e-2;
-  * every element within 2^-7 |oracle| + 25% of the tensor's RMS + 1e-3.
+operands, fp32 accumulation), per gradient tensor (assert_tensor_close):
+  * relative Frobenius error ||gpu - oracle|| / ||oracle|| at most 1e-2, for
+    the whole tensor and for every token row and every head on its own
+    (dq and dgate by row and by head, dc by row, dW_UK and dW_UV by head);
+  * a slice whose exact value is near zero is measured against half a
+    typical slice's norm instead of its own.
 The chain rounds q_abs, dol, P, dS, c and the stored da / ol to bf16, each at
 most 2^-9 relative, so a term carries about 1% relative error and a long sum
-less.  The bf16 outputs add their own rounding (2^-9 relative, doubled for
-headroom in the first term).  Single elements can sit further from the
-oracle where a gradient is a small difference: in the first positions dS =
-P (dP - D) is a difference of two values near 7 at full width (dP formed from
-bf16 dol, about 0.5% off), against an exact zero at t = 0, which puts dq of
-rows 0-1 at 10-13% of the tensor's RMS; the element bar allows that, and an
-indexing mistake would not pass the Frobenius bar.  The log-sum-exp is
+less.  Where a gradient is a small difference -- in the first positions dS =
+P (dP - D) is a difference of two values near 7 at full width, against an
+exact zero at t = 0 -- the row's own norm is small and the floor applies.
+One wrong head, or a few wrong rows, of a large tensor fail the slice bars
+although they barely move the whole-tensor error.  The log-sum-exp is
 compared at 2e-2 absolute (it is formed from bf16 q_abs).
 """
 import sys
@@ -24,12 +25,11 @@ import pytest
 
 import datagen as dg
 import oracle
-from gpu_util import to_dev, to_host_f64
+from gpu_util import assert_tensor_close, to_dev, to_host_f64
 
 pytestmark = pytest.mark.gpu
 
 SHAPES = {"toy": (16, 16, 32), "mid": (64, 64, 256), "full": (128, 128, 512)}
-FROB_REL, REL_ELEM, RMS_FRAC, ABS_FLOOR = 1e-2, 2.0 ** -7, 0.25, 1e-3
 
 
 def log(msg):
@@ -52,21 +52,21 @@ def gpu():
     return torch
 
 
-def _grad_close(got, ref, what):
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
-    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    frob = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
-    assert frob <= FROB_REL, f"{what}: relative Frobenius error {frob:.3g} > {FROB_REL}"
-    bar = REL_ELEM * np.abs(ref) + RMS_FRAC * rms + ABS_FLOOR
-    err = np.abs(got - ref)
-    if (err > bar).any():
-        idx = np.unravel_index(np.argmax(err), err.shape)
-        raise AssertionError(f"{what}: {(err > bar).sum()} of {err.size} beyond the bar (rms {rms:.3g}); "
-                             f"max err {err.max():.3g} at {idx} (gpu {got[idx]:.5g}, oracle {ref[idx]:.5g})")
-    return float(err.max() / max(rms, 1e-30))
+def core_grad_slices(k: str, shape, H: int):
+    """Rows (token positions) and heads of each gradient of the core."""
+    if k == "dgate":  # [B, T, H*d_v]
+        BT, W = shape[0] * shape[1], shape[2]
+        return [("row", (BT, W), (0,)), ("head", (BT, H, W // H), (1,))]
+    if k == "dq":  # [B, T, H, d_q]
+        BT = shape[0] * shape[1]
+        return [("row", (BT, shape[2] * shape[3]), (0,)), ("head", (BT, shape[2], shape[3]), (1,))]
+    if k == "dc":  # [B, T, r]
+        return [("row", (shape[0] * shape[1], shape[2]), (0,))]
+    return [("head", None, (0,))]  # dw_uk [H, d_q, r], dw_uv [H, d_v, r]
+
+
+def _grad_close(got, ref, what, k, H):
+    return assert_tensor_close(got, ref, what, core_grad_slices(k, np.shape(ref), H))
 
 
 def _case(B, T, H, shape, seed):
@@ -119,7 +119,7 @@ def test_backward_parity(o, B, T, H, shape):
                                         to_dev(ref_lse.astype(np.float32)), to_dev(dout), d["scale"])
     torch.cuda.synchronize()
     for k in ("dgate", "dq", "dc", "dw_uk", "dw_uv"):
-        _grad_close(to_host_f64(g[k]), want[k], f"{k} ({shape} B{B} T{T} H{H})")
+        _grad_close(to_host_f64(g[k]), want[k], f"{k} ({shape} B{B} T{T} H{H})", k, H)
 
 
 def test_backward_workspace_reuse_and_repeat():
@@ -177,7 +177,7 @@ def test_backward_poisoned_workspace(o, B, T, H, shape):
         if T == 1 and k in ("dq", "dw_uk"):
             assert np.all(want[k] == 0.0), f"oracle {k} at T=1 is not zero"
             continue
-        _grad_close(got, want[k], f"{k} ({shape} B{B} T{T} H{H}, poisoned workspace)")
+        _grad_close(got, want[k], f"{k} ({shape} B{B} T{T} H{H}, poisoned workspace)", k, H)
     if T == 1:
         # the query-side noise against the size of dq one position later
         d2, dout2 = _case(B, 2, H, shape, seed=9300 + T + H)

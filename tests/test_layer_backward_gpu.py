@@ -3,8 +3,10 @@ mla_gated_forward_train (whose y must equal mla_gated_forward's bit for
 bit) and mla_gated_backward against the oracle's layer backward.
 
 Tolerance, per gradient tensor, as for the core backward: relative
-Frobenius error at most 1e-2, and every element within 2^-7 |oracle| + 25%
-of the tensor's RMS + 1e-3.  The oracle keeps the forward's stage results
+Frobenius error at most 1e-2 for the whole tensor and for each token row
+(dx), each head (the head-structured weights) or each output feature (the
+down-projections), a near-zero slice being measured against half a typical
+slice's norm.  The oracle keeps the forward's stage results
 in float32 and every gradient in float64; the library stores the stage
 results (the norms' inputs and outputs, q, the gate, the core output) and
 the intermediate gradients (dO, dq, dc, the gate gradient, dql, the norms'
@@ -21,14 +23,13 @@ import pytest
 
 import datagen as dg
 import oracle
-from gpu_util import to_dev, to_host_f64
+from gpu_util import assert_tensor_close, to_dev, to_host_f64
 
 pytestmark = pytest.mark.gpu
 
 WIDTHS = {"toy": dict(D=256, q_rank=64, H=8, d_q=16, d_v=16, r=32),
           "mid": dict(D=1024, q_rank=384, H=32, d_q=64, d_v=64, r=256),
           "full": dict(D=7168, q_rank=1536, H=96, d_q=128, d_v=128, r=512)}
-FROB_REL, REL_ELEM, RMS_FRAC, ABS_FLOOR = 1e-2, 2.0 ** -7, 0.25, 1e-3
 
 
 def log(msg):
@@ -82,21 +83,27 @@ def _train(d, poison=False):
     return y, g
 
 
-def _grad_close(got, ref, what):
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
-    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    frob = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
-    assert frob <= FROB_REL, f"{what}: relative Frobenius error {frob:.3g} > {FROB_REL}"
-    bar = REL_ELEM * np.abs(ref) + RMS_FRAC * rms + ABS_FLOOR
-    err = np.abs(got - ref)
-    if (err > bar).any():
-        idx = np.unravel_index(np.argmax(err), err.shape)
-        raise AssertionError(f"{what}: {(err > bar).sum()} of {err.size} beyond the bar (rms {rms:.3g}); "
-                             f"max err {err.max():.3g} at {idx} (gpu {got[idx]:.5g}, oracle {ref[idx]:.5g})")
-    return frob
+def layer_grad_slices(k: str, shape, w: dict):
+    """Rows, output features or heads of each gradient of the layer."""
+    H, dq, dv = w["H"], w["d_q"], w["d_v"]
+    if k == "dx":  # [B, T, D]
+        return [("row", (shape[0] * shape[1], shape[2]), (0,))]
+    if k in ("dw_uk", "dw_uv"):  # [H, d, r]
+        return [("head", None, (0,))]
+    if k == "dw_q_up":  # [H*d_q, q_rank]
+        return [("head", (H, dq, shape[1]), (0,))]
+    if k == "dw_gate":  # [H*d_v, D]
+        return [("head", (H, dv, shape[1]), (0,))]
+    if k == "dw_o":  # [D, H*d_v]
+        return [("head", (shape[0], H, dv), (1,)), ("row", None, (0,))]
+    if len(shape) == 2:  # dw_kv_down [r, D], dw_q_down [q_rank, D]: per output feature
+        return [("row", None, (0,))]
+    return []  # the norm gains: the whole tensor
+
+
+def _grad_close(got, ref, what, k=None, w=None):
+    slices = layer_grad_slices(k, np.shape(ref), w) if k is not None else ()
+    return assert_tensor_close(got, ref, what, slices)
 
 
 @pytest.mark.parametrize("B,T,width", [(2, 64, "toy"), (1, 130, "mid")])
@@ -124,7 +131,7 @@ def test_layer_backward_parity(o, B, T, width, poison):
     ref = o.forward_backward(*[dg.as_f32(d[k]) for k in dg.FORWARD_KEYS], dg.as_f32(d["dy"]), d["eps"], d["scale"])
     errs = {}
     for k in o.GRAD_KEYS:
-        errs[k] = _grad_close(to_host_f64(g[k]), ref[k], f"{width} B{B} T{T} {k}")
+        errs[k] = _grad_close(to_host_f64(g[k]), ref[k], f"{width} B{B} T{T} {k}", k, WIDTHS[width])
     log("  relative Frobenius errors: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
 
 
@@ -161,7 +168,7 @@ def test_layer_backward_single_position(o):
             assert np.linalg.norm(got) <= 2.0 ** -6 * scale2, \
                 f"{k}: T=1 noise {np.linalg.norm(got):.3g} vs {scale2:.3g}"
         else:
-            _grad_close(to_host_f64(g1[k]), ref1[k], f"T=1 {k}")
+            _grad_close(to_host_f64(g1[k]), ref1[k], f"T=1 {k}", k, WIDTHS["toy"])
 
 
 def test_layer_backward_large_eps(o):
@@ -172,7 +179,7 @@ def test_layer_backward_large_eps(o):
     _, g = _train(d)
     ref = o.forward_backward(*[dg.as_f32(d[k]) for k in dg.FORWARD_KEYS], dg.as_f32(d["dy"]), d["eps"], d["scale"])
     for k in o.GRAD_KEYS:
-        _grad_close(to_host_f64(g[k]), ref[k], f"eps 0.5 {k}")
+        _grad_close(to_host_f64(g[k]), ref[k], f"eps 0.5 {k}", k, WIDTHS["toy"])
 
 
 def test_layer_backward_repeat_is_deterministic():

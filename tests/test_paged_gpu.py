@@ -74,7 +74,7 @@ def test_decode_paged_ragged(o, lens, H, shape, page_size, splits):
     d, lay, pool = _paged_decode_case(lens, H, shape, page_size, seed=8000 + sum(lens) % 997)
     log(f"decode paged {shape} H={H} page {page_size} lens {lens[:6]} splits {splits}")
     got = _run_decode_paged(d, lay, pool, num_splits=splits)
-    assert_parity(got, _oracle_decode_paged(o, d, lay, pool), dg.BF16, "decode paged")
+    assert_parity(got, _oracle_decode_paged(o, d, lay, pool), dg.BF16, "decode paged", block=d["d_v"])
 
 
 def test_decode_paged_matches_packed():
@@ -86,7 +86,7 @@ def test_decode_paged_matches_packed():
     d, lay, pool = _paged_decode_case([3000, 17, 2048, 999], 96, "full", 64, seed=8100)
     got = _run_decode_paged(d, lay, pool)
     ref = to_host_f64(run_decode(d))
-    assert_parity(got, ref, dg.BF16, "paged vs packed")
+    assert_parity(got, ref, dg.BF16, "paged vs packed", block=d["d_v"])
 
 
 def test_decode_paged_lengths_clamped(o):
@@ -97,7 +97,7 @@ def test_decode_paged_lengths_clamped(o):
     big = np.array([64, cap + 50], dtype=np.int64)
     got = _run_decode_paged(d, lay, pool, lens=big)
     ref = _oracle_decode_paged(o, d, lay, pool, lens=np.minimum(big, cap))
-    assert_parity(got, ref, dg.BF16, "clamped lengths")
+    assert_parity(got, ref, dg.BF16, "clamped lengths", block=d["d_v"])
 
 
 def test_decode_paged_full_workload_sampled(o):
@@ -109,7 +109,7 @@ def test_decode_paged_full_workload_sampled(o):
     log(f"decode paged full workload: {int(d['cu_seqlens'][-1])} rows in {lay['num_pages']} pages")
     got = _run_decode_paged(d, lay, pool)
     seqs = np.array([0, 1, 17, 31, 40, 63])
-    assert_parity(got[seqs], _oracle_decode_paged(o, d, lay, pool, seqs=seqs), dg.BF16, "decode paged full")
+    assert_parity(got[seqs], _oracle_decode_paged(o, d, lay, pool, seqs=seqs), dg.BF16, "decode paged full", block=d["d_v"])
 
 
 @pytest.mark.parametrize("B,T,S,H,shape,page_size", [
@@ -135,7 +135,7 @@ def test_extend_paged(o, B, T, S, H, shape, page_size):
     torch.cuda.synchronize()
     f = dg.as_f32
     ref = o.extend_paged(f(q), f(pool), lay["block_table"], S, f(d["w_uk"]), f(d["w_uv"]), f(g), scale)
-    assert_parity(to_host_f64(out), ref, dg.BF16, "extend paged")
+    assert_parity(to_host_f64(out), ref, dg.BF16, "extend paged", block=d["d_v"])
 
 
 def test_cache_append_then_decode(o):
@@ -168,7 +168,7 @@ def test_cache_append_then_decode(o):
     torch.cuda.synchronize()
     ref = o.decode_paged(f(full["q"]), want, lay["block_table"], lens + 1, f(full["w_uk"]), f(full["w_uv"]),
                          f(full["gate"]), 0.125)
-    assert_parity(to_host_f64(out), ref, dg.BF16, "append then decode")
+    assert_parity(to_host_f64(out), ref, dg.BF16, "append then decode", block=full["d_v"])
 
 
 def _high_word_view(buf, arr: np.ndarray, start: int):
@@ -202,7 +202,7 @@ def test_paged_tables_at_high_low_word_addresses(o):
     out = mla.mla_absorb_decode_paged(to_dev(d["q"]), to_dev(pool), bt, lens, to_dev(d["w_uk"]), to_dev(d["w_uv"]),
                                       to_dev(d["gate"]), d["scale"])
     torch.cuda.synchronize()
-    assert_parity(to_host_f64(out), _oracle_decode_paged(o, d, lay, pool), dg.BF16, "high-address tables")
+    assert_parity(to_host_f64(out), _oracle_decode_paged(o, d, lay, pool), dg.BF16, "high-address tables", block=d["d_v"])
     del buf
 
 
@@ -241,7 +241,7 @@ def test_extend_varlen_mixed_batch(o, S, T, H, shape, page_size):
     f = dg.as_f32
     ref = o.extend_varlen_paged(f(v["q"]), f(v["pool"]), v["lay"]["block_table"], v["cu_q"], v["S"], f(v["w_uk"]),
                                 f(v["w_uv"]), f(v["gate"]), v["scale"])
-    assert_parity(to_host_f64(out), ref, dg.BF16, "varlen")
+    assert_parity(to_host_f64(out), ref, dg.BF16, "varlen", block=SHAPES[shape][1])
 
 
 def test_extend_varlen_clamps_bad_ranges(o):
@@ -261,4 +261,4 @@ def test_extend_varlen_clamps_bad_ranges(o):
     f = dg.as_f32
     ref = o.extend_varlen_paged(f(v["q"]), f(v["pool"]), v["lay"]["block_table"], v["cu_q"], v["S"], f(v["w_uk"]),
                                 f(v["w_uv"]), f(v["gate"]), v["scale"])
-    assert_parity(to_host_f64(out)[:30], ref[:30], dg.BF16, "well-formed sequence next to bad ranges")
+    assert_parity(to_host_f64(out)[:30], ref[:30], dg.BF16, "well-formed sequence next to bad ranges", block=64)

@@ -41,7 +41,7 @@ def test_prefill_toy_f32_workload(o):
     d = dg.workload_inputs("toy_f32")
     log(f"prefill toy_f32 B={d['B']} T={d['T']} H={d['H']}")
     got = to_host_f64(run_prefill(d))
-    assert_parity(got, oracle_prefill(o, d), dg.F32, "toy_f32")
+    assert_parity(got, oracle_prefill(o, d), dg.F32, "toy_f32", block=d["d_v"])
 
 
 @pytest.mark.parametrize("B,T,H,shape", [
@@ -55,7 +55,7 @@ def test_prefill_bf16_ragged(o, B, T, H, shape):
     d["scale"] = dq ** -0.5
     log(f"prefill bf16 B={B} T={T} H={H} dq={dq} r={r}")
     got = to_host_f64(run_prefill(d))
-    assert_parity(got, oracle_prefill(o, d), dg.BF16, f"prefill {shape} B{B} T{T} H{H}")
+    assert_parity(got, oracle_prefill(o, d), dg.BF16, f"prefill {shape} B{B} T{T} H{H}", block=d["d_v"])
 
 
 @pytest.mark.parametrize("B,T,H,shape", [(1, 40, 4, "full"), (2, 50, 3, "toy")])
@@ -64,14 +64,14 @@ def test_prefill_f32_other_shapes(o, B, T, H, shape):
     d = dg.prefill_inputs(B, T, H, dq, dv, r, dtype=dg.F32, seed=2000 + T)
     log(f"prefill f32 B={B} T={T} H={H} r={r}")
     got = to_host_f64(run_prefill(d, scale=0.3))
-    assert_parity(got, oracle_prefill(o, d, scale=0.3), dg.F32, f"prefill f32 {shape}")
+    assert_parity(got, oracle_prefill(o, d, scale=0.3), dg.F32, f"prefill f32 {shape}", block=d["d_v"])
 
 
 def test_prefill_toy_max_workload(o):
     d = dg.workload_inputs("toy_max")
     log("prefill toy_max B=4 T=2048 H=8")
     got = to_host_f64(run_prefill(d))
-    assert_parity(got, oracle_prefill(o, d), dg.BF16, "toy_max")
+    assert_parity(got, oracle_prefill(o, d), dg.BF16, "toy_max", block=d["d_v"])
 
 
 def test_prefill_mid_workload_sampled(o):
@@ -79,7 +79,7 @@ def test_prefill_mid_workload_sampled(o):
     log("prefill mid B=4 T=4096 H=32 (sampled rows)")
     got = to_host_f64(run_prefill(d)).reshape(d["B"] * d["T"], -1)
     rows = sample_rows(d["B"], d["T"], 6, seed=5)
-    assert_parity(got[rows], oracle_prefill(o, d, rows=rows), dg.BF16, "mid sampled")
+    assert_parity(got[rows], oracle_prefill(o, d, rows=rows), dg.BF16, "mid sampled", block=d["d_v"])
 
 
 def test_prefill_full_workload_sampled(o):
@@ -87,7 +87,7 @@ def test_prefill_full_workload_sampled(o):
     log("prefill full B=1 T=8192 H=96 (sampled rows)")
     got = to_host_f64(run_prefill(d)).reshape(d["B"] * d["T"], -1)
     rows = sample_rows(d["B"], d["T"], 6, seed=6)
-    assert_parity(got[rows], oracle_prefill(o, d, rows=rows), dg.BF16, "full sampled")
+    assert_parity(got[rows], oracle_prefill(o, d, rows=rows), dg.BF16, "full sampled", block=d["d_v"])
 
 
 def test_prefill_first_position_closed_form():
@@ -99,7 +99,7 @@ def test_prefill_first_position_closed_form():
     wuv = dg.as_f32(d["w_uv"]).astype(np.float64)
     g = dg.as_f32(d["gate"])[:, 0].astype(np.float64)
     ref = np.einsum("bj,hvj->bhv", c0, wuv).reshape(2, -1) / (1 + np.exp(-g))
-    assert_parity(got[:, 0], ref, dg.BF16, "t=0 closed form")
+    assert_parity(got[:, 0], ref, dg.BF16, "t=0 closed form", block=d["d_v"])
 
 
 # ------------------------------------------------------------------ decode
@@ -119,14 +119,14 @@ def test_decode_bf16_ragged(o, lens, H, shape, splits):
     d["scale"] = dq ** -0.5
     log(f"decode bf16 lens={lens} H={H} r={r} splits={splits}")
     got = to_host_f64(run_decode(d, num_splits=splits))
-    assert_parity(got, oracle_decode(o, d), dg.BF16, f"decode {shape} {lens}")
+    assert_parity(got, oracle_decode(o, d), dg.BF16, f"decode {shape} {lens}", block=d["d_v"])
 
 
 def test_decode_f32(o):
     d = dg.decode_inputs(3, 8, 16, 16, 32, dtype=dg.F32, seed=4000, lengths=[9, 1, 130])
     log("decode f32 toy")
     got = to_host_f64(run_decode(d, scale=1.0))
-    assert_parity(got, oracle_decode(o, d, scale=1.0), dg.F32, "decode f32")
+    assert_parity(got, oracle_decode(o, d, scale=1.0), dg.F32, "decode f32", block=d["d_v"])
 
 
 def test_decode_split_count_invariance():
@@ -135,7 +135,7 @@ def test_decode_split_count_invariance():
     log("decode split invariance")
     outs = [to_host_f64(run_decode(d, num_splits=s)) for s in (1, 2, 5, 64, 256)]
     for s, x in zip((2, 5, 64, 256), outs[1:]):
-        assert np.abs(x - outs[0]).max() <= 2e-2, f"splits={s}"
+        assert_parity(x, outs[0], dg.BF16, f"splits={s} vs 1", block=d["d_v"])
 
 
 def test_decode_matches_prefill_last_row():
@@ -154,7 +154,7 @@ def test_decode_matches_prefill_last_row():
     pre = to_host_f64(run_prefill(d))
     dec = to_host_f64(run_decode(dd))
     ref = np.stack([pre[i, lens[i] - 1] for i in range(B)])
-    assert np.abs(dec - ref).max() <= 2e-2
+    assert_parity(dec, ref, dg.BF16, "decode vs prefill last row", block=128)
 
 
 def test_decode_full_workload_sampled(o):
@@ -162,7 +162,7 @@ def test_decode_full_workload_sampled(o):
     log(f"decode full B=64 total={int(d['cu_seqlens'][-1])} (sampled sequences)")
     got = to_host_f64(run_decode(d))
     seqs = np.array([0, 1, int(np.argmin(d["lengths"])), int(np.argmax(d["lengths"])), 31, 63], dtype=np.int64)
-    assert_parity(got[seqs], oracle_decode(o, d, seqs=seqs), dg.BF16, "full decode sampled")
+    assert_parity(got[seqs], oracle_decode(o, d, seqs=seqs), dg.BF16, "full decode sampled", block=d["d_v"])
 
 
 # ------------------------------------------------------------------ edges
@@ -175,7 +175,7 @@ def test_prefill_scale_extremes(o, scale):
     d = dg.prefill_inputs(1, 200, 4, 128, 128, 512, dtype=dg.BF16, seed=5100)
     log(f"prefill full width scale={scale}")
     got = to_host_f64(run_prefill(d, scale=scale))
-    assert_parity(got, oracle_prefill(o, d, scale=scale), dg.BF16, f"prefill scale={scale}")
+    assert_parity(got, oracle_prefill(o, d, scale=scale), dg.BF16, f"prefill scale={scale}", block=d["d_v"])
 
 
 def test_prefill_running_max_rescale():
@@ -190,7 +190,7 @@ def test_prefill_running_max_rescale():
     d["c"] = dg.f32_to_bf16_bits(dg.as_f32(d["c"]) * ramp)
     log("prefill ramped latent (rescale path)")
     got = to_host_f64(run_prefill(d, scale=0.35))
-    assert_parity(got, oracle_prefill(o, d, scale=0.35), dg.BF16, "prefill rescale path")
+    assert_parity(got, oracle_prefill(o, d, scale=0.35), dg.BF16, "prefill rescale path", block=d["d_v"])
 
 
 def test_prefill_long_sequence_sampled(o):
@@ -202,7 +202,7 @@ def test_prefill_long_sequence_sampled(o):
     log(f"prefill long T={T} H=2 (sampled rows)")
     got = to_host_f64(run_prefill(d)).reshape(T, -1)
     rows = np.array([0, 1, 31, 32, 33, 4095, 4096, 9999, 19967, 19968, 19999, 20000], dtype=np.int64)
-    assert_parity(got[rows], oracle_prefill(o, d, rows=rows), dg.BF16, "long prefill sampled")
+    assert_parity(got[rows], oracle_prefill(o, d, rows=rows), dg.BF16, "long prefill sampled", block=d["d_v"])
 
 
 def test_decode_long_sequence(o):
@@ -211,7 +211,7 @@ def test_decode_long_sequence(o):
     d["scale"] = 128 ** -0.5
     log("decode long sequence 150000 + 3 rows")
     got = to_host_f64(run_decode(d))
-    assert_parity(got, oracle_decode(o, d), dg.BF16, "decode long sequence")
+    assert_parity(got, oracle_decode(o, d), dg.BF16, "decode long sequence", block=d["d_v"])
 
 
 def test_side_stream_and_workspace_reuse():
@@ -251,14 +251,14 @@ def test_extend_bf16_ragged(o, B, T, S, H, shape):
     d["scale"] = dq ** -0.5
     log(f"extend bf16 B={B} T={T} S={S} H={H} r={r}")
     got = to_host_f64(run_extend(d, T))
-    assert_parity(got, oracle_extend(o, d, T), dg.BF16, f"extend {shape} B{B} T{T} S{S} H{H}")
+    assert_parity(got, oracle_extend(o, d, T), dg.BF16, f"extend {shape} B{B} T{T} S{S} H{H}", block=d["d_v"])
 
 
 def test_extend_f32(o):
     d = dg.prefill_inputs(2, 61, 3, 16, 16, 32, dtype=dg.F32, seed=6100)
     log("extend f32 toy T=20 S=61")
     got = to_host_f64(run_extend(d, 20, scale=0.7))
-    assert_parity(got, oracle_extend(o, d, 20, scale=0.7), dg.F32, "extend f32")
+    assert_parity(got, oracle_extend(o, d, 20, scale=0.7), dg.F32, "extend f32", block=d["d_v"])
 
 
 def test_extend_without_prefix_is_prefill():
@@ -278,4 +278,4 @@ def test_extend_full_width_sampled(o):
     log(f"extend full width T={T} S={S} H=96 (sampled rows)")
     got = to_host_f64(run_extend(d, T)).reshape(T, -1)
     rows = sample_rows(1, T, 4, seed=7)
-    assert_parity(got[rows], oracle_extend(o, d, T, rows=rows), dg.BF16, "extend full sampled")
+    assert_parity(got[rows], oracle_extend(o, d, T, rows=rows), dg.BF16, "extend full sampled", block=d["d_v"])
