@@ -7,16 +7,23 @@ element with |gpu - oracle| <= 2e-2 (absolute); fp32 with
 
 At the full widths the outputs have an RMS near 0.025, about the size of
 the absolute bar, so the element bar alone would pass a kernel that is a
-few percent off everywhere.  Every comparison therefore also bounds the
-normwise relative error of each output row (the last axis: one (b, t)
-position, or one decode sequence) and, where the caller names the head
-width, of each head's d_v block of a row:
-  ||gpu - oracle||_2 / ||oracle||_2 <= 1e-2 (bf16), 1e-4 (fp32).
+few percent off everywhere.  Every comparison therefore also bounds
+normwise relative errors ||gpu - oracle||_2 / ||oracle||_2:
+  * of each output row (the last axis: one (b, t) position, or one decode
+    sequence): 1e-2 (bf16), 1e-4 (fp32);
+  * where the caller names the head width d_v, of each head over all rows:
+    1e-2 (bf16), 1e-4 (fp32) -- a head scaled 2% off fails here;
+  * and of each head block of each row (d_v elements): 2e-2 (bf16), 1e-4
+    (fp32) -- a wrong head in a single row fails here.
 The bf16 chain rounds q_abs, P and o_lat / l to bf16 (2^-9 relative each)
-and the output itself, which gives normwise errors of a few 1e-3; a head
-scaled 3% off, a wrong row or a dropped term fails the bar.  The achieved
-maximum absolute error and maximum row / head normwise error are printed
-(and appended as JSON lines to the file named by MLA_PARITY_LOG, if set).
+and the output itself.  Measured on the test workloads at the default
+softmax scales: rows at most 0.006, head blocks of 128 elements at most
+0.008; a 16-element head block (the toy widths) is a ratio of two short
+sums and reached 0.016, and at four times the default scale (a peakier
+softmax, see the accuracy regime of the bf16 path) rows reached 0.0084 and
+blocks 0.017.  The achieved maximum absolute error and the maximum row,
+head and block errors are printed (and appended as JSON lines to the file
+named by MLA_PARITY_LOG, if set).
 """
 from __future__ import annotations
 
@@ -26,7 +33,8 @@ import datagen as dg
 
 BF16_ATOL = 2e-2
 F32_RTOL, F32_ATOL = 1e-4, 1e-6
-BF16_NORM_REL = 1e-2   # per row / per head block, normwise
+BF16_NORM_REL = 1e-2   # per row and per head (all rows), normwise
+BF16_BLOCK_REL = 2e-2  # per head block of one row, normwise
 F32_NORM_REL = 1e-4
 
 
@@ -114,27 +122,33 @@ def _normwise(got: np.ndarray, ref: np.ndarray, width: int) -> np.ndarray:
 
 def assert_parity(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, block: int | None = None):
     """Element bar plus the normwise bars per row (last axis) and, with
-    `block` (the head width d_v), per head block of each row."""
+    `block` (the head width d_v), per head over all rows and per head block
+    of each row."""
     assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - ref)
     if dtype == dg.BF16:
         bad = err > BF16_ATOL
         bar = f"atol {BF16_ATOL}"
-        nbar = BF16_NORM_REL
+        nbar, bbar = BF16_NORM_REL, BF16_BLOCK_REL
     else:
         bad = err > F32_RTOL * np.abs(ref) + F32_ATOL
         bar = f"rtol {F32_RTOL} + atol {F32_ATOL}"
-        nbar = F32_NORM_REL
+        nbar = bbar = F32_NORM_REL
     width = got.shape[-1] if got.ndim else 1
     row_rel = _normwise(got, ref, width) if got.size else np.zeros(1)
-    blk_rel = None
+    blk_rel = head_rel = None
     if block is not None and got.size:
         assert width % block == 0, f"{what}: row width {width} is not a multiple of {block}"
         blk_rel = _normwise(got, ref, block)
+        nh = width // block
+        g3 = got.reshape(-1, nh, block).transpose(1, 0, 2).reshape(nh, -1)
+        r3 = ref.reshape(-1, nh, block).transpose(1, 0, 2).reshape(nh, -1)
+        head_rel = _normwise(g3, r3, g3.shape[1])
     stats = dict(what=what, dtype=dtype, elements=int(got.size), max_abs=float(err.max()) if got.size else 0.0,
                  max_row_rel=float(row_rel.max()),
-                 max_head_rel=None if blk_rel is None else float(blk_rel.max()),
+                 max_head_rel=None if head_rel is None else float(head_rel.max()),
+                 max_block_rel=None if blk_rel is None else float(blk_rel.max()),
                  ref_rms=float(np.sqrt(np.mean(ref * ref))) if got.size else 0.0)
     _report(stats)
     if bad.any():
@@ -145,10 +159,13 @@ def assert_parity(got: np.ndarray, ref: np.ndarray, dtype: str, what: str, block
         i = int(np.argmax(row_rel))
         raise AssertionError(f"{what}: row {i} normwise error {row_rel[i]:.3g} > {nbar} "
                              f"({int((row_rel > nbar).sum())} of {row_rel.size} rows)")
-    if blk_rel is not None and blk_rel.max() > nbar:
+    if head_rel is not None and head_rel.max() > nbar:
+        i = int(np.argmax(head_rel))
+        raise AssertionError(f"{what}: head {i} normwise error over all rows {head_rel[i]:.3g} > {nbar}")
+    if blk_rel is not None and blk_rel.max() > bbar:
         i = int(np.argmax(blk_rel))
         raise AssertionError(f"{what}: head block {i} (row {i * block // width}, head {i % (width // block)}) "
-                             f"normwise error {blk_rel[i]:.3g} > {nbar} ({int((blk_rel > nbar).sum())} of "
+                             f"normwise error {blk_rel[i]:.3g} > {bbar} ({int((blk_rel > bbar).sum())} of "
                              f"{blk_rel.size} blocks)")
     return float(err.max()) if got.size else 0.0
 
@@ -189,26 +206,30 @@ def oracle_forward(o, d, rows=None, eps=None, scale=None):
 
 
 # ---------------------------------------------------------------- gradients
-GRAD_FROB_REL = 1e-2   # whole tensor and every slice, normwise
-GRAD_FLOOR = 0.5       # a slice is measured against at least this fraction of a typical slice's norm
+GRAD_FROB_REL = 1e-2   # the whole tensor, normwise
+GRAD_SLICE_REL = 2e-2  # every row / head slice, normwise
+GRAD_FLOOR = 0.5       # slices below this fraction of a typical slice's norm count as near zero
 
 
 def assert_tensor_close(got, ref, what: str, slices=(), frob_rel: float = GRAD_FROB_REL,
-                        floor: float = GRAD_FLOOR) -> float:
+                        slice_rel: float = GRAD_SLICE_REL, floor: float = GRAD_FLOOR,
+                        near_zero: dict | None = None) -> float:
     """Normwise comparison of a computed tensor (a gradient, a recurrent
     state) with the oracle's, as a whole and slice by slice.
 
+    The whole tensor must satisfy ||gpu - oracle|| <= frob_rel ||oracle||.
     `slices` lists (label, shape, axes): the tensors are viewed with `shape`
     (None keeps theirs) and every index combination of `axes` is one slice
-    (e.g. one token row, or one head).  Each slice s must satisfy
-        ||gpu_s - oracle_s|| <= frob_rel * max(||oracle_s||, floor * rms * sqrt(n_s)),
-    rms being the whole tensor's RMS and n_s the slice's element count: a
-    slice as large as a typical one is held to frob_rel of its own norm, and
-    a slice whose exact value is (near) zero -- where a gradient is a small
-    difference, e.g. the first positions' query gradient -- to frob_rel of
-    `floor` typical slices.  A wrong head, a wrong row or a few wrong rows of
-    a large tensor fail here even when the whole-tensor error stays small.
-    Returns the whole-tensor relative error; every figure is printed."""
+    (e.g. one token row, or one head).  With typ = rms * sqrt(n_s) the norm
+    of a typical slice (rms of the whole tensor, n_s elements per slice):
+      * a slice with ||oracle_s|| >= floor * typ must satisfy
+        ||gpu_s - oracle_s|| <= slice_rel * ||oracle_s||;
+      * a smaller one (its exact value is near zero, e.g. where a gradient
+        is a small difference) ||gpu_s - oracle_s|| <= z * typ, with
+        z = near_zero[label] if given, else slice_rel * floor.
+    A wrong head, or a few wrong rows, of a large tensor fail here even when
+    the whole-tensor error stays small.  Returns the whole-tensor relative
+    error; every figure is printed."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, f"{what}: shape {got.shape} vs {ref.shape}"
@@ -226,14 +247,21 @@ def assert_tensor_close(got, ref, what: str, slices=(), frob_rel: float = GRAD_F
         n_s = int(np.prod([g.shape[a] for a in other])) if other else 1
         en = np.sqrt(np.sum((g - r) ** 2, axis=other)).ravel()
         rn = np.sqrt(np.sum(r * r, axis=other)).ravel()
-        den = np.maximum(rn, floor * rms * np.sqrt(n_s))
-        ratio = en / np.where(den > 0, den, 1.0)
-        stats[f"max_{label}_rel"] = float(ratio.max())
-        if ratio.max() > frob_rel:
+        typ = rms * np.sqrt(n_s)
+        z = (near_zero or {}).get(label, slice_rel * floor)
+        small = rn < floor * typ
+        bar = np.where(small, z * typ, slice_rel * rn)
+        # errors in units of each slice's own bar
+        ratio = en / np.where(bar > 0, bar, 1.0)
+        stats[f"max_{label}_rel"] = float(np.max(np.where(small, 0.0, en / np.where(rn > 0, rn, 1.0))))
+        stats[f"max_{label}_small_abs"] = float(np.max(np.where(small, en / max(typ, 1e-300), 0.0)))
+        if ratio.max() > 1.0:
             i = int(np.argmax(ratio))
             idx = np.unravel_index(i, [g.shape[a] for a in axes])
-            fails.append(f"{label} {tuple(int(x) for x in idx)}: normwise error {ratio[i]:.3g} > {frob_rel} "
-                         f"({int((ratio > frob_rel).sum())} of {ratio.size} {label}s)")
+            kind = (f"error {en[i] / max(typ, 1e-300):.3g} of a typical slice > {z}" if small[i]
+                    else f"normwise error {en[i] / rn[i]:.3g} > {slice_rel}")
+            fails.append(f"{label} {tuple(int(x) for x in idx)}: {kind} "
+                         f"({int((ratio > 1).sum())} of {ratio.size} {label}s)")
     _report(stats)
     assert not fails, f"{what}: " + "; ".join(fails)
     return frob

@@ -3,13 +3,13 @@ oracle's step-by-step recurrence, float64.
 
 Tolerance, per output tensor (o, and the final state when asked for), with
 the structure of the backward tests (assert_tensor_close): relative
-Frobenius error at most 1e-2 for the whole tensor and for every token row
-and every value head of o (every (batch, value head) of a state), a slice
-whose exact value is near zero being measured against half a typical
-slice's norm.  The chunked evaluation rounds its per-chunk operands (the
+Frobenius error at most 1e-2 for the whole tensor and at most 2e-2 for
+every token row and every value head of o (every (batch, value head) of a
+state), a slice whose exact norm is below half a typical slice's being held
+to 1% of a typical slice's norm instead.  The chunked evaluation rounds its per-chunk operands (the
 decayed q and key factors, W, U, the in-chunk read-out matrix, S and the
 residuals R) to bf16, 2^-9 relative each, and accumulates in fp32: measured,
-the relative Frobenius error is about 4e-3.  A wrong row, chunk or head
+the relative Frobenius error is about 4e-3 and single rows reach 9e-3.  A wrong row, chunk or head
 fails its slice bar even where the whole-tensor error would stay small; a
 dropped term, a wrong decay or a transposed operand fails every bar.
 """
