@@ -36,7 +36,9 @@
  *    reported by the HIP runtime returns MLA_ERR_HIP.
  *  - Inputs are read only.  `out` must not alias any input or the workspace.
  *  - Calls may run concurrently on different streams with distinct
- *    workspaces; the library holds no mutable global state.
+ *    workspaces.  The only global state is the scratch buffer of
+ *    mla_absorb_decode_noalloc (one per GPU) and the cached device address
+ *    of it, resolved once per device under a lock.
  *
  * Supported element types: MLA_DTYPE_BF16 (bf16 storage, fp32 accumulation,
  * MFMA kernels; (d_q, d_v, r) in {(16,16,32), (64,64,256), (128,128,512)}) and
@@ -157,6 +159,32 @@ mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* 
                              int B, int H, int d_q, int d_v, int r, int64_t total_len, float scale,
                              int num_splits, mla_dtype dtype, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* Bytes of the per-GPU static scratch buffer of mla_absorb_decode_noalloc. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * mla_absorb_decode (same arguments, kernels and result), but its scratch
+ * (q_abs and the split partials) lives in a static device buffer of
+ * MLA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on,
+ * from the first call on that device until the process ends.  The call
+ * allocates and frees nothing.  Sizes whose scratch exceeds the buffer
+ * (mla_absorb_decode_workspace_size(B, H, d_q, r, num_splits, dtype) >
+ * MLA_NOALLOC_SCRATCH_BYTES; e.g. B = 128 sequences at H = 96, r = 512 and
+ * the default 256 splits need 48.3 MiB) return MLA_ERR_WORKSPACE before
+ * anything is launched.  Every call on one GPU shares that GPU's buffer:
+ * calls that overlap on one GPU (different streams, or different host
+ * threads) race and give undefined results; serialise them.  Nothing in the
+ * buffer needs to start at zero: each call writes every scratch byte it
+ * reads.  Errors otherwise as for mla_absorb_decode; MLA_ERR_HIP also if the
+ * buffer's address cannot be resolved on the current device.
+ */
+mla_status mla_absorb_decode_noalloc(const void* q, const void* c_cache, const int32_t* cu_seqlens,
+                                     const void* w_uk, const void* w_uv, const void* gate, void* out,
+                                     int B, int H, int d_q, int d_v, int r, int64_t total_len, float scale,
+                                     int num_splits, mla_dtype dtype, void* stream);
 
 /*
  * Paged latent cache (the pages cache only c, page "Gated MLA（矩阵吸收版）",

@@ -18,6 +18,7 @@ __all__ = [
     "MLA_ERR_HIP", "DTYPE_F32", "DTYPE_BF16", "MLAError", "lib", "status_string",
     "prefill_workspace_size", "workspace_size", "decode_workspace_size", "decode_paged_workspace_size", "forward_workspace_size",
     "mla_absorb_prefill", "mla_absorb_extend", "mla_absorb_extend_paged", "mla_absorb_decode",
+    "mla_absorb_decode_noalloc",
     "mla_absorb_decode_paged", "mla_cache_append_paged", "mla_gated_forward", "mla_absorb_prefill_train",
     "backward_workspace_size", "mla_absorb_prefill_backward", "varlen_workspace_size",
     "mla_absorb_extend_varlen_paged", "train_state_size", "mla_gated_forward_train",
@@ -38,6 +39,7 @@ EXPORTS = (
     "mla_absorb_extend",
     "mla_absorb_decode_workspace_size",
     "mla_absorb_decode",
+    "mla_absorb_decode_noalloc",
     "mla_absorb_extend_paged",
     "mla_absorb_extend_varlen_workspace_size",
     "mla_absorb_extend_varlen_paged",
@@ -88,6 +90,8 @@ def lib() -> ct.CDLL:
         L.mla_absorb_decode_workspace_size.restype = sz
         L.mla_absorb_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, I64, F, I, I, vp, sz, vp]
         L.mla_absorb_decode.restype = I
+        L.mla_absorb_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, I, I, I, I, I, I64, F, I, I, vp]
+        L.mla_absorb_decode_noalloc.restype = I
         L.mla_absorb_extend_paged.argtypes = [vp] * 7 + [I] * 7 + [I64, I, I, F, I, vp, sz, vp]
         L.mla_absorb_extend_paged.restype = I
         L.mla_absorb_extend_varlen_workspace_size.argtypes = [I] * 6
@@ -317,6 +321,32 @@ def mla_absorb_decode(q, c_cache, cu_seqlens, w_uk, w_uv, gate, scale: float, nu
                                  workspace.numel() * workspace.element_size(), _stream(stream))
     if st != MLA_OK:
         raise MLAError(st, "mla_absorb_decode")
+    return out
+
+
+def mla_absorb_decode_noalloc(q, c_cache, cu_seqlens, w_uk, w_uv, gate, scale: float, num_splits: int = 0,
+                              out=None, stream=None):
+    """mla_absorb_decode with its scratch in the library's static per-GPU
+    buffer (no workspace argument; the C call allocates nothing).  Passing
+    `out` keeps this wrapper allocation-free as well."""
+    torch = _torch()
+    B, H, dq = q.shape
+    N, r = c_cache.shape
+    dv = w_uv.shape[1]
+    dt = q.dtype
+    code = _dtype_code(q)
+    for t, shp, n in ((q, (B, H, dq), "q"), (c_cache, (N, r), "c_cache"), (w_uk, (H, dq, r), "w_uk"),
+                      (w_uv, (H, dv, r), "w_uv"), (gate, (B, H * dv), "gate")):
+        _check(t, shp, dt, n)
+    _check(cu_seqlens, (B + 1,), torch.int32, "cu_seqlens")
+    if out is None:
+        out = torch.empty((B, H * dv), dtype=dt, device=q.device)
+    _check(out, (B, H * dv), dt, "out")
+    st = lib().mla_absorb_decode_noalloc(q.data_ptr(), c_cache.data_ptr(), cu_seqlens.data_ptr(), w_uk.data_ptr(),
+                                         w_uv.data_ptr(), gate.data_ptr(), out.data_ptr(), B, H, dq, dv, r, N,
+                                         float(scale), int(num_splits), code, _stream(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_absorb_decode_noalloc")
     return out
 
 

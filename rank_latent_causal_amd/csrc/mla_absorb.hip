@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "common.h"
 #include "backward_bf16.h"
@@ -15,6 +16,13 @@
 #include "gemm_bf16.h"
 #include "layer_backward_bf16.h"
 #include "prefill_bf16.h"
+
+// Scratch of mla_absorb_decode_noalloc: one static device buffer per GPU
+// (each device that loads this code object holds its own copy at its own
+// address until the process ends).  Its host-side name is not a device
+// address: host code only ever uses the pointer hipGetSymbolAddress returns
+// for the current device, resolved once per device and kept below.
+static __device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -50,6 +58,24 @@ int device_cu_count() {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   return n;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, null until resolved
+
+// The scratch buffer's device address on the current device.
+mla_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
 }
 
 struct DecodeLayout {
@@ -567,11 +593,13 @@ size_t mla_absorb_decode_workspace_size(int B, int H, int d_q, int r, int num_sp
   return decode_layout(B, H, r, G).total;
 }
 
-mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* cu_seqlens,
-                             const void* w_uk, const void* w_uv, const void* gate, void* out,
-                             int B, int H, int d_q, int d_v, int r, int64_t total_len, float scale,
-                             int num_splits, mla_dtype dtype, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+// Decode over a packed cache with the scratch in the caller's workspace, or
+// (noalloc) in the library's static scratch buffer of the current device.
+static mla_status decode_impl(const void* q, const void* c_cache, const int32_t* cu_seqlens,
+                              const void* w_uk, const void* w_uv, const void* gate, void* out,
+                              int B, int H, int d_q, int d_v, int r, int64_t total_len, float scale,
+                              int num_splits, mla_dtype dtype, void* workspace,
+                              size_t workspace_bytes, void* stream, bool noalloc) {
   if (!q || !c_cache || !cu_seqlens || !w_uk || !w_uv || !gate || !out) return MLA_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || d_q <= 0 || d_v <= 0 || r <= 0 || total_len < B) return MLA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return MLA_ERR_INVALID_ARG;
@@ -600,6 +628,12 @@ mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* 
   int G = num_splits > 0 ? num_splits : device_cu_count();
   if (G <= 0) return MLA_ERR_HIP;
   const size_t need = decode_layout(B, H, r, G).total;
+  if (noalloc) {
+    if (need > MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+    const mla_status st = scratch_for_current_device(&workspace);
+    if (st != MLA_OK) return st;
+    workspace_bytes = MLA_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
   if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
   // every range must own at least one cache row (the merge relies on it)
@@ -622,6 +656,23 @@ mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* 
   else if (d_q == 64) launch_decode_bf16<64, 64, 256>(aa, sa, ma, s);
   else launch_decode_bf16<128, 128, 512>(aa, sa, ma, s);
   return launch_status();
+}
+
+mla_status mla_absorb_decode(const void* q, const void* c_cache, const int32_t* cu_seqlens,
+                             const void* w_uk, const void* w_uv, const void* gate, void* out,
+                             int B, int H, int d_q, int d_v, int r, int64_t total_len, float scale,
+                             int num_splits, mla_dtype dtype, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return decode_impl(q, c_cache, cu_seqlens, w_uk, w_uv, gate, out, B, H, d_q, d_v, r, total_len, scale,
+                     num_splits, dtype, workspace, workspace_bytes, stream, false);
+}
+
+mla_status mla_absorb_decode_noalloc(const void* q, const void* c_cache, const int32_t* cu_seqlens,
+                                     const void* w_uk, const void* w_uv, const void* gate, void* out,
+                                     int B, int H, int d_q, int d_v, int r, int64_t total_len, float scale,
+                                     int num_splits, mla_dtype dtype, void* stream) {
+  return decode_impl(q, c_cache, cu_seqlens, w_uk, w_uv, gate, out, B, H, d_q, d_v, r, total_len, scale,
+                     num_splits, dtype, nullptr, 0, stream, true);
 }
 
 size_t mla_absorb_decode_paged_workspace_size(int B, int H, int d_q, int r, int num_splits, mla_dtype dtype) {

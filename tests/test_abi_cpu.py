@@ -430,3 +430,36 @@ def _kda(**kw):
 ])
 def test_kda_rejects(kw, status):
     assert _kda(**kw) == status
+
+
+def _decode_noalloc(**kw):
+    a = dict(q=FAKE, c=FAKE, cu=FAKE, w_uk=FAKE, w_uv=FAKE, gate=FAKE, out=FAKE, B=2, H=4, dq=128, dv=128,
+             r=512, N=100, scale=0.1, splits=8, dtype=mla.DTYPE_BF16, stream=None)
+    a.update(kw)
+    return mla.lib().mla_absorb_decode_noalloc(a["q"], a["c"], a["cu"], a["w_uk"], a["w_uv"], a["gate"], a["out"],
+                                               a["B"], a["H"], a["dq"], a["dv"], a["r"], a["N"], a["scale"],
+                                               a["splits"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), mla.MLA_ERR_INVALID_ARG),
+    (dict(c=FAKE + 8), mla.MLA_ERR_INVALID_ARG),
+    (dict(N=1), mla.MLA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mla.MLA_ERR_INVALID_ARG),
+    (dict(dq=96, dv=96, r=384), mla.MLA_ERR_UNSUPPORTED),
+    # scratch beyond the static buffer: rejected before the buffer is looked up
+    (dict(B=300, H=96, N=1000, splits=256), mla.MLA_ERR_WORKSPACE),
+    (dict(B=2, H=96, N=1000, splits=1 << 20), mla.MLA_ERR_WORKSPACE),
+])
+def test_decode_noalloc_rejects(kw, status):
+    assert _decode_noalloc(**kw) == status
+
+
+def test_decode_noalloc_limit_matches_workspace_size():
+    """The largest default-split batch the static buffer serves at full width
+    is the one whose explicit workspace still fits in it."""
+    limit = 64 << 20
+    fits = [B for B in range(1, 400) if mla.decode_workspace_size(B, 96, 128, 512, 256, mla.DTYPE_BF16) <= limit]
+    assert fits and max(fits) >= 128
+    B = max(fits) + 1
+    assert _decode_noalloc(B=B, H=96, N=10 * B, splits=256) == mla.MLA_ERR_WORKSPACE
