@@ -43,7 +43,7 @@ constexpr int copies_per_wave(int nwaves) {
 // count, so a lane's byte offset is a fixed per-lane base XOR a wave-uniform
 // constant (swizzle term and row offset occupy disjoint bits): one VALU op
 // per copy.
-template <int R, int NW>
+template <int R, int NW, int SW = 0>
 struct TileCopier {
   static constexpr int COPIES = LatentTile<R>::COPIES;
   static constexpr int CPW = copies_per_wave<R>(NW);
@@ -64,7 +64,7 @@ struct TileCopier {
     unsigned ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
     const unsigned sl = ln / CPR;
-    return (sl * R + (((ln % CPR) ^ (unsigned)chunk_swizzle<R>((int)sl)) * 8)) * 2;
+    return (sl * R + (((ln % CPR) ^ (unsigned)tile_swizzle<R, SW>((int)sl)) * 8)) * 2;
   }
 
   // A tile's descriptor and this wave's copy offsets, formed once; the
@@ -97,9 +97,19 @@ struct TileCopier {
       const int qi = w + NW * c;
       if (COPIES % NW == 0 || qi < COPIES) {
         const int srow = qi * RPI;
-        const unsigned k = (unsigned)((chunk_swizzle<R>(srow) << 4) | (srow * R * 2));
+        const unsigned k = (unsigned)((tile_swizzle<R, SW>(srow) << 4) | (srow * R * 2));
         buf2lds16(p.rs, p.lb ^ k, p.stage + qi * 1024);
       }
+    }
+  }
+
+  // Copy c alone (c < CPW; a constant once the caller is unrolled).
+  __device__ __forceinline__ void issue_one(const Pending& p, int c) const {
+    const int qi = w + NW * c;
+    if (COPIES % NW == 0 || qi < COPIES) {
+      const int srow = qi * RPI;
+      const unsigned k = (unsigned)((tile_swizzle<R, SW>(srow) << 4) | (srow * R * 2));
+      buf2lds16(p.rs, p.lb ^ k, p.stage + qi * 1024);
     }
   }
 

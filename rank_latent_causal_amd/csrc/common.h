@@ -45,6 +45,33 @@ __device__ __host__ __forceinline__ constexpr int chunk_swizzle(int s) {
   }
 }
 
+// The chunk swizzle of the single-wave prefill tiles (32x32x16 operands):
+// row bits 0-1 and 2-3 exchanged, f(4a + e) = 4e + a, applied to the low 4
+// bits of the chunk index.  Bank-conflict free for
+//  * ds_read_b128 of one chunk from 16 consecutive rows (score operand), and
+//  * ds_read_b64_tr_b16 where each 32-lane half reads 4 consecutive rows x
+//    4 consecutive chunks (value operand: f's high bits differ across the 4
+//    rows, the chunk's low bits across the 4 chunks).
+// (chunk_swizzle maps such a 4 x 4 block onto 8 bank groups only.)
+template <int R>
+__device__ __host__ __forceinline__ constexpr int chunk_swizzle_x(int s) {
+  if constexpr (R / 8 >= 16) {
+    return ((s & 3) << 2) | ((s >> 2) & 3);
+  } else {
+    return 0;
+  }
+}
+
+// SW = 0: chunk_swizzle, SW = 1: chunk_swizzle_x.
+template <int R, int SW>
+__device__ __host__ __forceinline__ constexpr int tile_swizzle(int s) {
+  if constexpr (SW == 1) {
+    return chunk_swizzle_x<R>(s);
+  } else {
+    return chunk_swizzle<R>(s);
+  }
+}
+
 // Byte offset of (row s, logical 16-byte chunk L) in a swizzled tile.
 template <int R>
 __device__ __forceinline__ int tile_off(int s, int L) {

@@ -91,9 +91,11 @@ __global__ void __launch_bounds__(256) mla_varlen_prepare(const int* __restrict_
 
 // Issues the copies of key tile j (rows 32j .. 32j+31 of sequence b) into an
 // LDS stage: from the contiguous latent [B, S, R], or through the block table.
-template <bool PAGED, int R, int NW>
-__device__ __forceinline__ void issue_key_tile(const TileCopier<R, NW>& copier, const PrefillArgs& a, int b, int S,
-                                               int j, MLA_LDS char* stage) {
+// prepare_key_tile forms the descriptor and offsets only; the copies then go
+// out with copier.issue_range.
+template <bool PAGED, int R, int NW, int SW>
+__device__ __forceinline__ typename TileCopier<R, NW, SW>::Pending prepare_key_tile(
+    const TileCopier<R, NW, SW>& copier, const PrefillArgs& a, int b, int S, int j, MLA_LDS char* stage) {
   constexpr int KT = LatentTile<R>::KT;
   if constexpr (PAGED) {
     const int pos = j * KT;
@@ -104,10 +106,16 @@ __device__ __forceinline__ void issue_key_tile(const TileCopier<R, NW>& copier, 
       valid = 0;
     }
     const size_t row = ((size_t)pg << a.page_shift) + (pos & ((1 << a.page_shift) - 1));
-    copier.issue(a.c + row * R, 0, valid, stage);
+    return copier.prepare(a.c + row * R, 0, valid, stage);
   } else {
-    copier.issue(a.c + (size_t)b * S * R, j * KT, S, stage);
+    return copier.prepare(a.c + (size_t)b * S * R, j * KT, S, stage);
   }
+}
+
+template <bool PAGED, int R, int NW, int SW>
+__device__ __forceinline__ void issue_key_tile(const TileCopier<R, NW, SW>& copier, const PrefillArgs& a, int b, int S,
+                                               int j, MLA_LDS char* stage) {
+  copier.template issue_range<0, TileCopier<R, NW, SW>::CPW>(prepare_key_tile<PAGED>(copier, a, b, S, j, stage));
 }
 
 // waves per workgroup: 4 heads x (kPrefillWaves / 4) blocks of 16 positions

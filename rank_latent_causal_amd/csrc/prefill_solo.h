@@ -1,0 +1,526 @@
+// Single-wave-per-SIMD bf16 prefill for the absorbed Gated MLA layer (r >= 256)
+// on gfx950.
+//
+// One workgroup = 4 waves = 32 query positions x 4 heads; each wave owns one
+// head's 32 positions over the WHOLE latent width r, so the score of page
+// "Gated MLA（矩阵吸收版）", section 完整计算流（四步） step 2 is complete
+// inside the wave: no partial scores are exchanged.  Per 32-key tile of c the
+// wave runs, on v_mfma_f32_32x32x16_bf16 (transposed products, each lane owns
+// one query column):
+//   S^T  = c_tile . q_abs^T          32x32 fp32 (VGPRs)
+//   P    = exp2(S - m), online softmax (lanes l and l^32 share a column)
+//   O^T += c_tile^T . P^T             [r x 32] fp32 (accumulation registers)
+// The accumulator O^T takes r/2 = 256 registers per lane at r = 512, so the
+// kernel runs one wave per SIMD with the accumulation register file for O^T
+// and the architectural file for q_abs^T (r/4 registers) and the pipeline.
+// With a single wave per SIMD, latency is hidden inside the wave: the score
+// products of tile i+1 are issued under the softmax of tile i and between the
+// value products of tile i, so the matrix pipe has independent work while the
+// softmax arithmetic and the LDS reads are in flight.
+// Every c tile is copied once per workgroup into LDS (LDS-DMA, four stages,
+// two tiles of lookahead) and read by the four heads.
+#pragma once
+
+#include <type_traits>
+
+#include "prefill_bf16.h"
+
+namespace mla {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// v_mfma_f32_32x32x16_bf16: D = A * B + C.  Lane l holds A row (l % 32),
+// k = 8 (l / 32) + 0..7; B column (l % 32) with the same k; C/D column
+// (l % 32), register i at row 8 (i / 4) + 4 (l / 32) + i % 4.
+//
+// Every product of this kernel is issued from inline assembly, with the
+// accumulator's register file fixed by the constraint: O^T in accumulation
+// registers ("a"), the score, absorb and epilogue chains in VGPRs ("v").
+// Through the builtin, the compiler selects the accumulation-register form
+// for every MFMA of a one-wave-per-SIMD kernel, so the score accumulator
+// competes with the 256 registers of O^T, and its allocator then spills O^T
+// at every loop header.  The compiler does not see these MFMAs, so the code
+// around them keeps each hazard explicit:
+//  * a chain starts with the zero-accumulator form (no write of the
+//    accumulator precedes it) or follows settle_*() after a VALU write;
+//  * chained products accumulate into the exact same registers, which the
+//    hardware forwards without wait states;
+//  * a result is read by VALU or memory instructions only after settle_*()
+//    (24 wait states, above what an XDL write followed by a read needs);
+//  * an operand written by a VALU instruction is pinned right after it is
+//    formed (an empty asm that takes it as an in-out operand, so the compiler
+//    cannot sink its computation towards the product) and separated from
+//    its product by operand_gap() (2 wait states); operands loaded from
+//    memory are ordered by the lgkmcnt / vmcnt waits the compiler puts
+//    before the asm.
+__device__ __forceinline__ void mfma32v_first(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32v(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32a(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void settle_v(f32x16& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
+}
+__device__ __forceinline__ void wait_states_24() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+__device__ __forceinline__ void operand_gap() { asm volatile("s_nop 1" ::: "memory"); }
+// Pins an accumulator in its accumulation registers at this point of the
+// instruction stream (orders compiler reads and writes of it against the
+// volatile asm around).
+__device__ __forceinline__ void pin_a(f32x16& c) { asm volatile("" : "+a"(c)); }
+
+// c = 0 in accumulation registers, as the product of zero operands: every
+// block is then a value of its own (one shared zero constant would stay live
+// beside O^T), and the value products that follow read it as their
+// accumulator straight from the matrix pipe.
+__device__ __forceinline__ void zero_a(f32x16& c, const bf16x8& z) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=&a"(c) : "v"(z));
+}
+
+// c *= alpha on accumulation registers, element by element in assembly so
+// the accumulator never becomes a VGPR value (a compiler multiply would copy
+// all of O^T through VGPRs and break its allocation).
+__device__ __forceinline__ void scale_acc(f32x16& c, float alpha) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(c[k]), "=&v"(tmp)
+                 : "v"(alpha));
+  }
+}
+
+// 8 fp32 values (scaled) -> bf16 MFMA operand, round-to-nearest-even.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base, float s) {
+  bf16x8 r;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) r[p] = (bf16)(v[base + p] * s);
+  return r;
+}
+
+constexpr int kSoloWaves = 4;
+constexpr int kSoloStages = 4;
+constexpr int kSoloRows = 32;  // query positions per workgroup
+constexpr int kSoloScoreLookahead = 2;
+constexpr int kSoloValueLookahead = 2;
+
+template <int R>
+struct SoloAttn {
+  static constexpr int NKK = R / 16;  // score k-blocks (16 latent dims)
+  static constexpr int NLB = R / 32;  // 32-dim latent blocks of O^T
+  static constexpr int ROWB = R * 2;
+  static_assert(R / 8 >= 16 && R % 128 == 0, "solo layout needs r >= 256");
+
+  // Operand addresses inside a tile (XOR chunk swizzle folded in):
+  //  * score operand of k-block kk: key row l % 32, chunk 2kk + l / 32, at
+  //    qb[kk & 7] + 256 (kk >> 3);
+  //  * value operand of latent block t, key block kb (keys 16kb + ...), two
+  //    transposing reads: rows 16kb + 4 (l / 32) + e (+ 8), chunk
+  //    4t + 2 ((l / 16) & 1) + (l % 4) / 2, at vb[4j + (t & 3)] + 256 (t >> 2)
+  //    + 16 ROWB kb.
+  int qb[8], vb[8];
+
+  __device__ __forceinline__ void init_addressing(int lane) {
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int xs = chunk_swizzle_x<R>(l32);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) qb[u] = l32 * ROWB + (((2 * u + hh) ^ xs) << 4);
+    const int g = lane >> 4, i = lane & 15, e = i >> 2, q = i & 3;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = 4 * (g >> 1) + e + 8 * j;
+      const int xr = chunk_swizzle_x<R>(row);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vb[4 * j + u] = row * ROWB + (((4 * u + 2 * (g & 1) + (q >> 1)) ^ xr) << 4) + (q & 1) * 8;
+    }
+  }
+
+  __device__ __forceinline__ bf16x8 score_operand(const MLA_LDS char* tile, int kk) const {
+    return lds_read_b128(tile + qb[kk & 7] + 256 * (kk >> 3));
+  }
+  __device__ __forceinline__ bf16x8 value_operand(const MLA_LDS char* tile, int n) const {
+    // n = 2t + kb
+    const int t = n >> 1, kb = n & 1;
+    const MLA_LDS char* p = tile + 256 * (t >> 2) + 16 * ROWB * kb;
+    return cat4(lds_read_tr16(p + vb[t & 3]), lds_read_tr16(p + vb[4 + (t & 3)]));
+  }
+};
+
+// q_abs^T for 32 rows (one head): qT[kk] is the score B operand for k-block
+// kk (lane column l % 32, latent dims 16kk + 8 (l / 32) + 0..7), scaled by
+// qscale.  The A operand row rho of the 32-dim block loads latent dim
+// perm(rho) (bits 2 and 3 swapped) so that C registers 0-7 / 8-15 of a lane
+// are exactly the 8 consecutive dims of k-blocks 2blk / 2blk + 1.
+template <int DQ, int R, typename AfterFirstLoads>
+__device__ __forceinline__ void absorb_solo(const bf16* __restrict__ qrow, const bf16* __restrict__ wkT,
+                                            float qscale, int lane, bf16x8 (&qT)[R / 16],
+                                            AfterFirstLoads&& after_first_loads) {
+  constexpr int NKS = DQ / 16;
+  constexpr int NB = R / 32;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int prow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+  // The products are volatile assembly, which the compiler does not move
+  // memory accesses across, so the loads are placed by hand: the W_UK^T
+  // operands run two 32-row blocks ahead of their products.
+  bf16x8 qb[NKS], wa[2][NKS];
+  auto load_block = [&](int blk, bf16x8(&wv)[NKS]) {
+    const bf16* wrow = wkT + (size_t)(32 * blk + prow) * DQ + 8 * hh;
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) wv[k] = *(const bf16x8*)(wrow + 16 * k);
+  };
+#pragma unroll
+  for (int k = 0; k < NKS; ++k) qb[k] = *(const bf16x8*)(qrow + 16 * k + 8 * hh);
+  load_block(0, wa[0]);
+  if constexpr (NB > 1) load_block(1, wa[1]);
+  after_first_loads();
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    f32x16 acc;
+    mfma32v_first(acc, wa[blk & 1][0], qb[0]);
+#pragma unroll
+    for (int k = 1; k < NKS; ++k) mfma32v(acc, wa[blk & 1][k], qb[k]);
+    if (blk + 2 < NB) load_block(blk + 2, wa[blk & 1]);
+    settle_v(acc);
+    qT[2 * blk] = pack8(acc, 0, qscale);
+    qT[2 * blk + 1] = pack8(acc, 8, qscale);
+    // materialise the packed operands here: left to itself the compiler sinks
+    // the scale-and-pack to the first use and keeps all R fp32 values live
+    asm volatile("" : "+v"(qT[2 * blk]), "+v"(qT[2 * blk + 1]));
+  }
+}
+
+template <int DQ, int DV, int R, bool PAGED = false, bool VARLEN = false>
+__global__ void __launch_bounds__(64 * kSoloWaves)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+mla_prefill_solo_kernel(PrefillArgs a) {
+  using LT = LatentTile<R>;
+  using SA = SoloAttn<R>;
+  constexpr int NS = kSoloStages;
+  constexpr int NW = kSoloWaves;
+  constexpr int CPW = copies_per_wave<R>(NW);
+  constexpr int NKK = SA::NKK, NLB = SA::NLB;
+  constexpr int EPK = 16 / (NKK / 2);  // exponentials per phase-A product
+  // products of lookahead for the LDS operand reads (score / value)
+  constexpr int SPF = kSoloScoreLookahead, VPF = kSoloValueLookahead;
+  static_assert(LT::COPIES % NW == 0, "copy split");
+  static_assert(DQ % 16 == 0 && DV % 32 == 0, "shape");
+  static_assert(NS >= 3 && NS <= 5 && CPW * (NS - 2) < 64, "stages and vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * LT::BYTES];
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+
+  // ---- work item (32 positions x 4 heads), heaviest query blocks first
+  const int x = blockIdx.x;
+  int tb, b, hg;
+  if constexpr (VARLEN) {
+    hg = x % a.nhg;
+    const int i = x / a.nhg;
+    if (i >= __builtin_amdgcn_readfirstlane(*a.nblocks)) return;  // the whole workgroup
+    const int2 e = a.blocks[i];
+    b = __builtin_amdgcn_readfirstlane(e.x);
+    tb = __builtin_amdgcn_readfirstlane(e.y);
+  } else if (a.xcd_remap) {
+    // gridDim.x = 8 * per; XCD x % 8 owns head groups hg = x % 8 (mod 8)
+    const int xcd = x & 7, pos = x >> 3, nh8 = a.nhg >> 3;
+    hg = (pos % nh8) * 8 + xcd;
+    const int rest = pos / nh8;
+    b = rest % a.B;
+    tb = a.ntb - 1 - rest / a.B;
+  } else {
+    hg = x % a.nhg;
+    const int rest = x / a.nhg;
+    b = rest % a.B;
+    tb = a.ntb - 1 - rest / a.B;
+  }
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int h = hg * NW + w;
+  const bool hvalid = h < a.H;
+  const int hc = hvalid ? h : a.H - 1;
+  const int H = a.H;
+  int T = a.T, S = a.S;
+  size_t qr0 = (size_t)b * a.T;  // packed row of query 0 of sequence b
+  if constexpr (VARLEN) {
+    const int4 sq = a.seq[b];
+    qr0 = (size_t)__builtin_amdgcn_readfirstlane(sq.x);
+    T = __builtin_amdgcn_readfirstlane(sq.y);
+    S = __builtin_amdgcn_readfirstlane(sq.z);
+  }
+  const int t0 = tb * kSoloRows;
+  const int t = t0 + l32;  // this lane's query column
+  const bool tvalid = t < T;
+  const int P = S - T;  // query t sits at position P + t
+  const int ntiles = (P + min(t0 + kSoloRows, T) + LT::KT - 1) / LT::KT;
+
+  TileCopier<R, NW, 1> copier;
+  copier.init(w, lane);
+
+  // absorb; the first latent tiles are copied once the first operand blocks
+  // of the absorb are requested (their vmcnt waits then do not include them)
+  bf16x8 qT[NKK];
+  absorb_solo<DQ, R>(a.q + ((qr0 + (tvalid ? t : T - 1)) * H + hc) * DQ, a.wukT + (size_t)hc * R * DQ, a.qscale,
+                     lane, qT, [&]() {
+#pragma unroll
+                       for (int p = 0; p < NS - 1; ++p)
+                         if (p < ntiles) issue_key_tile<PAGED>(copier, a, b, S, p, smem + p * LT::BYTES);
+                     });
+  SA sa;
+  sa.init_addressing(lane);
+
+  f32x16 oT[NLB];
+  {
+    bf16x8 z = bf16x8{};
+    asm volatile("" : "+v"(z));
+    operand_gap();
+#pragma unroll
+    for (int u = 0; u < NLB; ++u) zero_a(oT[u], z);
+  }
+  float m_run, l_run = 0.0f;
+
+  // causal mask of key tile j (also hides keys past S); key of register r is
+  // 32j + 8 (r / 4) + 4 (l / 32) + r % 4
+  auto mask = [&](f32x16& s, int j) {
+    const int s0 = j * LT::KT;
+    if (s0 + LT::KT - 1 > P + t0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (s0 + 8 * (r >> 2) + 4 * hh + (r & 3) > P + t) s[r] = -INFINITY;
+    }
+  };
+  // column maximum over the tile: 16 keys in this lane, 16 in lane l ^ 32
+  auto rowmax = [&](const f32x16& s) {
+    const float m0 = max3_nn(s[0], s[1], s[2]), m1 = max3_nn(s[3], s[4], s[5]);
+    const float m2 = max3_nn(s[6], s[7], s[8]), m3 = max3_nn(s[9], s[10], s[11]);
+    const float m4 = max3_nn(s[12], s[13], s[14]);
+    return xhalf_max(max3_nn(max3_nn(m0, m1, m2), max3_nn(m3, m4, s[15]), -INFINITY));
+  };
+  auto tile_at = [&](int j) { return smem + (j % NS) * LT::BYTES; };
+  // this wave's copies of a tile have landed once at most those of the
+  // `younger` tiles issued after it are still outstanding
+  auto wait_tile = [&](int younger) {
+    if (NS >= 5 && younger >= 3) wait_vmcnt<(NS >= 5 ? 3 : 0) * CPW>();
+    else if (younger == 2) wait_vmcnt<2 * CPW>();
+    else if (younger == 1) wait_vmcnt<CPW>();
+    else wait_vmcnt<0>();
+  };
+
+  // ---- tile 0: scores only (each step below starts with its tile's softmax)
+  wait_tile(min(NS - 2, ntiles - 1));
+  wg_barrier();
+  f32x16 sc;
+  {
+    bf16x8 ao[3];
+    ao[0] = sa.score_operand(smem, 0);
+    ao[1] = sa.score_operand(smem, 1);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (kk + 2 < NKK) ao[(kk + 2) % 3] = sa.score_operand(smem, kk + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0) mfma32v_first(sc, ao[0], qT[0]);
+      else mfma32v(sc, ao[kk % 3], qT[kk]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  settle_v(sc);
+  mask(sc, 0);
+  float mx = rowmax(sc);
+  m_run = mx;
+
+  // The reference max moves only when a score exceeds it by more than 8 (so
+  // P <= 2^8): the O^T rescale is rare.  Every lane of a column pair holds
+  // the same maxima, so both halves take the same decision.
+  auto maybe_rescale = [&]() {
+    const bool need = mx > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float m_new = need ? mx : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      wait_states_24();  // the last value products have written O^T
+#pragma unroll
+      for (int u = 0; u < NLB; ++u) scale_acc(oT[u], alpha);
+      wait_states_24();  // the rescaled O^T feeds the next value products
+      m_run = m_new;
+    }
+  };
+  auto softmax_sum = [&](const f32x16& p) {
+    const float s0 = (p[0] + p[1]) + (p[2] + p[3]), s1 = (p[4] + p[5]) + (p[6] + p[7]);
+    const float s2 = (p[8] + p[9]) + (p[10] + p[11]), s3 = (p[12] + p[13]) + (p[14] + p[15]);
+    l_run += (s0 + s1) + (s2 + s3);
+  };
+
+  // One key tile `it`: on entry sc holds the masked scores of tile it and mx
+  // their column maxima; on exit, those of tile it+1 (garbage after the last
+  // tile, never used).
+  auto step_next = [&](int it) {
+    const MLA_LDS char* tile = tile_at(it);
+    const MLA_LDS char* tnext = tile_at(it + 1);
+    // tile it+1 (if any) landed; tiles it+2 .. it+NS-2 may still be in flight
+    wait_tile(max(0, min(NS - 3, ntiles - 2 - it)));
+    wg_barrier();  // tile it+1 visible; every wave is done with tile it-1
+    // tile it+NS-1 goes into the stage tile it-1 has left; its copies are
+    // spread over phase B, one after every fourth value product (sent all at
+    // once they stall the wave for several hundred cycles)
+    const bool copy = it + NS - 1 < ntiles;
+    const auto pend = prepare_key_tile<PAGED>(copier, a, b, S, it + NS - 1, tile_at(it + NS - 1));
+    maybe_rescale();
+
+    // phase A: score products of tile it+1 (k-blocks 0 .. NKK/2-1) under the
+    // exponentials of tile it; operands read SPF products ahead
+    f32x16 sn;
+    bf16x8 ao[SPF + 1];
+#pragma unroll
+    for (int u = 0; u < SPF; ++u) ao[u] = sa.score_operand(tnext, u);
+#pragma unroll
+    for (int kk = 0; kk < NKK / 2; ++kk) {
+      ao[(kk + SPF) % (SPF + 1)] = sa.score_operand(tnext, kk + SPF);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0) mfma32v_first(sn, ao[0], qT[0]);
+      else mfma32v(sn, ao[kk % (SPF + 1)], qT[kk]);
+#pragma unroll
+      for (int e = EPK * kk; e < EPK * (kk + 1); ++e) sc[e] = fast_exp2(sc[e] - m_run);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    softmax_sum(sc);
+    bf16x8 pB0 = pack8(sc, 0, 1.0f), pB1 = pack8(sc, 8, 1.0f);
+    // phase B: value products of tile it (n = 2 t + kb: latent block t, key
+    // block kb); the first NKK/2 are each followed by one of the remaining
+    // score products of tile it+1
+    bf16x8 av[VPF + 1];
+#pragma unroll
+    for (int u = 0; u < VPF; ++u) av[u] = sa.value_operand(tile, u);
+    // P is packed by VALU instructions: materialise both halves here (the
+    // compiler would otherwise sink a half to its first product, past the
+    // gap), then the two wait states before a product reads them
+    asm volatile("" : "+v"(pB0), "+v"(pB1));
+    operand_gap();
+#pragma unroll
+    for (int n = 0; n < 2 * NLB; ++n) {
+      if (n + VPF < 2 * NLB) av[(n + VPF) % (VPF + 1)] = sa.value_operand(tile, n + VPF);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma32a(oT[n >> 1], av[n % (VPF + 1)], (n & 1) ? pB1 : pB0);
+      __builtin_amdgcn_sched_barrier(0);
+      if ((n & 3) == 1 && (n >> 2) < CPW) {
+        if (copy) copier.issue_one(pend, n >> 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (n < NKK / 2) {
+        const int kk = NKK / 2 + n;
+        if (kk + SPF < NKK) ao[(kk + SPF) % (SPF + 1)] = sa.score_operand(tnext, kk + SPF);
+        mfma32v(sn, ao[kk % (SPF + 1)], qT[kk]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (n == NKK / 2 + 1) {
+        // tile it+1's scores are complete: mask and column maxima under the
+        // remaining value products
+        settle_v(sn);
+        mask(sn, it + 1);
+        mx = rowmax(sn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    sc = sn;
+  };
+
+  // Every tile runs the same step, the last one included: its look-ahead
+  // score products read a stage no copy is writing (stale bytes) and are
+  // discarded, about half a tile of extra products per workgroup.  A peeled
+  // last step after the loop would be cheaper in products, but the extra live
+  // ranges push the architectural registers over 256 and the allocator then
+  // evicts O^T from its registers; a branch inside the loop whose arms both
+  // update O^T does the same at its join.
+  for (int it = 0; it < ntiles; ++it) step_next(it);
+
+  // ---- epilogue: o^T = W_UV[h] (O^T / l), gate, store
+  wait_states_24();  // the last value products have written O^T
+#pragma unroll
+  for (int u = 0; u < NLB; ++u) pin_a(oT[u]);
+  const float l_tot = xhalf_sum(l_run);
+  const float inv_l = 1.0f / l_tot;
+  if (a.lse && hh == 0 && tvalid && hvalid)
+    a.lse[((size_t)b * H + h) * T + t] = (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
+  const bool store = tvalid && hvalid;
+  const size_t orow = (qr0 + (tvalid ? t : T - 1)) * (size_t)H * DV + (size_t)hc * DV;
+  // gate logits of this lane's row, v = 32 vb + 8 c + 4 (l / 32) + 0..3
+  constexpr int NVB = DV / 32;
+  bf16x4 gv[NVB][4];
+#pragma unroll
+  for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      gv[vb][c] = *(const bf16x4*)(a.gate + orow + 32 * vb + 8 * c + 4 * hh);  // orow is a valid row
+  bf16x8 ob[2 * NLB];
+#pragma unroll
+  for (int u = 0; u < NLB; ++u) {
+    ob[2 * u] = pack8(oT[u], 0, inv_l);
+    ob[2 * u + 1] = pack8(oT[u], 8, inv_l);
+  }
+  // W_UV[h] goes through this wave's own 32 KiB of the (now free) stages, in
+  // chunks of 32 rows x R/2 latent columns, two chunks in flight; chunk j
+  // covers v-block j / 2, latent half j % 2.  Rows are R bytes apart, and
+  // the 16-byte chunk index is XOR-ed with the row's low 4 bits.
+  // take the gate loads' vmcnt wait here, where nothing else is in flight
+  // (placed by the compiler at their first use it would also wait for the
+  // W_UV copies issued below)
+#pragma unroll
+  for (int vb = 0; vb < NVB; ++vb) asm volatile("" : "+v"(gv[vb][0]), "+v"(gv[vb][1]), "+v"(gv[vb][2]), "+v"(gv[vb][3]));
+  wg_barrier();  // every wave is done with the key tiles
+  constexpr int HALF = R / 2;                 // latent columns per chunk
+  constexpr int CHB = 32 * HALF * 2;          // bytes per chunk
+  constexpr int CPC = CHB / 1024;             // 1 KiB copies per chunk
+  constexpr int RPC = 1024 / (HALF * 2);      // rows per copy
+  static_assert(2 * CHB <= LT::BYTES && RPC * HALF * 2 == 1024, "chunk layout");
+  MLA_LDS char* wbuf = smem + w * LT::BYTES;
+  const u32x4 wrs = make_rsrc(a.wuv + (size_t)hc * DV * R, (unsigned)(DV * R * 2));
+  auto issue_chunk = [&](int j) {
+    unsigned ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int vb = j >> 1, half = j & 1;
+    const unsigned cpr = HALF / 8, rsub = ln / cpr, cl = ln % cpr;
+#pragma unroll
+    for (int i = 0; i < CPC; ++i) {
+      const unsigned row = RPC * i + rsub;  // row of the v-block
+      const unsigned src = ((32 * vb + row) * R + HALF * half) * 2 + ((cl ^ (row & 15)) << 4);
+      buf2lds16(wrs, src, wbuf + (j & 1) * CHB + i * 1024);
+    }
+  };
+  issue_chunk(0);
+  issue_chunk(1);
+#pragma unroll
+  for (int vb = 0; vb < NVB; ++vb) {
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int j = 2 * vb + half;
+      if (j + 1 < 2 * NVB) wait_vmcnt<CPC>();
+      else wait_vmcnt<0>();
+      const MLA_LDS char* cb = wbuf + (j & 1) * CHB + l32 * (HALF * 2) + 8 * hh;
+#pragma unroll
+      for (int kb = 0; kb < HALF / 16; ++kb) {
+        // k-block = latent HALF half + 16 kb + 8 c + 4 (l / 32) + e for slot 4 c + e
+        const bf16x4 lo = *(const MLA_LDS bf16x4*)(cb + (((2 * kb) ^ (l32 & 15)) << 4));
+        const bf16x4 hi = *(const MLA_LDS bf16x4*)(cb + (((2 * kb + 1) ^ (l32 & 15)) << 4));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat4(lo, hi), ob[(HALF / 16) * half + kb], acc, 0, 0, 0);
+      }
+      // this chunk's LDS reads have returned (their products are issued):
+      // its buffer takes chunk j + 2
+      if (j + 2 < 2 * NVB) {
+        wait_lgkmcnt0();
+        issue_chunk(j + 2);
+      }
+    }
+    if (store) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[4 * c + e] * sigmoidf_((float)gv[vb][c][e]));
+        *(bf16x4*)(a.out + orow + 32 * vb + 8 * c + 4 * hh) = ov;
+      }
+    }
+  }
+}
+
+}  // namespace mla
