@@ -103,7 +103,7 @@ template <int DQ, int DV, int R, bool PAGED = false>
 void launch_prefill_bf16(mla::PrefillArgs a, hipStream_t s) {
   if constexpr (R == 512) {
     a.ntb = (a.T + mla::kSoloRows - 1) / mla::kSoloRows;
-    a.nhg = (a.H + mla::kSoloWaves - 1) / mla::kSoloWaves;
+    a.nhg = a.H;  // one head per workgroup
     a.xcd_remap = (a.nhg % 8) == 0 ? 1 : 0;
     hipLaunchKernelGGL((mla::mla_prefill_solo_kernel<DQ, DV, R, PAGED>), dim3(a.B * a.ntb * a.nhg),
                        dim3(64 * mla::kSoloWaves), 0, s, a);
@@ -314,7 +314,7 @@ void launch_varlen_bf16(mla::PrefillArgs a, const int* cu_q, const int* seq_lens
   hipLaunchKernelGGL(mla::mla_varlen_prepare, dim3(1), dim3(256), 0, s, cu_q, seq_lens, a.B, Nq, max_rows, BR,
                      max_blocks, const_cast<int4*>(a.seq), const_cast<int2*>(a.blocks), const_cast<int*>(a.nblocks));
   if constexpr (R == 512) {
-    a.nhg = (a.H + mla::kSoloWaves - 1) / mla::kSoloWaves;
+    a.nhg = a.H;  // one head per workgroup
     a.xcd_remap = 0;
     hipLaunchKernelGGL((mla::mla_prefill_solo_kernel<DQ, DV, R, true, true>), dim3(max_blocks * a.nhg),
                        dim3(64 * mla::kSoloWaves), 0, s, a);

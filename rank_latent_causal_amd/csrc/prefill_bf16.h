@@ -92,15 +92,18 @@ __global__ void __launch_bounds__(256) mla_varlen_prepare(const int* __restrict_
 // Issues the copies of key tile j (rows 32j .. 32j+31 of sequence b) into an
 // LDS stage: from the contiguous latent [B, S, R], or through the block table.
 // prepare_key_tile forms the descriptor and offsets only; the copies then go
-// out with copier.issue_range.
+// out with copier.issue_range / issue_one.  With real = false the descriptor
+// covers no bytes (the copies write zero rows), so callers can issue a tile's
+// copies without a branch; the block-table lookup then reads entry 0.
 template <bool PAGED, int R, int NW, int SW>
 __device__ __forceinline__ typename TileCopier<R, NW, SW>::Pending prepare_key_tile(
-    const TileCopier<R, NW, SW>& copier, const PrefillArgs& a, int b, int S, int j, MLA_LDS char* stage) {
+    const TileCopier<R, NW, SW>& copier, const PrefillArgs& a, int b, int S, int j, MLA_LDS char* stage,
+    bool real = true) {
   constexpr int KT = LatentTile<R>::KT;
   if constexpr (PAGED) {
-    const int pos = j * KT;
+    const int pos = real ? j * KT : 0;
     int pg = sload_i32(a.block_table + (size_t)b * a.max_pages + (pos >> a.page_shift));
-    int valid = min(S - pos, KT);
+    int valid = real ? min(S - pos, KT) : 0;
     if ((unsigned)pg >= (unsigned)a.num_pages) {
       pg = 0;
       valid = 0;
@@ -108,14 +111,15 @@ __device__ __forceinline__ typename TileCopier<R, NW, SW>::Pending prepare_key_t
     const size_t row = ((size_t)pg << a.page_shift) + (pos & ((1 << a.page_shift) - 1));
     return copier.prepare(a.c + row * R, 0, valid, stage);
   } else {
-    return copier.prepare(a.c + (size_t)b * S * R, j * KT, S, stage);
+    return copier.prepare(a.c + (size_t)b * S * R, j * KT, real ? S : 0, stage);
   }
 }
 
 template <bool PAGED, int R, int NW, int SW>
 __device__ __forceinline__ void issue_key_tile(const TileCopier<R, NW, SW>& copier, const PrefillArgs& a, int b, int S,
-                                               int j, MLA_LDS char* stage) {
-  copier.template issue_range<0, TileCopier<R, NW, SW>::CPW>(prepare_key_tile<PAGED>(copier, a, b, S, j, stage));
+                                               int j, MLA_LDS char* stage, bool real = true) {
+  copier.template issue_range<0, TileCopier<R, NW, SW>::CPW>(
+      prepare_key_tile<PAGED>(copier, a, b, S, j, stage, real));
 }
 
 // waves per workgroup: 4 heads x (kPrefillWaves / 4) blocks of 16 positions

@@ -1,8 +1,8 @@
 // Single-wave-per-SIMD bf16 prefill for the absorbed Gated MLA layer (r >= 256)
 // on gfx950.
 //
-// One workgroup = 4 waves = 32 query positions x 4 heads; each wave owns one
-// head's 32 positions over the WHOLE latent width r, so the score of page
+// One workgroup = 4 waves = 128 query positions of one head; each wave owns
+// 32 of the positions over the WHOLE latent width r, so the score of page
 // "Gated MLA（矩阵吸收版）", section 完整计算流（四步） step 2 is complete
 // inside the wave: no partial scores are exchanged.  Per 32-key tile of c the
 // wave runs, on v_mfma_f32_32x32x16_bf16 (transposed products, each lane owns
@@ -18,7 +18,11 @@
 // value products of tile i, so the matrix pipe has independent work while the
 // softmax arithmetic and the LDS reads are in flight.
 // Every c tile is copied once per workgroup into LDS (LDS-DMA, four stages,
-// two tiles of lookahead) and read by the four heads.
+// two tiles of lookahead) and read by the four waves.  The workgroup's key
+// range is that of its last wave; the earlier waves see their extra tiles
+// fully masked (about 1% of the products at 8192 positions).  One head per
+// workgroup lets the four waves share the head's weights: the W_UK rows
+// through the L1 cache, W_UV staged once in LDS for the epilogue.
 #pragma once
 
 #include <type_traits>
@@ -103,7 +107,8 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base, float s) {
 
 constexpr int kSoloWaves = 4;
 constexpr int kSoloStages = 4;
-constexpr int kSoloRows = 32;  // query positions per workgroup
+constexpr int kSoloWaveRows = 32;                     // query positions per wave
+constexpr int kSoloRows = kSoloWaveRows * kSoloWaves;  // per workgroup (one head)
 constexpr int kSoloScoreLookahead = 2;
 constexpr int kSoloValueLookahead = 2;
 
@@ -117,8 +122,8 @@ struct SoloAttn {
   // Operand addresses inside a tile (XOR chunk swizzle folded in):
   //  * score operand of k-block kk: key row l % 32, chunk 2kk + l / 32, at
   //    qb[kk & 7] + 256 (kk >> 3);
-  //  * value operand of latent block t, key block kb (keys 16kb + ...), two
-  //    transposing reads: rows 16kb + 4 (l / 32) + e (+ 8), chunk
+  //  * value operand n = NLB kb + t of latent block t, key block kb (keys
+  //    16kb + ...), two transposing reads: rows 16kb + 4 (l / 32) + e (+ 8), chunk
   //    4t + 2 ((l / 16) & 1) + (l % 4) / 2, at vb[4j + (t & 3)] + 256 (t >> 2)
   //    + 16 ROWB kb.
   int qb[8], vb[8];
@@ -142,8 +147,8 @@ struct SoloAttn {
     return lds_read_b128(tile + qb[kk & 7] + 256 * (kk >> 3));
   }
   __device__ __forceinline__ bf16x8 value_operand(const MLA_LDS char* tile, int n) const {
-    // n = 2t + kb
-    const int t = n >> 1, kb = n & 1;
+    // n = NLB kb + t
+    const int t = n % NLB, kb = n / NLB;
     const MLA_LDS char* p = tile + 256 * (t >> 2) + 16 * ROWB * kb;
     return cat4(lds_read_tr16(p + vb[t & 3]), lds_read_tr16(p + vb[4 + (t & 3)]));
   }
@@ -154,35 +159,36 @@ struct SoloAttn {
 // qscale.  The A operand row rho of the 32-dim block loads latent dim
 // perm(rho) (bits 2 and 3 swapped) so that C registers 0-7 / 8-15 of a lane
 // are exactly the 8 consecutive dims of k-blocks 2blk / 2blk + 1.
-template <int DQ, int R, typename AfterFirstLoads>
-__device__ __forceinline__ void absorb_solo(const bf16* __restrict__ qrow, const bf16* __restrict__ wkT,
-                                            float qscale, int lane, bf16x8 (&qT)[R / 16],
-                                            AfterFirstLoads&& after_first_loads) {
+// q_abs^T blocks [blk0, blk1) of 32 latent dims from W_UK^T[h] held in LDS
+// ([R, DQ] rows of DQ * 2 bytes, 16-byte chunk L of row j at L ^ (j & 15)).
+// qb[k] is the B operand q^T for d = 16 k + 8 (l / 32) + 0..7.  The A operand
+// row rho of a block loads latent dim perm(rho) (bits 2 and 3 swapped) so
+// that C registers 0-7 / 8-15 of a lane are exactly the 8 consecutive dims of
+// k-blocks 2 blk / 2 blk + 1.
+template <int DQ, int R>
+__device__ __forceinline__ void absorb_lds(const MLA_LDS char* wk, const bf16x8 (&qb)[DQ / 16], float qscale,
+                                           int lane, int blk0, int blk1, bf16x8 (&qT)[R / 16]) {
   constexpr int NKS = DQ / 16;
-  constexpr int NB = R / 32;
+  static_assert(DQ / 8 <= 16, "chunk swizzle covers a row");
   const int l32 = lane & 31, hh = lane >> 5;
   const int prow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
-  // The products are volatile assembly, which the compiler does not move
-  // memory accesses across, so the loads are placed by hand: the W_UK^T
-  // operands run two 32-row blocks ahead of their products.
-  bf16x8 qb[NKS], wa[2][NKS];
-  auto load_block = [&](int blk, bf16x8(&wv)[NKS]) {
-    const bf16* wrow = wkT + (size_t)(32 * blk + prow) * DQ + 8 * hh;
-#pragma unroll
-    for (int k = 0; k < NKS; ++k) wv[k] = *(const bf16x8*)(wrow + 16 * k);
+  const int xw = prow & (DQ / 8 - 1);
+  auto operand = [&](int blk, int k) {
+    return lds_read_b128(wk + (32 * blk + prow) * (DQ * 2) + (((2 * k + hh) ^ xw) << 4));
   };
 #pragma unroll
-  for (int k = 0; k < NKS; ++k) qb[k] = *(const bf16x8*)(qrow + 16 * k + 8 * hh);
-  load_block(0, wa[0]);
-  if constexpr (NB > 1) load_block(1, wa[1]);
-  after_first_loads();
-#pragma unroll
-  for (int blk = 0; blk < NB; ++blk) {
+  for (int blk = blk0; blk < blk1; ++blk) {
+    bf16x8 a0 = operand(blk, 0), a1 = operand(blk, NKS > 1 ? 1 : 0);
     f32x16 acc;
-    mfma32v_first(acc, wa[blk & 1][0], qb[0]);
 #pragma unroll
-    for (int k = 1; k < NKS; ++k) mfma32v(acc, wa[blk & 1][k], qb[k]);
-    if (blk + 2 < NB) load_block(blk + 2, wa[blk & 1]);
+    for (int k = 0; k < NKS; ++k) {
+      bf16x8 an = a1;
+      if (k + 2 < NKS) an = operand(blk, k + 2);
+      if (k == 0) mfma32v_first(acc, a0, qb[0]);
+      else mfma32v(acc, a0, qb[k]);
+      a0 = a1;
+      a1 = an;
+    }
     settle_v(acc);
     qT[2 * blk] = pack8(acc, 0, qscale);
     qT[2 * blk + 1] = pack8(acc, 8, qscale);
@@ -211,7 +217,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[NS * LT::BYTES];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
 
-  // ---- work item (32 positions x 4 heads), heaviest query blocks first
+  // ---- work item (128 positions of one head), heaviest query blocks first
   const int x = blockIdx.x;
   int tb, b, hg;
   if constexpr (VARLEN) {
@@ -237,9 +243,9 @@ mla_prefill_solo_kernel(PrefillArgs a) {
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int h = hg * NW + w;
-  const bool hvalid = h < a.H;
-  const int hc = hvalid ? h : a.H - 1;
+  const int h = hg;  // one head per workgroup (hg < H)
+  constexpr bool hvalid = true;
+  const int hc = h;
   const int H = a.H;
   int T = a.T, S = a.S;
   size_t qr0 = (size_t)b * a.T;  // packed row of query 0 of sequence b
@@ -249,8 +255,9 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     T = __builtin_amdgcn_readfirstlane(sq.y);
     S = __builtin_amdgcn_readfirstlane(sq.z);
   }
-  const int t0 = tb * kSoloRows;
-  const int t = t0 + l32;  // this lane's query column
+  const int t0 = tb * kSoloRows;           // first query of the workgroup
+  const int tw = t0 + kSoloWaveRows * w;   // first query of this wave
+  const int t = tw + l32;  // this lane's query column
   const bool tvalid = t < T;
   const int P = S - T;  // query t sits at position P + t
   const int ntiles = (P + min(t0 + kSoloRows, T) + LT::KT - 1) / LT::KT;
@@ -258,15 +265,51 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   TileCopier<R, NW, 1> copier;
   copier.init(w, lane);
 
-  // absorb; the first latent tiles are copied once the first operand blocks
-  // of the absorb are requested (their vmcnt waits then do not include them)
-  bf16x8 qT[NKK];
-  absorb_solo<DQ, R>(a.q + ((qr0 + (tvalid ? t : T - 1)) * H + hc) * DQ, a.wukT + (size_t)hc * R * DQ, a.qscale,
-                     lane, qT, [&]() {
+  // ---- absorb.  W_UK^T[h] ([R, DQ], 128 KiB at full width) is staged in the
+  // LDS stages by the four waves together (1 KiB LDS-DMA copies), then each
+  // wave forms its q_abs^T in two halves of the latent: once the first half
+  // is done, its stages take the first latent tiles, which land while the
+  // second half runs.
+  constexpr int WKB = R * DQ * 2;                 // W_UK^T bytes
+  constexpr int CPRW = DQ / 8;                    // 16-byte chunks per W_UK^T row
+  constexpr int WCPW = WKB / 1024 / NW;           // copies per wave
+  static_assert(WKB <= NS * LT::BYTES && WKB % (1024 * NW) == 0 && 64 % CPRW == 0, "W_UK^T staging");
+  static_assert(NS == 4 && 2 * LT::BYTES * 2 >= WKB, "first-half stages take tiles 0 and 1");
+  {
+    const u32x4 krs = make_rsrc(a.wukT + (size_t)hc * R * DQ, (unsigned)WKB);
+    unsigned ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const unsigned rsub = ln / CPRW, cl = ln % CPRW;
 #pragma unroll
-                       for (int p = 0; p < NS - 1; ++p)
-                         if (p < ntiles) issue_key_tile<PAGED>(copier, a, b, S, p, smem + p * LT::BYTES);
-                     });
+    for (int c = 0; c < WCPW; ++c) {
+      const int i = c * NW + w;  // copy i: rows (64 / CPRW) i ..
+      const unsigned row = (64 / CPRW) * i + rsub;
+      buf2lds16(krs, (row * DQ + ((cl ^ (row & (CPRW - 1))) * 8)) * 2, smem + i * 1024);
+    }
+  }
+  constexpr int NKS = DQ / 16;
+  bf16x8 qb[NKS];
+  {
+    const bf16* qrow = a.q + ((qr0 + (tvalid ? t : T - 1)) * H + hc) * DQ + 8 * hh;
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) qb[k] = *(const bf16x8*)(qrow + 16 * k);
+    // the compiler's wait for these loads also covers the W_UK^T copies
+    // issued before them (vmcnt retires in order)
+#pragma unroll
+    for (int k = 0; k < NKS; ++k) asm volatile("" : "+v"(qb[k]));
+  }
+  wait_vmcnt<0>();
+  wg_barrier();  // W_UK^T staged
+  bf16x8 qT[NKK];
+  absorb_lds<DQ, R>(smem, qb, a.qscale, lane, 0, NLB / 2, qT);
+  wg_barrier();  // every wave is done with the first half (stages 0 and 1)
+  // tiles past the last are copied as zero rows (no branches; every step
+  // below then has exactly NS - 3 younger tiles in flight)
+#pragma unroll
+  for (int p = 0; p < 2; ++p) issue_key_tile<PAGED>(copier, a, b, S, p, smem + p * LT::BYTES, p < ntiles);
+  absorb_lds<DQ, R>(smem, qb, a.qscale, lane, NLB / 2, NLB, qT);
+  wg_barrier();  // every wave is done with the second half
+  issue_key_tile<PAGED>(copier, a, b, S, NS - 2, smem + (NS - 2) * LT::BYTES, NS - 2 < ntiles);
   SA sa;
   sa.init_addressing(lane);
 
@@ -284,7 +327,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   // 32j + 8 (r / 4) + 4 (l / 32) + r % 4
   auto mask = [&](f32x16& s, int j) {
     const int s0 = j * LT::KT;
-    if (s0 + LT::KT - 1 > P + t0) {
+    if (s0 + LT::KT - 1 > P + tw) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (s0 + 8 * (r >> 2) + 4 * hh + (r & 3) > P + t) s[r] = -INFINITY;
@@ -298,17 +341,10 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     return xhalf_max(max3_nn(max3_nn(m0, m1, m2), max3_nn(m3, m4, s[15]), -INFINITY));
   };
   auto tile_at = [&](int j) { return smem + (j % NS) * LT::BYTES; };
-  // this wave's copies of a tile have landed once at most those of the
-  // `younger` tiles issued after it are still outstanding
-  auto wait_tile = [&](int younger) {
-    if (NS >= 5 && younger >= 3) wait_vmcnt<(NS >= 5 ? 3 : 0) * CPW>();
-    else if (younger == 2) wait_vmcnt<2 * CPW>();
-    else if (younger == 1) wait_vmcnt<CPW>();
-    else wait_vmcnt<0>();
-  };
+
 
   // ---- tile 0: scores only (each step below starts with its tile's softmax)
-  wait_tile(min(NS - 2, ntiles - 1));
+  wait_vmcnt<(NS - 2) * CPW>();  // tile 0 landed (tiles 1 .. NS-2 may be in flight)
   wg_barrier();
   f32x16 sc;
   {
@@ -357,22 +393,29 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   auto step_next = [&](int it) {
     const MLA_LDS char* tile = tile_at(it);
     const MLA_LDS char* tnext = tile_at(it + 1);
-    // tile it+1 (if any) landed; tiles it+2 .. it+NS-2 may still be in flight
-    wait_tile(max(0, min(NS - 3, ntiles - 2 - it)));
+    // tile it+1 landed; tiles it+2 .. it+NS-2 may still be in flight
+    wait_vmcnt<(NS - 3) * CPW>();
     wg_barrier();  // tile it+1 visible; every wave is done with tile it-1
+    // the first score operands of tile it+1 go out before anything else, and
+    // the first value operands of tile it (resident since the last step)
+    // right after: their LDS latency runs under the bookkeeping below
+    bf16x8 ao[SPF + 1], av[VPF + 1];
+#pragma unroll
+    for (int u = 0; u < SPF; ++u) ao[u] = sa.score_operand(tnext, u);
+#pragma unroll
+    for (int u = 0; u < VPF; ++u) av[u] = sa.value_operand(tile, u);
     // tile it+NS-1 goes into the stage tile it-1 has left; its copies are
     // spread over phase B, one after every fourth value product (sent all at
-    // once they stall the wave for several hundred cycles)
-    const bool copy = it + NS - 1 < ntiles;
-    const auto pend = prepare_key_tile<PAGED>(copier, a, b, S, it + NS - 1, tile_at(it + NS - 1));
+    // once they stall the wave for several hundred cycles).  Past the last
+    // tile they are issued anyway, with an empty range that writes zeros
+    // into that free stage: a branch around each copy costs more than it.
+    const auto pend =
+        prepare_key_tile<PAGED>(copier, a, b, S, it + NS - 1, tile_at(it + NS - 1), it + NS - 1 < ntiles);
     maybe_rescale();
 
     // phase A: score products of tile it+1 (k-blocks 0 .. NKK/2-1) under the
     // exponentials of tile it; operands read SPF products ahead
     f32x16 sn;
-    bf16x8 ao[SPF + 1];
-#pragma unroll
-    for (int u = 0; u < SPF; ++u) ao[u] = sa.score_operand(tnext, u);
 #pragma unroll
     for (int kk = 0; kk < NKK / 2; ++kk) {
       ao[(kk + SPF) % (SPF + 1)] = sa.score_operand(tnext, kk + SPF);
@@ -383,27 +426,24 @@ mla_prefill_solo_kernel(PrefillArgs a) {
       for (int e = EPK * kk; e < EPK * (kk + 1); ++e) sc[e] = fast_exp2(sc[e] - m_run);
       __builtin_amdgcn_sched_barrier(0);
     }
-    softmax_sum(sc);
-    bf16x8 pB0 = pack8(sc, 0, 1.0f), pB1 = pack8(sc, 8, 1.0f);
-    // phase B: value products of tile it (n = 2 t + kb: latent block t, key
-    // block kb); the first NKK/2 are each followed by one of the remaining
-    // score products of tile it+1
-    bf16x8 av[VPF + 1];
-#pragma unroll
-    for (int u = 0; u < VPF; ++u) av[u] = sa.value_operand(tile, u);
-    // P is packed by VALU instructions: materialise both halves here (the
-    // compiler would otherwise sink a half to its first product, past the
-    // gap), then the two wait states before a product reads them
-    asm volatile("" : "+v"(pB0), "+v"(pB1));
+    // P is packed by VALU instructions: each half is materialised where it is
+    // formed (the compiler would otherwise sink it towards its products,
+    // past the gap) and read by a product at least two wait states later
+    bf16x8 pB0 = pack8(sc, 0, 1.0f), pB1;
+    asm volatile("" : "+v"(pB0));
     operand_gap();
+    // phase B: value products of tile it in key-block-major order (n = NLB kb
+    // + t: latent block t, key block kb), so the first NLB use only the first
+    // half of P; the first NKK/2 are each followed by one of the remaining
+    // score products of tile it+1
 #pragma unroll
     for (int n = 0; n < 2 * NLB; ++n) {
       if (n + VPF < 2 * NLB) av[(n + VPF) % (VPF + 1)] = sa.value_operand(tile, n + VPF);
       __builtin_amdgcn_sched_barrier(0);
-      mfma32a(oT[n >> 1], av[n % (VPF + 1)], (n & 1) ? pB1 : pB0);
+      mfma32a(oT[n % NLB], av[n % (VPF + 1)], n < NLB ? pB0 : pB1);
       __builtin_amdgcn_sched_barrier(0);
       if ((n & 3) == 1 && (n >> 2) < CPW) {
-        if (copy) copier.issue_one(pend, n >> 2);
+        copier.issue_one(pend, n >> 2);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (n < NKK / 2) {
@@ -412,17 +452,33 @@ mla_prefill_solo_kernel(PrefillArgs a) {
         mfma32v(sn, ao[kk % (SPF + 1)], qT[kk]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // the rest of the softmax of tile it, and the mask and column maxima
+      // of tile it+1 once its scores are complete, each under one product
+      if (n == 0) {
+        pB1 = pack8(sc, 8, 1.0f);
+        asm volatile("" : "+v"(pB1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (n == 1) {
+        softmax_sum(sc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (n == NKK / 2 + 1) {
-        // tile it+1's scores are complete: mask and column maxima under the
-        // remaining value products
         settle_v(sn);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (n == NKK / 2 + 2) {
         mask(sn, it + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (n == NKK / 2 + 3) {
         mx = rowmax(sn);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     sc = sn;
   };
+
 
   // Every tile runs the same step, the last one included: its look-ahead
   // score products read a stage no copy is writing (stale bytes) and are
@@ -457,59 +513,51 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     ob[2 * u] = pack8(oT[u], 0, inv_l);
     ob[2 * u + 1] = pack8(oT[u], 8, inv_l);
   }
-  // W_UV[h] goes through this wave's own 32 KiB of the (now free) stages, in
-  // chunks of 32 rows x R/2 latent columns, two chunks in flight; chunk j
-  // covers v-block j / 2, latent half j % 2.  Rows are R bytes apart, and
-  // the 16-byte chunk index is XOR-ed with the row's low 4 bits.
+  // W_UV[h] ([DV, R], 64 KiB to 128 KiB) is staged whole in the (now free)
+  // stages by the four waves together: row v at v R 2 bytes, its 16-byte
+  // chunk L at L ^ (v & 15).  The copies go out in v-block order; v-block vb
+  // is waited for (and made visible by a barrier) just before its products.
+  constexpr int CPR = R / 8;                  // 16-byte chunks per row
+  constexpr int RPC = 64 / CPR;               // rows per 1 KiB copy
+  constexpr int CPV = 32 / RPC / NW;          // copies per wave per v-block
+  static_assert(DV * R * 2 <= NS * LT::BYTES && CPV >= 1 && CPV * NVB < 64, "W_UV staging");
   // take the gate loads' vmcnt wait here, where nothing else is in flight
   // (placed by the compiler at their first use it would also wait for the
   // W_UV copies issued below)
 #pragma unroll
   for (int vb = 0; vb < NVB; ++vb) asm volatile("" : "+v"(gv[vb][0]), "+v"(gv[vb][1]), "+v"(gv[vb][2]), "+v"(gv[vb][3]));
-  wg_barrier();  // every wave is done with the key tiles
-  constexpr int HALF = R / 2;                 // latent columns per chunk
-  constexpr int CHB = 32 * HALF * 2;          // bytes per chunk
-  constexpr int CPC = CHB / 1024;             // 1 KiB copies per chunk
-  constexpr int RPC = 1024 / (HALF * 2);      // rows per copy
-  static_assert(2 * CHB <= LT::BYTES && RPC * HALF * 2 == 1024, "chunk layout");
-  MLA_LDS char* wbuf = smem + w * LT::BYTES;
-  const u32x4 wrs = make_rsrc(a.wuv + (size_t)hc * DV * R, (unsigned)(DV * R * 2));
-  auto issue_chunk = [&](int j) {
+  wait_vmcnt<0>();  // also the zero-row copies of the tiles past the last
+  wg_barrier();     // every wave is done with the key tiles
+  {
+    const u32x4 wrs = make_rsrc(a.wuv + (size_t)hc * DV * R, (unsigned)(DV * R * 2));
     unsigned ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
-    const int vb = j >> 1, half = j & 1;
-    const unsigned cpr = HALF / 8, rsub = ln / cpr, cl = ln % cpr;
+    const unsigned rsub = ln / CPR, cl = ln % CPR;
 #pragma unroll
-    for (int i = 0; i < CPC; ++i) {
-      const unsigned row = RPC * i + rsub;  // row of the v-block
-      const unsigned src = ((32 * vb + row) * R + HALF * half) * 2 + ((cl ^ (row & 15)) << 4);
-      buf2lds16(wrs, src, wbuf + (j & 1) * CHB + i * 1024);
-    }
-  };
-  issue_chunk(0);
-  issue_chunk(1);
+    for (int vb = 0; vb < NVB; ++vb)
+#pragma unroll
+      for (int c = 0; c < CPV; ++c) {
+        const int i = (vb * CPV + c) * NW + w;  // copy index: rows RPC i ..
+        const unsigned row = RPC * i + rsub;
+        buf2lds16(wrs, (row * R + ((cl ^ (row & 15)) * 8)) * 2, smem + i * 1024);
+      }
+  }
+  const MLA_LDS char* wrow = smem + l32 * (R * 2) + 8 * hh;  // + 32 vb R 2
 #pragma unroll
   for (int vb = 0; vb < NVB; ++vb) {
+    if (vb + 3 < NVB) wait_vmcnt<3 * CPV>();
+    else if (vb + 2 < NVB) wait_vmcnt<2 * CPV>();
+    else if (vb + 1 < NVB) wait_vmcnt<CPV>();
+    else wait_vmcnt<0>();
+    wg_barrier();  // v-block vb copied by every wave
+    const MLA_LDS char* rb = wrow + vb * 32 * (R * 2);
     f32x16 acc = f32x16{};
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int j = 2 * vb + half;
-      if (j + 1 < 2 * NVB) wait_vmcnt<CPC>();
-      else wait_vmcnt<0>();
-      const MLA_LDS char* cb = wbuf + (j & 1) * CHB + l32 * (HALF * 2) + 8 * hh;
-#pragma unroll
-      for (int kb = 0; kb < HALF / 16; ++kb) {
-        // k-block = latent HALF half + 16 kb + 8 c + 4 (l / 32) + e for slot 4 c + e
-        const bf16x4 lo = *(const MLA_LDS bf16x4*)(cb + (((2 * kb) ^ (l32 & 15)) << 4));
-        const bf16x4 hi = *(const MLA_LDS bf16x4*)(cb + (((2 * kb + 1) ^ (l32 & 15)) << 4));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat4(lo, hi), ob[(HALF / 16) * half + kb], acc, 0, 0, 0);
-      }
-      // this chunk's LDS reads have returned (their products are issued):
-      // its buffer takes chunk j + 2
-      if (j + 2 < 2 * NVB) {
-        wait_lgkmcnt0();
-        issue_chunk(j + 2);
-      }
+    for (int kb = 0; kb < 2 * NLB; ++kb) {
+      // k-block kb = latent 16 kb + 8 c + 4 (l / 32) + e for slot 4 c + e
+      const bf16x4 lo = *(const MLA_LDS bf16x4*)(rb + (((2 * kb) ^ (l32 & 15)) << 4));
+      const bf16x4 hi = *(const MLA_LDS bf16x4*)(rb + (((2 * kb + 1) ^ (l32 & 15)) << 4));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat4(lo, hi), ob[kb], acc, 0, 0, 0);
     }
     if (store) {
 #pragma unroll
