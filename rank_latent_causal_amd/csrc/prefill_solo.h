@@ -109,6 +109,7 @@ constexpr int kSoloWaves = 4;
 constexpr int kSoloStages = 4;
 constexpr int kSoloWaveRows = 32;                     // query positions per wave
 constexpr int kSoloRows = kSoloWaveRows * kSoloWaves;  // per workgroup (one head)
+constexpr int kSoloSpareBytes = 32768;  // LDS after the stages (the epilogue's gate rows)
 constexpr int kSoloScoreLookahead = 2;
 constexpr int kSoloValueLookahead = 2;
 
@@ -165,6 +166,20 @@ struct SoloAttn {
 // row rho of a block loads latent dim perm(rho) (bits 2 and 3 swapped) so
 // that C registers 0-7 / 8-15 of a lane are exactly the 8 consecutive dims of
 // k-blocks 2 blk / 2 blk + 1.
+// q_abs^T blocks [blk0, blk1) of 32 latent dims from W_UK^T[h] held in LDS
+// ([R, DQ] rows of DQ * 2 bytes, 16-byte chunk L of row j at L ^ (j & 15)).
+// qb[k] is the B operand q^T for d = 16 k + 8 (l / 32) + 0..7.  The A operand
+// row rho of a block loads latent dim perm(rho) (bits 2 and 3 swapped) so
+// that C registers 0-7 / 8-15 of a lane are exactly the 8 consecutive dims of
+// k-blocks 2 blk / 2 blk + 1.  Two blocks run as interleaved chains, and the
+// operand reads run two products ahead across block pairs.
+// q_abs^T blocks [blk0, blk1) of 32 latent dims from W_UK^T[h] held in LDS
+// ([R, DQ] rows of DQ * 2 bytes, 16-byte chunk L of row j at L ^ (j & 15)).
+// qb[k] is the B operand q^T for d = 16 k + 8 (l / 32) + 0..7.  The A operand
+// row rho of a block loads latent dim perm(rho) (bits 2 and 3 swapped) so
+// that C registers 0-7 / 8-15 of a lane are exactly the 8 consecutive dims of
+// k-blocks 2 blk / 2 blk + 1.  Two blocks run as interleaved chains, their
+// operand reads two products ahead.
 template <int DQ, int R>
 __device__ __forceinline__ void absorb_lds(const MLA_LDS char* wk, const bf16x8 (&qb)[DQ / 16], float qscale,
                                            int lane, int blk0, int blk1, bf16x8 (&qT)[R / 16]) {
@@ -173,28 +188,33 @@ __device__ __forceinline__ void absorb_lds(const MLA_LDS char* wk, const bf16x8 
   const int l32 = lane & 31, hh = lane >> 5;
   const int prow = (l32 & 0x13) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   const int xw = prow & (DQ / 8 - 1);
-  auto operand = [&](int blk, int k) {
-    return lds_read_b128(wk + (32 * blk + prow) * (DQ * 2) + (((2 * k + hh) ^ xw) << 4));
-  };
+  const MLA_LDS char* base = wk + prow * (DQ * 2);
 #pragma unroll
-  for (int blk = blk0; blk < blk1; ++blk) {
-    bf16x8 a0 = operand(blk, 0), a1 = operand(blk, NKS > 1 ? 1 : 0);
-    f32x16 acc;
+  for (int bp = blk0; bp < blk1; bp += 2) {
+    // products p = 2 k + u of blocks bp + u
+    auto operand = [&](int p) {
+      return lds_read_b128(base + 32 * (bp + (p & 1)) * (DQ * 2) + (((2 * (p >> 1) + hh) ^ xw) << 4));
+    };
+    bf16x8 ar[3];
+    ar[0] = operand(0);
+    ar[1] = operand(1);
+    f32x16 acc[2];
 #pragma unroll
-    for (int k = 0; k < NKS; ++k) {
-      bf16x8 an = a1;
-      if (k + 2 < NKS) an = operand(blk, k + 2);
-      if (k == 0) mfma32v_first(acc, a0, qb[0]);
-      else mfma32v(acc, a0, qb[k]);
-      a0 = a1;
-      a1 = an;
+    for (int p = 0; p < 2 * NKS; ++p) {
+      if (p + 2 < 2 * NKS) ar[(p + 2) % 3] = operand(p + 2);
+      if (p < 2) mfma32v_first(acc[p & 1], ar[p % 3], qb[0]);
+      else mfma32v(acc[p & 1], ar[p % 3], qb[p >> 1]);
     }
-    settle_v(acc);
-    qT[2 * blk] = pack8(acc, 0, qscale);
-    qT[2 * blk + 1] = pack8(acc, 8, qscale);
-    // materialise the packed operands here: left to itself the compiler sinks
-    // the scale-and-pack to the first use and keeps all R fp32 values live
-    asm volatile("" : "+v"(qT[2 * blk]), "+v"(qT[2 * blk + 1]));
+    settle_v(acc[0]);
+    settle_v(acc[1]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      qT[2 * (bp + u)] = pack8(acc[u], 0, qscale);
+      qT[2 * (bp + u) + 1] = pack8(acc[u], 8, qscale);
+      // materialise the packed operands here: left to itself the compiler
+      // sinks the scale-and-pack to the first use and keeps the fp32 values
+      asm volatile("" : "+v"(qT[2 * (bp + u)]), "+v"(qT[2 * (bp + u) + 1]));
+    }
   }
 }
 
@@ -214,7 +234,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   static_assert(LT::COPIES % NW == 0, "copy split");
   static_assert(DQ % 16 == 0 && DV % 32 == 0, "shape");
   static_assert(NS >= 3 && NS <= 5 && CPW * (NS - 2) < 64, "stages and vmcnt range");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * LT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * LT::BYTES + kSoloSpareBytes];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
 
   // ---- work item (128 positions of one head), heaviest query blocks first
@@ -490,48 +510,36 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   for (int it = 0; it < ntiles; ++it) step_next(it);
 
   // ---- epilogue: o^T = W_UV[h] (O^T / l), gate, store
-  wait_states_24();  // the last value products have written O^T
-#pragma unroll
-  for (int u = 0; u < NLB; ++u) pin_a(oT[u]);
-  const float l_tot = xhalf_sum(l_run);
-  const float inv_l = 1.0f / l_tot;
-  if (a.lse && hh == 0 && tvalid && hvalid)
-    a.lse[((size_t)b * H + h) * T + t] = (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
-  const bool store = tvalid && hvalid;
-  const size_t orow = (qr0 + (tvalid ? t : T - 1)) * (size_t)H * DV + (size_t)hc * DV;
-  // gate logits of this lane's row, v = 32 vb + 8 c + 4 (l / 32) + 0..3
+  // W_UV[h] ([DV, R], 64 KiB to 128 KiB) is staged whole in the stages by the
+  // four waves together (row v at v R 2 bytes, chunk L at L ^ (v & 15)), and
+  // each wave's 32 gate rows (DV logits each) in the region after them (row
+  // r at r DV 2 bytes, chunk L at L ^ (r & 15)): every load of the epilogue
+  // is an LDS-DMA copy, waited for with explicit counts.  The copies go out
+  // first; O^T is normalised and packed under them.
   constexpr int NVB = DV / 32;
-  bf16x4 gv[NVB][4];
-#pragma unroll
-  for (int vb = 0; vb < NVB; ++vb)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      gv[vb][c] = *(const bf16x4*)(a.gate + orow + 32 * vb + 8 * c + 4 * hh);  // orow is a valid row
-  bf16x8 ob[2 * NLB];
-#pragma unroll
-  for (int u = 0; u < NLB; ++u) {
-    ob[2 * u] = pack8(oT[u], 0, inv_l);
-    ob[2 * u + 1] = pack8(oT[u], 8, inv_l);
-  }
-  // W_UV[h] ([DV, R], 64 KiB to 128 KiB) is staged whole in the (now free)
-  // stages by the four waves together: row v at v R 2 bytes, its 16-byte
-  // chunk L at L ^ (v & 15).  The copies go out in v-block order; v-block vb
-  // is waited for (and made visible by a barrier) just before its products.
-  constexpr int CPR = R / 8;                  // 16-byte chunks per row
-  constexpr int RPC = 64 / CPR;               // rows per 1 KiB copy
+  constexpr int CPR = R / 8;                  // 16-byte chunks per W_UV row
+  constexpr int RPC = 64 / CPR;               // W_UV rows per 1 KiB copy
   constexpr int CPV = 32 / RPC / NW;          // copies per wave per v-block
-  static_assert(DV * R * 2 <= NS * LT::BYTES && CPV >= 1 && CPV * NVB < 64, "W_UV staging");
-  // take the gate loads' vmcnt wait here, where nothing else is in flight
-  // (placed by the compiler at their first use it would also wait for the
-  // W_UV copies issued below)
-#pragma unroll
-  for (int vb = 0; vb < NVB; ++vb) asm volatile("" : "+v"(gv[vb][0]), "+v"(gv[vb][1]), "+v"(gv[vb][2]), "+v"(gv[vb][3]));
-  wait_vmcnt<0>();  // also the zero-row copies of the tiles past the last
+  constexpr int GCR = DV / 8;                 // 16-byte chunks per gate row
+  constexpr int GCW = 32 * DV * 2 / 1024;     // gate copies per wave
+  static_assert(DV * R * 2 <= NS * LT::BYTES && CPV >= 1 && CPV * NVB + GCW < 64, "W_UV staging");
+  static_assert(64 % GCR == 0 && GCR <= 16 && NW * GCW * 1024 <= kSoloSpareBytes, "gate staging");
+  MLA_LDS char* gbuf = smem + NS * LT::BYTES + w * (GCW * 1024);
+  wait_vmcnt<0>();  // the zero-row copies of the tiles past the last write the stages
   wg_barrier();     // every wave is done with the key tiles
   {
-    const u32x4 wrs = make_rsrc(a.wuv + (size_t)hc * DV * R, (unsigned)(DV * R * 2));
     unsigned ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    // gate rows tw + r of head h (rows past T repeat row T - 1)
+    const u32x4 grs = make_rsrc(a.gate + qr0 * (size_t)H * DV + (size_t)hc * DV, (unsigned)((size_t)T * H * DV * 2));
+    const unsigned gsub = ln / GCR, gcl = ln % GCR;
+#pragma unroll
+    for (int i = 0; i < GCW; ++i) {
+      const unsigned r = (64 / GCR) * i + gsub;
+      const unsigned row = (unsigned)min(tw + (int)r, T - 1);
+      buf2lds16(grs, (row * (unsigned)(H * DV) + ((gcl ^ (r & 15)) * 8)) * 2, gbuf + i * 1024);
+    }
+    const u32x4 wrs = make_rsrc(a.wuv + (size_t)hc * DV * R, (unsigned)(DV * R * 2));
     const unsigned rsub = ln / CPR, cl = ln % CPR;
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb)
@@ -542,6 +550,23 @@ mla_prefill_solo_kernel(PrefillArgs a) {
         buf2lds16(wrs, (row * R + ((cl ^ (row & 15)) * 8)) * 2, smem + i * 1024);
       }
   }
+  wait_states_24();  // the last value products have written O^T
+#pragma unroll
+  for (int u = 0; u < NLB; ++u) pin_a(oT[u]);
+  const float l_tot = xhalf_sum(l_run);
+  const float inv_l = 1.0f / l_tot;
+  if (a.lse && hh == 0 && tvalid && hvalid)
+    a.lse[((size_t)b * H + h) * T + t] = (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
+  const bool store = tvalid && hvalid;
+  const size_t orow = (qr0 + (tvalid ? t : T - 1)) * (size_t)H * DV + (size_t)hc * DV;
+  bf16x8 ob[2 * NLB];
+#pragma unroll
+  for (int u = 0; u < NLB; ++u) {
+    ob[2 * u] = pack8(oT[u], 0, inv_l);
+    ob[2 * u + 1] = pack8(oT[u], 8, inv_l);
+  }
+  // this lane's gate logits v = 32 vb + 8 c + 4 (l / 32) + 0..3 of row l32
+  const MLA_LDS char* grow = gbuf + l32 * (DV * 2) + 8 * hh;
   const MLA_LDS char* wrow = smem + l32 * (R * 2) + 8 * hh;  // + 32 vb R 2
 #pragma unroll
   for (int vb = 0; vb < NVB; ++vb) {
@@ -563,8 +588,9 @@ mla_prefill_solo_kernel(PrefillArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         bf16x4 ov;
+        const bf16x4 gl = *(const MLA_LDS bf16x4*)(grow + (((4 * vb + c) ^ (l32 & 15)) << 4));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[4 * c + e] * sigmoidf_((float)gv[vb][c][e]));
+        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[4 * c + e] * sigmoidf_((float)gl[e]));
         *(bf16x4*)(a.out + orow + 32 * vb + 8 * c + 4 * hh) = ov;
       }
     }
