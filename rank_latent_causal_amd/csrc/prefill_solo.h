@@ -286,53 +286,44 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   copier.init(w, lane);
 
   // ---- absorb.  W_UK^T[h] ([R, DQ], 128 KiB at full width) is staged in the
-  // LDS stages by the four waves together (1 KiB LDS-DMA copies), then each
-  // wave forms its q_abs^T in two halves of the latent: once the first half
-  // is done, its stages take the first latent tiles, which land while the
-  // second half runs.
+  // LDS stages by the four waves together (1 KiB LDS-DMA copies) in four
+  // chunks of R/4 rows, one per stage, and each wave's 32 query rows in the
+  // region after the stages.  Each wave forms its q_abs^T chunk by chunk as
+  // the chunks land; stage c then takes latent tile c (tiles 0 .. NS-2).
+  // Every load here is an LDS-DMA copy with an explicit wait count (a
+  // compiler-visible load would get a vmcnt(0) that also waits for the
+  // copies issued after it).
   constexpr int WKB = R * DQ * 2;                 // W_UK^T bytes
-  constexpr int CPRW = DQ / 8;                    // 16-byte chunks per W_UK^T row
-  constexpr int WCPW = WKB / 1024 / NW;           // copies per wave
-  static_assert(WKB <= NS * LT::BYTES && WKB % (1024 * NW) == 0 && 64 % CPRW == 0, "W_UK^T staging");
-  static_assert(NS == 4 && 2 * LT::BYTES * 2 >= WKB, "first-half stages take tiles 0 and 1");
+  constexpr int CPRW = DQ / 8;                    // 16-byte chunks per W_UK^T / q row
+  constexpr int WCC = WKB / NS / 1024 / NW;       // copies per wave per chunk
+  constexpr int QCW = 32 * DQ * 2 / 1024;         // q copies per wave
+  constexpr int NKS = DQ / 16;
+  static_assert(WKB == NS * LT::BYTES && NS == 4 && 64 % CPRW == 0 && CPRW <= 16, "W_UK^T chunks fill the stages");
+  static_assert(NW * QCW * 1024 <= kSoloSpareBytes && NS * WCC + QCW < 64, "q staging");
+  MLA_LDS char* qbuf = smem + NS * LT::BYTES + w * (QCW * 1024);
   {
-    const u32x4 krs = make_rsrc(a.wukT + (size_t)hc * R * DQ, (unsigned)WKB);
     unsigned ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
     const unsigned rsub = ln / CPRW, cl = ln % CPRW;
+    // q rows tw + r of head h (rows past T repeat row T - 1): row r at
+    // r DQ 2 bytes, chunk L at L ^ (r & 15)
+    const u32x4 qrs = make_rsrc(a.q + qr0 * (size_t)H * DQ + (size_t)hc * DQ, (unsigned)((size_t)T * H * DQ * 2));
 #pragma unroll
-    for (int c = 0; c < WCPW; ++c) {
-      const int i = c * NW + w;  // copy i: rows (64 / CPRW) i ..
+    for (int i = 0; i < QCW; ++i) {
+      const unsigned r = (64 / CPRW) * i + rsub;
+      const unsigned row = (unsigned)min(tw + (int)r, T - 1);
+      buf2lds16(qrs, (row * (unsigned)(H * DQ) + ((cl ^ (r & 15)) * 8)) * 2, qbuf + i * 1024);
+    }
+    const u32x4 krs = make_rsrc(a.wukT + (size_t)hc * R * DQ, (unsigned)WKB);
+#pragma unroll
+    for (int c = 0; c < NS * WCC; ++c) {
+      const int i = c * NW + w;  // copy i: rows (64 / CPRW) i .. (chunk c / WCC)
       const unsigned row = (64 / CPRW) * i + rsub;
       buf2lds16(krs, (row * DQ + ((cl ^ (row & (CPRW - 1))) * 8)) * 2, smem + i * 1024);
     }
   }
-  constexpr int NKS = DQ / 16;
-  bf16x8 qb[NKS];
-  {
-    const bf16* qrow = a.q + ((qr0 + (tvalid ? t : T - 1)) * H + hc) * DQ + 8 * hh;
-#pragma unroll
-    for (int k = 0; k < NKS; ++k) qb[k] = *(const bf16x8*)(qrow + 16 * k);
-    // the compiler's wait for these loads also covers the W_UK^T copies
-    // issued before them (vmcnt retires in order)
-#pragma unroll
-    for (int k = 0; k < NKS; ++k) asm volatile("" : "+v"(qb[k]));
-  }
-  wait_vmcnt<0>();
-  wg_barrier();  // W_UK^T staged
-  bf16x8 qT[NKK];
-  absorb_lds<DQ, R>(smem, qb, a.qscale, lane, 0, NLB / 2, qT);
-  wg_barrier();  // every wave is done with the first half (stages 0 and 1)
-  // tiles past the last are copied as zero rows (no branches; every step
-  // below then has exactly NS - 3 younger tiles in flight)
-#pragma unroll
-  for (int p = 0; p < 2; ++p) issue_key_tile<PAGED>(copier, a, b, S, p, smem + p * LT::BYTES, p < ntiles);
-  absorb_lds<DQ, R>(smem, qb, a.qscale, lane, NLB / 2, NLB, qT);
-  wg_barrier();  // every wave is done with the second half
-  issue_key_tile<PAGED>(copier, a, b, S, NS - 2, smem + (NS - 2) * LT::BYTES, NS - 2 < ntiles);
   SA sa;
   sa.init_addressing(lane);
-
   f32x16 oT[NLB];
   {
     bf16x8 z = bf16x8{};
@@ -341,6 +332,33 @@ mla_prefill_solo_kernel(PrefillArgs a) {
 #pragma unroll
     for (int u = 0; u < NLB; ++u) zero_a(oT[u], z);
   }
+  bf16x8 qT[NKK];
+  bf16x8 qb[NKS];
+  constexpr int BPC = NLB / NS;  // 32-row latent blocks per chunk
+  // chunk 0 (and the q rows, copied first)
+  wait_vmcnt<(NS - 1) * WCC>();
+  wg_barrier();
+#pragma unroll
+  for (int k = 0; k < NKS; ++k)
+    qb[k] = lds_read_b128(qbuf + l32 * (DQ * 2) + (((2 * k + hh) ^ (l32 & 15)) << 4));
+  absorb_lds<DQ, R>(smem, qb, a.qscale, lane, 0, BPC, qT);
+  // chunk c + 1 has landed once at most the younger chunks (NS - 2 - c of
+  // them) and tiles 0 .. c - 1 (two chunks' worth of copies each) are
+  // outstanding; the barrier also frees stage c for tile c.  Tiles past the
+  // last are copied as zero rows (no branches; every step below then has
+  // exactly NS - 3 younger tiles in flight).
+  wait_vmcnt<(NS - 2) * WCC>();
+  wg_barrier();
+  issue_key_tile<PAGED>(copier, a, b, S, 0, smem, 0 < ntiles);
+  absorb_lds<DQ, R>(smem, qb, a.qscale, lane, BPC, 2 * BPC, qT);
+  wait_vmcnt<(NS - 3) * WCC + CPW>();
+  wg_barrier();
+  issue_key_tile<PAGED>(copier, a, b, S, 1, smem + LT::BYTES, 1 < ntiles);
+  absorb_lds<DQ, R>(smem, qb, a.qscale, lane, 2 * BPC, 3 * BPC, qT);
+  wait_vmcnt<2 * CPW>();
+  wg_barrier();
+  issue_key_tile<PAGED>(copier, a, b, S, 2, smem + 2 * LT::BYTES, 2 < ntiles);
+  absorb_lds<DQ, R>(smem, qb, a.qscale, lane, 3 * BPC, 4 * BPC, qT);
   float m_run, l_run = 0.0f;
 
   // causal mask of key tile j (also hides keys past S); key of register r is
