@@ -25,6 +25,12 @@ def _compile(srcs, out_path: str, verbose: bool) -> str:
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # packed fp32 VALU forms are kept out of every kernel
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # the one-wave-per-SIMD kernels unroll their 32-product phases
+           # completely (operand arrays must stay in registers); the default
+           # size limit for "#pragma unroll" loops is below that of the decode
+           # kernel's phase, which then keeps a loop with dynamically
+           # indexed operands and spills
+           "-mllvm", "-pragma-unroll-threshold=65536",
            f"-I{INCLUDE}", *srcs, "-o", out_path + ".tmp"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "not a recognized feature" not in l)

@@ -113,6 +113,13 @@ struct TileCopier {
     }
   }
 
+  // This lane's byte offset for copy qi of any tile (for a wave that keeps
+  // it in a register and issues that one copy of every tile).
+  __device__ __forceinline__ unsigned offset_of(int qi) const {
+    const int srow = qi * RPI;
+    return lane_base() ^ (unsigned)((tile_swizzle<R, SW>(srow) << 4) | (srow * R * 2));
+  }
+
   __device__ __forceinline__ void issue(const bf16* __restrict__ base, int row0, int row_end,
                                         MLA_LDS char* stage) const {
     issue_range<0, CPW>(prepare(base, row0, row_end, stage));

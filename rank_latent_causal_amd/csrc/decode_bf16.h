@@ -284,6 +284,8 @@ struct DecodeMergeArgs {
   long long N;
   const int* n_dev;      // if set, N and G are read from n_dev[0] and n_dev[1] (paged decode:
                          // cu holds tile counts, G the number of non-empty ranges)
+  const int* krange;     // if set, [B, 2]: the first and last range holding rows of each
+                         // sequence (the ranges then come from that table, not from N and G)
 };
 
 // index of the range that holds cache row x (every range is non-empty)
@@ -347,8 +349,15 @@ __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
     const int l32 = lane & 31;
     const int i = bb * kMergeSeqs + sl;
     const int ic = i < a.B ? i : a.B - 1;
-    const long long s0 = a.cu[ic], s1 = a.cu[ic + 1];
-    const int k0 = range_of(s0, N, G), k1 = range_of(s1 - 1, N, G);
+    int k0, k1;
+    if (a.krange) {
+      k0 = a.krange[2 * ic];
+      k1 = a.krange[2 * ic + 1];
+    } else {
+      const long long s0 = a.cu[ic], s1 = a.cu[ic + 1];
+      k0 = range_of(s0, N, G);
+      k1 = range_of(s1 - 1, N, G);
+    }
     const int j0 = CPL * l32;
     float m = -INFINITY, L = 0.0f;
     float acc[CPL];
@@ -423,40 +432,96 @@ __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
 // belongs to exactly one sequence.  Partial slots, the merge and its
 // range arithmetic are those of the packed decode, in tile units.
 
-// One workgroup: clamps the lengths to [1, max_pages * page_size] and writes
-// them, the exclusive prefix sums of the tile counts (cu_t[B] = NT) and the
-// number of ranges cu_t[B + 1] = min(G, NT), so that no range is empty (the
-// merge walks every range between a sequence's first and last).
-__global__ void __launch_bounds__(256) mla_paged_prepare(const int* __restrict__ seq_lens, int B, int max_rows,
-                                                         int G, int* __restrict__ lens, int* __restrict__ cu_t) {
-  __shared__ int wsum[4];
+// One workgroup: clamps the lengths to [1, max_rows] and writes them, the
+// exclusive prefix sums of the tile counts (cu_t[B] = NT) and the number of
+// ranges cu_t[B + 1] = min(G, NT), so that no range is empty (the merge walks
+// every range between a sequence's first and last).  The lengths come from
+// seq_lens, or (cu != nullptr, packed cache) from the row prefix sums
+// cu[i + 1] - cu[i].  The sums run in 64 bits and are capped at 2^30 tiles,
+// which only lengths that break the callers' preconditions reach: the prefix
+// sums stay monotone whatever the lengths, and sequences past the cap get no
+// tiles.
+//
+// With rt != nullptr the G ranges are cut by cost instead: a tile costs 1 and
+// the start of a sequence switch_tiles more (a workgroup that reaches a new
+// sequence stores a partial and loads that sequence's query), so ranges that
+// cross many sequence starts take fewer tiles.  Range k covers tiles
+// [rt[k], rt[k + 1]) (rt[G] = NT; a range may be empty), and krange[2i],
+// krange[2i + 1] are the first and last range holding tiles of sequence i.
+__global__ void __launch_bounds__(256) mla_paged_prepare(const int* __restrict__ seq_lens,
+                                                         const int* __restrict__ cu, int B, int max_rows,
+                                                         int G, int* __restrict__ lens, int* __restrict__ cu_t,
+                                                         int* __restrict__ rt, int* __restrict__ krange,
+                                                         int switch_tiles) {
+  constexpr long long kCap = 1LL << 30;
+  __shared__ long long wsum[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int carry = 0;
+  long long carry = 0;
   if (tid == 0) cu_t[0] = 0;
   for (int base = 0; base < B; base += 256) {
     const int i = base + tid;
-    int len = 0, tiles = 0;
+    long long tiles = 0;
     if (i < B) {
-      len = seq_lens[i];
+      long long len = cu ? (long long)cu[i + 1] - cu[i] : (long long)seq_lens[i];
       len = len < 1 ? 1 : (len > max_rows ? max_rows : len);
       tiles = (len + 31) / 32;
-      lens[i] = len;
+      lens[i] = (int)len;
     }
-    int incl = tiles;  // inclusive scan inside the wave
+    long long incl = tiles;  // inclusive scan inside the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
+      const long long v = __shfl_up(incl, o, 64);
       if (lane >= o) incl += v;
     }
     if (lane == 63) wsum[w] = incl;
     __syncthreads();
-    int before = carry;
+    long long before = carry;
     for (int u = 0; u < w; ++u) before += wsum[u];
-    if (i < B) cu_t[i + 1] = before + incl;
+    if (i < B) cu_t[i + 1] = (int)min(before + incl, kCap);
     carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
-  if (tid == 0) cu_t[B + 1] = min(G, carry);
+  const long long NT = min(carry, kCap);
+  if (tid == 0) cu_t[B + 1] = (int)min((long long)G, NT);
+  if (!rt) return;
+  __syncthreads();  // cu_t complete
+  // cost of everything before sequence i: cu_t[i] + S i; range k < Ge starts
+  // at cost floor(k C / Ge), C = NT + S B, inside sequence i: at its first
+  // tile while in the sequence's start cost, else after (cost - S) of its
+  // tiles.  Ge = min(G, C) keeps every range at least one cost unit wide, so
+  // only ranges inside a start cost are empty (none lies within a
+  // sequence's tiles); the ranges from Ge on are empty and past the end.
+  const long long S = switch_tiles, C = NT + S * B;
+  const long long Ge = min((long long)G, C);
+  for (int k = tid; k <= G; k += 256) {
+    if (k >= Ge) {
+      rt[k] = (int)NT;
+      continue;
+    }
+    const long long c = (long long)k * C / Ge;
+    int l = 0, r = B - 1;  // the largest i with cu_t[i] + S i <= c
+    while (l < r) {
+      const int mid = (l + r + 1) >> 1;
+      if ((long long)cu_t[mid] + S * mid <= c) l = mid; else r = mid - 1;
+    }
+    const long long off = c - ((long long)cu_t[l] + S * l);
+    const long long t = off < S ? cu_t[l] : min((long long)cu_t[l] + (off - S), (long long)cu_t[l + 1]);
+    rt[k] = (int)t;
+  }
+  __syncthreads();  // rt complete
+  for (int i = tid; i < B; i += 256) {
+    // the range holding tile x: the largest k < G with rt[k] <= x
+    auto range_at = [&](int x) {
+      int l = 0, r = G - 1;
+      while (l < r) {
+        const int mid = (l + r + 1) >> 1;
+        if (rt[mid] <= x) l = mid; else r = mid - 1;
+      }
+      return l;
+    };
+    krange[2 * i] = range_at(cu_t[i]);
+    krange[2 * i + 1] = range_at(cu_t[i + 1] - 1);
+  }
 }
 
 struct DecodePagedArgs {

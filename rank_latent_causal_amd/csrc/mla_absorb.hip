@@ -11,6 +11,7 @@
 #include "common.h"
 #include "backward_bf16.h"
 #include "decode_bf16.h"
+#include "decode_solo.h"
 #include "f32_kernels.h"
 #include "forward_bf16.h"
 #include "gemm_bf16.h"
@@ -140,17 +141,40 @@ template <int DQ, int DV, int R>
 void launch_decode_paged_bf16(const mla::DecodeAbsorbArgs& aa, const int* seq_lens, int max_rows,
                               const mla::DecodePagedArgs& sa, const mla::DecodeMergeArgs& ma, hipStream_t s) {
   constexpr int JC = R < 64 ? R : 64;
-  hipLaunchKernelGGL(mla::mla_paged_prepare, dim3(1), dim3(256), 0, s, seq_lens, sa.B, max_rows, sa.G,
-                     const_cast<int*>(sa.lens), const_cast<int*>(sa.cu_t));
+  hipLaunchKernelGGL(mla::mla_paged_prepare, dim3(1), dim3(256), 0, s, seq_lens, nullptr, sa.B, max_rows, sa.G,
+                     const_cast<int*>(sa.lens), const_cast<int*>(sa.cu_t), nullptr, nullptr, 0);
   hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(aa.H * (R / JC)), dim3(256), 0, s, aa);
   hipLaunchKernelGGL((mla::mla_decode_split_paged<R>), dim3(sa.G), dim3(64 * mla::kDecodeWaves), 0, s, sa);
   hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + mla::kMergeSeqs - 1) / mla::kMergeSeqs) * ma.H),
                      dim3(256), 0, s, ma);
 }
 
+// r = 512: per-sequence tiles, one-wave-per-SIMD split kernel (packed cache:
+// cu != nullptr, paged: seq_lens != nullptr); the merge takes its ranges in
+// tile units from the prepared prefix sums.
+template <int DQ, int DV, int R, bool PAGED>
+void launch_decode_solo(const mla::DecodeAbsorbArgs& aa, const int* seq_lens, const int* cu, int max_rows, int G,
+                        int* krange, const mla::DecodeSoloArgs& sa, mla::DecodeMergeArgs ma, hipStream_t s) {
+  constexpr int JC = R < 64 ? R : 64;
+  hipLaunchKernelGGL(mla::mla_paged_prepare, dim3(1), dim3(256), 0, s, seq_lens, cu, sa.B, max_rows, G,
+                     const_cast<int*>(sa.lens), const_cast<int*>(sa.cu_t), const_cast<int*>(sa.rt), krange,
+                     mla::kDecodeSwitchTiles);
+  hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(aa.H * (R / JC)), dim3(256), 0, s, aa);
+  if (sa.H <= 3 * 32)
+    hipLaunchKernelGGL((mla::mla_decode_solo<R, PAGED, true>), dim3(G), dim3(64 * mla::kDecodeSoloWaves), 0, s, sa);
+  else
+    hipLaunchKernelGGL((mla::mla_decode_solo<R, PAGED, false>), dim3(G), dim3(64 * mla::kDecodeSoloWaves), 0, s, sa);
+  ma.cu = sa.cu_t;
+  ma.n_dev = sa.cu_t + sa.B;
+  ma.N = 0;
+  ma.krange = krange;
+  hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + mla::kMergeSeqs - 1) / mla::kMergeSeqs) * ma.H),
+                     dim3(256), 0, s, ma);
+}
+
 struct PagedDecodeLayout {
   DecodeLayout d;
-  size_t lens = 0, cu_t = 0, total = 0;
+  size_t lens = 0, cu_t = 0, rt = 0, krange = 0, total = 0;
 };
 
 PagedDecodeLayout paged_decode_layout(int B, int H, int r, int G) {
@@ -161,6 +185,10 @@ PagedDecodeLayout paged_decode_layout(int B, int H, int r, int G) {
   off = align_up(off + (size_t)B * sizeof(int));
   L.cu_t = off;
   off = align_up(off + (size_t)(B + 2) * sizeof(int));
+  L.rt = off;
+  off = align_up(off + (size_t)(G + 1) * sizeof(int));
+  L.krange = off;
+  off = align_up(off + (size_t)B * 2 * sizeof(int));
   L.total = off;
   return L;
 }
@@ -604,7 +632,7 @@ size_t mla_absorb_decode_workspace_size(int B, int H, int d_q, int r, int num_sp
   if (dtype != MLA_DTYPE_BF16) return kBadSize;
   int G = num_splits > 0 ? num_splits : device_cu_count();
   if (G <= 0) return kBadSize;
-  return decode_layout(B, H, r, G).total;
+  return paged_decode_layout(B, H, r, G).total;
 }
 
 // Decode over a packed cache with the scratch in the caller's workspace, or
@@ -641,7 +669,8 @@ static mla_status decode_impl(const void* q, const void* c_cache, const int32_t*
   if (H > 16 * mla::kDecodeWaves) return MLA_ERR_UNSUPPORTED;  // 16 heads per wave
   int G = num_splits > 0 ? num_splits : device_cu_count();
   if (G <= 0) return MLA_ERR_HIP;
-  const size_t need = decode_layout(B, H, r, G).total;
+  // the tile prefix sums of the r = 512 path live after the split scratch
+  const size_t need = paged_decode_layout(B, H, r, G).total;
   if (noalloc) {
     if (need > MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
     const mla_status st = scratch_for_current_device(&workspace);
@@ -650,10 +679,27 @@ static mla_status decode_impl(const void* q, const void* c_cache, const int32_t*
   }
   if (!workspace || !aligned16(workspace)) return MLA_ERR_WORKSPACE;
   if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  if (d_q == 128) {
+    const PagedDecodeLayout L = paged_decode_layout(B, H, r, G);
+    mla::DecodeAbsorbArgs aa{};
+    aa.q = (const bf16*)q; aa.wuk = (const bf16*)w_uk; aa.qabs = (bf16*)(ws + L.d.qabs);
+    aa.B = B; aa.H = H; aa.qscale = scale * mla::kLog2e;
+    mla::DecodeSoloArgs sa{};
+    sa.qabs = aa.qabs; sa.cache = (const bf16*)c_cache; sa.cu = cu_seqlens;
+    sa.lens = (const int*)(ws + L.lens); sa.cu_t = (const int*)(ws + L.cu_t); sa.rt = (const int*)(ws + L.rt);
+    sa.part_o = (bf16*)(ws + L.d.part_o); sa.part_ml = (float*)(ws + L.d.part_ml);
+    sa.B = B; sa.H = H; sa.N = (int)total_len;
+    mla::DecodeMergeArgs ma{};
+    ma.part_o = sa.part_o; ma.part_ml = sa.part_ml;
+    ma.wuv = (const bf16*)w_uv; ma.gate = (const bf16*)gate; ma.out = (bf16*)out;
+    ma.B = B; ma.H = H; ma.G = G;
+    launch_decode_solo<128, 128, 512, false>(aa, nullptr, cu_seqlens, (int)total_len, G, (int*)(ws + L.krange), sa, ma, s);
+    return launch_status();
+  }
   // every range must own at least one cache row (the merge relies on it)
   if ((long long)G > total_len) G = (int)total_len;
   const DecodeLayout L = decode_layout(B, H, r, G);
-  char* ws = (char*)workspace;
 
   mla::DecodeAbsorbArgs aa{};
   aa.q = (const bf16*)q; aa.wuk = (const bf16*)w_uk; aa.qabs = (bf16*)(ws + L.qabs);
@@ -667,8 +713,7 @@ static mla_status decode_impl(const void* q, const void* c_cache, const int32_t*
   ma.wuv = (const bf16*)w_uv; ma.gate = (const bf16*)gate; ma.out = (bf16*)out;
   ma.B = B; ma.H = H; ma.G = G; ma.N = total_len;
   if (d_q == 16) launch_decode_bf16<16, 16, 32>(aa, sa, ma, s);
-  else if (d_q == 64) launch_decode_bf16<64, 64, 256>(aa, sa, ma, s);
-  else launch_decode_bf16<128, 128, 512>(aa, sa, ma, s);
+  else launch_decode_bf16<64, 64, 256>(aa, sa, ma, s);
   return launch_status();
 }
 
@@ -724,6 +769,21 @@ mla_status mla_absorb_decode_paged(const void* q, const void* c_pages, const int
   mla::DecodeAbsorbArgs aa{};
   aa.q = (const bf16*)q; aa.wuk = (const bf16*)w_uk; aa.qabs = (bf16*)(ws + L.d.qabs);
   aa.B = B; aa.H = H; aa.qscale = scale * mla::kLog2e;
+  const int max_rows = max_pages * page_size;
+  if (d_q == 128) {
+    mla::DecodeSoloArgs sa{};
+    sa.qabs = aa.qabs; sa.cache = (const bf16*)c_pages; sa.block_table = block_table;
+    sa.lens = (const int*)(ws + L.lens); sa.cu_t = (const int*)(ws + L.cu_t); sa.rt = (const int*)(ws + L.rt);
+    sa.part_o = (bf16*)(ws + L.d.part_o); sa.part_ml = (float*)(ws + L.d.part_ml);
+    sa.B = B; sa.H = H;
+    sa.page_shift = log2_exact(page_size); sa.max_pages = max_pages; sa.num_pages = (int)num_pages;
+    mla::DecodeMergeArgs ma{};
+    ma.part_o = sa.part_o; ma.part_ml = sa.part_ml;
+    ma.wuv = (const bf16*)w_uv; ma.gate = (const bf16*)gate; ma.out = (bf16*)out;
+    ma.B = B; ma.H = H; ma.G = G;
+    launch_decode_solo<128, 128, 512, true>(aa, seq_lens, nullptr, max_rows, G, (int*)(ws + L.krange), sa, ma, s);
+    return launch_status();
+  }
   mla::DecodePagedArgs sa{};
   sa.qabs = aa.qabs; sa.pages = (const bf16*)c_pages; sa.block_table = block_table;
   sa.lens = (const int*)(ws + L.lens); sa.cu_t = (const int*)(ws + L.cu_t);
@@ -734,10 +794,8 @@ mla_status mla_absorb_decode_paged(const void* q, const void* c_pages, const int
   ma.part_o = sa.part_o; ma.part_ml = sa.part_ml; ma.cu = sa.cu_t; ma.n_dev = sa.cu_t + B;
   ma.wuv = (const bf16*)w_uv; ma.gate = (const bf16*)gate; ma.out = (bf16*)out;
   ma.B = B; ma.H = H; ma.G = G; ma.N = 0;
-  const int max_rows = max_pages * page_size;
   if (d_q == 16) launch_decode_paged_bf16<16, 16, 32>(aa, seq_lens, max_rows, sa, ma, s);
-  else if (d_q == 64) launch_decode_paged_bf16<64, 64, 256>(aa, seq_lens, max_rows, sa, ma, s);
-  else launch_decode_paged_bf16<128, 128, 512>(aa, seq_lens, max_rows, sa, ma, s);
+  else launch_decode_paged_bf16<64, 64, 256>(aa, seq_lens, max_rows, sa, ma, s);
   return launch_status();
 }
 

@@ -276,7 +276,10 @@ def test_layer_training_sizes():
 
 def test_paged_decode_workspace_size():
     n = mla.decode_paged_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_BF16)
-    assert n >= mla.decode_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_BF16) + 4 * (2 * 64 + 1)
+    # q_abs, (G+B) partials, then the clamped lengths and tile prefix sums
+    # (B + B + 2 int32), which the packed decode holds as well
+    assert n >= 64 * 96 * 512 * 2 + (256 + 64) * 96 * (512 * 2 + 2 * 4) + 4 * (2 * 64 + 2)
+    assert n == mla.decode_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_BF16)
     with pytest.raises(mla.MLAError):
         mla.decode_paged_workspace_size(64, 96, 128, 512, 256, mla.DTYPE_F32)
 

@@ -214,6 +214,21 @@ def test_decode_long_sequence(o):
     assert_parity(got, oracle_decode(o, d), dg.BF16, "decode long sequence", block=d["d_v"])
 
 
+def test_decode_running_max_rescale(o):
+    """Cache rows that grow from 2% to full size over each sequence's first
+    300 rows, with four times the default scale: inside a workgroup's range
+    the running max moves by more than 8 (log2 units) after the first tiles,
+    so the accumulator rescale runs, and again after each sequence switch."""
+    lens = [3000, 40, 1500]
+    d = dg.decode_inputs(3, 32, 128, 128, 512, dtype=dg.BF16, seed=5350, lengths=lens)
+    u = np.concatenate([np.arange(n) for n in lens]).astype(np.float32)
+    ramp = np.minimum(1.0, 0.02 + u / 300.0)[:, None]
+    d["c_cache"] = dg.f32_to_bf16_bits(dg.as_f32(d["c_cache"]) * ramp)
+    log("decode ramped cache (rescale path), 2 splits")
+    got = to_host_f64(run_decode(d, scale=0.35, num_splits=2))
+    assert_parity(got, oracle_decode(o, d, scale=0.35), dg.BF16, "decode rescale path", block=d["d_v"])
+
+
 def test_side_stream_and_workspace_reuse():
     """Calls enqueued on a non-default stream with a caller workspace reused
     across shapes give the same bits as default-stream calls."""
