@@ -248,6 +248,7 @@ def bench_prefill_workload(torch, mla, name, calls, warmup):
     tf = fl / (ms * 1e-3) / 1e12
     if bf:
         kernel = ("mla_prefill_bf16_kernel<16,16,32>" if r == 32 else
+                  f"mla_prefill_solo_kernel<{dq},{dv},{r}>" if r == 512 else
                   f"mla_prefill_pair_kernel<{dq},{dv},{r}>") + " (+ W_UK transpose in the same call)"
         roof = {"bound": "mfma", "peak": PEAK_BF16_TFLOPS}
     else:
@@ -609,14 +610,14 @@ def main():
     if do_pre:
         res["roofline"] = {"bound": "mfma", "achieved": round(p_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(p_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                           "kernel": "mla_prefill_pair_kernel<128,128,512> (+ W_UK transpose in the same call)", "flop_per_launch": pf,
+                           "kernel": "mla_prefill_solo_kernel<128,128,512> (+ W_UK transpose in the same call)", "flop_per_launch": pf,
                            "ms_per_launch": round(p_ms, 4)}
     if do_dec:
         res["decode"] = {"value": round(d_gbs, 1), "unit": "GB/s", "ms": round(d_ms, 4),
                          "tflops": round(df / (d_ms * 1e-3) / 1e12, 2),
                          "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS,
                                       "unit": "GB/s", "frac": round(d_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                                      "kernel": "mla_decode_split<512> + absorb + merge",
+                                      "kernel": "mla_decode_solo<512> + absorb (with the range table) + merge",
                                       "bytes_per_launch": dbytes}}
     traffic = measured_traffic()
     if traffic is not None:

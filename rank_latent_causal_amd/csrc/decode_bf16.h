@@ -51,6 +51,115 @@ __global__ void __launch_bounds__(256) mla_wuk_transpose(const T* __restrict__ w
   }
 }
 
+// One workgroup (256 threads): clamps the lengths to [1, max_rows] and writes them, the
+// exclusive prefix sums of the tile counts (cu_t[B] = NT) and the number of
+// ranges cu_t[B + 1] = min(G, NT), so that no range is empty (the merge walks
+// every range between a sequence's first and last).  The lengths come from
+// seq_lens, or (cu != nullptr, packed cache) from the row prefix sums
+// cu[i + 1] - cu[i].  The sums run in 64 bits and are capped at 2^30 tiles,
+// which only lengths that break the callers' preconditions reach: the prefix
+// sums stay monotone whatever the lengths, and sequences past the cap get no
+// tiles.
+//
+// With rt != nullptr the G ranges are cut by cost instead: a tile costs 1 and
+// the start of a sequence switch_tiles more (a workgroup that reaches a new
+// sequence stores a partial and loads that sequence's query), so ranges that
+// cross many sequence starts take fewer tiles.  Range k covers tiles
+// [rt[k], rt[k + 1]) (rt[G] = NT; a range may be empty), and krange[2i],
+// krange[2i + 1] are the first and last range holding tiles of sequence i.
+struct PrepareArgs {
+  const int* seq_lens;  // [B] (paged), or
+  const int* cu;        // [B + 1] row prefix sums (packed)
+  int B, max_rows, G;
+  int* lens;            // [B]
+  int* cu_t;            // [B + 2]
+  int* rt;              // [G + 1] or null
+  int* krange;          // [B, 2] (with rt)
+  int switch_tiles;
+};
+
+__device__ __forceinline__ void decode_prepare(const PrepareArgs& pa) {
+  const int* __restrict__ seq_lens = pa.seq_lens;
+  const int* __restrict__ cu = pa.cu;
+  const int B = pa.B, max_rows = pa.max_rows, G = pa.G;
+  int* __restrict__ lens = pa.lens;
+  int* __restrict__ cu_t = pa.cu_t;
+  int* __restrict__ rt = pa.rt;
+  int* __restrict__ krange = pa.krange;
+  const int switch_tiles = pa.switch_tiles;
+  constexpr long long kCap = 1LL << 30;
+  __shared__ long long wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  long long carry = 0;
+  if (tid == 0) cu_t[0] = 0;
+  for (int base = 0; base < B; base += 256) {
+    const int i = base + tid;
+    long long tiles = 0;
+    if (i < B) {
+      long long len = cu ? (long long)cu[i + 1] - cu[i] : (long long)seq_lens[i];
+      len = len < 1 ? 1 : (len > max_rows ? max_rows : len);
+      tiles = (len + 31) / 32;
+      lens[i] = (int)len;
+    }
+    long long incl = tiles;  // inclusive scan inside the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[w] = incl;
+    __syncthreads();
+    long long before = carry;
+    for (int u = 0; u < w; ++u) before += wsum[u];
+    if (i < B) cu_t[i + 1] = (int)min(before + incl, kCap);
+    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  const long long NT = min(carry, kCap);
+  if (tid == 0) cu_t[B + 1] = (int)min((long long)G, NT);
+  if (!rt) return;
+  __syncthreads();  // cu_t complete
+  // cost of everything before sequence i: cu_t[i] + S i; range k < Ge starts
+  // at cost floor(k C / Ge), C = NT + S B, inside sequence i: at its first
+  // tile while in the sequence's start cost, else after (cost - S) of its
+  // tiles.  Ge = min(G, C) keeps every range at least one cost unit wide, so
+  // only ranges inside a start cost are empty (none lies within a
+  // sequence's tiles); the ranges from Ge on are empty and past the end.
+  const long long S = switch_tiles, C = NT + S * B;
+  const long long Ge = min((long long)G, C);
+  for (int k = tid; k <= G; k += 256) {
+    if (k >= Ge) {
+      rt[k] = (int)NT;
+      continue;
+    }
+    const long long c = (long long)k * C / Ge;
+    int l = 0, r = B - 1;  // the largest i with cu_t[i] + S i <= c
+    while (l < r) {
+      const int mid = (l + r + 1) >> 1;
+      if ((long long)cu_t[mid] + S * mid <= c) l = mid; else r = mid - 1;
+    }
+    const long long off = c - ((long long)cu_t[l] + S * l);
+    const long long t = off < S ? cu_t[l] : min((long long)cu_t[l] + (off - S), (long long)cu_t[l + 1]);
+    rt[k] = (int)t;
+  }
+  __syncthreads();  // rt complete
+  for (int i = tid; i < B; i += 256) {
+    // the range holding tile x: the largest k < G with rt[k] <= x
+    auto range_at = [&](int x) {
+      int l = 0, r = G - 1;
+      while (l < r) {
+        const int mid = (l + r + 1) >> 1;
+        if (rt[mid] <= x) l = mid; else r = mid - 1;
+      }
+      return l;
+    };
+    krange[2 * i] = range_at(cu_t[i]);
+    krange[2 * i + 1] = range_at(cu_t[i + 1] - 1);
+  }
+}
+
+__global__ void __launch_bounds__(256) mla_paged_prepare(PrepareArgs pa) { decode_prepare(pa); }
+
 // ----------------------------------------------------------------- absorb
 struct DecodeAbsorbArgs {
   const bf16* q;    // [B, H, DQ]
@@ -58,14 +167,18 @@ struct DecodeAbsorbArgs {
   bf16* qabs;       // [B, H, R]
   int B, H;
   float qscale;
+  int with_prep;    // the last workgroup runs decode_prepare(prep) instead
+  PrepareArgs prep;
 };
 
 // Workgroup (head h, latent columns [J0, J0 + JC)), 4 waves; wave w owns the
-// 16 latent columns J0 + 16w .. and walks the sequences 16 at a time:
-// q_abs^T[j, i] = sum_d W_UK[h, d, j] q[i, h, d] on MFMA.  The W_UK slice
-// [DQ x JC] is staged in LDS as stored (d-major); the A operand (row j,
-// 8 consecutive d) comes from two transposing ds_read_b64_tr_b16 reads.
-// Output rows are stored in the plain [B, H, R] layout, scaled by qscale.
+// 16 latent columns J0 + 16w .. and walks the sequences 64 at a time (the
+// queries of all 64 in flight together, the first 64 before the W_UK slice
+// is staged): q_abs^T[j, i] = sum_d W_UK[h, d, j] q[i, h, d] on MFMA.  The
+// W_UK slice [DQ x JC] is staged in LDS as stored (d-major); the A operand
+// (row j, 8 consecutive d) comes from two transposing ds_read_b64_tr_b16
+// reads.  Output rows are stored in the plain [B, H, R] layout, scaled by
+// qscale.
 template <int DQ, int R>
 __global__ void __launch_bounds__(256) mla_decode_absorb(DecodeAbsorbArgs a) {
   constexpr int JC = R < 64 ? R : 64;    // latent columns per workgroup
@@ -73,18 +186,35 @@ __global__ void __launch_bounds__(256) mla_decode_absorb(DecodeAbsorbArgs a) {
   constexpr int NK = DP / 32;
   constexpr int LD = JC + 8;             // padded row (elements): spreads the tr16 rows over banks
   static_assert(R % JC == 0 && JC % 16 == 0 && DQ % 8 == 0, "absorb tiling");
+  constexpr int IT = 4;                  // 16-sequence blocks in flight
   __shared__ __attribute__((aligned(16))) bf16 wt[DP][LD];
+  if (a.with_prep && blockIdx.x == gridDim.x - 1) {
+    decode_prepare(a.prep);
+    return;
+  }
   const int h = blockIdx.x / (R / JC), J0 = (blockIdx.x % (R / JC)) * JC;
   const bf16* __restrict__ src = a.wuk + (size_t)h * DQ * R + J0;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  bf16x8 bq[IT][NK];
+  auto load_q = [&](int i00) {
+#pragma unroll
+    for (int t = 0; t < IT; ++t) {
+      const int i = i00 + 16 * t + l16;
+      const bf16* qrow = a.q + ((size_t)(i < a.B ? i : a.B - 1) * a.H + h) * DQ;
+#pragma unroll
+      for (int k = 0; k < NK; ++k)
+        bq[t][k] = (32 * k + 8 * kq < DQ) ? *(const bf16x8*)(qrow + 32 * k + 8 * kq) : bf16x8{};
+    }
+  };
+  load_q(0);
   for (int e = threadIdx.x; e < DP * JC / 8; e += 256) {
     const int d = e / (JC / 8), j8 = e % (JC / 8);
     const bf16x8 v = d < DQ ? *(const bf16x8*)(src + (size_t)d * R + 8 * j8) : bf16x8{};
     *(bf16x8*)&wt[d][8 * j8] = v;
   }
   __syncthreads();
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (16 * w >= JC) return;
-  const int l16 = lane & 15, kq = lane >> 4;
   const int e4 = l16 >> 2, q4 = l16 & 3;
   bf16x8 af[NK];
 #pragma unroll
@@ -93,22 +223,23 @@ __global__ void __launch_bounds__(256) mla_decode_absorb(DecodeAbsorbArgs a) {
     af[k] = cat4(lds_read_tr16((const MLA_LDS char*)&wt[d][16 * w + 4 * q4]),
                  lds_read_tr16((const MLA_LDS char*)&wt[d + 4][16 * w + 4 * q4]));
   }
-  for (int i0 = 0; i0 < a.B; i0 += 16) {
-    const int i = i0 + l16;
-    const bool ok = i < a.B;
-    const bf16* qrow = a.q + ((size_t)(ok ? i : a.B - 1) * a.H + h) * DQ;
-    f32x4 acc = f32x4{};
+  for (int i00 = 0;;) {
 #pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      const bf16x8 bq = (32 * k + 8 * kq < DQ) ? *(const bf16x8*)(qrow + 32 * k + 8 * kq) : bf16x8{};
-      acc = mfma16(af[k], bq, acc);
-    }
-    if (ok) {
-      bf16x4 v;
+    for (int t = 0; t < IT; ++t) {
+      const int i = i00 + 16 * t + l16;
+      f32x4 acc = f32x4{};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[e] * a.qscale);
-      *(bf16x4*)(a.qabs + ((size_t)i * a.H + h) * R + J0 + 16 * w + 4 * kq) = v;
+      for (int k = 0; k < NK; ++k) acc = mfma16(af[k], bq[t][k], acc);
+      if (i < a.B) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[e] * a.qscale);
+        *(bf16x4*)(a.qabs + ((size_t)i * a.H + h) * R + J0 + 16 * w + 4 * kq) = v;
+      }
     }
+    i00 += 16 * IT;
+    if (i00 >= a.B) break;
+    load_q(i00);
   }
 }
 
@@ -431,98 +562,6 @@ __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
 // k of G covers tiles [floor(k NT / G), floor((k+1) NT / G)), and a tile
 // belongs to exactly one sequence.  Partial slots, the merge and its
 // range arithmetic are those of the packed decode, in tile units.
-
-// One workgroup: clamps the lengths to [1, max_rows] and writes them, the
-// exclusive prefix sums of the tile counts (cu_t[B] = NT) and the number of
-// ranges cu_t[B + 1] = min(G, NT), so that no range is empty (the merge walks
-// every range between a sequence's first and last).  The lengths come from
-// seq_lens, or (cu != nullptr, packed cache) from the row prefix sums
-// cu[i + 1] - cu[i].  The sums run in 64 bits and are capped at 2^30 tiles,
-// which only lengths that break the callers' preconditions reach: the prefix
-// sums stay monotone whatever the lengths, and sequences past the cap get no
-// tiles.
-//
-// With rt != nullptr the G ranges are cut by cost instead: a tile costs 1 and
-// the start of a sequence switch_tiles more (a workgroup that reaches a new
-// sequence stores a partial and loads that sequence's query), so ranges that
-// cross many sequence starts take fewer tiles.  Range k covers tiles
-// [rt[k], rt[k + 1]) (rt[G] = NT; a range may be empty), and krange[2i],
-// krange[2i + 1] are the first and last range holding tiles of sequence i.
-__global__ void __launch_bounds__(256) mla_paged_prepare(const int* __restrict__ seq_lens,
-                                                         const int* __restrict__ cu, int B, int max_rows,
-                                                         int G, int* __restrict__ lens, int* __restrict__ cu_t,
-                                                         int* __restrict__ rt, int* __restrict__ krange,
-                                                         int switch_tiles) {
-  constexpr long long kCap = 1LL << 30;
-  __shared__ long long wsum[4];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  long long carry = 0;
-  if (tid == 0) cu_t[0] = 0;
-  for (int base = 0; base < B; base += 256) {
-    const int i = base + tid;
-    long long tiles = 0;
-    if (i < B) {
-      long long len = cu ? (long long)cu[i + 1] - cu[i] : (long long)seq_lens[i];
-      len = len < 1 ? 1 : (len > max_rows ? max_rows : len);
-      tiles = (len + 31) / 32;
-      lens[i] = (int)len;
-    }
-    long long incl = tiles;  // inclusive scan inside the wave
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const long long v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    if (lane == 63) wsum[w] = incl;
-    __syncthreads();
-    long long before = carry;
-    for (int u = 0; u < w; ++u) before += wsum[u];
-    if (i < B) cu_t[i + 1] = (int)min(before + incl, kCap);
-    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-  }
-  const long long NT = min(carry, kCap);
-  if (tid == 0) cu_t[B + 1] = (int)min((long long)G, NT);
-  if (!rt) return;
-  __syncthreads();  // cu_t complete
-  // cost of everything before sequence i: cu_t[i] + S i; range k < Ge starts
-  // at cost floor(k C / Ge), C = NT + S B, inside sequence i: at its first
-  // tile while in the sequence's start cost, else after (cost - S) of its
-  // tiles.  Ge = min(G, C) keeps every range at least one cost unit wide, so
-  // only ranges inside a start cost are empty (none lies within a
-  // sequence's tiles); the ranges from Ge on are empty and past the end.
-  const long long S = switch_tiles, C = NT + S * B;
-  const long long Ge = min((long long)G, C);
-  for (int k = tid; k <= G; k += 256) {
-    if (k >= Ge) {
-      rt[k] = (int)NT;
-      continue;
-    }
-    const long long c = (long long)k * C / Ge;
-    int l = 0, r = B - 1;  // the largest i with cu_t[i] + S i <= c
-    while (l < r) {
-      const int mid = (l + r + 1) >> 1;
-      if ((long long)cu_t[mid] + S * mid <= c) l = mid; else r = mid - 1;
-    }
-    const long long off = c - ((long long)cu_t[l] + S * l);
-    const long long t = off < S ? cu_t[l] : min((long long)cu_t[l] + (off - S), (long long)cu_t[l + 1]);
-    rt[k] = (int)t;
-  }
-  __syncthreads();  // rt complete
-  for (int i = tid; i < B; i += 256) {
-    // the range holding tile x: the largest k < G with rt[k] <= x
-    auto range_at = [&](int x) {
-      int l = 0, r = G - 1;
-      while (l < r) {
-        const int mid = (l + r + 1) >> 1;
-        if (rt[mid] <= x) l = mid; else r = mid - 1;
-      }
-      return l;
-    };
-    krange[2 * i] = range_at(cu_t[i]);
-    krange[2 * i + 1] = range_at(cu_t[i + 1] - 1);
-  }
-}
 
 struct DecodePagedArgs {
   const bf16* qabs;         // [B, H, R]

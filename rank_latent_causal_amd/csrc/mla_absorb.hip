@@ -141,8 +141,9 @@ template <int DQ, int DV, int R>
 void launch_decode_paged_bf16(const mla::DecodeAbsorbArgs& aa, const int* seq_lens, int max_rows,
                               const mla::DecodePagedArgs& sa, const mla::DecodeMergeArgs& ma, hipStream_t s) {
   constexpr int JC = R < 64 ? R : 64;
-  hipLaunchKernelGGL(mla::mla_paged_prepare, dim3(1), dim3(256), 0, s, seq_lens, nullptr, sa.B, max_rows, sa.G,
-                     const_cast<int*>(sa.lens), const_cast<int*>(sa.cu_t), nullptr, nullptr, 0);
+  mla::PrepareArgs pa{seq_lens, nullptr, sa.B, max_rows, sa.G, const_cast<int*>(sa.lens), const_cast<int*>(sa.cu_t),
+                      nullptr, nullptr, 0};
+  hipLaunchKernelGGL(mla::mla_paged_prepare, dim3(1), dim3(256), 0, s, pa);
   hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(aa.H * (R / JC)), dim3(256), 0, s, aa);
   hipLaunchKernelGGL((mla::mla_decode_split_paged<R>), dim3(sa.G), dim3(64 * mla::kDecodeWaves), 0, s, sa);
   hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + mla::kMergeSeqs - 1) / mla::kMergeSeqs) * ma.H),
@@ -153,13 +154,14 @@ void launch_decode_paged_bf16(const mla::DecodeAbsorbArgs& aa, const int* seq_le
 // cu != nullptr, paged: seq_lens != nullptr); the merge takes its ranges in
 // tile units from the prepared prefix sums.
 template <int DQ, int DV, int R, bool PAGED>
-void launch_decode_solo(const mla::DecodeAbsorbArgs& aa, const int* seq_lens, const int* cu, int max_rows, int G,
+void launch_decode_solo(mla::DecodeAbsorbArgs aa, const int* seq_lens, const int* cu, int max_rows, int G,
                         int* krange, const mla::DecodeSoloArgs& sa, mla::DecodeMergeArgs ma, hipStream_t s) {
   constexpr int JC = R < 64 ? R : 64;
-  hipLaunchKernelGGL(mla::mla_paged_prepare, dim3(1), dim3(256), 0, s, seq_lens, cu, sa.B, max_rows, G,
-                     const_cast<int*>(sa.lens), const_cast<int*>(sa.cu_t), const_cast<int*>(sa.rt), krange,
-                     mla::kDecodeSwitchTiles);
-  hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(aa.H * (R / JC)), dim3(256), 0, s, aa);
+  // the absorb's last workgroup prepares the tile sums and the range table
+  aa.with_prep = 1;
+  aa.prep = mla::PrepareArgs{seq_lens, cu, sa.B, max_rows, G, const_cast<int*>(sa.lens), const_cast<int*>(sa.cu_t),
+                             const_cast<int*>(sa.rt), krange, mla::kDecodeSwitchTiles};
+  hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(aa.H * (R / JC) + 1), dim3(256), 0, s, aa);
   if (sa.H <= 3 * 32)
     hipLaunchKernelGGL((mla::mla_decode_solo<R, PAGED, true>), dim3(G), dim3(64 * mla::kDecodeSoloWaves), 0, s, sa);
   else
