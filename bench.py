@@ -248,8 +248,7 @@ def bench_prefill_workload(torch, mla, name, calls, warmup):
     tf = fl / (ms * 1e-3) / 1e12
     if bf:
         kernel = ("mla_prefill_bf16_kernel<16,16,32>" if r == 32 else
-                  f"mla_prefill_solo_kernel<{dq},{dv},{r}>" if r == 512 else
-                  f"mla_prefill_pair_kernel<{dq},{dv},{r}>") + " (+ W_UK transpose in the same call)"
+                  f"mla_prefill_solo_kernel<{dq},{dv},{r}>") + " (+ W_UK transpose in the same call)"
         roof = {"bound": "mfma", "peak": PEAK_BF16_TFLOPS}
     else:
         kernel = "mla_f32_kernel"

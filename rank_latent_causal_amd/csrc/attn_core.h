@@ -368,222 +368,3 @@ __device__ __forceinline__ void project_gate_store(const f32x4 (&oT)[R / 16], fl
 }
 
 }  // namespace mla
-
-namespace mla {
-
-// ---------------------------------------------------------------------------
-// Wave-pair variant: two waves share 32 query columns (two 16-column groups)
-// and split the latent dimension r in halves.  Each latent operand read from
-// LDS then feeds two MFMAs (one per column group), halving LDS traffic per
-// FLOP, while each wave still holds only a [r/2 x 32] O^T accumulator.  The
-// score needs the full r, so the pair adds its two partial S^T tiles through
-// LDS once per key tile; both waves then run the same softmax.
-// ---------------------------------------------------------------------------
-
-// q_abs^T for two 16-row column groups, latent dims [jbase, jbase + R/2).
-template <int DQ, int R>
-__device__ __forceinline__ void absorb_pair(const bf16* __restrict__ qrow0, const bf16* __restrict__ qrow1,
-                                            const bf16* __restrict__ wkT, int jbase, float qscale, int l16,
-                                            int kq, bf16x8 (&qT)[2][R / 64]) {
-  constexpr int NKQ = (DQ + 31) / 32;
-  bf16x8 qb[2][NKQ];
-#pragma unroll
-  for (int k = 0; k < NKQ; ++k) {
-    const bool ok = 32 * k + 8 * kq < DQ;
-    qb[0][k] = ok ? *(const bf16x8*)(qrow0 + 32 * k + 8 * kq) : bf16x8{};
-    qb[1][k] = ok ? *(const bf16x8*)(qrow1 + 32 * k + 8 * kq) : bf16x8{};
-  }
-#pragma unroll
-  for (int kk = 0; kk < R / 64; ++kk) {
-    f32x4 acc[2][2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      // A row rho loads latent dim jbase + 32kk + 8(rho/4) + 4u + rho%4, so C
-      // row 4kq + e of this fragment is dim jbase + 32kk + 8kq + 4u + e
-      const int j = jbase + 32 * kk + 8 * (l16 >> 2) + 4 * u + (l16 & 3);
-      const bf16* wrow = wkT + (size_t)j * DQ;
-      acc[0][u] = f32x4{};
-      acc[1][u] = f32x4{};
-#pragma unroll
-      for (int k = 0; k < NKQ; ++k) {
-        const bf16x8 av = (32 * k + 8 * kq < DQ) ? *(const bf16x8*)(wrow + 32 * k + 8 * kq) : bf16x8{};
-        acc[0][u] = mfma16(av, qb[0][k], acc[0][u]);
-        acc[1][u] = mfma16(av, qb[1][k], acc[1][u]);
-      }
-    }
-    qT[0][kk] = pack44(acc[0][0], acc[0][1], qscale);
-    qT[1][kk] = pack44(acc[1][0], acc[1][1], qscale);
-  }
-}
-
-// SPF: score operands of k-step kk+1 are read from LDS while the MFMAs of
-// k-step kk run; VPF > 0: value operands run VPF tiles ahead.  Without them,
-// QCH / VCH k-steps / value tiles form one chunk (its LDS reads, then its
-// MFMAs).  One step of each lookahead measured +2.4% apiece on the full-width
-// prefill; two value tiles ahead no longer fit the registers.
-template <int R, int QCH = 1, int VCH = 4, bool SPF = true, int VPF = 1>
-struct PairAttn {
-  static constexpr int RH = R / 2;     // latent dims owned by this wave
-  static constexpr int NKK = RH / 32;  // score k-steps
-  static constexpr int NJT = RH / 16;  // value tiles
-  static constexpr int ROWB = R * 2;
-  static_assert(R / 8 >= 16 && NKK % 4 == 0 && NJT % 8 == 0, "pair split needs r >= 256");
-  bf16x8 qT[2][NKK];
-  f32x4 oT[2][NJT];
-  float m_run[2], l_run[2];
-  // Operand addresses (latent half folded in): the score operand of k-step kk
-  // is qkb[kk & 3] + 256 (kk >> 2), the value operand of tile t is
-  // trb[t & 7] + 256 (t >> 3); the immediates fold into the ds_read offsets.
-  int qkb[4], trb[8];
-
-  __device__ __forceinline__ void init_addressing(int l16, int kq, int jh) {
-    const int x = chunk_swizzle<R>(l16);
-    const int qk_base = l16 * ROWB + (((kq ^ x) & 3) << 4) + jh * RH * 2;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) qkb[u] = qk_base + ((u ^ (x >> 2)) << 6);
-    const int r = 4 * kq + (l16 >> 2), q = l16 & 3;
-    const int xr = chunk_swizzle<R>(r);
-    const int tr_base = r * ROWB + (((q >> 1) ^ (xr & 1)) << 4) + (q & 1) * 8 + jh * RH * 2;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) trb[u] = tr_base + ((u ^ (xr >> 1)) << 5);
-  }
-
-  __device__ __forceinline__ void reset() {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int t = 0; t < NJT; ++t) oT[c][t] = f32x4{};
-      m_run[c] = -INFINITY;
-      l_run[c] = 0.0f;
-    }
-  }
-
-  // Partial S^T over this wave's latent half: s[cg][u] holds keys
-  // [16u, 16u+16) of the tile for column group cg.
-  // hook(k0) runs after the chunk that starts at k-step k0 (used to spread
-  // the next tile's copies over the score products).
-  template <typename Hook>
-  __device__ __forceinline__ void partial_scores(const MLA_LDS char* tile, f32x4 (&s)[2][2], Hook&& hook) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) s[c][0] = s[c][1] = f32x4{};
-    // Launder the 4 bases in place each tile: the compiler then cannot hoist
-    // 16 base + offset sums out of the loop (they would stay live and
-    // spill), and every address is one base plus a ds_read immediate.
-    asm volatile("" : "+v"(qkb[0]), "+v"(qkb[1]), "+v"(qkb[2]), "+v"(qkb[3]));
-    const int* bq = qkb;
-    if constexpr (SPF) {
-      // operands of k-step kk+1 are read while the MFMAs of k-step kk run
-      bf16x8 a0 = lds_read_b128(tile + bq[0]);
-      bf16x8 a1 = lds_read_b128(tile + bq[0] + 16 * ROWB);
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        bf16x8 n0 = a0, n1 = a1;
-        if (kk + 1 < NKK) {
-          const MLA_LDS char* p = tile + bq[(kk + 1) & 3] + ((kk + 1) >> 2) * 256;
-          n0 = lds_read_b128(p);
-          n1 = lds_read_b128(p + 16 * ROWB);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        s[0][0] = mfma16(a0, qT[0][kk], s[0][0]);
-        s[1][0] = mfma16(a0, qT[1][kk], s[1][0]);
-        s[0][1] = mfma16(a1, qT[0][kk], s[0][1]);
-        s[1][1] = mfma16(a1, qT[1][kk], s[1][1]);
-        __builtin_amdgcn_sched_barrier(0);
-        hook(kk);
-        a0 = n0;
-        a1 = n1;
-      }
-    } else {
-#pragma unroll
-    for (int k0 = 0; k0 < NKK; k0 += QCH) {
-#pragma unroll
-      for (int kk = k0; kk < k0 + QCH; ++kk) {
-        const MLA_LDS char* p = tile + bq[kk & 3] + (kk >> 2) * 256;
-        const bf16x8 a0 = lds_read_b128(p);
-        const bf16x8 a1 = lds_read_b128(p + 16 * ROWB);
-        s[0][0] = mfma16(a0, qT[0][kk], s[0][0]);
-        s[1][0] = mfma16(a0, qT[1][kk], s[1][0]);
-        s[0][1] = mfma16(a1, qT[0][kk], s[0][1]);
-        s[1][1] = mfma16(a1, qT[1][kk], s[1][1]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      hook(k0);
-    }
-    }
-  }
-
-  // Online softmax of both column groups over the full (masked, log2-domain)
-  // scores; returns P^T as the value product's B operands.
-  __device__ __forceinline__ void softmax(const f32x4 (&s)[2][2], bf16x8 (&pB)[2]) {
-    float mx[2];
-    bool need[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const f32x4& a = s[c][0];
-      const f32x4& b = s[c][1];
-      mx[c] = col_max(max8_nn(a, b));
-      need[c] = mx[c] > m_run[c] + 8.0f;
-    }
-    if (__builtin_amdgcn_ballot_w64(need[0] || need[1])) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const float m_new = need[c] ? mx[c] : m_run[c];
-        const float alpha = fast_exp2(m_run[c] - m_new);
-        l_run[c] *= alpha;
-#pragma unroll
-        for (int t = 0; t < NJT; ++t) oT[c][t] *= alpha;
-        m_run[c] = m_new;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      f32x4 p0, p1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p0[e] = fast_exp2(s[c][0][e] - m_run[c]);
-        p1[e] = fast_exp2(s[c][1][e] - m_run[c]);
-      }
-      l_run[c] += (p0[0] + p0[1]) + (p0[2] + p0[3]) + (p1[0] + p1[1]) + (p1[2] + p1[3]);
-      pB[c] = pack44(p0, p1, 1.0f);
-    }
-  }
-
-  __device__ __forceinline__ bf16x8 value_operand(const MLA_LDS char* tile, int t) const {
-    const MLA_LDS char* p = tile + trb[t & 7] + (t >> 3) * 256;
-    return cat4(lds_read_tr16(p), lds_read_tr16(p + 16 * ROWB));
-  }
-
-  // Value accumulation of this wave's latent half: O^T += c_tile^T P^T.
-  __device__ __forceinline__ void values(const MLA_LDS char* tile, const bf16x8 (&pB)[2]) {
-    asm volatile("" : "+v"(trb[0]), "+v"(trb[1]), "+v"(trb[2]), "+v"(trb[3]), "+v"(trb[4]), "+v"(trb[5]),
-                      "+v"(trb[6]), "+v"(trb[7]));  // as in partial_scores
-    if constexpr (VPF > 0) {
-      // operands of value tiles t+1 .. t+VPF are read while the MFMAs of
-      // tile t run
-      bf16x8 a[VPF + 1];
-#pragma unroll
-      for (int u = 0; u < VPF; ++u) a[u] = value_operand(tile, u);
-#pragma unroll
-      for (int t = 0; t < NJT; ++t) {
-        if (t + VPF < NJT) a[(t + VPF) % (VPF + 1)] = value_operand(tile, t + VPF);
-        __builtin_amdgcn_sched_barrier(0);
-        oT[0][t] = mfma16(a[t % (VPF + 1)], pB[0], oT[0][t]);
-        oT[1][t] = mfma16(a[t % (VPF + 1)], pB[1], oT[1][t]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-#pragma unroll
-      for (int t0 = 0; t0 < NJT; t0 += VCH) {
-#pragma unroll
-        for (int t = t0; t < t0 + VCH; ++t) {
-          const bf16x8 a = value_operand(tile, t);
-          oT[0][t] = mfma16(a, pB[0], oT[0][t]);
-          oT[1][t] = mfma16(a, pB[1], oT[1][t]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-};
-
-}  // namespace mla

@@ -97,27 +97,16 @@ DecodeLayout decode_layout(int B, int H, int r, int G) {
   return L;
 }
 
-// r = 512: one wave per SIMD owns a head's 32 positions over the whole
-// latent; r = 256: wave pairs split r; r = 32: one wave per (head, 16
-// positions).
+// r >= 256: one wave per SIMD owns a head's 32 positions over the whole
+// latent; r = 32: one wave per (head, 16 positions).
 template <int DQ, int DV, int R, bool PAGED = false>
 void launch_prefill_bf16(mla::PrefillArgs a, hipStream_t s) {
-  if constexpr (R == 512) {
+  if constexpr (R >= 256) {
     a.ntb = (a.T + mla::kSoloRows - 1) / mla::kSoloRows;
     a.nhg = a.H;  // one head per workgroup
     a.xcd_remap = (a.nhg % 8) == 0 ? 1 : 0;
     hipLaunchKernelGGL((mla::mla_prefill_solo_kernel<DQ, DV, R, PAGED>), dim3(a.B * a.ntb * a.nhg),
                        dim3(64 * mla::kSoloWaves), 0, s, a);
-  } else if constexpr (R >= 256) {
-    // Two 4-wave workgroups per CU (80 KiB of LDS each), one tile of
-    // lookahead.  One 8-wave workgroup with 3 or 4 stages measured 8% slower:
-    // two independent workgroups overlap their phases better.
-    constexpr int NW = 4, NS = 2;
-    a.ntb = (a.T + 31) / 32;
-    a.nhg = (a.H + NW / 2 - 1) / (NW / 2);
-    a.xcd_remap = (a.nhg % 8) == 0 ? 1 : 0;
-    hipLaunchKernelGGL((mla::mla_prefill_pair_kernel<DQ, DV, R, NW, NS, PAGED>), dim3(a.B * a.ntb * a.nhg),
-                       dim3(64 * NW), 0, s, a);
   } else {
     a.ntb = (a.T + mla::kPrefillRows - 1) / mla::kPrefillRows;
     a.nhg = (a.H + 3) / 4;
@@ -338,22 +327,15 @@ void launch_backward_bf16(const mla::BwdPrepArgs& pa, const mla::BwdArgs& ba, co
 template <int DQ, int DV, int R>
 void launch_varlen_bf16(mla::PrefillArgs a, const int* cu_q, const int* seq_lens, int Nq, int max_rows,
                         hipStream_t s) {
-  constexpr bool PAIR = R >= 256;
-  constexpr int BR = R == 512 ? mla::kSoloRows : PAIR ? 32 : mla::kPrefillRows;
+  constexpr int BR = R >= 256 ? mla::kSoloRows : mla::kPrefillRows;
   const int max_blocks = (Nq + BR - 1) / BR + a.B;
   hipLaunchKernelGGL(mla::mla_varlen_prepare, dim3(1), dim3(256), 0, s, cu_q, seq_lens, a.B, Nq, max_rows, BR,
                      max_blocks, const_cast<int4*>(a.seq), const_cast<int2*>(a.blocks), const_cast<int*>(a.nblocks));
-  if constexpr (R == 512) {
+  if constexpr (R >= 256) {
     a.nhg = a.H;  // one head per workgroup
     a.xcd_remap = 0;
     hipLaunchKernelGGL((mla::mla_prefill_solo_kernel<DQ, DV, R, true, true>), dim3(max_blocks * a.nhg),
                        dim3(64 * mla::kSoloWaves), 0, s, a);
-  } else if constexpr (PAIR) {
-    constexpr int NW = 4, NS = 2;
-    a.nhg = (a.H + NW / 2 - 1) / (NW / 2);
-    a.xcd_remap = 0;
-    hipLaunchKernelGGL((mla::mla_prefill_pair_kernel<DQ, DV, R, NW, NS, true, true>), dim3(max_blocks * a.nhg),
-                       dim3(64 * NW), 0, s, a);
   } else {
     a.nhg = (a.H + 3) / 4;
     a.xcd_remap = 0;

@@ -1,16 +1,19 @@
-// Fused bf16 prefill kernel for the absorbed Gated MLA layer on gfx950.
+// bf16 prefill pieces for the absorbed Gated MLA layer on gfx950: the
+// kernel arguments, the varlen block list, the key-tile copies that every
+// prefill kernel uses, and the prefill kernel for narrow latents (r = 32; the
+// one-wave-per-SIMD kernel of prefill_solo.h covers r >= 256).
 //
-// One workgroup = 8 waves = a block of 32 query positions x 4 heads (two
-// 16-row halves per head).  Each wave runs the whole chain of page
-// "Gated MLA（矩阵吸收版）", section 完整计算流（四步） steps 2-4 (the same
-// contractions are listed in page "符号表", section Einsum 速查) for its rows:
+// mla_prefill_bf16_kernel: one workgroup = 4 waves = 16 query positions x 4
+// heads; each wave runs the whole chain of page "Gated MLA（矩阵吸收版）",
+// section 完整计算流（四步） steps 2-4 (the same contractions are listed in
+// page "符号表", section Einsum 速查) for its rows:
 //   prologue  q_abs^T = W_UK[h]^T q^T on MFMA, kept in VGPRs (absorb)
 //   main loop causal latent flash attention over 32-key tiles of c
 //   epilogue  o^T = W_UV[h] (O^T / l) on MFMA, sigmoid gate, store
 // Every latent tile is copied once from global memory straight into LDS
-// (global_load_lds, no register staging) and shared by the eight waves,
-// i.e. by 4 heads x 32 positions: heads are folded into the rows that reuse
-// one c tile.  Two LDS stages let the copy of tile n+1 overlap tile n.
+// (LDS-DMA, no register staging) and shared by the four heads: heads are
+// folded into the rows that reuse one c tile.  Two LDS stages let the copy
+// of tile n+1 overlap tile n.
 #pragma once
 
 #include <type_traits>
@@ -227,225 +230,6 @@ mla_prefill_bf16_kernel(PrefillArgs a) {
   const size_t orow = (qr0 + tc) * (size_t)H * DV + (size_t)hc * DV;
   project_gate_store<DV, R>(st.oT, inv_l, a.wuv + (size_t)hc * DV * R, a.gate + orow, a.out + orow,
                             tvalid && hvalid, l16, kq);
-}
-
-// ---------------------------------------------------------------------------
-// Wave-pair prefill for r >= 256: one workgroup = NW waves = NW/2 heads x a
-// block of 32 positions.  Waves (2p, 2p+1) serve head (NW/2) hg + p, both
-// 16-row column groups, and latent halves 0 / 1.  Per 32-key tile: partial
-// scores over the wave's half, exchange through LDS, full causal softmax
-// (identical in both waves), values of the wave's half.  The epilogue adds
-// the two halves' W_UV products through LDS before the gate.  NS LDS stages
-// keep NS - 1 tiles in flight; every c tile is copied once per workgroup and
-// serves its NW/2 heads.
-// ---------------------------------------------------------------------------
-template <int R, int NW, int NS>
-struct PairConfig {
-  static constexpr int XBUF = NW * 4 * 64 * 16;                  // partial-score exchange
-  static constexpr int LDS = NS * LatentTile<R>::BYTES + XBUF;   // bytes per workgroup
-};
-
-template <int DQ, int DV, int R, int NW, int NS, bool PAGED = false, bool VARLEN = false>
-__global__ void __launch_bounds__(64 * NW)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
-mla_prefill_pair_kernel(PrefillArgs a) {
-  using LT = LatentTile<R>;
-  using PA = PairAttn<R>;
-  using CFG = PairConfig<R, NW, NS>;
-  constexpr int CPW = copies_per_wave<R>(NW);
-  constexpr int NV = DV / 16;
-  constexpr int HPW = NW / 2;  // heads per workgroup
-  static_assert(NW % 2 == 0 && NS >= 2, "pairs and at least two stages");
-  static_assert(LT::COPIES % NW == 0, "copy split");
-  static_assert(DQ % 16 == 0 && DV % 16 == 0, "shape");
-  static_assert((NS - 2) * CPW < 64, "vmcnt range");
-  // epilogue partials of o^T reuse the stage and exchange memory
-  static_assert(NW * NV * 2 * 1024 <= CFG::LDS, "epilogue exchange fits the LDS");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[CFG::LDS];
-  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
-  f32x4* xbuf = (f32x4*)(smem_raw + NS * LT::BYTES);  // [wave][4][lane]
-
-  // ---- work item (32 positions x NW/2 heads), heaviest query blocks first
-  const int x = blockIdx.x;
-  int tb, b, hg;
-  if constexpr (VARLEN) {
-    hg = x % a.nhg;
-    const int i = x / a.nhg;
-    if (i >= __builtin_amdgcn_readfirstlane(*a.nblocks)) return;  // the whole workgroup
-    const int2 e = a.blocks[i];
-    b = __builtin_amdgcn_readfirstlane(e.x);
-    tb = __builtin_amdgcn_readfirstlane(e.y);
-  } else if (a.xcd_remap) {
-    const int xcd = x & 7, pos = x >> 3, nh8 = a.nhg >> 3;
-    hg = (pos % nh8) * 8 + xcd;
-    const int rest = pos / nh8;
-    b = rest % a.B;
-    tb = a.ntb - 1 - rest / a.B;
-  } else {
-    hg = x % a.nhg;
-    const int rest = x / a.nhg;
-    b = rest % a.B;
-    tb = a.ntb - 1 - rest / a.B;
-  }
-
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int l16 = lane & 15, kq = lane >> 4;
-  const int jh = w & 1, partner = w ^ 1;
-  const int h = hg * HPW + (w >> 1);
-  const bool hvalid = h < a.H;
-  const int hc = hvalid ? h : a.H - 1;
-  const int H = a.H;
-  int T = a.T, S = a.S;
-  size_t qr0 = (size_t)b * a.T;  // packed row of query 0 of sequence b
-  if constexpr (VARLEN) {
-    const int4 sq = a.seq[b];
-    qr0 = (size_t)__builtin_amdgcn_readfirstlane(sq.x);
-    T = __builtin_amdgcn_readfirstlane(sq.y);
-    S = __builtin_amdgcn_readfirstlane(sq.z);
-  }
-  const int t0 = tb * 32;
-  int tq[2];
-  bool tv[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    tq[c] = t0 + 16 * c + l16;
-    tv[c] = tq[c] < T;
-  }
-  const int P = S - T;  // query t sits at position P + t
-  const int ntiles = (P + min(t0 + 32, T) + LT::KT - 1) / LT::KT;
-
-  TileCopier<R, NW> copier;
-  copier.init(w, lane);
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < ntiles) issue_key_tile<PAGED>(copier, a, b, S, p, smem + p * LT::BYTES);
-
-  PA st;
-  {
-    const size_t q0 = ((qr0 + (tv[0] ? tq[0] : T - 1)) * H + hc) * DQ;
-    const size_t q1 = ((qr0 + (tv[1] ? tq[1] : T - 1)) * H + hc) * DQ;
-    absorb_pair<DQ, R>(a.q + q0, a.q + q1, a.wukT + (size_t)hc * R * DQ, jh * PA::RH, a.qscale, l16, kq, st.qT);
-  }
-  st.reset();
-  st.init_addressing(l16, kq, jh);
-
-  // One key tile; STG (the LDS stage of tile `it`, it % NS) is a
-  // compile-time constant so every operand address is a per-lane base plus
-  // an immediate.
-  auto tile_step = [&](int it, auto stage_tag) {
-    constexpr int STG = decltype(stage_tag)::value;
-    // This wave's copies of tile `it` have landed once at most the copies of
-    // the younger tiles already issued (it+1 .. it+NS-2, those that exist)
-    // are outstanding.
-    {
-      const int younger = min(NS - 2, ntiles - 1 - it);
-      if constexpr (NS >= 4) {
-        if (younger >= 2) wait_vmcnt<2 * CPW>();
-        else if (younger == 1) wait_vmcnt<CPW>();
-        else wait_vmcnt<0>();
-      } else if constexpr (NS == 3) {
-        if (younger >= 1) wait_vmcnt<CPW>();
-        else wait_vmcnt<0>();
-      } else {
-        wait_vmcnt<0>();
-      }
-    }
-    wg_barrier();  // tile visible; iteration it-1 finished (its stage and xbuf are free)
-    const MLA_LDS char* tile = smem + STG * LT::BYTES;
-
-    f32x4 sc[2][2];
-    st.partial_scores(tile, sc, [](int) {});
-    xbuf[(w * 4 + 0) * 64 + lane] = sc[0][0];
-    xbuf[(w * 4 + 1) * 64 + lane] = sc[0][1];
-    xbuf[(w * 4 + 2) * 64 + lane] = sc[1][0];
-    xbuf[(w * 4 + 3) * 64 + lane] = sc[1][1];
-    wait_lgkmcnt0();
-    wg_barrier();  // partial scores of both halves visible
-    // The copies of tile it+NS-1 go out here, between the two barriers of
-    // this tile rather than right after the first one, where every wave of
-    // the workgroup would queue its copies at the same moment.
-    if (it + NS - 1 < ntiles)
-      issue_key_tile<PAGED>(copier, a, b, S, it + NS - 1, smem + ((STG + NS - 1) % NS) * LT::BYTES);
-    {
-      const f32x4 o00 = xbuf[(partner * 4 + 0) * 64 + lane], o01 = xbuf[(partner * 4 + 1) * 64 + lane];
-      const f32x4 o10 = xbuf[(partner * 4 + 2) * 64 + lane], o11 = xbuf[(partner * 4 + 3) * 64 + lane];
-      // add in a fixed order (half 0 + half 1) so both waves get identical sums
-      if (jh == 0) {
-        sc[0][0] += o00; sc[0][1] += o01; sc[1][0] += o10; sc[1][1] += o11;
-      } else {
-        sc[0][0] = o00 + sc[0][0]; sc[0][1] = o01 + sc[0][1];
-        sc[1][0] = o10 + sc[1][0]; sc[1][1] = o11 + sc[1][1];
-      }
-    }
-    const int s0 = it * LT::KT;
-    if (s0 + LT::KT - 1 > P + t0) {  // causal mask on the diagonal tile (also hides keys past S)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (s0 + 4 * kq + e > P + tq[c]) sc[c][0][e] = -INFINITY;
-          if (s0 + 16 + 4 * kq + e > P + tq[c]) sc[c][1][e] = -INFINITY;
-        }
-      }
-    }
-    bf16x8 pB[2];
-    st.softmax(sc, pB);
-    st.values(tile, pB);
-  };
-  for (int it = 0; it < ntiles; it += NS) {
-    tile_step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < ntiles) tile_step(it + 1, std::integral_constant<int, 1 % NS>{});
-    if constexpr (NS >= 3)
-      if (it + 2 < ntiles) tile_step(it + 2, std::integral_constant<int, 2 % NS>{});
-    if constexpr (NS >= 4)
-      if (it + 3 < ntiles) tile_step(it + 3, std::integral_constant<int, 3 % NS>{});
-  }
-  static_assert(NS <= 4, "the loop above unrolls at most four stages");
-
-  // ---- epilogue: partial o^T = W_UV[h][:, half] (O^T_half / l), summed by the pair
-  bf16x8 ob[2][PA::NKK];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const float l_tot = col_sum(st.l_run[c]);
-    const float inv_l = 1.0f / l_tot;
-    if (a.lse && jh == 0 && kq == 0 && tv[c] && hvalid)
-      a.lse[((size_t)b * H + h) * T + tq[c]] = (st.m_run[c] + __builtin_log2f(l_tot)) * 0.69314718055994531f;
-#pragma unroll
-    for (int kk = 0; kk < PA::NKK; ++kk) ob[c][kk] = pack44(st.oT[c][2 * kk], st.oT[c][2 * kk + 1], inv_l);
-  }
-  wg_barrier();  // every wave is done with the stages and xbuf: reuse them for the o^T partials
-  f32x4* obuf = (f32x4*)smem_raw;  // [wave][vt][cg][lane]
-  const bf16* wv = a.wuv + (size_t)hc * DV * R + jh * PA::RH;
-#pragma unroll
-  for (int vt = 0; vt < NV; ++vt) {
-    const bf16* wrow = wv + (size_t)(16 * vt + l16) * R + 4 * kq;
-    f32x4 acc0 = f32x4{}, acc1 = f32x4{};
-#pragma unroll
-    for (int kk = 0; kk < PA::NKK; ++kk) {
-      const bf16x8 av = cat4(*(const bf16x4*)(wrow + 32 * kk), *(const bf16x4*)(wrow + 32 * kk + 16));
-      acc0 = mfma16(av, ob[0][kk], acc0);
-      acc1 = mfma16(av, ob[1][kk], acc1);
-    }
-    obuf[((w * NV + vt) * 2 + 0) * 64 + lane] = acc0;
-    obuf[((w * NV + vt) * 2 + 1) * 64 + lane] = acc1;
-  }
-  wait_lgkmcnt0();
-  wg_barrier();
-  const int w0 = w & ~1, w1 = w0 + 1;  // half 0 and half 1 of this pair
-  for (int vt = jh; vt < NV; vt += 2) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const f32x4 o = obuf[((w0 * NV + vt) * 2 + c) * 64 + lane] + obuf[((w1 * NV + vt) * 2 + c) * 64 + lane];
-      if (tv[c] && hvalid) {
-        const size_t orow = (qr0 + tq[c]) * (size_t)H * DV + (size_t)h * DV + 16 * vt + 4 * kq;
-        const bf16x4 gv = *(const bf16x4*)(a.gate + orow);
-        bf16x4 ov;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(o[e] * sigmoidf_((float)gv[e]));
-        *(bf16x4*)(a.out + orow) = ov;
-      }
-    }
-  }
 }
 
 }  // namespace mla

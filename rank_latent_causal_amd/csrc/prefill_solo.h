@@ -41,7 +41,7 @@ constexpr int kSoloScoreLookahead = 2;
 constexpr int kSoloValueLookahead = 2;
 
 // q_abs^T blocks [blk0, blk1) of 32 latent dims from W_UK^T[h] held in LDS
-// ([R, DQ] rows of DQ * 2 bytes, 16-byte chunk L of row j at L ^ (j & 15)),
+// ([R, DQ] rows of DQ * 2 bytes, 16-byte chunk L of row j at L ^ (j & (DQ/8 - 1))),
 // scaled by qscale: qT[kk] is the score B operand for k-block kk (lane column
 // l % 32, latent dims 16 kk + 8 (l / 32) + 0..7).  qb[k] is the B operand q^T
 // for d = 16 k + 8 (l / 32) + 0..7.  The A operand row rho of a block loads
@@ -167,7 +167,9 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   constexpr int WCC = WKB / NS / 1024 / NW;       // copies per wave per chunk
   constexpr int QCW = 32 * DQ * 2 / 1024;         // q copies per wave
   constexpr int NKS = DQ / 16;
-  static_assert(WKB == NS * LT::BYTES && NS == 4 && 64 % CPRW == 0 && CPRW <= 16, "W_UK^T chunks fill the stages");
+  constexpr int WCB = WKB / NS;                    // W_UK^T chunk bytes (chunk c sits in stage c)
+  static_assert(WKB % (NS * NW * 1024) == 0 && WCB <= LT::BYTES && NS == 4 && 64 % CPRW == 0 && CPRW <= 16,
+                "W_UK^T chunks fit the stages");
   static_assert(NW * QCW * 1024 <= kSoloSpareBytes && NS * WCC + QCW < 64, "q staging");
   MLA_LDS char* qbuf = smem + NS * LT::BYTES + w * (QCW * 1024);
   {
@@ -175,20 +177,22 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
     const unsigned rsub = ln / CPRW, cl = ln % CPRW;
     // q rows tw + r of head h (rows past T repeat row T - 1): row r at
-    // r DQ 2 bytes, chunk L at L ^ (r & 15)
+    // r DQ 2 bytes, chunk L at L ^ (r & (CPRW - 1))
     const u32x4 qrs = make_rsrc(a.q + qr0 * (size_t)H * DQ + (size_t)hc * DQ, (unsigned)((size_t)T * H * DQ * 2));
 #pragma unroll
     for (int i = 0; i < QCW; ++i) {
       const unsigned r = (64 / CPRW) * i + rsub;
       const unsigned row = (unsigned)min(tw + (int)r, T - 1);
-      buf2lds16(qrs, (row * (unsigned)(H * DQ) + ((cl ^ (r & 15)) * 8)) * 2, qbuf + i * 1024);
+      buf2lds16(qrs, (row * (unsigned)(H * DQ) + ((cl ^ (r & (CPRW - 1))) * 8)) * 2, qbuf + i * 1024);
     }
     const u32x4 krs = make_rsrc(a.wukT + (size_t)hc * R * DQ, (unsigned)WKB);
 #pragma unroll
     for (int c = 0; c < NS * WCC; ++c) {
       const int i = c * NW + w;  // copy i: rows (64 / CPRW) i .. (chunk c / WCC)
       const unsigned row = (64 / CPRW) * i + rsub;
-      buf2lds16(krs, (row * DQ + ((cl ^ (row & (CPRW - 1))) * 8)) * 2, smem + i * 1024);
+      const int ch = i / (NW * WCC);
+      buf2lds16(krs, (row * DQ + ((cl ^ (row & (CPRW - 1))) * 8)) * 2,
+                smem + ch * LT::BYTES + (i - ch * NW * WCC) * 1024);
     }
   }
   SA sa;
@@ -209,8 +213,11 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   wg_barrier();
 #pragma unroll
   for (int k = 0; k < NKS; ++k)
-    qb[k] = lds_read_b128(qbuf + l32 * (DQ * 2) + (((2 * k + hh) ^ (l32 & 15)) << 4));
-  absorb_lds<DQ, R>(smem, qb, a.qscale, lane, 0, BPC, qT);
+    qb[k] = lds_read_b128(qbuf + l32 * (DQ * 2) + (((2 * k + hh) ^ (l32 & (CPRW - 1))) << 4));
+  // rows of chunk c sit in stage c: the base of chunk c's rows as if the
+  // chunks were contiguous
+  auto wk_base = [&](int c) { return smem + c * (LT::BYTES - WCB); };
+  absorb_lds<DQ, R>(wk_base(0), qb, a.qscale, lane, 0, BPC, qT);
   // chunk c + 1 has landed once at most the younger chunks (NS - 2 - c of
   // them) and tiles 0 .. c - 1 (two chunks' worth of copies each) are
   // outstanding; the barrier also frees stage c for tile c.  Tiles past the
@@ -219,15 +226,15 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   wait_vmcnt<(NS - 2) * WCC>();
   wg_barrier();
   issue_key_tile<PAGED>(copier, a, b, S, 0, smem, 0 < ntiles);
-  absorb_lds<DQ, R>(smem, qb, a.qscale, lane, BPC, 2 * BPC, qT);
+  absorb_lds<DQ, R>(wk_base(1), qb, a.qscale, lane, BPC, 2 * BPC, qT);
   wait_vmcnt<(NS - 3) * WCC + CPW>();
   wg_barrier();
   issue_key_tile<PAGED>(copier, a, b, S, 1, smem + LT::BYTES, 1 < ntiles);
-  absorb_lds<DQ, R>(smem, qb, a.qscale, lane, 2 * BPC, 3 * BPC, qT);
+  absorb_lds<DQ, R>(wk_base(2), qb, a.qscale, lane, 2 * BPC, 3 * BPC, qT);
   wait_vmcnt<2 * CPW>();
   wg_barrier();
   issue_key_tile<PAGED>(copier, a, b, S, 2, smem + 2 * LT::BYTES, 2 < ntiles);
-  absorb_lds<DQ, R>(smem, qb, a.qscale, lane, 3 * BPC, 4 * BPC, qT);
+  absorb_lds<DQ, R>(wk_base(3), qb, a.qscale, lane, 3 * BPC, 4 * BPC, qT);
   float m_run, l_run = 0.0f;
 
   // causal mask of key tile j (also hides keys past S); key of register r is
@@ -400,7 +407,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   // W_UV[h] ([DV, R], 64 KiB to 128 KiB) is staged whole in the stages by the
   // four waves together (row v at v R 2 bytes, chunk L at L ^ (v & 15)), and
   // each wave's 32 gate rows (DV logits each) in the region after them (row
-  // r at r DV 2 bytes, chunk L at L ^ (r & 15)): every load of the epilogue
+  // r at r DV 2 bytes, chunk L at L ^ (r & (DV/8 - 1))): every load of the epilogue
   // is an LDS-DMA copy, waited for with explicit counts.  The copies go out
   // first; O^T is normalised and packed under them.
   constexpr int NVB = DV / 32;
@@ -424,7 +431,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     for (int i = 0; i < GCW; ++i) {
       const unsigned r = (64 / GCR) * i + gsub;
       const unsigned row = (unsigned)min(tw + (int)r, T - 1);
-      buf2lds16(grs, (row * (unsigned)(H * DV) + ((gcl ^ (r & 15)) * 8)) * 2, gbuf + i * 1024);
+      buf2lds16(grs, (row * (unsigned)(H * DV) + ((gcl ^ (r & (GCR - 1))) * 8)) * 2, gbuf + i * 1024);
     }
     const u32x4 wrs = make_rsrc(a.wuv + (size_t)hc * DV * R, (unsigned)(DV * R * 2));
     const unsigned rsub = ln / CPR, cl = ln % CPR;
@@ -475,7 +482,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         bf16x4 ov;
-        const bf16x4 gl = *(const MLA_LDS bf16x4*)(grow + (((4 * vb + c) ^ (l32 & 15)) << 4));
+        const bf16x4 gl = *(const MLA_LDS bf16x4*)(grow + (((4 * vb + c) ^ (l32 & (GCR - 1))) << 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[4 * c + e] * sigmoidf_((float)gl[e]));
         *(bf16x4*)(a.out + orow + 32 * vb + 8 * c + 4 * hh) = ov;
