@@ -87,6 +87,11 @@ __device__ __forceinline__ void absorb_lds(const MLA_LDS char* wk, const bf16x8 
   }
 }
 
+template <bool M>
+struct SoloMask {
+  static constexpr bool value = M;
+};
+
 template <int DQ, int DV, int R, bool PAGED = false, bool VARLEN = false>
 __global__ void __launch_bounds__(64 * kSoloWaves)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -97,13 +102,28 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   constexpr int NW = kSoloWaves;
   constexpr int CPW = copies_per_wave<R>(NW);
   constexpr int NKK = SA::NKK, NLB = SA::NLB;
-  constexpr int EPK = 16 / (NKK / 2);  // exponentials per phase-A product
+  // A key tile is KH latent tiles of 32 rows in consecutive halves of one
+  // stage: 64 keys at r = 256, 32 at r = 512, so that every tile carries 32
+  // score and 32 value products per wave whatever r is (the per-tile waits,
+  // barrier and softmax bookkeeping then weigh the same against them).
+  constexpr int KH = R <= 256 ? 2 : 1;
+  constexpr int KT = 32 * KH;             // keys per tile
+  constexpr int STB = KH * LT::BYTES;     // stage bytes
+  constexpr int CPT = KH * CPW;           // copies per wave per tile
+  constexpr int NG = KH * NKK;            // score products per tile
+  constexpr int NV = 2 * KH * NLB;        // value products per tile
+  static_assert(NG == 32 && NV == 32 && CPT <= 8, "tile schedule");
+  // At r = 256 (registers to spare) the score chains start from -m_run
+  // instead of zero, so the scores arrive relative to the running maximum
+  // and the exponentials need no subtraction; at r = 512 the scores are
+  // absolute and the exponentials subtract m_run.
+  constexpr bool PRESHIFT = KH == 2;
   // products of lookahead for the LDS operand reads (score / value)
   constexpr int SPF = kSoloScoreLookahead, VPF = kSoloValueLookahead;
   static_assert(LT::COPIES % NW == 0, "copy split");
   static_assert(DQ % 16 == 0 && DV % 32 == 0, "shape");
-  static_assert(NS >= 3 && NS <= 5 && CPW * (NS - 2) < 64, "stages and vmcnt range");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * LT::BYTES + kSoloSpareBytes];
+  static_assert(NS >= 3 && NS <= 5 && CPT * (NS - 2) < 64, "stages and vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[NS * STB + kSoloSpareBytes];
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
 
   // ---- work item (128 positions of one head), heaviest query blocks first
@@ -149,10 +169,22 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   const int t = tw + l32;  // this lane's query column
   const bool tvalid = t < T;
   const int P = S - T;  // query t sits at position P + t
-  const int ntiles = (P + min(t0 + kSoloRows, T) + LT::KT - 1) / LT::KT;
+  const int kend = P + min(t0 + kSoloRows, T);  // keys [0, kend) reach a query of the workgroup
+  const int ntiles = (kend + KT - 1) / KT;
 
   TileCopier<R, NW, 1> copier;
   copier.init(w, lane);
+
+  // copies of the 32-row half hf of key tile j into its stage; halves past
+  // the keys the workgroup needs are copied as zero rows
+  auto prepare_half = [&](int j, int hf) {
+    const int jj = KH * j + hf;
+    return prepare_key_tile<PAGED>(copier, a, b, S, jj, smem + (j % NS) * STB + hf * LT::BYTES, 32 * jj < kend);
+  };
+  auto issue_tile = [&](int j) {
+#pragma unroll
+    for (int hf = 0; hf < KH; ++hf) copier.template issue_range<0, CPW>(prepare_half(j, hf));
+  };
 
   // ---- absorb.  W_UK^T[h] ([R, DQ], 128 KiB at full width) is staged in the
   // LDS stages by the four waves together (1 KiB LDS-DMA copies) in four
@@ -168,10 +200,10 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   constexpr int QCW = 32 * DQ * 2 / 1024;         // q copies per wave
   constexpr int NKS = DQ / 16;
   constexpr int WCB = WKB / NS;                    // W_UK^T chunk bytes (chunk c sits in stage c)
-  static_assert(WKB % (NS * NW * 1024) == 0 && WCB <= LT::BYTES && NS == 4 && 64 % CPRW == 0 && CPRW <= 16,
+  static_assert(WKB % (NS * NW * 1024) == 0 && WCB <= STB && NS == 4 && 64 % CPRW == 0 && CPRW <= 16,
                 "W_UK^T chunks fit the stages");
   static_assert(NW * QCW * 1024 <= kSoloSpareBytes && NS * WCC + QCW < 64, "q staging");
-  MLA_LDS char* qbuf = smem + NS * LT::BYTES + w * (QCW * 1024);
+  MLA_LDS char* qbuf = smem + NS * STB + w * (QCW * 1024);
   {
     unsigned ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
@@ -192,7 +224,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
       const unsigned row = (64 / CPRW) * i + rsub;
       const int ch = i / (NW * WCC);
       buf2lds16(krs, (row * DQ + ((cl ^ (row & (CPRW - 1))) * 8)) * 2,
-                smem + ch * LT::BYTES + (i - ch * NW * WCC) * 1024);
+                smem + ch * STB + (i - ch * NW * WCC) * 1024);
     }
   }
   SA sa;
@@ -216,7 +248,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     qb[k] = lds_read_b128(qbuf + l32 * (DQ * 2) + (((2 * k + hh) ^ (l32 & (CPRW - 1))) << 4));
   // rows of chunk c sit in stage c: the base of chunk c's rows as if the
   // chunks were contiguous
-  auto wk_base = [&](int c) { return smem + c * (LT::BYTES - WCB); };
+  auto wk_base = [&](int c) { return smem + c * (STB - WCB); };
   absorb_lds<DQ, R>(wk_base(0), qb, a.qscale, lane, 0, BPC, qT);
   // chunk c + 1 has landed once at most the younger chunks (NS - 2 - c of
   // them) and tiles 0 .. c - 1 (two chunks' worth of copies each) are
@@ -225,97 +257,146 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   // exactly NS - 3 younger tiles in flight).
   wait_vmcnt<(NS - 2) * WCC>();
   wg_barrier();
-  issue_key_tile<PAGED>(copier, a, b, S, 0, smem, 0 < ntiles);
+  issue_tile(0);
   absorb_lds<DQ, R>(wk_base(1), qb, a.qscale, lane, BPC, 2 * BPC, qT);
-  wait_vmcnt<(NS - 3) * WCC + CPW>();
+  wait_vmcnt<(NS - 3) * WCC + CPT>();
   wg_barrier();
-  issue_key_tile<PAGED>(copier, a, b, S, 1, smem + LT::BYTES, 1 < ntiles);
+  issue_tile(1);
   absorb_lds<DQ, R>(wk_base(2), qb, a.qscale, lane, 2 * BPC, 3 * BPC, qT);
-  wait_vmcnt<2 * CPW>();
+  wait_vmcnt<2 * CPT>();
   wg_barrier();
-  issue_key_tile<PAGED>(copier, a, b, S, 2, smem + 2 * LT::BYTES, 2 < ntiles);
+  issue_tile(2);
   absorb_lds<DQ, R>(wk_base(3), qb, a.qscale, lane, 3 * BPC, 4 * BPC, qT);
   float m_run, l_run = 0.0f;
 
-  // causal mask of key tile j (also hides keys past S); key of register r is
-  // 32j + 8 (r / 4) + 4 (l / 32) + r % 4
-  auto mask = [&](f32x16& s, int j) {
-    const int s0 = j * LT::KT;
-    if (s0 + LT::KT - 1 > P + tw) {
+  // causal mask of the 32 keys from s0 (also hides keys past S); key of
+  // register r is s0 + 8 (r / 4) + 4 (l / 32) + r % 4
+  auto mask = [&](f32x16& s, int s0) __attribute__((always_inline)) {
+    if (s0 + 31 > P + tw) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (s0 + 8 * (r >> 2) + 4 * hh + (r & 3) > P + t) s[r] = -INFINITY;
     }
   };
-  // column maximum over the tile: 16 keys in this lane, 16 in lane l ^ 32
-  auto rowmax = [&](const f32x16& s) {
+  // column maximum of 32 keys and v over this lane's 16 keys; the other 16
+  // sit in lane l ^ 32 (xhalf_max)
+  auto lane_max = [&](const f32x16& s, float v) {
     const float m0 = max3_nn(s[0], s[1], s[2]), m1 = max3_nn(s[3], s[4], s[5]);
     const float m2 = max3_nn(s[6], s[7], s[8]), m3 = max3_nn(s[9], s[10], s[11]);
     const float m4 = max3_nn(s[12], s[13], s[14]);
-    return xhalf_max(max3_nn(max3_nn(m0, m1, m2), max3_nn(m3, m4, s[15]), -INFINITY));
+    return max3_nn(max3_nn(m0, m1, m2), max3_nn(m3, m4, s[15]), v);
   };
-  auto tile_at = [&](int j) { return smem + (j % NS) * LT::BYTES; };
+  auto tile_at = [&](int j) { return smem + (j % NS) * STB; };
+  // score operand g of a tile: k-block g % NKK of its half g / NKK
+  auto score_op = [&](const MLA_LDS char* tile, int g) {
+    return sa.score_operand(tile + (g / NKK) * LT::BYTES, g % NKK);
+  };
 
 
   // ---- tile 0: scores only (each step below starts with its tile's softmax)
-  wait_vmcnt<(NS - 2) * CPW>();  // tile 0 landed (tiles 1 .. NS-2 may be in flight)
+  wait_vmcnt<(NS - 2) * CPT>();  // tile 0 landed (tiles 1 .. NS-2 may be in flight)
   wg_barrier();
-  f32x16 sc;
+  f32x16 sc[KH];
   {
     bf16x8 ao[3];
-    ao[0] = sa.score_operand(smem, 0);
-    ao[1] = sa.score_operand(smem, 1);
+    ao[0] = score_op(smem, 0);
+    ao[1] = score_op(smem, 1);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      if (kk + 2 < NKK) ao[(kk + 2) % 3] = sa.score_operand(smem, kk + 2);
+    for (int g = 0; g < NG; ++g) {
+      if (g + 2 < NG) ao[(g + 2) % 3] = score_op(smem, g + 2);
       __builtin_amdgcn_sched_barrier(0);
-      if (kk == 0) mfma32v_first(sc, ao[0], qT[0]);
-      else mfma32v(sc, ao[kk % 3], qT[kk]);
+      if (g % NKK == 0) mfma32v_first(sc[g / NKK], ao[g % 3], qT[0]);
+      else mfma32v(sc[g / NKK], ao[g % 3], qT[g % NKK]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  settle_v(sc);
-  mask(sc, 0);
-  float mx = rowmax(sc);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int hf = 0; hf < KH; ++hf) {
+    settle_v(sc[hf]);
+    mask(sc[hf], 32 * hf);
+    mx = lane_max(sc[hf], mx);
+  }
+  mx = xhalf_max(mx);
   m_run = mx;
+  // -m_run in every accumulator slot (the chains' start with PRESHIFT)
+  f32x16 negm;
+  auto set_negm = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[i] = -m_run;
+    asm volatile("" : "+v"(negm));
+    operand_gap();
+  };
+  if constexpr (PRESHIFT) {
+#pragma unroll
+    for (int hf = 0; hf < KH; ++hf)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[hf][i] -= m_run;
+    mx = 0.0f;
+    set_negm();
+  }
 
   // The reference max moves only when a score exceeds it by more than 8 (so
   // P <= 2^8): the O^T rescale is rare.  Every lane of a column pair holds
   // the same maxima, so both halves take the same decision.
-  auto maybe_rescale = [&]() {
-    const bool need = mx > m_run + 8.0f;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_new = need ? mx : m_run;
-      const float alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
-      wait_states_24();  // the last value products have written O^T
+  auto maybe_rescale = [&]() __attribute__((always_inline)) {
+    if constexpr (PRESHIFT) {
+      // mx and the scores of tile it are relative to m_run
+      const bool need = mx > 8.0f;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float d = need ? mx : 0.0f;
+        const float alpha = fast_exp2(-d);
+        l_run *= alpha;
+        wait_states_24();  // the last value products have written O^T
 #pragma unroll
-      for (int u = 0; u < NLB; ++u) scale_acc(oT[u], alpha);
-      wait_states_24();  // the rescaled O^T feeds the next value products
-      m_run = m_new;
+        for (int u = 0; u < NLB; ++u) scale_acc(oT[u], alpha);
+        wait_states_24();  // the rescaled O^T feeds the next value products
+        m_run += d;
+#pragma unroll
+        for (int hf = 0; hf < KH; ++hf)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[hf][i] -= d;
+        set_negm();
+      }
+    } else {
+      const bool need = mx > m_run + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mx : m_run;
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+        wait_states_24();  // the last value products have written O^T
+#pragma unroll
+        for (int u = 0; u < NLB; ++u) scale_acc(oT[u], alpha);
+        wait_states_24();  // the rescaled O^T feeds the next value products
+        m_run = m_new;
+      }
     }
   };
-  auto softmax_sum = [&](const f32x16& p) {
-    const float s0 = (p[0] + p[1]) + (p[2] + p[3]), s1 = (p[4] + p[5]) + (p[6] + p[7]);
-    const float s2 = (p[8] + p[9]) + (p[10] + p[11]), s3 = (p[12] + p[13]) + (p[14] + p[15]);
-    l_run += (s0 + s1) + (s2 + s3);
+  // p = 2^(s - m_run) for a score s of tile it
+  auto expo = [&](float s_) __attribute__((always_inline)) {
+    if constexpr (PRESHIFT) return fast_exp2(s_);
+    else return fast_exp2(s_ - m_run);
   };
 
   // One key tile `it`: on entry sc holds the masked scores of tile it and mx
   // their column maxima; on exit, those of tile it+1 (garbage after the last
-  // tile, never used).
-  auto step_next = [&](int it) {
+  // tile, never used).  Score product g (k-block g % NKK of half g / NKK) and
+  // value product n (latent block n % NLB, key block n / NLB) number the
+  // tile's 32 + 32 products.  masked (a SoloMask) says whether tile it+1
+  // needs the causal mask; the steps before the diagonal run without it.
+  auto step_next = [&](int it, auto masked) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
     const MLA_LDS char* tile = tile_at(it);
     const MLA_LDS char* tnext = tile_at(it + 1);
     // tile it+1 landed; tiles it+2 .. it+NS-2 may still be in flight
-    wait_vmcnt<(NS - 3) * CPW>();
+    wait_vmcnt<(NS - 3) * CPT>();
     wg_barrier();  // tile it+1 visible; every wave is done with tile it-1
     // the first score operands of tile it+1 go out before anything else, and
     // the first value operands of tile it (resident since the last step)
     // right after: their LDS latency runs under the bookkeeping below
     bf16x8 ao[SPF + 1], av[VPF + 1];
 #pragma unroll
-    for (int u = 0; u < SPF; ++u) ao[u] = sa.score_operand(tnext, u);
+    for (int u = 0; u < SPF; ++u) ao[u] = score_op(tnext, u);
 #pragma unroll
     for (int u = 0; u < VPF; ++u) av[u] = sa.value_operand(tile, u);
     // tile it+NS-1 goes into the stage tile it-1 has left; its copies are
@@ -323,74 +404,117 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     // once they stall the wave for several hundred cycles).  Past the last
     // tile they are issued anyway, with an empty range that writes zeros
     // into that free stage: a branch around each copy costs more than it.
-    const auto pend =
-        prepare_key_tile<PAGED>(copier, a, b, S, it + NS - 1, tile_at(it + NS - 1), it + NS - 1 < ntiles);
+    typename TileCopier<R, NW, 1>::Pending pend[KH];
+#pragma unroll
+    for (int hf = 0; hf < KH; ++hf) pend[hf] = prepare_half(it + NS - 1, hf);
     maybe_rescale();
 
-    // phase A: score products of tile it+1 (k-blocks 0 .. NKK/2-1) under the
-    // exponentials of tile it; operands read SPF products ahead
-    f32x16 sn;
+    // phase A: score products 0 .. NG/2-1 of tile it+1 (operands read SPF
+    // products ahead) under the exponentials of half 0 of tile it; those of
+    // half 1 (r = 256) run under the first phase-B slots
+    f32x16 sn[KH];
 #pragma unroll
-    for (int kk = 0; kk < NKK / 2; ++kk) {
-      ao[(kk + SPF) % (SPF + 1)] = sa.score_operand(tnext, kk + SPF);
+    for (int g = 0; g < NG / 2; ++g) {
+      ao[(g + SPF) % (SPF + 1)] = score_op(tnext, g + SPF);
       __builtin_amdgcn_sched_barrier(0);
-      if (kk == 0) mfma32v_first(sn, ao[0], qT[0]);
-      else mfma32v(sn, ao[kk % (SPF + 1)], qT[kk]);
-#pragma unroll
-      for (int e = EPK * kk; e < EPK * (kk + 1); ++e) sc[e] = fast_exp2(sc[e] - m_run);
+      if (g % NKK == 0) {
+        if constexpr (PRESHIFT) mfma32v_init(sn[g / NKK], ao[g % (SPF + 1)], qT[0], negm);
+        else mfma32v_first(sn[g / NKK], ao[g % (SPF + 1)], qT[0]);
+      } else {
+        mfma32v(sn[g / NKK], ao[g % (SPF + 1)], qT[g % NKK]);
+      }
+      sc[0][g] = expo(sc[0][g]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // P is packed by VALU instructions: each half is materialised where it is
-    // formed (the compiler would otherwise sink it towards its products,
+    // P is packed by VALU instructions: each quarter is materialised where it
+    // is formed (the compiler would otherwise sink it towards its products,
     // past the gap) and read by a product at least two wait states later
-    bf16x8 pB0 = pack8(sc, 0, 1.0f), pB1;
-    asm volatile("" : "+v"(pB0));
+    bf16x8 pB[2 * KH];
+    pB[0] = pack8(sc[0], 0, 1.0f);
+    asm volatile("" : "+v"(pB[0]));
     operand_gap();
-    // phase B: value products of tile it in key-block-major order (n = NLB kb
-    // + t: latent block t, key block kb), so the first NLB use only the first
-    // half of P; the first NKK/2 are each followed by one of the remaining
-    // score products of tile it+1
+    // phase B: value products of tile it in key-block-major order, so the
+    // first NLB use only the first quarter of P; the first NG/2 are each
+    // followed by one of the remaining score products of tile it+1
+    float m_half = -INFINITY;
 #pragma unroll
-    for (int n = 0; n < 2 * NLB; ++n) {
-      if (n + VPF < 2 * NLB) av[(n + VPF) % (VPF + 1)] = sa.value_operand(tile, n + VPF);
+    for (int n = 0; n < NV; ++n) {
+      if (n + VPF < NV) av[(n + VPF) % (VPF + 1)] = sa.value_operand(tile, n + VPF);
       __builtin_amdgcn_sched_barrier(0);
-      mfma32a(oT[n % NLB], av[n % (VPF + 1)], n < NLB ? pB0 : pB1);
+      mfma32a(oT[n % NLB], av[n % (VPF + 1)], pB[n / NLB]);
       __builtin_amdgcn_sched_barrier(0);
-      if ((n & 3) == 1 && (n >> 2) < CPW) {
-        copier.issue_one(pend, n >> 2);
+      if ((n & 3) == 1 && (n >> 2) < CPT) {
+        copier.issue_one(pend[(n >> 2) / CPW], (n >> 2) % CPW);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (n < NKK / 2) {
-        const int kk = NKK / 2 + n;
-        if (kk + SPF < NKK) ao[(kk + SPF) % (SPF + 1)] = sa.score_operand(tnext, kk + SPF);
-        mfma32v(sn, ao[kk % (SPF + 1)], qT[kk]);
+      if (n < NG / 2) {
+        const int g = NG / 2 + n;
+        if (g + SPF < NG) ao[(g + SPF) % (SPF + 1)] = score_op(tnext, g + SPF);
+        if (g % NKK == 0) {
+          if constexpr (PRESHIFT) mfma32v_init(sn[g / NKK], ao[g % (SPF + 1)], qT[0], negm);
+          else mfma32v_first(sn[g / NKK], ao[g % (SPF + 1)], qT[0]);
+        } else {
+          mfma32v(sn[g / NKK], ao[g % (SPF + 1)], qT[g % NKK]);
+        }
+        if constexpr (KH == 2) sc[1][n] = expo(sc[1][n]);
         __builtin_amdgcn_sched_barrier(0);
       }
       // the rest of the softmax of tile it, and the mask and column maxima
       // of tile it+1 once its scores are complete, each under one product
       if (n == 0) {
-        pB1 = pack8(sc, 8, 1.0f);
-        asm volatile("" : "+v"(pB1));
+        pB[1] = pack8(sc[0], 8, 1.0f);
+        asm volatile("" : "+v"(pB[1]));
         __builtin_amdgcn_sched_barrier(0);
       }
       if (n == 1) {
-        softmax_sum(sc);
+        l_run = sum8_bf16(pB[1], sum8_bf16(pB[0], l_run));
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (n == NKK / 2 + 1) {
-        settle_v(sn);
+      if constexpr (KH == 2) {
+        if (n == NG / 4) {  // exponentials 0 .. 7 of half 1 are done
+          pB[2] = pack8(sc[1], 0, 1.0f);
+          asm volatile("" : "+v"(pB[2]));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (n == NG / 2) {
+          pB[3] = pack8(sc[1], 8, 1.0f);
+          asm volatile("" : "+v"(pB[3]));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (n == NG / 2 + 1) {
+          l_run = sum8_bf16(pB[3], sum8_bf16(pB[2], l_run));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // half 0 of tile it+1 is complete after phase A
+        if (n == 2) {
+          settle_v(sn[0]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (n == 3) {
+          if constexpr (MASKED) mask(sn[0], (it + 1) * KT);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (n == 4) {
+          m_half = lane_max(sn[0], -INFINITY);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // the last half of tile it+1 is complete after phase-B slot NG/2 - 1
+      if (n == NG / 2 + KH) {
+        settle_v(sn[KH - 1]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (n == NKK / 2 + 2) {
-        mask(sn, it + 1);
+      if (n == NG / 2 + KH + 1) {
+        if constexpr (MASKED) mask(sn[KH - 1], (it + 1) * KT + 32 * (KH - 1));
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (n == NKK / 2 + 3) {
-        mx = rowmax(sn);
+      if (n == NG / 2 + KH + 2) {
+        mx = xhalf_max(lane_max(sn[KH - 1], m_half));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    sc = sn;
+#pragma unroll
+    for (int hf = 0; hf < KH; ++hf) sc[hf] = sn[hf];
   };
 
 
@@ -401,7 +525,14 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   // ranges push the architectural registers over 256 and the allocator then
   // evicts O^T from its registers; a branch inside the loop whose arms both
   // update O^T does the same at its join.
-  for (int it = 0; it < ntiles; ++it) step_next(it);
+  // Tiles 0 .. nfull-1 hold no key past this wave's first query, so the
+  // steps that form their scores need no mask (wave-uniform; every wave
+  // still runs ntiles steps and meets the same barriers).
+  const int nfull = (P + tw + 1) / KT;
+  const int nfree = min(max(nfull - 1, 0), ntiles);
+  int it = 0;
+  for (; it < nfree; ++it) step_next(it, SoloMask<false>{});
+  for (; it < ntiles; ++it) step_next(it, SoloMask<true>{});
 
   // ---- epilogue: o^T = W_UV[h] (O^T / l), gate, store
   // W_UV[h] ([DV, R], 64 KiB to 128 KiB) is staged whole in the stages by the
@@ -416,9 +547,9 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   constexpr int CPV = 32 / RPC / NW;          // copies per wave per v-block
   constexpr int GCR = DV / 8;                 // 16-byte chunks per gate row
   constexpr int GCW = 32 * DV * 2 / 1024;     // gate copies per wave
-  static_assert(DV * R * 2 <= NS * LT::BYTES && CPV >= 1 && CPV * NVB + GCW < 64, "W_UV staging");
+  static_assert(DV * R * 2 <= NS * STB && CPV >= 1 && CPV * NVB + GCW < 64, "W_UV staging");
   static_assert(64 % GCR == 0 && GCR <= 16 && NW * GCW * 1024 <= kSoloSpareBytes, "gate staging");
-  MLA_LDS char* gbuf = smem + NS * LT::BYTES + w * (GCW * 1024);
+  MLA_LDS char* gbuf = smem + NS * STB + w * (GCW * 1024);
   wait_vmcnt<0>();  // the zero-row copies of the tiles past the last write the stages
   wg_barrier();     // every wave is done with the key tiles
   {

@@ -41,6 +41,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ void mfma32v_first(f32x16& c, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
 }
+// chain start from an accumulator held in other registers (init is only read)
+__device__ __forceinline__ void mfma32v_init(f32x16& c, const bf16x8& a, const bf16x8& b, const f32x16& init) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(c) : "v"(a), "v"(b), "v"(init));
+}
 __device__ __forceinline__ void mfma32v(f32x16& c, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
 }
@@ -84,6 +88,19 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base, float s) {
 #pragma unroll
   for (int p = 0; p < 8; ++p) r[p] = (bf16)(v[base + p] * s);
   return r;
+}
+
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + the sum of the 8 bf16 values of p: four v_dot2 against (1, 1).  The
+// softmax denominator then adds the bf16 P that the value products use, in
+// half the instructions of an fp32 sum of the unrounded exponentials.
+__device__ __forceinline__ float sum8_bf16(const bf16x8& p, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
 }
 
 template <int R>

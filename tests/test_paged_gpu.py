@@ -115,6 +115,7 @@ def test_decode_paged_full_workload_sampled(o):
 @pytest.mark.parametrize("B,T,S,H,shape,page_size", [
     (2, 37, 100, 3, "toy", 32),
     (2, 30, 161, 9, "mid", 64),
+    (1, 90, 250, 5, "mid", 32),
     (1, 33, 1000, 8, "full", 128),
     (3, 1, 77, 4, "full", 32),
     (1, 130, 131, 8, "full", 64),

@@ -46,7 +46,7 @@ def test_prefill_toy_f32_workload(o):
 
 @pytest.mark.parametrize("B,T,H,shape", [
     (1, 1, 1, "toy"), (2, 37, 3, "toy"), (3, 100, 5, "toy"),
-    (1, 45, 2, "mid"), (2, 97, 9, "mid"),
+    (1, 45, 2, "mid"), (2, 97, 9, "mid"), (1, 300, 3, "mid"),
     (1, 33, 1, "full"), (2, 70, 5, "full"), (1, 130, 8, "full"),
 ])
 def test_prefill_bf16_ragged(o, B, T, H, shape):
