@@ -149,8 +149,6 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// s_waitcnt lgkmcnt(0): this wave's LDS writes have landed (before a barrier
-// that publishes them to the other waves).
 // Scalar (SMEM) load of a wave-uniform int.  A plain load of a value the
 // compiler cannot prove read-only becomes a vector load, and waiting for it
 // (vmcnt) would also wait for every LDS-DMA tile copy in flight.  The SMEM

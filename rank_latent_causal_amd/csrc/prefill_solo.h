@@ -87,11 +87,6 @@ __device__ __forceinline__ void absorb_lds(const MLA_LDS char* wk, const bf16x8 
   }
 }
 
-template <bool M>
-struct SoloMask {
-  static constexpr bool value = M;
-};
-
 template <int DQ, int DV, int R, bool PAGED = false, bool VARLEN = false>
 __global__ void __launch_bounds__(64 * kSoloWaves)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -382,7 +377,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   // their column maxima; on exit, those of tile it+1 (garbage after the last
   // tile, never used).  Score product g (k-block g % NKK of half g / NKK) and
   // value product n (latent block n % NLB, key block n / NLB) number the
-  // tile's 32 + 32 products.  masked (a SoloMask) says whether tile it+1
+  // tile's 32 + 32 products.  masked (a BoolTag) says whether tile it+1
   // needs the causal mask; the steps before the diagonal run without it.
   auto step_next = [&](int it, auto masked) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
@@ -531,8 +526,8 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   const int nfull = (P + tw + 1) / KT;
   const int nfree = min(max(nfull - 1, 0), ntiles);
   int it = 0;
-  for (; it < nfree; ++it) step_next(it, SoloMask<false>{});
-  for (; it < ntiles; ++it) step_next(it, SoloMask<true>{});
+  for (; it < nfree; ++it) step_next(it, BoolTag<false>{});
+  for (; it < ntiles; ++it) step_next(it, BoolTag<true>{});
 
   // ---- epilogue: o^T = W_UV[h] (O^T / l), gate, store
   // W_UV[h] ([DV, R], 64 KiB to 128 KiB) is staged whole in the stages by the

@@ -90,6 +90,12 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base, float s) {
   return r;
 }
 
+// a compile-time flag passed to a generic lambda (one specialised body each)
+template <bool V>
+struct BoolTag {
+  static constexpr bool value = V;
+};
+
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // acc + the sum of the 8 bf16 values of p: four v_dot2 against (1, 1).  The
