@@ -280,7 +280,7 @@ mla_decode_solo(DecodeSoloArgs a) {
 
   // keys at or past nvalid (rows past the sequence's end) are masked; the
   // key of register r is 8 (r / 4) + 4 (l / 32) + r % 4
-  auto mask = [&](f32x16& sv, int nvalid) {
+  auto mask = [&](f32x16& sv, int nvalid) __attribute__((always_inline)) {
     if (nvalid < KT) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -338,7 +338,7 @@ mla_decode_solo(DecodeSoloArgs a) {
 
   // The reference max moves only when a score exceeds it by more than 8 (so
   // P <= 2^8): the O^T rescale is rare.
-  auto maybe_rescale = [&]() {
+  auto maybe_rescale = [&]() __attribute__((always_inline)) {
     const bool need = mx > m_run + 8.0f;
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float m_new = need ? mx : m_run;
@@ -360,7 +360,7 @@ mla_decode_solo(DecodeSoloArgs a) {
   // With next_q >= 0, tile it+2 starts sequence next_q: its q_abs is loaded
   // once the last score product of this step has read q_abs, and waited for
   // at the end of the step.
-  auto step = [&](int it, int nvalid1, int next_q) {
+  auto step = [&](int it, int nvalid1, int next_q) __attribute__((always_inline)) {
     const MLA_LDS char* tile = tile_at(it);
     const MLA_LDS char* tnext = tile_at(it + 1);
     const MLA_LDS char* tnext2 = tile_at(it + 2);
@@ -409,8 +409,8 @@ mla_decode_solo(DecodeSoloArgs a) {
         asm volatile("" : "+v"(pB1));
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (n >= 1 && n <= 8) {
-        l_run += sc[2 * n - 2] + sc[2 * n - 1];
+      if (n == 1) {
+        l_run = sum8_bf16(pB1, sum8_bf16(pB0, l_run));
         __builtin_amdgcn_sched_barrier(0);
       }
       if (n == NKK / 2 + 1) {

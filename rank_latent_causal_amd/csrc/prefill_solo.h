@@ -334,7 +334,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   // The reference max moves only when a score exceeds it by more than 8 (so
   // P <= 2^8): the O^T rescale is rare.  Every lane of a column pair holds
   // the same maxima, so both halves take the same decision.
-  auto maybe_rescale = [&]() __attribute__((always_inline)) {
+  auto maybe_rescale = [&](f32x16 (&sc)[KH]) __attribute__((always_inline)) {
     if constexpr (PRESHIFT) {
       // mx and the scores of tile it are relative to m_run
       const bool need = mx > 8.0f;
@@ -379,7 +379,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   // value product n (latent block n % NLB, key block n / NLB) number the
   // tile's 32 + 32 products.  masked (a BoolTag) says whether tile it+1
   // needs the causal mask; the steps before the diagonal run without it.
-  auto step_next = [&](int it, auto masked) __attribute__((always_inline)) {
+  auto step_next = [&](int it, auto masked, f32x16 (&sc)[KH], f32x16 (&sn)[KH]) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked)::value;
     const MLA_LDS char* tile = tile_at(it);
     const MLA_LDS char* tnext = tile_at(it + 1);
@@ -402,12 +402,11 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     typename TileCopier<R, NW, 1>::Pending pend[KH];
 #pragma unroll
     for (int hf = 0; hf < KH; ++hf) pend[hf] = prepare_half(it + NS - 1, hf);
-    maybe_rescale();
+    maybe_rescale(sc);
 
     // phase A: score products 0 .. NG/2-1 of tile it+1 (operands read SPF
     // products ahead) under the exponentials of half 0 of tile it; those of
     // half 1 (r = 256) run under the first phase-B slots
-    f32x16 sn[KH];
 #pragma unroll
     for (int g = 0; g < NG / 2; ++g) {
       ao[(g + SPF) % (SPF + 1)] = score_op(tnext, g + SPF);
@@ -508,8 +507,6 @@ mla_prefill_solo_kernel(PrefillArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-#pragma unroll
-    for (int hf = 0; hf < KH; ++hf) sc[hf] = sn[hf];
   };
 
 
@@ -525,9 +522,21 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   // still runs ntiles steps and meets the same barriers).
   const int nfull = (P + tw + 1) / KT;
   const int nfree = min(max(nfull - 1, 0), ntiles);
+  // The scores alternate between two register sets, two steps per
+  // iteration (a copy of the next tile's scores at every step would cost as
+  // many moves); an odd last mask-free step runs with the masked ones (the
+  // mask changes nothing on a tile wholly before the wave's queries).
+  f32x16 sc2[KH];
   int it = 0;
-  for (; it < nfree; ++it) step_next(it, BoolTag<false>{});
-  for (; it < ntiles; ++it) step_next(it, BoolTag<true>{});
+  for (; it + 1 < nfree; it += 2) {
+    step_next(it, BoolTag<false>{}, sc, sc2);
+    step_next(it + 1, BoolTag<false>{}, sc2, sc);
+  }
+  for (; it < ntiles; ++it) {
+    step_next(it, BoolTag<true>{}, sc, sc2);
+#pragma unroll
+    for (int hf = 0; hf < KH; ++hf) sc[hf] = sc2[hf];
+  }
 
   // ---- epilogue: o^T = W_UV[h] (O^T / l), gate, store
   // W_UV[h] ([DV, R], 64 KiB to 128 KiB) is staged whole in the stages by the
