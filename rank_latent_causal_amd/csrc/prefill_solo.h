@@ -433,6 +433,11 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     float m_half = -INFINITY;
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
+      // the score operand of slot n + SPF goes out before the value operand
+      // of slot n + VPF: the wait for a slot's value operand then covers its
+      // score operand too (one s_waitcnt per slot)
+      if (n < NG / 2 && NG / 2 + n + SPF < NG) ao[(NG / 2 + n + SPF) % (SPF + 1)] = score_op(tnext, NG / 2 + n + SPF);
+      __builtin_amdgcn_sched_barrier(0);
       if (n + VPF < NV) av[(n + VPF) % (VPF + 1)] = sa.value_operand(tile, n + VPF);
       __builtin_amdgcn_sched_barrier(0);
       mfma32a(oT[n % NLB], av[n % (VPF + 1)], pB[n / NLB]);
@@ -443,7 +448,6 @@ mla_prefill_solo_kernel(PrefillArgs a) {
       }
       if (n < NG / 2) {
         const int g = NG / 2 + n;
-        if (g + SPF < NG) ao[(g + SPF) % (SPF + 1)] = score_op(tnext, g + SPF);
         if (g % NKK == 0) {
           if constexpr (PRESHIFT) mfma32v_init(sn[g / NKK], ao[g % (SPF + 1)], qT[0], negm);
           else mfma32v_first(sn[g / NKK], ao[g % (SPF + 1)], qT[0]);
