@@ -78,9 +78,9 @@ struct TileCopier {
   };
 
   __device__ __forceinline__ Pending prepare(const bf16* __restrict__ base, int row0, int row_end,
-                                             MLA_LDS char* stage) const {
+                                             MLA_LDS char* stage, bool with_lane_base = true) const {
     Pending p;
-    p.lb = lane_base();
+    p.lb = with_lane_base ? lane_base() : 0u;  // without: the caller keeps the copy offsets
     int rows = row_end - row0;
     rows = rows > KT ? KT : rows;
     rows = rows < 0 ? 0 : rows;  // a tile wholly past row_end reads as zeros

@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(256) mla_varlen_prepare(const int* __restrict_
 template <bool PAGED, int R, int NW, int SW>
 __device__ __forceinline__ typename TileCopier<R, NW, SW>::Pending prepare_key_tile(
     const TileCopier<R, NW, SW>& copier, const PrefillArgs& a, int b, int S, int j, MLA_LDS char* stage,
-    bool real = true) {
+    bool real = true, bool with_lane_base = true) {
   constexpr int KT = LatentTile<R>::KT;
   if constexpr (PAGED) {
     const int pos = real ? j * KT : 0;
@@ -112,9 +112,9 @@ __device__ __forceinline__ typename TileCopier<R, NW, SW>::Pending prepare_key_t
       valid = 0;
     }
     const size_t row = ((size_t)pg << a.page_shift) + (pos & ((1 << a.page_shift) - 1));
-    return copier.prepare(a.c + row * R, 0, valid, stage);
+    return copier.prepare(a.c + row * R, 0, valid, stage, with_lane_base);
   } else {
-    return copier.prepare(a.c + (size_t)b * S * R, j * KT, real ? S : 0, stage);
+    return copier.prepare(a.c + (size_t)b * S * R, j * KT, real ? S : 0, stage, with_lane_base);
   }
 }
 

@@ -172,9 +172,10 @@ mla_prefill_solo_kernel(PrefillArgs a) {
 
   // copies of the 32-row half hf of key tile j into its stage; halves past
   // the keys the workgroup needs are copied as zero rows
-  auto prepare_half = [&](int j, int hf) {
+  auto prepare_half = [&](int j, int hf, bool with_lane_base = true) {
     const int jj = KH * j + hf;
-    return prepare_key_tile<PAGED>(copier, a, b, S, jj, smem + (j % NS) * STB + hf * LT::BYTES, 32 * jj < kend);
+    return prepare_key_tile<PAGED>(copier, a, b, S, jj, smem + (j % NS) * STB + hf * LT::BYTES, 32 * jj < kend,
+                                   with_lane_base);
   };
   auto issue_tile = [&](int j) {
 #pragma unroll
@@ -373,6 +374,15 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     else return fast_exp2(s_ - m_run);
   };
 
+  // At r = 256 (registers to spare) this wave's lane offsets of its copies
+  // of a tile are formed once here instead of at every tile.
+  constexpr bool KEEP_OFFSETS = KH == 2;
+  unsigned coff[CPW];
+  if constexpr (KEEP_OFFSETS) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) coff[c] = copier.offset_of(w + NW * c);
+  }
+
   // One key tile `it`: on entry sc holds the masked scores of tile it and mx
   // their column maxima; on exit, those of tile it+1 (garbage after the last
   // tile, never used).  Score product g (k-block g % NKK of half g / NKK) and
@@ -401,7 +411,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     // into that free stage: a branch around each copy costs more than it.
     typename TileCopier<R, NW, 1>::Pending pend[KH];
 #pragma unroll
-    for (int hf = 0; hf < KH; ++hf) pend[hf] = prepare_half(it + NS - 1, hf);
+    for (int hf = 0; hf < KH; ++hf) pend[hf] = prepare_half(it + NS - 1, hf, !KEEP_OFFSETS);
     maybe_rescale(sc);
 
     // phase A: score products 0 .. NG/2-1 of tile it+1 (operands read SPF
@@ -443,7 +453,12 @@ mla_prefill_solo_kernel(PrefillArgs a) {
       mfma32a(oT[n % NLB], av[n % (VPF + 1)], pB[n / NLB]);
       __builtin_amdgcn_sched_barrier(0);
       if ((n & 3) == 1 && (n >> 2) < CPT) {
-        copier.issue_one(pend[(n >> 2) / CPW], (n >> 2) % CPW);
+        if constexpr (KEEP_OFFSETS) {
+          const int c = (n >> 2) % CPW;
+          buf2lds16(pend[(n >> 2) / CPW].rs, coff[c], pend[(n >> 2) / CPW].stage + (w + NW * c) * 1024);
+        } else {
+          copier.issue_one(pend[(n >> 2) / CPW], (n >> 2) % CPW);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       if (n < NG / 2) {
