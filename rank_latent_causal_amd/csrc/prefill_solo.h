@@ -374,14 +374,11 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     else return fast_exp2(s_ - m_run);
   };
 
-  // At r = 256 (registers to spare) this wave's lane offsets of its copies
-  // of a tile are formed once here instead of at every tile.
-  constexpr bool KEEP_OFFSETS = KH == 2;
+  // This wave's lane offsets of its copies of a tile, formed once here
+  // instead of at every tile (the tile's descriptor changes, they do not).
   unsigned coff[CPW];
-  if constexpr (KEEP_OFFSETS) {
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) coff[c] = copier.offset_of(w + NW * c);
-  }
+  for (int c = 0; c < CPW; ++c) coff[c] = copier.offset_of(w + NW * c);
 
   // One key tile `it`: on entry sc holds the masked scores of tile it and mx
   // their column maxima; on exit, those of tile it+1 (garbage after the last
@@ -411,7 +408,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     // into that free stage: a branch around each copy costs more than it.
     typename TileCopier<R, NW, 1>::Pending pend[KH];
 #pragma unroll
-    for (int hf = 0; hf < KH; ++hf) pend[hf] = prepare_half(it + NS - 1, hf, !KEEP_OFFSETS);
+    for (int hf = 0; hf < KH; ++hf) pend[hf] = prepare_half(it + NS - 1, hf, false);
     maybe_rescale(sc);
 
     // phase A: score products 0 .. NG/2-1 of tile it+1 (operands read SPF
@@ -453,12 +450,8 @@ mla_prefill_solo_kernel(PrefillArgs a) {
       mfma32a(oT[n % NLB], av[n % (VPF + 1)], pB[n / NLB]);
       __builtin_amdgcn_sched_barrier(0);
       if ((n & 3) == 1 && (n >> 2) < CPT) {
-        if constexpr (KEEP_OFFSETS) {
-          const int c = (n >> 2) % CPW;
-          buf2lds16(pend[(n >> 2) / CPW].rs, coff[c], pend[(n >> 2) / CPW].stage + (w + NW * c) * 1024);
-        } else {
-          copier.issue_one(pend[(n >> 2) / CPW], (n >> 2) % CPW);
-        }
+        const int c = (n >> 2) % CPW;
+        buf2lds16(pend[(n >> 2) / CPW].rs, coff[c], pend[(n >> 2) / CPW].stage + (w + NW * c) * 1024);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (n < NG / 2) {
