@@ -12,7 +12,7 @@
 //                       MFMA columns, 16 per wave, up to 8 waves).  Every
 //                       sequence piece in a range leaves an unnormalised
 //                       partial (m, l in fp32, O[r] in bf16).
-//  mla_decode_merge     per (head, 8 sequences): log-sum-exp merge of the
+//  mla_decode_merge     per (head, 16 sequences): log-sum-exp merge of the
 //                       partials, then o = o_lat W_UV[h]^T on MFMA, the
 //                       sigmoid gate and the store.
 //
@@ -67,6 +67,11 @@ __global__ void __launch_bounds__(256) mla_wuk_transpose(const T* __restrict__ w
 // cross many sequence starts take fewer tiles.  Range k covers tiles
 // [rt[k], rt[k + 1]) (rt[G] = NT; a range may be empty), and krange[2i],
 // krange[2i + 1] are the first and last range holding tiles of sequence i.
+// When B + G + 2 <= kPrepareLds the binary searches read LDS copies of cu_t
+// and rt instead of the global arrays just written (a few hundred cycles per
+// step less).
+constexpr int kPrepareLds = 2048;
+
 struct PrepareArgs {
   const int* seq_lens;  // [B] (paged), or
   const int* cu;        // [B + 1] row prefix sums (packed)
@@ -89,9 +94,17 @@ __device__ __forceinline__ void decode_prepare(const PrepareArgs& pa) {
   const int switch_tiles = pa.switch_tiles;
   constexpr long long kCap = 1LL << 30;
   __shared__ long long wsum[4];
+  __shared__ int s_cut[kPrepareLds];  // cu_t[0..B], then rt[0..G]
+  const bool in_lds = B + G + 2 <= kPrepareLds;  // uniform
+  int* s_rt = s_cut + (in_lds ? B + 1 : 0);
+  auto cut = [&](int i) { return in_lds ? s_cut[i] : cu_t[i]; };
+  auto rts = [&](int k) { return in_lds ? s_rt[k] : rt[k]; };
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   long long carry = 0;
-  if (tid == 0) cu_t[0] = 0;
+  if (tid == 0) {
+    cu_t[0] = 0;
+    if (in_lds) s_cut[0] = 0;
+  }
   for (int base = 0; base < B; base += 256) {
     const int i = base + tid;
     long long tiles = 0;
@@ -111,7 +124,11 @@ __device__ __forceinline__ void decode_prepare(const PrepareArgs& pa) {
     __syncthreads();
     long long before = carry;
     for (int u = 0; u < w; ++u) before += wsum[u];
-    if (i < B) cu_t[i + 1] = (int)min(before + incl, kCap);
+    if (i < B) {
+      const int v = (int)min(before + incl, kCap);
+      cu_t[i + 1] = v;
+      if (in_lds) s_cut[i + 1] = v;
+    }
     carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
@@ -128,19 +145,20 @@ __device__ __forceinline__ void decode_prepare(const PrepareArgs& pa) {
   const long long S = switch_tiles, C = NT + S * B;
   const long long Ge = min((long long)G, C);
   for (int k = tid; k <= G; k += 256) {
-    if (k >= Ge) {
-      rt[k] = (int)NT;
-      continue;
+    int t = (int)NT;
+    if (k < Ge) {
+      const long long c = (long long)k * C / Ge;
+      int l = 0, r = B - 1;  // the largest i with cu_t[i] + S i <= c
+      while (l < r) {
+        const int mid = (l + r + 1) >> 1;
+        if ((long long)cut(mid) + S * mid <= c) l = mid; else r = mid - 1;
+      }
+      const long long cl = cut(l);
+      const long long off = c - (cl + S * l);
+      t = (int)(off < S ? cl : min(cl + (off - S), (long long)cut(l + 1)));
     }
-    const long long c = (long long)k * C / Ge;
-    int l = 0, r = B - 1;  // the largest i with cu_t[i] + S i <= c
-    while (l < r) {
-      const int mid = (l + r + 1) >> 1;
-      if ((long long)cu_t[mid] + S * mid <= c) l = mid; else r = mid - 1;
-    }
-    const long long off = c - ((long long)cu_t[l] + S * l);
-    const long long t = off < S ? cu_t[l] : min((long long)cu_t[l] + (off - S), (long long)cu_t[l + 1]);
-    rt[k] = (int)t;
+    rt[k] = t;
+    if (in_lds) s_rt[k] = t;
   }
   __syncthreads();  // rt complete
   for (int i = tid; i < B; i += 256) {
@@ -149,12 +167,12 @@ __device__ __forceinline__ void decode_prepare(const PrepareArgs& pa) {
       int l = 0, r = G - 1;
       while (l < r) {
         const int mid = (l + r + 1) >> 1;
-        if (rt[mid] <= x) l = mid; else r = mid - 1;
+        if (rts(mid) <= x) l = mid; else r = mid - 1;
       }
       return l;
     };
-    krange[2 * i] = range_at(cu_t[i]);
-    krange[2 * i + 1] = range_at(cu_t[i + 1] - 1);
+    krange[2 * i] = range_at(cut(i));
+    krange[2 * i + 1] = range_at(cut(i + 1) - 1);
   }
 }
 
@@ -424,24 +442,32 @@ __device__ __forceinline__ int range_of(long long x, long long N, long long G) {
   return (int)(((x + 1) * G - 1) / N);
 }
 
-// Workgroup (head h, 8 sequences), 4 waves.  Phase 1: wave w merges the
+// Workgroup (head h, 16 sequences), 8 waves.  Phase 1: wave w merges the
 // partials of sequences 2w and 2w+1 of the group (half a wave each, 32 lanes
 // over the R latent columns), loading the partials of up to kMergeChunk ranges
 // at once, and writes o_lat = O / l (bf16) to LDS.  Phase 2: wave w computes
-// v-tiles w, w+4, ... of o^T = W_UV[h] o_lat^T on MFMA (the 16 MFMA columns
-// are the group's sequences, 8 of them used), gates and stores; the first
-// v-tile's W_UV operands and gate values are loaded before phase 1.
-constexpr int kMergeSeqs = 8;
-constexpr int kMergeChunk = 4;
+// v-tiles w, w+8, ... of o^T = W_UV[h] o_lat^T on MFMA (the 16 MFMA columns
+// are the group's sequences), gates and stores; the first v-tile's W_UV
+// operands and gate values are requested at the end of phase 1, before the
+// barrier.  At up to 128 VGPRs two workgroups fit on a CU, so the 384
+// workgroups of 64 sequences x 96 heads run in one round.
+constexpr int kMergeSeqs = 16;
+constexpr int kMergeWaves = 8;
+constexpr int kMergeChunk = 8;
 
 template <int DV, int R>
-__global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
+__global__ void __launch_bounds__(64 * kMergeWaves) __attribute__((amdgpu_waves_per_eu(4)))
+mla_decode_merge(DecodeMergeArgs a) {
   constexpr int CPL = R / 32;  // latent columns per lane (32 lanes per sequence)
   constexpr int NKK = R / 32;
-  static_assert(CPL == 1 || CPL % 4 == 0, "merge split");
-  __shared__ __attribute__((aligned(16))) bf16 olat[16][R + 8];
+  constexpr int CV = CPL >= 8 ? 8 : CPL;  // elements per partial load
+  constexpr int NL = CPL / CV;            // loads per partial and lane
+  static_assert(CPL % CV == 0 && (CV == 1 || CV == 8), "merge split");
+  static_assert(kMergeSeqs == 2 * kMergeWaves, "one half wave per sequence");
+  using raw_t = std::conditional_t<CV == 8, bf16x8, bf16>;
+  __shared__ __attribute__((aligned(16))) bf16 olat[kMergeSeqs][R + 8];
 
-  // 1-D grid of H x nb workgroups (nb = ceil(B / 8)).  With H % 8 == 0 the
+  // 1-D grid of H x nb workgroups (nb = ceil(B / 16)).  With H % 8 == 0 the
   // nb workgroups of head h get ids congruent to h mod 8, i.e. they run on
   // one XCD and read W_UV[h] from HBM once.
   const int nb = (a.B + kMergeSeqs - 1) / kMergeSeqs;
@@ -457,9 +483,9 @@ __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l16 = lane & 15, kq = lane >> 4;
 
-  // phase 2 operands (MFMA column l16 = sequence bb*8 + l16 for l16 < 8)
-  const int ip = bb * kMergeSeqs + (l16 & (kMergeSeqs - 1));
-  const bool pvalid = l16 < kMergeSeqs && ip < a.B;
+  // phase 2 operands (MFMA column l16 = sequence bb*16 + l16)
+  const int ip = bb * kMergeSeqs + l16;
+  const bool pvalid = ip < a.B;
   const int ipc = ip < a.B ? ip : a.B - 1;
   const bf16* wv = a.wuv + (size_t)h * DV * R;
   const size_t orow = (size_t)ipc * a.H * DV + (size_t)h * DV;
@@ -471,7 +497,6 @@ __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
   };
   bf16x8 wa[NKK];
   bf16x4 gv;
-  if (w < DV / 16) load_w(w, wa, gv);
 
   {
     const long long N = a.n_dev ? (long long)a.n_dev[0] : a.N;
@@ -495,25 +520,19 @@ __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
 #pragma unroll
     for (int u = 0; u < CPL; ++u) acc[u] = 0.0f;
     for (int kc = k0; kc <= k1; kc += kMergeChunk) {
-      // every partial of the chunk is in flight at once
-      float mk[kMergeChunk], lk[kMergeChunk], ok[kMergeChunk][CPL];
+      // every partial of the chunk is in flight at once, kept as loaded until used
+      float mk[kMergeChunk], lk[kMergeChunk];
+      raw_t ok[kMergeChunk][NL];
 #pragma unroll
       for (int c = 0; c < kMergeChunk; ++c) {
         const int k = min(kc + c, k1);
         const size_t base = (size_t)(k + ic) * a.H + h;
-        mk[c] = a.part_ml[base * 2];
-        lk[c] = a.part_ml[base * 2 + 1];
+        const float2 ml = *(const float2*)(a.part_ml + base * 2);
+        mk[c] = ml.x;
+        lk[c] = ml.y;
         const bf16* src = a.part_o + base * R + j0;
-        if constexpr (CPL % 4 == 0) {
 #pragma unroll
-          for (int u = 0; u < CPL; u += 4) {
-            const bf16x4 v = *(const bf16x4*)(src + u);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ok[c][u + e] = (float)v[e];
-          }
-        } else {
-          ok[c][0] = (float)src[0];
-        }
+        for (int u = 0; u < NL; ++u) ok[c][u] = *(const raw_t*)(src + CV * u);
       }
 #pragma unroll
       for (int c = 0; c < kMergeChunk; ++c) {
@@ -522,21 +541,29 @@ __global__ void __launch_bounds__(256) mla_decode_merge(DecodeMergeArgs a) {
         const float sa = fast_exp2(m - m_new), sb = fast_exp2(mk[c] - m_new);
         L = L * sa + lk[c] * sb;
 #pragma unroll
-        for (int u = 0; u < CPL; ++u) acc[u] = acc[u] * sa + ok[c][u] * sb;
+        for (int u = 0; u < NL; ++u) {
+          if constexpr (CV == 8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[8 * u + e] = acc[8 * u + e] * sa + (float)ok[c][u][e] * sb;
+          } else {
+            acc[u] = acc[u] * sa + (float)ok[c][u] * sb;
+          }
+        }
         m = m_new;
       }
     }
+    // the first v-tile's operands are requested only now: a wave's loads
+    // complete in order, so issued earlier they would delay krange and the
+    // partials behind them
+    if (w < DV / 16) load_w(w, wa, gv);
     const float invL = 1.0f / L;
 #pragma unroll
     for (int u = 0; u < CPL; ++u) olat[sl][j0 + u] = (bf16)(acc[u] * invL);
-    // rows 8..15 are the unused MFMA columns: keep them finite
-#pragma unroll
-    for (int u = 0; u < CPL; ++u) olat[kMergeSeqs + sl][j0 + u] = (bf16)0.0f;
   }
   __syncthreads();
 
   // o_lat^T B operand for k-step kk: slot p <-> latent dim 32kk + 8kq + p
-  for (int vt = w; vt < DV / 16; vt += 4) {
+  for (int vt = w; vt < DV / 16; vt += kMergeWaves) {
     if (vt != w) load_w(vt, wa, gv);
     f32x4 acc = f32x4{};
 #pragma unroll

@@ -123,7 +123,7 @@ void launch_decode_bf16(const mla::DecodeAbsorbArgs& aa, const mla::DecodeSplitA
   hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(aa.H * (R / JC)), dim3(256), 0, s, aa);
   hipLaunchKernelGGL((mla::mla_decode_split<R>), dim3(sa.G), dim3(64 * mla::kDecodeWaves), 0, s, sa);
   hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + mla::kMergeSeqs - 1) / mla::kMergeSeqs) * ma.H),
-                     dim3(256), 0, s, ma);
+                     dim3(64 * mla::kMergeWaves), 0, s, ma);
 }
 
 template <int DQ, int DV, int R>
@@ -136,7 +136,7 @@ void launch_decode_paged_bf16(const mla::DecodeAbsorbArgs& aa, const int* seq_le
   hipLaunchKernelGGL((mla::mla_decode_absorb<DQ, R>), dim3(aa.H * (R / JC)), dim3(256), 0, s, aa);
   hipLaunchKernelGGL((mla::mla_decode_split_paged<R>), dim3(sa.G), dim3(64 * mla::kDecodeWaves), 0, s, sa);
   hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + mla::kMergeSeqs - 1) / mla::kMergeSeqs) * ma.H),
-                     dim3(256), 0, s, ma);
+                     dim3(64 * mla::kMergeWaves), 0, s, ma);
 }
 
 // r = 512: per-sequence tiles, one-wave-per-SIMD split kernel (packed cache:
@@ -160,7 +160,7 @@ void launch_decode_solo(mla::DecodeAbsorbArgs aa, const int* seq_lens, const int
   ma.N = 0;
   ma.krange = krange;
   hipLaunchKernelGGL((mla::mla_decode_merge<DV, R>), dim3(((ma.B + mla::kMergeSeqs - 1) / mla::kMergeSeqs) * ma.H),
-                     dim3(256), 0, s, ma);
+                     dim3(64 * mla::kMergeWaves), 0, s, ma);
 }
 
 struct PagedDecodeLayout {
