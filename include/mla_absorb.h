@@ -69,7 +69,9 @@ const char* mla_status_string(mla_status s);
 
 /*
  * Bytes of workspace mla_absorb_prefill needs for these sizes (0 is a valid
- * answer).  Returns (size_t)-1 for invalid sizes.
+ * answer).  Returns (size_t)-1 for invalid sizes.  The bf16 workspace holds
+ * W_UK transposed per head and a work-item counter that the call itself
+ * clears before use; calls that overlap on one workspace race.
  */
 size_t mla_absorb_prefill_workspace_size(int B, int T, int H, int d_q, int r, mla_dtype dtype);
 

@@ -30,9 +30,11 @@ namespace mla {
 // ----------------------------------------------------------------- W_UK^T
 template <typename T>
 __global__ void __launch_bounds__(256) mla_wuk_transpose(const T* __restrict__ w, T* __restrict__ wt,
-                                                         int DQ, int R) {
+                                                         int DQ, int R, unsigned* queue) {
   // one 32 (d) x 32 (j) tile per workgroup (head blockIdx.z): read rows of W_UK[h], write rows of W_UK^T[h]
   __shared__ T tile[32][33];
+  // the prefill that follows on the stream takes its work items from *queue
+  if (queue && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *queue = 0u;
   const int h = blockIdx.z;
   const int j0 = blockIdx.x * 32, d0 = blockIdx.y * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8

@@ -104,7 +104,7 @@ void launch_prefill_bf16(mla::PrefillArgs a, hipStream_t s) {
   if constexpr (R >= 256) {
     a.ntb = (a.T + mla::kSoloRows - 1) / mla::kSoloRows;
     a.nhg = a.H;  // one head per workgroup
-    a.xcd_remap = (a.nhg % 8) == 0 ? 1 : 0;
+    a.xcd_remap = (a.nhg % 8) == 0 ? 1 : 0;  // the order without a queue
     hipLaunchKernelGGL((mla::mla_prefill_solo_kernel<DQ, DV, R, PAGED>), dim3(a.B * a.ntb * a.nhg),
                        dim3(64 * mla::kSoloWaves), 0, s, a);
   } else {
@@ -198,9 +198,16 @@ bool paged_geometry_ok(int B, int r, long long num_pages, int page_size, int max
          (long long)B * max_pages * page_size / 32 < (1LL << 31);
 }
 
-void launch_wuk_transpose(const bf16* w, bf16* wt, int H, int dq, int r, hipStream_t s) {
+void launch_wuk_transpose(const bf16* w, bf16* wt, int H, int dq, int r, hipStream_t s,
+                          unsigned* queue = nullptr) {
   hipLaunchKernelGGL((mla::mla_wuk_transpose<bf16>), dim3((r + 31) / 32, (dq + 31) / 32, H), dim3(256), 0, s,
-                     w, wt, dq, r);
+                     w, wt, dq, r, queue);
+}
+
+// Prefill workspace: W_UK^T [H, r, d_q] bf16, then the work-item counter of
+// the r >= 256 kernel in a slot of its own.
+size_t prefill_ws_bytes(int H, int r, int dq) {
+  return align_up((size_t)H * r * dq * sizeof(bf16)) + kAlign;
 }
 
 struct ForwardLayout {
@@ -218,7 +225,7 @@ ForwardLayout forward_layout(int B, int T, int q_rank, int H, int dq, int dv, in
   L.q = off;    off = align_up(off + N * H * dq * sizeof(bf16));
   L.gate = off; off = align_up(off + N * H * dv * sizeof(bf16));
   L.o = off;    off = align_up(off + N * H * dv * sizeof(bf16));
-  L.core = off; off = align_up(off + (size_t)H * r * dq * sizeof(bf16));
+  L.core = off; off = align_up(off + prefill_ws_bytes(H, r, dq));
   L.total = off;
   return L;
 }
@@ -366,7 +373,7 @@ TrainLayout train_layout(int B, int T, int q_rank, int H, int dq, int dv, int r)
   L.gate = off;   off = align_up(off + N * H * dv * sizeof(bf16));
   L.o = off;      off = align_up(off + N * H * dv * sizeof(bf16));
   L.lse = off;    off = align_up(off + N * H * sizeof(float));
-  L.core = off;   off = align_up(off + (size_t)H * r * dq * sizeof(bf16));
+  L.core = off;   off = align_up(off + prefill_ws_bytes(H, r, dq));
   L.total = off;
   return L;
 }
@@ -442,7 +449,7 @@ size_t mla_absorb_prefill_workspace_size(int B, int T, int H, int d_q, int r, ml
   if (B <= 0 || T <= 0 || H <= 0 || d_q <= 0 || r <= 0) return kBadSize;
   if (dtype == MLA_DTYPE_F32) return 0;
   if (dtype != MLA_DTYPE_BF16) return kBadSize;
-  return align_up((size_t)H * r * d_q * sizeof(bf16));
+  return prefill_ws_bytes(H, r, d_q);
 }
 
 mla_status mla_absorb_prefill(const void* q, const void* c, const void* w_uk, const void* w_uv,
@@ -492,9 +499,11 @@ static mla_status extend_impl(const void* q, const void* c, const int32_t* block
   if ((long long)B * ((T + 15) / 16) * ((H + 1) / 2) >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
 
   bf16* wukT = (bf16*)workspace;
-  launch_wuk_transpose((const bf16*)w_uk, wukT, H, d_q, r, s);
+  unsigned* queue = (unsigned*)((char*)workspace + align_up((size_t)H * r * d_q * sizeof(bf16)));
+  launch_wuk_transpose((const bf16*)w_uk, wukT, H, d_q, r, s, queue);
 
   mla::PrefillArgs a{};
+  a.queue = queue;
   a.q = (const bf16*)q; a.c = (const bf16*)c; a.wukT = wukT; a.wuv = (const bf16*)w_uv;
   a.gate = (const bf16*)gate; a.out = (bf16*)out;
   a.B = B; a.T = T; a.S = S; a.H = H;

@@ -35,6 +35,10 @@ struct PrefillArgs {
   int ntb;           // ceil(T / kPrefillRows) query blocks
   int nhg;           // ceil(H / 4) head groups
   int xcd_remap;     // 1: head group hg runs on XCD hg % 8 (weights stay in its L2)
+  // if set (r >= 256 kernel, not varlen): workgroups take work items in the
+  // order they start from this counter, which is zero at launch (the W_UK
+  // transpose clears it), instead of from blockIdx
+  unsigned* queue;
   // paged latent (the kernels' PAGED instantiations): c is a pool of
   // num_pages pages of 2^page_shift rows (at least the 32-row key tile);
   // row u of sequence b is page block_table[b, u >> page_shift], slot

@@ -122,7 +122,21 @@ mla_prefill_solo_kernel(PrefillArgs a) {
   MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
 
   // ---- work item (128 positions of one head), heaviest query blocks first
-  const int x = blockIdx.x;
+  int x = blockIdx.x;
+  if constexpr (!VARLEN) {
+    if (a.queue) {
+      // Items go out in the order workgroups start, so the XCDs that run at
+      // a higher clock take more of them (the clock differs by XCD under
+      // this load, and a fixed share per XCD waits for the slowest).  The
+      // item is passed on through the first LDS word, which every wave has
+      // read before the second barrier lets any copy into the stages start.
+      if (threadIdx.x == 0) *(MLA_LDS unsigned*)smem = atomicAdd(a.queue, 1u);
+      __syncthreads();
+      const unsigned item = __builtin_amdgcn_readfirstlane(*(const MLA_LDS unsigned*)smem);
+      __syncthreads();
+      x = item < gridDim.x ? (int)item : x;  // a counter not cleared cannot send work out of range
+    }
+  }
   int tb, b, hg;
   if constexpr (VARLEN) {
     hg = x % a.nhg;
@@ -131,7 +145,7 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     const int2 e = a.blocks[i];
     b = __builtin_amdgcn_readfirstlane(e.x);
     tb = __builtin_amdgcn_readfirstlane(e.y);
-  } else if (a.xcd_remap) {
+  } else if (a.xcd_remap && !a.queue) {
     // gridDim.x = 8 * per; XCD x % 8 owns head groups hg = x % 8 (mod 8)
     const int xcd = x & 7, pos = x >> 3, nh8 = a.nhg >> 3;
     hg = (pos % nh8) * 8 + xcd;
