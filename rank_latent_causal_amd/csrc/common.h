@@ -225,7 +225,9 @@ __device__ __forceinline__ float col_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + fast_exp2(-g * kLog2e)); }
+// (v_rcp_f32, about 1 ulp: the gated value is rounded to bf16 anyway; a
+// correctly rounded divide costs a dozen instructions more per element)
+__device__ __forceinline__ float sigmoidf_(float g) { return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-g * kLog2e)); }
 
 // Two 4-value C fragments (scaled) -> one bf16 MFMA operand (k slots 0-3
 // from lo, 4-7 from hi), round-to-nearest-even.

@@ -614,41 +614,65 @@ mla_prefill_solo_kernel(PrefillArgs a) {
     a.lse[((size_t)b * H + h) * T + t] = (m_run + __builtin_log2f(l_tot)) * 0.69314718055994531f;
   const bool store = tvalid && hvalid;
   const size_t orow = (qr0 + (tvalid ? t : T - 1)) * (size_t)H * DV + (size_t)hc * DV;
+  // O^T is packed unnormalised (bf16 keeps the same relative precision) and
+  // 1/l is applied to the products instead: 16 values per v-block and lane
+  // rather than 16 per latent block
   bf16x8 ob[2 * NLB];
 #pragma unroll
   for (int u = 0; u < NLB; ++u) {
-    ob[2 * u] = pack8(oT[u], 0, inv_l);
-    ob[2 * u + 1] = pack8(oT[u], 8, inv_l);
+    ob[2 * u] = pack8(oT[u], 0, 1.0f);
+    ob[2 * u + 1] = pack8(oT[u], 8, 1.0f);
+    // packed here, not sunk into the products below, where the fp32 values
+    // would hold the registers the operand reads run ahead in
+    asm volatile("" : "+v"(ob[2 * u]), "+v"(ob[2 * u + 1]));
   }
   // this lane's gate logits v = 32 vb + 8 c + 4 (l / 32) + 0..3 of row l32
   const MLA_LDS char* grow = gbuf + l32 * (DV * 2) + 8 * hh;
   const MLA_LDS char* wrow = smem + l32 * (R * 2) + 8 * hh;  // + 32 vb R 2
+  // All of W_UV and the gate rows have landed by now (the packing above
+  // runs under the copies), so one wait and one barrier cover them, and the
+  // v-blocks run as NVB independent chains over the shared O^T operands:
+  // the operand reads run ahead of the products and the products issue
+  // back to back.
+  wait_vmcnt<0>();
+  wg_barrier();  // W_UV and the gate rows copied by every wave
+  f32x16 acc[NVB];
+  // k-block kb = latent 16 kb + 8 c + 4 (l / 32) + e for slot 4 c + e; the
+  // operands of k-block kb + 1 are read while the products of kb issue.
+  // The products are compiler builtins (their register hazards stay the
+  // compiler's), fenced by scheduling barriers so that the reads stay a
+  // k-block ahead instead of being sunk to each product.
+  bf16x8 wop[2][NVB];
+  auto read_w = [&](int kb, bf16x8 (&o)[NVB]) {
 #pragma unroll
-  for (int vb = 0; vb < NVB; ++vb) {
-    if (vb + 3 < NVB) wait_vmcnt<3 * CPV>();
-    else if (vb + 2 < NVB) wait_vmcnt<2 * CPV>();
-    else if (vb + 1 < NVB) wait_vmcnt<CPV>();
-    else wait_vmcnt<0>();
-    wg_barrier();  // v-block vb copied by every wave
-    const MLA_LDS char* rb = wrow + vb * 32 * (R * 2);
-    f32x16 acc = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < 2 * NLB; ++kb) {
-      // k-block kb = latent 16 kb + 8 c + 4 (l / 32) + e for slot 4 c + e
+    for (int vb = 0; vb < NVB; ++vb) {
+      const MLA_LDS char* rb = wrow + vb * 32 * (R * 2);
       const bf16x4 lo = *(const MLA_LDS bf16x4*)(rb + (((2 * kb) ^ (l32 & 15)) << 4));
       const bf16x4 hi = *(const MLA_LDS bf16x4*)(rb + (((2 * kb + 1) ^ (l32 & 15)) << 4));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat4(lo, hi), ob[kb], acc, 0, 0, 0);
+      o[vb] = cat4(lo, hi);
     }
-    if (store) {
+  };
+  read_w(0, wop[0]);
+#pragma unroll
+  for (int kb = 0; kb < 2 * NLB; ++kb) {
+    if (kb + 1 < 2 * NLB) read_w(kb + 1, wop[(kb + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb)
+      acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[kb & 1][vb], ob[kb], kb == 0 ? f32x16{} : acc[vb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (store) {
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         bf16x4 ov;
         const bf16x4 gl = *(const MLA_LDS bf16x4*)(grow + (((4 * vb + c) ^ (l32 & (GCR - 1))) << 4));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[4 * c + e] * sigmoidf_((float)gl[e]));
+        for (int e = 0; e < 4; ++e) ov[e] = (bf16)(acc[vb][4 * c + e] * (inv_l * sigmoidf_((float)gl[e])));
         *(bf16x4*)(a.out + orow + 32 * vb + 8 * c + 4 * hh) = ov;
       }
-    }
   }
 }
 
