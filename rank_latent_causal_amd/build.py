@@ -21,17 +21,21 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# device code generation flags, shared by the library and its assembly listing
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+         # packed fp32 VALU forms are kept out of every kernel
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # the one-wave-per-SIMD kernels unroll their 32-product phases
+         # completely (operand arrays must stay in registers); the default
+         # size limit for "#pragma unroll" loops is below that of the decode
+         # kernel's phase, which then keeps a loop with dynamically
+         # indexed operands and spills
+         "-mllvm", "-pragma-unroll-threshold=65536",
+         f"-I{INCLUDE}"]
+
+
 def _compile(srcs, out_path: str, verbose: bool) -> str:
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           # packed fp32 VALU forms are kept out of every kernel
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           # the one-wave-per-SIMD kernels unroll their 32-product phases
-           # completely (operand arrays must stay in registers); the default
-           # size limit for "#pragma unroll" loops is below that of the decode
-           # kernel's phase, which then keeps a loop with dynamically
-           # indexed operands and spills
-           "-mllvm", "-pragma-unroll-threshold=65536",
-           f"-I{INCLUDE}", *srcs, "-o", out_path + ".tmp"]
+    cmd = [hipcc(), *FLAGS, "-fPIC", "-shared", *srcs, "-o", out_path + ".tmp"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "not a recognized feature" not in l)
     if res.returncode != 0:
@@ -39,6 +43,15 @@ def _compile(srcs, out_path: str, verbose: bool) -> str:
     if verbose and msgs.strip():
         print(msgs)
     os.replace(out_path + ".tmp", out_path)
+    return out_path
+
+
+def device_asm(src: str, out_path: str) -> str:
+    """The gfx950 assembly that the library build generates for one source."""
+    cmd = [hipcc(), *FLAGS, "--cuda-device-only", "-S", src, "-o", out_path]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     return out_path
 
 

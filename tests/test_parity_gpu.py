@@ -90,6 +90,26 @@ def test_prefill_full_workload_sampled(o):
     assert_parity(got[rows], oracle_prefill(o, d, rows=rows), dg.BF16, "full sampled", block=d["d_v"])
 
 
+@pytest.mark.parametrize("B,T,H,shape", [(1, 130, 5, "mid"), (2, 300, 16, "mid"), (2, 70, 9, "full"), (1, 520, 24, "full")])
+def test_prefill_deterministic(B, T, H, shape):
+    """Repeated calls give the same bits.  Work items go to whichever
+    workgroup starts next, so an item lands on a different CU from call to
+    call; with other GPU work in between, a read of LDS or registers that
+    the item did not write itself (or a missed hazard) shows up here as a
+    run-to-run difference."""
+    import torch
+    dq, dv, r = SHAPES[shape]
+    d = dg.prefill_inputs(B, T, H, dq, dv, r, dtype=dg.BF16, seed=4400 + T + H)
+    d["scale"] = dq ** -0.5
+    log(f"prefill determinism B={B} T={T} H={H} r={r}")
+    first = run_prefill(d)
+    for rep in range(4):
+        torch.randn(1 << 22, device="cuda").sum()  # other work between the calls
+        again = run_prefill(d)
+        n = int((again != first).sum().item())
+        assert n == 0, f"call {rep + 1} differs from call 0 in {n} elements"
+
+
 def test_prefill_first_position_closed_form():
     """t = 0 sees only its own latent: out = sigmoid(g) * (c_0 W_UV^T) for any
     q and scale (checked on the GPU output alone, at the full width)."""
