@@ -9,7 +9,7 @@ import pytest
 import datagen as dg
 import oracle
 from gpu_util import (assert_parity, oracle_decode, oracle_extend, oracle_prefill, run_decode, run_extend,
-                      run_prefill, sample_rows, to_host_f64)
+                      run_prefill, sample_rows, to_dev, to_host_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -108,6 +108,30 @@ def test_prefill_deterministic(B, T, H, shape):
         again = run_prefill(d)
         n = int((again != first).sum().item())
         assert n == 0, f"call {rep + 1} differs from call 0 in {n} elements"
+
+
+@pytest.mark.parametrize("shape", ["mid", "full"])
+def test_prefill_poisoned_workspace(shape):
+    """The r = 256 / 512 prefill takes its work items from a counter in the
+    workspace that the call clears before its kernel starts: a workspace full
+    of 0xFF bytes (the counter far out of range), and the same workspace
+    reused by a second call, give the bits of a call with a fresh one."""
+    import torch
+    import rank_latent_causal_amd as mla
+    dq, dv, r = SHAPES[shape]
+    B, T, H = 2, 200, 12
+    d = dg.prefill_inputs(B, T, H, dq, dv, r, dtype=dg.BF16, seed=4700 + r)
+    d["scale"] = dq ** -0.5
+    log(f"prefill poisoned workspace B={B} T={T} H={H} r={r}")
+    args = [to_dev(d[k]) for k in ("q", "c", "w_uk", "w_uv", "gate")]
+    ref = mla.mla_absorb_prefill(*args, d["scale"])
+    n = mla.prefill_workspace_size(B, T, H, dq, r, mla.DTYPE_BF16)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    first = mla.mla_absorb_prefill(*args, d["scale"], workspace=ws)
+    second = mla.mla_absorb_prefill(*args, d["scale"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(first, ref), "poisoned workspace changed the result"
+    assert torch.equal(second, ref), "a reused workspace changed the result"
 
 
 def test_prefill_first_position_closed_form():
