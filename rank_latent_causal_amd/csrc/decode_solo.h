@@ -520,8 +520,12 @@ mla_decode_solo(DecodeSoloArgs a) {
       m_run = mx;
     }
   }
+  // this wave's zero-row copies past the range still write the stages: they
+  // must land before the workgroup's LDS is released.  The wait comes before
+  // the last partial's stores, which the wave leaves in flight (the counter
+  // covers stores too, and waiting for them held every workgroup's end)
+  wait_vmcnt<0>();
   emit(cur);
-  wait_vmcnt<0>();  // this wave's zero-row copies past the range still write the stages
 }
 
 }  // namespace mla
