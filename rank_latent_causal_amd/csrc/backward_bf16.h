@@ -78,27 +78,54 @@ struct BwdPrepArgs {
 };
 
 // One workgroup per token row; wave w takes heads w, w+4, ...; lanes walk the
-// DV values of a head.
+// DV values of a head.  The heads go in batches of HB whose loads are all
+// issued before the batch's first store: the stores may alias the loads as
+// far as the compiler knows, so a loop storing head by head would wait one
+// memory round trip per head.
+template <int DV>
 __global__ void __launch_bounds__(256) mla_bwd_prep(BwdPrepArgs a) {
+  constexpr int NV = (DV + 63) / 64;  // values per lane and head
+  constexpr int HB = 6;               // heads per batch of loads
   const int bt = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int b = bt / a.T, t = bt % a.T;
-  const size_t row = (size_t)bt * a.H * a.DV;
-  for (int h = w; h < a.H; h += 4) {
-    float dsum = 0.0f;
-    for (int v = lane; v < a.DV; v += 64) {
-      const size_t i = row + (size_t)h * a.DV + v;
-      const float g = (float)a.gate[i], o = (float)a.out[i], d = (float)a.dout[i];
-      const float s = sigmoidf_(g);
-      a.dgate[(size_t)bt * a.ldg + (size_t)h * a.DV + v] = (bf16)(d * o * (1.0f - s));
-      a.dov[((size_t)h * a.B * a.T + bt) * a.DV + v] = (bf16)(d * s);
-      dsum += d * o;
+  const size_t row = (size_t)bt * a.H * DV;
+  for (int hb = w; hb < a.H; hb += 4 * HB) {
+    float g[HB][NV], o[HB][NV], d[HB][NV], lse[HB];
+#pragma unroll
+    for (int u = 0; u < HB; ++u) {
+      // clamped addresses: every load is issued, none behind a branch
+      const int hc = min(hb + 4 * u, a.H - 1);
+      lse[u] = a.lse[((size_t)b * a.H + hc) * a.T + t];
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const size_t i = row + (size_t)hc * DV + min(lane + 64 * j, DV - 1);
+        g[u][j] = (float)a.gate[i];
+        o[u][j] = (float)a.out[i];
+        d[u][j] = (float)a.dout[i];
+      }
     }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, 64);
-    if (lane == 0) {
-      float* dst = a.ld + ((size_t)h * a.B * a.T + bt) * 2;
-      dst[0] = a.lse[((size_t)b * a.H + h) * a.T + t] * kLog2e;
-      dst[1] = dsum;
+    for (int u = 0; u < HB; ++u) {
+      const int h = hb + 4 * u;
+      if (h >= a.H) break;  // wave-uniform
+      float dsum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int v = lane + 64 * j;
+        if (v < DV) {
+          const float s = sigmoidf_(g[u][j]);
+          a.dgate[(size_t)bt * a.ldg + (size_t)h * DV + v] = (bf16)(d[u][j] * o[u][j] * (1.0f - s));
+          a.dov[((size_t)h * a.B * a.T + bt) * DV + v] = (bf16)(d[u][j] * s);
+          dsum += d[u][j] * o[u][j];
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, 64);
+      if (lane == 0) {
+        float* dst = a.ld + ((size_t)h * a.B * a.T + bt) * 2;
+        dst[0] = lse[u] * kLog2e;
+        dst[1] = dsum;
+      }
     }
   }
 }

@@ -321,7 +321,7 @@ void launch_backward_projections(const bf16* q, const bf16* wukT, const bf16* do
 template <int DQ, int DV, int R>
 void launch_backward_bf16(const mla::BwdPrepArgs& pa, const mla::BwdArgs& ba, const bf16* q, const bf16* wukT,
                           const bf16* wuvT, hipStream_t s) {
-  hipLaunchKernelGGL(mla::mla_bwd_prep, dim3(pa.B * pa.T), dim3(256), 0, s, pa);
+  hipLaunchKernelGGL(mla::mla_bwd_prep<DV>, dim3(pa.B * pa.T), dim3(256), 0, s, pa);
   launch_backward_projections(q, wukT, pa.dov, wuvT, const_cast<bf16*>(ba.qabs), const_cast<bf16*>(ba.dolat),
                               pa.B * pa.T, ba.H, DQ, DV, R, ba.scale * mla::kLog2e, s);
   hipLaunchKernelGGL((mla::mla_bwd_query<R>), dim3(ba.B * ba.ntb * ba.H), dim3(64 * mla::kBwdWaves), 0, s, ba);
