@@ -187,7 +187,7 @@ struct DecodeAbsorbArgs {
   bf16* qabs;       // [B, H, R]
   int B, H;
   float qscale;
-  int with_prep;    // the last workgroup runs decode_prepare(prep) instead
+  int with_prep;    // workgroup 0 runs decode_prepare(prep) instead
   PrepareArgs prep;
 };
 
@@ -208,11 +208,14 @@ __global__ void __launch_bounds__(256) mla_decode_absorb(DecodeAbsorbArgs a) {
   static_assert(R % JC == 0 && JC % 16 == 0 && DQ % 8 == 0, "absorb tiling");
   constexpr int IT = 4;                  // 16-sequence blocks in flight
   __shared__ __attribute__((aligned(16))) bf16 wt[DP][LD];
-  if (a.with_prep && blockIdx.x == gridDim.x - 1) {
+  // The range table's workgroup is block 0, so that its chain of dependent
+  // steps starts with the first blocks rather than after the last.
+  if (a.with_prep && blockIdx.x == 0) {
     decode_prepare(a.prep);
     return;
   }
-  const int h = blockIdx.x / (R / JC), J0 = (blockIdx.x % (R / JC)) * JC;
+  const int bx = blockIdx.x - a.with_prep;
+  const int h = bx / (R / JC), J0 = (bx % (R / JC)) * JC;
   const bf16* __restrict__ src = a.wuk + (size_t)h * DQ * R + J0;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l16 = lane & 15, kq = lane >> 4;

@@ -146,7 +146,7 @@ template <int DQ, int DV, int R, bool PAGED>
 void launch_decode_solo(mla::DecodeAbsorbArgs aa, const int* seq_lens, const int* cu, int max_rows, int G,
                         int* krange, const mla::DecodeSoloArgs& sa, mla::DecodeMergeArgs ma, hipStream_t s) {
   constexpr int JC = R < 64 ? R : 64;
-  // the absorb's last workgroup prepares the tile sums and the range table
+  // the absorb's first workgroup prepares the tile sums and the range table
   aa.with_prep = 1;
   aa.prep = mla::PrepareArgs{seq_lens, cu, sa.B, max_rows, G, const_cast<int*>(sa.lens), const_cast<int*>(sa.cu_t),
                              const_cast<int*>(sa.rt), krange, mla::kDecodeSwitchTiles};
